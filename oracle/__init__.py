@@ -1,0 +1,167 @@
+"""CPU oracle for the reproducible add-reductions (sum, keyed scatter-add, anchored scan).
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU-baseline
+leg may import this package.  The GPU library (``scan_fixed_order_amd``) never imports,
+loads or calls it; the two share no code.
+
+The arithmetic lives in ``detref.c`` (plain C, single-threaded, one IEEE addition per
+``+``); this module only builds it with gcc and marshals numpy arrays through ctypes.
+Every function here follows the association order stated in ``detref.c``:
+
+* ``pw``            -- adjacent-pair tree padded with -0.0 (course page "Floating point and
+                       reproducibility", the fixed bracket over pairs).
+* ``det_sum``       -- ``pw`` of the array, +0.0 when empty.
+* ``scatter_add``   -- stable grouping by destination in ascending source index, ``pw`` per
+                       destination and column, initial value added last (Warp "Deterministic
+                       Execution", Pattern 1; ``warp.tile_atomic_add_indexed`` for rows).
+* ``scan``          -- tiles of V*L elements, anchor intervals of A tiles (drjit-core pull
+                       request "Make CUDA floating-point prefix sums deterministic").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "detref.c")
+_LIB_PATH = os.path.join(_HERE, "libdetref.so")
+
+# Spec constants of the scan (tile = L lanes x V elements; A tiles per anchor interval).
+SPEC_V = 32
+SPEC_L = 256
+SPEC_A = 256
+
+EXCLUSIVE = 1
+REVERSE = 2
+
+_CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-std=c99", "-Wall"]
+
+
+def build(force: bool = True) -> str:
+    """Compile detref.c twice (f32, f64) with gcc and link libdetref.so."""
+    if not force and os.path.exists(_LIB_PATH):
+        return _LIB_PATH
+    objs = []
+    for t, suf in (("float", "_f32"), ("double", "_f64")):
+        obj = os.path.join(_HERE, f"detref{suf}.o")
+        subprocess.check_call(["gcc", *_CFLAGS, f"-DDET_T={t}", f"-DDET_SUF={suf}", "-c", _SRC,
+                               "-o", obj])
+        objs.append(obj)
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-shared", "-o", tmp, *objs])
+    os.replace(tmp, _LIB_PATH)
+    for o in objs:
+        os.remove(o)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    for suf, ct in (("_f32", ctypes.c_float), ("_f64", ctypes.c_double)):
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        f = getattr(lib, "oref_pw" + suf)
+        f.argtypes, f.restype = [p, i64], ct
+        f = getattr(lib, "oref_sum" + suf)
+        f.argtypes, f.restype = [p, i64], ct
+        f = getattr(lib, "oref_scatter_add" + suf)
+        f.argtypes, f.restype = [p, p, i64, i64, p, i64, p], i64
+        f = getattr(lib, "oref_scan" + suf)
+        f.argtypes = [p, p, i64, ctypes.c_uint, p, i64, i64, i64, i64]
+        f.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _suffix(dtype) -> str:
+    dt = np.dtype(dtype)
+    if dt == np.float32:
+        return "_f32"
+    if dt == np.float64:
+        return "_f64"
+    raise TypeError(f"oracle supports float32/float64, got {dt}")
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def pw(v: np.ndarray):
+    """Pairwise tree over ``v`` (1-D float32/float64), returned as a numpy scalar."""
+    v = np.ascontiguousarray(v)
+    suf = _suffix(v.dtype)
+    r = getattr(_load(), "oref_pw" + suf)(_ptr(v), v.size)
+    return v.dtype.type(r)
+
+
+def det_sum(x: np.ndarray):
+    """Reproducible sum: ``pw(x)`` for n >= 1, +0.0 for an empty array."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    suf = _suffix(x.dtype)
+    r = getattr(_load(), "oref_sum" + suf)(_ptr(x), x.size)
+    return x.dtype.type(r)
+
+
+def scatter_add(values: np.ndarray, index: np.ndarray, out: np.ndarray,
+                want_prev: bool = False) -> Tuple[np.ndarray, Optional[np.ndarray], int]:
+    """Keyed scatter-add along axis 0.
+
+    ``values`` has shape [n] or [n, d]; ``index`` int32 [n]; ``out`` shape [B] or [B, d].
+    Returns ``(new_out, prev, n_skipped)``; ``out`` itself is not modified.  ``prev`` has the
+    shape of ``values`` and holds the destination's value before the call for every valid
+    source row (rows with an out-of-range index keep NaN there).
+    """
+    values = np.ascontiguousarray(values)
+    index = np.ascontiguousarray(index, dtype=np.int32).reshape(-1)
+    n = index.size
+    row_len = 1 if values.ndim == 1 else int(np.prod(values.shape[1:]))
+    if values.size != n * row_len:
+        raise ValueError("values and index disagree on n")
+    if out.dtype != values.dtype:
+        raise TypeError("values and out must share a dtype")
+    new = np.array(out, dtype=out.dtype, copy=True, order="C")
+    num_out = new.size // row_len if row_len else 0
+    if new.size != num_out * row_len:
+        raise ValueError("out is not a whole number of rows")
+    prev = np.full(values.shape, np.nan, dtype=values.dtype) if want_prev else None
+    suf = _suffix(values.dtype)
+    k = getattr(_load(), "oref_scatter_add" + suf)(_ptr(values), _ptr(index), n, row_len,
+                                                    _ptr(new), num_out, _ptr(prev))
+    if k < 0:
+        raise RuntimeError(f"oracle scatter_add failed ({k})")
+    return new, prev, int(k)
+
+
+def scan(x: np.ndarray, exclusive: bool = False, reverse: bool = False,
+         offsets: Optional[np.ndarray] = None, V: int = SPEC_V, L: int = SPEC_L,
+         A: int = SPEC_A) -> np.ndarray:
+    """Anchored prefix sum; ``offsets`` (int64 [S+1], 0 = o_0 <= ... <= o_S = n) makes it
+    segmented.  V, L, A default to the spec constants."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    y = np.empty_like(x)
+    flags = (EXCLUSIVE if exclusive else 0) | (REVERSE if reverse else 0)
+    offs = None
+    nseg = 0
+    if offsets is not None:
+        offs = np.ascontiguousarray(offsets, dtype=np.int64).reshape(-1)
+        nseg = offs.size - 1
+        if nseg < 0:
+            raise ValueError("offsets needs at least one entry")
+    suf = _suffix(x.dtype)
+    rc = getattr(_load(), "oref_scan" + suf)(_ptr(x), _ptr(y), x.size, flags, _ptr(offs), nseg,
+                                             V, L, A)
+    if rc != 0:
+        raise ValueError(f"oracle scan rejected its arguments ({rc})")
+    return y

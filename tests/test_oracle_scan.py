@@ -1,0 +1,299 @@
+"""Pins for the oracle's anchored prefix scan.
+
+The scan's order (tiles of L lanes x V elements, lane-serial runs, a Kogge-Stone pass
+over lane totals, pairwise trees over tile totals inside anchor intervals of A tiles, and a
+carry that only crosses intervals) follows drjit-core pull request "Make CUDA
+floating-point prefix sums deterministic" (sections "Implementation" and "Validation").
+The oracle takes V, L, A as parameters so tiny instances can be worked out by hand.
+
+Checks, none of which reuses the oracle's code:
+* hand-written expressions for tiny (V, L, A) instances, evaluated with numpy scalars;
+* a top-down brute-force evaluator that builds every output's expression tree from the
+  stated order and evaluates it (tiny n, many tiles and intervals);
+* textbook special cases: n <= V is a sequential cumulative sum (numpy's ``cumsum``);
+  all-ones inputs give exact integers in every mode;
+* invariants at the real constants: exclusive is inclusive shifted, reverse is the mirror
+  of forward, one segment equals the unsegmented scan, a segment's outputs equal the
+  unsegmented scan with everything before the segment replaced by the identity;
+* the error bound of the expression depth against exact prefix sums.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+F32 = np.float32
+F64 = np.float64
+
+
+def rounding_values(n, dtype, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 4, n)
+            * np.where(rng.random(n) < 0.5, -1, 1)).astype(dtype)
+
+
+def same_bits(a, b):
+    return np.asarray(a).tobytes() == np.asarray(b).tobytes()
+
+
+# ---------------------------------------------------------------- hand-written tiny instances
+
+@pytest.mark.parametrize("seed", range(20))
+def test_hand_V2_L2_A2_two_tiles(seed):
+    x = rounding_values(8, F32, seed)
+    x0, x1, x2, x3, x4, x5, x6, x7 = x
+    agg0 = (x0 + x1) + (x2 + x3)
+    want = [x0, x0 + x1, (x0 + x1) + x2, (x0 + x1) + (x2 + x3),
+            agg0 + x4, agg0 + (x4 + x5), (agg0 + (x4 + x5)) + x6, (agg0 + (x4 + x5)) + (x6 + x7)]
+    y = oracle.scan(x, V=2, L=2, A=2)
+    assert same_bits(y, np.array(want, F32))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_hand_V1_L1_A2_carry_chain(seed):
+    # one element per tile; intervals of two tiles; the carry into interval q+1 is
+    # C_q + (x_2q + x_2q+1), while the last output of interval q is (C_q + x_2q) + x_2q+1
+    x = rounding_values(7, F32, seed)
+    c1 = x[0] + x[1]
+    c2 = c1 + (x[2] + x[3])
+    c3 = c2 + (x[4] + x[5])
+    want = [x[0], x[0] + x[1], c1 + x[2], (c1 + x[2]) + x[3], c2 + x[4], (c2 + x[4]) + x[5],
+            c3 + x[6]]
+    assert same_bits(oracle.scan(x, V=1, L=1, A=2), np.array(want, F32))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_hand_V1_L1_A4_lookback_tree(seed):
+    x = rounding_values(8, F32, seed)
+    x0, x1, x2, x3, x4, x5, x6, x7 = x
+    c1 = (x0 + x1) + (x2 + x3)
+    want = [x0, x0 + x1, (x0 + x1) + x2, ((x0 + x1) + x2) + x3,
+            c1 + x4, (c1 + x4) + x5, (c1 + (x4 + x5)) + x6, (c1 + ((x4 + x5) + x6)) + x7]
+    assert same_bits(oracle.scan(x, V=1, L=1, A=4), np.array(want, F32))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_hand_V1_L4_A1_kogge_stone(seed):
+    x = rounding_values(8, F32, seed)
+    x0, x1, x2, x3, x4, x5, x6, x7 = x
+    a0 = (x0 + x1) + (x2 + x3)
+    want = [x0, x0 + x1, (x0 + x1) + x2, (x0 + (x1 + x2)) + x3,
+            a0 + x4, (a0 + x4) + x5, (a0 + (x4 + x5)) + x6, (a0 + (x4 + (x5 + x6))) + x7]
+    assert same_bits(oracle.scan(x, V=1, L=4, A=1), np.array(want, F32))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_hand_segmented_and_exclusive(seed):
+    # V=1, L=4, A=1, segments [0,2) [2,5) [5,8)
+    x = rounding_values(8, F32, seed)
+    x0, x1, x2, x3, x4, x5, x6, x7 = x
+    offs = np.array([0, 2, 5, 8])
+    incl = [x0, x0 + x1, x2, x2 + x3, (x2 + x3) + x4, x5, x5 + x6, (x5 + x6) + x7]
+    assert same_bits(oracle.scan(x, offsets=offs, V=1, L=4, A=1), np.array(incl, F32))
+    excl = [0.0, incl[0], 0.0, incl[2], incl[3], 0.0, incl[5], incl[6]]
+    assert same_bits(oracle.scan(x, exclusive=True, offsets=offs, V=1, L=4, A=1),
+                     np.array(excl, F32))
+
+
+# ---------------------------------------------------------------- brute force, top down
+
+def _pw_expr(items):
+    if not items:
+        return None
+    if len(items) == 1:
+        return items[0]
+    k = 1
+    while 2 * k < len(items):
+        k *= 2
+    return (_pw_expr(items[:k]), _pw_expr(items[k:]))
+
+
+def _brute_exprs(n, V, L, A):
+    """Expression of every forward inclusive output; leaves are indices, None = identity."""
+    T = V * L
+
+    def leaf(i):
+        return i if i < n else None
+
+    def lane_prefix(j, t, k):
+        e = leaf(j * T + t * V)
+        for r in range(1, k + 1):
+            e = (e, leaf(j * T + t * V + r))
+        return e
+
+    def ks(j, t, d):  # lane t after the Kogge-Stone steps with offsets < d
+        if d == 1:
+            return lane_prefix(j, t, V - 1)
+        h = d // 2
+        return (ks(j, t - h, h), ks(j, t, h)) if t >= h else ks(j, t, h)
+
+    D = 1
+    while D < L:
+        D *= 2
+
+    def agg(j):
+        return ks(j, L - 1, D)
+
+    def carry(q):
+        if q == 0:
+            return None
+        nt = (n + T - 1) // T
+        grp = [agg(jj) for jj in range((q - 1) * A, min(q * A, nt))]
+        return (carry(q - 1), _pw_expr(grp))
+
+    out = []
+    for i in range(n):
+        j, r = divmod(i, T)
+        t, k = divmod(r, V)
+        q = j // A
+        e = (carry(q), _pw_expr([agg(jj) for jj in range(q * A, j)]))
+        p = ks(j, t - 1, D) if t > 0 else None
+        out.append(((e, p), lane_prefix(j, t, k)))
+    return out
+
+
+def _eval(expr, x, ident):
+    if expr is None:
+        return ident
+    if isinstance(expr, tuple):
+        return _eval(expr[0], x, ident) + _eval(expr[1], x, ident)
+    return x[expr]
+
+
+@pytest.mark.parametrize("V,L,A", [(2, 2, 2), (1, 4, 2), (3, 2, 3), (2, 4, 1), (1, 1, 3),
+                                   (4, 3, 2)])
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_brute_force_expressions(V, L, A, dtype):
+    rng = np.random.default_rng(V * 100 + L * 10 + A)
+    eps = float(np.finfo(dtype).eps)
+    alphabet = np.array([1.0, eps, eps / 2, -1.0, 3.0, -eps / 2, 0.75], dtype)
+    ident = dtype(-0.0)
+    for n in (1, 5, V * L * A + 1, 3 * V * L * A + 2, 40):
+        exprs = _brute_exprs(n, V, L, A)
+        for trial in range(4):
+            x = alphabet[rng.integers(0, alphabet.size, n)]
+            want = np.array([_eval(e, x, ident) for e in exprs], dtype)
+            assert same_bits(oracle.scan(x, V=V, L=L, A=A), want), (n, trial)
+            # reverse: mirror of the forward scan of the flipped input
+            wr = np.array([_eval(e, x[::-1].copy(), ident) for e in exprs], dtype)[::-1]
+            assert same_bits(oracle.scan(x, reverse=True, V=V, L=L, A=A), wr)
+            # segmented: mask everything before the segment start with the identity
+            cuts = np.sort(rng.choice(np.arange(1, n), size=min(3, max(0, n - 1)),
+                                      replace=False)) if n > 1 else np.zeros(0, int)
+            offs = np.concatenate([[0], cuts, [n]])
+            ws = np.empty(n, dtype)
+            for a, b in zip(offs[:-1], offs[1:]):
+                xm = x.copy()
+                xm[:a] = ident
+                for i in range(a, b):
+                    ws[i] = _eval(exprs[i], xm, ident)
+            assert same_bits(oracle.scan(x, offsets=offs, V=V, L=L, A=A), ws), (n, offs)
+
+
+# ---------------------------------------------------------------- textbook special cases
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_single_lane_is_sequential_cumsum(dtype):
+    for n in range(1, 33):
+        x = rounding_values(n, dtype, n)
+        assert same_bits(oracle.scan(x), np.cumsum(x, dtype=dtype))
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 8191, 8192, 8193, 16384, 164738])
+def test_all_ones_every_mode(n):
+    x = np.ones(n, F32)
+    i = np.arange(n, dtype=np.float64)
+    assert np.array_equal(oracle.scan(x), i + 1)
+    assert np.array_equal(oracle.scan(x, exclusive=True), i)
+    assert np.array_equal(oracle.scan(x, reverse=True), n - i)
+    assert np.array_equal(oracle.scan(x, exclusive=True, reverse=True), n - 1 - i)
+    offs = np.unique(np.concatenate([[0], np.arange(0, n, 97), [n]]))
+    start = offs[np.searchsorted(offs, np.arange(n), side="right") - 1]
+    assert np.array_equal(oracle.scan(x, offsets=offs), np.arange(n) - start + 1)
+
+
+def test_all_ones_many_intervals():
+    n = 3 * 256 * 8192 + 5                     # four anchor intervals at the spec constants
+    y = oracle.scan(np.ones(n, F32))
+    assert np.array_equal(y, np.arange(1, n + 1, dtype=np.float64))
+
+
+# ---------------------------------------------------------------- invariants at spec constants
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n", [16384, 164738, 2 * 256 * 8192 + 4097])
+def test_shift_mirror_and_segment_relations(dtype, n):
+    x = rounding_values(n, dtype, 7)
+    inc = oracle.scan(x)
+    exc = oracle.scan(x, exclusive=True)
+    assert same_bits(exc[1:], inc[:-1]) and same_bits(exc[:1], np.zeros(1, dtype))
+    rev = oracle.scan(x, reverse=True)
+    assert same_bits(rev, oracle.scan(x[::-1].copy())[::-1])
+    rex = oracle.scan(x, exclusive=True, reverse=True)
+    assert same_bits(rex[:-1], rev[1:]) and same_bits(rex[-1:], np.zeros(1, dtype))
+    one = np.array([0, n])
+    assert same_bits(oracle.scan(x, offsets=one), inc)
+    assert same_bits(oracle.scan(x, offsets=one, reverse=True, exclusive=True), rex)
+    # a few long segments, one empty: masking equivalence for each segment
+    offs = np.array([0, 5000, 5000, n // 2 + 3, n - 1, n])
+    seg = oracle.scan(x, offsets=offs)
+    for a, b in zip(offs[:-1], offs[1:]):
+        if a == b:
+            continue
+        xm = x.copy()
+        xm[:a] = -0.0
+        assert same_bits(seg[a:b], oracle.scan(xm)[a:b])
+    segr = oracle.scan(x, offsets=offs, reverse=True)
+    for a, b in zip(offs[:-1], offs[1:]):
+        if a == b:
+            continue
+        xm = x.copy()
+        xm[b:] = -0.0
+        assert same_bits(segr[a:b], oracle.scan(xm, reverse=True)[a:b])
+
+
+def test_heads_everywhere_copy_input():
+    x = rounding_values(1000, F32, 3)
+    offs = np.arange(0, 1001)
+    assert same_bits(oracle.scan(x, offsets=offs), x)
+    assert same_bits(oracle.scan(x, offsets=offs, exclusive=True), np.zeros(1000, F32))
+
+
+def test_signed_zero_and_nonfinite():
+    x = np.full(10, -0.0, F32)
+    assert same_bits(oracle.scan(x), x)                        # -0.0 prefixes stay -0.0
+    ex = oracle.scan(x, exclusive=True)
+    assert ex[0].tobytes() == np.float32(0.0).tobytes()       # exclusive starts at +0.0
+    x = np.array([1, np.inf, 1, -np.inf, 2], F32)
+    y = oracle.scan(x)
+    assert y[0] == 1 and y[1] == np.inf and y[2] == np.inf and np.isnan(y[3]) and np.isnan(y[4])
+
+
+def test_bad_offsets_rejected():
+    x = np.ones(10, F32)
+    for offs in ([1, 10], [0, 9], [0, 6, 4, 10]):
+        with pytest.raises(ValueError):
+            oracle.scan(x, offsets=np.array(offs))
+
+
+# ---------------------------------------------------------------- error bound
+
+@pytest.mark.parametrize("dtype,u", [(F32, 2.0**-24), (F64, 2.0**-53)])
+def test_error_bound_against_exact_prefix(dtype, u):
+    V, L, A = 4, 4, 2                                 # many tiles and intervals at small n
+    n = 3000
+    x = rounding_values(n, dtype, 9)
+    y = oracle.scan(x, V=V, L=L, A=A)
+    T = V * L
+    nq = -(-(-(-n // T)) // A)
+    depth = V + math.ceil(math.log2(L)) + math.ceil(math.log2(A)) + nq + 4
+    g = depth * u / (1 - depth * u)
+    acc = Fraction(0)
+    absacc = 0.0
+    for i in range(n):
+        acc += Fraction(float(x[i]))
+        absacc += abs(float(x[i]))
+        assert abs(Fraction(float(y[i])) - acc) <= Fraction(g * absacc * (1 + 1e-9)), i
