@@ -14,7 +14,7 @@ Every function here follows the association order stated in ``detref.c``:
 * ``scatter_add``   -- stable grouping by destination in ascending source index, ``pw`` per
                        destination and column, initial value added last (Warp "Deterministic
                        Execution", Pattern 1; ``warp.tile_atomic_add_indexed`` for rows).
-* ``scan``          -- tiles of V*L elements, anchor intervals of A tiles (drjit-core pull
+* ``scan``          -- tiles of V*W*NW elements, anchor intervals of A tiles (drjit-core pull
                        request "Make CUDA floating-point prefix sums deterministic").
 """
 from __future__ import annotations
@@ -30,9 +30,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "detref.c")
 _LIB_PATH = os.path.join(_HERE, "libdetref.so")
 
-# Spec constants of the scan (tile = L lanes x V elements; A tiles per anchor interval).
+# Spec constants of the scan: V elements per lane, W lanes per wave, NW waves per tile
+# (tile = V * W * NW = 8192 elements), A tiles per anchor interval.
 SPEC_V = 32
-SPEC_L = 256
+SPEC_W = 64
+SPEC_NW = 4
 SPEC_A = 256
 
 EXCLUSIVE = 1
@@ -79,7 +81,7 @@ def _load():
         f = getattr(lib, "oref_scatter_add" + suf)
         f.argtypes, f.restype = [p, p, i64, i64, p, i64, p], i64
         f = getattr(lib, "oref_scan" + suf)
-        f.argtypes = [p, p, i64, ctypes.c_uint, p, i64, i64, i64, i64]
+        f.argtypes = [p, p, i64, ctypes.c_uint, p, i64, i64, i64, i64, i64]
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -145,10 +147,10 @@ def scatter_add(values: np.ndarray, index: np.ndarray, out: np.ndarray,
 
 
 def scan(x: np.ndarray, exclusive: bool = False, reverse: bool = False,
-         offsets: Optional[np.ndarray] = None, V: int = SPEC_V, L: int = SPEC_L,
-         A: int = SPEC_A) -> np.ndarray:
+         offsets: Optional[np.ndarray] = None, V: int = SPEC_V, W: int = SPEC_W,
+         NW: int = SPEC_NW, A: int = SPEC_A) -> np.ndarray:
     """Anchored prefix sum; ``offsets`` (int64 [S+1], 0 = o_0 <= ... <= o_S = n) makes it
-    segmented.  V, L, A default to the spec constants."""
+    segmented.  V, W, NW, A default to the spec constants."""
     x = np.ascontiguousarray(x).reshape(-1)
     y = np.empty_like(x)
     flags = (EXCLUSIVE if exclusive else 0) | (REVERSE if reverse else 0)
@@ -161,7 +163,7 @@ def scan(x: np.ndarray, exclusive: bool = False, reverse: bool = False,
             raise ValueError("offsets needs at least one entry")
     suf = _suffix(x.dtype)
     rc = getattr(_load(), "oref_scan" + suf)(_ptr(x), _ptr(y), x.size, flags, _ptr(offs), nseg,
-                                             V, L, A)
+                                             V, W, NW, A)
     if rc != 0:
         raise ValueError(f"oracle scan rejected its arguments ({rc})")
     return y

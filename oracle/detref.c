@@ -38,8 +38,9 @@
  *      ascending source index; if M is non-empty out = out_init + PW(M), else out
  *      is left untouched.  Indices outside [0, num_out) are skipped and counted.
  *      prev[i] is out_init at i's destination (snapshot before the call).
- *  R5  scan tile / lane / anchor layout, see oref_scan below (V, L, A are
- *      parameters so tiny instances can be checked by hand and by brute force).
+ *  R5  scan tile / wave / lane / anchor layout, see scan_forward_inclusive below
+ *      (V, W, NW, A are parameters so tiny instances can be checked by hand and by
+ *      brute force).
  *  R6  exclusive = inclusive shifted by one with +0.0 entering at every segment
  *      head; reverse = flip, forward scan, flip; segments via head flags and the
  *      standard segmented operator (flag_a|flag_b, flag_b ? b : a+b).
@@ -183,16 +184,20 @@ static pair_t pw_pairs(const pair_t* v, int64_t m) {
     return r;
 }
 
-/* Local part of tile j (tile = L lanes x V elements, lane t owns a run of V
- * consecutive elements):
- *   s[t*V+k]  lane-serial inclusive prefix of lane t's run,
- *   p[t]      exclusive prefix over the lane totals by a Kogge-Stone scan
- *             (offsets 1, 2, 4, ... < L, each step using the previous step's values),
- *   *agg      the tile total (last Kogge-Stone value).
+/* Local part of tile j.  A tile is NW waves of W lanes; lane t (= w*W + l) owns a run of
+ * V consecutive elements.
+ *   s[t*V+k]  lane-serial inclusive prefix of lane t's run;
+ *   p[t]      exclusive prefix of lane t inside its wave: a Kogge-Stone scan over the W lane
+ *             totals of the wave (offsets 1, 2, 4, ... < W, each step using the previous
+ *             step's values), shifted by one lane;
+ *   pw[w]     exclusive prefix of wave w inside the tile: the same Kogge-Stone rule over the
+ *             NW wave totals (offsets 1, 2, ... < NW), shifted by one wave;
+ *   *agg      the tile total (last wave-level Kogge-Stone value).
  * Positions at or past n are identity leaves. */
 static void tile_local(const DET_T* x, const unsigned char* h, int64_t n, int64_t j,
-                       int64_t V, int64_t L, pair_t* s, pair_t* u, pair_t* tmp, pair_t* p,
-                       pair_t* agg) {
+                       int64_t V, int64_t W, int64_t NW, pair_t* s, pair_t* u, pair_t* tmp,
+                       pair_t* p, pair_t* om, pair_t* pw, pair_t* agg) {
+    int64_t L = W * NW;
     int64_t T = V * L;
     for (int64_t t = 0; t < L; ++t) {
         for (int64_t k = 0; k < V; ++k) {
@@ -203,39 +208,49 @@ static void tile_local(const DET_T* x, const unsigned char* h, int64_t n, int64_
         }
         u[t] = s[t * V + V - 1];
     }
-    for (int64_t d = 1; d < L; d *= 2) {
-        for (int64_t t = 0; t < L; ++t) tmp[t] = (t >= d) ? segop(u[t - d], u[t]) : u[t];
+    for (int64_t d = 1; d < W; d *= 2) {
+        for (int64_t t = 0; t < L; ++t) tmp[t] = (t % W >= d) ? segop(u[t - d], u[t]) : u[t];
         memcpy(u, tmp, (size_t)L * sizeof(pair_t));
     }
-    for (int64_t t = 0; t < L; ++t) p[t] = (t == 0) ? pair_identity() : u[t - 1];
-    *agg = u[L - 1];
+    for (int64_t t = 0; t < L; ++t) p[t] = (t % W == 0) ? pair_identity() : u[t - 1];
+    for (int64_t w = 0; w < NW; ++w) om[w] = u[w * W + W - 1];
+    for (int64_t d = 1; d < NW; d *= 2) {
+        for (int64_t w = 0; w < NW; ++w) tmp[w] = (w >= d) ? segop(om[w - d], om[w]) : om[w];
+        memcpy(om, tmp, (size_t)NW * sizeof(pair_t));
+    }
+    for (int64_t w = 0; w < NW; ++w) pw[w] = (w == 0) ? pair_identity() : om[w - 1];
+    *agg = om[NW - 1];
 }
 
-/* Forward inclusive scan of (x, h) into y with constants V, L, A.
+/* Forward inclusive scan of (x, h) into y with constants V, W, NW, A.
  *   Agg_j        tile totals;
  *   interval q   = tiles [qA, qA+A);
  *   G_q          = PW(Agg of every tile of interval q);
  *   C_0 = id,    C_{q+1} = C_q (+) G_q          (the carry through anchor q);
  *   W_j          = PW(Agg_{qA}, ..., Agg_{j-1})  (identity for the interval's first tile);
  *   E_j          = C_q (+) W_j;
- *   y            = (E_j (+) p_t) (+) s[t*V+k]. */
+ *   y            = ((E_j (+) pw[w]) (+) p[t]) (+) s[t*V+k]. */
 static int scan_forward_inclusive(const DET_T* x, const unsigned char* h, int64_t n,
-                                  int64_t V, int64_t L, int64_t A, DET_T* y) {
+                                  int64_t V, int64_t W, int64_t NW, int64_t A, DET_T* y) {
     if (n == 0) return OREF_OK;
+    int64_t L = W * NW;
     int64_t T = V * L;
     int64_t nt = (n + T - 1) / T;
     int64_t nq = (nt + A - 1) / A;
+    int64_t big = L > NW ? L : NW;
     pair_t* agg = (pair_t*)malloc((size_t)nt * sizeof(pair_t));
     pair_t* carry = (pair_t*)malloc((size_t)(nq + 1) * sizeof(pair_t));
     pair_t* s = (pair_t*)malloc((size_t)T * sizeof(pair_t));
     pair_t* u = (pair_t*)malloc((size_t)L * sizeof(pair_t));
-    pair_t* tmp = (pair_t*)malloc((size_t)L * sizeof(pair_t));
+    pair_t* tmp = (pair_t*)malloc((size_t)big * sizeof(pair_t));
     pair_t* p = (pair_t*)malloc((size_t)L * sizeof(pair_t));
-    if (!agg || !carry || !s || !u || !tmp || !p) {
-        free(agg); free(carry); free(s); free(u); free(tmp); free(p);
+    pair_t* om = (pair_t*)malloc((size_t)NW * sizeof(pair_t));
+    pair_t* pw = (pair_t*)malloc((size_t)NW * sizeof(pair_t));
+    if (!agg || !carry || !s || !u || !tmp || !p || !om || !pw) {
+        free(agg); free(carry); free(s); free(u); free(tmp); free(p); free(om); free(pw);
         return OREF_NO_MEM;
     }
-    for (int64_t j = 0; j < nt; ++j) tile_local(x, h, n, j, V, L, s, u, tmp, p, &agg[j]);
+    for (int64_t j = 0; j < nt; ++j) tile_local(x, h, n, j, V, W, NW, s, u, tmp, p, om, pw, &agg[j]);
     carry[0] = pair_identity();
     for (int64_t q = 0; q < nq; ++q) {
         int64_t cnt = (nt - q * A < A) ? nt - q * A : A;
@@ -243,18 +258,18 @@ static int scan_forward_inclusive(const DET_T* x, const unsigned char* h, int64_
     }
     for (int64_t j = 0; j < nt; ++j) {
         pair_t a;
-        tile_local(x, h, n, j, V, L, s, u, tmp, p, &a);
+        tile_local(x, h, n, j, V, W, NW, s, u, tmp, p, om, pw, &a);
         int64_t q = j / A;
         pair_t e = segop(carry[q], pw_pairs(agg + q * A, j - q * A));
         for (int64_t t = 0; t < L; ++t) {
-            pair_t xt = segop(e, p[t]);
+            pair_t xt = segop(segop(e, pw[t / W]), p[t]);
             for (int64_t k = 0; k < V; ++k) {
                 int64_t i = j * T + t * V + k;
                 if (i < n) y[i] = segop(xt, s[t * V + k]).v;
             }
         }
     }
-    free(agg); free(carry); free(s); free(u); free(tmp); free(p);
+    free(agg); free(carry); free(s); free(u); free(tmp); free(p); free(om); free(pw);
     return OREF_OK;
 }
 
@@ -262,8 +277,9 @@ static int scan_forward_inclusive(const DET_T* x, const unsigned char* h, int64_
  * offsets[0..S] with offsets[0] == 0 <= ... <= offsets[S] == n.  x and y must not
  * overlap.  Returns OREF_OK or an error code. */
 int FN(oref_scan)(const DET_T* x, DET_T* y, int64_t n, unsigned flags, const int64_t* offsets,
-                  int64_t num_segments, int64_t V, int64_t L, int64_t A) {
-    if (n < 0 || V < 1 || L < 1 || A < 1 || (flags & ~(OREF_EXCLUSIVE | OREF_REVERSE)))
+                  int64_t num_segments, int64_t V, int64_t W, int64_t NW, int64_t A) {
+    if (n < 0 || V < 1 || W < 1 || NW < 1 || A < 1 ||
+        (flags & ~(OREF_EXCLUSIVE | OREF_REVERSE)))
         return OREF_BAD_ARG;
     if (offsets) {
         if (num_segments < 0 || offsets[0] != 0 || offsets[num_segments] != n) return OREF_BAD_ARG;
@@ -289,7 +305,7 @@ int FN(oref_scan)(const DET_T* x, DET_T* y, int64_t n, unsigned flags, const int
             }
         }
     }
-    int rc = scan_forward_inclusive(xs, h, n, V, L, A, ys);
+    int rc = scan_forward_inclusive(xs, h, n, V, W, NW, A, ys);
     if (rc == OREF_OK) {
         for (int64_t f = 0; f < n; ++f) {
             DET_T v;

@@ -1,13 +1,13 @@
 """Pins for the oracle's anchored prefix scan.
 
-The scan's order (tiles of L lanes x V elements, lane-serial runs, a Kogge-Stone pass
-over lane totals, pairwise trees over tile totals inside anchor intervals of A tiles, and a
-carry that only crosses intervals) follows drjit-core pull request "Make CUDA
+The scan's order (tiles of NW waves x W lanes x V elements, lane-serial runs, Kogge-Stone
+passes over lane totals inside each wave and over the wave totals, pairwise trees over tile
+totals inside anchor intervals of A tiles, and a carry that only crosses intervals) follows drjit-core pull request "Make CUDA
 floating-point prefix sums deterministic" (sections "Implementation" and "Validation").
-The oracle takes V, L, A as parameters so tiny instances can be worked out by hand.
+The oracle takes V, W, NW, A as parameters so tiny instances can be worked out by hand.
 
 Checks, none of which reuses the oracle's code:
-* hand-written expressions for tiny (V, L, A) instances, evaluated with numpy scalars;
+* hand-written expressions for tiny (V, W, NW, A) instances, evaluated with numpy scalars;
 * a top-down brute-force evaluator that builds every output's expression tree from the
   stated order and evaluates it (tiny n, many tiles and intervals);
 * textbook special cases: n <= V is a sequential cumulative sum (numpy's ``cumsum``);
@@ -42,18 +42,18 @@ def same_bits(a, b):
 # ---------------------------------------------------------------- hand-written tiny instances
 
 @pytest.mark.parametrize("seed", range(20))
-def test_hand_V2_L2_A2_two_tiles(seed):
+def test_hand_V2_W2_A2_two_tiles(seed):
     x = rounding_values(8, F32, seed)
     x0, x1, x2, x3, x4, x5, x6, x7 = x
     agg0 = (x0 + x1) + (x2 + x3)
     want = [x0, x0 + x1, (x0 + x1) + x2, (x0 + x1) + (x2 + x3),
             agg0 + x4, agg0 + (x4 + x5), (agg0 + (x4 + x5)) + x6, (agg0 + (x4 + x5)) + (x6 + x7)]
-    y = oracle.scan(x, V=2, L=2, A=2)
+    y = oracle.scan(x, V=2, W=2, NW=1, A=2)
     assert same_bits(y, np.array(want, F32))
 
 
 @pytest.mark.parametrize("seed", range(20))
-def test_hand_V1_L1_A2_carry_chain(seed):
+def test_hand_V1_W1_A2_carry_chain(seed):
     # one element per tile; intervals of two tiles; the carry into interval q+1 is
     # C_q + (x_2q + x_2q+1), while the last output of interval q is (C_q + x_2q) + x_2q+1
     x = rounding_values(7, F32, seed)
@@ -62,39 +62,51 @@ def test_hand_V1_L1_A2_carry_chain(seed):
     c3 = c2 + (x[4] + x[5])
     want = [x[0], x[0] + x[1], c1 + x[2], (c1 + x[2]) + x[3], c2 + x[4], (c2 + x[4]) + x[5],
             c3 + x[6]]
-    assert same_bits(oracle.scan(x, V=1, L=1, A=2), np.array(want, F32))
+    assert same_bits(oracle.scan(x, V=1, W=1, NW=1, A=2), np.array(want, F32))
 
 
 @pytest.mark.parametrize("seed", range(20))
-def test_hand_V1_L1_A4_lookback_tree(seed):
+def test_hand_V1_W1_A4_lookback_tree(seed):
     x = rounding_values(8, F32, seed)
     x0, x1, x2, x3, x4, x5, x6, x7 = x
     c1 = (x0 + x1) + (x2 + x3)
     want = [x0, x0 + x1, (x0 + x1) + x2, ((x0 + x1) + x2) + x3,
             c1 + x4, (c1 + x4) + x5, (c1 + (x4 + x5)) + x6, (c1 + ((x4 + x5) + x6)) + x7]
-    assert same_bits(oracle.scan(x, V=1, L=1, A=4), np.array(want, F32))
+    assert same_bits(oracle.scan(x, V=1, W=1, NW=1, A=4), np.array(want, F32))
 
 
 @pytest.mark.parametrize("seed", range(20))
-def test_hand_V1_L4_A1_kogge_stone(seed):
+def test_hand_V1_W4_A1_kogge_stone(seed):
     x = rounding_values(8, F32, seed)
     x0, x1, x2, x3, x4, x5, x6, x7 = x
     a0 = (x0 + x1) + (x2 + x3)
     want = [x0, x0 + x1, (x0 + x1) + x2, (x0 + (x1 + x2)) + x3,
             a0 + x4, (a0 + x4) + x5, (a0 + (x4 + x5)) + x6, (a0 + (x4 + (x5 + x6))) + x7]
-    assert same_bits(oracle.scan(x, V=1, L=4, A=1), np.array(want, F32))
+    assert same_bits(oracle.scan(x, V=1, W=4, NW=1, A=1), np.array(want, F32))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_hand_V1_W2_NW2_A1_two_level(seed):
+    # two waves of two lanes: lane prefixes inside a wave, then the wave totals
+    # (a single Kogge-Stone over four lanes would give y3 = (x0 + (x1 + x2)) + x3 instead)
+    x = rounding_values(8, F32, seed)
+    x0, x1, x2, x3, x4, x5, x6, x7 = x
+    a0 = (x0 + x1) + (x2 + x3)
+    want = [x0, x0 + x1, (x0 + x1) + x2, ((x0 + x1) + x2) + x3,
+            a0 + x4, (a0 + x4) + x5, (a0 + (x4 + x5)) + x6, ((a0 + (x4 + x5)) + x6) + x7]
+    assert same_bits(oracle.scan(x, V=1, W=2, NW=2, A=1), np.array(want, F32))
 
 
 @pytest.mark.parametrize("seed", range(20))
 def test_hand_segmented_and_exclusive(seed):
-    # V=1, L=4, A=1, segments [0,2) [2,5) [5,8)
+    # V=1, W=4, NW=1, A=1, segments [0,2) [2,5) [5,8)
     x = rounding_values(8, F32, seed)
     x0, x1, x2, x3, x4, x5, x6, x7 = x
     offs = np.array([0, 2, 5, 8])
     incl = [x0, x0 + x1, x2, x2 + x3, (x2 + x3) + x4, x5, x5 + x6, (x5 + x6) + x7]
-    assert same_bits(oracle.scan(x, offsets=offs, V=1, L=4, A=1), np.array(incl, F32))
+    assert same_bits(oracle.scan(x, offsets=offs, V=1, W=4, NW=1, A=1), np.array(incl, F32))
     excl = [0.0, incl[0], 0.0, incl[2], incl[3], 0.0, incl[5], incl[6]]
-    assert same_bits(oracle.scan(x, exclusive=True, offsets=offs, V=1, L=4, A=1),
+    assert same_bits(oracle.scan(x, exclusive=True, offsets=offs, V=1, W=4, NW=1, A=1),
                      np.array(excl, F32))
 
 
@@ -111,9 +123,9 @@ def _pw_expr(items):
     return (_pw_expr(items[:k]), _pw_expr(items[k:]))
 
 
-def _brute_exprs(n, V, L, A):
+def _brute_exprs(n, V, W, NW, A):
     """Expression of every forward inclusive output; leaves are indices, None = identity."""
-    T = V * L
+    T = V * W * NW
 
     def leaf(i):
         return i if i < n else None
@@ -124,34 +136,46 @@ def _brute_exprs(n, V, L, A):
             e = (e, leaf(j * T + t * V + r))
         return e
 
-    def ks(j, t, d):  # lane t after the Kogge-Stone steps with offsets < d
+    def pow2_at_least(m):
+        d = 1
+        while d < m:
+            d *= 2
+        return d
+
+    DW, DN = pow2_at_least(W), pow2_at_least(NW)
+
+    def ks(j, t, d):  # lane t after the in-wave Kogge-Stone steps with offsets < d
         if d == 1:
             return lane_prefix(j, t, V - 1)
         h = d // 2
-        return (ks(j, t - h, h), ks(j, t, h)) if t >= h else ks(j, t, h)
+        return (ks(j, t - h, h), ks(j, t, h)) if t % W >= h else ks(j, t, h)
 
-    D = 1
-    while D < L:
-        D *= 2
+    def wks(j, w, d):  # wave total w after the wave-level steps with offsets < d
+        if d == 1:
+            return ks(j, w * W + W - 1, DW)
+        h = d // 2
+        return (wks(j, w - h, h), wks(j, w, h)) if w >= h else wks(j, w, h)
 
     def agg(j):
-        return ks(j, L - 1, D)
+        return wks(j, NW - 1, DN)
+
+    nt = (n + T - 1) // T
 
     def carry(q):
         if q == 0:
             return None
-        nt = (n + T - 1) // T
-        grp = [agg(jj) for jj in range((q - 1) * A, min(q * A, nt))]
-        return (carry(q - 1), _pw_expr(grp))
+        return (carry(q - 1), _pw_expr([agg(jj) for jj in range((q - 1) * A, min(q * A, nt))]))
 
     out = []
     for i in range(n):
         j, r = divmod(i, T)
         t, k = divmod(r, V)
+        w, l = divmod(t, W)
         q = j // A
         e = (carry(q), _pw_expr([agg(jj) for jj in range(q * A, j)]))
-        p = ks(j, t - 1, D) if t > 0 else None
-        out.append(((e, p), lane_prefix(j, t, k)))
+        pw_ = wks(j, w - 1, DN) if w > 0 else None
+        p = ks(j, t - 1, DW) if l > 0 else None
+        out.append((((e, pw_), p), lane_prefix(j, t, k)))
     return out
 
 
@@ -163,23 +187,23 @@ def _eval(expr, x, ident):
     return x[expr]
 
 
-@pytest.mark.parametrize("V,L,A", [(2, 2, 2), (1, 4, 2), (3, 2, 3), (2, 4, 1), (1, 1, 3),
-                                   (4, 3, 2)])
+@pytest.mark.parametrize("V,W,NW,A", [(2, 2, 1, 2), (1, 4, 1, 2), (3, 2, 2, 3), (2, 2, 2, 1),
+                                       (1, 1, 3, 3), (4, 3, 2, 2), (1, 2, 3, 2), (2, 4, 4, 2)])
 @pytest.mark.parametrize("dtype", [F32, F64])
-def test_brute_force_expressions(V, L, A, dtype):
-    rng = np.random.default_rng(V * 100 + L * 10 + A)
+def test_brute_force_expressions(V, W, NW, A, dtype):
+    rng = np.random.default_rng(V * 1000 + W * 100 + NW * 10 + A)
     eps = float(np.finfo(dtype).eps)
     alphabet = np.array([1.0, eps, eps / 2, -1.0, 3.0, -eps / 2, 0.75], dtype)
     ident = dtype(-0.0)
-    for n in (1, 5, V * L * A + 1, 3 * V * L * A + 2, 40):
-        exprs = _brute_exprs(n, V, L, A)
+    for n in (1, 5, V * W * NW * A + 1, 3 * V * W * NW * A + 2, 40):
+        exprs = _brute_exprs(n, V, W, NW, A)
         for trial in range(4):
             x = alphabet[rng.integers(0, alphabet.size, n)]
             want = np.array([_eval(e, x, ident) for e in exprs], dtype)
-            assert same_bits(oracle.scan(x, V=V, L=L, A=A), want), (n, trial)
+            assert same_bits(oracle.scan(x, V=V, W=W, NW=NW, A=A), want), (n, trial)
             # reverse: mirror of the forward scan of the flipped input
             wr = np.array([_eval(e, x[::-1].copy(), ident) for e in exprs], dtype)[::-1]
-            assert same_bits(oracle.scan(x, reverse=True, V=V, L=L, A=A), wr)
+            assert same_bits(oracle.scan(x, reverse=True, V=V, W=W, NW=NW, A=A), wr)
             # segmented: mask everything before the segment start with the identity
             cuts = np.sort(rng.choice(np.arange(1, n), size=min(3, max(0, n - 1)),
                                       replace=False)) if n > 1 else np.zeros(0, int)
@@ -190,7 +214,7 @@ def test_brute_force_expressions(V, L, A, dtype):
                 xm[:a] = ident
                 for i in range(a, b):
                     ws[i] = _eval(exprs[i], xm, ident)
-            assert same_bits(oracle.scan(x, offsets=offs, V=V, L=L, A=A), ws), (n, offs)
+            assert same_bits(oracle.scan(x, offsets=offs, V=V, W=W, NW=NW, A=A), ws), (n, offs)
 
 
 # ---------------------------------------------------------------- textbook special cases
@@ -283,13 +307,13 @@ def test_bad_offsets_rejected():
 
 @pytest.mark.parametrize("dtype,u", [(F32, 2.0**-24), (F64, 2.0**-53)])
 def test_error_bound_against_exact_prefix(dtype, u):
-    V, L, A = 4, 4, 2                                 # many tiles and intervals at small n
+    V, W, NW, A = 4, 2, 2, 2                          # many tiles and intervals at small n
     n = 3000
     x = rounding_values(n, dtype, 9)
-    y = oracle.scan(x, V=V, L=L, A=A)
-    T = V * L
+    y = oracle.scan(x, V=V, W=W, NW=NW, A=A)
+    T = V * W * NW
     nq = -(-(-(-n // T)) // A)
-    depth = V + math.ceil(math.log2(L)) + math.ceil(math.log2(A)) + nq + 4
+    depth = V + math.ceil(math.log2(W)) + math.ceil(math.log2(NW)) + math.ceil(math.log2(A)) + nq + 5
     g = depth * u / (1 - depth * u)
     acc = Fraction(0)
     absacc = 0.0
