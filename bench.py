@@ -1,0 +1,228 @@
+"""Benchmark of the reproducible add-reductions on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic f32 input at
+n = 2^28: det_sum (uniform [0,1) values), det_scan (inclusive forward, normal x 10^U(-4,4)
+values with random signs) and det_scatter_add (normal values into 65,536 uniform int32 bins).
+Inputs are resident in HBM before the timed region.  `value` is the step's algorithmic bytes
+(sum 4n, scan 8n, scatter 8n + 8*bins) divided by the step time.
+
+Prints ONE JSON line.  Besides the contract fields it carries:
+  roofline      the kernel with the largest share of the step, its algorithmic bytes per launch
+                over its average launch time (HIP events on the launching stream), vs 8 TB/s;
+  ops           per operation: time, GB/s, Gelem/s, fraction of 8 TB/s, the non-deterministic
+                baseline's time on the same input and the deterministic-mode overhead;
+  cpu_baseline  the CPU oracle (single thread) on a bounded sample of the same workload.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--log2n", type=int, default=28)
+    ap.add_argument("--bins", type=int, default=65536)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baselines", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of sum,scan,scatter (profiling)")
+    return ap.parse_args()
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from scan_fixed_order_amd import det, workloads
+
+    dev = torch.device("cuda:0")
+    n = 1 << args.log2n
+    B = args.bins
+    only = set(filter(None, args.only.split(","))) or {"sum", "scan", "scatter"}
+
+    # ---------------------------------------------------------------- inputs (host -> HBM)
+    t0 = time.time()
+    host = {}
+    if "sum" in only:
+        host["x_sum"] = workloads.uniform01(n, seed=0)
+    if "scan" in only:
+        host["x_scan"] = workloads.scan_values(n, np.float32, seed=2)
+    if "scatter" in only:
+        host["v_sc"] = workloads.normal(n, seed=1)
+        host["b_sc"] = workloads.bins_uniform(n, B, seed=1)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    g = {k: torch.from_numpy(v).to(dev) for k, v in host.items()}
+    y_scan = torch.empty(n, dtype=torch.float32, device=dev) if "scan" in only else None
+    out_sc = torch.zeros(B, dtype=torch.float32, device=dev) if "scatter" in only else None
+    s_out = torch.empty((), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(det.det_sum_workspace_size(n, 0), det.det_scan_workspace_size(n, 0, 0, 0),
+                         det.det_scatter_add_workspace_size(n, B, 1, 0)),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    ops = []
+    if "sum" in only:
+        ops.append(("sum", lambda: det.det_sum(g["x_sum"], out=s_out, ws=ws), 4.0 * n))
+    if "scan" in only:
+        ops.append(("scan", lambda: det.det_scan(g["x_scan"], y=y_scan, ws=ws), 8.0 * n))
+    if "scatter" in only:
+        ops.append(("scatter", lambda: det.det_scatter_add(g["v_sc"], g["b_sc"], out_sc, ws=ws),
+                    8.0 * n + 8.0 * B))
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        for _, fn, _ in ops:
+            fn()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # ---------------------------------------------------------------- timed steps
+    ev = {name: [] for name, _, _ in ops}
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        for name, fn, _ in ops:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev[name].append((a, b))
+    stop.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(stop) / args.steps
+    op_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name in ev}
+    log(f"timed {args.steps} steps: {step_ms:.3f} ms/step")
+
+    step_bytes = sum(bts for _, _, bts in ops)
+    value = step_bytes / (step_ms * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- non-deterministic baselines
+    base_ms = {}
+    if not args.no_baselines:
+        bl = ctypes.CDLL(os.path.join(ROOT, "scan_fixed_order_amd", "libdet_baselines.so"))
+        sp = ctypes.c_void_p(stream.cuda_stream)
+        vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        tmp = torch.empty((), dtype=torch.float32, device=dev)
+        out_b = torch.zeros(B, dtype=torch.float32, device=dev)
+        bl.detbase_dlb_scan_workspace_size.restype = ctypes.c_size_t
+        wsb = torch.empty(bl.detbase_dlb_scan_workspace_size(ctypes.c_int64(n)), dtype=torch.uint8,
+                          device=dev)
+        calls = {
+            "sum": lambda: bl.detbase_atomic_sum(vp(g["x_sum"]), ctypes.c_int64(n), 0, vp(tmp), sp),
+            "scan": lambda: bl.detbase_dlb_scan(vp(g["x_scan"]), vp(y_scan), ctypes.c_int64(n),
+                                                vp(wsb), sp),
+            "scatter": lambda: bl.detbase_atomic_scatter(vp(g["v_sc"]), vp(g["b_sc"]),
+                                                         ctypes.c_int64(n), 0, vp(out_b),
+                                                         ctypes.c_int64(B), sp),
+        }
+        for name, _, _ in ops:
+            fn = calls[name]
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(args.steps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            base_ms[name] = a.elapsed_time(b) / args.steps
+        log("baselines timed")
+
+    # ---------------------------------------------------------------- per-op report
+    op_rep = {}
+    for name, _, bts in ops:
+        ms = op_ms[name]
+        gbs = bts / (ms * 1e-3) / 1e9
+        r = {"ms": round(ms, 4), "GB_s": round(gbs, 1), "Gelem_s": round(n / (ms * 1e-3) / 1e9, 2),
+             "frac_hbm": round(gbs / PEAK_GBS, 4), "algorithmic_bytes": int(bts)}
+        if name in base_ms:
+            r["nondet_baseline_ms"] = round(base_ms[name], 4)
+            r["det_overhead"] = round(ms / base_ms[name] - 1.0, 4)
+        op_rep[name] = r
+
+    # dominant kernel: the operation with the largest share of the step; for the scan and the
+    # sum the operation is one main kernel (plus a tiny clearing launch for the scan)
+    dom = max(op_ms, key=op_ms.get)
+    dom_kernel = {"sum": "k_sum_chunks<float>", "scan": "k_scan<float, false>",
+                  "scatter": "det_scatter_add (sort + reduce kernels)"}[dom]
+    dom_bytes = dict((nm, b) for nm, _, b in ops)[dom]
+    achieved = dom_bytes / (op_ms[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": None, "kernel": dom_kernel,
+                "algorithmic_bytes_per_launch": int(dom_bytes)}
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        m = 1 << 24
+        xs = host.get("x_sum", workloads.uniform01(m, seed=0))[:m].copy()
+        xc = host.get("x_scan", workloads.scan_values(m, np.float32, seed=2))[:m].copy()
+        vs = host.get("v_sc", workloads.normal(m, seed=1))[:m].copy()
+        bs = host.get("b_sc", workloads.bins_uniform(m, B, seed=1))[:m].copy()
+        t = time.perf_counter()
+        oracle.det_sum(xs)
+        oracle.scan(xc)
+        oracle.scatter_add(vs, bs, np.zeros(B, np.float32))
+        dt = time.perf_counter() - t
+        cpu_bytes = 4.0 * m + 8.0 * m + 8.0 * m + 8.0 * B
+        cpu = {"value": round(cpu_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"first 2^24 elements of each input (sum + scan + scatter into {B} bins), "
+                         f"{dt:.1f} s single-threaded"}
+        log(f"cpu oracle sample took {dt:.1f}s")
+
+    line = {
+        "metric": "GB/s & % HBM peak for bit-reproducible f32 sum/scatter-add/scan at 2^28, 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"f32 n=2^{args.log2n}: sum (U[0,1)), inclusive scan "
+                               f"(N(0,1)*10^U(-4,4), random signs), scatter-add "
+                               f"(N(0,1) into {B} uniform bins)",
+                   "n": n, "bins": B, "ops": sorted(only)},
+        "frac_hbm": round(value / PEAK_GBS, 4),
+        "roofline": roofline,
+        "ops": op_rep,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,152 @@
+/*
+ * det.h -- reproducible floating-point add-reductions on AMD Instinct MI355X (gfx950).
+ *
+ * Three operations whose result bits depend only on (op, flags, dtype, input): never on the
+ * grid, occupancy, CU count, stream, run or device.  Every addition is one IEEE-754
+ * round-to-nearest-even addition in the input dtype (no contraction, subnormals kept); the
+ * association order is fixed by the problem size alone:
+ *
+ *  PW(v)   adjacent-pair tree: pad v with -0.0 to a power of two, then replace the list by
+ *          v0+v1, v2+v3, ... until one value remains (course page "Floating point and
+ *          reproducibility", section "Fix the order of every addition": a fixed bracket over
+ *          pairs instead of an atomic tail).
+ *
+ * Conventions for every entry point:
+ *  - Data pointers are DEVICE pointers owned by the caller.  Any element-aligned address is
+ *    accepted (tensor views); alignment never changes the bits.
+ *  - The library never allocates and never synchronises.  Scratch memory is a caller-provided
+ *    device workspace of at least *_workspace_size(...) bytes, 256-byte aligned; its contents
+ *    on entry do not matter and are undefined on return.  Calls that overlap in time must not
+ *    share a workspace.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *    returns without waiting for it.
+ *  - Host-checkable problems return a status and enqueue nothing.  Data-dependent conditions
+ *    never fail: out-of-range scatter indices are skipped and counted.
+ *  - Sizes: 0 <= n <= DET_MAX_N (2^31 - 1), as scatter record slots are signed 32-bit
+ *    (Warp "Deterministic Execution", section "Limitations", large launches).
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef DET_H
+#define DET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DET_F32 = 0, DET_F64 = 1 } det_dtype;
+
+typedef enum {
+    DET_SUCCESS = 0,
+    DET_ERROR_INVALID_VALUE = 1, /* bad argument (negative size, NULL pointer, bad flags...) */
+    DET_ERROR_UNSUPPORTED = 2,   /* unknown dtype */
+    DET_ERROR_TOO_LARGE = 3,     /* n or a derived size beyond DET_MAX_N */
+    DET_ERROR_WORKSPACE = 4,     /* ws NULL or smaller than the matching *_workspace_size */
+    DET_ERROR_LAUNCH = 5         /* the HIP runtime refused a launch */
+} det_status;
+
+#define DET_MAX_N 2147483647LL
+
+/* det_scan flags (inclusive and forward when 0) */
+#define DET_SCAN_EXCLUSIVE 1u
+#define DET_SCAN_REVERSE 2u
+
+/* ------------------------------------------------------------------ sum */
+
+/* Bytes of workspace det_sum needs for n elements (0 when the arguments are invalid). */
+size_t det_sum_workspace_size(int64_t n, det_dtype dtype);
+
+/* *out = PW(x[0..n)) for n >= 1, +0.0 for n == 0.
+ * x:   device, n elements of dtype (read only).
+ * out: device, one element of dtype (written).
+ * The fixed tree replaces the atomic tail of a block-partials reduction (course page
+ * "Floating point and reproducibility", sections "Twenty answers, none of them wrong" and
+ * "Fix the order of every addition").  Any aligned power-of-two chunk of x is a subtree of
+ * PW, so the kernels may split x into chunks of any power-of-two size without moving a bit. */
+det_status det_sum(const void* x, int64_t n, det_dtype dtype, void* out, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ scan */
+
+/* Bytes of workspace det_scan needs. */
+size_t det_scan_workspace_size(int64_t n, det_dtype dtype, unsigned flags, int64_t num_segments);
+
+/* Prefix sum with look-back through fixed anchor intervals (drjit-core pull request "Make
+ * CUDA floating-point prefix sums deterministic", sections "Root cause" and
+ * "Implementation"; inclusive/exclusive, forward/reverse, full/segmented per "Validation").
+ *
+ * Order (constants from det_spec_constants: V = 32 elements per lane, W = 64 lanes per wave,
+ * 4 waves per tile, T = 8192 elements per tile, A = 256 tiles per anchor interval):
+ *   lane-serial prefix s over each lane's run of V elements; Kogge-Stone over the lane totals
+ *   inside each wave (p = lane-exclusive prefix); Kogge-Stone over the 4 wave totals
+ *   (P = wave-exclusive prefix; the last value is the tile total Agg_j); for tile j in anchor
+ *   interval q: W_j = PW(Agg_{qA..j-1}), carry C_{q+1} = C_q + PW(Agg of all tiles of q),
+ *   C_0 = -0.0; y = (((C_q + W_j) + P) + p) + s.  Only carries cross interval boundaries, so
+ *   the bits do not depend on which predecessors a tile saw as finished.
+ *
+ * x, y:   device, n elements of dtype.  Inclusive scans may run in place (y == x); exclusive
+ *         scans must not overlap x and y (DET_ERROR_INVALID_VALUE if the ranges overlap).
+ * flags:  DET_SCAN_EXCLUSIVE (y[0] = +0.0, y[i] = inclusive[i-1]) and/or DET_SCAN_REVERSE
+ *         (scan of the flipped array, flipped back).
+ * seg_offsets: NULL for one segment, else device int64 [num_segments + 1] with
+ *         0 = o_0 <= o_1 <= ... <= o_S = n (precondition, not checked on the device).  Each
+ *         segment restarts the scan: the head-flag operator (f1|f2, f2 ? b : a + b) runs
+ *         through the same order; exclusive scans write +0.0 at every segment head (for
+ *         reverse: at every segment's last element).  num_segments >= 1 when n > 0. */
+det_status det_scan(const void* x, void* y, int64_t n, det_dtype dtype, unsigned flags,
+                    const int64_t* seg_offsets, int64_t num_segments, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* ------------------------------------------------------------------ scatter-add */
+
+/* Bytes of workspace det_scatter_add needs. */
+size_t det_scatter_add_workspace_size(int64_t n, int64_t num_out, int64_t row_len,
+                                      det_dtype dtype);
+
+/* Keyed scatter-add along axis 0, the reproducible form of atomic_add(out, index[i],
+ * values[i]) (Warp "Deterministic Execution", sections "Pattern 1: Accumulation" and
+ * "Writing Manual Deterministic Code") and, for row_len > 1, of the row-indexed tile
+ * accumulate (Warp reference "warp.tile_atomic_add_indexed").
+ *
+ * For destination r and column c: M = [values[i*row_len + c] for ascending i with
+ * index[i] == r]; if M is non-empty, out[r*row_len + c] = out[r*row_len + c] + PW(M), else
+ * out is left untouched.
+ *
+ * values:  device, [n * row_len] of dtype, row-major (read only; must not alias out).
+ * index:   device int32 [n].  Entries outside [0, num_out) are skipped, never an error.
+ * out:     device, [num_out * row_len] of dtype, updated in place.
+ * prev:    NULL, or device [n * row_len]: for every valid i, the destination row as it was
+ *          before this call (rows of skipped i are not written).
+ * n_skipped: NULL, or device int64: set (not accumulated) to the number of skipped i.
+ * row_len: >= 1. */
+det_status det_scatter_add(const void* values, const int32_t* index, int64_t n, int64_t row_len,
+                           det_dtype dtype, void* out, int64_t num_out, void* prev,
+                           int64_t* n_skipped, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------ introspection */
+
+/* Version of the association order; results of one version never change. */
+int det_spec_version(void);
+
+/* Scan constants of this version: elements per lane, lanes per tile, tiles per anchor
+ * interval (any pointer may be NULL). */
+void det_spec_constants(int64_t* V, int64_t* L, int64_t* A);
+
+/* Static string naming a status code. */
+const char* det_status_string(det_status s);
+
+/* ------------------------------------------------------------------ test hooks */
+
+/* Not part of the stable interface.  Overrides how the work is spread over the GPU, for the
+ * tests that show the bits do not depend on it: grid_wgs > 0 caps the number of workgroups
+ * of the sum and scan kernels (0 = default); sum_chunk_log2 in [10, 24] sets the elements per
+ * sum partial (0 = default).  Process-wide; returns DET_ERROR_INVALID_VALUE when out of range. */
+det_status det_debug_set_launch(int grid_wgs, int sum_chunk_log2);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DET_H */

@@ -1,0 +1,130 @@
+// api.hip -- the library's C interface: argument checks, workspace sizing, dispatch.
+//
+// Every check that needs no device data happens here, before anything is enqueued; the
+// kernels never see an argument this file rejected.
+#include <string.h>
+
+#include "det_internal.h"
+
+namespace det {
+
+static LaunchOverride g_override = {0, 0};
+
+const LaunchOverride& launch_override() { return g_override; }
+
+static bool valid_dtype(det_dtype d) { return d == DET_F32 || d == DET_F64; }
+
+static bool ranges_overlap(const void* a, const void* b, size_t bytes) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a);
+    const uintptr_t y = reinterpret_cast<uintptr_t>(b);
+    return x < y + bytes && y < x + bytes;
+}
+
+}  // namespace det
+
+using namespace det;
+
+extern "C" {
+
+size_t det_sum_workspace_size(int64_t n, det_dtype dtype) {
+    if (n < 0 || n > DET_MAX_N || !valid_dtype(dtype)) return 0;
+    return sum_workspace(n, dtype);
+}
+
+det_status det_sum(const void* x, int64_t n, det_dtype dtype, void* out, void* ws,
+                   size_t ws_bytes, void* stream) {
+    if (!valid_dtype(dtype)) return DET_ERROR_UNSUPPORTED;
+    if (n < 0) return DET_ERROR_INVALID_VALUE;
+    if (n > DET_MAX_N) return DET_ERROR_TOO_LARGE;
+    if (!out || (n > 0 && !x)) return DET_ERROR_INVALID_VALUE;
+    if (!ws || ws_bytes < sum_workspace(n, dtype)) return DET_ERROR_WORKSPACE;
+    return sum_launch(x, n, dtype, out, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t det_scan_workspace_size(int64_t n, det_dtype dtype, unsigned flags, int64_t num_segments) {
+    if (n < 0 || n > DET_MAX_N || !valid_dtype(dtype) || num_segments < 0) return 0;
+    if (flags & ~(DET_SCAN_EXCLUSIVE | DET_SCAN_REVERSE)) return 0;
+    return scan_workspace(n, dtype, flags, num_segments);
+}
+
+det_status det_scan(const void* x, void* y, int64_t n, det_dtype dtype, unsigned flags,
+                    const int64_t* seg_offsets, int64_t num_segments, void* ws, size_t ws_bytes,
+                    void* stream) {
+    if (!valid_dtype(dtype)) return DET_ERROR_UNSUPPORTED;
+    if (n < 0 || num_segments < 0) return DET_ERROR_INVALID_VALUE;
+    if (n > DET_MAX_N || num_segments > DET_MAX_N) return DET_ERROR_TOO_LARGE;
+    if (flags & ~(DET_SCAN_EXCLUSIVE | DET_SCAN_REVERSE)) return DET_ERROR_INVALID_VALUE;
+    if (n > 0 && (!x || !y)) return DET_ERROR_INVALID_VALUE;
+    if (seg_offsets && n > 0 && num_segments < 1) return DET_ERROR_INVALID_VALUE;
+    const size_t bytes = (size_t)n * dtype_size(dtype);
+    if ((flags & DET_SCAN_EXCLUSIVE) && n > 0 && ranges_overlap(x, y, bytes))
+        return DET_ERROR_INVALID_VALUE;
+    if (n > 0 && x != y && ranges_overlap(x, y, bytes)) return DET_ERROR_INVALID_VALUE;
+    if (!ws || ws_bytes < scan_workspace(n, dtype, flags, num_segments))
+        return DET_ERROR_WORKSPACE;
+    return scan_launch(x, y, n, dtype, flags, seg_offsets, num_segments, ws, ws_bytes,
+                       static_cast<hipStream_t>(stream));
+}
+
+size_t det_scatter_add_workspace_size(int64_t n, int64_t num_out, int64_t row_len,
+                                      det_dtype dtype) {
+    if (n < 0 || n > DET_MAX_N || num_out < 0 || num_out > DET_MAX_N || row_len < 1 ||
+        !valid_dtype(dtype))
+        return 0;
+    return scatter_workspace(n, num_out, row_len, dtype);
+}
+
+det_status det_scatter_add(const void* values, const int32_t* index, int64_t n, int64_t row_len,
+                           det_dtype dtype, void* out, int64_t num_out, void* prev,
+                           int64_t* n_skipped, void* ws, size_t ws_bytes, void* stream) {
+    if (!valid_dtype(dtype)) return DET_ERROR_UNSUPPORTED;
+    if (n < 0 || num_out < 0 || row_len < 1) return DET_ERROR_INVALID_VALUE;
+    if (n > DET_MAX_N || num_out > DET_MAX_N) return DET_ERROR_TOO_LARGE;
+    if ((double)n * (double)row_len > 9.0e18 || (double)num_out * (double)row_len > 9.0e18)
+        return DET_ERROR_TOO_LARGE;
+    if (n > 0 && (!values || !index)) return DET_ERROR_INVALID_VALUE;
+    if (num_out > 0 && !out) return DET_ERROR_INVALID_VALUE;
+    const size_t es = dtype_size(dtype);
+    if (n > 0 && num_out > 0) {
+        const uintptr_t v0 = reinterpret_cast<uintptr_t>(values);
+        const uintptr_t v1 = v0 + (size_t)n * row_len * es;
+        const uintptr_t o0 = reinterpret_cast<uintptr_t>(out);
+        const uintptr_t o1 = o0 + (size_t)num_out * row_len * es;
+        if (v0 < o1 && o0 < v1) return DET_ERROR_INVALID_VALUE;
+    }
+    if (!ws || ws_bytes < scatter_workspace(n, num_out, row_len, dtype))
+        return DET_ERROR_WORKSPACE;
+    return scatter_launch(values, index, n, row_len, dtype, out, num_out, prev, n_skipped, ws,
+                          ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int det_spec_version(void) { return 1; }
+
+void det_spec_constants(int64_t* V, int64_t* L, int64_t* A) {
+    if (V) *V = kScanV;
+    if (L) *L = kScanL;
+    if (A) *A = kScanA;
+}
+
+const char* det_status_string(det_status s) {
+    switch (s) {
+        case DET_SUCCESS: return "DET_SUCCESS";
+        case DET_ERROR_INVALID_VALUE: return "DET_ERROR_INVALID_VALUE";
+        case DET_ERROR_UNSUPPORTED: return "DET_ERROR_UNSUPPORTED";
+        case DET_ERROR_TOO_LARGE: return "DET_ERROR_TOO_LARGE";
+        case DET_ERROR_WORKSPACE: return "DET_ERROR_WORKSPACE";
+        case DET_ERROR_LAUNCH: return "DET_ERROR_LAUNCH";
+    }
+    return "DET_UNKNOWN_STATUS";
+}
+
+det_status det_debug_set_launch(int grid_wgs, int sum_chunk_log2) {
+    if (grid_wgs < 0) return DET_ERROR_INVALID_VALUE;
+    if (sum_chunk_log2 != 0 && (sum_chunk_log2 < 14 || sum_chunk_log2 > 24))
+        return DET_ERROR_INVALID_VALUE;
+    g_override.grid_wgs = grid_wgs;
+    g_override.sum_chunk_log2 = sum_chunk_log2;
+    return DET_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// det_internal.h -- host-side declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "det.h"
+
+namespace det {
+
+// Launch overrides for the shape-invariance tests (0 = default).
+struct LaunchOverride {
+    int grid_wgs;
+    int sum_chunk_log2;
+};
+const LaunchOverride& launch_override();
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline size_t dtype_size(det_dtype d) { return d == DET_F64 ? 8 : 4; }
+
+// ---- sum
+size_t sum_workspace(int64_t n, det_dtype dt);
+det_status sum_launch(const void* x, int64_t n, det_dtype dt, void* out, void* ws, size_t ws_bytes,
+                      hipStream_t s);
+
+// ---- scan
+constexpr int kScanV = 32;       // elements per lane
+constexpr int kScanW = 64;       // lanes per wave
+constexpr int kScanWaves = 4;    // waves per tile
+constexpr int kScanL = kScanW * kScanWaves;   // lanes per tile
+constexpr int kScanT = kScanV * kScanL;       // elements per tile
+constexpr int kScanA = 256;      // tiles per anchor interval
+
+size_t scan_workspace(int64_t n, det_dtype dt, unsigned flags, int64_t num_segments);
+det_status scan_launch(const void* x, void* y, int64_t n, det_dtype dt, unsigned flags,
+                       const int64_t* offs, int64_t nseg, void* ws, size_t ws_bytes,
+                       hipStream_t s);
+
+// ---- scatter-add
+size_t scatter_workspace(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt);
+det_status scatter_launch(const void* values, const int32_t* index, int64_t n, int64_t row_len,
+                          det_dtype dt, void* out, int64_t num_out, void* prev, int64_t* n_skipped,
+                          void* ws, size_t ws_bytes, hipStream_t s);
+
+inline det_status launch_status() {
+    return hipGetLastError() == hipSuccess ? DET_SUCCESS : DET_ERROR_LAUNCH;
+}
+
+}  // namespace det

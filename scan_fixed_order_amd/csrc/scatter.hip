@@ -1,0 +1,807 @@
+// scatter.hip -- det_scatter_add: keyed scatter-add with a fixed per-destination order.
+//
+// Order (Warp "Deterministic Execution", sections "Pattern 1: Accumulation", "Writing Manual
+// Deterministic Code" and "Picking the Right Mode"; rows per "warp.tile_atomic_add_indexed"):
+// the contributions to destination r are taken in ascending source index and combined by the
+// adjacent-pair tree PW over their local rank 0, 1, 2, ...; the destination's old value is
+// added last: out[r] = out[r] + PW(M_r).  Empty destinations are untouched; out-of-range
+// indices are skipped and counted.
+//
+// Pipeline on gfx950 (every step integer-exact or a fixed tree, so no atomics touch a value):
+//   prev   optional snapshot prev[i] = out[index[i]] before anything changes;
+//   sort   stable LSD radix sort of (key, payload) with 8-bit digits; the first pass also
+//          splits off out-of-range keys into a 257th bucket at the end, and later passes only
+//          see the valid prefix.  Payload = the value (row_len 1) or the source row (rows).
+//          Per pass: per-chunk digit histogram, integer exclusive scan, then each workgroup
+//          ranks its chunk stably (wave ballots + per-wave digit counters), stages it in LDS
+//          in digit order and writes contiguous runs;
+//   bins   off[b] = first sorted position with key >= b (binary search per bin);
+//   reduce a destination's members are cut at local ranks that are multiples of D (D = 8192
+//          values, or 64 rows).  Each block is a subtree of PW; one pass reduces every block
+//          (a lane per block of at most 32 values, a wave per larger block) and applies
+//          destinations with one block; a second pass combines the block values of longer
+//          destinations by the same tree and applies them.
+#include "det_device.h"
+#include "det_internal.h"
+
+namespace det {
+namespace {
+
+constexpr int kSegD = 8192;     // scalar: ranks per block
+constexpr int kRowD = 64;       // rows: member rows per block
+constexpr int kBuckets0 = 257;  // first pass: 256 digits + the out-of-range bucket
+
+__host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- integer block helpers
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* s4) {
+    v = wave_sum_u32(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) s4[wave] = v;
+    __syncthreads();
+    const uint32_t t = s4[0] + s4[1] + s4[2] + s4[3];
+    __syncthreads();
+    return t;
+}
+
+// exclusive prefix over the 256 threads (integers: exact in any order); *total = sum
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s4, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t inc = v;
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = shfl_up(inc, d, lane);
+        if (lane >= d) inc += o;
+    }
+    if (lane == 63) s4[wave] = inc;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += s4[w];
+    *total = s4[0] + s4[1] + s4[2] + s4[3];
+    __syncthreads();
+    return before + inc - v;
+}
+
+// ---------------------------------------------------------------- u32 exclusive scan
+
+constexpr int kU32Blk = 4096;
+
+__global__ __launch_bounds__(256) void k_u32_block_sums(const uint32_t* __restrict__ a, int64_t N,
+                                                        uint32_t* __restrict__ sums) {
+    __shared__ uint32_t s4[4];
+    const int64_t base = (int64_t)blockIdx.x * kU32Blk;
+    uint32_t s = 0;
+    for (int i = 0; i < kU32Blk / 256; ++i) {
+        const int64_t k = base + i * 256 + threadIdx.x;
+        if (k < N) s += a[k];
+    }
+    s = block_sum_u32(s, s4);
+    if (threadIdx.x == 0) sums[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void k_u32_scan_sums(uint32_t* __restrict__ sums, int64_t nb) {
+    __shared__ uint32_t s4[4];
+    uint32_t carry = 0;
+    for (int64_t base = 0; base < nb; base += 256) {
+        const int64_t k = base + threadIdx.x;
+        const uint32_t v = k < nb ? sums[k] : 0u;
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan_u32(v, s4, &tot);
+        if (k < nb) sums[k] = carry + ex;
+        carry += tot;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_u32_block_apply(uint32_t* __restrict__ a, int64_t N,
+                                                         const uint32_t* __restrict__ sums) {
+    __shared__ uint32_t s4[4];
+    constexpr int IPT = kU32Blk / 256;
+    const int64_t base = (int64_t)blockIdx.x * kU32Blk + (int64_t)threadIdx.x * IPT;
+    uint32_t v[IPT];
+    uint32_t tsum = 0;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        v[i] = (base + i < N) ? a[base + i] : 0u;
+        tsum += v[i];
+    }
+    uint32_t tot;
+    uint32_t run = block_excl_scan_u32(tsum, s4, &tot) + sums[blockIdx.x];
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+        if (base + i < N) a[base + i] = run;
+        run += v[i];
+    }
+}
+
+det_status u32_exclusive_scan(uint32_t* a, int64_t N, uint32_t* sums, hipStream_t s) {
+    const int64_t nb = cdiv(N, kU32Blk);
+    k_u32_block_sums<<<dim3((unsigned)nb), dim3(256), 0, s>>>(a, N, sums);
+    k_u32_scan_sums<<<1, 256, 0, s>>>(sums, nb);
+    k_u32_block_apply<<<dim3((unsigned)nb), dim3(256), 0, s>>>(a, N, sums);
+    return launch_status();
+}
+
+// ---------------------------------------------------------------- radix sort passes
+
+// digit of a key; in the first pass keys outside [0, B) (as unsigned: also negatives) go to 256
+template <bool FIRST>
+__device__ __forceinline__ int digit_of(uint32_t key, uint32_t B, int shift) {
+    if (FIRST && key >= B) return 256;
+    return (int)((key >> shift) & 255u);
+}
+
+template <bool FIRST>
+__global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n,
+                                                    const uint32_t* __restrict__ nvalid, uint32_t B,
+                                                    int shift, int nb, int64_t nchunks, int H,
+                                                    uint32_t* __restrict__ hist) {
+    __shared__ uint32_t cnt[kBuckets0];
+    for (int i = threadIdx.x; i < kBuckets0; i += 256) cnt[i] = 0u;
+    __syncthreads();
+    const int64_t m = FIRST ? n : (int64_t)*nvalid;
+    const int64_t base = (int64_t)blockIdx.x * H;
+    for (int i = threadIdx.x; i < H; i += 256) {
+        const int64_t p = base + i;
+        if (p < m) atomicAdd(&cnt[digit_of<FIRST>(keys[p], B, shift)], 1u);
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < nb; d += 256) hist[(int64_t)d * nchunks + blockIdx.x] = cnt[d];
+}
+
+// P: payload word (uint32_t: f32 value bits or source row; uint64_t: f64 value bits)
+template <typename P, bool FIRST, bool ROWS>
+__global__ __launch_bounds__(256) void k_radix_scatter(
+    const uint32_t* __restrict__ keys_in, const P* __restrict__ pay_in,
+    uint32_t* __restrict__ keys_out, P* __restrict__ pay_out, int64_t n,
+    const uint32_t* __restrict__ nvalid, uint32_t B, int shift, int64_t nchunks,
+    const uint32_t* __restrict__ hist_ex) {
+    constexpr int IPT = sizeof(P) == 4 ? 32 : 16;   // items per thread
+    constexpr int H = 256 * IPT;                     // elements per chunk
+    constexpr int WE = 64 * IPT;                     // elements per wave
+    constexpr int NB = FIRST ? kBuckets0 : 256;
+    constexpr int BITS = FIRST ? 9 : 8;
+    __shared__ uint32_t s_keys[H];
+    __shared__ P s_pay[H];
+    __shared__ uint32_t s_cnt[4][kBuckets0];   // per-wave digit counters, then wave offsets
+    __shared__ uint32_t s_dstart[kBuckets0];
+    __shared__ int64_t s_gbase[kBuckets0];
+    __shared__ uint32_t s4[4];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t c = blockIdx.x;
+    const int64_t m = FIRST ? n : (int64_t)*nvalid;
+    const int64_t base = c * H;
+    if (base >= m) return;
+
+    for (int i = tid; i < 4 * kBuckets0; i += 256) (&s_cnt[0][0])[i] = 0u;
+    __syncthreads();
+
+    uint32_t key[IPT];
+    P pay[IPT];
+    uint32_t rk[IPT];
+    int dg[IPT];
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+        const int64_t p = base + (int64_t)wave * WE + k * 64 + lane;
+        const bool valid = p < m;
+        key[k] = valid ? keys_in[p] : 0u;
+        if constexpr (ROWS && FIRST) {
+            pay[k] = (P)(valid ? p : 0);
+        } else {
+            pay[k] = valid ? pay_in[p] : (P)0;
+        }
+        const int d = valid ? digit_of<FIRST>(key[k], B, shift) : 0;
+        dg[k] = d;
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) {
+            const bool bit = (d >> b) & 1;
+            const uint64_t mb = __ballot(bit);
+            peers &= bit ? mb : ~mb;
+        }
+        const uint32_t rank = (uint32_t)__popcll(peers & below);
+        uint32_t seen = 0;
+        if (valid) seen = s_cnt[wave][d];
+        rk[k] = seen + rank;
+        if (valid && (peers & below) == 0ull) s_cnt[wave][d] = seen + (uint32_t)__popcll(peers);
+    }
+    __syncthreads();
+    // per digit: wave offsets (exclusive over waves) and totals
+    uint32_t tot_lo = 0, tot_hi = 0;
+    {
+        const int d = tid;
+        uint32_t run = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t cw = s_cnt[w][d];
+            s_cnt[w][d] = run;
+            run += cw;
+        }
+        tot_lo = run;
+        if (NB > 256 && tid == 0) {
+            uint32_t r2 = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t cw = s_cnt[w][256];
+                s_cnt[w][256] = r2;
+                r2 += cw;
+            }
+            tot_hi = r2;
+        }
+    }
+    uint32_t total;
+    const uint32_t ds = block_excl_scan_u32(tot_lo, s4, &total);
+    s_dstart[tid] = ds;
+    s_gbase[tid] = (int64_t)hist_ex[(int64_t)tid * nchunks + c] - (int64_t)ds;
+    if (NB > 256 && tid == 0) {
+        s_dstart[256] = total;
+        s_gbase[256] = (int64_t)hist_ex[(int64_t)256 * nchunks + c] - (int64_t)total;
+    }
+    (void)tot_hi;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+        const int64_t p = base + (int64_t)wave * WE + k * 64 + lane;
+        if (p < m) {
+            const int d = dg[k];
+            const uint32_t lp = s_dstart[d] + s_cnt[wave][d] + rk[k];
+            s_keys[lp] = key[k];
+            s_pay[lp] = pay[k];
+        }
+    }
+    __syncthreads();
+    const int cntc = (int)((m - base) < H ? (m - base) : H);
+    for (int i = tid; i < cntc; i += 256) {
+        const uint32_t kk = s_keys[i];
+        const int64_t g = s_gbase[digit_of<FIRST>(kk, B, shift)] + i;
+        keys_out[g] = kk;
+        pay_out[g] = s_pay[i];
+    }
+}
+
+__global__ void k_copy_word(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst) {
+    dst[0] = src[0];
+}
+
+// ---------------------------------------------------------------- destinations
+
+// off[b] = first sorted position with key >= b, for b in [0, B]; n_skipped = n - valid
+__global__ __launch_bounds__(256) void k_bin_offsets(const uint32_t* __restrict__ K,
+                                                     const uint32_t* __restrict__ nvalid,
+                                                     int64_t B, int64_t n, uint32_t* __restrict__ off,
+                                                     int64_t* __restrict__ n_skipped) {
+    const int64_t m = *nvalid;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b <= B;
+         b += (int64_t)gridDim.x * blockDim.x) {
+        int64_t lo = 0, hi = m;
+        while (lo < hi) {
+            const int64_t mid = (lo + hi) >> 1;
+            if ((int64_t)K[mid] < b) lo = mid + 1;
+            else hi = mid;
+        }
+        off[b] = (uint32_t)lo;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && n_skipped) *n_skipped = n - m;
+}
+
+template <typename T>
+__global__ void k_prev_gather(const int32_t* __restrict__ index, int64_t n, int64_t d, int64_t B,
+                              const T* __restrict__ out, T* __restrict__ prev) {
+    const int64_t total = n * d;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = e / d;
+        const int64_t c = e - i * d;
+        const int64_t b = index[i];
+        if (b >= 0 && b < B) prev[e] = out[b * d + c];
+    }
+}
+
+template <typename T>
+__global__ void k_write_skipped_all(int64_t* n_skipped, int64_t n) {
+    *n_skipped = n;
+}
+
+// ---------------------------------------------------------------- scalar reduction
+
+// PW over p[0 .. len), len <= 8192 (element 0 replaced by v0 when use_v0): 32 blocks of
+// 256; lane l of block i holds elements 256 i + 4 l .. + 4 combined as (a0 + a1) + (a2 + a3),
+// then the wave butterfly.  Blocks combine by a 3-level tree inside each group of 8 and a
+// 2-level tree over the 4 groups (together the 5-level tree over the 32 blocks; identity for
+// blocks past len).  Uniform result.
+template <typename T>
+__device__ __forceinline__ T wave_pw_range(const T* __restrict__ p, int64_t len, int lane,
+                                           bool use_v0, T v0) {
+    T g[4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+        g[gi] = ident<T>();
+        if ((int64_t)gi * 2048 < len) {
+            T b[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int blk = (gi * 8 + i) * 256;
+                b[i] = ident<T>();
+                if (blk < len) {
+                    const T* q = p + blk + 4 * lane;
+                    T a0, a1, a2, a3;
+                    if (blk + 256 <= len) {
+                        a0 = q[0]; a1 = q[1]; a2 = q[2]; a3 = q[3];
+                    } else {
+                        const int rem = (int)(len - blk) - 4 * lane;
+                        a0 = rem > 0 ? q[0] : ident<T>();
+                        a1 = rem > 1 ? q[1] : ident<T>();
+                        a2 = rem > 2 ? q[2] : ident<T>();
+                        a3 = rem > 3 ? q[3] : ident<T>();
+                    }
+                    if (use_v0 && blk == 0 && lane == 0) a0 = v0;
+                    b[i] = wave_pw<T>((a0 + a1) + (a2 + a3));
+                }
+            }
+            g[gi] = ((b[0] + b[1]) + (b[2] + b[3])) + ((b[4] + b[5]) + (b[6] + b[7]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    return (g[0] + g[1]) + (g[2] + g[3]);
+}
+
+// PW over p[0 .. len) for any len (element 0 replaced by v0 when use_v0): blocks of 8192
+// by wave_pw_range, merged by a binary counter whose stack lives in LDS (lane 0), then
+// folded right-nested.
+template <typename T>
+__device__ __forceinline__ T wave_pw_long(const T* __restrict__ p, int64_t len, int lane, bool use_v0,
+                                       T v0, T* stk) {
+    const int64_t nblk = cdiv(len, 8192);
+    for (int64_t s = 0; s < nblk; ++s) {
+        const int64_t o = s * 8192;
+        const int64_t l = (len - o) < 8192 ? (len - o) : 8192;
+        T v = wave_pw_range<T>(p + o, l, lane, use_v0 && s == 0, v0);
+        if (lane == 0) {
+            int64_t k = s;
+            int lvl = 0;
+            while (k & 1) {
+                v = stk[lvl] + v;
+                k >>= 1;
+                ++lvl;
+            }
+            stk[lvl] = v;
+        }
+    }
+    T acc = ident<T>();
+    if (lane == 0) {
+        bool have = false;
+        for (int lvl = 0; lvl < 40; ++lvl) {
+            if ((nblk >> lvl) & 1) {
+                acc = have ? stk[lvl] + acc : stk[lvl];
+                have = true;
+            }
+        }
+    }
+    return readlane(acc, 0);
+}
+
+// PW over v[0 .. len), len <= 32, by one lane: pad to 32 with the identity, 5-level tree
+template <typename T>
+__device__ __forceinline__ T lane_pw_32(const T* __restrict__ v, int len) {
+    T a[32];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) a[q] = ident<T>();
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+        if (q < len) a[q] = v[q];
+    }
+#pragma unroll
+    for (int w = 32; w > 1; w /= 2) {
+#pragma unroll
+        for (int i = 0; i < w / 2; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+    }
+    return a[0];
+}
+
+// Store the value of the block starting at sorted position ps (local rank k*D of bin b).
+template <typename T>
+__device__ __forceinline__ void emit_scalar(T S, int64_t ps, uint32_t b, int64_t seg_s,
+                                            int64_t seg_e, T* __restrict__ out,
+                                            T* __restrict__ pF, T* __restrict__ pC) {
+    if (seg_e - seg_s <= kSegD) {
+        out[b] = out[b] + S;
+    } else if (ps == seg_s) {
+        pF[ps / kSegD] = S;
+    } else {
+        pC[ps / kSegD] = S;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_segred_scalar(const uint32_t* __restrict__ K,
+                                                       const T* __restrict__ V,
+                                                       const uint32_t* __restrict__ off,
+                                                       const uint32_t* __restrict__ nvalid,
+                                                       T* __restrict__ out, T* __restrict__ pF,
+                                                       T* __restrict__ pC) {
+    __shared__ uint32_t s_big[kSegD / 32 + 2];
+    __shared__ uint32_t s_nbig;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t m = *nvalid;
+    const int64_t lo = (int64_t)blockIdx.x * kSegD;
+    if (lo >= m) return;
+    const int64_t hi = (lo + kSegD < m) ? lo + kSegD : m;
+    if (tid == 0) s_nbig = 0u;
+    __syncthreads();
+
+    // a block starts at every segment start, and at most once more inside this range: the
+    // next multiple of D (in local rank) of the destination running into the range
+    auto item = [&](int64_t ps, uint32_t b) {
+        const int64_t seg_s = off[b], seg_e = off[b + 1];
+        const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
+        if (len <= 32) {
+            const T S = lane_pw_32<T>(V + ps, (int)len);
+            emit_scalar<T>(S, ps, b, seg_s, seg_e, out, pF, pC);
+        } else {
+            s_big[atomicAdd(&s_nbig, 1u)] = (uint32_t)(ps - lo);
+        }
+    };
+    for (int i = 0; i < kSegD / 256; ++i) {
+        const int64_t p = lo + i * 256 + tid;
+        if (p < hi) {
+            const uint32_t b = K[p];
+            if (p == 0 || K[p - 1] != b) item(p, b);
+            if (p == lo) {
+                const int64_t s0 = off[b];
+                if (s0 < lo) {
+                    const int64_t pc = s0 + cdiv(lo - s0, kSegD) * kSegD;
+                    const int64_t e0 = off[b + 1];
+                    if (pc < hi && pc < e0) item(pc, b);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int nbig = (int)s_nbig;
+    for (int it = wave; it < nbig; it += 4) {
+        const int64_t ps = lo + s_big[it];
+        const uint32_t b = K[ps];
+        const int64_t seg_s = off[b], seg_e = off[b + 1];
+        const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
+        const T S = wave_pw_range<T>(V + ps, len, lane, false, ident<T>());
+        if (lane == 0) emit_scalar<T>(S, ps, b, seg_s, seg_e, out, pF, pC);
+    }
+}
+
+// destinations with more than D members: PW over their block values, then apply
+template <typename T>
+__global__ __launch_bounds__(256) void k_segred_scalar_long(const uint32_t* __restrict__ off,
+                                                            int64_t B, const T* __restrict__ pF,
+                                                            const T* __restrict__ pC,
+                                                            T* __restrict__ out) {
+    __shared__ T s_stk[4][40];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    for (int64_t g = gw; g * 64 < B; g += nw) {
+        const int64_t b = g * 64 + lane;
+        const bool lng = b < B && (int64_t)off[b + 1] - (int64_t)off[b] > kSegD;
+        uint64_t mask = __ballot(lng);
+        while (mask) {
+            const int l = __ffsll((long long)mask) - 1;
+            mask &= mask - 1;
+            const int64_t bb = g * 64 + l;
+            const int64_t seg_s = off[bb], seg_e = off[bb + 1];
+            const int64_t nblk = cdiv(seg_e - seg_s, kSegD);
+            const int64_t r0 = seg_s / kSegD;
+            // block values: pF[r0] for the first block, pC[r0 + k] for block k >= 1
+            const T S = wave_pw_long<T>(pC + r0, nblk, lane, true, pF[r0], s_stk[wave]);
+            if (lane == 0) out[bb] = out[bb] + S;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- row reduction
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_segred_rows(const uint32_t* __restrict__ K,
+                                                     const uint32_t* __restrict__ R,
+                                                     const uint32_t* __restrict__ off,
+                                                     const uint32_t* __restrict__ nvalid,
+                                                     const T* __restrict__ src, int64_t d,
+                                                     T* __restrict__ out, T* __restrict__ pF,
+                                                     T* __restrict__ pC) {
+    constexpr int CPL = 4;   // columns per lane per pass
+    __shared__ uint32_t s_item[kRowD + 2];
+    __shared__ uint32_t s_nitem;
+    __shared__ uint32_t s_rows[4][kRowD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t m = *nvalid;
+    const int64_t lo = (int64_t)blockIdx.x * kRowD;
+    if (lo >= m) return;
+    const int64_t hi = (lo + kRowD < m) ? lo + kRowD : m;
+    if (tid == 0) s_nitem = 0u;
+    __syncthreads();
+    if (tid < kRowD) {
+        const int64_t p = lo + tid;
+        if (p < hi) {
+            const uint32_t b = K[p];
+            if (p == 0 || K[p - 1] != b) s_item[atomicAdd(&s_nitem, 1u)] = (uint32_t)p;
+            if (p == lo) {
+                const int64_t s0 = off[b];
+                if (s0 < lo) {
+                    const int64_t pc = s0 + cdiv(lo - s0, kRowD) * kRowD;
+                    if (pc < hi && pc < (int64_t)off[b + 1])
+                        s_item[atomicAdd(&s_nitem, 1u)] = (uint32_t)pc;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int nitem = (int)s_nitem;
+    for (int it = wave; it < nitem; it += 4) {
+        const int64_t ps = s_item[it];
+        const uint32_t b = K[ps];
+        const int64_t seg_s = off[b], seg_e = off[b + 1];
+        const int len = (int)((seg_e - ps) < kRowD ? (seg_e - ps) : kRowD);
+        if (lane < len) s_rows[wave][lane] = R[ps + lane];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        T* dst;
+        if (seg_e - seg_s <= kRowD) dst = out + (int64_t)b * d;
+        else if (ps == seg_s) dst = pF + (ps / kRowD) * d;
+        else dst = pC + (ps / kRowD) * d;
+        const bool single = seg_e - seg_s <= kRowD;
+        for (int64_t c0 = 0; c0 < d; c0 += 64 * CPL) {
+            // PW over the 64 rank positions of the block (identity past len): 8 groups of 8
+            // rows, each a 3-level tree, then a 3-level tree over the group values
+            T g8[8][CPL];
+#pragma unroll
+            for (int gi = 0; gi < 8; ++gi) {
+                if (gi * 8 >= len) {
+#pragma unroll
+                    for (int cc = 0; cc < CPL; ++cc) g8[gi][cc] = ident<T>();
+                    continue;
+                }
+                T v[8][CPL];
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const int q = gi * 8 + r;
+                    if (q < len) {
+                        const T* row = src + (int64_t)s_rows[wave][q] * d;
+#pragma unroll
+                        for (int cc = 0; cc < CPL; ++cc) {
+                            const int64_t col = c0 + cc * 64 + lane;
+                            v[r][cc] = col < d ? row[col] : ident<T>();
+                        }
+                    } else {
+#pragma unroll
+                        for (int cc = 0; cc < CPL; ++cc) v[r][cc] = ident<T>();
+                    }
+                }
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc)
+                    g8[gi][cc] = ((v[0][cc] + v[1][cc]) + (v[2][cc] + v[3][cc])) +
+                                 ((v[4][cc] + v[5][cc]) + (v[6][cc] + v[7][cc]));
+            }
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const T r = ((g8[0][cc] + g8[1][cc]) + (g8[2][cc] + g8[3][cc])) +
+                            ((g8[4][cc] + g8[5][cc]) + (g8[6][cc] + g8[7][cc]));
+                const int64_t col = c0 + cc * 64 + lane;
+                if (col < d) dst[col] = single ? dst[col] + r : r;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// rows of destinations with more than 64 members: PW over their block rows per column
+template <typename T>
+__global__ __launch_bounds__(256) void k_segred_rows_long(const uint32_t* __restrict__ off,
+                                                          int64_t B, int64_t d,
+                                                          const T* __restrict__ pF,
+                                                          const T* __restrict__ pC,
+                                                          T* __restrict__ out) {
+    __shared__ T s_stk[32][256];
+    __shared__ uint32_t s_list[256];
+    __shared__ uint32_t s_n;
+    const int tid = threadIdx.x;
+    for (int64_t g = blockIdx.x; g * 256 < B; g += gridDim.x) {
+        if (tid == 0) s_n = 0u;
+        __syncthreads();
+        const int64_t b = g * 256 + tid;
+        if (b < B && (int64_t)off[b + 1] - (int64_t)off[b] > kRowD)
+            s_list[atomicAdd(&s_n, 1u)] = (uint32_t)tid;
+        __syncthreads();
+        const int cnt = (int)s_n;
+        for (int i = 0; i < cnt; ++i) {
+            const int64_t bb = g * 256 + s_list[i];
+            const int64_t seg_s = off[bb], seg_e = off[bb + 1];
+            const int64_t nblk = cdiv(seg_e - seg_s, kRowD);
+            const int64_t r0 = seg_s / kRowD;
+            for (int64_t col = tid; col < d; col += 256) {
+                // binary counter over the block rows, stack in LDS (one column per thread)
+                for (int64_t s = 0; s < nblk; ++s) {
+                    T v = (s == 0) ? pF[r0 * d + col] : pC[(r0 + s) * d + col];
+                    int64_t k = s;
+                    int lvl = 0;
+                    while (k & 1) {
+                        v = s_stk[lvl][tid] + v;
+                        k >>= 1;
+                        ++lvl;
+                    }
+                    s_stk[lvl][tid] = v;
+                }
+                T acc = ident<T>();
+                bool have = false;
+                for (int lvl = 0; lvl < 32; ++lvl) {
+                    if ((nblk >> lvl) & 1) {
+                        acc = have ? s_stk[lvl][tid] + acc : s_stk[lvl][tid];
+                        have = true;
+                    }
+                }
+                out[bb * d + col] = out[bb * d + col] + acc;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- host side
+
+int key_passes(int64_t B) {
+    int bits = 0;
+    while (bits < 32 && (B - 1) >> bits) ++bits;   // bits of B - 1 (0 for B = 1)
+    const int p = (bits + 7) / 8;
+    return p < 1 ? 1 : p;
+}
+
+struct SLayout {
+    int64_t H, nchunks, nhist, nsums, nrange;
+    size_t keysA, keysB, payA, payB, hist, sums, ctrl, off, pF, pC, total;
+};
+
+SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
+    SLayout L;
+    const bool rows = row_len > 1;
+    const size_t pw = rows ? 4 : dtype_size(dt);    // payload bytes
+    L.H = 256 * (pw == 4 ? 32 : 16);
+    L.nchunks = cdiv(n > 0 ? n : 1, L.H);
+    L.nhist = (int64_t)kBuckets0 * L.nchunks;
+    L.nsums = cdiv(L.nhist, kU32Blk);
+    const int64_t D = rows ? kRowD : kSegD;
+    L.nrange = cdiv(n > 0 ? n : 1, D);
+    const size_t es = dtype_size(dt);
+    const size_t pe = rows ? (size_t)row_len * es : es;   // bytes per partial
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += round_up(bytes > 0 ? bytes : 1, 256);
+        return at;
+    };
+    L.ctrl = take(256);
+    L.keysA = take((size_t)n * 4);
+    L.keysB = take((size_t)n * 4);
+    L.payA = take((size_t)n * pw);
+    L.payB = take((size_t)n * pw);
+    L.hist = take((size_t)L.nhist * 4);
+    L.sums = take((size_t)L.nsums * 4);
+    L.off = take((size_t)(num_out + 1) * 4);
+    L.pF = take((size_t)L.nrange * pe);
+    L.pC = take((size_t)L.nrange * pe);
+    L.total = o;
+    return L;
+}
+
+template <typename T, typename P, bool ROWS>
+det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_t row_len, T* out,
+                        int64_t num_out, T* prev, int64_t* n_skipped, char* ws, hipStream_t s) {
+    const SLayout L = slayout(n, num_out, row_len, sizeof(T) == 8 ? DET_F64 : DET_F32);
+    if (n == 0) {
+        if (n_skipped) {
+            k_write_skipped_all<T><<<1, 1, 0, s>>>(n_skipped, 0);
+            return launch_status();
+        }
+        return DET_SUCCESS;
+    }
+    if (prev) {
+        const int64_t total = n * row_len;
+        int64_t g = cdiv(total, 256);
+        if (g > 65536) g = 65536;
+        k_prev_gather<T><<<dim3((unsigned)g), dim3(256), 0, s>>>(index, n, row_len, num_out, out, prev);
+    }
+    if (num_out == 0) {
+        if (n_skipped) k_write_skipped_all<T><<<1, 1, 0, s>>>(n_skipped, n);
+        return launch_status();
+    }
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);   // [0] = number of valid keys
+    uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(ws + L.keysA),
+                         reinterpret_cast<uint32_t*>(ws + L.keysB)};
+    P* pay[2] = {reinterpret_cast<P*>(ws + L.payA), reinterpret_cast<P*>(ws + L.payB)};
+    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    uint32_t* sums = reinterpret_cast<uint32_t*>(ws + L.sums);
+    uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
+    const uint32_t B = (uint32_t)num_out;
+    const int passes = key_passes(num_out);
+    const unsigned grid = (unsigned)L.nchunks;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = 8 * p;
+        const bool first = p == 0;
+        const uint32_t* kin = first ? reinterpret_cast<const uint32_t*>(index) : keys[(p - 1) & 1];
+        const P* pin = first ? reinterpret_cast<const P*>(values) : pay[(p - 1) & 1];
+        const int nb = first ? kBuckets0 : 256;
+        if (first)
+            k_radix_hist<true><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb, L.nchunks, (int)L.H,
+                                                    hist);
+        else
+            k_radix_hist<false><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb, L.nchunks,
+                                                     (int)L.H, hist);
+        det_status st = u32_exclusive_scan(hist, (int64_t)nb * L.nchunks, sums, s);
+        if (st != DET_SUCCESS) return st;
+        if (first) k_copy_word<<<1, 1, 0, s>>>(hist + (int64_t)256 * L.nchunks, ctrl);
+        if (first)
+            k_radix_scatter<P, true, ROWS><<<grid, 256, 0, s>>>(kin, pin, keys[p & 1], pay[p & 1], n,
+                                                                ctrl, B, shift, L.nchunks, hist);
+        else
+            k_radix_scatter<P, false, ROWS><<<grid, 256, 0, s>>>(kin, pin, keys[p & 1], pay[p & 1],
+                                                                 n, ctrl, B, shift, L.nchunks, hist);
+        st = launch_status();
+        if (st != DET_SUCCESS) return st;
+    }
+    const uint32_t* K = keys[(passes - 1) & 1];
+    const P* SP = pay[(passes - 1) & 1];
+    {
+        int64_t g = cdiv(num_out + 1, 256);
+        if (g > 8192) g = 8192;
+        k_bin_offsets<<<dim3((unsigned)g), dim3(256), 0, s>>>(K, ctrl, num_out, n, off, n_skipped);
+    }
+    T* pF = reinterpret_cast<T*>(ws + L.pF);
+    T* pC = reinterpret_cast<T*>(ws + L.pC);
+    int64_t lg = cdiv(num_out, 64 * 4);
+    if (lg > 4096) lg = 4096;
+    if constexpr (!ROWS) {
+        k_segred_scalar<T><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
+            K, reinterpret_cast<const T*>(SP), off, ctrl, out, pF, pC);
+        k_segred_scalar_long<T><<<dim3((unsigned)lg), dim3(256), 0, s>>>(off, num_out, pF, pC, out);
+    } else {
+        k_segred_rows<T><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
+            K, reinterpret_cast<const uint32_t*>(SP), off, ctrl, values, row_len, out, pF, pC);
+        int64_t rg = cdiv(num_out, 256);
+        if (rg > 4096) rg = 4096;
+        k_segred_rows_long<T><<<dim3((unsigned)rg), dim3(256), 0, s>>>(off, num_out, row_len, pF,
+                                                                        pC, out);
+    }
+    return launch_status();
+}
+
+}  // namespace
+
+size_t scatter_workspace(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
+    return slayout(n, num_out, row_len, dt).total;
+}
+
+det_status scatter_launch(const void* values, const int32_t* index, int64_t n, int64_t row_len,
+                          det_dtype dt, void* out, int64_t num_out, void* prev, int64_t* n_skipped,
+                          void* ws, size_t ws_bytes, hipStream_t s) {
+    (void)ws_bytes;
+    char* w = static_cast<char*>(ws);
+    if (dt == DET_F32) {
+        const float* v = static_cast<const float*>(values);
+        float* o = static_cast<float*>(out);
+        float* pr = static_cast<float*>(prev);
+        if (row_len == 1)
+            return scatter_impl<float, uint32_t, false>(v, index, n, 1, o, num_out, pr, n_skipped, w, s);
+        return scatter_impl<float, uint32_t, true>(v, index, n, row_len, o, num_out, pr, n_skipped, w, s);
+    }
+    const double* v = static_cast<const double*>(values);
+    double* o = static_cast<double*>(out);
+    double* pr = static_cast<double*>(prev);
+    if (row_len == 1)
+        return scatter_impl<double, uint64_t, false>(v, index, n, 1, o, num_out, pr, n_skipped, w, s);
+    return scatter_impl<double, uint32_t, true>(v, index, n, row_len, o, num_out, pr, n_skipped, w, s);
+}
+
+}  // namespace det

@@ -1,0 +1,219 @@
+"""ctypes binding of libdet.so (the HIP library), with the C interface's names.
+
+Argument marshalling only: tensors become device pointers and sizes, the workspace is a
+torch uint8 tensor from the caching allocator, and the current torch stream is passed
+through.  Every step of every operation runs in the library's kernels; there is no CPU or
+PyTorch fallback, and a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdet.so")
+
+DET_F32 = 0
+DET_F64 = 1
+DET_SCAN_EXCLUSIVE = 1
+DET_SCAN_REVERSE = 2
+
+_STATUS = {
+    0: "DET_SUCCESS",
+    1: "DET_ERROR_INVALID_VALUE",
+    2: "DET_ERROR_UNSUPPORTED",
+    3: "DET_ERROR_TOO_LARGE",
+    4: "DET_ERROR_WORKSPACE",
+    5: "DET_ERROR_LAUNCH",
+}
+
+
+class DetError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_STATUS.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdet.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python __graft_entry__.py` "
+                           "(hipcc --offload-arch=gfx950); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, sz, u, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint, ctypes.c_int
+    L.det_sum_workspace_size.argtypes, L.det_sum_workspace_size.restype = [i64, i], sz
+    L.det_sum.argtypes, L.det_sum.restype = [p, i64, i, p, p, sz, p], i
+    L.det_scan_workspace_size.argtypes, L.det_scan_workspace_size.restype = [i64, i, u, i64], sz
+    L.det_scan.argtypes, L.det_scan.restype = [p, p, i64, i, u, p, i64, p, sz, p], i
+    L.det_scatter_add_workspace_size.argtypes = [i64, i64, i64, i]
+    L.det_scatter_add_workspace_size.restype = sz
+    L.det_scatter_add.argtypes = [p, p, i64, i64, i, p, i64, p, p, p, sz, p]
+    L.det_scatter_add.restype = i
+    L.det_spec_version.argtypes, L.det_spec_version.restype = [], i
+    L.det_spec_constants.argtypes = [ctypes.POINTER(i64)] * 3
+    L.det_spec_constants.restype = None
+    L.det_status_string.argtypes, L.det_status_string.restype = [i], ctypes.c_char_p
+    L.det_debug_set_launch.argtypes, L.det_debug_set_launch.restype = [i, i], i
+    _lib = L
+    return L
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DET_F32
+    if t.dtype == torch.float64:
+        return DET_F64
+    raise TypeError(f"det supports float32 and float64, got {t.dtype}")
+
+
+def _dev_ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("det operates on device tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError(f"workspace of {nbytes} bytes needed")
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise DetError(st, what)
+
+
+def _flat(t: torch.Tensor) -> torch.Tensor:
+    if not t.is_contiguous():
+        raise ValueError("det needs contiguous tensors (views with an offset are fine)")
+    return t
+
+
+# ------------------------------------------------------------------ sum
+
+def det_sum_workspace_size(n: int, dtype_code: int) -> int:
+    return lib().det_sum_workspace_size(n, dtype_code)
+
+
+def det_sum(x: torch.Tensor, out: Optional[torch.Tensor] = None,
+            ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Reproducible sum of all elements of ``x``; returns a 0-d tensor (or fills ``out``)."""
+    x = _flat(x)
+    dt = _dtype_code(x)
+    n = x.numel()
+    if out is None:
+        out = torch.empty((), dtype=x.dtype, device=x.device)
+    w = _workspace(det_sum_workspace_size(n, dt), x.device, ws)
+    _check(lib().det_sum(_dev_ptr(x), n, dt, _dev_ptr(out), _dev_ptr(w), w.numel(),
+                         _stream(x.device)), "det_sum")
+    return out
+
+
+# ------------------------------------------------------------------ scan
+
+def det_scan_workspace_size(n: int, dtype_code: int, flags: int = 0, num_segments: int = 0) -> int:
+    return lib().det_scan_workspace_size(n, dtype_code, flags, num_segments)
+
+
+def det_scan(x: torch.Tensor, y: Optional[torch.Tensor] = None, exclusive: bool = False,
+             reverse: bool = False, offsets: Optional[torch.Tensor] = None,
+             ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Reproducible prefix sum of ``x`` (1-D).  ``offsets``: int64 device tensor [S+1]
+    (0 = o_0 <= ... <= o_S = n) for a segmented scan."""
+    x = _flat(x)
+    dt = _dtype_code(x)
+    n = x.numel()
+    if y is None:
+        y = torch.empty_like(x)
+    flags = (DET_SCAN_EXCLUSIVE if exclusive else 0) | (DET_SCAN_REVERSE if reverse else 0)
+    nseg = 0
+    if offsets is not None:
+        if offsets.dtype != torch.int64:
+            raise TypeError("offsets must be int64")
+        offsets = _flat(offsets)
+        nseg = offsets.numel() - 1
+    w = _workspace(det_scan_workspace_size(n, dt, flags, max(nseg, 0)), x.device, ws)
+    _check(lib().det_scan(_dev_ptr(x), _dev_ptr(y), n, dt, flags, _dev_ptr(offsets), nseg,
+                          _dev_ptr(w), w.numel(), _stream(x.device)), "det_scan")
+    return y
+
+
+# ------------------------------------------------------------------ scatter-add
+
+def det_scatter_add_workspace_size(n: int, num_out: int, row_len: int, dtype_code: int) -> int:
+    return lib().det_scatter_add_workspace_size(n, num_out, row_len, dtype_code)
+
+
+def det_scatter_add(values: torch.Tensor, index: torch.Tensor, out: torch.Tensor,
+                    prev: Optional[torch.Tensor] = None, n_skipped: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``out[index[i]] += values[i]`` along axis 0 in the fixed order; returns ``out``.
+
+    ``values``: [n] or [n, *row]; ``index``: int32 [n]; ``out``: [num_out] or [num_out, *row].
+    ``prev`` (same shape as values) receives the destination rows before the call;
+    ``n_skipped`` (int64, one element) receives the number of out-of-range indices."""
+    values = _flat(values)
+    index = _flat(index)
+    out = _flat(out)
+    dt = _dtype_code(values)
+    if out.dtype != values.dtype:
+        raise TypeError("values and out must share a dtype")
+    if index.dtype != torch.int32:
+        raise TypeError("index must be int32")
+    n = index.numel()
+    row_len = values.numel() // n if n else (out[0].numel() if out.dim() > 1 and len(out) else 1)
+    if n and values.numel() != n * row_len:
+        raise ValueError("values and index disagree on n")
+    if row_len < 1:
+        row_len = 1
+    num_out = out.numel() // row_len
+    if out.numel() != num_out * row_len:
+        raise ValueError("out is not a whole number of rows")
+    if prev is not None:
+        prev = _flat(prev)
+        if prev.numel() != n * row_len or prev.dtype != values.dtype:
+            raise ValueError("prev must match values")
+    if n_skipped is not None and (n_skipped.dtype != torch.int64 or n_skipped.numel() < 1):
+        raise ValueError("n_skipped must be an int64 tensor with one element")
+    w = _workspace(det_scatter_add_workspace_size(n, num_out, row_len, dt), values.device, ws)
+    _check(lib().det_scatter_add(_dev_ptr(values), _dev_ptr(index), n, row_len, dt, _dev_ptr(out),
+                                 num_out, _dev_ptr(prev), _dev_ptr(n_skipped), _dev_ptr(w),
+                                 w.numel(), _stream(values.device)), "det_scatter_add")
+    return out
+
+
+# ------------------------------------------------------------------ introspection
+
+def det_spec_version() -> int:
+    return lib().det_spec_version()
+
+
+def det_spec_constants():
+    v, l_, a = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    lib().det_spec_constants(ctypes.byref(v), ctypes.byref(l_), ctypes.byref(a))
+    return v.value, l_.value, a.value
+
+
+def det_status_string(status: int) -> str:
+    return lib().det_status_string(status).decode()
+
+
+def det_debug_set_launch(grid_wgs: int = 0, sum_chunk_log2: int = 0) -> None:
+    _check(lib().det_debug_set_launch(grid_wgs, sum_chunk_log2), "det_debug_set_launch")

@@ -1,6 +1,7 @@
 import os
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -10,10 +11,45 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (runs through the HIP library)")
-    config.addinivalue_line("markers", "slow: large host-side work (full-size cases)")
 
 
-def pytest_collection_modifyitems(config, items):
-    # A GPU test on a machine without a GPU is an error, not a skip, unless the run
-    # deselected GPU tests with -m "not gpu".
-    pass
+@pytest.fixture(autouse=True)
+def _announce(request):
+    # name the case on the real stderr before it runs, so a run that dies mid-test says where
+    if request.node.get_closest_marker("gpu"):
+        sys.__stderr__.write(f"\n[start] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield
+
+
+@pytest.fixture(scope="session")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test collected on a machine without a GPU (deselect with -m 'not gpu')")
+    return torch.device("cuda:0")
+
+
+def bits_equal(got, want):
+    """Bitwise equality of two float arrays, NaN compared by class (payloads may differ)."""
+    got = np.ascontiguousarray(got)
+    want = np.ascontiguousarray(want)
+    if got.shape != want.shape or got.dtype != want.dtype:
+        return False
+    gn, wn = np.isnan(got), np.isnan(want)
+    if not np.array_equal(gn, wn):
+        return False
+    it = np.uint32 if got.dtype == np.float32 else np.uint64
+    return np.array_equal(got.view(it)[~gn], want.view(it)[~wn])
+
+
+def first_mismatch(got, want):
+    got = np.ascontiguousarray(got).reshape(-1)
+    want = np.ascontiguousarray(want).reshape(-1)
+    it = np.uint32 if got.dtype == np.float32 else np.uint64
+    bad = (got.view(it) != want.view(it)) & ~(np.isnan(got) & np.isnan(want))
+    idx = np.flatnonzero(bad)
+    if idx.size == 0:
+        return "no mismatch"
+    i = int(idx[0])
+    return f"{idx.size} mismatches, first at {i}: got {got[i]!r} want {want[i]!r}"

@@ -1,0 +1,113 @@
+"""The C-ABI boundary, checked without a GPU.
+
+libdet.so must load and export every function include/det.h declares; the workspace-size
+functions and argument validation are host-only code and are exercised here (every call
+below returns before anything is enqueued).  The spec constants the library reports must be
+the ones the oracle is written for.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from scan_fixed_order_amd import det
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "det.h")
+
+E_INVALID, E_UNSUPPORTED, E_TOO_LARGE, E_WORKSPACE = 1, 2, 3, 4
+NULL = None
+FAKE = ctypes.c_void_p(0x10000)      # never dereferenced: every call here fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(det_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert {"det_sum", "det_scan", "det_scatter_add"} <= set(names)
+    lib = det.lib()
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_spec_constants_match_oracle():
+    V, L, A = det.det_spec_constants()
+    assert V == oracle.SPEC_V and L == oracle.SPEC_W * oracle.SPEC_NW and A == oracle.SPEC_A
+    assert det.det_spec_version() == 1
+    assert det.det_status_string(0) == "DET_SUCCESS"
+    assert det.det_status_string(4) == "DET_ERROR_WORKSPACE"
+
+
+def test_workspace_sizes():
+    lib = det.lib()
+    assert lib.det_sum_workspace_size(0, 0) >= 256
+    assert lib.det_sum_workspace_size(-1, 0) == 0
+    assert lib.det_sum_workspace_size(1, 7) == 0
+    assert lib.det_sum_workspace_size(1 << 28, 0) >= (1 << 14) * 4
+    s32 = lib.det_scan_workspace_size(1 << 28, 0, 0, 0)
+    s64 = lib.det_scan_workspace_size(1 << 28, 1, 0, 0)
+    assert s64 > s32 > (1 << 28) // 8192 * 8
+    assert lib.det_scan_workspace_size(10, 0, 4, 0) == 0          # unknown flag bit
+    w = lib.det_scatter_add_workspace_size(1 << 24, 65536, 1, 0)
+    assert w >= (1 << 24) * 16                                     # two key + two value buffers
+    assert lib.det_scatter_add_workspace_size(10, 10, 0, 0) == 0   # row_len < 1
+
+
+def test_validation_errors_enqueue_nothing():
+    lib = det.lib()
+    ws = FAKE
+    # sum
+    assert lib.det_sum(FAKE, -1, 0, FAKE, ws, 1 << 20, NULL) == E_INVALID
+    assert lib.det_sum(FAKE, 10, 9, FAKE, ws, 1 << 20, NULL) == E_UNSUPPORTED
+    assert lib.det_sum(FAKE, 1 << 31, 0, FAKE, ws, 1 << 40, NULL) == E_TOO_LARGE
+    assert lib.det_sum(NULL, 10, 0, FAKE, ws, 1 << 20, NULL) == E_INVALID
+    assert lib.det_sum(FAKE, 10, 0, NULL, ws, 1 << 20, NULL) == E_INVALID
+    assert lib.det_sum(FAKE, 1 << 20, 0, FAKE, NULL, 1 << 20, NULL) == E_WORKSPACE
+    assert lib.det_sum(FAKE, 1 << 24, 0, FAKE, ws, 16, NULL) == E_WORKSPACE
+    # scan
+    assert lib.det_scan(FAKE, FAKE, 10, 0, 8, NULL, 0, ws, 1 << 20, NULL) == E_INVALID
+    x = ctypes.c_void_p(0x100000)
+    y_overlap = ctypes.c_void_p(0x100000 + 4)
+    assert lib.det_scan(x, y_overlap, 10, 0, 0, NULL, 0, ws, 1 << 20, NULL) == E_INVALID
+    assert lib.det_scan(x, x, 10, 0, 1, NULL, 0, ws, 1 << 20, NULL) == E_INVALID  # excl in place
+    assert lib.det_scan(FAKE, ctypes.c_void_p(0x900000), 10, 0, 0, FAKE, 0, ws, 1 << 20,
+                        NULL) == E_INVALID                                          # S = 0, n > 0
+    assert lib.det_scan(FAKE, ctypes.c_void_p(0x900000), 1 << 20, 0, 0, NULL, 0, ws, 8,
+                        NULL) == E_WORKSPACE
+    assert lib.det_scan(FAKE, FAKE, 10, 3, 0, NULL, 0, ws, 1 << 20, NULL) == E_UNSUPPORTED
+    # scatter
+    sa = lib.det_scatter_add
+    assert sa(FAKE, FAKE, 10, 0, 0, ctypes.c_void_p(0x900000), 4, NULL, NULL, ws, 1 << 30,
+              NULL) == E_INVALID                                                    # row_len 0
+    assert sa(FAKE, FAKE, -5, 1, 0, ctypes.c_void_p(0x900000), 4, NULL, NULL, ws, 1 << 30,
+              NULL) == E_INVALID
+    assert sa(x, FAKE, 10, 1, 0, ctypes.c_void_p(0x100000 + 8), 4, NULL, NULL, ws, 1 << 30,
+              NULL) == E_INVALID                                                    # values alias out
+    assert sa(FAKE, FAKE, 1 << 31, 1, 0, ctypes.c_void_p(0x900000), 4, NULL, NULL, ws, 1 << 40,
+              NULL) == E_TOO_LARGE
+    assert sa(FAKE, FAKE, 1000, 1, 0, ctypes.c_void_p(0x900000), 4, NULL, NULL, ws, 64,
+              NULL) == E_WORKSPACE
+    assert sa(FAKE, FAKE, 10, 1, 5, ctypes.c_void_p(0x900000), 4, NULL, NULL, ws, 1 << 30,
+              NULL) == E_UNSUPPORTED
+
+
+def test_debug_hook_range():
+    lib = det.lib()
+    assert lib.det_debug_set_launch(-1, 0) == E_INVALID
+    assert lib.det_debug_set_launch(0, 13) == E_INVALID
+    assert lib.det_debug_set_launch(0, 25) == E_INVALID
+    assert lib.det_debug_set_launch(0, 0) == 0
+
+
+def test_binding_rejects_cpu_tensors_and_bad_dtypes():
+    import torch
+    with pytest.raises(ValueError):
+        det.det_sum(torch.ones(10))                 # host tensor: no CPU path exists
+    with pytest.raises(TypeError):
+        det.det_sum(torch.ones(10, dtype=torch.float16))

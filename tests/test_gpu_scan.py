@@ -1,0 +1,143 @@
+"""det_scan on the GPU against the oracle, bit for bit (through the C interface).
+
+Sizes straddle lanes (32), waves (2048), tiles (8192) and anchor intervals (256 tiles), in
+f32 and f64, inclusive/exclusive x forward/reverse x full/segmented (drjit-core pull request
+"Make CUDA floating-point prefix sums deterministic", "Validation": the same matrix, and 20
+repeated scans of 164,738 elements).  Also: in-place scans, unaligned views, empty segments,
+and grid caps that must not move a bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from scan_fixed_order_amd import det, workloads
+from conftest import bits_equal, first_mismatch
+
+pytestmark = pytest.mark.gpu
+
+F32, F64 = np.float32, np.float64
+T = 8192
+A = 256
+MODES = [(False, False), (True, False), (False, True), (True, True)]
+
+
+def gpu_scan(x, dev, exclusive=False, reverse=False, offsets=None):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    o = None if offsets is None else torch.from_numpy(np.asarray(offsets, np.int64)).to(dev)
+    return det.det_scan(t, exclusive=exclusive, reverse=reverse, offsets=o).cpu().numpy()
+
+
+def random_offsets(n, mean, seed, empty_every=0):
+    rng = np.random.default_rng(seed)
+    cuts = [0]
+    while cuts[-1] < n:
+        cuts.append(min(n, cuts[-1] + int(rng.geometric(1.0 / mean))))
+        if empty_every and len(cuts) % empty_every == 0:
+            cuts.append(cuts[-1])                    # an empty segment
+    return np.array(cuts, np.int64)
+
+
+SIZES = [1, 31, 32, 33, 2047, 2048, 2049, 8191, 8192, 8193, 16384, 164738, 1048577,
+         A * T + 1, 3 * A * T + 5]
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n", SIZES)
+def test_scan_parity_all_modes(dev, dtype, n):
+    x = workloads.scan_values(n, dtype, seed=n % 97)
+    for excl, rev in MODES:
+        got = gpu_scan(x, dev, excl, rev)
+        want = oracle.scan(x, exclusive=excl, reverse=rev)
+        assert bits_equal(got, want), (n, excl, rev, first_mismatch(got, want))
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n,mean", [(1, 5), (100, 3), (8193, 40), (164738, 100),
+                                    (1048577, 5000), (A * T + 77, 100), (3 * A * T + 5, 1e6)])
+def test_segmented_parity(dev, dtype, n, mean):
+    x = workloads.scan_values(n, dtype, seed=3)
+    offs = random_offsets(n, mean, seed=n, empty_every=7)
+    for excl, rev in MODES:
+        got = gpu_scan(x, dev, excl, rev, offs)
+        want = oracle.scan(x, exclusive=excl, reverse=rev, offsets=offs)
+        assert bits_equal(got, want), (n, excl, rev, first_mismatch(got, want))
+
+
+def test_segment_edge_layouts(dev):
+    n = 3 * T + 17
+    x = workloads.scan_values(n, F32, seed=11)
+    layouts = [
+        np.array([0, n]),                                        # one segment
+        np.arange(0, n + 1),                                     # every element a head
+        np.array([0, 0, 0, n, n]),                               # empty segments at both ends
+        np.array([0, T - 1, T, T + 1, 2 * T, n]),                # heads around tile borders
+        np.concatenate([[0], np.arange(32, n, 32), [n]]),        # heads at lane starts
+    ]
+    for offs in layouts:
+        for excl, rev in MODES:
+            got = gpu_scan(x, dev, excl, rev, offs)
+            want = oracle.scan(x, exclusive=excl, reverse=rev, offsets=offs)
+            assert bits_equal(got, want), (offs[:6], excl, rev, first_mismatch(got, want))
+
+
+@pytest.mark.parametrize("n", [1, 8193, 3 * A * T + 5])
+def test_all_ones_exact(dev, n):
+    x = np.ones(n, F32)
+    i = np.arange(n, dtype=np.float64)
+    assert np.array_equal(gpu_scan(x, dev), i + 1)
+    assert np.array_equal(gpu_scan(x, dev, exclusive=True), i)
+    assert np.array_equal(gpu_scan(x, dev, reverse=True), n - i)
+    assert np.array_equal(gpu_scan(x, dev, exclusive=True, reverse=True), n - 1 - i)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_repeat_164738_twenty_times(dev, dtype):
+    # the regression size of the drjit-core pull request, repeated 20 times per mode
+    x = workloads.scan_values(164738, dtype, seed=2)
+    t = torch.from_numpy(x).to(dev)
+    for excl, rev in MODES:
+        want = oracle.scan(x, exclusive=excl, reverse=rev)
+        outs = [det.det_scan(t, exclusive=excl, reverse=rev) for _ in range(20)]
+        for o in outs:
+            assert bits_equal(o.cpu().numpy(), want), (excl, rev)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_in_place_and_unaligned(dev, dtype):
+    n = 2 * A * T + 333
+    x = workloads.scan_values(n, dtype, seed=5)
+    want = oracle.scan(x)
+    t = torch.from_numpy(x).to(dev)
+    det.det_scan(t, y=t)                                     # inclusive in place
+    assert bits_equal(t.cpu().numpy(), want)
+    t = torch.from_numpy(x).to(dev)
+    for k in (1, 3):
+        for excl, rev in MODES:
+            got = det.det_scan(t[k:], exclusive=excl, reverse=rev).cpu().numpy()
+            assert bits_equal(got, oracle.scan(x[k:], exclusive=excl, reverse=rev)), (k, excl, rev)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_grid_invariance(dev, dtype):
+    n = 3 * A * T + 5
+    x = workloads.scan_values(n, dtype, seed=6)
+    offs = random_offsets(n, 3000, seed=1)
+    t = torch.from_numpy(x).to(dev)
+    o = torch.from_numpy(offs).to(dev)
+    want = oracle.scan(x)
+    wseg = oracle.scan(x, offsets=offs, reverse=True)
+    try:
+        for grid in (1, 2, 7, 64, 256, 1000):
+            det.det_debug_set_launch(grid, 0)
+            assert bits_equal(det.det_scan(t).cpu().numpy(), want), grid
+            assert bits_equal(det.det_scan(t, offsets=o, reverse=True).cpu().numpy(), wseg), grid
+    finally:
+        det.det_debug_set_launch(0, 0)
+
+
+def test_empty_scan(dev):
+    t = torch.empty(0, device=dev)
+    assert det.det_scan(t).numel() == 0
+    assert det.det_scan(t, exclusive=True, offsets=torch.zeros(1, dtype=torch.int64,
+                                                               device=dev)).numel() == 0

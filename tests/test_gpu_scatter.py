@@ -1,0 +1,143 @@
+"""det_scatter_add on the GPU against the oracle, bit for bit (through the C interface).
+
+Scalar bins (f32, f64) across radix-pass counts (1, 2, 3 digit passes), out-of-range indices,
+the fully contended case (every value into one bin, so the split of long destinations into
+blocks and block values is exercised), identity bins, prev snapshots and skip counts; rows
+(the tile accumulate) including the worked example on the "warp.tile_atomic_add_indexed"
+page, row lengths that are not multiples of 64, and destinations with more than 64 rows.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from scan_fixed_order_amd import det, workloads
+from conftest import bits_equal, first_mismatch
+
+pytestmark = pytest.mark.gpu
+
+F32, F64 = np.float32, np.float64
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gpu_scatter(v, idx, out0, dev, want_prev=False):
+    vt = torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+    it = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to(dev)
+    ot = torch.from_numpy(np.array(out0, copy=True)).to(dev)
+    pt = torch.full(v.shape, float("nan"), dtype=vt.dtype, device=dev) if want_prev else None
+    sk = torch.full((1,), -7, dtype=torch.int64, device=dev)
+    det.det_scatter_add(vt, it, ot, prev=pt, n_skipped=sk)
+    return ot.cpu().numpy(), (pt.cpu().numpy() if want_prev else None), int(sk.item())
+
+
+def rounding(shape, dtype, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(shape) * 10.0 ** rng.uniform(-4, 4, shape)).astype(dtype)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n,B", [(1, 1), (7, 1), (1000, 7), (65537, 256), (65537, 257),
+                                 (100003, 1000), (300007, 65536), (300007, 65537),
+                                 (1 << 20, 1 << 20), (200000, 3)])
+def test_scalar_parity(dev, dtype, n, B):
+    rng = np.random.default_rng(n + B)
+    v = rounding(n, dtype, n)
+    idx = rng.integers(-2, B + 2, n).astype(np.int32)
+    o = rounding(B, dtype, B)
+    got, prev, k = gpu_scatter(v, idx, o, dev, want_prev=True)
+    want, wprev, wk = oracle.scatter_add(v, idx, o, want_prev=True)
+    assert bits_equal(got, want), (n, B, first_mismatch(got, want))
+    assert k == wk
+    assert bits_equal(prev, wprev)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n", [1, 4096, 8192, 8193, 100003, 3 * 8192 * 8192 // 1024 + 1])
+def test_contended_one_bin(dev, dtype, n):
+    v = rounding(n, dtype, 1)
+    idx = np.zeros(n, np.int32)
+    o = np.zeros(65536, dtype)
+    got, _, k = gpu_scatter(v, idx, o, dev)
+    want, _, _ = oracle.scatter_add(v, idx, o)
+    assert bits_equal(got, want), first_mismatch(got, want)
+    assert k == 0
+    # cross-op identity: +0.0 plus the reproducible sum
+    s = det.det_sum(torch.from_numpy(v).to(dev)).cpu().numpy()
+    assert bits_equal(got[:1], (dtype(0.0) + s).reshape(1))
+
+
+def test_quickstart(dev):
+    got, _, k = gpu_scatter(np.ones(4096, F32), np.zeros(4096, np.int32), np.zeros(1, F32), dev)
+    assert got[0] == 4096.0 and k == 0
+
+
+def test_identity_bins_and_all_skipped(dev):
+    n = 70000
+    v = rounding(n, F32, 2)
+    o = rounding(n, F32, 3)
+    got, prev, k = gpu_scatter(v, np.arange(n, dtype=np.int32), o, dev, want_prev=True)
+    assert bits_equal(got, o + v) and bits_equal(prev, o) and k == 0
+    idx = np.full(n, -1, np.int32)
+    got, prev, k = gpu_scatter(v, idx, o, dev, want_prev=True)
+    assert bits_equal(got, o) and k == n and np.isnan(prev).all()
+
+
+def test_empty_inputs(dev):
+    got, _, k = gpu_scatter(np.zeros(0, F32), np.zeros(0, np.int32), np.ones(5, F32), dev)
+    assert bits_equal(got, np.ones(5, F32)) and k == 0
+    got, _, k = gpu_scatter(np.ones(9, F32), np.zeros(9, np.int32), np.zeros(0, F32), dev)
+    assert got.size == 0 and k == 9
+
+
+def test_c2_shape_2_24(dev):
+    n = 1 << 24
+    v = workloads.normal(n, seed=1)
+    idx = workloads.bins_uniform(n, 65536, seed=1)
+    o = np.zeros(65536, F32)
+    got, _, _ = gpu_scatter(v, idx, o, dev)
+    want, _, _ = oracle.scatter_add(v, idx, o)
+    assert bits_equal(got, want), first_mismatch(got, want)
+
+
+def test_zipf_f64(dev):
+    n = 1 << 22
+    v = workloads.mixed_f64(n, seed=4)
+    idx = workloads.zipf_bins(n, 1 << 20, seed=4)
+    o = np.zeros(1 << 20, F64)
+    got, _, _ = gpu_scatter(v, idx, o, dev)
+    want, _, _ = oracle.scatter_add(v, idx, o)
+    assert bits_equal(got, want), first_mismatch(got, want)
+
+
+# ---------------------------------------------------------------- rows
+
+def test_rows_worked_example(dev):
+    g = json.load(open(os.path.join(GOLDEN, "tile_atomic_add_indexed_example.json")))
+    got, prev, k = gpu_scatter(np.array(g["x"], F32), np.array(g["rows"], np.int32),
+                               np.array(g["y_init"], F32), dev, want_prev=True)
+    assert np.array_equal(got, np.array(g["y_expected"], F32))
+    assert np.array_equal(prev, np.array(g["previous_expected"], F32)) and k == 0
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n,d,B", [(100, 3, 10), (1000, 100, 37), (4096, 256, 1 << 10),
+                                   (5000, 65, 1), (3000, 300, 2), (20000, 8, 1 << 15)])
+def test_rows_parity(dev, dtype, n, d, B):
+    rng = np.random.default_rng(n * d + B)
+    v = rounding((n, d), dtype, n)
+    idx = rng.integers(-1, B + 1, n).astype(np.int32)
+    o = rounding((B, d), dtype, d)
+    got, prev, k = gpu_scatter(v, idx, o, dev, want_prev=True)
+    want, wprev, wk = oracle.scatter_add(v, idx, o, want_prev=True)
+    assert bits_equal(got, want), (n, d, B, first_mismatch(got, want))
+    assert k == wk and bits_equal(prev, wprev)
+
+
+def test_rows_c4_shape(dev):
+    src, rows, out0 = workloads.rows_case()
+    got, _, _ = gpu_scatter(src, rows, out0, dev)
+    want, _, _ = oracle.scatter_add(src, rows, out0)
+    assert bits_equal(got, want), first_mismatch(got, want)
