@@ -14,8 +14,9 @@ Every function here follows the association order stated in ``detref.c``:
 * ``scatter_add``   -- stable grouping by destination in ascending source index, ``pw`` per
                        destination and column, initial value added last (Warp "Deterministic
                        Execution", Pattern 1; ``warp.tile_atomic_add_indexed`` for rows).
-* ``scan``          -- tiles of V*W*NW elements, anchor intervals of A tiles (drjit-core pull
-                       request "Make CUDA floating-point prefix sums deterministic").
+* ``scan``          -- tiles of V*W*NW elements, anchors every A tiles and every A*A2 tiles
+                       (drjit-core pull request "Make CUDA floating-point prefix sums
+                       deterministic").
 """
 from __future__ import annotations
 
@@ -31,11 +32,13 @@ _SRC = os.path.join(_HERE, "detref.c")
 _LIB_PATH = os.path.join(_HERE, "libdetref.so")
 
 # Spec constants of the scan: V elements per lane, W lanes per wave, NW waves per tile
-# (tile = V * W * NW = 8192 elements), A tiles per anchor interval.
+# (tile = V * W * NW = 8192 elements), A tiles per anchor interval, A2 intervals per
+# super-interval.
 SPEC_V = 32
 SPEC_W = 64
 SPEC_NW = 4
 SPEC_A = 256
+SPEC_A2 = 256
 
 EXCLUSIVE = 1
 REVERSE = 2
@@ -81,7 +84,7 @@ def _load():
         f = getattr(lib, "oref_scatter_add" + suf)
         f.argtypes, f.restype = [p, p, i64, i64, p, i64, p], i64
         f = getattr(lib, "oref_scan" + suf)
-        f.argtypes = [p, p, i64, ctypes.c_uint, p, i64, i64, i64, i64, i64]
+        f.argtypes = [p, p, i64, ctypes.c_uint, p, i64, i64, i64, i64, i64, i64]
         f.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -148,9 +151,9 @@ def scatter_add(values: np.ndarray, index: np.ndarray, out: np.ndarray,
 
 def scan(x: np.ndarray, exclusive: bool = False, reverse: bool = False,
          offsets: Optional[np.ndarray] = None, V: int = SPEC_V, W: int = SPEC_W,
-         NW: int = SPEC_NW, A: int = SPEC_A) -> np.ndarray:
+         NW: int = SPEC_NW, A: int = SPEC_A, A2: int = SPEC_A2) -> np.ndarray:
     """Anchored prefix sum; ``offsets`` (int64 [S+1], 0 = o_0 <= ... <= o_S = n) makes it
-    segmented.  V, W, NW, A default to the spec constants."""
+    segmented.  V, W, NW, A, A2 default to the spec constants."""
     x = np.ascontiguousarray(x).reshape(-1)
     y = np.empty_like(x)
     flags = (EXCLUSIVE if exclusive else 0) | (REVERSE if reverse else 0)
@@ -163,7 +166,7 @@ def scan(x: np.ndarray, exclusive: bool = False, reverse: bool = False,
             raise ValueError("offsets needs at least one entry")
     suf = _suffix(x.dtype)
     rc = getattr(_load(), "oref_scan" + suf)(_ptr(x), _ptr(y), x.size, flags, _ptr(offs), nseg,
-                                             V, W, NW, A)
+                                             V, W, NW, A, A2)
     if rc != 0:
         raise ValueError(f"oracle scan rejected its arguments ({rc})")
     return y

@@ -39,8 +39,9 @@
  *      is left untouched.  Indices outside [0, num_out) are skipped and counted.
  *      prev[i] is out_init at i's destination (snapshot before the call).
  *  R5  scan tile / wave / lane / anchor layout, see scan_forward_inclusive below
- *      (V, W, NW, A are parameters so tiny instances can be checked by hand and by
- *      brute force).
+ *      (V, W, NW, A, A2 are parameters so tiny instances can be checked by hand and by
+ *      brute force).  Anchors are two-level: every interval of A tiles publishes its
+ *      total, every super-interval of A2 intervals carries the running prefix.
  *  R6  exclusive = inclusive shifted by one with +0.0 entering at every segment
  *      head; reverse = flip, forward scan, flip; segments via head flags and the
  *      standard segmented operator (flag_a|flag_b, flag_b ? b : a+b).
@@ -222,45 +223,55 @@ static void tile_local(const DET_T* x, const unsigned char* h, int64_t n, int64_
     *agg = om[NW - 1];
 }
 
-/* Forward inclusive scan of (x, h) into y with constants V, W, NW, A.
+/* Forward inclusive scan of (x, h) into y with constants V, W, NW, A, A2.
  *   Agg_j        tile totals;
- *   interval q   = tiles [qA, qA+A);
- *   G_q          = PW(Agg of every tile of interval q);
- *   C_0 = id,    C_{q+1} = C_q (+) G_q          (the carry through anchor q);
+ *   interval q   = tiles [qA, qA+A);            G_q = PW(Agg of every tile of interval q);
+ *   super-interval Q = intervals [Q*A2, Q*A2+A2);  H_Q = PW(G of every interval of Q);
+ *   CC_0 = id,   CC_{Q+1} = CC_Q (+) H_Q        (the carry through super-anchor Q);
+ *   C_q          = CC_Q (+) PW(G_{Q*A2}, ..., G_{q-1})   (the carry into interval q);
  *   W_j          = PW(Agg_{qA}, ..., Agg_{j-1})  (identity for the interval's first tile);
  *   E_j          = C_q (+) W_j;
  *   y            = ((E_j (+) pw[w]) (+) p[t]) (+) s[t*V+k]. */
 static int scan_forward_inclusive(const DET_T* x, const unsigned char* h, int64_t n,
-                                  int64_t V, int64_t W, int64_t NW, int64_t A, DET_T* y) {
+                                  int64_t V, int64_t W, int64_t NW, int64_t A, int64_t A2,
+                                  DET_T* y) {
     if (n == 0) return OREF_OK;
     int64_t L = W * NW;
     int64_t T = V * L;
     int64_t nt = (n + T - 1) / T;
     int64_t nq = (nt + A - 1) / A;
+    int64_t nQ = (nq + A2 - 1) / A2;
     int64_t big = L > NW ? L : NW;
     pair_t* agg = (pair_t*)malloc((size_t)nt * sizeof(pair_t));
-    pair_t* carry = (pair_t*)malloc((size_t)(nq + 1) * sizeof(pair_t));
+    pair_t* g = (pair_t*)malloc((size_t)nq * sizeof(pair_t));
+    pair_t* cc = (pair_t*)malloc((size_t)(nQ + 1) * sizeof(pair_t));
     pair_t* s = (pair_t*)malloc((size_t)T * sizeof(pair_t));
     pair_t* u = (pair_t*)malloc((size_t)L * sizeof(pair_t));
     pair_t* tmp = (pair_t*)malloc((size_t)big * sizeof(pair_t));
     pair_t* p = (pair_t*)malloc((size_t)L * sizeof(pair_t));
     pair_t* om = (pair_t*)malloc((size_t)NW * sizeof(pair_t));
     pair_t* pw = (pair_t*)malloc((size_t)NW * sizeof(pair_t));
-    if (!agg || !carry || !s || !u || !tmp || !p || !om || !pw) {
-        free(agg); free(carry); free(s); free(u); free(tmp); free(p); free(om); free(pw);
+    if (!agg || !g || !cc || !s || !u || !tmp || !p || !om || !pw) {
+        free(agg); free(g); free(cc); free(s); free(u); free(tmp); free(p); free(om); free(pw);
         return OREF_NO_MEM;
     }
     for (int64_t j = 0; j < nt; ++j) tile_local(x, h, n, j, V, W, NW, s, u, tmp, p, om, pw, &agg[j]);
-    carry[0] = pair_identity();
     for (int64_t q = 0; q < nq; ++q) {
         int64_t cnt = (nt - q * A < A) ? nt - q * A : A;
-        carry[q + 1] = segop(carry[q], pw_pairs(agg + q * A, cnt));
+        g[q] = pw_pairs(agg + q * A, cnt);
+    }
+    cc[0] = pair_identity();
+    for (int64_t Q = 0; Q < nQ; ++Q) {
+        int64_t cnt = (nq - Q * A2 < A2) ? nq - Q * A2 : A2;
+        cc[Q + 1] = segop(cc[Q], pw_pairs(g + Q * A2, cnt));
     }
     for (int64_t j = 0; j < nt; ++j) {
         pair_t a;
         tile_local(x, h, n, j, V, W, NW, s, u, tmp, p, om, pw, &a);
         int64_t q = j / A;
-        pair_t e = segop(carry[q], pw_pairs(agg + q * A, j - q * A));
+        int64_t Q = q / A2;
+        pair_t c = segop(cc[Q], pw_pairs(g + Q * A2, q - Q * A2));
+        pair_t e = segop(c, pw_pairs(agg + q * A, j - q * A));
         for (int64_t t = 0; t < L; ++t) {
             pair_t xt = segop(segop(e, pw[t / W]), p[t]);
             for (int64_t k = 0; k < V; ++k) {
@@ -269,7 +280,7 @@ static int scan_forward_inclusive(const DET_T* x, const unsigned char* h, int64_
             }
         }
     }
-    free(agg); free(carry); free(s); free(u); free(tmp); free(p); free(om); free(pw);
+    free(agg); free(g); free(cc); free(s); free(u); free(tmp); free(p); free(om); free(pw);
     return OREF_OK;
 }
 
@@ -277,8 +288,9 @@ static int scan_forward_inclusive(const DET_T* x, const unsigned char* h, int64_
  * offsets[0..S] with offsets[0] == 0 <= ... <= offsets[S] == n.  x and y must not
  * overlap.  Returns OREF_OK or an error code. */
 int FN(oref_scan)(const DET_T* x, DET_T* y, int64_t n, unsigned flags, const int64_t* offsets,
-                  int64_t num_segments, int64_t V, int64_t W, int64_t NW, int64_t A) {
-    if (n < 0 || V < 1 || W < 1 || NW < 1 || A < 1 ||
+                  int64_t num_segments, int64_t V, int64_t W, int64_t NW, int64_t A,
+                  int64_t A2) {
+    if (n < 0 || V < 1 || W < 1 || NW < 1 || A < 1 || A2 < 1 ||
         (flags & ~(OREF_EXCLUSIVE | OREF_REVERSE)))
         return OREF_BAD_ARG;
     if (offsets) {
@@ -305,7 +317,7 @@ int FN(oref_scan)(const DET_T* x, DET_T* y, int64_t n, unsigned flags, const int
             }
         }
     }
-    int rc = scan_forward_inclusive(xs, h, n, V, W, NW, A, ys);
+    int rc = scan_forward_inclusive(xs, h, n, V, W, NW, A, A2, ys);
     if (rc == OREF_OK) {
         for (int64_t f = 0; f < n; ++f) {
             DET_T v;

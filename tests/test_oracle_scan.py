@@ -2,12 +2,14 @@
 
 The scan's order (tiles of NW waves x W lanes x V elements, lane-serial runs, Kogge-Stone
 passes over lane totals inside each wave and over the wave totals, pairwise trees over tile
-totals inside anchor intervals of A tiles, and a carry that only crosses intervals) follows drjit-core pull request "Make CUDA
-floating-point prefix sums deterministic" (sections "Implementation" and "Validation").
-The oracle takes V, W, NW, A as parameters so tiny instances can be worked out by hand.
+totals inside anchor intervals of A tiles and over interval totals inside super-intervals of
+A2 intervals, and a carry that only crosses super-intervals) follows drjit-core pull request
+"Make CUDA floating-point prefix sums deterministic" (sections "Implementation" and
+"Validation").  The oracle takes V, W, NW, A, A2 as parameters so tiny instances can be worked
+out by hand.
 
 Checks, none of which reuses the oracle's code:
-* hand-written expressions for tiny (V, W, NW, A) instances, evaluated with numpy scalars;
+* hand-written expressions for tiny (V, W, NW, A, A2) instances, evaluated with numpy scalars;
 * a top-down brute-force evaluator that builds every output's expression tree from the
   stated order and evaluates it (tiny n, many tiles and intervals);
 * textbook special cases: n <= V is a sequential cumulative sum (numpy's ``cumsum``);
@@ -53,16 +55,17 @@ def test_hand_V2_W2_A2_two_tiles(seed):
 
 
 @pytest.mark.parametrize("seed", range(20))
-def test_hand_V1_W1_A2_carry_chain(seed):
-    # one element per tile; intervals of two tiles; the carry into interval q+1 is
-    # C_q + (x_2q + x_2q+1), while the last output of interval q is (C_q + x_2q) + x_2q+1
+def test_hand_V1_W1_A1_A2_2_carry_chain(seed):
+    # one element per tile and per interval; super-intervals of two; the carry into
+    # super-interval Q+1 is CC_Q + (x_2Q + x_2Q+1), while the last output of Q is
+    # (CC_Q + x_2Q) + x_2Q+1
     x = rounding_values(7, F32, seed)
     c1 = x[0] + x[1]
     c2 = c1 + (x[2] + x[3])
     c3 = c2 + (x[4] + x[5])
     want = [x[0], x[0] + x[1], c1 + x[2], (c1 + x[2]) + x[3], c2 + x[4], (c2 + x[4]) + x[5],
             c3 + x[6]]
-    assert same_bits(oracle.scan(x, V=1, W=1, NW=1, A=2), np.array(want, F32))
+    assert same_bits(oracle.scan(x, V=1, W=1, NW=1, A=1, A2=2), np.array(want, F32))
 
 
 @pytest.mark.parametrize("seed", range(20))
@@ -73,6 +76,33 @@ def test_hand_V1_W1_A4_lookback_tree(seed):
     want = [x0, x0 + x1, (x0 + x1) + x2, ((x0 + x1) + x2) + x3,
             c1 + x4, (c1 + x4) + x5, (c1 + (x4 + x5)) + x6, (c1 + ((x4 + x5) + x6)) + x7]
     assert same_bits(oracle.scan(x, V=1, W=1, NW=1, A=4), np.array(want, F32))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_hand_interval_tree_A1_A2_8(seed):
+    # intervals of one tile, super-intervals of 8: the carry into interval q is the pairwise
+    # tree of the earlier interval totals (not a left-to-right chain)
+    x = rounding_values(9, F32, seed)
+    x0, x1, x2, x3, x4, x5, x6, x7, x8 = x
+    p4 = (x0 + x1) + (x2 + x3)
+    p8 = p4 + ((x4 + x5) + (x6 + x7))
+    want = [x0, x0 + x1, (x0 + x1) + x2, ((x0 + x1) + x2) + x3, p4 + x4, (p4 + x4) + x5,
+            (p4 + (x4 + x5)) + x6, (p4 + ((x4 + x5) + x6)) + x7, p8 + x8]
+    assert same_bits(oracle.scan(x, V=1, W=1, NW=1, A=1, A2=8), np.array(want, F32))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_hand_A2_A2_2_two_level_anchors(seed):
+    # tiles of one element, intervals of 2 tiles, super-intervals of 2 intervals
+    x = rounding_values(9, F32, seed)
+    x0, x1, x2, x3, x4, x5, x6, x7, x8 = x
+    g0, g1, g2, g3 = x0 + x1, x2 + x3, x4 + x5, x6 + x7
+    cc1 = g0 + g1
+    c3 = cc1 + g2
+    cc2 = cc1 + (g2 + g3)
+    want = [x0, x0 + x1, g0 + x2, (g0 + x2) + x3, cc1 + x4, (cc1 + x4) + x5, c3 + x6,
+            (c3 + x6) + x7, cc2 + x8]
+    assert same_bits(oracle.scan(x, V=1, W=1, NW=1, A=2, A2=2), np.array(want, F32))
 
 
 @pytest.mark.parametrize("seed", range(20))
@@ -123,7 +153,7 @@ def _pw_expr(items):
     return (_pw_expr(items[:k]), _pw_expr(items[k:]))
 
 
-def _brute_exprs(n, V, W, NW, A):
+def _brute_exprs(n, V, W, NW, A, A2):
     """Expression of every forward inclusive output; leaves are indices, None = identity."""
     T = V * W * NW
 
@@ -160,11 +190,19 @@ def _brute_exprs(n, V, W, NW, A):
         return wks(j, NW - 1, DN)
 
     nt = (n + T - 1) // T
+    nq = (nt + A - 1) // A
 
-    def carry(q):
-        if q == 0:
+    def g(q):        # interval total
+        return _pw_expr([agg(jj) for jj in range(q * A, min(q * A + A, nt))])
+
+    def cc(Q):       # carry into super-interval Q
+        if Q == 0:
             return None
-        return (carry(q - 1), _pw_expr([agg(jj) for jj in range((q - 1) * A, min(q * A, nt))]))
+        return (cc(Q - 1), _pw_expr([g(qq) for qq in range((Q - 1) * A2, min(Q * A2, nq))]))
+
+    def carry(q):    # carry into interval q
+        Q = q // A2
+        return (cc(Q), _pw_expr([g(qq) for qq in range(Q * A2, q)]))
 
     out = []
     for i in range(n):
@@ -187,23 +225,25 @@ def _eval(expr, x, ident):
     return x[expr]
 
 
-@pytest.mark.parametrize("V,W,NW,A", [(2, 2, 1, 2), (1, 4, 1, 2), (3, 2, 2, 3), (2, 2, 2, 1),
-                                       (1, 1, 3, 3), (4, 3, 2, 2), (1, 2, 3, 2), (2, 4, 4, 2)])
+@pytest.mark.parametrize("V,W,NW,A,A2", [(2, 2, 1, 2, 3), (1, 4, 1, 2, 2), (3, 2, 2, 3, 1),
+                                          (2, 2, 2, 1, 4), (1, 1, 3, 3, 2), (4, 3, 2, 2, 5),
+                                          (1, 2, 3, 2, 256), (2, 4, 4, 2, 2), (1, 1, 1, 1, 3)])
 @pytest.mark.parametrize("dtype", [F32, F64])
-def test_brute_force_expressions(V, W, NW, A, dtype):
-    rng = np.random.default_rng(V * 1000 + W * 100 + NW * 10 + A)
+def test_brute_force_expressions(V, W, NW, A, A2, dtype):
+    rng = np.random.default_rng(V * 10000 + W * 1000 + NW * 100 + A * 10 + A2)
     eps = float(np.finfo(dtype).eps)
     alphabet = np.array([1.0, eps, eps / 2, -1.0, 3.0, -eps / 2, 0.75], dtype)
     ident = dtype(-0.0)
-    for n in (1, 5, V * W * NW * A + 1, 3 * V * W * NW * A + 2, 40):
-        exprs = _brute_exprs(n, V, W, NW, A)
+    for n in (1, 5, V * W * NW * A + 1, 3 * V * W * NW * A + 2, 40,
+              min(300, 2 * V * W * NW * A * A2 + 3)):
+        exprs = _brute_exprs(n, V, W, NW, A, A2)
         for trial in range(4):
             x = alphabet[rng.integers(0, alphabet.size, n)]
             want = np.array([_eval(e, x, ident) for e in exprs], dtype)
-            assert same_bits(oracle.scan(x, V=V, W=W, NW=NW, A=A), want), (n, trial)
+            assert same_bits(oracle.scan(x, V=V, W=W, NW=NW, A=A, A2=A2), want), (n, trial)
             # reverse: mirror of the forward scan of the flipped input
             wr = np.array([_eval(e, x[::-1].copy(), ident) for e in exprs], dtype)[::-1]
-            assert same_bits(oracle.scan(x, reverse=True, V=V, W=W, NW=NW, A=A), wr)
+            assert same_bits(oracle.scan(x, reverse=True, V=V, W=W, NW=NW, A=A, A2=A2), wr)
             # segmented: mask everything before the segment start with the identity
             cuts = np.sort(rng.choice(np.arange(1, n), size=min(3, max(0, n - 1)),
                                       replace=False)) if n > 1 else np.zeros(0, int)
@@ -214,7 +254,7 @@ def test_brute_force_expressions(V, W, NW, A, dtype):
                 xm[:a] = ident
                 for i in range(a, b):
                     ws[i] = _eval(exprs[i], xm, ident)
-            assert same_bits(oracle.scan(x, offsets=offs, V=V, W=W, NW=NW, A=A), ws), (n, offs)
+            assert same_bits(oracle.scan(x, offsets=offs, V=V, W=W, NW=NW, A=A, A2=A2), ws), (n, offs)
 
 
 # ---------------------------------------------------------------- textbook special cases
@@ -307,13 +347,14 @@ def test_bad_offsets_rejected():
 
 @pytest.mark.parametrize("dtype,u", [(F32, 2.0**-24), (F64, 2.0**-53)])
 def test_error_bound_against_exact_prefix(dtype, u):
-    V, W, NW, A = 4, 2, 2, 2                          # many tiles and intervals at small n
+    V, W, NW, A, A2 = 4, 2, 2, 2, 3                   # many tiles, intervals and super-intervals
     n = 3000
     x = rounding_values(n, dtype, 9)
-    y = oracle.scan(x, V=V, W=W, NW=NW, A=A)
+    y = oracle.scan(x, V=V, W=W, NW=NW, A=A, A2=A2)
     T = V * W * NW
-    nq = -(-(-(-n // T)) // A)
-    depth = V + math.ceil(math.log2(W)) + math.ceil(math.log2(NW)) + math.ceil(math.log2(A)) + nq + 5
+    nQ = -(-(-(-(-(-n // T)) // A)) // A2)
+    depth = (V + math.ceil(math.log2(W)) + math.ceil(math.log2(NW)) + math.ceil(math.log2(A))
+             + math.ceil(math.log2(A2)) + nQ + 6)
     g = depth * u / (1 - depth * u)
     acc = Fraction(0)
     absacc = 0.0
