@@ -78,13 +78,16 @@ size_t det_scan_workspace_size(int64_t n, det_dtype dtype, unsigned flags, int64
  * "Implementation"; inclusive/exclusive, forward/reverse, full/segmented per "Validation").
  *
  * Order (constants from det_spec_constants: V = 32 elements per lane, W = 64 lanes per wave,
- * 4 waves per tile, T = 8192 elements per tile, A = 256 tiles per anchor interval):
+ * 4 waves per tile, T = 8192 elements per tile, A = 256 tiles per anchor interval, A2 = 256
+ * intervals per super-interval):
  *   lane-serial prefix s over each lane's run of V elements; Kogge-Stone over the lane totals
  *   inside each wave (p = lane-exclusive prefix); Kogge-Stone over the 4 wave totals
  *   (P = wave-exclusive prefix; the last value is the tile total Agg_j); for tile j in anchor
- *   interval q: W_j = PW(Agg_{qA..j-1}), carry C_{q+1} = C_q + PW(Agg of all tiles of q),
- *   C_0 = -0.0; y = (((C_q + W_j) + P) + p) + s.  Only carries cross interval boundaries, so
- *   the bits do not depend on which predecessors a tile saw as finished.
+ *   interval q of super-interval Q: W_j = PW(Agg_{qA..j-1}); interval totals
+ *   G_q = PW(all Agg of q); WG = PW(G_{Q*A2..q-1}); super-interval carries CC_0 = -0.0,
+ *   CC_{Q+1} = CC_Q + PW(all G of Q); y = ((((CC_Q + WG) + W_j) + P) + p) + s.  Only fixed
+ *   anchors publish totals and carries, so the bits do not depend on which predecessors a tile
+ *   saw as finished.
  *
  * x, y:   device, n elements of dtype.  Inclusive scans may run in place (y == x); exclusive
  *         scans must not overlap x and y (DET_ERROR_INVALID_VALUE if the ranges overlap).
@@ -131,8 +134,8 @@ det_status det_scatter_add(const void* values, const int32_t* index, int64_t n, 
 int det_spec_version(void);
 
 /* Scan constants of this version: elements per lane, lanes per tile, tiles per anchor
- * interval (any pointer may be NULL). */
-void det_spec_constants(int64_t* V, int64_t* L, int64_t* A);
+ * interval, anchor intervals per super-interval (any pointer may be NULL). */
+void det_spec_constants(int64_t* V, int64_t* L, int64_t* A, int64_t* A2);
 
 /* Static string naming a status code. */
 const char* det_status_string(det_status s);
@@ -141,9 +144,16 @@ const char* det_status_string(det_status s);
 
 /* Not part of the stable interface.  Overrides how the work is spread over the GPU, for the
  * tests that show the bits do not depend on it: grid_wgs > 0 caps the number of workgroups
- * of the sum and scan kernels (0 = default); sum_chunk_log2 in [10, 24] sets the elements per
+ * of the sum and scan kernels (0 = default); sum_chunk_log2 in [14, 24] sets the elements per
  * sum partial (0 = default).  Process-wide; returns DET_ERROR_INVALID_VALUE when out of range. */
 det_status det_debug_set_launch(int grid_wgs, int sum_chunk_log2);
+
+/* Not part of the stable interface.  Replaces the scan's anchor constants (tiles per anchor
+ * interval A, intervals per super-interval A2; each in [1, 256], 0 = the spec's 256) so tests
+ * can exercise many intervals and super-interval carries at small n against the oracle run
+ * with the same constants.  Results then follow that variant's order, not SPEC v1.
+ * Process-wide; DET_ERROR_INVALID_VALUE when out of range. */
+det_status det_debug_set_scan_anchors(int A, int A2);
 
 #ifdef __cplusplus
 }

@@ -4,13 +4,40 @@
 // kernels never see an argument this file rejected.
 #include <string.h>
 
+#include <mutex>
+
 #include "det_internal.h"
 
 namespace det {
 
-static LaunchOverride g_override = {0, 0};
+static LaunchOverride g_override = {0, 0, 0, 0};
 
 const LaunchOverride& launch_override() { return g_override; }
+
+int64_t resident_wgs(const void* fn, int block) {
+    struct Entry {
+        int dev;
+        const void* fn;
+        int block;
+        int64_t wgs;
+    };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int used = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+        if (cache[i].dev == dev && cache[i].fn == fn && cache[i].block == block)
+            return cache[i].wgs;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int64_t wgs = (int64_t)(per_cu < 1 ? 1 : per_cu) * cus;
+    if (used < 64) cache[used++] = Entry{dev, fn, block, wgs};
+    return wgs;
+}
 
 static bool valid_dtype(det_dtype d) { return d == DET_F32 || d == DET_F64; }
 
@@ -100,10 +127,11 @@ det_status det_scatter_add(const void* values, const int32_t* index, int64_t n, 
 
 int det_spec_version(void) { return 1; }
 
-void det_spec_constants(int64_t* V, int64_t* L, int64_t* A) {
+void det_spec_constants(int64_t* V, int64_t* L, int64_t* A, int64_t* A2) {
     if (V) *V = kScanV;
     if (L) *L = kScanL;
     if (A) *A = kScanA;
+    if (A2) *A2 = kScanA2;
 }
 
 const char* det_status_string(det_status s) {
@@ -124,6 +152,13 @@ det_status det_debug_set_launch(int grid_wgs, int sum_chunk_log2) {
         return DET_ERROR_INVALID_VALUE;
     g_override.grid_wgs = grid_wgs;
     g_override.sum_chunk_log2 = sum_chunk_log2;
+    return DET_SUCCESS;
+}
+
+det_status det_debug_set_scan_anchors(int A, int A2) {
+    if (A < 0 || A > kScanA || A2 < 0 || A2 > kScanA2) return DET_ERROR_INVALID_VALUE;
+    g_override.scan_A = A;
+    g_override.scan_A2 = A2;
     return DET_SUCCESS;
 }
 

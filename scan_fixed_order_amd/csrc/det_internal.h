@@ -13,6 +13,8 @@ namespace det {
 struct LaunchOverride {
     int grid_wgs;
     int sum_chunk_log2;
+    int scan_A;    // test-only scan anchor constants (0 = the spec's)
+    int scan_A2;
 };
 const LaunchOverride& launch_override();
 
@@ -31,6 +33,7 @@ constexpr int kScanWaves = 4;    // waves per tile
 constexpr int kScanL = kScanW * kScanWaves;   // lanes per tile
 constexpr int kScanT = kScanV * kScanL;       // elements per tile
 constexpr int kScanA = 256;      // tiles per anchor interval
+constexpr int kScanA2 = 256;     // anchor intervals per super-interval
 
 size_t scan_workspace(int64_t n, det_dtype dt, unsigned flags, int64_t num_segments);
 det_status scan_launch(const void* x, void* y, int64_t n, det_dtype dt, unsigned flags,
@@ -42,6 +45,10 @@ size_t scatter_workspace(int64_t n, int64_t num_out, int64_t row_len, det_dtype 
 det_status scatter_launch(const void* values, const int32_t* index, int64_t n, int64_t row_len,
                           det_dtype dt, void* out, int64_t num_out, void* prev, int64_t* n_skipped,
                           void* ws, size_t ws_bytes, hipStream_t s);
+
+// Workgroups of `block` threads of kernel `fn` that are resident on the current device at once
+// (occupancy x compute units), cached per device and kernel; 0 if the runtime cannot tell.
+int64_t resident_wgs(const void* fn, int block);
 
 inline det_status launch_status() {
     return hipGetLastError() == hipSuccess ? DET_SUCCESS : DET_ERROR_LAUNCH;

@@ -10,16 +10,20 @@
 //   Agg_j  the tile total (last wave-level value), published at once;
 //   W_j    PW(Agg_{qA} .. Agg_{j-1}) over the earlier tiles of the same anchor interval
 //          q = j / 256 (each of 256 threads reads one predecessor's status slot);
-//   C_q    carry into interval q: C_0 = -0.0, C_{q+1} = C_q + PW(all 256 Agg of interval q),
-//          published only by the last tile of interval q (the anchor);
-//   y      (((C_q + W_j) + P) + p) + s.
+//   G_q    PW(all 256 Agg of interval q), published by the interval's last tile (its anchor),
+//          which needs nothing from earlier intervals;
+//   WG     PW(G_{Q*256} .. G_{q-1}) over the earlier intervals of super-interval Q = q / 256;
+//   CC_Q   carry into super-interval Q: CC_0 = -0.0, CC_{Q+1} = CC_Q + PW(all 256 G of Q),
+//          published by the super-interval's last tile; the only serial chain, one link per
+//          2^29 elements;
+//   y      ((((CC_Q + WG) + W_j) + P) + p) + s.
 // A tile never reads an inclusive prefix of a non-anchor predecessor, so whether a
 // predecessor was seen as finished or not cannot change the association order.
 //
 // Status slots are 64-bit words (tag << 32 | payload): tag bit 0 = ready, bit 1 = segment
 // head seen; f64 payloads take two words, each carrying the tag.  Every word validates itself,
 // so relaxed agent-scope atomics suffice and no fence is needed.  The slots and the tile
-// ticket are cleared by a small kernel before each scan.
+// counters are cleared by a small kernel before each scan.
 //
 // Segmented scans run the pair operator (f1 | f2, f2 ? b : a + b) through the same dataflow;
 // head flags of a tile come from a workgroup-parallel search of the offsets.  Reverse scans
@@ -33,9 +37,10 @@ namespace {
 
 constexpr int kV = kScanV;
 constexpr int kT = kScanT;
-constexpr int kA = kScanA;
+
 constexpr int kWaveElems = kScanV * kScanW;                 // 2048
-constexpr int kStage = kWaveElems + kWaveElems / 32;        // one spare LDS slot per 32
+constexpr int kHalf = kWaveElems / 2;                       // elements staged at a time
+constexpr int kStage = kHalf + kHalf / 32;                  // one spare LDS slot per 32
 constexpr int kHeadWords = kT / 32 + 1;                     // bits for positions [F0, F0 + T]
 
 constexpr uint32_t kReady = 1u;
@@ -103,6 +108,16 @@ __device__ __forceinline__ uint64_t wait_word(uint64_t* w, uint32_t* err) {
 }
 
 template <typename T>
+__device__ __forceinline__ Seg<T> unpack(uint64_t w0, uint64_t w1) {
+    if constexpr (sizeof(T) == 4) {
+        return Seg<T>{__uint_as_float((uint32_t)w0), (uint32_t)(w0 >> 33) & 1u};
+    } else {
+        const uint64_t b = (w1 << 32) | (w0 & 0xffffffffull);
+        return Seg<T>{__longlong_as_double((long long)b), (uint32_t)(w0 >> 33) & 1u};
+    }
+}
+
+template <typename T>
 __device__ __forceinline__ Seg<T> wait_slot(uint64_t* slot, uint32_t* err) {
     if constexpr (sizeof(T) == 4) {
         const uint64_t w = wait_word(slot, err);
@@ -113,6 +128,59 @@ __device__ __forceinline__ Seg<T> wait_slot(uint64_t* slot, uint32_t* err) {
         const uint64_t b = (w1 << 32) | (w0 & 0xffffffffull);
         return Seg<T>{__longlong_as_double((long long)b), (uint32_t)(w0 >> 33) & 1u};
     }
+}
+
+// Status polls in two halves, so the first round trip can overlap other memory traffic:
+// poll_issue loads up to two slots (unused ones read as ready), poll_finish re-polls the words
+// that were not ready yet (bounded) and unpacks the values.
+template <typename T>
+struct Poll {
+    uint64_t w[2 * slot_words<T>()];
+};
+
+template <typename T>
+__device__ __forceinline__ void poll_issue(Poll<T>& pl, const uint64_t* s1, bool use1,
+                                           const uint64_t* s2, bool use2) {
+    constexpr int SW = slot_words<T>();
+    constexpr uint64_t kDone = (uint64_t)kReady << 32;
+#pragma unroll
+    for (int i = 0; i < SW; ++i) {
+        pl.w[i] = use1 ? __hip_atomic_load(s1 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : kDone;
+        pl.w[SW + i] = use2 ? __hip_atomic_load(s2 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : kDone;
+    }
+}
+
+__device__ __forceinline__ void repoll(uint64_t& w, const uint64_t* slot) {
+    if (!((w >> 32) & kReady)) w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ void poll_finish(Poll<T>& pl, const uint64_t* s1, bool use1, Seg<T>& v1,
+                                            const uint64_t* s2, bool use2, Seg<T>& v2,
+                                            uint32_t* err) {
+    constexpr int SW = slot_words<T>();
+    uint32_t spins = 0;
+    for (;;) {
+        bool all = true;
+#pragma unroll
+        for (int i = 0; i < 2 * SW; ++i) all = all && ((pl.w[i] >> 32) & kReady);
+        if (all) break;
+        if (++spins > kSpinLimit) {
+            __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        repoll(pl.w[0], s1);
+        repoll(pl.w[SW], s2);
+        if constexpr (SW == 2) {
+            repoll(pl.w[1], s1 + 1);
+            repoll(pl.w[3], s2 + 1);
+        }
+    }
+    if (use1) v1 = unpack<T>(pl.w[0], SW == 2 ? pl.w[1] : 0ull);
+    if (use2) v2 = unpack<T>(pl.w[SW], SW == 2 ? pl.w[SW + 1] : 0ull);
 }
 
 // ---------------------------------------------------------------- cross-lane pieces
@@ -202,85 +270,127 @@ __device__ void build_heads(const int64_t* __restrict__ offs, int64_t nseg, int6
 
 // ---------------------------------------------------------------- wave load / store
 
+// Vector types for 16-byte accesses with non-temporal hints (streaming data is touched once).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
 template <typename T>
-__device__ __forceinline__ void load_wave(const T* __restrict__ x, int64_t n, bool rev, int64_t fw,
-                                          T* st, int lane) {
-    const bool vec = !rev && (fw + kWaveElems <= n) &&
-                     ((reinterpret_cast<uintptr_t>(x + fw) & 15) == 0);
+__device__ __forceinline__ bool aligned16(const T* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+}
+
+// Lane t's run (flipped positions f0 .. f0 + 31, f0 = fw + 32 t) straight into registers: each
+// lane reads its own 128 (f32) or 256 (f64) contiguous bytes.  Identity past n.  `vec` (uniform)
+// selects 16-byte loads; it requires the whole wave in range and 16-byte aligned runs.  No
+// streaming hint here: consecutive loads of a lane share cache lines.
+template <typename T, bool REV>
+__device__ __forceinline__ void load_run(const T* __restrict__ x, int64_t n, int64_t fw, bool vec,
+                                         T (&r)[kV], int lane) {
+    const int64_t f0 = fw + (int64_t)lane * kV;
     if (vec) {
+        // forward: run = x[f0 .. f0 + 32); reverse: original x[n - f0 - 32 .. n - f0) backwards
+        const T* p = REV ? x + (n - f0 - kV) : x + f0;
         if constexpr (sizeof(T) == 4) {
 #pragma unroll
-            for (int r = 0; r < kWaveElems / 256; ++r) {
-                const int e = r * 256 + 4 * lane;
-                const float4 q = *reinterpret_cast<const float4*>(x + fw + e);
-                const int a = pad(e);
-                st[a] = q.x; st[a + 1] = q.y; st[a + 2] = q.z; st[a + 3] = q.w;
+            for (int i = 0; i < kV / 4; ++i) {
+                const f32x4 q = reinterpret_cast<const f32x4*>(p)[i];
+                if (REV) {
+                    r[kV - 1 - 4 * i] = q.x; r[kV - 2 - 4 * i] = q.y;
+                    r[kV - 3 - 4 * i] = q.z; r[kV - 4 - 4 * i] = q.w;
+                } else {
+                    r[4 * i] = q.x; r[4 * i + 1] = q.y; r[4 * i + 2] = q.z; r[4 * i + 3] = q.w;
+                }
             }
         } else {
 #pragma unroll
-            for (int r = 0; r < kWaveElems / 128; ++r) {
-                const int e = r * 128 + 2 * lane;
-                const double2 q = *reinterpret_cast<const double2*>(x + fw + e);
-                const int a = pad(e);
-                st[a] = q.x; st[a + 1] = q.y;
+            for (int i = 0; i < kV / 2; ++i) {
+                const f64x2 q = reinterpret_cast<const f64x2*>(p)[i];
+                if (REV) {
+                    r[kV - 1 - 2 * i] = q.x; r[kV - 2 - 2 * i] = q.y;
+                } else {
+                    r[2 * i] = q.x; r[2 * i + 1] = q.y;
+                }
             }
         }
     } else {
-#pragma unroll 8
-        for (int r = 0; r < kWaveElems / 64; ++r) {
-            const int e = r * 64 + lane;
-            const int64_t f = fw + e;
-            st[pad(e)] = (f < n) ? x[rev ? n - 1 - f : f] : ident<T>();
+#pragma unroll
+        for (int k = 0; k < kV; ++k) {
+            const int64_t f = f0 + k;
+            r[k] = (f < n) ? x[REV ? n - 1 - f : f] : ident<T>();
         }
     }
 }
 
-template <typename T, bool SEG>
-__device__ __forceinline__ void store_wave(T* __restrict__ y, int64_t n, bool rev, bool excl,
-                                           int64_t F0, int64_t fw, const T* st,
-                                           const uint32_t* s_heads, int lane) {
-    if (!excl) {
-        const bool vec = !rev && (fw + kWaveElems <= n) &&
-                         ((reinterpret_cast<uintptr_t>(y + fw) & 15) == 0);
-        if (vec) {
-            if constexpr (sizeof(T) == 4) {
+template <typename T>
+__device__ __forceinline__ void nt_store4(T* p, T a, T b, T c, T d) {
+    if constexpr (sizeof(T) == 4) {
+        f32x4 v = {a, b, c, d};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+    } else {
+        f64x2 v0 = {a, b}, v1 = {c, d};
+        __builtin_nontemporal_store(v0, reinterpret_cast<f64x2*>(p));
+        __builtin_nontemporal_store(v1, reinterpret_cast<f64x2*>(p) + 1);
+    }
+}
+
+// Half h of the wave's results (flipped positions hw .. hw + 1023, hw = fw + 1024 h) from the
+// LDS stage to y with coalesced stores: 16-byte non-temporal stores where the whole half is in
+// range and aligned, otherwise 4- or 8-byte stores.
+template <typename T, bool REV>
+__device__ __forceinline__ void store_half(T* __restrict__ y, int64_t n, int64_t fw, int h,
+                                           const T* st, int lane) {
+    const int64_t hw = fw + h * kHalf;
+    const bool full = hw + kHalf <= n;
+    T* base = REV ? y + (n - hw - kHalf) : y + hw;   // lowest original index of the half
+    if (full && aligned16(base)) {
 #pragma unroll
-                for (int r = 0; r < kWaveElems / 256; ++r) {
-                    const int e = r * 256 + 4 * lane;
-                    const int a = pad(e);
-                    *reinterpret_cast<float4*>(y + fw + e) =
-                        make_float4(st[a], st[a + 1], st[a + 2], st[a + 3]);
-                }
+        for (int r = 0; r < kHalf / 256; ++r) {
+            const int o = r * 256 + 4 * lane;            // original offset within the half
+            if (REV) {
+                const int e = (kHalf - 1) - o;          // flipped element of original offset o
+                nt_store4<T>(base + o, st[pad(e)], st[pad(e - 1)], st[pad(e - 2)], st[pad(e - 3)]);
             } else {
-#pragma unroll
-                for (int r = 0; r < kWaveElems / 128; ++r) {
-                    const int e = r * 128 + 2 * lane;
-                    const int a = pad(e);
-                    *reinterpret_cast<double2*>(y + fw + e) = make_double2(st[a], st[a + 1]);
-                }
-            }
-        } else {
-#pragma unroll 8
-            for (int r = 0; r < kWaveElems / 64; ++r) {
-                const int e = r * 64 + lane;
-                const int64_t f = fw + e;
-                if (f < n) y[rev ? n - 1 - f : f] = st[pad(e)];
+                const int a = pad(o);
+                nt_store4<T>(base + o, st[a], st[a + 1], st[a + 2], st[a + 3]);
             }
         }
+    } else if (full) {
+#pragma unroll
+        for (int r = 0; r < kHalf / 64; ++r) {
+            const int o = r * 64 + lane;
+            base[o] = st[pad(REV ? (kHalf - 1) - o : o)];
+        }
     } else {
-        // inclusive value of position f goes to position f + 1; +0.0 at segment heads
+        const int64_t left = n - hw;
+        const int valid = left < 0 ? 0 : (int)left;
 #pragma unroll 8
-        for (int r = 0; r < kWaveElems / 64; ++r) {
+        for (int r = 0; r < kHalf / 64; ++r) {
             const int e = r * 64 + lane;
-            const int64_t f = fw + e + 1;
-            if (f < n) {
-                T v = st[pad(e)];
-                if constexpr (SEG) {
-                    const int bit = (int)(f - F0);
-                    if ((s_heads[bit >> 5] >> (bit & 31)) & 1u) v = T(0.0);
-                }
-                y[rev ? n - 1 - f : f] = v;
+            if (e < valid) y[REV ? (n - 1 - hw) - e : hw + e] = st[pad(e)];
+        }
+    }
+}
+
+// Exclusive scans: the inclusive value of flipped position f goes to f + 1 (+0.0 at heads).
+template <typename T, bool SEG, bool REV>
+__device__ __forceinline__ void store_half_excl(T* __restrict__ y, int64_t n, int64_t F0,
+                                                int64_t fw, int h, const T* st,
+                                                const uint32_t* s_heads, int lane) {
+    const int64_t hw = fw + h * kHalf;
+    const int64_t left = n - (hw + 1);
+    const int valid = left < 0 ? 0 : (left < kHalf ? (int)left : kHalf);
+    T* yb = REV ? y + (n - 2 - hw) : y + (hw + 1);
+#pragma unroll 8
+    for (int r = 0; r < kHalf / 64; ++r) {
+        const int e = r * 64 + lane;
+        if (e < valid) {
+            T v = st[pad(e)];
+            if constexpr (SEG) {
+                const int bit = (int)(hw + e + 1 - F0);
+                if ((s_heads[bit >> 5] >> (bit & 31)) & 1u) v = T(0.0);
             }
+            if (REV) yb[-e] = v;
+            else yb[e] = v;
         }
     }
 }
@@ -294,118 +404,261 @@ struct ScanArgs {
     int64_t n;
     const int64_t* offs;
     int64_t nseg;
-    uint64_t* agg;       // slot_words<T>() words per tile
-    uint64_t* carry;     // slot_words<T>() words per interval boundary
-    uint32_t* ticket;    // [0] tile ticket, [1] error word (a wait hit the spin bound)
+    uint64_t* agg;       // slot_words<T>() words per tile: tile totals
+    uint64_t* gtot;      // slot_words<T>() words per anchor interval: interval totals
+    uint64_t* carry;     // slot_words<T>() words per super-interval boundary: carries
+    uint32_t* ticket;    // kCounters tile counters, kCounterStride words apart
+    uint32_t* err;       // raised when a wait hit the spin bound
     int ntiles;
+    int nctr;            // tile counters in use: min(kCounters, grid)
     int rev;
     int excl;
+    int A;               // tiles per anchor interval (the spec's 256; smaller only in tests)
+    int A2;              // intervals per super-interval (likewise)
 };
 
-template <typename T, bool SEG>
+// Local part of one tile once its runs are in registers: segment heads, lane-serial prefixes
+// (left in r), in-wave and wave-level Kogge-Stone; returns the tile total.
+template <typename T, bool SEG, bool REV>
+__device__ __forceinline__ Seg<T> tile_local(const ScanArgs<T>& a, int j, T (&r)[kV], uint32_t& hb,
+                                             Seg<T>& P, Seg<T>& p, uint32_t* s_heads,
+                                             Seg<T>* s_wtot, int tid, int lane, int wave) {
+    const int64_t F0 = (int64_t)j * kT;
+    if constexpr (SEG) {
+        build_heads(a.offs, a.nseg, a.n, REV, F0, s_heads, tid);
+        hb = s_heads[wave * 64 + lane];
+    } else {
+        hb = 0u;
+    }
+
+    // lane-serial prefix
+#pragma unroll
+    for (int k = 1; k < kV; ++k) {
+        if (SEG && ((hb >> k) & 1u)) continue;
+        r[k] = r[k - 1] + r[k];
+    }
+    Seg<T> u{r[kV - 1], hb != 0u ? 1u : 0u};
+
+    // Kogge-Stone over the lane totals of the wave
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+        Seg<T> o{shfl_up(u.v, d, lane), SEG ? shfl_up(u.f, d, lane) : 0u};
+        if (lane >= d) u = op<SEG>(o, u);
+    }
+    p = Seg<T>{shfl_up(u.v, 1, lane), SEG ? shfl_up(u.f, 1, lane) : 0u};
+    if (lane == 0) p = seg_ident<T>();
+
+    // Kogge-Stone over the 4 wave totals
+    if (lane == 63) s_wtot[wave] = u;
+    __syncthreads();
+    const Seg<T> w0 = s_wtot[0], w1 = s_wtot[1], w2 = s_wtot[2], w3 = s_wtot[3];
+    const Seg<T> o1 = op<SEG>(w0, w1), o2 = op<SEG>(w1, w2), o3 = op<SEG>(w2, w3);
+    const Seg<T> om2 = op<SEG>(w0, o2), om3 = op<SEG>(o1, o3);
+    P = wave == 0 ? seg_ident<T>() : wave == 1 ? w0 : wave == 2 ? o1 : om2;
+    return om3;
+}
+
+// Runs of the wave's part of tile j into registers (vector loads when the wave is whole and
+// aligned, else element loads with identity past n).
+template <typename T, bool REV>
+__device__ __forceinline__ void load_tile(const ScanArgs<T>& a, int j, int wave, T (&r)[kV],
+                                          int lane) {
+    const int64_t fw = (int64_t)j * kT + (int64_t)wave * kWaveElems;
+    const int64_t reg0 = REV ? a.n - fw - kWaveElems : fw;   // lowest original index
+    const bool vec = (fw + kWaveElems <= a.n) && aligned16(a.x + reg0);
+    load_run<T, REV>(a.x, a.n, fw, vec, r, lane);
+}
+
+// Where tile j's look-back polls go: the earlier tile totals of its anchor interval and the
+// earlier interval totals of its super-interval.
+struct LookBack {
+    int q, cnt, Q, qcnt;
+};
+
+__device__ __forceinline__ LookBack look_back_of(int j, int A, int A2) {
+    LookBack lb;
+    lb.q = j / A;
+    lb.cnt = j - lb.q * A;
+    lb.Q = lb.q / A2;
+    lb.qcnt = lb.q - lb.Q * A2;
+    return lb;
+}
+
+template <typename T>
+__device__ __forceinline__ void issue_look_back(const ScanArgs<T>& a, const LookBack& lb,
+                                                Poll<T>& pl, int tid) {
+    constexpr int SW = slot_words<T>();
+    poll_issue<T>(pl, a.agg + (size_t)(lb.q * a.A + tid) * SW, tid < lb.cnt,
+                  a.gtot + (size_t)(lb.Q * a.A2 + tid) * SW, tid < lb.qcnt);
+}
+
+// Everything after tile j's local part: finish the look-back, publish the interval total (the
+// interval's last tile) and forward the super-interval carry (its last tile), combine the tile
+// with its prefix and store it through the wave's LDS stage in two halves.
+template <typename T, bool SEG, bool REV, bool EXCL>
+__device__ __forceinline__ void finish_tile(const ScanArgs<T>& a, int j, const LookBack& lb,
+                                            Poll<T>& pl, T (&r)[kV], uint32_t hb, Seg<T> P,
+                                            Seg<T> p, Seg<T> agg, Seg<T>* s_tmp, Seg<T>& s_carry,
+                                            const uint32_t* s_heads, T* st, int tid, int lane,
+                                            int wave) {
+    constexpr int SW = slot_words<T>();
+    uint32_t* err = a.err;
+    Seg<T> mine = seg_ident<T>(), gmine = seg_ident<T>();
+    poll_finish<T>(pl, a.agg + (size_t)(lb.q * a.A + tid) * SW, tid < lb.cnt, mine,
+                   a.gtot + (size_t)(lb.Q * a.A2 + tid) * SW, tid < lb.qcnt, gmine, err);
+    const Seg<T> Wj = block_pw<SEG, T>(mine, lane, wave, s_tmp);
+    // the interval's last tile publishes the interval total G_q (needs no carry)
+    const bool ianchor = (lb.cnt == a.A - 1) && (j + 1 < a.ntiles);
+    Seg<T> Gq = seg_ident<T>();
+    if (ianchor) {
+        Gq = block_pw<SEG, T>(tid == a.A - 1 ? agg : mine, lane, wave, s_tmp);
+        if (tid == 0) publish<T>(a.gtot + (size_t)lb.q * SW, Gq);
+    }
+    const Seg<T> WG = block_pw<SEG, T>(gmine, lane, wave, s_tmp);
+    const bool sanchor = ianchor && (lb.qcnt == a.A2 - 1);
+    Seg<T> H = seg_ident<T>();
+    if (sanchor) H = block_pw<SEG, T>(tid == a.A2 - 1 ? Gq : gmine, lane, wave, s_tmp);
+
+    // carry into the super-interval; its last tile forwards the next one
+    if (tid == 0) {
+        const Seg<T> CC =
+            (lb.Q == 0) ? seg_ident<T>() : wait_slot<T>(a.carry + (size_t)lb.Q * SW, err);
+        if (sanchor) publish<T>(a.carry + (size_t)(lb.Q + 1) * SW, op<SEG>(CC, H));
+        s_carry = CC;
+    }
+    __syncthreads();
+    const Seg<T> E = op<SEG>(op<SEG>(s_carry, WG), Wj);
+    const Seg<T> X = op<SEG>(op<SEG>(E, P), p);
+
+    // combine (lane index re-derived so stage addresses are recomputed here, not kept live)
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int k = 0; k < kV; ++k) {
+        if constexpr (SEG) {
+            const uint32_t upto = (k == 31) ? hb : (hb & ((2u << k) - 1u));
+            if (!upto) r[k] = X.v + r[k];
+        } else {
+            r[k] = X.v + r[k];
+        }
+    }
+    const int64_t F0 = (int64_t)j * kT;
+    const int64_t fw = F0 + (int64_t)wave * kWaveElems;
+    const int rb = (lane & 31) * 33;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if ((lane >> 5) == h) {
+#pragma unroll
+            for (int k = 0; k < kV; ++k) st[rb + k] = r[k];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (!EXCL)
+            store_half<T, REV>(a.y, a.n, fw, h, st, lane);
+        else
+            store_half_excl<T, SEG, REV>(a.y, a.n, F0, fw, h, st, s_heads, lane);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    if (EXCL && j == 0 && tid == 0) a.y[REV ? a.n - 1 : 0] = T(0.0);
+}
+
+// Tiles are claimed from nc <= kCounters counters (nc <= the grid), one per 256-byte line:
+// workgroup b draws from counter c = b mod nc, whose k-th claim is tile k * nc + c.  One
+// counter would serialise every claim on a single address (about 87 claims per microsecond on
+// this chip, well below the tile rate at full bandwidth).  Each counter's tiles are claimed in
+// order, and workgroups 0 .. nc-1, the first on their counters, are dispatched no later than
+// any other workgroup of their counter, so every counter keeps a running workgroup until its
+// tiles run out and every tile a workgroup waits on is, or will be, claimed by one.
+constexpr int kCounters = 8;
+constexpr int kCounterStride = 64;   // words between counters
+
+__device__ __forceinline__ int claim_tile(uint32_t* counters, int c, int nc) {
+    const uint32_t k = __hip_atomic_fetch_add(counters + c * kCounterStride, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    return (int)k * nc + c;
+}
+
+// Persistent workgroups, two tiles in flight each.  Per iteration: the loads of the next tile,
+// the claim of the tile after it and the current tile's first look-back polls share one round
+// trip; the next tile's local part runs and its total is published; the current tile finishes
+// its look-back and is stored; only then is the claimed tile number needed, so the claim's
+// latency hides behind the whole iteration.  A tile's total is published a whole iteration
+// before its workgroup waits on anything.  A workgroup only waits on smaller tiles, which are
+// claimed in counter order by running workgroups that finish them without waiting on it, so
+// every wait ends.
+template <typename T, bool SEG, bool REV, bool EXCL>
 __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     __shared__ T s_stage[kScanWaves][kStage];
-    __shared__ uint32_t s_heads[SEG ? kHeadWords : 1];
+    __shared__ uint32_t s_heads[2][SEG ? kHeadWords : 1];
     __shared__ Seg<T> s_tmp[kScanWaves];
     __shared__ Seg<T> s_wtot[kScanWaves];
     __shared__ Seg<T> s_carry;
-    __shared__ int s_tile;
+    __shared__ int s_tick[2];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    const int lane0 = tid & 63;
     const int wave = tid >> 6;
     constexpr int SW = slot_words<T>();
-    const bool rev = a.rev != 0;
+    T* st = s_stage[wave];
+
+    const int ctr = (int)(blockIdx.x % (unsigned)a.nctr);
+    if (tid == 0) s_tick[0] = claim_tile(a.ticket, ctr, a.nctr);
+    __syncthreads();
+    int cur = s_tick[0];
+    if (cur >= a.ntiles) return;
+    T r[kV];
+    load_tile<T, REV>(a, cur, wave, r, lane0);
+    uint32_t hb;
+    Seg<T> P, p;
+    Seg<T> agg = tile_local<T, SEG, REV>(a, cur, r, hb, P, p, s_heads[0], s_wtot, tid, lane0, wave);
+    if (tid == 0) {
+        publish<T>(a.agg + (size_t)cur * SW, agg);
+        s_tick[1] = claim_tile(a.ticket, ctr, a.nctr);
+    }
+    LookBack lb = look_back_of(cur, a.A, a.A2);
+    Poll<T> pl;
+    int par = 1;   // s_tick[par] holds the next tile; s_heads[par ^ 1] holds cur's heads
 
     for (;;) {
-        if (tid == 0)
-            s_tile = (int)__hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+        // Re-derive the lane index each iteration so per-lane addresses are recomputed instead
+        // of being held live across the loop (register pressure decides occupancy).
+        int lane = lane0;
+        asm volatile("" : "+v"(lane));
         __syncthreads();
-        const int j = s_tile;
-        if (j >= a.ntiles) break;
-        const int64_t F0 = (int64_t)j * kT;
-        const int64_t fw = F0 + (int64_t)wave * kWaveElems;
-        T* st = s_stage[wave];
+        const int nxt = s_tick[par];
+        const bool more = nxt < a.ntiles;
 
-        if constexpr (SEG) build_heads(a.offs, a.nseg, a.n, rev, F0, s_heads, tid);
-
-        // ---- load the wave's 2048 elements, then each lane takes its run of 32
-        load_wave<T>(a.x, a.n, rev, fw, st, lane);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        T r[kV];
-#pragma unroll
-        for (int k = 0; k < kV; ++k) r[k] = st[lane * 33 + k];
-        const uint32_t hb = SEG ? s_heads[wave * 64 + lane] : 0u;
-
-        // ---- lane-serial prefix
-#pragma unroll
-        for (int k = 1; k < kV; ++k) {
-            if (SEG && ((hb >> k) & 1u)) continue;
-            r[k] = r[k - 1] + r[k];
+        T rn[kV];
+        int claimed = 0;
+        if (more) {
+            load_tile<T, REV>(a, nxt, wave, rn, lane);
+            if (tid == 0) claimed = claim_tile(a.ticket, ctr, a.nctr);
         }
-        Seg<T> u{r[kV - 1], hb != 0u ? 1u : 0u};
-
-        // ---- Kogge-Stone over the lane totals of the wave
-#pragma unroll
-        for (int d = 1; d < 64; d *= 2) {
-            Seg<T> o{shfl_up(u.v, d, lane), SEG ? shfl_up(u.f, d, lane) : 0u};
-            if (lane >= d) u = op<SEG>(o, u);
-        }
-        Seg<T> p{shfl_up(u.v, 1, lane), SEG ? shfl_up(u.f, 1, lane) : 0u};
-        if (lane == 0) p = seg_ident<T>();
-
-        // ---- Kogge-Stone over the 4 wave totals
-        if (lane == 63) s_wtot[wave] = u;
-        __syncthreads();
-        const Seg<T> w0 = s_wtot[0], w1 = s_wtot[1], w2 = s_wtot[2], w3 = s_wtot[3];
-        const Seg<T> o1 = op<SEG>(w0, w1), o2 = op<SEG>(w1, w2), o3 = op<SEG>(w2, w3);
-        const Seg<T> om1 = o1, om2 = op<SEG>(w0, o2), om3 = op<SEG>(o1, o3);
-        const Seg<T> P = wave == 0 ? seg_ident<T>() : wave == 1 ? w0 : wave == 2 ? om1 : om2;
-        const Seg<T> agg = om3;
-
-        // ---- publish this tile's total
-        if (tid == 0) publish<T>(a.agg + (size_t)j * SW, agg);
-
-        // ---- look-back inside the anchor interval
-        const int q = j / kA;
-        const int cnt = j - q * kA;
-        Seg<T> mine = seg_ident<T>();
-        if (tid < cnt) mine = wait_slot<T>(a.agg + (size_t)(q * kA + tid) * SW, a.ticket + 1);
-        const Seg<T> Wj = block_pw<SEG, T>(mine, lane, wave, s_tmp);
-        const bool anchor = (cnt == kA - 1) && (j + 1 < a.ntiles);
-        Seg<T> G = seg_ident<T>();
-        if (anchor) G = block_pw<SEG, T>(tid == kA - 1 ? agg : mine, lane, wave, s_tmp);
-
-        // ---- carry into the interval; the anchor forwards the next one
-        if (tid == 0) {
-            const Seg<T> C = (q == 0) ? seg_ident<T>() : wait_slot<T>(a.carry + (size_t)q * SW, a.ticket + 1);
-            if (anchor) publish<T>(a.carry + (size_t)(q + 1) * SW, op<SEG>(C, G));
-            s_carry = C;
-        }
-        __syncthreads();
-        const Seg<T> E = op<SEG>(s_carry, Wj);
-        const Seg<T> X = op<SEG>(op<SEG>(E, P), p);
-
-        // ---- combine and stage the results
-#pragma unroll
-        for (int k = 0; k < kV; ++k) {
-            if constexpr (SEG) {
-                const uint32_t upto = (k == 31) ? hb : (hb & ((2u << k) - 1u));
-                if (!upto) r[k] = X.v + r[k];
-            } else {
-                r[k] = X.v + r[k];
+        issue_look_back<T>(a, lb, pl, tid);
+        uint32_t hbn = 0;
+        Seg<T> Pn = seg_ident<T>(), pn = seg_ident<T>(), aggn = seg_ident<T>();
+        if (more) {
+            aggn = tile_local<T, SEG, REV>(a, nxt, rn, hbn, Pn, pn, s_heads[par], s_wtot, tid,
+                                           lane, wave);
+            if (tid == 0) {
+                publish<T>(a.agg + (size_t)nxt * SW, aggn);
             }
-            st[lane * 33 + k] = r[k];
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        store_wave<T, SEG>(a.y, a.n, rev, a.excl != 0, F0, fw, st, s_heads, lane);
-        if (a.excl && j == 0 && tid == 0) a.y[rev ? a.n - 1 : 0] = T(0.0);
-        __syncthreads();
+        finish_tile<T, SEG, REV, EXCL>(a, cur, lb, pl, r, hb, P, p, agg, s_tmp, s_carry,
+                                       s_heads[par ^ 1], st, tid, lane, wave);
+        if (!more) break;
+        if (tid == 0) s_tick[par ^ 1] = claimed;
+#pragma unroll
+        for (int k = 0; k < kV; ++k) r[k] = rn[k];
+        hb = hbn;
+        P = Pn;
+        p = pn;
+        agg = aggn;
+        lb = look_back_of(nxt, a.A, a.A2);
+        cur = nxt;
+        par ^= 1;
     }
 }
 
@@ -415,19 +668,32 @@ __global__ void k_zero_words(uint64_t* p, int64_t nwords) {
         p[i] = 0ull;
 }
 
+// Workspace header: the tile counters, then the error word, each on its own line.
+constexpr size_t kHeader = (size_t)(kCounters * kCounterStride * 4) + 256;
+
 struct Layout {
-    int64_t ntiles, nq;
-    size_t agg_off, carry_off, total;
+    int64_t ntiles, nq, nQ;
+    size_t agg_off, g_off, carry_off, used, total;
 };
 
-Layout layout(int64_t n, det_dtype dt) {
+// Slots for tile totals, interval totals and super-interval carries.  The reservation assumes
+// the smallest anchors (A = A2 = 1) so the test hook never needs a larger workspace; only the
+// part the current constants use is cleared.
+Layout layout(int64_t n, det_dtype dt, int A, int A2) {
     Layout L;
     const size_t sw = dt == DET_F64 ? 2 : 1;
     L.ntiles = (n + kT - 1) / kT;
-    L.nq = (L.ntiles + kA - 1) / kA;
-    L.agg_off = 256;
-    L.carry_off = L.agg_off + round_up((size_t)L.ntiles * sw * 8, 256);
-    L.total = L.carry_off + round_up((size_t)(L.nq + 1) * sw * 8, 256);
+    L.nq = (L.ntiles + A - 1) / A;
+    L.nQ = (L.nq + A2 - 1) / A2;
+    const size_t tile_bytes = round_up((size_t)L.ntiles * sw * 8, 256);
+    const size_t worst = round_up((size_t)(L.ntiles + 1) * sw * 8, 256);
+    L.agg_off = kHeader;
+    L.g_off = L.agg_off + tile_bytes;
+    L.carry_off = L.g_off + tile_bytes;
+    L.used = L.carry_off + round_up((size_t)(L.nQ + 1) * sw * 8, 256);
+    L.total = L.carry_off + worst;
+    // the cleared range must cover the interval totals in use as well
+    (void)L.nq;
     return L;
 }
 
@@ -435,8 +701,11 @@ template <typename T>
 det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t* offs,
                      int64_t nseg, char* ws, hipStream_t s) {
     if (n == 0) return DET_SUCCESS;
-    const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32);
-    const int64_t words = (int64_t)(L.total / 8);
+    const LaunchOverride& ov = launch_override();
+    const int A = ov.scan_A ? ov.scan_A : kScanA;
+    const int A2 = ov.scan_A2 ? ov.scan_A2 : kScanA2;
+    const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32, A, A2);
+    const int64_t words = (int64_t)(L.used / 8);
     int zg = (int)((words + 255) / 256);
     if (zg > 1024) zg = 1024;
     k_zero_words<<<zg, 256, 0, s>>>(reinterpret_cast<uint64_t*>(ws), words);
@@ -449,18 +718,37 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     a.offs = offs;
     a.nseg = nseg;
     a.agg = reinterpret_cast<uint64_t*>(ws + L.agg_off);
+    a.gtot = reinterpret_cast<uint64_t*>(ws + L.g_off);
     a.carry = reinterpret_cast<uint64_t*>(ws + L.carry_off);
     a.ticket = reinterpret_cast<uint32_t*>(ws);
+    a.err = reinterpret_cast<uint32_t*>(ws + kCounters * kCounterStride * 4);
     a.ntiles = (int)L.ntiles;
     a.rev = (flags & DET_SCAN_REVERSE) ? 1 : 0;
     a.excl = (flags & DET_SCAN_EXCLUSIVE) ? 1 : 0;
-    int64_t grid = L.ntiles;
-    const LaunchOverride& ov = launch_override();
+    a.A = A;
+    a.A2 = A2;
+    const int mode = (offs ? 4 : 0) | (a.rev ? 2 : 0) | (a.excl ? 1 : 0);
+    const void* fn = nullptr;
+    switch (mode) {
+        case 0: fn = (const void*)k_scan<T, false, false, false >; break;
+        case 1: fn = (const void*)k_scan<T, false, false, true >; break;
+        case 2: fn = (const void*)k_scan<T, false, true, false >; break;
+        case 3: fn = (const void*)k_scan<T, false, true, true >; break;
+        case 4: fn = (const void*)k_scan<T, true, false, false >; break;
+        case 5: fn = (const void*)k_scan<T, true, false, true >; break;
+        case 6: fn = (const void*)k_scan<T, true, true, false >; break;
+        default: fn = (const void*)k_scan<T, true, true, true >; break;
+    }
+    // Persistent grid: as many workgroups as are resident at once.  More would only queue
+    // behind them, and a workgroup that starts late has lost its pipeline's overlap.
+    int64_t grid = resident_wgs(fn, 256);
+    if (grid <= 0) return DET_ERROR_LAUNCH;
+    if (grid > L.ntiles) grid = L.ntiles;
     if (ov.grid_wgs > 0 && grid > ov.grid_wgs) grid = ov.grid_wgs;
-    if (offs)
-        k_scan<T, true><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
-    else
-        k_scan<T, false><<<dim3((unsigned)grid), dim3(256), 0, s>>>(a);
+    a.nctr = (int)(grid < kCounters ? grid : kCounters);
+    void* args[] = {&a};
+    if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, s) != hipSuccess)
+        return DET_ERROR_LAUNCH;
     return launch_status();
 }
 
@@ -469,7 +757,7 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
 size_t scan_workspace(int64_t n, det_dtype dt, unsigned flags, int64_t num_segments) {
     (void)flags;
     (void)num_segments;
-    return layout(n, dt).total;
+    return layout(n, dt, 1, 1).total;
 }
 
 det_status scan_launch(const void* x, void* y, int64_t n, det_dtype dt, unsigned flags,

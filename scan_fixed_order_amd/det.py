@@ -59,10 +59,11 @@ def lib() -> ctypes.CDLL:
     L.det_scatter_add.argtypes = [p, p, i64, i64, i, p, i64, p, p, p, sz, p]
     L.det_scatter_add.restype = i
     L.det_spec_version.argtypes, L.det_spec_version.restype = [], i
-    L.det_spec_constants.argtypes = [ctypes.POINTER(i64)] * 3
+    L.det_spec_constants.argtypes = [ctypes.POINTER(i64)] * 4
     L.det_spec_constants.restype = None
     L.det_status_string.argtypes, L.det_status_string.restype = [i], ctypes.c_char_p
     L.det_debug_set_launch.argtypes, L.det_debug_set_launch.restype = [i, i], i
+    L.det_debug_set_scan_anchors.argtypes, L.det_debug_set_scan_anchors.restype = [i, i], i
     _lib = L
     return L
 
@@ -206,9 +207,9 @@ def det_spec_version() -> int:
 
 
 def det_spec_constants():
-    v, l_, a = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-    lib().det_spec_constants(ctypes.byref(v), ctypes.byref(l_), ctypes.byref(a))
-    return v.value, l_.value, a.value
+    v, l_, a, a2 = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    lib().det_spec_constants(ctypes.byref(v), ctypes.byref(l_), ctypes.byref(a), ctypes.byref(a2))
+    return v.value, l_.value, a.value, a2.value
 
 
 def det_status_string(status: int) -> str:
@@ -217,3 +218,8 @@ def det_status_string(status: int) -> str:
 
 def det_debug_set_launch(grid_wgs: int = 0, sum_chunk_log2: int = 0) -> None:
     _check(lib().det_debug_set_launch(grid_wgs, sum_chunk_log2), "det_debug_set_launch")
+
+
+def det_debug_set_scan_anchors(A: int = 0, A2: int = 0) -> None:
+    """Test hook: scan anchor constants (0 = the spec's 256)."""
+    _check(lib().det_debug_set_scan_anchors(A, A2), "det_debug_set_scan_anchors")

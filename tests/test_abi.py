@@ -37,8 +37,9 @@ def test_header_symbols_exported():
 
 
 def test_spec_constants_match_oracle():
-    V, L, A = det.det_spec_constants()
+    V, L, A, A2 = det.det_spec_constants()
     assert V == oracle.SPEC_V and L == oracle.SPEC_W * oracle.SPEC_NW and A == oracle.SPEC_A
+    assert A2 == oracle.SPEC_A2
     assert det.det_spec_version() == 1
     assert det.det_status_string(0) == "DET_SUCCESS"
     assert det.det_status_string(4) == "DET_ERROR_WORKSPACE"
@@ -103,6 +104,9 @@ def test_debug_hook_range():
     assert lib.det_debug_set_launch(0, 13) == E_INVALID
     assert lib.det_debug_set_launch(0, 25) == E_INVALID
     assert lib.det_debug_set_launch(0, 0) == 0
+    assert lib.det_debug_set_scan_anchors(257, 0) == E_INVALID
+    assert lib.det_debug_set_scan_anchors(0, -1) == E_INVALID
+    assert lib.det_debug_set_scan_anchors(0, 0) == 0
 
 
 def test_binding_rejects_cpu_tensors_and_bad_dtypes():

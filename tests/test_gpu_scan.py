@@ -141,3 +141,29 @@ def test_empty_scan(dev):
     assert det.det_scan(t).numel() == 0
     assert det.det_scan(t, exclusive=True, offsets=torch.zeros(1, dtype=torch.int64,
                                                                device=dev)).numel() == 0
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("A,A2", [(1, 1), (2, 3), (3, 2), (256, 1), (1, 256), (7, 5)])
+def test_small_anchor_variants(dev, dtype, A, A2):
+    # many anchor intervals and super-interval carries at small n: the kernel run with anchor
+    # constants (A, A2) against the oracle run with the same constants
+    n = 37 * T + 123
+    x = workloads.scan_values(n, dtype, seed=A * 10 + A2)
+    offs = random_offsets(n, 20000, seed=A + A2)
+    t = torch.from_numpy(x).to(dev)
+    o = torch.from_numpy(offs).to(dev)
+    try:
+        det.det_debug_set_scan_anchors(A, A2)
+        for grid in (0, 1, 3):
+            det.det_debug_set_launch(grid, 0)
+            for excl, rev in MODES:
+                got = det.det_scan(t, exclusive=excl, reverse=rev).cpu().numpy()
+                want = oracle.scan(x, exclusive=excl, reverse=rev, A=A, A2=A2)
+                assert bits_equal(got, want), (grid, excl, rev, first_mismatch(got, want))
+                got = det.det_scan(t, exclusive=excl, reverse=rev, offsets=o).cpu().numpy()
+                want = oracle.scan(x, exclusive=excl, reverse=rev, offsets=offs, A=A, A2=A2)
+                assert bits_equal(got, want), (grid, excl, rev, "seg", first_mismatch(got, want))
+    finally:
+        det.det_debug_set_scan_anchors(0, 0)
+        det.det_debug_set_launch(0, 0)
