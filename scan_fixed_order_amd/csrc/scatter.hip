@@ -145,9 +145,20 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__
     __syncthreads();
     const int64_t m = FIRST ? n : (int64_t)*nvalid;
     const int64_t base = (int64_t)blockIdx.x * H;
-    for (int i = threadIdx.x; i < H; i += 256) {
-        const int64_t p = base + i;
-        if (p < m) atomicAdd(&cnt[digit_of<FIRST>(keys[p], B, shift)], 1u);
+    // keys in batches of 16 per thread, all loads of a batch issued before the first count
+    for (int i0 = 0; i0 < H; i0 += 256 * 16) {
+        uint32_t kb[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t p = base + i0 + k * 256 + threadIdx.x;
+            kb[k] = (i0 + k * 256 + (int)threadIdx.x < H && p < m) ? keys[p] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int64_t p = base + i0 + k * 256 + threadIdx.x;
+            if (i0 + k * 256 + (int)threadIdx.x < H && p < m)
+                atomicAdd(&cnt[digit_of<FIRST>(kb[k], B, shift)], 1u);
+        }
     }
     __syncthreads();
     for (int d = threadIdx.x; d < nb; d += 256) hist[(int64_t)d * nchunks + blockIdx.x] = cnt[d];
@@ -186,16 +197,26 @@ __global__ __launch_bounds__(256) void k_radix_scatter(
     uint32_t rk[IPT];
     int dg[IPT];
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // every load of the chunk first, so they share one round trip
+    const int64_t p0 = base + (int64_t)wave * WE + lane;
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
-        const int64_t p = base + (int64_t)wave * WE + k * 64 + lane;
-        const bool valid = p < m;
-        key[k] = valid ? keys_in[p] : 0u;
+        const int64_t p = p0 + k * 64;
+        key[k] = p < m ? keys_in[p] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+        const int64_t p = p0 + k * 64;
         if constexpr (ROWS && FIRST) {
-            pay[k] = (P)(valid ? p : 0);
+            pay[k] = (P)(p < m ? p : 0);
         } else {
-            pay[k] = valid ? pay_in[p] : (P)0;
+            pay[k] = p < m ? pay_in[p] : (P)0;
         }
+    }
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+        const int64_t p = p0 + k * 64;
+        const bool valid = p < m;
         const int d = valid ? digit_of<FIRST>(key[k], B, shift) : 0;
         dg[k] = d;
         uint64_t peers = __ballot(valid);
