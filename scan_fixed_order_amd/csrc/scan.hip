@@ -39,8 +39,6 @@ constexpr int kV = kScanV;
 constexpr int kT = kScanT;
 
 constexpr int kWaveElems = kScanV * kScanW;                 // 2048
-constexpr int kHalf = kWaveElems / 2;                       // elements staged at a time
-constexpr int kStage = kHalf + kHalf / 32;                  // one spare LDS slot per 32
 constexpr int kHeadWords = kT / 32 + 1;                     // bits for positions [F0, F0 + T]
 
 constexpr uint32_t kReady = 1u;
@@ -333,60 +331,81 @@ __device__ __forceinline__ void nt_store4(T* p, T a, T b, T c, T d) {
     }
 }
 
-// Half h of the wave's results (flipped positions hw .. hw + 1023, hw = fw + 1024 h) from the
-// LDS stage to y with coalesced stores: 16-byte non-temporal stores where the whole half is in
-// range and aligned, otherwise 4- or 8-byte stores.
-template <typename T, bool REV>
-__device__ __forceinline__ void store_half(T* __restrict__ y, int64_t n, int64_t fw, int h,
-                                           const T* st, int lane) {
-    const int64_t hw = fw + h * kHalf;
-    const bool full = hw + kHalf <= n;
-    T* base = REV ? y + (n - hw - kHalf) : y + hw;   // lowest original index of the half
+// Parked tile: each wave keeps its 2048 lane-serial prefixes in LDS in run order, lane t's run
+// at t * 33 (one spare slot per run keeps both the run-wise writes and the element-wise reads
+// free of bank conflicts), together with each lane's combine value X and head bits.
+constexpr int kPark = kWaveElems + kWaveElems / 32;
+
+template <typename T>
+__device__ __forceinline__ void park_runs(T* pk, const T (&r)[kV], int lane) {
+    const int rb = lane * (kV + 1);
+#pragma unroll
+    for (int k = 0; k < kV; ++k) pk[rb + k] = r[k];
+}
+
+// Flipped element e of the wave (lane e / 32, position e % 32): y = X + s, except that a
+// segment head at or before the position inside the lane's run keeps s.
+template <typename T, bool SEG>
+__device__ __forceinline__ T combine_at(const T* pk, const T* xs, const uint32_t* hbs, int e) {
+    const T sv = pk[pad(e)];
+    const int L = e >> 5;
+    if constexpr (SEG) {
+        if (hbs[L] << (31 - (e & 31))) return sv;
+    }
+    return xs[L] + sv;
+}
+
+// Whole-wave readout, inclusive: flipped positions fw .. fw + 2047 to y.  16-byte
+// non-temporal stores where the wave is in range and aligned, else element stores.
+template <typename T, bool SEG, bool REV>
+__device__ __forceinline__ void readout_incl(T* __restrict__ y, int64_t n, int64_t fw, const T* pk,
+                                             const T* xs, const uint32_t* hbs, int lane) {
+    const bool full = fw + kWaveElems <= n;
+    T* base = REV ? y + (n - fw - kWaveElems) : y + fw;   // lowest original index of the wave
     if (full && aligned16(base)) {
 #pragma unroll
-        for (int r = 0; r < kHalf / 256; ++r) {
-            const int o = r * 256 + 4 * lane;            // original offset within the half
+        for (int r = 0; r < kWaveElems / 256; ++r) {
+            const int o = r * 256 + 4 * lane;                 // original offset within the wave
             if (REV) {
-                const int e = (kHalf - 1) - o;          // flipped element of original offset o
-                nt_store4<T>(base + o, st[pad(e)], st[pad(e - 1)], st[pad(e - 2)], st[pad(e - 3)]);
+                const int e = (kWaveElems - 1) - o;           // flipped element of offset o
+                nt_store4<T>(base + o, combine_at<T, SEG>(pk, xs, hbs, e),
+                             combine_at<T, SEG>(pk, xs, hbs, e - 1),
+                             combine_at<T, SEG>(pk, xs, hbs, e - 2),
+                             combine_at<T, SEG>(pk, xs, hbs, e - 3));
             } else {
-                const int a = pad(o);
-                nt_store4<T>(base + o, st[a], st[a + 1], st[a + 2], st[a + 3]);
+                nt_store4<T>(base + o, combine_at<T, SEG>(pk, xs, hbs, o),
+                             combine_at<T, SEG>(pk, xs, hbs, o + 1),
+                             combine_at<T, SEG>(pk, xs, hbs, o + 2),
+                             combine_at<T, SEG>(pk, xs, hbs, o + 3));
             }
         }
-    } else if (full) {
-#pragma unroll
-        for (int r = 0; r < kHalf / 64; ++r) {
-            const int o = r * 64 + lane;
-            base[o] = st[pad(REV ? (kHalf - 1) - o : o)];
-        }
     } else {
-        const int64_t left = n - hw;
-        const int valid = left < 0 ? 0 : (int)left;
+        const int64_t left = n - fw;
+        const int valid = left < 0 ? 0 : (left < kWaveElems ? (int)left : kWaveElems);
 #pragma unroll 8
-        for (int r = 0; r < kHalf / 64; ++r) {
+        for (int r = 0; r < kWaveElems / 64; ++r) {
             const int e = r * 64 + lane;
-            if (e < valid) y[REV ? (n - 1 - hw) - e : hw + e] = st[pad(e)];
+            if (e < valid) y[REV ? (n - 1 - fw) - e : fw + e] = combine_at<T, SEG>(pk, xs, hbs, e);
         }
     }
 }
 
-// Exclusive scans: the inclusive value of flipped position f goes to f + 1 (+0.0 at heads).
+// Whole-wave readout, exclusive: the inclusive value of flipped position f goes to f + 1
+// (+0.0 where f + 1 is a segment head).
 template <typename T, bool SEG, bool REV>
-__device__ __forceinline__ void store_half_excl(T* __restrict__ y, int64_t n, int64_t F0,
-                                                int64_t fw, int h, const T* st,
-                                                const uint32_t* s_heads, int lane) {
-    const int64_t hw = fw + h * kHalf;
-    const int64_t left = n - (hw + 1);
-    const int valid = left < 0 ? 0 : (left < kHalf ? (int)left : kHalf);
-    T* yb = REV ? y + (n - 2 - hw) : y + (hw + 1);
+__device__ __forceinline__ void readout_excl(T* __restrict__ y, int64_t n, int64_t F0, int64_t fw,
+                                             const T* pk, const T* xs, const uint32_t* hbs,
+                                             const uint32_t* s_heads, int lane) {
+    const int64_t left = n - (fw + 1);
+    const int valid = left < 0 ? 0 : (left < kWaveElems ? (int)left : kWaveElems);
+    T* yb = REV ? y + (n - 2 - fw) : y + (fw + 1);
 #pragma unroll 8
-    for (int r = 0; r < kHalf / 64; ++r) {
+    for (int r = 0; r < kWaveElems / 64; ++r) {
         const int e = r * 64 + lane;
         if (e < valid) {
-            T v = st[pad(e)];
+            T v = combine_at<T, SEG>(pk, xs, hbs, e);
             if constexpr (SEG) {
-                const int bit = (int)(hw + e + 1 - F0);
+                const int bit = (int)(fw + e + 1 - F0);
                 if ((s_heads[bit >> 5] >> (bit & 31)) & 1u) v = T(0.0);
             }
             if (REV) yb[-e] = v;
@@ -492,15 +511,16 @@ __device__ __forceinline__ void issue_look_back(const ScanArgs<T>& a, const Look
                   a.gtot + (size_t)(lb.Q * a.A2 + tid) * SW, tid < lb.qcnt);
 }
 
-// Everything after tile j's local part: finish the look-back, publish the interval total (the
-// interval's last tile) and forward the super-interval carry (its last tile), combine the tile
-// with its prefix and store it through the wave's LDS stage in two halves.
+// Everything after a parked tile's look-back polls were issued: finish the look-back, publish
+// the interval total (the interval's last tile) and forward the super-interval carry (its last
+// tile), then each lane's combine value X = ((((CC + WG) + W_j) + P) + p) goes to LDS and the
+// wave reads its parked prefixes out, adds X and stores them.
 template <typename T, bool SEG, bool REV, bool EXCL>
 __device__ __forceinline__ void finish_tile(const ScanArgs<T>& a, int j, const LookBack& lb,
-                                            Poll<T>& pl, T (&r)[kV], uint32_t hb, Seg<T> P,
-                                            Seg<T> p, Seg<T> agg, Seg<T>* s_tmp, Seg<T>& s_carry,
-                                            const uint32_t* s_heads, T* st, int tid, int lane,
-                                            int wave) {
+                                            Poll<T>& pl, Seg<T> P, Seg<T> p, Seg<T> agg,
+                                            Seg<T>* s_tmp, Seg<T>& s_carry, const T* pk, T* xs,
+                                            const uint32_t* hbs, const uint32_t* s_heads, int tid,
+                                            int lane, int wave) {
     constexpr int SW = slot_words<T>();
     uint32_t* err = a.err;
     Seg<T> mine = seg_ident<T>(), gmine = seg_ident<T>();
@@ -528,40 +548,20 @@ __device__ __forceinline__ void finish_tile(const ScanArgs<T>& a, int j, const L
     }
     __syncthreads();
     const Seg<T> E = op<SEG>(op<SEG>(s_carry, WG), Wj);
-    const Seg<T> X = op<SEG>(op<SEG>(E, P), p);
-
-    // combine (lane index re-derived so stage addresses are recomputed here, not kept live)
-    asm volatile("" : "+v"(lane));
-#pragma unroll
-    for (int k = 0; k < kV; ++k) {
-        if constexpr (SEG) {
-            const uint32_t upto = (k == 31) ? hb : (hb & ((2u << k) - 1u));
-            if (!upto) r[k] = X.v + r[k];
-        } else {
-            r[k] = X.v + r[k];
-        }
-    }
+    xs[lane] = op<SEG>(op<SEG>(E, P), p).v;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int64_t F0 = (int64_t)j * kT;
     const int64_t fw = F0 + (int64_t)wave * kWaveElems;
-    const int rb = (lane & 31) * 33;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        if ((lane >> 5) == h) {
-#pragma unroll
-            for (int k = 0; k < kV; ++k) st[rb + k] = r[k];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (!EXCL)
-            store_half<T, REV>(a.y, a.n, fw, h, st, lane);
-        else
-            store_half_excl<T, SEG, REV>(a.y, a.n, F0, fw, h, st, s_heads, lane);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+    if (!EXCL)
+        readout_incl<T, SEG, REV>(a.y, a.n, fw, pk, xs, hbs, lane);
+    else
+        readout_excl<T, SEG, REV>(a.y, a.n, F0, fw, pk, xs, hbs, s_heads, lane);
     if (EXCL && j == 0 && tid == 0) a.y[REV ? a.n - 1 : 0] = T(0.0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Tiles are claimed from nc <= kCounters counters (nc <= the grid), one per 256-byte line:
@@ -580,17 +580,19 @@ __device__ __forceinline__ int claim_tile(uint32_t* counters, int c, int nc) {
     return (int)k * nc + c;
 }
 
-// Persistent workgroups, two tiles in flight each.  Per iteration: the loads of the next tile,
-// the claim of the tile after it and the current tile's first look-back polls share one round
-// trip; the next tile's local part runs and its total is published; the current tile finishes
-// its look-back and is stored; only then is the claimed tile number needed, so the claim's
-// latency hides behind the whole iteration.  A tile's total is published a whole iteration
-// before its workgroup waits on anything.  A workgroup only waits on smaller tiles, which are
-// claimed in counter order by running workgroups that finish them without waiting on it, so
-// every wait ends.
+// Persistent workgroups, three tiles in flight each: tile c parked in LDS (published, waiting
+// for its look-back), tile u in registers (its loads were issued one iteration earlier) and
+// tile v loading.  Per iteration: c's look-back polls leave; u's local part runs and u's total
+// is published; v's loads are issued and the tile after v is claimed; c finishes and is stored
+// from LDS; u is parked in c's place.  Load latency thus overlaps a whole iteration, and a
+// tile's total is published one iteration before its workgroup waits on anything.  A
+// workgroup only waits on smaller tiles, which are claimed in counter order by running
+// workgroups that publish and finish them without waiting on it, so every wait ends.
 template <typename T, bool SEG, bool REV, bool EXCL>
 __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
-    __shared__ T s_stage[kScanWaves][kStage];
+    __shared__ T s_park[kScanWaves][kPark];
+    __shared__ T s_x[kScanWaves][kScanW];
+    __shared__ uint32_t s_hbits[SEG ? kScanWaves : 1][kScanW];
     __shared__ uint32_t s_heads[2][SEG ? kHeadWords : 1];
     __shared__ Seg<T> s_tmp[kScanWaves];
     __shared__ Seg<T> s_wtot[kScanWaves];
@@ -601,64 +603,88 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     const int lane0 = tid & 63;
     const int wave = tid >> 6;
     constexpr int SW = slot_words<T>();
-    T* st = s_stage[wave];
-
+    T* pk = s_park[wave];
+    T* xs = s_x[wave];
+    const uint32_t* hbs = s_hbits[SEG ? wave : 0];
     const int ctr = (int)(blockIdx.x % (unsigned)a.nctr);
+
+    // ---- prologue: c loaded, local, published, parked; u's loads issued
     if (tid == 0) s_tick[0] = claim_tile(a.ticket, ctr, a.nctr);
     __syncthreads();
-    int cur = s_tick[0];
-    if (cur >= a.ntiles) return;
+    int c = s_tick[0];
+    if (c >= a.ntiles) return;
     T r[kV];
-    load_tile<T, REV>(a, cur, wave, r, lane0);
-    uint32_t hb;
-    Seg<T> P, p;
-    Seg<T> agg = tile_local<T, SEG, REV>(a, cur, r, hb, P, p, s_heads[0], s_wtot, tid, lane0, wave);
+    load_tile<T, REV>(a, c, wave, r, lane0);
+    int claimed = 0;
+    if (tid == 0) claimed = claim_tile(a.ticket, ctr, a.nctr);
+    uint32_t hbc;
+    Seg<T> Pc, pc;
+    Seg<T> aggc =
+        tile_local<T, SEG, REV>(a, c, r, hbc, Pc, pc, s_heads[0], s_wtot, tid, lane0, wave);
     if (tid == 0) {
-        publish<T>(a.agg + (size_t)cur * SW, agg);
-        s_tick[1] = claim_tile(a.ticket, ctr, a.nctr);
+        publish<T>(a.agg + (size_t)c * SW, aggc);
+        s_tick[1] = claimed;
     }
-    LookBack lb = look_back_of(cur, a.A, a.A2);
-    Poll<T> pl;
-    int par = 1;   // s_tick[par] holds the next tile; s_heads[par ^ 1] holds cur's heads
+    park_runs<T>(pk, r, lane0);
+    if constexpr (SEG) s_hbits[wave][lane0] = hbc;
+    __syncthreads();
+    int u = s_tick[1];
+    if (u < a.ntiles) {
+        load_tile<T, REV>(a, u, wave, r, lane0);
+        if (tid == 0) claimed = claim_tile(a.ticket, ctr, a.nctr);
+    }
+    LookBack lbc = look_back_of(c, a.A, a.A2);
+    int par = 0;   // s_heads[par] holds c's heads, s_heads[par ^ 1] receives u's
 
     for (;;) {
         // Re-derive the lane index each iteration so per-lane addresses are recomputed instead
         // of being held live across the loop (register pressure decides occupancy).
         int lane = lane0;
         asm volatile("" : "+v"(lane));
-        __syncthreads();
-        const int nxt = s_tick[par];
-        const bool more = nxt < a.ntiles;
+        const bool have_u = u < a.ntiles;
+        if (tid == 0) s_tick[par] = claimed;   // v (meaningful only when u exists)
+        // c's look-back polls first: they sit in front of every load issued after them
+        Poll<T> pl;
+        issue_look_back<T>(a, lbc, pl, tid);
 
-        T rn[kV];
-        int claimed = 0;
-        if (more) {
-            load_tile<T, REV>(a, nxt, wave, rn, lane);
+        // ---- u: local part (its loads were issued an iteration ago), total published at once
+        uint32_t hbu = 0u;
+        Seg<T> Pu = seg_ident<T>(), pu = seg_ident<T>(), aggu = seg_ident<T>();
+        if (have_u) {
+            aggu = tile_local<T, SEG, REV>(a, u, r, hbu, Pu, pu, s_heads[par ^ 1], s_wtot, tid,
+                                           lane, wave);
+            if (tid == 0) publish<T>(a.agg + (size_t)u * SW, aggu);
+        }
+        __syncthreads();
+        const int v = s_tick[par];
+        const bool have_v = have_u && v < a.ntiles;
+
+        // ---- v: loads issued now, consumed in the next iteration; the tile after v claimed
+        T rv[kV];
+        if (have_v) {
+            load_tile<T, REV>(a, v, wave, rv, lane);
             if (tid == 0) claimed = claim_tile(a.ticket, ctr, a.nctr);
         }
-        issue_look_back<T>(a, lb, pl, tid);
-        uint32_t hbn = 0;
-        Seg<T> Pn = seg_ident<T>(), pn = seg_ident<T>(), aggn = seg_ident<T>();
-        if (more) {
-            aggn = tile_local<T, SEG, REV>(a, nxt, rn, hbn, Pn, pn, s_heads[par], s_wtot, tid,
-                                           lane, wave);
-            if (tid == 0) {
-                publish<T>(a.agg + (size_t)nxt * SW, aggn);
-            }
-        }
-        finish_tile<T, SEG, REV, EXCL>(a, cur, lb, pl, r, hb, P, p, agg, s_tmp, s_carry,
-                                       s_heads[par ^ 1], st, tid, lane, wave);
-        if (!more) break;
-        if (tid == 0) s_tick[par ^ 1] = claimed;
+
+        // ---- c: finish the look-back, store from LDS
+        finish_tile<T, SEG, REV, EXCL>(a, c, lbc, pl, Pc, pc, aggc, s_tmp, s_carry, pk, xs, hbs,
+                                       s_heads[par], tid, lane, wave);
+        if (!have_u) break;
+
+        // ---- u takes c's place in LDS (this wave's readout of c is complete)
+        park_runs<T>(pk, r, lane);
+        if constexpr (SEG) s_hbits[wave][lane] = hbu;
 #pragma unroll
-        for (int k = 0; k < kV; ++k) r[k] = rn[k];
-        hb = hbn;
-        P = Pn;
-        p = pn;
-        agg = aggn;
-        lb = look_back_of(nxt, a.A, a.A2);
-        cur = nxt;
+        for (int k = 0; k < kV; ++k) r[k] = rv[k];
+        Pc = Pu;
+        pc = pu;
+        aggc = aggu;
+        lbc = look_back_of(u, a.A, a.A2);
+        c = u;
+        u = have_v ? v : a.ntiles;
         par ^= 1;
+        // the next tile's heads go where c's were: every wave must be done reading them
+        if constexpr (SEG) __syncthreads();
     }
 }
 
