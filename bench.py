@@ -7,16 +7,21 @@ Inputs are resident in HBM before the timed region.  `value` is the step's algor
 (sum 4n, scan 8n, scatter 8n + 8*bins) divided by the step time.
 
 Prints ONE JSON line.  Besides the contract fields it carries:
-  roofline      the kernel with the largest share of the step, its algorithmic bytes per launch
-                over its average launch time (HIP events on the launching stream), vs 8 TB/s;
+  roofline      the kernel with the largest share of the step (by the library's own per-launch
+                HIP events, recorded on the launching stream during the timed steps): its
+                algorithmic bytes per launch over its average launch time, against 8 TB/s; and
+                `traffic`, the HBM bytes per launch that rocprofv3 counters measured for the same
+                kernel source (read from profiles/, null when that source has changed since);
+  kernels       every library kernel of the step: launches per step, average ms;
   ops           per operation: time, GB/s, Gelem/s, fraction of 8 TB/s, the non-deterministic
                 baseline's time on the same input and the deterministic-mode overhead;
-  cpu_baseline  the CPU oracle (single thread) on a bounded sample of the same workload.
+  cpu_baseline  the CPU oracle (single thread) on the same workload, timed on the host.
 """
 import argparse
-import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "scan_fixed_order_amd", "csrc")
 
 
 def parse():
@@ -36,12 +42,56 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--only", default="", help="comma list of sum,scan,scatter (profiling)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain device copy of 2^log2n f32 (1 GiB each way at 2^28): "
+                         "the known-size kernel that scales rocprofv3 byte counters")
     return ap.parse_args()
 
 
 def log(msg):
     sys.stderr.write(f"[bench] {msg}\n")
     sys.stderr.flush()
+
+
+def kernel_bytes_per_step(n, B):
+    """Algorithmic HBM bytes each library kernel must move in one step (f32, row_len 1)."""
+    parts = -(-n // (1 << 14))
+    return {
+        "k_sum_chunks<f32>": 4.0 * n + 4.0 * parts,      # values, then the partials' level
+        "k_scan<f32>": 8.0 * n,                          # read x, write y
+        "k_radix_hist": 2 * 4.0 * n,                     # keys, one pass per 8-bit digit
+        "k_radix_scatter": 2 * 16.0 * n,                 # keys + values in and out, two passes
+        "k_segred_scalar": 8.0 * n + 8.0 * B,            # sorted keys + values, out r/w
+    }
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from a committed counter summary for `kernel`, or None when there is
+    none or the kernel's source has changed since the counters were taken."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    for fn in sorted(os.listdir(pdir)):
+        if not fn.endswith(".md"):
+            continue
+        text = open(os.path.join(pdir, fn)).read()
+        m_k = re.search(r"^traffic-kernel: (\S+)\s*$", text, re.M)
+        if not m_k or m_k.group(1) != kernel:
+            continue
+        m_s = re.search(r"^traffic-source: (\S+) sha256 ([0-9a-f]{64})\s*$", text, re.M)
+        m_b = re.search(r"^traffic-bytes-per-launch: (\d+)\s*$", text, re.M)
+        if not m_s or not m_b:
+            continue
+        src = os.path.join(ROOT, m_s.group(1))
+        if not os.path.exists(src) or source_hash(src) != m_s.group(2):
+            return None
+        return int(m_b.group(1))
+    return None
 
 
 def main():
@@ -51,6 +101,8 @@ def main():
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+
+    import ctypes
 
     import numpy as np
     import torch
@@ -102,6 +154,7 @@ def main():
     ev = {name: [] for name, _, _ in ops}
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    det.det_debug_kernel_timing(True)
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(args.steps):
@@ -114,12 +167,22 @@ def main():
             ev[name].append((a, b))
     stop.record(stream)
     torch.cuda.synchronize()
+    kernels = det.det_debug_kernel_report()
+    det.det_debug_kernel_timing(False)
     step_ms = start.elapsed_time(stop) / args.steps
     op_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name in ev}
     log(f"timed {args.steps} steps: {step_ms:.3f} ms/step")
 
     step_bytes = sum(bts for _, _, bts in ops)
     value = step_bytes / (step_ms * 1e-3) / 1e9
+
+    if args.calibrate_copy:
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {n} f32 elements, 3 times")
 
     # ---------------------------------------------------------------- non-deterministic baselines
     base_ms = {}
@@ -167,37 +230,50 @@ def main():
             r["det_overhead"] = round(ms / base_ms[name] - 1.0, 4)
         op_rep[name] = r
 
-    # dominant kernel: the operation with the largest share of the step; for the scan and the
-    # sum the operation is one main kernel (plus a tiny clearing launch for the scan)
-    dom = max(op_ms, key=op_ms.get)
-    dom_kernel = {"sum": "k_sum_chunks<float>", "scan": "k_scan<float, false>",
-                  "scatter": "det_scatter_add (sort + reduce kernels)"}[dom]
-    dom_bytes = dict((nm, b) for nm, _, b in ops)[dom]
-    achieved = dom_bytes / (op_ms[dom] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBS, 4), "traffic": None, "kernel": dom_kernel,
-                "algorithmic_bytes_per_launch": int(dom_bytes)}
+    # ---------------------------------------------------------------- dominant kernel
+    kern_rep = {k: {"launches_per_step": round(c / args.steps, 3), "avg_ms": round(avg, 5),
+                    "ms_per_step": round(tot / args.steps, 5)}
+                for k, (c, tot, avg) in kernels.items()}
+    roofline = None
+    if kernels:
+        dom = max(kernels, key=lambda k: kernels[k][1])
+        c, tot, avg = kernels[dom]
+        per_step = kernel_bytes_per_step(n, B).get(dom)
+        if per_step is not None:
+            per_launch = per_step / (c / args.steps)
+            achieved = per_launch / (avg * 1e-3) / 1e9
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                        "traffic": measured_traffic(dom), "kernel": dom,
+                        "algorithmic_bytes_per_launch": int(per_launch),
+                        "avg_launch_ms": round(avg, 5)}
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
 
-        m = 1 << 24
-        xs = host.get("x_sum", workloads.uniform01(m, seed=0))[:m].copy()
-        xc = host.get("x_scan", workloads.scan_values(m, np.float32, seed=2))[:m].copy()
-        vs = host.get("v_sc", workloads.normal(m, seed=1))[:m].copy()
-        bs = host.get("b_sc", workloads.bins_uniform(m, B, seed=1))[:m].copy()
-        t = time.perf_counter()
-        oracle.det_sum(xs)
-        oracle.scan(xc)
-        oracle.scatter_add(vs, bs, np.zeros(B, np.float32))
-        dt = time.perf_counter() - t
-        cpu_bytes = 4.0 * m + 8.0 * m + 8.0 * m + 8.0 * B
-        cpu = {"value": round(cpu_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"first 2^24 elements of each input (sum + scan + scatter into {B} bins), "
-                         f"{dt:.1f} s single-threaded"}
-        log(f"cpu oracle sample took {dt:.1f}s")
+        xs = host.get("x_sum")
+        xc = host.get("x_scan")
+        vs, bs = host.get("v_sc"), host.get("b_sc")
+        reps, dt, cpu_bytes = 0, 0.0, 0.0
+        while reps < 3 and dt < 10.0:
+            t = time.perf_counter()
+            if xs is not None:
+                oracle.det_sum(xs)
+            if xc is not None:
+                oracle.scan(xc)
+            if vs is not None:
+                oracle.scatter_add(vs, bs, np.zeros(B, np.float32))
+            dt += time.perf_counter() - t
+            cpu_bytes += step_bytes
+            reps += 1
+        cpu = {"value": round(cpu_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"the whole step's workload ({', '.join(sorted(only))} at n=2^{args.log2n}, "
+                         f"{B} bins) run {reps} time(s) through the single-threaded C oracle: "
+                         f"{dt:.1f} s on {os.cpu_count()} visible host cores"}
+        log(f"cpu oracle: {reps} pass(es), {dt:.1f}s")
 
     line = {
         "metric": "GB/s & % HBM peak for bit-reproducible f32 sum/scatter-add/scan at 2^28, 1 GPU",
@@ -218,6 +294,7 @@ def main():
                    "n": n, "bins": B, "ops": sorted(only)},
         "frac_hbm": round(value / PEAK_GBS, 4),
         "roofline": roofline,
+        "kernels": kern_rep,
         "ops": op_rep,
         "cpu_baseline": cpu,
     }

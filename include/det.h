@@ -155,6 +155,19 @@ det_status det_debug_set_launch(int grid_wgs, int sum_chunk_log2);
  * Process-wide; DET_ERROR_INVALID_VALUE when out of range. */
 det_status det_debug_set_scan_anchors(int A, int A2);
 
+/* Not part of the stable interface.  Kernel timing for benchmarks: while enabled, every kernel
+ * the library enqueues is bracketed by two HIP events recorded on the call's stream.
+ * enable = 1 drops earlier records and starts recording, 0 drops them and stops; anything else
+ * is DET_ERROR_INVALID_VALUE.  Recording adds an event pair per launch. */
+det_status det_debug_kernel_timing(int enable);
+
+/* Not part of the stable interface.  Waits for every recorded event pair, then writes one line
+ * per kernel name, "name launches total_ms average_ms", into buf (at most len bytes including
+ * the terminating NUL; buf may be NULL).  The records stay until det_debug_kernel_timing is
+ * called again.  Launches whose events failed are counted in a last line starting with '#'.
+ * Returns the bytes the full report needs, NUL included. */
+size_t det_debug_kernel_report(char* buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif

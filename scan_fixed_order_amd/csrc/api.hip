@@ -2,9 +2,14 @@
 //
 // Every check that needs no device data happens here, before anything is enqueued; the
 // kernels never see an argument this file rejected.
+#include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <map>
 #include <mutex>
+#include <string>
+#include <vector>
 
 #include "det_internal.h"
 
@@ -37,6 +42,61 @@ int64_t resident_wgs(const void* fn, int block) {
     const int64_t wgs = (int64_t)(per_cu < 1 ? 1 : per_cu) * cus;
     if (used < 64) cache[used++] = Entry{dev, fn, block, wgs};
     return wgs;
+}
+
+// ---------------------------------------------------------------- kernel timing hook
+
+namespace {
+struct TimedLaunch {
+    const char* name;
+    hipEvent_t a, b;
+};
+std::mutex g_tm;
+std::atomic<bool> g_timing{false};
+unsigned g_gen = 0;                    // bumped whenever the records are dropped
+std::vector<TimedLaunch> g_launches;
+std::vector<hipEvent_t> g_events;      // idle events for reuse
+
+hipEvent_t take_event() {
+    if (!g_events.empty()) {
+        hipEvent_t e = g_events.back();
+        g_events.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+void drop_launches() {
+    for (const TimedLaunch& t : g_launches) {
+        if (t.a) g_events.push_back(t.a);
+        if (t.b) g_events.push_back(t.b);
+    }
+    g_launches.clear();
+    ++g_gen;
+}
+}  // namespace
+
+KernelTimer::KernelTimer(const char* name, hipStream_t s) : s_(s), slot_(-1), gen_(0) {
+    if (!g_timing.load(std::memory_order_relaxed)) return;
+    std::lock_guard<std::mutex> lock(g_tm);
+    TimedLaunch t{name, take_event(), take_event()};
+    if (!t.a || !t.b || hipEventRecord(t.a, s) != hipSuccess) {
+        if (t.a) g_events.push_back(t.a);
+        if (t.b) g_events.push_back(t.b);
+        return;
+    }
+    g_launches.push_back(t);
+    slot_ = (long)g_launches.size() - 1;
+    gen_ = g_gen;
+}
+
+KernelTimer::~KernelTimer() {
+    if (slot_ < 0) return;
+    std::lock_guard<std::mutex> lock(g_tm);
+    if (gen_ != g_gen || slot_ >= (long)g_launches.size()) return;
+    if (hipEventRecord(g_launches[slot_].b, s_) != hipSuccess) g_launches[slot_].name = nullptr;
 }
 
 static bool valid_dtype(det_dtype d) { return d == DET_F32 || d == DET_F64; }
@@ -160,6 +220,55 @@ det_status det_debug_set_scan_anchors(int A, int A2) {
     g_override.scan_A = A;
     g_override.scan_A2 = A2;
     return DET_SUCCESS;
+}
+
+det_status det_debug_kernel_timing(int enable) {
+    if (enable != 0 && enable != 1) return DET_ERROR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lock(g_tm);
+    drop_launches();
+    g_timing.store(enable == 1, std::memory_order_relaxed);
+    return DET_SUCCESS;
+}
+
+size_t det_debug_kernel_report(char* buf, size_t len) {
+    std::map<std::string, std::pair<long, double>> agg;   // name -> launches, total ms
+    std::string out;
+    long failed = 0;
+    hipError_t last = hipSuccess;
+    {
+        std::lock_guard<std::mutex> lock(g_tm);
+        for (const TimedLaunch& t : g_launches) {
+            float ms = 0.f;
+            hipError_t e1 = t.name ? hipEventSynchronize(t.b) : hipErrorInvalidValue;
+            hipError_t e2 = e1 == hipSuccess ? hipEventElapsedTime(&ms, t.a, t.b) : e1;
+            if (e2 != hipSuccess) {
+                ++failed;
+                last = e2;
+                continue;
+            }
+            auto& e = agg[t.name];
+            e.first += 1;
+            e.second += ms;
+        }
+    }
+    if (failed) {
+        char line[256];
+        snprintf(line, sizeof line, "# %ld launch(es) not timed: %s\n", failed,
+                 hipGetErrorString(last));
+        out += line;
+    }
+    for (const auto& kv : agg) {
+        char line[256];
+        snprintf(line, sizeof line, "%s %ld %.6f %.6f\n", kv.first.c_str(), kv.second.first,
+                 kv.second.second, kv.second.second / (double)kv.second.first);
+        out += line;
+    }
+    if (buf && len > 0) {
+        const size_t m = out.size() < len - 1 ? out.size() : len - 1;
+        memcpy(buf, out.data(), m);
+        buf[m] = '\0';
+    }
+    return out.size() + 1;
 }
 
 }  // extern "C"

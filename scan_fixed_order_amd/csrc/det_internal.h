@@ -50,6 +50,22 @@ det_status scatter_launch(const void* values, const int32_t* index, int64_t n, i
 // (occupancy x compute units), cached per device and kernel; 0 if the runtime cannot tell.
 int64_t resident_wgs(const void* fn, int block);
 
+// Kernel timing (a test hook): while it is switched on, a KernelTimer brackets one launch with
+// two HIP events on the launch's stream; det_debug_kernel_report reads them.  Off, it costs one
+// relaxed load.
+class KernelTimer {
+  public:
+    KernelTimer(const char* name, hipStream_t s);
+    ~KernelTimer();
+    KernelTimer(const KernelTimer&) = delete;
+    KernelTimer& operator=(const KernelTimer&) = delete;
+
+  private:
+    hipStream_t s_;
+    long slot_;
+    unsigned gen_;
+};
+
 inline det_status launch_status() {
     return hipGetLastError() == hipSuccess ? DET_SUCCESS : DET_ERROR_LAUNCH;
 }

@@ -734,7 +734,10 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     const int64_t words = (int64_t)(L.used / 8);
     int zg = (int)((words + 255) / 256);
     if (zg > 1024) zg = 1024;
-    k_zero_words<<<zg, 256, 0, s>>>(reinterpret_cast<uint64_t*>(ws), words);
+    {
+        KernelTimer kt("k_zero_words", s);
+        k_zero_words<<<zg, 256, 0, s>>>(reinterpret_cast<uint64_t*>(ws), words);
+    }
     det_status st = launch_status();
     if (st != DET_SUCCESS) return st;
     ScanArgs<T> a;
@@ -773,6 +776,7 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     if (ov.grid_wgs > 0 && grid > ov.grid_wgs) grid = ov.grid_wgs;
     a.nctr = (int)(grid < kCounters ? grid : kCounters);
     void* args[] = {&a};
+    KernelTimer kt(sizeof(T) == 4 ? "k_scan<f32>" : "k_scan<f64>", s);
     if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, s) != hipSuccess)
         return DET_ERROR_LAUNCH;
     return launch_status();

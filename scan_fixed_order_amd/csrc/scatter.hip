@@ -120,6 +120,7 @@ __global__ __launch_bounds__(256) void k_u32_block_apply(uint32_t* __restrict__ 
 
 det_status u32_exclusive_scan(uint32_t* a, int64_t N, uint32_t* sums, hipStream_t s) {
     const int64_t nb = cdiv(N, kU32Blk);
+    KernelTimer kt("k_u32_exclusive_scan", s);
     k_u32_block_sums<<<dim3((unsigned)nb), dim3(256), 0, s>>>(a, N, sums);
     k_u32_scan_sums<<<1, 256, 0, s>>>(sums, nb);
     k_u32_block_apply<<<dim3((unsigned)nb), dim3(256), 0, s>>>(a, N, sums);
@@ -754,15 +755,19 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
         const uint32_t* kin = first ? reinterpret_cast<const uint32_t*>(index) : keys[(p - 1) & 1];
         const P* pin = first ? reinterpret_cast<const P*>(values) : pay[(p - 1) & 1];
         const int nb = first ? kBuckets0 : 256;
-        if (first)
-            k_radix_hist<true><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb, L.nchunks, (int)L.H,
-                                                    hist);
-        else
-            k_radix_hist<false><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb, L.nchunks,
-                                                     (int)L.H, hist);
+        {
+            KernelTimer kt("k_radix_hist", s);
+            if (first)
+                k_radix_hist<true><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb, L.nchunks,
+                                                        (int)L.H, hist);
+            else
+                k_radix_hist<false><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb, L.nchunks,
+                                                         (int)L.H, hist);
+        }
         det_status st = u32_exclusive_scan(hist, (int64_t)nb * L.nchunks, sums, s);
         if (st != DET_SUCCESS) return st;
         if (first) k_copy_word<<<1, 1, 0, s>>>(hist + (int64_t)256 * L.nchunks, ctrl);
+        KernelTimer kt("k_radix_scatter", s);
         if (first)
             k_radix_scatter<P, true, ROWS><<<grid, 256, 0, s>>>(kin, pin, keys[p & 1], pay[p & 1], n,
                                                                 ctrl, B, shift, L.nchunks, hist);
@@ -777,6 +782,7 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
     {
         int64_t g = cdiv(num_out + 1, 256);
         if (g > 8192) g = 8192;
+        KernelTimer kt("k_bin_offsets", s);
         k_bin_offsets<<<dim3((unsigned)g), dim3(256), 0, s>>>(K, ctrl, num_out, n, off, n_skipped);
     }
     T* pF = reinterpret_cast<T*>(ws + L.pF);
@@ -784,12 +790,18 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
     int64_t lg = cdiv(num_out, 64 * 4);
     if (lg > 4096) lg = 4096;
     if constexpr (!ROWS) {
-        k_segred_scalar<T><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
-            K, reinterpret_cast<const T*>(SP), off, ctrl, out, pF, pC);
+        {
+            KernelTimer kt("k_segred_scalar", s);
+            k_segred_scalar<T><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
+                K, reinterpret_cast<const T*>(SP), off, ctrl, out, pF, pC);
+        }
         k_segred_scalar_long<T><<<dim3((unsigned)lg), dim3(256), 0, s>>>(off, num_out, pF, pC, out);
     } else {
-        k_segred_rows<T><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
-            K, reinterpret_cast<const uint32_t*>(SP), off, ctrl, values, row_len, out, pF, pC);
+        {
+            KernelTimer kt("k_segred_rows", s);
+            k_segred_rows<T><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
+                K, reinterpret_cast<const uint32_t*>(SP), off, ctrl, values, row_len, out, pF, pC);
+        }
         int64_t rg = cdiv(num_out, 256);
         if (rg > 4096) rg = 4096;
         k_segred_rows_long<T><<<dim3((unsigned)rg), dim3(256), 0, s>>>(off, num_out, row_len, pF,

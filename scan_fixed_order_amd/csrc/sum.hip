@@ -143,6 +143,7 @@ det_status sum_impl(const T* x, int64_t n, T* out, char* ws, hipStream_t s) {
         T* dst = (nchunks == 1) ? out : reinterpret_cast<T*>(ws);
         int64_t grid = nchunks;
         if (ov.grid_wgs > 0 && grid > ov.grid_wgs) grid = ov.grid_wgs;
+        KernelTimer kt(sizeof(T) == 4 ? "k_sum_chunks<f32>" : "k_sum_chunks<f64>", s);
         k_sum_chunks<T><<<dim3((unsigned)grid), dim3(256), 0, s>>>(src, m, clog2, nchunks, dst);
         det_status st = launch_status();
         if (st != DET_SUCCESS || nchunks == 1) return st;

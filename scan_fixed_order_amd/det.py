@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
     L.det_status_string.argtypes, L.det_status_string.restype = [i], ctypes.c_char_p
     L.det_debug_set_launch.argtypes, L.det_debug_set_launch.restype = [i, i], i
     L.det_debug_set_scan_anchors.argtypes, L.det_debug_set_scan_anchors.restype = [i, i], i
+    L.det_debug_kernel_timing.argtypes, L.det_debug_kernel_timing.restype = [i], i
+    L.det_debug_kernel_report.argtypes = [ctypes.c_char_p, sz]
+    L.det_debug_kernel_report.restype = sz
     _lib = L
     return L
 
@@ -223,3 +226,23 @@ def det_debug_set_launch(grid_wgs: int = 0, sum_chunk_log2: int = 0) -> None:
 def det_debug_set_scan_anchors(A: int = 0, A2: int = 0) -> None:
     """Test hook: scan anchor constants (0 = the spec's 256)."""
     _check(lib().det_debug_set_scan_anchors(A, A2), "det_debug_set_scan_anchors")
+
+
+def det_debug_kernel_timing(enable: bool) -> None:
+    """Test hook: bracket every library kernel launch with HIP events (drops earlier records)."""
+    _check(lib().det_debug_kernel_timing(1 if enable else 0), "det_debug_kernel_timing")
+
+
+def det_debug_kernel_report() -> dict:
+    """Wait for the recorded launches; {kernel: (launches, total_ms, average_ms)}."""
+    L = lib()
+    need = L.det_debug_kernel_report(None, 0)
+    buf = ctypes.create_string_buffer(need)
+    L.det_debug_kernel_report(buf, need)
+    rep = {}
+    for line in buf.value.decode().splitlines():
+        if line.startswith("#"):
+            raise RuntimeError("kernel timing: " + line[1:].strip())
+        name, cnt, tot, avg = line.rsplit(" ", 3)
+        rep[name] = (int(cnt), float(tot), float(avg))
+    return rep

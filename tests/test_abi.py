@@ -107,6 +107,10 @@ def test_debug_hook_range():
     assert lib.det_debug_set_scan_anchors(257, 0) == E_INVALID
     assert lib.det_debug_set_scan_anchors(0, -1) == E_INVALID
     assert lib.det_debug_set_scan_anchors(0, 0) == 0
+    assert lib.det_debug_kernel_timing(2) == E_INVALID
+    assert lib.det_debug_kernel_timing(-1) == E_INVALID
+    assert lib.det_debug_kernel_timing(0) == 0
+    assert det.det_debug_kernel_report() == {}          # nothing recorded: an empty report
 
 
 def test_binding_rejects_cpu_tensors_and_bad_dtypes():
