@@ -31,6 +31,21 @@ constexpr int kSegD = 8192;     // scalar: ranks per block
 constexpr int kRowD = 64;       // rows: member rows per block
 constexpr int kBuckets0 = 257;  // first pass: 256 digits + the out-of-range bucket
 
+// keys per thread of a radix chunk: 8192 keys for 4-byte payloads, 4096 for 8-byte ones.
+// Long chunks give long runs per bucket (32 keys on average for 256 buckets), so the
+// scattered writes leave mostly whole lines.
+template <typename P>
+constexpr int kItems = sizeof(P) == 4 ? 32 : 16;
+
+// Workgroup b runs on XCD b mod 8 (round-robin dispatch); give each XCD a contiguous range of
+// chunks, so the writes of consecutive chunks into a bucket's region meet in one L2 and leave
+// it as whole lines.  Any bijection is correct; this one only changes where the work runs.
+__device__ __forceinline__ int64_t xcd_chunk(int64_t b, int64_t nchunks) {
+    const int64_t x = b & 7, j = b >> 3;
+    const int64_t q = nchunks >> 3, r = nchunks & 7;
+    return x * q + (x < r ? x : r) + j;
+}
+
 __host__ __device__ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------- integer block helpers
@@ -67,63 +82,111 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s4
     return before + inc - v;
 }
 
-// ---------------------------------------------------------------- u32 exclusive scan
+// ---------------------------------------------------------------- histogram offsets
 
-constexpr int kU32Blk = 4096;
+// The digit histogram of a pass is row-major, hist[c * nb + d] = keys of chunk c with digit d,
+// so each workgroup writes its counts contiguously.  The scatter needs, for chunk c and digit
+// d, off[c][d] = (keys with a digit below d) + (keys with digit d in chunks before c): an
+// exclusive scan in digit-major order, done in four launches over blocks of kRowBlk rows:
+// column sums per row block (stored column-major), an exclusive scan of each column's block
+// sums, an exclusive scan of the digit totals, then each row block writes its offsets in
+// place.  Integers, so exact in any order.
+constexpr int kRowBlk = 128;
+constexpr int kRowBatch = 16;   // rows whose loads are in flight together
 
-__global__ __launch_bounds__(256) void k_u32_block_sums(const uint32_t* __restrict__ a, int64_t N,
-                                                        uint32_t* __restrict__ sums) {
-    __shared__ uint32_t s4[4];
-    const int64_t base = (int64_t)blockIdx.x * kU32Blk;
-    uint32_t s = 0;
-    for (int i = 0; i < kU32Blk / 256; ++i) {
-        const int64_t k = base + i * 256 + threadIdx.x;
-        if (k < N) s += a[k];
+// csum[d * nrb + rb] = sum over the rows of block rb of column d (thread t: column t, and
+// thread 0 also column 256 when nb = 257)
+__global__ __launch_bounds__(256) void k_hist_colsums(const uint32_t* __restrict__ hist,
+                                                      int64_t nrows, int nb, int64_t nrb,
+                                                      uint32_t* __restrict__ csum) {
+    const int t = threadIdx.x;
+    const bool extra = nb > 256 && t == 0;
+    const int64_t r0 = (int64_t)blockIdx.x * kRowBlk;
+    const int64_t r1 = (r0 + kRowBlk < nrows) ? r0 + kRowBlk : nrows;
+    uint32_t s0 = 0, s1 = 0;
+    for (int64_t r = r0; r < r1; r += kRowBatch) {
+        uint32_t v[kRowBatch], w[kRowBatch];
+#pragma unroll
+        for (int k = 0; k < kRowBatch; ++k) {
+            v[k] = (r + k < r1) ? hist[(r + k) * nb + t] : 0u;
+            w[k] = (extra && r + k < r1) ? hist[(r + k) * nb + 256] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < kRowBatch; ++k) {
+            s0 += v[k];
+            s1 += w[k];
+        }
     }
-    s = block_sum_u32(s, s4);
-    if (threadIdx.x == 0) sums[blockIdx.x] = s;
+    csum[(int64_t)t * nrb + blockIdx.x] = s0;
+    if (extra) csum[(int64_t)256 * nrb + blockIdx.x] = s1;
 }
 
-__global__ __launch_bounds__(256) void k_u32_scan_sums(uint32_t* __restrict__ sums, int64_t nb) {
+// column d = blockIdx.x: exclusive scan of its block sums in place; tot[d] = the column total
+__global__ __launch_bounds__(256) void k_hist_colscan(uint32_t* __restrict__ csum, int64_t nrb,
+                                                      uint32_t* __restrict__ tot) {
     __shared__ uint32_t s4[4];
+    uint32_t* col = csum + (int64_t)blockIdx.x * nrb;
     uint32_t carry = 0;
-    for (int64_t base = 0; base < nb; base += 256) {
+    for (int64_t base = 0; base < nrb; base += 256) {
         const int64_t k = base + threadIdx.x;
-        const uint32_t v = k < nb ? sums[k] : 0u;
-        uint32_t tot;
-        const uint32_t ex = block_excl_scan_u32(v, s4, &tot);
-        if (k < nb) sums[k] = carry + ex;
-        carry += tot;
+        const uint32_t v = k < nrb ? col[k] : 0u;
+        uint32_t total;
+        const uint32_t ex = block_excl_scan_u32(v, s4, &total);
+        if (k < nrb) col[k] = carry + ex;
+        carry += total;
     }
+    if (threadIdx.x == 0) tot[blockIdx.x] = carry;
 }
 
-__global__ __launch_bounds__(256) void k_u32_block_apply(uint32_t* __restrict__ a, int64_t N,
-                                                         const uint32_t* __restrict__ sums) {
+// tot[d] <- keys with a digit below d (d < nb <= 257; thread 0 also handles d = 256)
+__global__ __launch_bounds__(256) void k_hist_digitscan(uint32_t* __restrict__ tot, int nb) {
     __shared__ uint32_t s4[4];
-    constexpr int IPT = kU32Blk / 256;
-    const int64_t base = (int64_t)blockIdx.x * kU32Blk + (int64_t)threadIdx.x * IPT;
-    uint32_t v[IPT];
-    uint32_t tsum = 0;
+    const int t = threadIdx.x;
+    const uint32_t v = tot[t];
+    uint32_t total;
+    const uint32_t ex = block_excl_scan_u32(v, s4, &total);
+    tot[t] = ex;
+    if (nb > 256 && t == 0) tot[256] = total;
+}
+
+__global__ __launch_bounds__(256) void k_hist_apply(uint32_t* __restrict__ hist, int64_t nrows,
+                                                    int nb, int64_t nrb,
+                                                    const uint32_t* __restrict__ csum,
+                                                    const uint32_t* __restrict__ tot) {
+    const int t = threadIdx.x;
+    const bool extra = nb > 256 && t == 0;
+    const int64_t r0 = (int64_t)blockIdx.x * kRowBlk;
+    const int64_t r1 = (r0 + kRowBlk < nrows) ? r0 + kRowBlk : nrows;
+    uint32_t run0 = tot[t] + csum[(int64_t)t * nrb + blockIdx.x];
+    uint32_t run1 = extra ? tot[256] + csum[(int64_t)256 * nrb + blockIdx.x] : 0u;
+    for (int64_t r = r0; r < r1; r += kRowBatch) {
+        uint32_t v[kRowBatch], w[kRowBatch];
 #pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-        v[i] = (base + i < N) ? a[base + i] : 0u;
-        tsum += v[i];
-    }
-    uint32_t tot;
-    uint32_t run = block_excl_scan_u32(tsum, s4, &tot) + sums[blockIdx.x];
+        for (int k = 0; k < kRowBatch; ++k) {
+            v[k] = (r + k < r1) ? hist[(r + k) * nb + t] : 0u;
+            w[k] = (extra && r + k < r1) ? hist[(r + k) * nb + 256] : 0u;
+        }
 #pragma unroll
-    for (int i = 0; i < IPT; ++i) {
-        if (base + i < N) a[base + i] = run;
-        run += v[i];
+        for (int k = 0; k < kRowBatch; ++k) {
+            if (r + k < r1) {
+                hist[(r + k) * nb + t] = run0;
+                if (extra) hist[(r + k) * nb + 256] = run1;
+            }
+            run0 += v[k];
+            run1 += w[k];
+        }
     }
 }
 
-det_status u32_exclusive_scan(uint32_t* a, int64_t N, uint32_t* sums, hipStream_t s) {
-    const int64_t nb = cdiv(N, kU32Blk);
-    KernelTimer kt("k_u32_exclusive_scan", s);
-    k_u32_block_sums<<<dim3((unsigned)nb), dim3(256), 0, s>>>(a, N, sums);
-    k_u32_scan_sums<<<1, 256, 0, s>>>(sums, nb);
-    k_u32_block_apply<<<dim3((unsigned)nb), dim3(256), 0, s>>>(a, N, sums);
+// csum needs nb * nrb words, tot nb words (nb <= 257)
+det_status hist_offsets(uint32_t* hist, int64_t nrows, int nb, uint32_t* csum, uint32_t* tot,
+                        hipStream_t s) {
+    const int64_t nrb = cdiv(nrows, kRowBlk);
+    KernelTimer kt("k_hist_offsets", s);
+    k_hist_colsums<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum);
+    k_hist_colscan<<<dim3((unsigned)nb), dim3(256), 0, s>>>(csum, nrb, tot);
+    k_hist_digitscan<<<1, 256, 0, s>>>(tot, nb);
+    k_hist_apply<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum, tot);
     return launch_status();
 }
 
@@ -162,7 +225,7 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__
         }
     }
     __syncthreads();
-    for (int d = threadIdx.x; d < nb; d += 256) hist[(int64_t)d * nchunks + blockIdx.x] = cnt[d];
+    for (int d = threadIdx.x; d < nb; d += 256) hist[(int64_t)blockIdx.x * nb + d] = cnt[d];
 }
 
 // P: payload word (uint32_t: f32 value bits or source row; uint64_t: f64 value bits)
@@ -172,7 +235,7 @@ __global__ __launch_bounds__(256) void k_radix_scatter(
     uint32_t* __restrict__ keys_out, P* __restrict__ pay_out, int64_t n,
     const uint32_t* __restrict__ nvalid, uint32_t B, int shift, int64_t nchunks,
     const uint32_t* __restrict__ hist_ex) {
-    constexpr int IPT = sizeof(P) == 4 ? 32 : 16;   // items per thread
+    constexpr int IPT = kItems<P>;                   // items per thread
     constexpr int H = 256 * IPT;                     // elements per chunk
     constexpr int WE = 64 * IPT;                     // elements per wave
     constexpr int NB = FIRST ? kBuckets0 : 256;
@@ -185,10 +248,13 @@ __global__ __launch_bounds__(256) void k_radix_scatter(
     __shared__ uint32_t s4[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t c = blockIdx.x;
+    const int64_t c = xcd_chunk(blockIdx.x, nchunks);
     const int64_t m = FIRST ? n : (int64_t)*nvalid;
     const int64_t base = c * H;
     if (base >= m) return;
+    // this chunk's bucket offsets, fetched with the keys
+    const uint32_t off0 = hist_ex[c * NB + tid];
+    const uint32_t off1 = (NB > 256 && tid == 0) ? hist_ex[c * NB + 256] : 0u;
 
     for (int i = tid; i < 4 * kBuckets0; i += 256) (&s_cnt[0][0])[i] = 0u;
     __syncthreads();
@@ -260,10 +326,10 @@ __global__ __launch_bounds__(256) void k_radix_scatter(
     uint32_t total;
     const uint32_t ds = block_excl_scan_u32(tot_lo, s4, &total);
     s_dstart[tid] = ds;
-    s_gbase[tid] = (int64_t)hist_ex[(int64_t)tid * nchunks + c] - (int64_t)ds;
+    s_gbase[tid] = (int64_t)off0 - (int64_t)ds;
     if (NB > 256 && tid == 0) {
         s_dstart[256] = total;
-        s_gbase[256] = (int64_t)hist_ex[(int64_t)256 * nchunks + c] - (int64_t)total;
+        s_gbase[256] = (int64_t)off1 - (int64_t)total;
     }
     (void)tot_hi;
     __syncthreads();
@@ -690,10 +756,10 @@ SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
     SLayout L;
     const bool rows = row_len > 1;
     const size_t pw = rows ? 4 : dtype_size(dt);    // payload bytes
-    L.H = 256 * (pw == 4 ? 32 : 16);
+    L.H = 256 * (pw == 4 ? kItems<uint32_t> : kItems<uint64_t>);
     L.nchunks = cdiv(n > 0 ? n : 1, L.H);
     L.nhist = (int64_t)kBuckets0 * L.nchunks;
-    L.nsums = cdiv(L.nhist, kU32Blk);
+    L.nsums = (int64_t)kBuckets0 * cdiv(L.nchunks, kRowBlk) + 512;   // column sums + totals
     const int64_t D = rows ? kRowD : kSegD;
     L.nrange = cdiv(n > 0 ? n : 1, D);
     const size_t es = dtype_size(dt);
@@ -764,9 +830,10 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
                 k_radix_hist<false><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb, L.nchunks,
                                                          (int)L.H, hist);
         }
-        det_status st = u32_exclusive_scan(hist, (int64_t)nb * L.nchunks, sums, s);
+        det_status st = hist_offsets(hist, L.nchunks, nb, sums + 512, sums, s);
         if (st != DET_SUCCESS) return st;
-        if (first) k_copy_word<<<1, 1, 0, s>>>(hist + (int64_t)256 * L.nchunks, ctrl);
+        // valid keys = offset of the out-of-range bucket in chunk 0
+        if (first) k_copy_word<<<1, 1, 0, s>>>(hist + 256, ctrl);
         KernelTimer kt("k_radix_scatter", s);
         if (first)
             k_radix_scatter<P, true, ROWS><<<grid, 256, 0, s>>>(kin, pin, keys[p & 1], pay[p & 1], n,
