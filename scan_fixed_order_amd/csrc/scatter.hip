@@ -400,43 +400,44 @@ __global__ void k_write_skipped_all(int64_t* n_skipped, int64_t n) {
 
 // PW over p[0 .. len), len <= 8192 (element 0 replaced by v0 when use_v0): 32 blocks of
 // 256; lane l of block i holds elements 256 i + 4 l .. + 4 combined as (a0 + a1) + (a2 + a3),
-// then the wave butterfly.  Blocks combine by a 3-level tree inside each group of 8 and a
-// 2-level tree over the 4 groups (together the 5-level tree over the 32 blocks; identity for
-// blocks past len).  Uniform result.
+// then the wave butterfly; the 32 block values meet in a 5-level tree (identity for blocks
+// past len).  The loads of G blocks are in flight together.  Uniform result.
 template <typename T>
 __device__ __forceinline__ T wave_pw_range(const T* __restrict__ p, int64_t len, int lane,
                                            bool use_v0, T v0) {
-    T g[4];
+    constexpr int G = sizeof(T) == 4 ? 16 : 8;
+    T b[32];
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-        g[gi] = ident<T>();
-        if ((int64_t)gi * 2048 < len) {
-            T b[8];
+    for (int g0 = 0; g0 < 32; g0 += G) {
+        if ((int64_t)g0 * 256 >= len) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int blk = (gi * 8 + i) * 256;
-                b[i] = ident<T>();
-                if (blk < len) {
-                    const T* q = p + blk + 4 * lane;
-                    T a0, a1, a2, a3;
-                    if (blk + 256 <= len) {
-                        a0 = q[0]; a1 = q[1]; a2 = q[2]; a3 = q[3];
-                    } else {
-                        const int rem = (int)(len - blk) - 4 * lane;
-                        a0 = rem > 0 ? q[0] : ident<T>();
-                        a1 = rem > 1 ? q[1] : ident<T>();
-                        a2 = rem > 2 ? q[2] : ident<T>();
-                        a3 = rem > 3 ? q[3] : ident<T>();
-                    }
-                    if (use_v0 && blk == 0 && lane == 0) a0 = v0;
-                    b[i] = wave_pw<T>((a0 + a1) + (a2 + a3));
-                }
-            }
-            g[gi] = ((b[0] + b[1]) + (b[2] + b[3])) + ((b[4] + b[5]) + (b[6] + b[7]));
+            for (int i = 0; i < G; ++i) b[g0 + i] = ident<T>();
+            continue;
+        }
+        T a[G][4];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const int blk = (g0 + i) * 256;
+            const T* q = p + blk + 4 * lane;
+            const int rem = (int)((len - blk) < 256 ? (len - blk) : 256) - 4 * lane;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[i][r] = rem > r ? q[r] : ident<T>();
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            if (use_v0 && g0 + i == 0 && lane == 0) a[i][0] = v0;
+            b[g0 + i] = (int64_t)(g0 + i) * 256 < len
+                            ? wave_pw<T>((a[i][0] + a[i][1]) + (a[i][2] + a[i][3]))
+                            : ident<T>();
         }
         __builtin_amdgcn_sched_barrier(0);
     }
-    return (g[0] + g[1]) + (g[2] + g[3]);
+#pragma unroll
+    for (int w = 32; w > 1; w /= 2) {
+#pragma unroll
+        for (int i = 0; i < w / 2; ++i) b[i] = b[2 * i] + b[2 * i + 1];
+    }
+    return b[0];
 }
 
 // PW over p[0 .. len) for any len (element 0 replaced by v0 when use_v0): blocks of 8192
@@ -515,12 +516,31 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const uint32_t* __restric
                                                        T* __restrict__ pC) {
     __shared__ uint32_t s_big[kSegD / 32 + 2];
     __shared__ uint32_t s_nbig;
+    __shared__ uint32_t s_key[kSegD];
+    __shared__ uint32_t s_prev;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t m = *nvalid;
     const int64_t lo = (int64_t)blockIdx.x * kSegD;
     if (lo >= m) return;
     const int64_t hi = (lo + kSegD < m) ? lo + kSegD : m;
-    if (tid == 0) s_nbig = 0u;
+    if (tid == 0) {
+        s_nbig = 0u;
+        s_prev = lo > 0 ? K[lo - 1] : ~K[lo];
+    }
+    // the range's keys into LDS in one round trip (16-byte loads when the range is whole; K is
+    // 256-byte aligned and lo a multiple of kSegD)
+    if (hi - lo == kSegD) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 q[kSegD / 1024];
+#pragma unroll
+        for (int i = 0; i < kSegD / 1024; ++i)
+            q[i] = reinterpret_cast<const u32x4*>(K + lo)[i * 256 + tid];
+#pragma unroll
+        for (int i = 0; i < kSegD / 1024; ++i)
+            reinterpret_cast<u32x4*>(s_key)[i * 256 + tid] = q[i];
+    } else {
+        for (int i = tid; i < (int)(hi - lo); i += 256) s_key[i] = K[lo + i];
+    }
     __syncthreads();
 
     // a block starts at every segment start, and at most once more inside this range: the
@@ -536,10 +556,11 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const uint32_t* __restric
         }
     };
     for (int i = 0; i < kSegD / 256; ++i) {
-        const int64_t p = lo + i * 256 + tid;
+        const int e = i * 256 + tid;
+        const int64_t p = lo + e;
         if (p < hi) {
-            const uint32_t b = K[p];
-            if (p == 0 || K[p - 1] != b) item(p, b);
+            const uint32_t b = s_key[e];
+            if ((e == 0 ? s_prev : s_key[e - 1]) != b) item(p, b);
             if (p == lo) {
                 const int64_t s0 = off[b];
                 if (s0 < lo) {
@@ -554,7 +575,7 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const uint32_t* __restric
     const int nbig = (int)s_nbig;
     for (int it = wave; it < nbig; it += 4) {
         const int64_t ps = lo + s_big[it];
-        const uint32_t b = K[ps];
+        const uint32_t b = s_key[s_big[it]];
         const int64_t seg_s = off[b], seg_e = off[b + 1];
         const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
         const T S = wave_pw_range<T>(V + ps, len, lane, false, ident<T>());
