@@ -212,6 +212,35 @@ __device__ __forceinline__ Seg<T> block_pw(Seg<T> v, int lane, int wave, Seg<T>*
     return r;
 }
 
+// Two block_pw at once (leaf i = thread i of each), sharing the exchange and its barriers;
+// s_tmp holds 2 * 4 entries.
+template <bool SEG, typename T>
+__device__ __forceinline__ void block_pw2(Seg<T> v, Seg<T> w, int lane, int wave, Seg<T>* s_tmp,
+                                          Seg<T>& rv, Seg<T>& rw) {
+    v = bfly<1, SEG>(v, lane);
+    w = bfly<1, SEG>(w, lane);
+    v = bfly<2, SEG>(v, lane);
+    w = bfly<2, SEG>(w, lane);
+    v = bfly<4, SEG>(v, lane);
+    w = bfly<4, SEG>(w, lane);
+    v = bfly<8, SEG>(v, lane);
+    w = bfly<8, SEG>(w, lane);
+    v = bfly<16, SEG>(v, lane);
+    w = bfly<16, SEG>(w, lane);
+    const Seg<T> vlo{readlane(v.v, 0), SEG ? readlane(v.f, 0) : 0u};
+    const Seg<T> vhi{readlane(v.v, 32), SEG ? readlane(v.f, 32) : 0u};
+    const Seg<T> wlo{readlane(w.v, 0), SEG ? readlane(w.f, 0) : 0u};
+    const Seg<T> whi{readlane(w.v, 32), SEG ? readlane(w.f, 32) : 0u};
+    if (lane == 0) {
+        s_tmp[wave] = op<SEG>(vlo, vhi);
+        s_tmp[4 + wave] = op<SEG>(wlo, whi);
+    }
+    __syncthreads();
+    rv = op<SEG>(op<SEG>(s_tmp[0], s_tmp[1]), op<SEG>(s_tmp[2], s_tmp[3]));
+    rw = op<SEG>(op<SEG>(s_tmp[4], s_tmp[5]), op<SEG>(s_tmp[6], s_tmp[7]));
+    __syncthreads();
+}
+
 // ---------------------------------------------------------------- segment heads
 
 // First k in [0, cnt) with offs[k] >= target (cnt if none).  All threads take part.
@@ -391,25 +420,51 @@ __device__ __forceinline__ void readout_incl(T* __restrict__ y, int64_t n, int64
 }
 
 // Whole-wave readout, exclusive: the inclusive value of flipped position f goes to f + 1
-// (+0.0 where f + 1 is a segment head).
+// (+0.0 where f + 1 is a segment head).  The wave's output is one contiguous range of original
+// addresses; its 16-byte-aligned interior is written with 16-byte non-temporal stores, the at
+// most 3 + 3 elements at its ends with element stores.
+template <typename T, bool SEG, bool REV>
+__device__ __forceinline__ T excl_value(int64_t n, int64_t F0, int64_t fw, int64_t addr,
+                                       const T* pk, const T* xs, const uint32_t* hbs,
+                                       const uint32_t* s_heads) {
+    const int64_t fp = REV ? n - 1 - addr : addr;   // flipped position written
+    const int e = (int)(fp - 1 - fw);               // wave element whose inclusive value it takes
+    if constexpr (SEG) {
+        const int bit = (int)(fp - F0);
+        if ((s_heads[bit >> 5] >> (bit & 31)) & 1u) return T(0.0);
+    }
+    return combine_at<T, SEG>(pk, xs, hbs, e);
+}
+
 template <typename T, bool SEG, bool REV>
 __device__ __forceinline__ void readout_excl(T* __restrict__ y, int64_t n, int64_t F0, int64_t fw,
                                              const T* pk, const T* xs, const uint32_t* hbs,
                                              const uint32_t* s_heads, int lane) {
-    const int64_t left = n - (fw + 1);
-    const int valid = left < 0 ? 0 : (left < kWaveElems ? (int)left : kWaveElems);
-    T* yb = REV ? y + (n - 2 - fw) : y + (fw + 1);
-#pragma unroll 8
-    for (int r = 0; r < kWaveElems / 64; ++r) {
-        const int e = r * 64 + lane;
-        if (e < valid) {
-            T v = combine_at<T, SEG>(pk, xs, hbs, e);
-            if constexpr (SEG) {
-                const int bit = (int)(fw + e + 1 - F0);
-                if ((s_heads[bit >> 5] >> (bit & 31)) & 1u) v = T(0.0);
-            }
-            if (REV) yb[-e] = v;
-            else yb[e] = v;
+    // flipped positions fw + 1 .. fw + 2048, clipped to n - 1; as original addresses [lo, hi)
+    const int64_t last = (fw + kWaveElems < n - 1) ? fw + kWaveElems : n - 1;
+    if (last < fw + 1) return;
+    const int64_t lo = REV ? n - 1 - last : fw + 1;
+    const int64_t hi = REV ? n - 1 - fw : last + 1;
+    // interior [A, Z): starts at the first 16-byte-aligned element, whole groups of 4
+    constexpr int64_t EPV = 16 / sizeof(T);   // elements per 16 bytes
+    const int64_t ye = (int64_t)(reinterpret_cast<uintptr_t>(y) / sizeof(T));
+    int64_t A = lo + ((EPV - ((ye + lo) % EPV)) % EPV);
+    if (A > hi) A = hi;
+    const int64_t Z = A + ((hi - A) / 4) * 4;
+    for (int64_t k = lo + lane; k < A; k += 64)
+        y[k] = excl_value<T, SEG, REV>(n, F0, fw, k, pk, xs, hbs, s_heads);
+    for (int64_t k = Z + lane; k < hi; k += 64)
+        y[k] = excl_value<T, SEG, REV>(n, F0, fw, k, pk, xs, hbs, s_heads);
+    const int64_t ngroups = (Z - A) / 4;   // at most 512
+#pragma unroll
+    for (int r = 0; r < kWaveElems / 256; ++r) {
+        const int64_t gi = (int64_t)r * 64 + lane;
+        if (gi < ngroups) {
+            const int64_t g = A + 4 * gi;
+            nt_store4<T>(y + g, excl_value<T, SEG, REV>(n, F0, fw, g, pk, xs, hbs, s_heads),
+                         excl_value<T, SEG, REV>(n, F0, fw, g + 1, pk, xs, hbs, s_heads),
+                         excl_value<T, SEG, REV>(n, F0, fw, g + 2, pk, xs, hbs, s_heads),
+                         excl_value<T, SEG, REV>(n, F0, fw, g + 3, pk, xs, hbs, s_heads));
         }
     }
 }
@@ -526,7 +581,8 @@ __device__ __forceinline__ void finish_tile(const ScanArgs<T>& a, int j, const L
     Seg<T> mine = seg_ident<T>(), gmine = seg_ident<T>();
     poll_finish<T>(pl, a.agg + (size_t)(lb.q * a.A + tid) * SW, tid < lb.cnt, mine,
                    a.gtot + (size_t)(lb.Q * a.A2 + tid) * SW, tid < lb.qcnt, gmine, err);
-    const Seg<T> Wj = block_pw<SEG, T>(mine, lane, wave, s_tmp);
+    Seg<T> Wj, WG;
+    block_pw2<SEG, T>(mine, gmine, lane, wave, s_tmp, Wj, WG);
     // the interval's last tile publishes the interval total G_q (needs no carry)
     const bool ianchor = (lb.cnt == a.A - 1) && (j + 1 < a.ntiles);
     Seg<T> Gq = seg_ident<T>();
@@ -534,20 +590,20 @@ __device__ __forceinline__ void finish_tile(const ScanArgs<T>& a, int j, const L
         Gq = block_pw<SEG, T>(tid == a.A - 1 ? agg : mine, lane, wave, s_tmp);
         if (tid == 0) publish<T>(a.gtot + (size_t)lb.q * SW, Gq);
     }
-    const Seg<T> WG = block_pw<SEG, T>(gmine, lane, wave, s_tmp);
     const bool sanchor = ianchor && (lb.qcnt == a.A2 - 1);
     Seg<T> H = seg_ident<T>();
     if (sanchor) H = block_pw<SEG, T>(tid == a.A2 - 1 ? Gq : gmine, lane, wave, s_tmp);
 
-    // carry into the super-interval; its last tile forwards the next one
-    if (tid == 0) {
-        const Seg<T> CC =
-            (lb.Q == 0) ? seg_ident<T>() : wait_slot<T>(a.carry + (size_t)lb.Q * SW, err);
-        if (sanchor) publish<T>(a.carry + (size_t)(lb.Q + 1) * SW, op<SEG>(CC, H));
-        s_carry = CC;
+    // carry into the super-interval (the identity for the first); its last tile forwards the
+    // next one
+    Seg<T> CC = seg_ident<T>();
+    if (lb.Q > 0) {
+        if (tid == 0) s_carry = wait_slot<T>(a.carry + (size_t)lb.Q * SW, err);
+        __syncthreads();
+        CC = s_carry;
     }
-    __syncthreads();
-    const Seg<T> E = op<SEG>(op<SEG>(s_carry, WG), Wj);
+    if (sanchor && tid == 0) publish<T>(a.carry + (size_t)(lb.Q + 1) * SW, op<SEG>(CC, H));
+    const Seg<T> E = op<SEG>(op<SEG>(CC, WG), Wj);
     xs[lane] = op<SEG>(op<SEG>(E, P), p).v;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -594,7 +650,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     __shared__ T s_x[kScanWaves][kScanW];
     __shared__ uint32_t s_hbits[SEG ? kScanWaves : 1][kScanW];
     __shared__ uint32_t s_heads[2][SEG ? kHeadWords : 1];
-    __shared__ Seg<T> s_tmp[kScanWaves];
+    __shared__ Seg<T> s_tmp[2 * kScanWaves];
     __shared__ Seg<T> s_wtot[kScanWaves];
     __shared__ Seg<T> s_carry;
     __shared__ int s_tick[2];

@@ -167,3 +167,24 @@ def test_small_anchor_variants(dev, dtype, A, A2):
     finally:
         det.det_debug_set_scan_anchors(0, 0)
         det.det_debug_set_launch(0, 0)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_exclusive_into_unaligned_output(dev, dtype):
+    # the exclusive readout aligns its 16-byte stores to y's address: y views at every
+    # element offset within 16 bytes, both directions, ragged n
+    n = 2 * A * T // 64 + 4099
+    x = workloads.scan_values(n, dtype, seed=8)
+    offs = random_offsets(n, 700, seed=8)
+    t = torch.from_numpy(x).to(dev)
+    o = torch.from_numpy(offs).to(dev)
+    buf = torch.empty(n + 8, dtype=t.dtype, device=dev)
+    for k in range(4):
+        for rev in (False, True):
+            y = buf[k:k + n]
+            det.det_scan(t, y=y, exclusive=True, reverse=rev)
+            want = oracle.scan(x, exclusive=True, reverse=rev)
+            assert bits_equal(y.cpu().numpy(), want), (k, rev, first_mismatch(y.cpu().numpy(), want))
+            det.det_scan(t, y=y, exclusive=True, reverse=rev, offsets=o)
+            want = oracle.scan(x, exclusive=True, reverse=rev, offsets=offs)
+            assert bits_equal(y.cpu().numpy(), want), (k, rev, "seg")
