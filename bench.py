@@ -14,7 +14,9 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                 kernel source (read from profiles/, null when that source has changed since);
   kernels       every library kernel of the step: launches per step, average ms;
   ops           per operation: time, GB/s, Gelem/s, fraction of 8 TB/s, the non-deterministic
-                baseline's time on the same input and the deterministic-mode overhead;
+                baseline's time on the same input (atomic-tail sum, per-element atomic
+                scatter, the ROCm library scan), the deterministic-mode overhead, and the number
+                of distinct results over repeated runs of each;
   cpu_baseline  the CPU oracle (single thread) on the same workload, timed on the host.
 """
 import argparse
@@ -42,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baselines", action="store_true")
     ap.add_argument("--only", default="", help="comma list of sum,scan,scatter (profiling)")
+    ap.add_argument("--repeat-runs", type=int, default=100,
+                    help="runs whose distinct results are counted (library and baselines)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of 2^log2n f32 (1 GiB each way at 2^28): "
                          "the known-size kernel that scales rocprofv3 byte counters")
@@ -186,19 +190,20 @@ def main():
 
     # ---------------------------------------------------------------- non-deterministic baselines
     base_ms = {}
+    distinct = {}
     if not args.no_baselines:
         bl = ctypes.CDLL(os.path.join(ROOT, "scan_fixed_order_amd", "libdet_baselines.so"))
         sp = ctypes.c_void_p(stream.cuda_stream)
         vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
         tmp = torch.empty((), dtype=torch.float32, device=dev)
         out_b = torch.zeros(B, dtype=torch.float32, device=dev)
-        bl.detbase_dlb_scan_workspace_size.restype = ctypes.c_size_t
-        wsb = torch.empty(bl.detbase_dlb_scan_workspace_size(ctypes.c_int64(n)), dtype=torch.uint8,
-                          device=dev)
+        bl.detbase_lib_scan_workspace_size.restype = ctypes.c_size_t
+        wsb_bytes = bl.detbase_lib_scan_workspace_size(ctypes.c_int64(n))
+        wsb = torch.empty(max(wsb_bytes, 256), dtype=torch.uint8, device=dev)
         calls = {
             "sum": lambda: bl.detbase_atomic_sum(vp(g["x_sum"]), ctypes.c_int64(n), 0, vp(tmp), sp),
-            "scan": lambda: bl.detbase_dlb_scan(vp(g["x_scan"]), vp(y_scan), ctypes.c_int64(n),
-                                                vp(wsb), sp),
+            "scan": lambda: bl.detbase_lib_scan(vp(g["x_scan"]), vp(y_scan), ctypes.c_int64(n),
+                                                vp(wsb), ctypes.c_size_t(wsb_bytes), sp),
             "scatter": lambda: bl.detbase_atomic_scatter(vp(g["v_sc"]), vp(g["b_sc"]),
                                                          ctypes.c_int64(n), 0, vp(out_b),
                                                          ctypes.c_int64(B), sp),
@@ -218,6 +223,30 @@ def main():
             base_ms[name] = a.elapsed_time(b) / args.steps
         log("baselines timed")
 
+        # distinct results over repeated runs: the library and the baselines on the same input
+        # (the scan's output compared on its last 2^20 elements, which depend on every input)
+        import hashlib as _h
+
+        def digest(t):
+            return _h.sha256(t.cpu().numpy().tobytes()).hexdigest()
+
+        tail = min(n, 1 << 20)
+        probes = {
+            "sum": (lambda: (det.det_sum(g["x_sum"], out=s_out, ws=ws), s_out)[1],
+                    lambda: (calls["sum"](), tmp)[1]),
+            "scan": (lambda: det.det_scan(g["x_scan"], y=y_scan, ws=ws)[-tail:],
+                     lambda: (calls["scan"](), y_scan)[1][-tail:]),
+            "scatter": (lambda: (out_sc.zero_(), det.det_scatter_add(g["v_sc"], g["b_sc"], out_sc,
+                                                                      ws=ws))[1],
+                        lambda: (out_b.zero_(), calls["scatter"](), out_b)[2]),
+        }
+        for name, _, _ in ops:
+            dfn, bfn = probes[name]
+            hashes_det = {digest(dfn()) for _ in range(args.repeat_runs)}
+            hashes_base = {digest(bfn()) for _ in range(args.repeat_runs)}
+            distinct[name] = {"det": len(hashes_det), "nondet_baseline": len(hashes_base)}
+        log(f"repeatability over {args.repeat_runs} runs: {distinct}")
+
     # ---------------------------------------------------------------- per-op report
     op_rep = {}
     for name, _, bts in ops:
@@ -228,6 +257,8 @@ def main():
         if name in base_ms:
             r["nondet_baseline_ms"] = round(base_ms[name], 4)
             r["det_overhead"] = round(ms / base_ms[name] - 1.0, 4)
+        if name in distinct:
+            r["distinct_results"] = dict(distinct[name], runs=args.repeat_runs)
         op_rep[name] = r
 
     # ---------------------------------------------------------------- dominant kernel
