@@ -204,8 +204,11 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__
                                                     const uint32_t* __restrict__ nvalid, uint32_t B,
                                                     int shift, int nb, int64_t nchunks, int H,
                                                     uint32_t* __restrict__ hist) {
-    __shared__ uint32_t cnt[kBuckets0];
-    for (int i = threadIdx.x; i < kBuckets0; i += 256) cnt[i] = 0u;
+    // one histogram per wave (fewer LDS atomics on the same counter); a wave whose valid keys
+    // all share one digit adds them with a single atomic (skewed and contended inputs)
+    __shared__ uint32_t cnt[4][kBuckets0];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < 4 * kBuckets0; i += 256) (&cnt[0][0])[i] = 0u;
     __syncthreads();
     const int64_t m = FIRST ? n : (int64_t)*nvalid;
     const int64_t base = (int64_t)blockIdx.x * H;
@@ -220,12 +223,22 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int64_t p = base + i0 + k * 256 + threadIdx.x;
-            if (i0 + k * 256 + (int)threadIdx.x < H && p < m)
-                atomicAdd(&cnt[digit_of<FIRST>(kb[k], B, shift)], 1u);
+            const bool valid = i0 + k * 256 + (int)threadIdx.x < H && p < m;
+            const int d = digit_of<FIRST>(kb[k], B, shift);
+            const uint64_t vm = __ballot(valid);
+            if (vm == 0ull) continue;
+            const int first = __ffsll((long long)vm) - 1;
+            const int d0 = __shfl(d, first, 64);
+            if (__ballot(valid && d == d0) == vm) {
+                if (lane == first) atomicAdd(&cnt[wave][d0], (uint32_t)__popcll(vm));
+            } else if (valid) {
+                atomicAdd(&cnt[wave][d], 1u);
+            }
         }
     }
     __syncthreads();
-    for (int d = threadIdx.x; d < nb; d += 256) hist[(int64_t)blockIdx.x * nb + d] = cnt[d];
+    for (int d = threadIdx.x; d < nb; d += 256)
+        hist[(int64_t)blockIdx.x * nb + d] = (cnt[0][d] + cnt[1][d]) + (cnt[2][d] + cnt[3][d]);
 }
 
 // P: payload word (uint32_t: f32 value bits or source row; uint64_t: f64 value bits)
