@@ -102,6 +102,14 @@ det_status det_scan(const void* x, void* y, int64_t n, det_dtype dtype, unsigned
                     const int64_t* seg_offsets, int64_t num_segments, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* Health word of the last det_scan run in workspace ws, for callers that want to verify it.
+ * A scan's waits on its predecessors are bounded; a wait that runs past its bound (only a
+ * hardware fault or broken offsets precondition can cause one) sets this word and leaves y
+ * unspecified.  Enqueues on `stream` a copy of the word into *out (device int32: 0 = every
+ * wait ended normally, 1 = some wait gave up); returns without waiting.  ws: the workspace
+ * the scan used (device); out: device int32 (written).  DET_ERROR_INVALID_VALUE for NULL. */
+det_status det_scan_error(const void* ws, int32_t* out, void* stream);
+
 /* ------------------------------------------------------------------ scatter-add */
 
 /* Bytes of workspace det_scatter_add needs. */

@@ -153,6 +153,11 @@ det_status det_scan(const void* x, void* y, int64_t n, det_dtype dtype, unsigned
                        static_cast<hipStream_t>(stream));
 }
 
+det_status det_scan_error(const void* ws, int32_t* out, void* stream) {
+    if (!ws || !out) return DET_ERROR_INVALID_VALUE;
+    return scan_error(ws, out, static_cast<hipStream_t>(stream));
+}
+
 size_t det_scatter_add_workspace_size(int64_t n, int64_t num_out, int64_t row_len,
                                       det_dtype dtype) {
     if (n < 0 || n > DET_MAX_N || num_out < 0 || num_out > DET_MAX_N || row_len < 1 ||

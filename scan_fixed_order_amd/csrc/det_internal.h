@@ -36,6 +36,7 @@ constexpr int kScanA = 256;      // tiles per anchor interval
 constexpr int kScanA2 = 256;     // anchor intervals per super-interval
 
 size_t scan_workspace(int64_t n, det_dtype dt, unsigned flags, int64_t num_segments);
+det_status scan_error(const void* ws, int32_t* out, hipStream_t s);
 det_status scan_launch(const void* x, void* y, int64_t n, det_dtype dt, unsigned flags,
                        const int64_t* offs, int64_t nseg, void* ws, size_t ws_bytes,
                        hipStream_t s);

@@ -744,6 +744,10 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     }
 }
 
+__global__ void k_copy_error(const uint32_t* err, int32_t* out) {
+    out[0] = (int32_t)(err[0] != 0u);
+}
+
 __global__ void k_zero_words(uint64_t* p, int64_t nwords) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -839,6 +843,13 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
 }
 
 }  // namespace
+
+det_status scan_error(const void* ws, int32_t* out, hipStream_t s) {
+    const uint32_t* err = reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) +
+                                                            kCounters * kCounterStride * 4);
+    k_copy_error<<<1, 1, 0, s>>>(err, out);
+    return launch_status();
+}
 
 size_t scan_workspace(int64_t n, det_dtype dt, unsigned flags, int64_t num_segments) {
     (void)flags;

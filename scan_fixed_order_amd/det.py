@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
     L.det_spec_constants.argtypes = [ctypes.POINTER(i64)] * 4
     L.det_spec_constants.restype = None
     L.det_status_string.argtypes, L.det_status_string.restype = [i], ctypes.c_char_p
+    L.det_scan_error.argtypes, L.det_scan_error.restype = [p, p, p], i
     L.det_debug_set_launch.argtypes, L.det_debug_set_launch.restype = [i, i], i
     L.det_debug_set_scan_anchors.argtypes, L.det_debug_set_scan_anchors.restype = [i, i], i
     L.det_debug_kernel_timing.argtypes, L.det_debug_kernel_timing.restype = [i], i
@@ -157,6 +158,13 @@ def det_scan(x: torch.Tensor, y: Optional[torch.Tensor] = None, exclusive: bool 
     _check(lib().det_scan(_dev_ptr(x), _dev_ptr(y), n, dt, flags, _dev_ptr(offsets), nseg,
                           _dev_ptr(w), w.numel(), _stream(x.device)), "det_scan")
     return y
+
+
+def det_scan_error(ws: torch.Tensor) -> torch.Tensor:
+    """Health word of the last scan run in workspace ``ws`` (device int32: 0 = normal)."""
+    out = torch.empty((), dtype=torch.int32, device=ws.device)
+    _check(lib().det_scan_error(_dev_ptr(ws), _dev_ptr(out), _stream(ws.device)), "det_scan_error")
+    return out
 
 
 # ------------------------------------------------------------------ scatter-add

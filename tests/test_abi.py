@@ -82,6 +82,8 @@ def test_validation_errors_enqueue_nothing():
     assert lib.det_scan(FAKE, ctypes.c_void_p(0x900000), 1 << 20, 0, 0, NULL, 0, ws, 8,
                         NULL) == E_WORKSPACE
     assert lib.det_scan(FAKE, FAKE, 10, 3, 0, NULL, 0, ws, 1 << 20, NULL) == E_UNSUPPORTED
+    assert lib.det_scan_error(NULL, FAKE, NULL) == E_INVALID
+    assert lib.det_scan_error(FAKE, NULL, NULL) == E_INVALID
     # scatter
     sa = lib.det_scatter_add
     assert sa(FAKE, FAKE, 10, 0, 0, ctypes.c_void_p(0x900000), 4, NULL, NULL, ws, 1 << 30,

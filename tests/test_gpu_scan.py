@@ -188,3 +188,20 @@ def test_exclusive_into_unaligned_output(dev, dtype):
             det.det_scan(t, y=y, exclusive=True, reverse=rev, offsets=o)
             want = oracle.scan(x, exclusive=True, reverse=rev, offsets=offs)
             assert bits_equal(y.cpu().numpy(), want), (k, rev, "seg")
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_scan_health_word_stays_clear(dev, dtype):
+    # every look-back wait of these scans ends normally: the workspace's health word reads 0
+    n = 5 * A * T + 77
+    x = workloads.scan_values(n, dtype, seed=9)
+    offs = random_offsets(n, 900, seed=9)
+    t = torch.from_numpy(x).to(dev)
+    o = torch.from_numpy(offs).to(dev)
+    code = det.DET_F32 if dtype == F32 else det.DET_F64
+    ws = torch.empty(det.det_scan_workspace_size(n, code, 3, len(offs) - 1), dtype=torch.uint8,
+                     device=dev)
+    for excl, rev in MODES:
+        for seg in (None, o):
+            det.det_scan(t, exclusive=excl, reverse=rev, offsets=seg, ws=ws)
+            assert int(det.det_scan_error(ws).item()) == 0, (excl, rev, seg is not None)
