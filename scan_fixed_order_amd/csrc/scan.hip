@@ -129,8 +129,8 @@ __device__ __forceinline__ Seg<T> wait_slot(uint64_t* slot, uint32_t* err) {
 }
 
 // Status polls in two halves, so the first round trip can overlap other memory traffic:
-// poll_issue loads up to two slots (unused ones read as ready), poll_finish re-polls the words
-// that were not ready yet (bounded) and unpacks the values.
+// poll_issue loads up to two slots (unused ones read as ready), poll_finish_set re-polls the
+// words of one slot that were not ready yet (bounded) and unpacks the value.
 template <typename T>
 struct Poll {
     uint64_t w[2 * slot_words<T>()];
@@ -154,31 +154,26 @@ __device__ __forceinline__ void repoll(uint64_t& w, const uint64_t* slot) {
     if (!((w >> 32) & kReady)) w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Waits until one slot set of a Poll (words w[0 .. SW)) is ready, re-polling only that set, and
+// unpacks it (the identity when unused).  Lets a tile finish the waits it needs first.
 template <typename T>
-__device__ __forceinline__ void poll_finish(Poll<T>& pl, const uint64_t* s1, bool use1, Seg<T>& v1,
-                                            const uint64_t* s2, bool use2, Seg<T>& v2,
-                                            uint32_t* err) {
+__device__ __forceinline__ Seg<T> poll_finish_set(uint64_t* w, const uint64_t* slot, bool use,
+                                                  uint32_t* err) {
     constexpr int SW = slot_words<T>();
     uint32_t spins = 0;
     for (;;) {
-        bool all = true;
-#pragma unroll
-        for (int i = 0; i < 2 * SW; ++i) all = all && ((pl.w[i] >> 32) & kReady);
+        bool all = (w[0] >> 32) & kReady;
+        if constexpr (SW == 2) all = all && ((w[1] >> 32) & kReady);
         if (all) break;
         if (++spins > kSpinLimit) {
             __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
         __builtin_amdgcn_s_sleep(1);
-        repoll(pl.w[0], s1);
-        repoll(pl.w[SW], s2);
-        if constexpr (SW == 2) {
-            repoll(pl.w[1], s1 + 1);
-            repoll(pl.w[3], s2 + 1);
-        }
+        repoll(w[0], slot);
+        if constexpr (SW == 2) repoll(w[1], slot + 1);
     }
-    if (use1) v1 = unpack<T>(pl.w[0], SW == 2 ? pl.w[1] : 0ull);
-    if (use2) v2 = unpack<T>(pl.w[SW], SW == 2 ? pl.w[SW + 1] : 0ull);
+    return use ? unpack<T>(w[0], SW == 2 ? w[1] : 0ull) : seg_ident<T>();
 }
 
 // ---------------------------------------------------------------- cross-lane pieces
@@ -558,12 +553,28 @@ __device__ __forceinline__ LookBack look_back_of(int j, int A, int A2) {
     return lb;
 }
 
+// Interval totals never change once published, so thread t keeps the total of interval
+// Q * A2 + t once it has read it: gknown (uniform) counts the intervals of super-interval gQ
+// held that way.  Only newer intervals are polled.
+template <typename T>
+struct GCache {
+    Seg<T> g;
+    int known;
+    int Q;
+};
+
+template <typename T>
+__device__ __forceinline__ bool g_cached(const GCache<T>& gc, const LookBack& lb, int tid) {
+    return lb.Q == gc.Q && tid < gc.known;
+}
+
 template <typename T>
 __device__ __forceinline__ void issue_look_back(const ScanArgs<T>& a, const LookBack& lb,
-                                                Poll<T>& pl, int tid) {
+                                                const GCache<T>& gc, Poll<T>& pl, int tid) {
     constexpr int SW = slot_words<T>();
     poll_issue<T>(pl, a.agg + (size_t)(lb.q * a.A + tid) * SW, tid < lb.cnt,
-                  a.gtot + (size_t)(lb.Q * a.A2 + tid) * SW, tid < lb.qcnt);
+                  a.gtot + (size_t)(lb.Q * a.A2 + tid) * SW,
+                  tid < lb.qcnt && !g_cached(gc, lb, tid));
 }
 
 // Everything after a parked tile's look-back polls were issued: finish the look-back, publish
@@ -572,27 +583,33 @@ __device__ __forceinline__ void issue_look_back(const ScanArgs<T>& a, const Look
 // wave reads its parked prefixes out, adds X and stores them.
 template <typename T, bool SEG, bool REV, bool EXCL>
 __device__ __forceinline__ void finish_tile(const ScanArgs<T>& a, int j, const LookBack& lb,
-                                            Poll<T>& pl, Seg<T> P, Seg<T> p, Seg<T> agg,
+                                            Poll<T>& pl, GCache<T>& gc, Seg<T> P, Seg<T> p,
+                                            Seg<T> agg,
                                             Seg<T>* s_tmp, Seg<T>& s_carry, const T* pk, T* xs,
                                             const uint32_t* hbs, const uint32_t* s_heads, int tid,
                                             int lane, int wave) {
     constexpr int SW = slot_words<T>();
     uint32_t* err = a.err;
-    Seg<T> mine = seg_ident<T>(), gmine = seg_ident<T>();
-    poll_finish<T>(pl, a.agg + (size_t)(lb.q * a.A + tid) * SW, tid < lb.cnt, mine,
-                   a.gtot + (size_t)(lb.Q * a.A2 + tid) * SW, tid < lb.qcnt, gmine, err);
+    const Seg<T> mine =
+        poll_finish_set<T>(pl.w, a.agg + (size_t)(lb.q * a.A + tid) * SW, tid < lb.cnt, err);
+    const bool cached = g_cached(gc, lb, tid);
+    Seg<T> gmine = poll_finish_set<T>(pl.w + SW, a.gtot + (size_t)(lb.Q * a.A2 + tid) * SW,
+                                      tid < lb.qcnt && !cached, err);
+    if (cached) gmine = gc.g;
+    if (tid < lb.qcnt) gc.g = gmine;
+    gc.known = lb.qcnt;
+    gc.Q = lb.Q;
     Seg<T> Wj, WG;
     block_pw2<SEG, T>(mine, gmine, lane, wave, s_tmp, Wj, WG);
-    // the interval's last tile publishes the interval total G_q (needs no carry)
+    // the interval total G_q was published by this tile's local step (publish_interval_total);
+    // the super-interval's last tile needs it again for the next carry
     const bool ianchor = (lb.cnt == a.A - 1) && (j + 1 < a.ntiles);
-    Seg<T> Gq = seg_ident<T>();
-    if (ianchor) {
-        Gq = block_pw<SEG, T>(tid == a.A - 1 ? agg : mine, lane, wave, s_tmp);
-        if (tid == 0) publish<T>(a.gtot + (size_t)lb.q * SW, Gq);
-    }
     const bool sanchor = ianchor && (lb.qcnt == a.A2 - 1);
     Seg<T> H = seg_ident<T>();
-    if (sanchor) H = block_pw<SEG, T>(tid == a.A2 - 1 ? Gq : gmine, lane, wave, s_tmp);
+    if (sanchor) {
+        const Seg<T> Gq = block_pw<SEG, T>(tid == a.A - 1 ? agg : mine, lane, wave, s_tmp);
+        H = block_pw<SEG, T>(tid == a.A2 - 1 ? Gq : gmine, lane, wave, s_tmp);
+    }
 
     // carry into the super-interval (the identity for the first); its last tile forwards the
     // next one
@@ -629,6 +646,24 @@ __device__ __forceinline__ void finish_tile(const ScanArgs<T>& a, int j, const L
 // tiles run out and every tile a workgroup waits on is, or will be, claimed by one.
 constexpr int kCounters = 8;
 constexpr int kCounterStride = 64;   // words between counters
+
+// The last tile of an anchor interval publishes the interval total G_q = PW(all A tile totals)
+// right after its own local step, while its later tiles are still loading: G_q needs nothing but
+// those totals, and the first tiles of the next interval need G_q when they finish.  Every tile
+// total awaited here belongs to a smaller tile, published at that tile's local step.
+template <bool SEG, typename T>
+__device__ __forceinline__ void publish_interval_total(const ScanArgs<T>& a, int u, Seg<T> aggu,
+                                                       Seg<T>* s_tmp, int tid, int lane, int wave) {
+    const LookBack lb = look_back_of(u, a.A, a.A2);
+    if (!(lb.cnt == a.A - 1 && u + 1 < a.ntiles)) return;
+    constexpr int SW = slot_words<T>();
+    const uint64_t* slot = a.agg + (size_t)(lb.q * a.A + tid) * SW;
+    Poll<T> pa;
+    poll_issue<T>(pa, slot, tid < lb.cnt, slot, false);
+    const Seg<T> m = poll_finish_set<T>(pa.w, slot, tid < lb.cnt, a.err);
+    const Seg<T> G = block_pw<SEG, T>(tid == a.A - 1 ? aggu : m, lane, wave, s_tmp);
+    if (tid == 0) publish<T>(a.gtot + (size_t)lb.q * SW, G);
+}
 
 __device__ __forceinline__ int claim_tile(uint32_t* counters, int c, int nc) {
     const uint32_t k = __hip_atomic_fetch_add(counters + c * kCounterStride, 1u, __ATOMIC_RELAXED,
@@ -681,6 +716,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
         publish<T>(a.agg + (size_t)c * SW, aggc);
         s_tick[1] = claimed;
     }
+    publish_interval_total<SEG, T>(a, c, aggc, s_tmp, tid, lane0, wave);
     park_runs<T>(pk, r, lane0);
     if constexpr (SEG) s_hbits[wave][lane0] = hbc;
     __syncthreads();
@@ -690,6 +726,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
         if (tid == 0) claimed = claim_tile(a.ticket, ctr, a.nctr);
     }
     LookBack lbc = look_back_of(c, a.A, a.A2);
+    GCache<T> gc{seg_ident<T>(), 0, -1};
     int par = 0;   // s_heads[par] holds c's heads, s_heads[par ^ 1] receives u's
 
     for (;;) {
@@ -701,7 +738,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
         if (tid == 0) s_tick[par] = claimed;   // v (meaningful only when u exists)
         // c's look-back polls first: they sit in front of every load issued after them
         Poll<T> pl;
-        issue_look_back<T>(a, lbc, pl, tid);
+        issue_look_back<T>(a, lbc, gc, pl, tid);
 
         // ---- u: local part (its loads were issued an iteration ago), total published at once
         uint32_t hbu = 0u;
@@ -710,6 +747,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
             aggu = tile_local<T, SEG, REV>(a, u, r, hbu, Pu, pu, s_heads[par ^ 1], s_wtot, tid,
                                            lane, wave);
             if (tid == 0) publish<T>(a.agg + (size_t)u * SW, aggu);
+            publish_interval_total<SEG, T>(a, u, aggu, s_tmp, tid, lane, wave);
         }
         __syncthreads();
         const int v = s_tick[par];
@@ -723,8 +761,8 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
         }
 
         // ---- c: finish the look-back, store from LDS
-        finish_tile<T, SEG, REV, EXCL>(a, c, lbc, pl, Pc, pc, aggc, s_tmp, s_carry, pk, xs, hbs,
-                                       s_heads[par], tid, lane, wave);
+        finish_tile<T, SEG, REV, EXCL>(a, c, lbc, pl, gc, Pc, pc, aggc, s_tmp, s_carry, pk, xs,
+                                       hbs, s_heads[par], tid, lane, wave);
         if (!have_u) break;
 
         // ---- u takes c's place in LDS (this wave's readout of c is complete)
