@@ -303,42 +303,49 @@ __device__ __forceinline__ bool aligned16(const T* p) {
 
 // Lane t's run (flipped positions f0 .. f0 + 31, f0 = fw + 32 t) straight into registers: each
 // lane reads its own 128 (f32) or 256 (f64) contiguous bytes.  Identity past n.  `vec` (uniform)
-// selects 16-byte loads; it requires the whole wave in range and 16-byte aligned runs.  No
-// streaming hint here: consecutive loads of a lane share cache lines.
+// says the whole wave is in range and its runs are 16-byte aligned.  The 16-byte loads are
+// issued on every path (from a 256-byte dummy line when `vec` is false, the element loads then
+// supplying the values), so the count of loads issued after any earlier load is the same on
+// every path and the compiler can wait for that earlier load with a partial counter instead of
+// draining the queue.  No streaming hint: consecutive loads of a lane share cache lines.
 template <typename T, bool REV>
 __device__ __forceinline__ void load_run(const T* __restrict__ x, int64_t n, int64_t fw, bool vec,
-                                         T (&r)[kV], int lane) {
+                                         const T* __restrict__ dummy, T (&r)[kV], int lane) {
     const int64_t f0 = fw + (int64_t)lane * kV;
-    if (vec) {
-        // forward: run = x[f0 .. f0 + 32); reverse: original x[n - f0 - 32 .. n - f0) backwards
-        const T* p = REV ? x + (n - f0 - kV) : x + f0;
-        if constexpr (sizeof(T) == 4) {
+    // forward: run = x[f0 .. f0 + 32); reverse: original x[n - f0 - 32 .. n - f0) backwards
+    const T* p = vec ? (REV ? x + (n - f0 - kV) : x + f0) : dummy;
+    if constexpr (sizeof(T) == 4) {
 #pragma unroll
-            for (int i = 0; i < kV / 4; ++i) {
-                const f32x4 q = reinterpret_cast<const f32x4*>(p)[i];
-                if (REV) {
-                    r[kV - 1 - 4 * i] = q.x; r[kV - 2 - 4 * i] = q.y;
-                    r[kV - 3 - 4 * i] = q.z; r[kV - 4 - 4 * i] = q.w;
-                } else {
-                    r[4 * i] = q.x; r[4 * i + 1] = q.y; r[4 * i + 2] = q.z; r[4 * i + 3] = q.w;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < kV / 2; ++i) {
-                const f64x2 q = reinterpret_cast<const f64x2*>(p)[i];
-                if (REV) {
-                    r[kV - 1 - 2 * i] = q.x; r[kV - 2 - 2 * i] = q.y;
-                } else {
-                    r[2 * i] = q.x; r[2 * i + 1] = q.y;
-                }
+        for (int i = 0; i < kV / 4; ++i) {
+            const f32x4 q = reinterpret_cast<const f32x4*>(p)[i];
+            if (REV) {
+                r[kV - 1 - 4 * i] = q.x; r[kV - 2 - 4 * i] = q.y;
+                r[kV - 3 - 4 * i] = q.z; r[kV - 4 - 4 * i] = q.w;
+            } else {
+                r[4 * i] = q.x; r[4 * i + 1] = q.y; r[4 * i + 2] = q.z; r[4 * i + 3] = q.w;
             }
         }
     } else {
 #pragma unroll
+        for (int i = 0; i < kV / 2; ++i) {
+            const f64x2 q = reinterpret_cast<const f64x2*>(p)[i];
+            if (REV) {
+                r[kV - 1 - 2 * i] = q.x; r[kV - 2 - 2 * i] = q.y;
+            } else {
+                r[2 * i] = q.x; r[2 * i + 1] = q.y;
+            }
+        }
+    }
+    if (!vec) {
+        // element loads; positions past n read element n - 1 and take the identity (both
+        // operands of the select are plain values, so no branch around the load is formed)
+        const T id = ident<T>();
+#pragma unroll
         for (int k = 0; k < kV; ++k) {
             const int64_t f = f0 + k;
-            r[k] = (f < n) ? x[REV ? n - 1 - f : f] : ident<T>();
+            const int64_t fc = f < n ? f : n - 1;
+            const T v = x[REV ? n - 1 - fc : fc];
+            r[k] = (f < n) ? v : id;
         }
     }
 }
@@ -478,6 +485,7 @@ struct ScanArgs {
     uint64_t* carry;     // slot_words<T>() words per super-interval boundary: carries
     uint32_t* ticket;    // kCounters tile counters, kCounterStride words apart
     uint32_t* err;       // raised when a wait hit the spin bound
+    const T* dummy;      // 256 bytes that the 16-byte loads of a non-vector run read instead
     int ntiles;
     int nctr;            // tile counters in use: min(kCounters, grid)
     int rev;
@@ -535,7 +543,7 @@ __device__ __forceinline__ void load_tile(const ScanArgs<T>& a, int j, int wave,
     const int64_t fw = (int64_t)j * kT + (int64_t)wave * kWaveElems;
     const int64_t reg0 = REV ? a.n - fw - kWaveElems : fw;   // lowest original index
     const bool vec = (fw + kWaveElems <= a.n) && aligned16(a.x + reg0);
-    load_run<T, REV>(a.x, a.n, fw, vec, r, lane);
+    load_run<T, REV>(a.x, a.n, fw, vec, a.dummy, r, lane);
 }
 
 // Where tile j's look-back polls go: the earlier tile totals of its anchor interval and the
@@ -665,20 +673,28 @@ __device__ __forceinline__ void publish_interval_total(const ScanArgs<T>& a, int
     if (tid == 0) publish<T>(a.gtot + (size_t)lb.q * SW, G);
 }
 
-__device__ __forceinline__ int claim_tile(uint32_t* counters, int c, int nc) {
-    const uint32_t k = __hip_atomic_fetch_add(counters + c * kCounterStride, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    return (int)k * nc + c;
+// Issues the claim of counter c's next ticket k; the tile is k * nc + c.  The counter offset
+// passes through a vector register, so the compiler treats the atomic as per-lane and does not
+// combine it across the wave: that expansion reads the result back at once, which would wait
+// for every load issued before it.  The caller reads the ticket an iteration later.
+__device__ __forceinline__ uint32_t claim_issue(uint32_t* counters, int c) {
+    int off = c * kCounterStride;
+    asm volatile("" : "+v"(off));
+    return __hip_atomic_fetch_add(counters + off, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+__device__ __forceinline__ int ticket_tile(uint32_t k, int c, int nc) { return (int)k * nc + c; }
 
 // Persistent workgroups, three tiles in flight each: tile c parked in LDS (published, waiting
 // for its look-back), tile u in registers (its loads were issued one iteration earlier) and
-// tile v loading.  Per iteration: c's look-back polls leave; u's local part runs and u's total
-// is published; v's loads are issued and the tile after v is claimed; c finishes and is stored
-// from LDS; u is parked in c's place.  Load latency thus overlaps a whole iteration, and a
-// tile's total is published one iteration before its workgroup waits on anything.  A
-// workgroup only waits on smaller tiles, which are claimed in counter order by running
-// workgroups that publish and finish them without waiting on it, so every wait ends.
+// tile v loading.  Per iteration: u's local part runs and u's total is published; c's
+// look-back polls leave; v's loads are issued and the tile after v is claimed; c finishes and
+// is stored from LDS while v's loads are in flight; u is parked in c's place.  A tile's total
+// is thus published one iteration before its workgroup waits on anything.  Tile indices are
+// kept wave-uniform (scalar) and every path issues the same loads, so the wait for c's polls
+// counts only the loads issued after them.  A workgroup only waits on smaller tiles, which are
+// claimed in counter order by running workgroups that publish and finish them without
+// waiting on it, so every wait ends.
 template <typename T, bool SEG, bool REV, bool EXCL>
 __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     __shared__ T s_park[kScanWaves][kPark];
@@ -692,39 +708,39 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
 
     const int tid = threadIdx.x;
     const int lane0 = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     constexpr int SW = slot_words<T>();
     T* pk = s_park[wave];
     T* xs = s_x[wave];
     const uint32_t* hbs = s_hbits[SEG ? wave : 0];
-    const int ctr = (int)(blockIdx.x % (unsigned)a.nctr);
+    const int nc = a.nctr;
+    const int ctr = (int)(blockIdx.x % (unsigned)nc);
 
     // ---- prologue: c loaded, local, published, parked; u's loads issued
-    if (tid == 0) s_tick[0] = claim_tile(a.ticket, ctr, a.nctr);
+    if (tid == 0) s_tick[0] = ticket_tile(claim_issue(a.ticket, ctr), ctr, nc);
     __syncthreads();
-    int c = s_tick[0];
+    int c = __builtin_amdgcn_readfirstlane(s_tick[0]);
     if (c >= a.ntiles) return;
     T r[kV];
     load_tile<T, REV>(a, c, wave, r, lane0);
-    int claimed = 0;
-    if (tid == 0) claimed = claim_tile(a.ticket, ctr, a.nctr);
+    uint32_t claimed = 0u;
+    if (tid == 0) claimed = claim_issue(a.ticket, ctr);
     uint32_t hbc;
     Seg<T> Pc, pc;
     Seg<T> aggc =
         tile_local<T, SEG, REV>(a, c, r, hbc, Pc, pc, s_heads[0], s_wtot, tid, lane0, wave);
     if (tid == 0) {
         publish<T>(a.agg + (size_t)c * SW, aggc);
-        s_tick[1] = claimed;
+        s_tick[1] = ticket_tile(claimed, ctr, nc);
     }
     publish_interval_total<SEG, T>(a, c, aggc, s_tmp, tid, lane0, wave);
     park_runs<T>(pk, r, lane0);
     if constexpr (SEG) s_hbits[wave][lane0] = hbc;
     __syncthreads();
-    int u = s_tick[1];
-    if (u < a.ntiles) {
-        load_tile<T, REV>(a, u, wave, r, lane0);
-        if (tid == 0) claimed = claim_tile(a.ticket, ctr, a.nctr);
-    }
+    int u = __builtin_amdgcn_readfirstlane(s_tick[1]);
+    // u's loads (a tile past the end reads element n - 1 and is never used)
+    load_tile<T, REV>(a, u, wave, r, lane0);
+    if (tid == 0 && u < a.ntiles) claimed = claim_issue(a.ticket, ctr);
     LookBack lbc = look_back_of(c, a.A, a.A2);
     GCache<T> gc{seg_ident<T>(), 0, -1};
     int par = 0;   // s_heads[par] holds c's heads, s_heads[par ^ 1] receives u's
@@ -735,10 +751,6 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
         int lane = lane0;
         asm volatile("" : "+v"(lane));
         const bool have_u = u < a.ntiles;
-        if (tid == 0) s_tick[par] = claimed;   // v (meaningful only when u exists)
-        // c's look-back polls first: they sit in front of every load issued after them
-        Poll<T> pl;
-        issue_look_back<T>(a, lbc, gc, pl, tid);
 
         // ---- u: local part (its loads were issued an iteration ago), total published at once
         uint32_t hbu = 0u;
@@ -749,16 +761,19 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
             if (tid == 0) publish<T>(a.agg + (size_t)u * SW, aggu);
             publish_interval_total<SEG, T>(a, u, aggu, s_tmp, tid, lane, wave);
         }
+        // the ticket claimed last iteration (v, if u exists); then c's look-back polls go out
+        // ahead of v's loads
+        if (tid == 0) s_tick[par] = ticket_tile(claimed, ctr, nc);
+        Poll<T> pl;
+        issue_look_back<T>(a, lbc, gc, pl, tid);
         __syncthreads();
-        const int v = s_tick[par];
-        const bool have_v = have_u && v < a.ntiles;
+        const int v = have_u ? __builtin_amdgcn_readfirstlane(s_tick[par]) : a.ntiles;
+        const bool have_v = v < a.ntiles;
 
         // ---- v: loads issued now, consumed in the next iteration; the tile after v claimed
         T rv[kV];
-        if (have_v) {
-            load_tile<T, REV>(a, v, wave, rv, lane);
-            if (tid == 0) claimed = claim_tile(a.ticket, ctr, a.nctr);
-        }
+        load_tile<T, REV>(a, v, wave, rv, lane);
+        if (tid == 0 && have_v) claimed = claim_issue(a.ticket, ctr);
 
         // ---- c: finish the look-back, store from LDS
         finish_tile<T, SEG, REV, EXCL>(a, c, lbc, pl, gc, Pc, pc, aggc, s_tmp, s_carry, pk, xs,
@@ -775,7 +790,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
         aggc = aggu;
         lbc = look_back_of(u, a.A, a.A2);
         c = u;
-        u = have_v ? v : a.ntiles;
+        u = v;
         par ^= 1;
         // the next tile's heads go where c's were: every wave must be done reading them
         if constexpr (SEG) __syncthreads();
@@ -792,8 +807,11 @@ __global__ void k_zero_words(uint64_t* p, int64_t nwords) {
         p[i] = 0ull;
 }
 
-// Workspace header: the tile counters, then the error word, each on its own line.
-constexpr size_t kHeader = (size_t)(kCounters * kCounterStride * 4) + 256;
+// Workspace header: the tile counters, the error word and the dummy load line, each on lines
+// of their own.
+constexpr size_t kErrOff = (size_t)(kCounters * kCounterStride * 4);
+constexpr size_t kDummyOff = kErrOff + 256;
+constexpr size_t kHeader = kDummyOff + 256;
 
 struct Layout {
     int64_t ntiles, nq, nQ;
@@ -848,7 +866,8 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     a.gtot = reinterpret_cast<uint64_t*>(ws + L.g_off);
     a.carry = reinterpret_cast<uint64_t*>(ws + L.carry_off);
     a.ticket = reinterpret_cast<uint32_t*>(ws);
-    a.err = reinterpret_cast<uint32_t*>(ws + kCounters * kCounterStride * 4);
+    a.err = reinterpret_cast<uint32_t*>(ws + kErrOff);
+    a.dummy = reinterpret_cast<const T*>(ws + kDummyOff);
     a.ntiles = (int)L.ntiles;
     a.rev = (flags & DET_SCAN_REVERSE) ? 1 : 0;
     a.excl = (flags & DET_SCAN_EXCLUSIVE) ? 1 : 0;
@@ -883,8 +902,8 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
 }  // namespace
 
 det_status scan_error(const void* ws, int32_t* out, hipStream_t s) {
-    const uint32_t* err = reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) +
-                                                            kCounters * kCounterStride * 4);
+    const uint32_t* err =
+        reinterpret_cast<const uint32_t*>(static_cast<const char*>(ws) + kErrOff);
     k_copy_error<<<1, 1, 0, s>>>(err, out);
     return launch_status();
 }
