@@ -8,7 +8,7 @@ Inputs are resident in HBM before the timed region.  `value` is the step's algor
 
 Prints ONE JSON line.  Besides the contract fields it carries:
   roofline      the kernel with the largest share of the step (by the library's own per-launch
-                HIP events, recorded on the launching stream during the timed steps): its
+                HIP events, recorded on the launching stream over a timed pass of K steps): its
                 algorithmic bytes per launch over its average launch time, against 8 TB/s; and
                 `traffic`, the HBM bytes per launch that rocprofv3 counters measured for the same
                 kernel source (read from profiles/, null when that source has changed since);
@@ -155,12 +155,23 @@ def main():
     log("warmup done")
 
     # ---------------------------------------------------------------- timed steps
-    ev = {name: [] for name, _, _ in ops}
+    # Three passes of K steps each, so that no pass carries another's markers: the whole step
+    # bracketed by one event pair (ms_per_step, value); one event pair around each operation
+    # (per-operation times); the library's own per-launch events on its stream (the kernel
+    # table and the roofline).  Each marker adds a few microseconds of stream time.
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    det.det_debug_kernel_timing(True)
     torch.cuda.synchronize()
     start.record(stream)
+    for _ in range(args.steps):
+        for _, fn, _ in ops:
+            fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(stop) / args.steps
+    log(f"timed {args.steps} steps: {step_ms:.3f} ms/step")
+
+    ev = {name: [] for name, _, _ in ops}
     for _ in range(args.steps):
         for name, fn, _ in ops:
             a = torch.cuda.Event(enable_timing=True)
@@ -169,13 +180,18 @@ def main():
             fn()
             b.record(stream)
             ev[name].append((a, b))
-    stop.record(stream)
+    torch.cuda.synchronize()
+    op_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name in ev}
+
+    det.det_debug_kernel_timing(True)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        for _, fn, _ in ops:
+            fn()
     torch.cuda.synchronize()
     kernels = det.det_debug_kernel_report()
     det.det_debug_kernel_timing(False)
-    step_ms = start.elapsed_time(stop) / args.steps
-    op_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name in ev}
-    log(f"timed {args.steps} steps: {step_ms:.3f} ms/step")
+    log(f"per-operation and per-kernel passes done")
 
     step_bytes = sum(bts for _, _, bts in ops)
     value = step_bytes / (step_ms * 1e-3) / 1e9

@@ -13,9 +13,11 @@
  *
  * Conventions for every entry point:
  *  - Data pointers are DEVICE pointers owned by the caller.  Any element-aligned address is
- *    accepted (tensor views); alignment never changes the bits.
+ *    accepted (tensor views); alignment never changes the bits.  A data pointer that is not
+ *    aligned to its element size is rejected with DET_ERROR_INVALID_VALUE.
  *  - The library never allocates and never synchronises.  Scratch memory is a caller-provided
- *    device workspace of at least *_workspace_size(...) bytes, 256-byte aligned; its contents
+ *    device workspace of at least *_workspace_size(...) bytes, 256-byte aligned (else
+ *    DET_ERROR_WORKSPACE; torch's and hipMalloc's allocations are); its contents
  *    on entry do not matter and are undefined on return.  Calls that overlap in time must not
  *    share a workspace.
  *  - All work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
@@ -43,7 +45,8 @@ typedef enum {
     DET_ERROR_INVALID_VALUE = 1, /* bad argument (negative size, NULL pointer, bad flags...) */
     DET_ERROR_UNSUPPORTED = 2,   /* unknown dtype */
     DET_ERROR_TOO_LARGE = 3,     /* n or a derived size beyond DET_MAX_N */
-    DET_ERROR_WORKSPACE = 4,     /* ws NULL or smaller than the matching *_workspace_size */
+    DET_ERROR_WORKSPACE = 4,     /* ws NULL, not 256-byte aligned, or smaller than the
+                                    matching *_workspace_size */
     DET_ERROR_LAUNCH = 5         /* the HIP runtime refused a launch */
 } det_status;
 

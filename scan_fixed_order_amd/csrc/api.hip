@@ -111,6 +111,13 @@ static bool ranges_overlap(const void* a, const void* b, size_t bytes) {
 
 using namespace det;
 
+namespace {
+// The workspace must be 256-byte aligned (status words and counters sit on their own lines).
+bool ws_aligned(const void* ws) { return (reinterpret_cast<uintptr_t>(ws) & 255u) == 0; }
+// Data pointers must be aligned to their element size.
+bool elem_aligned(const void* p, size_t es) { return (reinterpret_cast<uintptr_t>(p) % es) == 0; }
+}  // namespace
+
 extern "C" {
 
 size_t det_sum_workspace_size(int64_t n, det_dtype dtype) {
@@ -124,7 +131,9 @@ det_status det_sum(const void* x, int64_t n, det_dtype dtype, void* out, void* w
     if (n < 0) return DET_ERROR_INVALID_VALUE;
     if (n > DET_MAX_N) return DET_ERROR_TOO_LARGE;
     if (!out || (n > 0 && !x)) return DET_ERROR_INVALID_VALUE;
-    if (!ws || ws_bytes < sum_workspace(n, dtype)) return DET_ERROR_WORKSPACE;
+    if (!elem_aligned(out, dtype_size(dtype)) || !elem_aligned(x, dtype_size(dtype)))
+        return DET_ERROR_INVALID_VALUE;
+    if (!ws || !ws_aligned(ws) || ws_bytes < sum_workspace(n, dtype)) return DET_ERROR_WORKSPACE;
     return sum_launch(x, n, dtype, out, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -143,11 +152,14 @@ det_status det_scan(const void* x, void* y, int64_t n, det_dtype dtype, unsigned
     if (flags & ~(DET_SCAN_EXCLUSIVE | DET_SCAN_REVERSE)) return DET_ERROR_INVALID_VALUE;
     if (n > 0 && (!x || !y)) return DET_ERROR_INVALID_VALUE;
     if (seg_offsets && n > 0 && num_segments < 1) return DET_ERROR_INVALID_VALUE;
+    if (!elem_aligned(x, dtype_size(dtype)) || !elem_aligned(y, dtype_size(dtype)) ||
+        !elem_aligned(seg_offsets, sizeof(int64_t)))
+        return DET_ERROR_INVALID_VALUE;
     const size_t bytes = (size_t)n * dtype_size(dtype);
     if ((flags & DET_SCAN_EXCLUSIVE) && n > 0 && ranges_overlap(x, y, bytes))
         return DET_ERROR_INVALID_VALUE;
     if (n > 0 && x != y && ranges_overlap(x, y, bytes)) return DET_ERROR_INVALID_VALUE;
-    if (!ws || ws_bytes < scan_workspace(n, dtype, flags, num_segments))
+    if (!ws || !ws_aligned(ws) || ws_bytes < scan_workspace(n, dtype, flags, num_segments))
         return DET_ERROR_WORKSPACE;
     return scan_launch(x, y, n, dtype, flags, seg_offsets, num_segments, ws, ws_bytes,
                        static_cast<hipStream_t>(stream));
@@ -177,6 +189,9 @@ det_status det_scatter_add(const void* values, const int32_t* index, int64_t n, 
     if (n > 0 && (!values || !index)) return DET_ERROR_INVALID_VALUE;
     if (num_out > 0 && !out) return DET_ERROR_INVALID_VALUE;
     const size_t es = dtype_size(dtype);
+    if (!elem_aligned(values, es) || !elem_aligned(out, es) || !elem_aligned(prev, es) ||
+        !elem_aligned(index, sizeof(int32_t)) || !elem_aligned(n_skipped, sizeof(int64_t)))
+        return DET_ERROR_INVALID_VALUE;
     if (n > 0 && num_out > 0) {
         const uintptr_t v0 = reinterpret_cast<uintptr_t>(values);
         const uintptr_t v1 = v0 + (size_t)n * row_len * es;
@@ -184,7 +199,7 @@ det_status det_scatter_add(const void* values, const int32_t* index, int64_t n, 
         const uintptr_t o1 = o0 + (size_t)num_out * row_len * es;
         if (v0 < o1 && o0 < v1) return DET_ERROR_INVALID_VALUE;
     }
-    if (!ws || ws_bytes < scatter_workspace(n, num_out, row_len, dtype))
+    if (!ws || !ws_aligned(ws) || ws_bytes < scatter_workspace(n, num_out, row_len, dtype))
         return DET_ERROR_WORKSPACE;
     return scatter_launch(values, index, n, row_len, dtype, out, num_out, prev, n_skipped, ws,
                           ws_bytes, static_cast<hipStream_t>(stream));

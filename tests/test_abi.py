@@ -100,6 +100,27 @@ def test_validation_errors_enqueue_nothing():
               NULL) == E_UNSUPPORTED
 
 
+def test_alignment_is_checked():
+    lib = det.lib()
+    ws_odd = ctypes.c_void_p(0x10000 + 128)        # 128-byte aligned only
+    assert lib.det_sum(FAKE, 10, 0, FAKE, ws_odd, 1 << 20, NULL) == E_WORKSPACE
+    assert lib.det_scan(FAKE, ctypes.c_void_p(0x900000), 10, 0, 0, NULL, 0, ws_odd, 1 << 20,
+                        NULL) == E_WORKSPACE
+    assert lib.det_scatter_add(FAKE, FAKE, 10, 1, 0, ctypes.c_void_p(0x900000), 4, NULL, NULL,
+                               ws_odd, 1 << 30, NULL) == E_WORKSPACE
+    odd = ctypes.c_void_p(0x100002)                 # not 4-byte aligned
+    assert lib.det_sum(odd, 10, 0, FAKE, FAKE, 1 << 20, NULL) == E_INVALID
+    assert lib.det_sum(ctypes.c_void_p(0x100004), 10, 1, FAKE, FAKE, 1 << 20, NULL) == E_INVALID
+    assert lib.det_scan(odd, ctypes.c_void_p(0x900000), 10, 0, 0, NULL, 0, FAKE, 1 << 20,
+                        NULL) == E_INVALID
+    assert lib.det_scan(FAKE, ctypes.c_void_p(0x900000), 10, 0, 0, ctypes.c_void_p(0x200004), 1,
+                        FAKE, 1 << 20, NULL) == E_INVALID                        # offsets int64
+    assert lib.det_scatter_add(FAKE, odd, 10, 1, 0, ctypes.c_void_p(0x900000), 4, NULL, NULL,
+                               FAKE, 1 << 30, NULL) == E_INVALID                 # index int32
+    assert lib.det_scatter_add(FAKE, FAKE, 10, 1, 0, ctypes.c_void_p(0x900002), 4, NULL, NULL,
+                               FAKE, 1 << 30, NULL) == E_INVALID                 # out f32
+
+
 def test_debug_hook_range():
     lib = det.lib()
     assert lib.det_debug_set_launch(-1, 0) == E_INVALID
