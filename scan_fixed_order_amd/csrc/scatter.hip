@@ -242,127 +242,182 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__
 }
 
 // P: payload word (uint32_t: f32 value bits or source row; uint64_t: f64 value bits)
+template <typename P>
+struct RadixSmem {
+    uint32_t keys[256 * kItems<P>];
+    P pay[256 * kItems<P>];
+    uint32_t cnt[4][kBuckets0];   // per-wave digit counters, then wave offsets
+    uint32_t dstart[kBuckets0];
+    int64_t gbase[kBuckets0];
+    uint32_t s4[4];
+};
+
+// A chunk's keys and payloads, loaded by thread (wave w, lane l) at positions
+// base + w * 64 * IPT + k * 64 + l.  FULL: the whole chunk is in range (no checks, so every
+// path issues the same loads).
+template <typename P, bool FIRST, bool ROWS, bool FULL>
+__device__ __forceinline__ void radix_load(const uint32_t* __restrict__ keys_in,
+                                           const P* __restrict__ pay_in, int64_t base, int64_t m,
+                                           uint32_t (&key)[kItems<P>], P (&pay)[kItems<P>],
+                                           int wave, int lane) {
+    constexpr int IPT = kItems<P>;
+    const int64_t p0 = base + (int64_t)wave * 64 * IPT + lane;
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+        const int64_t p = p0 + k * 64;
+        key[k] = (FULL || p < m) ? keys_in[p] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+        const int64_t p = p0 + k * 64;
+        if constexpr (ROWS && FIRST) {
+            pay[k] = (P)((FULL || p < m) ? p : 0);
+        } else {
+            pay[k] = (FULL || p < m) ? pay_in[p] : (P)0;
+        }
+    }
+}
+
+// Ranks one loaded chunk stably by digit, stages it in LDS in digit order and writes every
+// digit's run to its place in the output.  Rank of an item = (items of the chunk with a smaller
+// digit) + (items of its digit in earlier waves) + (items of its digit earlier in its wave):
+// the last part from the wave's ballots on each digit bit (the lanes that agree on every bit
+// are the item's peers), taken in item order k = 0 .. IPT-1 against per-wave counters in LDS,
+// which the lowest peer advances with one LDS atomic whose old value it hands to its peers.
+// Integers only, so exact.  Leaves every barrier it passes balanced; ends with the LDS counters
+// cleared for the next chunk.
+template <typename P, bool FIRST, bool ROWS, bool FULL>
+__device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_t (&key)[kItems<P>],
+                                                 const P (&pay)[kItems<P>], int64_t base, int64_t m,
+                                                 uint32_t B, int shift, uint32_t off0,
+                                                 uint32_t off1, uint32_t* __restrict__ keys_out,
+                                                 P* __restrict__ pay_out, int tid, int lane,
+                                                 int wave) {
+    constexpr int IPT = kItems<P>;
+    constexpr int H = 256 * IPT;
+    constexpr int BITS = FIRST ? 9 : 8;
+    constexpr int NB = FIRST ? kBuckets0 : 256;
+    uint32_t rk[IPT];
+    const int64_t p0 = base + (int64_t)wave * 64 * IPT + lane;
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+        const bool valid = FULL || p0 + k * 64 < m;
+        const int d = valid ? digit_of<FIRST>(key[k], B, shift) : 0;
+        uint32_t plo = FULL ? ~0u : (uint32_t)__ballot(valid);
+        uint32_t phi = FULL ? ~0u : (uint32_t)(__ballot(valid) >> 32);
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) {
+            const int rep = -((d >> b) & 1);            // 0 or all ones: the lane's bit
+            const uint64_t mb = __ballot(rep != 0);
+            plo &= ~((uint32_t)mb ^ (uint32_t)rep);      // keep lanes whose bit b agrees
+            phi &= ~((uint32_t)(mb >> 32) ^ (uint32_t)rep);
+        }
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi(phi, __builtin_amdgcn_mbcnt_lo(plo, 0u));
+        const uint32_t cnt = (uint32_t)__popc(plo) + (uint32_t)__popc(phi);
+        uint32_t old = 0u;
+        if (valid && below == 0u) old = atomicAdd(&sm.cnt[wave][d], cnt);
+        const int leader = plo ? __builtin_ctz(plo) : 32 + __builtin_ctz(phi | 0x80000000u);
+        const uint32_t seen = (uint32_t)__builtin_amdgcn_ds_bpermute(leader << 2, (int)old);
+        rk[k] = seen + below;
+    }
+    __syncthreads();
+    // per digit: wave offsets (exclusive over waves) and the chunk's count
+    uint32_t tot = 0;
+    {
+        uint32_t run = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t cw = sm.cnt[w][tid];
+            sm.cnt[w][tid] = run;
+            run += cw;
+        }
+        tot = run;
+        if (NB > 256 && tid == 0) {
+            uint32_t r2 = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t cw = sm.cnt[w][256];
+                sm.cnt[w][256] = r2;
+                r2 += cw;
+            }
+        }
+    }
+    uint32_t total;
+    const uint32_t ds = block_excl_scan_u32(tot, sm.s4, &total);
+    sm.dstart[tid] = ds;
+    sm.gbase[tid] = (int64_t)off0 - (int64_t)ds;
+    if (NB > 256 && tid == 0) {
+        sm.dstart[256] = total;
+        sm.gbase[256] = (int64_t)off1 - (int64_t)total;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+        if (FULL || p0 + k * 64 < m) {
+            const int d = digit_of<FIRST>(key[k], B, shift);
+            const uint32_t lp = sm.dstart[d] + sm.cnt[wave][d] + rk[k];
+            sm.keys[lp] = key[k];
+            sm.pay[lp] = pay[k];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < 4 * kBuckets0; i += 256) (&sm.cnt[0][0])[i] = 0u;
+    if constexpr (FULL) {
+        // a fixed number of stores, so a later wait on loads issued before them stays partial
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int i = k * 256 + tid;
+            const uint32_t kk = sm.keys[i];
+            const int64_t g = sm.gbase[digit_of<FIRST>(kk, B, shift)] + i;
+            keys_out[g] = kk;
+            pay_out[g] = sm.pay[i];
+        }
+    } else {
+        const int cntc = (int)((m - base) < H ? (m - base) : H);
+        for (int i = tid; i < cntc; i += 256) {
+            const uint32_t kk = sm.keys[i];
+            const int64_t g = sm.gbase[digit_of<FIRST>(kk, B, shift)] + i;
+            keys_out[g] = kk;
+            pay_out[g] = sm.pay[i];
+        }
+    }
+    __syncthreads();
+}
+
+// One chunk per workgroup, chunk xcd_chunk(b) for workgroup b: the dispatcher starts
+// workgroups in order, so the chunks an XCD holds at any moment are neighbours and their
+// writes into each bucket's region merge in its L2.
 template <typename P, bool FIRST, bool ROWS>
 __global__ __launch_bounds__(256) void k_radix_scatter(
     const uint32_t* __restrict__ keys_in, const P* __restrict__ pay_in,
     uint32_t* __restrict__ keys_out, P* __restrict__ pay_out, int64_t n,
     const uint32_t* __restrict__ nvalid, uint32_t B, int shift, int64_t nchunks,
     const uint32_t* __restrict__ hist_ex) {
-    constexpr int IPT = kItems<P>;                   // items per thread
-    constexpr int H = 256 * IPT;                     // elements per chunk
-    constexpr int WE = 64 * IPT;                     // elements per wave
+    constexpr int IPT = kItems<P>;
+    constexpr int H = 256 * IPT;
     constexpr int NB = FIRST ? kBuckets0 : 256;
-    constexpr int BITS = FIRST ? 9 : 8;
-    __shared__ uint32_t s_keys[H];
-    __shared__ P s_pay[H];
-    __shared__ uint32_t s_cnt[4][kBuckets0];   // per-wave digit counters, then wave offsets
-    __shared__ uint32_t s_dstart[kBuckets0];
-    __shared__ int64_t s_gbase[kBuckets0];
-    __shared__ uint32_t s4[4];
-
+    __shared__ RadixSmem<P> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t c = xcd_chunk(blockIdx.x, nchunks);
     const int64_t m = FIRST ? n : (int64_t)*nvalid;
+    const int64_t c = xcd_chunk(blockIdx.x, nchunks);
     const int64_t base = c * H;
     if (base >= m) return;
     // this chunk's bucket offsets, fetched with the keys
     const uint32_t off0 = hist_ex[c * NB + tid];
     const uint32_t off1 = (NB > 256 && tid == 0) ? hist_ex[c * NB + 256] : 0u;
-
-    for (int i = tid; i < 4 * kBuckets0; i += 256) (&s_cnt[0][0])[i] = 0u;
-    __syncthreads();
-
+    for (int i = tid; i < 4 * kBuckets0; i += 256) (&sm.cnt[0][0])[i] = 0u;
     uint32_t key[IPT];
     P pay[IPT];
-    uint32_t rk[IPT];
-    int dg[IPT];
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    // every load of the chunk first, so they share one round trip
-    const int64_t p0 = base + (int64_t)wave * WE + lane;
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-        const int64_t p = p0 + k * 64;
-        key[k] = p < m ? keys_in[p] : 0u;
-    }
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-        const int64_t p = p0 + k * 64;
-        if constexpr (ROWS && FIRST) {
-            pay[k] = (P)(p < m ? p : 0);
-        } else {
-            pay[k] = p < m ? pay_in[p] : (P)0;
-        }
-    }
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-        const int64_t p = p0 + k * 64;
-        const bool valid = p < m;
-        const int d = valid ? digit_of<FIRST>(key[k], B, shift) : 0;
-        dg[k] = d;
-        uint64_t peers = __ballot(valid);
-#pragma unroll
-        for (int b = 0; b < BITS; ++b) {
-            const bool bit = (d >> b) & 1;
-            const uint64_t mb = __ballot(bit);
-            peers &= bit ? mb : ~mb;
-        }
-        const uint32_t rank = (uint32_t)__popcll(peers & below);
-        uint32_t seen = 0;
-        if (valid) seen = s_cnt[wave][d];
-        rk[k] = seen + rank;
-        if (valid && (peers & below) == 0ull) s_cnt[wave][d] = seen + (uint32_t)__popcll(peers);
-    }
-    __syncthreads();
-    // per digit: wave offsets (exclusive over waves) and totals
-    uint32_t tot_lo = 0, tot_hi = 0;
-    {
-        const int d = tid;
-        uint32_t run = 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t cw = s_cnt[w][d];
-            s_cnt[w][d] = run;
-            run += cw;
-        }
-        tot_lo = run;
-        if (NB > 256 && tid == 0) {
-            uint32_t r2 = 0;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t cw = s_cnt[w][256];
-                s_cnt[w][256] = r2;
-                r2 += cw;
-            }
-            tot_hi = r2;
-        }
-    }
-    uint32_t total;
-    const uint32_t ds = block_excl_scan_u32(tot_lo, s4, &total);
-    s_dstart[tid] = ds;
-    s_gbase[tid] = (int64_t)off0 - (int64_t)ds;
-    if (NB > 256 && tid == 0) {
-        s_dstart[256] = total;
-        s_gbase[256] = (int64_t)off1 - (int64_t)total;
-    }
-    (void)tot_hi;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-        const int64_t p = base + (int64_t)wave * WE + k * 64 + lane;
-        if (p < m) {
-            const int d = dg[k];
-            const uint32_t lp = s_dstart[d] + s_cnt[wave][d] + rk[k];
-            s_keys[lp] = key[k];
-            s_pay[lp] = pay[k];
-        }
-    }
-    __syncthreads();
-    const int cntc = (int)((m - base) < H ? (m - base) : H);
-    for (int i = tid; i < cntc; i += 256) {
-        const uint32_t kk = s_keys[i];
-        const int64_t g = s_gbase[digit_of<FIRST>(kk, B, shift)] + i;
-        keys_out[g] = kk;
-        pay_out[g] = s_pay[i];
+    if (base + H <= m) {
+        radix_load<P, FIRST, ROWS, true>(keys_in, pay_in, base, m, key, pay, wave, lane);
+        __syncthreads();
+        radix_rank_write<P, FIRST, ROWS, true>(sm, key, pay, base, m, B, shift, off0, off1,
+                                               keys_out, pay_out, tid, lane, wave);
+    } else {
+        radix_load<P, FIRST, ROWS, false>(keys_in, pay_in, base, m, key, pay, wave, lane);
+        __syncthreads();
+        radix_rank_write<P, FIRST, ROWS, false>(sm, key, pay, base, m, B, shift, off0, off1,
+                                                keys_out, pay_out, tid, lane, wave);
     }
 }
 
