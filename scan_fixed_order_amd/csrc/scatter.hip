@@ -307,8 +307,8 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         uint32_t phi = FULL ? ~0u : (uint32_t)(__ballot(valid) >> 32);
 #pragma unroll
         for (int b = 0; b < BITS; ++b) {
-            const int rep = -((d >> b) & 1);            // 0 or all ones: the lane's bit
-            const uint64_t mb = __ballot(rep != 0);
+            const int rep = __builtin_amdgcn_sbfe(d, b, 1);   // 0 or all ones: the lane's bit
+            const uint64_t mb = __builtin_amdgcn_ballot_w64(rep != 0);
             plo &= ~((uint32_t)mb ^ (uint32_t)rep);      // keep lanes whose bit b agrees
             phi &= ~((uint32_t)(mb >> 32) ^ (uint32_t)rep);
         }
@@ -466,17 +466,19 @@ __global__ void k_write_skipped_all(int64_t* n_skipped, int64_t n) {
 
 // ---------------------------------------------------------------- scalar reduction
 
-// PW over p[0 .. len), len <= 8192 (element 0 replaced by v0 when use_v0): 32 blocks of
-// 256; lane l of block i holds elements 256 i + 4 l .. + 4 combined as (a0 + a1) + (a2 + a3),
-// then the wave butterfly; the 32 block values meet in a 5-level tree (identity for blocks
-// past len).  The loads of G blocks are in flight together.  Uniform result.
-template <typename T>
+// PW over p[0 .. len), len <= 256 NBLK (element 0 replaced by v0 when use_v0): NBLK blocks
+// of 256; lane l of block i holds elements 256 i + 4 l .. + 4 combined as (a0 + a1) + (a2 + a3),
+// then the wave butterfly; the NBLK block values meet in a log2(NBLK)-level tree (identity for
+// blocks past len), which is PW over 256 NBLK padded positions, the same value as over len.
+// The loads of G blocks are in flight together.  Uniform result.
+template <typename T, int NBLK = 32>
 __device__ __forceinline__ T wave_pw_range(const T* __restrict__ p, int64_t len, int lane,
                                            bool use_v0, T v0) {
-    constexpr int G = sizeof(T) == 4 ? 16 : 8;
-    T b[32];
+    constexpr int G0 = sizeof(T) == 4 ? 16 : 8;
+    constexpr int G = G0 < NBLK ? G0 : NBLK;
+    T b[NBLK];
 #pragma unroll
-    for (int g0 = 0; g0 < 32; g0 += G) {
+    for (int g0 = 0; g0 < NBLK; g0 += G) {
         if ((int64_t)g0 * 256 >= len) {
 #pragma unroll
             for (int i = 0; i < G; ++i) b[g0 + i] = ident<T>();
@@ -501,7 +503,7 @@ __device__ __forceinline__ T wave_pw_range(const T* __restrict__ p, int64_t len,
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int w = 32; w > 1; w /= 2) {
+    for (int w = NBLK; w > 1; w /= 2) {
 #pragma unroll
         for (int i = 0; i < w / 2; ++i) b[i] = b[2 * i] + b[2 * i + 1];
     }
@@ -582,7 +584,9 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const uint32_t* __restric
                                                        const uint32_t* __restrict__ nvalid,
                                                        T* __restrict__ out, T* __restrict__ pF,
                                                        T* __restrict__ pC) {
-    __shared__ uint32_t s_big[kSegD / 32 + 2];
+    // blocks longer than 32 values, for the waves: position in the range, destination, and the
+    // destination's first and end positions (read once, by the thread that found the block)
+    __shared__ uint32_t s_big[kSegD / 32 + 2][4];
     __shared__ uint32_t s_nbig;
     __shared__ uint32_t s_key[kSegD];
     __shared__ uint32_t s_prev;
@@ -613,14 +617,17 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const uint32_t* __restric
 
     // a block starts at every segment start, and at most once more inside this range: the
     // next multiple of D (in local rank) of the destination running into the range
-    auto item = [&](int64_t ps, uint32_t b) {
-        const int64_t seg_s = off[b], seg_e = off[b + 1];
+    auto item = [&](int64_t ps, uint32_t b, int64_t seg_s, int64_t seg_e) {
         const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
         if (len <= 32) {
             const T S = lane_pw_32<T>(V + ps, (int)len);
             emit_scalar<T>(S, ps, b, seg_s, seg_e, out, pF, pC);
         } else {
-            s_big[atomicAdd(&s_nbig, 1u)] = (uint32_t)(ps - lo);
+            uint32_t* e = s_big[atomicAdd(&s_nbig, 1u)];
+            e[0] = (uint32_t)(ps - lo);
+            e[1] = b;
+            e[2] = (uint32_t)seg_s;
+            e[3] = (uint32_t)seg_e;
         }
     };
     for (int i = 0; i < kSegD / 256; ++i) {
@@ -628,13 +635,13 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const uint32_t* __restric
         const int64_t p = lo + e;
         if (p < hi) {
             const uint32_t b = s_key[e];
-            if ((e == 0 ? s_prev : s_key[e - 1]) != b) item(p, b);
-            if (p == lo) {
-                const int64_t s0 = off[b];
-                if (s0 < lo) {
+            const bool head = (e == 0 ? s_prev : s_key[e - 1]) != b;
+            if (head || p == lo) {
+                const int64_t s0 = off[b], e0 = off[b + 1];
+                if (head) item(p, b, s0, e0);
+                if (p == lo && s0 < lo) {
                     const int64_t pc = s0 + cdiv(lo - s0, kSegD) * kSegD;
-                    const int64_t e0 = off[b + 1];
-                    if (pc < hi && pc < e0) item(pc, b);
+                    if (pc < hi && pc < e0) item(pc, b, s0, e0);
                 }
             }
         }
@@ -642,12 +649,23 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const uint32_t* __restric
     __syncthreads();
     const int nbig = (int)s_nbig;
     for (int it = wave; it < nbig; it += 4) {
-        const int64_t ps = lo + s_big[it];
-        const uint32_t b = s_key[s_big[it]];
-        const int64_t seg_s = off[b], seg_e = off[b + 1];
+        const int64_t ps = lo + s_big[it][0];
+        const uint32_t b = s_big[it][1];
+        const int64_t seg_s = s_big[it][2], seg_e = s_big[it][3];
         const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
-        const T S = wave_pw_range<T>(V + ps, len, lane, false, ident<T>());
-        if (lane == 0) emit_scalar<T>(S, ps, b, seg_s, seg_e, out, pF, pC);
+        const bool single = seg_e - seg_s <= kSegD;
+        // the destination's old value is read alongside the block's values
+        const T o = single ? out[b] : T(0);
+        // the shortest padded width that holds the block (all give the same value)
+        T S;
+        if (len <= 512) S = wave_pw_range<T, 2>(V + ps, len, lane, false, ident<T>());
+        else if (len <= 2048) S = wave_pw_range<T, 8>(V + ps, len, lane, false, ident<T>());
+        else S = wave_pw_range<T, 32>(V + ps, len, lane, false, ident<T>());
+        if (lane == 0) {
+            if (single) out[b] = o + S;
+            else if (ps == seg_s) pF[ps / kSegD] = S;
+            else pC[ps / kSegD] = S;
+        }
     }
 }
 
