@@ -286,11 +286,11 @@ __device__ __forceinline__ void radix_load(const uint32_t* __restrict__ keys_in,
 // which the lowest peer advances with one LDS atomic whose old value it hands to its peers.
 // Integers only, so exact.  Leaves every barrier it passes balanced; ends with the LDS counters
 // cleared for the next chunk.
-template <typename P, bool FIRST, bool ROWS, bool FULL>
+template <typename P, bool FIRST, bool ROWS, bool FULL, typename KO>
 __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_t (&key)[kItems<P>],
                                                  const P (&pay)[kItems<P>], int64_t base, int64_t m,
                                                  uint32_t B, int shift, uint32_t off0,
-                                                 uint32_t off1, uint32_t* __restrict__ keys_out,
+                                                 uint32_t off1, KO* __restrict__ keys_out,
                                                  P* __restrict__ pay_out, int tid, int lane,
                                                  int wave) {
     constexpr int IPT = kItems<P>;
@@ -369,7 +369,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
             const int i = k * 256 + tid;
             const uint32_t kk = sm.keys[i];
             const int64_t g = sm.gbase[digit_of<FIRST>(kk, B, shift)] + i;
-            keys_out[g] = kk;
+            keys_out[g] = (KO)kk;
             pay_out[g] = sm.pay[i];
         }
     } else {
@@ -377,7 +377,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         for (int i = tid; i < cntc; i += 256) {
             const uint32_t kk = sm.keys[i];
             const int64_t g = sm.gbase[digit_of<FIRST>(kk, B, shift)] + i;
-            keys_out[g] = kk;
+            keys_out[g] = (KO)kk;
             pay_out[g] = sm.pay[i];
         }
     }
@@ -387,10 +387,11 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
 // One chunk per workgroup, chunk xcd_chunk(b) for workgroup b: the dispatcher starts
 // workgroups in order, so the chunks an XCD holds at any moment are neighbours and their
 // writes into each bucket's region merge in its L2.
-template <typename P, bool FIRST, bool ROWS>
+// KO: the type keys are written in (uint16_t for the last pass when every valid key fits).
+template <typename P, bool FIRST, bool ROWS, typename KO>
 __global__ __launch_bounds__(256) void k_radix_scatter(
     const uint32_t* __restrict__ keys_in, const P* __restrict__ pay_in,
-    uint32_t* __restrict__ keys_out, P* __restrict__ pay_out, int64_t n,
+    KO* __restrict__ keys_out, P* __restrict__ pay_out, int64_t n,
     const uint32_t* __restrict__ nvalid, uint32_t B, int shift, int64_t nchunks,
     const uint32_t* __restrict__ hist_ex) {
     constexpr int IPT = kItems<P>;
@@ -411,12 +412,12 @@ __global__ __launch_bounds__(256) void k_radix_scatter(
     if (base + H <= m) {
         radix_load<P, FIRST, ROWS, true>(keys_in, pay_in, base, m, key, pay, wave, lane);
         __syncthreads();
-        radix_rank_write<P, FIRST, ROWS, true>(sm, key, pay, base, m, B, shift, off0, off1,
+        radix_rank_write<P, FIRST, ROWS, true, KO>(sm, key, pay, base, m, B, shift, off0, off1,
                                                keys_out, pay_out, tid, lane, wave);
     } else {
         radix_load<P, FIRST, ROWS, false>(keys_in, pay_in, base, m, key, pay, wave, lane);
         __syncthreads();
-        radix_rank_write<P, FIRST, ROWS, false>(sm, key, pay, base, m, B, shift, off0, off1,
+        radix_rank_write<P, FIRST, ROWS, false, KO>(sm, key, pay, base, m, B, shift, off0, off1,
                                                 keys_out, pay_out, tid, lane, wave);
     }
 }
@@ -428,7 +429,8 @@ __global__ void k_copy_word(const uint32_t* __restrict__ src, uint32_t* __restri
 // ---------------------------------------------------------------- destinations
 
 // off[b] = first sorted position with key >= b, for b in [0, B]; n_skipped = n - valid
-__global__ __launch_bounds__(256) void k_bin_offsets(const uint32_t* __restrict__ K,
+template <typename KT>
+__global__ __launch_bounds__(256) void k_bin_offsets(const KT* __restrict__ K,
                                                      const uint32_t* __restrict__ nvalid,
                                                      int64_t B, int64_t n, uint32_t* __restrict__ off,
                                                      int64_t* __restrict__ n_skipped) {
@@ -577,8 +579,8 @@ __device__ __forceinline__ void emit_scalar(T S, int64_t ps, uint32_t b, int64_t
     }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_segred_scalar(const uint32_t* __restrict__ K,
+template <typename T, typename KT>
+__global__ __launch_bounds__(256) void k_segred_scalar(const KT* __restrict__ K,
                                                        const T* __restrict__ V,
                                                        const uint32_t* __restrict__ off,
                                                        const uint32_t* __restrict__ nvalid,
@@ -597,19 +599,30 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const uint32_t* __restric
     const int64_t hi = (lo + kSegD < m) ? lo + kSegD : m;
     if (tid == 0) {
         s_nbig = 0u;
-        s_prev = lo > 0 ? K[lo - 1] : ~K[lo];
+        s_prev = lo > 0 ? (uint32_t)K[lo - 1] : ~(uint32_t)K[lo];
     }
     // the range's keys into LDS in one round trip (16-byte loads when the range is whole; K is
     // 256-byte aligned and lo a multiple of kSegD)
     if (hi - lo == kSegD) {
         typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 q[kSegD / 1024];
+        constexpr int KPV = 16 / sizeof(KT);             // keys per 16-byte load
+        u32x4 q[kSegD / KPV / 256];
 #pragma unroll
-        for (int i = 0; i < kSegD / 1024; ++i)
+        for (int i = 0; i < kSegD / KPV / 256; ++i)
             q[i] = reinterpret_cast<const u32x4*>(K + lo)[i * 256 + tid];
 #pragma unroll
-        for (int i = 0; i < kSegD / 1024; ++i)
-            reinterpret_cast<u32x4*>(s_key)[i * 256 + tid] = q[i];
+        for (int i = 0; i < kSegD / KPV / 256; ++i) {
+            if constexpr (sizeof(KT) == 4) {
+                reinterpret_cast<u32x4*>(s_key)[i * 256 + tid] = q[i];
+            } else {
+                // 8 keys: low and high halves of each word, in address order
+                const int e0 = (i * 256 + tid) * 8;
+                const u32x4 lo4 = {q[i].x & 0xffffu, q[i].x >> 16, q[i].y & 0xffffu, q[i].y >> 16};
+                const u32x4 hi4 = {q[i].z & 0xffffu, q[i].z >> 16, q[i].w & 0xffffu, q[i].w >> 16};
+                reinterpret_cast<u32x4*>(s_key + e0)[0] = lo4;
+                reinterpret_cast<u32x4*>(s_key + e0)[1] = hi4;
+            }
+        }
     } else {
         for (int i = tid; i < (int)(hi - lo); i += 256) s_key[i] = K[lo + i];
     }
@@ -921,6 +934,10 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
     uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
     const uint32_t B = (uint32_t)num_out;
     const int passes = key_passes(num_out);
+    // scalar destinations that all fit 16 bits: the last pass writes 16-bit keys, which the
+    // destination offsets and the reduction read (out-of-range keys land past the valid ones
+    // and are never read)
+    const bool k16 = !ROWS && num_out <= 65536;
     const unsigned grid = (unsigned)L.nchunks;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
@@ -942,22 +959,37 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
         // valid keys = offset of the out-of-range bucket in chunk 0
         if (first) k_copy_word<<<1, 1, 0, s>>>(hist + 256, ctrl);
         KernelTimer kt("k_radix_scatter", s);
-        if (first)
-            k_radix_scatter<P, true, ROWS><<<grid, 256, 0, s>>>(kin, pin, keys[p & 1], pay[p & 1], n,
-                                                                ctrl, B, shift, L.nchunks, hist);
+        uint32_t* ko = keys[p & 1];
+        uint16_t* ko16 = reinterpret_cast<uint16_t*>(ko);
+        const bool last16 = k16 && p == passes - 1;
+        if (first && last16)
+            k_radix_scatter<P, true, ROWS, uint16_t><<<grid, 256, 0, s>>>(
+                kin, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
+        else if (first)
+            k_radix_scatter<P, true, ROWS, uint32_t><<<grid, 256, 0, s>>>(
+                kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
+        else if (last16)
+            k_radix_scatter<P, false, ROWS, uint16_t><<<grid, 256, 0, s>>>(
+                kin, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         else
-            k_radix_scatter<P, false, ROWS><<<grid, 256, 0, s>>>(kin, pin, keys[p & 1], pay[p & 1],
-                                                                 n, ctrl, B, shift, L.nchunks, hist);
+            k_radix_scatter<P, false, ROWS, uint32_t><<<grid, 256, 0, s>>>(
+                kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         st = launch_status();
         if (st != DET_SUCCESS) return st;
     }
     const uint32_t* K = keys[(passes - 1) & 1];
+    const uint16_t* K16 = reinterpret_cast<const uint16_t*>(K);
     const P* SP = pay[(passes - 1) & 1];
     {
         int64_t g = cdiv(num_out + 1, 256);
         if (g > 8192) g = 8192;
         KernelTimer kt("k_bin_offsets", s);
-        k_bin_offsets<<<dim3((unsigned)g), dim3(256), 0, s>>>(K, ctrl, num_out, n, off, n_skipped);
+        if (k16)
+            k_bin_offsets<uint16_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(K16, ctrl, num_out, n,
+                                                                             off, n_skipped);
+        else
+            k_bin_offsets<uint32_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(K, ctrl, num_out, n,
+                                                                             off, n_skipped);
     }
     T* pF = reinterpret_cast<T*>(ws + L.pF);
     T* pC = reinterpret_cast<T*>(ws + L.pC);
@@ -966,8 +998,12 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
     if constexpr (!ROWS) {
         {
             KernelTimer kt("k_segred_scalar", s);
-            k_segred_scalar<T><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
-                K, reinterpret_cast<const T*>(SP), off, ctrl, out, pF, pC);
+            if (k16)
+                k_segred_scalar<T, uint16_t><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
+                    K16, reinterpret_cast<const T*>(SP), off, ctrl, out, pF, pC);
+            else
+                k_segred_scalar<T, uint32_t><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
+                    K, reinterpret_cast<const T*>(SP), off, ctrl, out, pF, pC);
         }
         k_segred_scalar_long<T><<<dim3((unsigned)lg), dim3(256), 0, s>>>(off, num_out, pF, pC, out);
     } else {
