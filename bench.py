@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--only", default="", help="comma list of sum,scan,scatter (profiling)")
     ap.add_argument("--repeat-runs", type=int, default=100,
                     help="runs whose distinct results are counted (library and baselines)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other configurations (parity cases) of the spec")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of 2^log2n f32 (1 GiB each way at 2^28): "
                          "the known-size kernel that scales rocprofv3 byte counters")
@@ -58,14 +60,20 @@ def log(msg):
 
 
 def kernel_bytes_per_step(n, B):
-    """Algorithmic HBM bytes each library kernel must move in one step (f32, row_len 1)."""
+    """Algorithmic HBM bytes each library kernel must move in one step (f32, row_len 1).
+
+    The scatter's two radix passes move key and value in and out: 16 bytes per element in the
+    first; the last pass writes 16-bit keys when every destination fits 16 bits, so 14 bytes.
+    The segment reduction reads the sorted keys (2 bytes then) and values, and reads and writes
+    each destination once."""
     parts = -(-n // (1 << 14))
+    kb = 2.0 if B <= 65536 else 4.0
     return {
         "k_sum_chunks<f32>": 4.0 * n + 4.0 * parts,      # values, then the partials' level
         "k_scan<f32>": 8.0 * n,                          # read x, write y
         "k_radix_hist": 2 * 4.0 * n,                     # keys, one pass per 8-bit digit
-        "k_radix_scatter": 2 * 16.0 * n,                 # keys + values in and out, two passes
-        "k_segred_scalar": 8.0 * n + 8.0 * B,            # sorted keys + values, out r/w
+        "k_radix_scatter": 16.0 * n + (12.0 + kb) * n,   # first pass, then the last pass
+        "k_segred_scalar": (kb + 4.0) * n + 8.0 * B,     # sorted keys + values, out r/w
     }
 
 
@@ -96,6 +104,131 @@ def measured_traffic(kernel):
             return None
         return int(m_b.group(1))
     return None
+
+
+def time_configs(det, workloads, dev, log):
+    """Times every configuration of the workload spec besides the headline step (one GPU,
+    inputs resident): median over repetitions of one call, bracketed by events on the current
+    stream.  Returns {case: {ms, GB_s, frac_hbm, Gelem_s}} with algorithmic bytes as in the
+    headline step; the large f64 case also reports the distinct results over launch grids of
+    1x, 2x and 4x the compute-unit count."""
+    import hashlib as _h
+
+    import numpy as np
+    import torch
+
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+
+    def med(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    def put(name, fn, nbytes, nelem, reps):
+        ms = med(fn, reps)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_GBS, 4),
+                     "Gelem_s": round(nelem / (ms * 1e-3) / 1e9, 3)}
+
+    def dev_t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def ws_of(nbytes):
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+    # sum, n = 2^20 uniform and n = 4096 ones
+    x = dev_t(workloads.uniform01(1 << 20, seed=0))
+    w = ws_of(det.det_sum_workspace_size(1 << 20, 0))
+    o = torch.empty((), dtype=torch.float32, device=dev)
+    put("sum f32 n=2^20 U[0,1)", lambda: det.det_sum(x, out=o, ws=w), 4 << 20, 1 << 20, 50)
+    ones = torch.ones(4096, dtype=torch.float32, device=dev)
+    put("sum f32 n=4096 ones", lambda: det.det_sum(ones, out=o, ws=w), 4 * 4096, 4096, 50)
+    # scatter, n = 2^24: uniform over 65,536 bins, and every value into bin 0
+    n = 1 << 24
+    v = dev_t(workloads.normal(n, seed=1))
+    for label, bins, B in (("65536 uniform bins", workloads.bins_uniform(n, 65536, seed=1), 65536),
+                           ("bin 0 (contended)", np.zeros(n, np.int32), 65536)):
+        bi = dev_t(bins)
+        out = torch.zeros(B, dtype=torch.float32, device=dev)
+        w = ws_of(det.det_scatter_add_workspace_size(n, B, 1, 0))
+        put(f"scatter f32 n=2^24 into {label}",
+            lambda: det.det_scatter_add(v, bi, out, ws=w), 8.0 * n + 8.0 * B, n, 20)
+    del v
+    # scan: f32 and f64, inclusive/exclusive x forward/reverse
+    modes = ((False, False, "incl"), (True, False, "excl"), (False, True, "incl rev"),
+             (True, True, "excl rev"))
+    for dt, tdt, code in ((np.float32, torch.float32, 0), (np.float64, torch.float64, 1)):
+        for n in (16384, 164738, 1048577, 1 << 28):
+            xs = dev_t(workloads.scan_values(n, dt, seed=2))
+            ys = torch.empty_like(xs)
+            w = ws_of(det.det_scan_workspace_size(n, code, 3, 0))
+            for ex, rv, tag in modes:
+                put(f"scan {np.dtype(dt).name} n={n if n < (1 << 28) else '2^28'} {tag}",
+                    lambda: det.det_scan(xs, y=ys, exclusive=ex, reverse=rv, ws=w),
+                    2.0 * n * xs.element_size(), n, 20 if n < (1 << 28) else 10)
+            del xs, ys
+    log("configs: sum, scatter, scan timed")
+    # segmented scan f32 2^26 (geometric segments, mean 100) and the row accumulate
+    n = 1 << 26
+    xs = dev_t(workloads.scan_values(n, np.float32, seed=3))
+    offs_h = workloads.segment_offsets(n, 100.0, seed=3)
+    offs = dev_t(offs_h)
+    ys = torch.empty_like(xs)
+    w = ws_of(det.det_scan_workspace_size(n, 0, 3, offs_h.size - 1))
+    for ex, rv, tag in modes:
+        put(f"segmented scan f32 n=2^26 mean 100 {tag}",
+            lambda: det.det_scan(xs, y=ys, exclusive=ex, reverse=rv, offsets=offs, ws=w),
+            8.0 * n + 8.0 * offs_h.size, n, 10)
+    del xs, ys
+    src, rows, out0 = workloads.rows_case()
+    st, rt, ot0 = dev_t(src), dev_t(rows), dev_t(out0)
+    ot = ot0.clone()
+    w = ws_of(det.det_scatter_add_workspace_size(src.shape[0], out0.shape[0], src.shape[1], 0))
+    put("rows f32 2^16x256 into 2^14 rows", lambda: det.det_scatter_add(st, rt, ot, ws=w),
+        4.0 * src.size + 4.0 * rows.size + 8.0 * out0.size, src.size, 20)
+    log("configs: segmented scan and rows timed")
+    # large mixed-magnitude f64, n = 2^29: sum, scan, scatter into 2^20 Zipf(1.1) bins
+    n = 1 << 29
+    xm = dev_t(workloads.mixed_f64(n, seed=4))
+    o64 = torch.empty((), dtype=torch.float64, device=dev)
+    w = ws_of(max(det.det_sum_workspace_size(n, 1), det.det_scan_workspace_size(n, 1, 0, 0)))
+    put("sum f64 n=2^29 mixed", lambda: det.det_sum(xm, out=o64, ws=w), 8.0 * n, n, 10)
+    ym = torch.empty_like(xm)
+    put("scan f64 n=2^29 mixed incl", lambda: det.det_scan(xm, y=ym, ws=w), 16.0 * n, n, 5)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    hs = {"sum": set(), "scan": set()}
+    for g in (cus, 2 * cus, 4 * cus):
+        det.det_debug_set_launch(g, 0)
+        det.det_sum(xm, out=o64, ws=w)
+        det.det_scan(xm, y=ym, ws=w)
+        torch.cuda.synchronize()
+        hs["sum"].add(_h.sha256(o64.cpu().numpy().tobytes()).hexdigest())
+        hs["scan"].add(_h.sha256(ym.cpu().numpy().tobytes()).hexdigest())
+    det.det_debug_set_launch(0, 0)
+    res["sum f64 n=2^29 mixed"]["distinct_over_grids_1x_2x_4x_CUs"] = len(hs["sum"])
+    res["scan f64 n=2^29 mixed incl"]["distinct_over_grids_1x_2x_4x_CUs"] = len(hs["scan"])
+    del ym
+    bi = dev_t(workloads.zipf_bins(n, 1 << 20, 1.1, seed=4))
+    out = torch.zeros(1 << 20, dtype=torch.float64, device=dev)
+    w = ws_of(det.det_scatter_add_workspace_size(n, 1 << 20, 1, 1))
+    put("scatter f64 n=2^29 mixed into 2^20 Zipf(1.1) bins",
+        lambda: det.det_scatter_add(xm, bi, out, ws=w), 12.0 * n + 16.0 * (1 << 20), n, 5)
+    del xm, bi, w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log("configs: f64 2^29 timed")
+    return res
 
 
 def main():
@@ -295,6 +428,11 @@ def main():
                         "algorithmic_bytes_per_launch": int(per_launch),
                         "avg_launch_ms": round(avg, 5)}
 
+    # ---------------------------------------------------------------- the other configurations
+    configs = None
+    if not args.no_configs:
+        configs = time_configs(det, workloads, dev, log)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -344,6 +482,7 @@ def main():
         "kernels": kern_rep,
         "ops": op_rep,
         "cpu_baseline": cpu,
+        "configs": configs,
     }
     print(json.dumps(line))
 
