@@ -350,15 +350,21 @@ __device__ __forceinline__ void load_run(const T* __restrict__ x, int64_t n, int
     }
 }
 
+// One 16-byte non-temporal store of kGW consecutive elements (4 f32 or 2 f64): a lane writes
+// 16 contiguous bytes per store, so a wave's store covers 1 KiB without gaps.  (Two 16-byte
+// stores per lane at a 32-byte stride, each leaving every other 16 bytes to the other, made
+// the f64 readout of a 2^28 scan about 25% to 80% slower on MI355X.)
 template <typename T>
-__device__ __forceinline__ void nt_store4(T* p, T a, T b, T c, T d) {
+constexpr int kGW = 16 / (int)sizeof(T);
+
+template <typename T>
+__device__ __forceinline__ void nt_store16(T* p, const T (&v)[kGW<T>]) {
     if constexpr (sizeof(T) == 4) {
-        f32x4 v = {a, b, c, d};
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+        f32x4 q = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(p));
     } else {
-        f64x2 v0 = {a, b}, v1 = {c, d};
-        __builtin_nontemporal_store(v0, reinterpret_cast<f64x2*>(p));
-        __builtin_nontemporal_store(v1, reinterpret_cast<f64x2*>(p) + 1);
+        f64x2 q = {v[0], v[1]};
+        __builtin_nontemporal_store(q, reinterpret_cast<f64x2*>(p));
     }
 }
 
@@ -393,22 +399,16 @@ __device__ __forceinline__ void readout_incl(T* __restrict__ y, int64_t n, int64
                                              const T* xs, const uint32_t* hbs, int lane) {
     const bool full = fw + kWaveElems <= n;
     T* base = REV ? y + (n - fw - kWaveElems) : y + fw;   // lowest original index of the wave
+    constexpr int GW = kGW<T>;
     if (full && aligned16(base)) {
 #pragma unroll
-        for (int r = 0; r < kWaveElems / 256; ++r) {
-            const int o = r * 256 + 4 * lane;                 // original offset within the wave
-            if (REV) {
-                const int e = (kWaveElems - 1) - o;           // flipped element of offset o
-                nt_store4<T>(base + o, combine_at<T, SEG>(pk, xs, hbs, e),
-                             combine_at<T, SEG>(pk, xs, hbs, e - 1),
-                             combine_at<T, SEG>(pk, xs, hbs, e - 2),
-                             combine_at<T, SEG>(pk, xs, hbs, e - 3));
-            } else {
-                nt_store4<T>(base + o, combine_at<T, SEG>(pk, xs, hbs, o),
-                             combine_at<T, SEG>(pk, xs, hbs, o + 1),
-                             combine_at<T, SEG>(pk, xs, hbs, o + 2),
-                             combine_at<T, SEG>(pk, xs, hbs, o + 3));
-            }
+        for (int r = 0; r < kWaveElems / (64 * GW); ++r) {
+            const int o = r * 64 * GW + GW * lane;            // original offset within the wave
+            T v[GW];
+#pragma unroll
+            for (int k = 0; k < GW; ++k)   // flipped element of offset o + k
+                v[k] = combine_at<T, SEG>(pk, xs, hbs, REV ? (kWaveElems - 1) - o - k : o + k);
+            nt_store16<T>(base + o, v);
         }
     } else {
         const int64_t left = n - fw;
@@ -447,26 +447,27 @@ __device__ __forceinline__ void readout_excl(T* __restrict__ y, int64_t n, int64
     if (last < fw + 1) return;
     const int64_t lo = REV ? n - 1 - last : fw + 1;
     const int64_t hi = REV ? n - 1 - fw : last + 1;
-    // interior [A, Z): starts at the first 16-byte-aligned element, whole groups of 4
-    constexpr int64_t EPV = 16 / sizeof(T);   // elements per 16 bytes
+    // interior [A, Z): starts at the first 16-byte-aligned element, whole 16-byte groups
+    constexpr int64_t GW = kGW<T>;   // elements per 16 bytes
     const int64_t ye = (int64_t)(reinterpret_cast<uintptr_t>(y) / sizeof(T));
-    int64_t A = lo + ((EPV - ((ye + lo) % EPV)) % EPV);
+    int64_t A = lo + ((GW - ((ye + lo) % GW)) % GW);
     if (A > hi) A = hi;
-    const int64_t Z = A + ((hi - A) / 4) * 4;
+    const int64_t Z = A + ((hi - A) / GW) * GW;
     for (int64_t k = lo + lane; k < A; k += 64)
         y[k] = excl_value<T, SEG, REV>(n, F0, fw, k, pk, xs, hbs, s_heads);
     for (int64_t k = Z + lane; k < hi; k += 64)
         y[k] = excl_value<T, SEG, REV>(n, F0, fw, k, pk, xs, hbs, s_heads);
-    const int64_t ngroups = (Z - A) / 4;   // at most 512
+    const int64_t ngroups = (Z - A) / GW;   // at most 2048 / GW
 #pragma unroll
-    for (int r = 0; r < kWaveElems / 256; ++r) {
+    for (int r = 0; r < kWaveElems / (64 * (int)GW); ++r) {
         const int64_t gi = (int64_t)r * 64 + lane;
         if (gi < ngroups) {
-            const int64_t g = A + 4 * gi;
-            nt_store4<T>(y + g, excl_value<T, SEG, REV>(n, F0, fw, g, pk, xs, hbs, s_heads),
-                         excl_value<T, SEG, REV>(n, F0, fw, g + 1, pk, xs, hbs, s_heads),
-                         excl_value<T, SEG, REV>(n, F0, fw, g + 2, pk, xs, hbs, s_heads),
-                         excl_value<T, SEG, REV>(n, F0, fw, g + 3, pk, xs, hbs, s_heads));
+            const int64_t g = A + GW * gi;
+            T v[GW];
+#pragma unroll
+            for (int k = 0; k < (int)GW; ++k)
+                v[k] = excl_value<T, SEG, REV>(n, F0, fw, g + k, pk, xs, hbs, s_heads);
+            nt_store16<T>(y + g, v);
         }
     }
 }
