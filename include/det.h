@@ -139,6 +139,17 @@ det_status det_scatter_add(const void* values, const int32_t* index, int64_t n, 
                            det_dtype dtype, void* out, int64_t num_out, void* prev,
                            int64_t* n_skipped, void* ws, size_t ws_bytes, void* stream);
 
+/* Keyed scatter-subtract, the reproducible form of atomic_sub(out, index[i], values[i]): the
+ * values are negated and then added in the order of det_scatter_add (Warp "Deterministic
+ * Execution", section "Pattern 1: Accumulation", its table of atomics).  So for destination r
+ * and column c, out = out + PW(-M) with every element of M negated on its own; this is not
+ * out - PW(M) where a destination's contributions cancel to zero (the zero's sign differs).
+ * Arguments, workspace (det_scatter_add_workspace_size), ownership and errors as for
+ * det_scatter_add; prev receives the destination rows before the call. */
+det_status det_scatter_sub(const void* values, const int32_t* index, int64_t n, int64_t row_len,
+                           det_dtype dtype, void* out, int64_t num_out, void* prev,
+                           int64_t* n_skipped, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------ introspection */
 
 /* Version of the association order; results of one version never change. */

@@ -14,6 +14,9 @@ Every function here follows the association order stated in ``detref.c``:
 * ``scatter_add``   -- stable grouping by destination in ascending source index, ``pw`` per
                        destination and column, initial value added last (Warp "Deterministic
                        Execution", Pattern 1; ``warp.tile_atomic_add_indexed`` for rows).
+* ``scatter_sub``   -- the values negated one by one, then ``scatter_add`` (Warp "Deterministic
+                       Execution", Pattern 1: atomic_sub's values are negated and added in a
+                       fixed order).
 * ``scan``          -- tiles of V*W*NW elements, anchors every A tiles and every A*A2 tiles
                        (drjit-core pull request "Make CUDA floating-point prefix sums
                        deterministic").
@@ -147,6 +150,14 @@ def scatter_add(values: np.ndarray, index: np.ndarray, out: np.ndarray,
     if k < 0:
         raise RuntimeError(f"oracle scatter_add failed ({k})")
     return new, prev, int(k)
+
+
+def scatter_sub(values: np.ndarray, index: np.ndarray, out: np.ndarray,
+                want_prev: bool = False) -> Tuple[np.ndarray, Optional[np.ndarray], int]:
+    """Keyed scatter-subtract: each value negated (an exact sign flip), then ``scatter_add``.
+    Not ``out - pw(M)``: when a destination's contributions cancel, the two differ in the
+    sign of the zero."""
+    return scatter_add(np.negative(np.ascontiguousarray(values)), index, out, want_prev)
 
 
 def scan(x: np.ndarray, exclusive: bool = False, reverse: bool = False,

@@ -178,9 +178,13 @@ size_t det_scatter_add_workspace_size(int64_t n, int64_t num_out, int64_t row_le
     return scatter_workspace(n, num_out, row_len, dtype);
 }
 
-det_status det_scatter_add(const void* values, const int32_t* index, int64_t n, int64_t row_len,
+}  // extern "C"
+
+namespace {
+det_status scatter_checked(const void* values, const int32_t* index, int64_t n, int64_t row_len,
                            det_dtype dtype, void* out, int64_t num_out, void* prev,
-                           int64_t* n_skipped, void* ws, size_t ws_bytes, void* stream) {
+                           int64_t* n_skipped, void* ws, size_t ws_bytes, bool negate,
+                           void* stream) {
     if (!valid_dtype(dtype)) return DET_ERROR_UNSUPPORTED;
     if (n < 0 || num_out < 0 || row_len < 1) return DET_ERROR_INVALID_VALUE;
     if (n > DET_MAX_N || num_out > DET_MAX_N) return DET_ERROR_TOO_LARGE;
@@ -202,7 +206,24 @@ det_status det_scatter_add(const void* values, const int32_t* index, int64_t n, 
     if (!ws || !ws_aligned(ws) || ws_bytes < scatter_workspace(n, num_out, row_len, dtype))
         return DET_ERROR_WORKSPACE;
     return scatter_launch(values, index, n, row_len, dtype, out, num_out, prev, n_skipped, ws,
-                          ws_bytes, static_cast<hipStream_t>(stream));
+                          ws_bytes, negate, static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+extern "C" {
+
+det_status det_scatter_add(const void* values, const int32_t* index, int64_t n, int64_t row_len,
+                           det_dtype dtype, void* out, int64_t num_out, void* prev,
+                           int64_t* n_skipped, void* ws, size_t ws_bytes, void* stream) {
+    return scatter_checked(values, index, n, row_len, dtype, out, num_out, prev, n_skipped, ws,
+                           ws_bytes, false, stream);
+}
+
+det_status det_scatter_sub(const void* values, const int32_t* index, int64_t n, int64_t row_len,
+                           det_dtype dtype, void* out, int64_t num_out, void* prev,
+                           int64_t* n_skipped, void* ws, size_t ws_bytes, void* stream) {
+    return scatter_checked(values, index, n, row_len, dtype, out, num_out, prev, n_skipped, ws,
+                           ws_bytes, true, stream);
 }
 
 int det_spec_version(void) { return 1; }

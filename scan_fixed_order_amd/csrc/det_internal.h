@@ -43,9 +43,10 @@ det_status scan_launch(const void* x, void* y, int64_t n, det_dtype dt, unsigned
 
 // ---- scatter-add
 size_t scatter_workspace(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt);
+// negate: every value enters negated (scatter-subtract)
 det_status scatter_launch(const void* values, const int32_t* index, int64_t n, int64_t row_len,
                           det_dtype dt, void* out, int64_t num_out, void* prev, int64_t* n_skipped,
-                          void* ws, size_t ws_bytes, hipStream_t s);
+                          void* ws, size_t ws_bytes, bool negate, hipStream_t s);
 
 // Workgroups of `block` threads of kernel `fn` that are resident on the current device at once
 // (occupancy x compute units), cached per device and kernel; 0 if the runtime cannot tell.

@@ -468,12 +468,13 @@ __global__ void k_write_skipped_all(int64_t* n_skipped, int64_t n) {
 
 // ---------------------------------------------------------------- scalar reduction
 
-// PW over p[0 .. len), len <= 256 NBLK (element 0 replaced by v0 when use_v0): NBLK blocks
+// PW over p[0 .. len) (each element negated when NEG; the identity padding is not), len <= 256
+// NBLK (element 0 replaced by v0 when use_v0): NBLK blocks
 // of 256; lane l of block i holds elements 256 i + 4 l .. + 4 combined as (a0 + a1) + (a2 + a3),
 // then the wave butterfly; the NBLK block values meet in a log2(NBLK)-level tree (identity for
 // blocks past len), which is PW over 256 NBLK padded positions, the same value as over len.
 // The loads of G blocks are in flight together.  Uniform result.
-template <typename T, int NBLK = 32>
+template <typename T, int NBLK = 32, bool NEG = false>
 __device__ __forceinline__ T wave_pw_range(const T* __restrict__ p, int64_t len, int lane,
                                            bool use_v0, T v0) {
     constexpr int G0 = sizeof(T) == 4 ? 16 : 8;
@@ -493,7 +494,7 @@ __device__ __forceinline__ T wave_pw_range(const T* __restrict__ p, int64_t len,
             const T* q = p + blk + 4 * lane;
             const int rem = (int)((len - blk) < 256 ? (len - blk) : 256) - 4 * lane;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a[i][r] = rem > r ? q[r] : ident<T>();
+            for (int r = 0; r < 4; ++r) a[i][r] = rem > r ? (NEG ? -q[r] : q[r]) : ident<T>();
         }
 #pragma unroll
         for (int i = 0; i < G; ++i) {
@@ -547,15 +548,16 @@ __device__ __forceinline__ T wave_pw_long(const T* __restrict__ p, int64_t len, 
     return readlane(acc, 0);
 }
 
-// PW over v[0 .. len), len <= 32, by one lane: pad to 32 with the identity, 5-level tree
-template <typename T>
+// PW over v[0 .. len) (each element negated when NEG), len <= 32, by one lane: pad to 32 with
+// the identity, 5-level tree
+template <typename T, bool NEG = false>
 __device__ __forceinline__ T lane_pw_32(const T* __restrict__ v, int len) {
     T a[32];
 #pragma unroll
     for (int q = 0; q < 32; ++q) a[q] = ident<T>();
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
-        if (q < len) a[q] = v[q];
+        if (q < len) a[q] = NEG ? -v[q] : v[q];
     }
 #pragma unroll
     for (int w = 32; w > 1; w /= 2) {
@@ -579,7 +581,9 @@ __device__ __forceinline__ void emit_scalar(T S, int64_t ps, uint32_t b, int64_t
     }
 }
 
-template <typename T, typename KT>
+// NEG: every value enters negated (scatter-subtract: the values are negated, then added in the
+// same order).
+template <typename T, typename KT, bool NEG>
 __global__ __launch_bounds__(256) void k_segred_scalar(const KT* __restrict__ K,
                                                        const T* __restrict__ V,
                                                        const uint32_t* __restrict__ off,
@@ -633,7 +637,7 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const KT* __restrict__ K,
     auto item = [&](int64_t ps, uint32_t b, int64_t seg_s, int64_t seg_e) {
         const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
         if (len <= 32) {
-            const T S = lane_pw_32<T>(V + ps, (int)len);
+            const T S = lane_pw_32<T, NEG>(V + ps, (int)len);
             emit_scalar<T>(S, ps, b, seg_s, seg_e, out, pF, pC);
         } else {
             uint32_t* e = s_big[atomicAdd(&s_nbig, 1u)];
@@ -671,9 +675,9 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const KT* __restrict__ K,
         const T o = single ? out[b] : T(0);
         // the shortest padded width that holds the block (all give the same value)
         T S;
-        if (len <= 512) S = wave_pw_range<T, 2>(V + ps, len, lane, false, ident<T>());
-        else if (len <= 2048) S = wave_pw_range<T, 8>(V + ps, len, lane, false, ident<T>());
-        else S = wave_pw_range<T, 32>(V + ps, len, lane, false, ident<T>());
+        if (len <= 512) S = wave_pw_range<T, 2, NEG>(V + ps, len, lane, false, ident<T>());
+        else if (len <= 2048) S = wave_pw_range<T, 8, NEG>(V + ps, len, lane, false, ident<T>());
+        else S = wave_pw_range<T, 32, NEG>(V + ps, len, lane, false, ident<T>());
         if (lane == 0) {
             if (single) out[b] = o + S;
             else if (ps == seg_s) pF[ps / kSegD] = S;
@@ -712,7 +716,7 @@ __global__ __launch_bounds__(256) void k_segred_scalar_long(const uint32_t* __re
 
 // ---------------------------------------------------------------- row reduction
 
-template <typename T>
+template <typename T, bool NEG>
 __global__ __launch_bounds__(256) void k_segred_rows(const uint32_t* __restrict__ K,
                                                      const uint32_t* __restrict__ R,
                                                      const uint32_t* __restrict__ off,
@@ -782,7 +786,7 @@ __global__ __launch_bounds__(256) void k_segred_rows(const uint32_t* __restrict_
 #pragma unroll
                         for (int cc = 0; cc < CPL; ++cc) {
                             const int64_t col = c0 + cc * 64 + lane;
-                            v[r][cc] = col < d ? row[col] : ident<T>();
+                            v[r][cc] = col < d ? (NEG ? -row[col] : row[col]) : ident<T>();
                         }
                     } else {
 #pragma unroll
@@ -906,7 +910,8 @@ SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
 
 template <typename T, typename P, bool ROWS>
 det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_t row_len, T* out,
-                        int64_t num_out, T* prev, int64_t* n_skipped, char* ws, hipStream_t s) {
+                        int64_t num_out, T* prev, int64_t* n_skipped, char* ws, bool neg,
+                        hipStream_t s) {
     const SLayout L = slayout(n, num_out, row_len, sizeof(T) == 8 ? DET_F64 : DET_F32);
     if (n == 0) {
         if (n_skipped) {
@@ -998,19 +1003,28 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
     if constexpr (!ROWS) {
         {
             KernelTimer kt("k_segred_scalar", s);
-            if (k16)
-                k_segred_scalar<T, uint16_t><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
-                    K16, reinterpret_cast<const T*>(SP), off, ctrl, out, pF, pC);
+            const dim3 g((unsigned)L.nrange), b(256);
+            const T* SV = reinterpret_cast<const T*>(SP);
+            if (k16 && !neg)
+                k_segred_scalar<T, uint16_t, false><<<g, b, 0, s>>>(K16, SV, off, ctrl, out, pF, pC);
+            else if (k16)
+                k_segred_scalar<T, uint16_t, true><<<g, b, 0, s>>>(K16, SV, off, ctrl, out, pF, pC);
+            else if (!neg)
+                k_segred_scalar<T, uint32_t, false><<<g, b, 0, s>>>(K, SV, off, ctrl, out, pF, pC);
             else
-                k_segred_scalar<T, uint32_t><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
-                    K, reinterpret_cast<const T*>(SP), off, ctrl, out, pF, pC);
+                k_segred_scalar<T, uint32_t, true><<<g, b, 0, s>>>(K, SV, off, ctrl, out, pF, pC);
         }
         k_segred_scalar_long<T><<<dim3((unsigned)lg), dim3(256), 0, s>>>(off, num_out, pF, pC, out);
     } else {
         {
             KernelTimer kt("k_segred_rows", s);
-            k_segred_rows<T><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
-                K, reinterpret_cast<const uint32_t*>(SP), off, ctrl, values, row_len, out, pF, pC);
+            const uint32_t* SR = reinterpret_cast<const uint32_t*>(SP);
+            if (!neg)
+                k_segred_rows<T, false><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
+                    K, SR, off, ctrl, values, row_len, out, pF, pC);
+            else
+                k_segred_rows<T, true><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
+                    K, SR, off, ctrl, values, row_len, out, pF, pC);
         }
         int64_t rg = cdiv(num_out, 256);
         if (rg > 4096) rg = 4096;
@@ -1028,7 +1042,7 @@ size_t scatter_workspace(int64_t n, int64_t num_out, int64_t row_len, det_dtype 
 
 det_status scatter_launch(const void* values, const int32_t* index, int64_t n, int64_t row_len,
                           det_dtype dt, void* out, int64_t num_out, void* prev, int64_t* n_skipped,
-                          void* ws, size_t ws_bytes, hipStream_t s) {
+                          void* ws, size_t ws_bytes, bool negate, hipStream_t s) {
     (void)ws_bytes;
     char* w = static_cast<char*>(ws);
     if (dt == DET_F32) {
@@ -1036,15 +1050,15 @@ det_status scatter_launch(const void* values, const int32_t* index, int64_t n, i
         float* o = static_cast<float*>(out);
         float* pr = static_cast<float*>(prev);
         if (row_len == 1)
-            return scatter_impl<float, uint32_t, false>(v, index, n, 1, o, num_out, pr, n_skipped, w, s);
-        return scatter_impl<float, uint32_t, true>(v, index, n, row_len, o, num_out, pr, n_skipped, w, s);
+            return scatter_impl<float, uint32_t, false>(v, index, n, 1, o, num_out, pr, n_skipped, w, negate, s);
+        return scatter_impl<float, uint32_t, true>(v, index, n, row_len, o, num_out, pr, n_skipped, w, negate, s);
     }
     const double* v = static_cast<const double*>(values);
     double* o = static_cast<double*>(out);
     double* pr = static_cast<double*>(prev);
     if (row_len == 1)
-        return scatter_impl<double, uint64_t, false>(v, index, n, 1, o, num_out, pr, n_skipped, w, s);
-    return scatter_impl<double, uint32_t, true>(v, index, n, row_len, o, num_out, pr, n_skipped, w, s);
+        return scatter_impl<double, uint64_t, false>(v, index, n, 1, o, num_out, pr, n_skipped, w, negate, s);
+    return scatter_impl<double, uint32_t, true>(v, index, n, row_len, o, num_out, pr, n_skipped, w, negate, s);
 }
 
 }  // namespace det

@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
     L.det_scatter_add_workspace_size.restype = sz
     L.det_scatter_add.argtypes = [p, p, i64, i64, i, p, i64, p, p, p, sz, p]
     L.det_scatter_add.restype = i
+    L.det_scatter_sub.argtypes = [p, p, i64, i64, i, p, i64, p, p, p, sz, p]
+    L.det_scatter_sub.restype = i
     L.det_spec_version.argtypes, L.det_spec_version.restype = [], i
     L.det_spec_constants.argtypes = [ctypes.POINTER(i64)] * 4
     L.det_spec_constants.restype = None
@@ -173,14 +175,9 @@ def det_scatter_add_workspace_size(n: int, num_out: int, row_len: int, dtype_cod
     return lib().det_scatter_add_workspace_size(n, num_out, row_len, dtype_code)
 
 
-def det_scatter_add(values: torch.Tensor, index: torch.Tensor, out: torch.Tensor,
-                    prev: Optional[torch.Tensor] = None, n_skipped: Optional[torch.Tensor] = None,
-                    ws: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """``out[index[i]] += values[i]`` along axis 0 in the fixed order; returns ``out``.
-
-    ``values``: [n] or [n, *row]; ``index``: int32 [n]; ``out``: [num_out] or [num_out, *row].
-    ``prev`` (same shape as values) receives the destination rows before the call;
-    ``n_skipped`` (int64, one element) receives the number of out-of-range indices."""
+def _scatter(entry: str, values: torch.Tensor, index: torch.Tensor, out: torch.Tensor,
+             prev: Optional[torch.Tensor], n_skipped: Optional[torch.Tensor],
+             ws: Optional[torch.Tensor]) -> torch.Tensor:
     values = _flat(values)
     index = _flat(index)
     out = _flat(out)
@@ -205,10 +202,58 @@ def det_scatter_add(values: torch.Tensor, index: torch.Tensor, out: torch.Tensor
     if n_skipped is not None and (n_skipped.dtype != torch.int64 or n_skipped.numel() < 1):
         raise ValueError("n_skipped must be an int64 tensor with one element")
     w = _workspace(det_scatter_add_workspace_size(n, num_out, row_len, dt), values.device, ws)
-    _check(lib().det_scatter_add(_dev_ptr(values), _dev_ptr(index), n, row_len, dt, _dev_ptr(out),
+    _check(getattr(lib(), entry)(_dev_ptr(values), _dev_ptr(index), n, row_len, dt, _dev_ptr(out),
                                  num_out, _dev_ptr(prev), _dev_ptr(n_skipped), _dev_ptr(w),
-                                 w.numel(), _stream(values.device)), "det_scatter_add")
+                                 w.numel(), _stream(values.device)), entry)
     return out
+
+
+def det_scatter_add(values: torch.Tensor, index: torch.Tensor, out: torch.Tensor,
+                    prev: Optional[torch.Tensor] = None, n_skipped: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``out[index[i]] += values[i]`` along axis 0 in the fixed order; returns ``out``.
+
+    ``values``: [n] or [n, *row]; ``index``: int32 [n]; ``out``: [num_out] or [num_out, *row].
+    ``prev`` (same shape as values) receives the destination rows before the call;
+    ``n_skipped`` (int64, one element) receives the number of out-of-range indices."""
+    return _scatter("det_scatter_add", values, index, out, prev, n_skipped, ws)
+
+
+def det_scatter_sub(values: torch.Tensor, index: torch.Tensor, out: torch.Tensor,
+                    prev: Optional[torch.Tensor] = None, n_skipped: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``out[index[i]] -= values[i]``: the values negated, then added in the fixed order of
+    det_scatter_add (arguments as there); returns ``out``."""
+    return _scatter("det_scatter_sub", values, index, out, prev, n_skipped, ws)
+
+
+class _Gather(torch.autograd.Function):
+    """``values[index]`` along axis 0; the gradient scatters back through det_scatter_add."""
+
+    @staticmethod
+    def forward(ctx, values, index):
+        ctx.save_for_backward(index)
+        ctx.shape = values.shape
+        return values.index_select(0, index.long())
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        (index,) = ctx.saved_tensors
+        grad = torch.zeros(ctx.shape, dtype=grad_out.dtype, device=grad_out.device)
+        det_scatter_add(grad_out.contiguous(), index, grad)
+        return grad, None
+
+
+def gather(values: torch.Tensor, index: torch.Tensor) -> torch.Tensor:
+    """Rows ``values[index[i]]`` (``index`` int32, in range).  The forward pass only moves data;
+    in the backward pass the gradient rows that share a source row are accumulated by
+    det_scatter_add, so the gradient's bits do not depend on scheduling (the gather case of the
+    Warp guide's "Tape and Backward Passes")."""
+    if index.dtype != torch.int32:
+        raise TypeError("index must be int32")
+    if index.numel() and (int(index.min()) < 0 or int(index.max()) >= values.shape[0]):
+        raise IndexError("gather index out of range")
+    return _Gather.apply(values, index)
 
 
 # ------------------------------------------------------------------ introspection

@@ -141,3 +141,81 @@ def test_rows_c4_shape(dev):
     got, _, _ = gpu_scatter(src, rows, out0, dev)
     want, _, _ = oracle.scatter_add(src, rows, out0)
     assert bits_equal(got, want), first_mismatch(got, want)
+
+
+# ---------------------------------------------------------------- scatter-subtract, gather
+
+def gpu_scatter_sub(v, idx, out0, dev, want_prev=False):
+    vt = torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+    it = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to(dev)
+    ot = torch.from_numpy(np.array(out0, copy=True)).to(dev)
+    pt = torch.full(v.shape, float("nan"), dtype=vt.dtype, device=dev) if want_prev else None
+    sk = torch.full((1,), -7, dtype=torch.int64, device=dev)
+    det.det_scatter_sub(vt, it, ot, prev=pt, n_skipped=sk)
+    return ot.cpu().numpy(), (pt.cpu().numpy() if want_prev else None), int(sk.item())
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n,B", [(7, 1), (100003, 1000), (300007, 65536), (300007, 65537),
+                                 (200000, 3), (3 * 8192 * 8 + 5, 1)])
+def test_scatter_sub_parity(dev, dtype, n, B):
+    rng = np.random.default_rng(n * 7 + B)
+    v = rounding(n, dtype, n + 1)
+    idx = rng.integers(-2, B + 2, n).astype(np.int32)
+    o = rounding(B, dtype, B + 1)
+    got, prev, k = gpu_scatter_sub(v, idx, o, dev, want_prev=True)
+    want, wprev, wk = oracle.scatter_sub(v, idx, o, want_prev=True)
+    assert bits_equal(got, want), (n, B, first_mismatch(got, want))
+    assert k == wk and bits_equal(prev, wprev)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_scatter_sub_signed_zero_and_tree(dev, dtype):
+    # -0.0 minus contributions that cancel is +0.0 (negate, then add); the tree is kept
+    v = np.array([0.0, -0.0, 1.0, -1.0], dtype)
+    got, _, _ = gpu_scatter_sub(v, np.array([0, 0, 1, 1], np.int32), np.array([-0.0, -0.0], dtype),
+                                dev)
+    want, _, _ = oracle.scatter_sub(v, np.array([0, 0, 1, 1], np.int32),
+                                    np.array([-0.0, -0.0], dtype))
+    assert bits_equal(got, want) and not np.signbit(got).any()
+    e = np.finfo(dtype).eps / 2
+    v = np.array([1.0, e, e, e], dtype)
+    got, _, _ = gpu_scatter_sub(v, np.zeros(4, np.int32), np.zeros(1, dtype), dev)
+    assert got[0] == -(1.0 + 2 * e)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n,rows,d", [(5000, 300, 96), (20000, 8, 33)])
+def test_scatter_sub_rows_parity(dev, dtype, n, rows, d):
+    rng = np.random.default_rng(n + d)
+    v = rounding((n, d), dtype, n)
+    idx = rng.integers(0, rows, n).astype(np.int32)
+    o = rounding((rows, d), dtype, rows)
+    got, _, _ = gpu_scatter_sub(v, idx, o, dev)
+    want, _, _ = oracle.scatter_sub(v, idx, o)
+    assert bits_equal(got, want), first_mismatch(got, want)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_gather_gradient_is_the_fixed_scatter(dev, dtype):
+    # the gradient of values[index] accumulates out.grad rows sharing a source row through
+    # det_scatter_add: bit-equal to the oracle, and the same over repeated backward passes
+    rng = np.random.default_rng(11)
+    src, m, d = 4096, 100003, 4
+    vals = torch.from_numpy(rounding((src, d), dtype, 1)).to(dev).requires_grad_(True)
+    idx_h = rng.integers(0, src, m).astype(np.int32)
+    idx = torch.from_numpy(idx_h).to(dev)
+    g_h = rounding((m, d), dtype, 2)
+    g = torch.from_numpy(g_h).to(dev)
+    out = det.gather(vals, idx)
+    assert torch.equal(out, vals.detach()[idx.long()])
+    grads = set()
+    for _ in range(3):
+        vals.grad = None
+        det.gather(vals, idx).backward(g)
+        grads.add(vals.grad.cpu().numpy().tobytes())
+    assert len(grads) == 1
+    want, _, _ = oracle.scatter_add(g_h, idx_h, np.zeros((src, d), dtype))
+    assert bits_equal(vals.grad.cpu().numpy(), want)
+    with pytest.raises(IndexError):
+        det.gather(vals, torch.tensor([src], dtype=torch.int32, device=dev))

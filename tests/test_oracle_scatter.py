@@ -131,3 +131,44 @@ def test_per_bin_error_bound(dtype, u):
         k = math.ceil(math.log2(m.size)) + 1
         g = k * u / (1 - k * u)
         assert abs(float(out[b]) - exact) <= g * (abs(float(o[b])) + np.abs(m).sum()) * (1 + 1e-9)
+
+
+# ---------------------------------------------------------------- scatter-subtract
+# Warp "Deterministic Execution", Pattern 1, table of atomics: atomic_sub's values are negated
+# and added in a fixed order.  Pins worked by hand, each separating that reading from the
+# plausible alternatives.
+
+def test_sub_signed_zero_is_negate_then_add():
+    # out = -0.0, contributions [+0.0, -0.0] and [1, -1]: negated they still cancel to +0.0,
+    # and -0.0 + +0.0 = +0.0.  Subtracting the reduced sum instead gives -0.0 - (+0.0) = -0.0.
+    for vals in ([0.0, -0.0], [1.0, -1.0]):
+        v = np.array(vals, np.float32)
+        got, _, _ = oracle.scatter_sub(v, np.zeros(2, np.int32), np.array([-0.0], np.float32))
+        assert got.view(np.uint32)[0] == 0x00000000, vals
+
+
+def test_sub_keeps_the_tree():
+    # [1, 2^-24, 2^-24, 2^-24] into bin 0 (out = +0.0), negated: (-1 - 2^-24) rounds to -1,
+    # (-2^-24 - 2^-24) = -2^-23, so the tree gives -(1 + 2^-23) = 0xbf800001; a left-to-right
+    # walk would give -1.0 (0xbf800000).
+    u = np.float32(2.0 ** -24)
+    v = np.array([1.0, u, u, u], np.float32)
+    got, _, _ = oracle.scatter_sub(v, np.zeros(4, np.int32), np.zeros(1, np.float32))
+    assert got.view(np.uint32)[0] == 0xBF800001
+    got64, _, _ = oracle.scatter_sub(np.array([1.0, 2.0 ** -53, 2.0 ** -53, 2.0 ** -53]),
+                                     np.zeros(4, np.int32), np.zeros(1))
+    assert got64[0] == -(1.0 + 2.0 ** -52)
+
+
+def test_sub_ones_and_integers_exact():
+    got, _, _ = oracle.scatter_sub(np.ones(4096, np.float32), np.zeros(4096, np.int32),
+                                   np.zeros(1, np.float32))
+    assert got[0] == -4096.0
+    rng = np.random.default_rng(5)
+    v = rng.integers(-1000, 1000, 20000).astype(np.float64)
+    idx = rng.integers(0, 37, 20000).astype(np.int32)
+    o = rng.integers(-10 ** 6, 10 ** 6, 37).astype(np.float64)
+    got, _, k = oracle.scatter_sub(v, idx, o)
+    want = o.copy()
+    np.subtract.at(want, idx, v)        # integers: exact in any order
+    assert k == 0 and np.array_equal(got, want)
