@@ -38,7 +38,10 @@
 extern "C" {
 #endif
 
-typedef enum { DET_F32 = 0, DET_F64 = 1 } det_dtype;
+/* DET_I32 is accepted by det_scan only (Warp "Deterministic Execution", section "Pattern 2:
+ * Slot Allocation": the count-scan-write workflow's prefix scan over int32 slot counts); its
+ * sums wrap modulo 2^32 as two's complement, which no association order can change. */
+typedef enum { DET_F32 = 0, DET_F64 = 1, DET_I32 = 2 } det_dtype;
 
 typedef enum {
     DET_SUCCESS = 0,
@@ -92,6 +95,8 @@ size_t det_scan_workspace_size(int64_t n, det_dtype dtype, unsigned flags, int64
  *   anchors publish totals and carries, so the bits do not depend on which predecessors a tile
  *   saw as finished.
  *
+ * dtype DET_I32: int32 elements, sums wrapping modulo 2^32 (the same dataflow; every order
+ *         gives the same integers), the exclusive scan's first value 0.
  * x, y:   device, n elements of dtype.  Inclusive scans may run in place (y == x); exclusive
  *         scans must not overlap x and y (DET_ERROR_INVALID_VALUE if the ranges overlap).
  * flags:  DET_SCAN_EXCLUSIVE (y[0] = +0.0, y[i] = inclusive[i-1]) and/or DET_SCAN_REVERSE

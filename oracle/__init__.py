@@ -17,6 +17,9 @@ Every function here follows the association order stated in ``detref.c``:
 * ``scatter_sub``   -- the values negated one by one, then ``scatter_add`` (Warp "Deterministic
                        Execution", Pattern 1: atomic_sub's values are negated and added in a
                        fixed order).
+* ``scan_int32``    -- int32 prefix sums modulo 2^32 (Warp "Deterministic Execution", Pattern 2:
+                       the count-scan-write prefix scan); integers need no order, so this is
+                       the plain definition, written in numpy.
 * ``scan``          -- tiles of V*W*NW elements, anchors every A tiles and every A*A2 tiles
                        (drjit-core pull request "Make CUDA floating-point prefix sums
                        deterministic").
@@ -158,6 +161,30 @@ def scatter_sub(values: np.ndarray, index: np.ndarray, out: np.ndarray,
     Not ``out - pw(M)``: when a destination's contributions cancel, the two differ in the
     sign of the zero."""
     return scatter_add(np.negative(np.ascontiguousarray(values)), index, out, want_prev)
+
+
+def scan_int32(x: np.ndarray, exclusive: bool = False, reverse: bool = False,
+               offsets: Optional[np.ndarray] = None) -> np.ndarray:
+    """Inclusive/exclusive, forward/reverse, optionally segmented prefix sums of int32 values,
+    wrapping modulo 2^32 as two's complement.  Segments restart the sum; an exclusive scan
+    starts each segment at 0.  Reverse mirrors the values and the segments together."""
+    x = np.ascontiguousarray(x, dtype=np.int32).reshape(-1)
+    n = x.size
+    offs = (np.array([0, n], np.int64) if offsets is None
+            else np.ascontiguousarray(offsets, dtype=np.int64).reshape(-1))
+    if reverse:
+        x = x[::-1]
+        offs = (n - offs[::-1]).astype(np.int64)
+    y = np.empty(n, np.int64)
+    for a, b in zip(offs[:-1], offs[1:]):
+        if b <= a:
+            continue
+        run = np.cumsum(x[a:b].astype(np.int64))
+        if exclusive:
+            run = np.concatenate([[0], run[:-1]])
+        y[a:b] = run
+    out = (y & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+    return np.ascontiguousarray(out[::-1]) if reverse else out
 
 
 def scan(x: np.ndarray, exclusive: bool = False, reverse: bool = False,

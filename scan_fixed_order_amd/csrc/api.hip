@@ -100,6 +100,8 @@ KernelTimer::~KernelTimer() {
 }
 
 static bool valid_dtype(det_dtype d) { return d == DET_F32 || d == DET_F64; }
+// det_scan also takes int32 (wrapping sums: the order cannot change them)
+static bool valid_scan_dtype(det_dtype d) { return valid_dtype(d) || d == DET_I32; }
 
 static bool ranges_overlap(const void* a, const void* b, size_t bytes) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a);
@@ -138,7 +140,7 @@ det_status det_sum(const void* x, int64_t n, det_dtype dtype, void* out, void* w
 }
 
 size_t det_scan_workspace_size(int64_t n, det_dtype dtype, unsigned flags, int64_t num_segments) {
-    if (n < 0 || n > DET_MAX_N || !valid_dtype(dtype) || num_segments < 0) return 0;
+    if (n < 0 || n > DET_MAX_N || !valid_scan_dtype(dtype) || num_segments < 0) return 0;
     if (flags & ~(DET_SCAN_EXCLUSIVE | DET_SCAN_REVERSE)) return 0;
     return scan_workspace(n, dtype, flags, num_segments);
 }
@@ -146,7 +148,7 @@ size_t det_scan_workspace_size(int64_t n, det_dtype dtype, unsigned flags, int64
 det_status det_scan(const void* x, void* y, int64_t n, det_dtype dtype, unsigned flags,
                     const int64_t* seg_offsets, int64_t num_segments, void* ws, size_t ws_bytes,
                     void* stream) {
-    if (!valid_dtype(dtype)) return DET_ERROR_UNSUPPORTED;
+    if (!valid_scan_dtype(dtype)) return DET_ERROR_UNSUPPORTED;
     if (n < 0 || num_segments < 0) return DET_ERROR_INVALID_VALUE;
     if (n > DET_MAX_N || num_segments > DET_MAX_N) return DET_ERROR_TOO_LARGE;
     if (flags & ~(DET_SCAN_EXCLUSIVE | DET_SCAN_REVERSE)) return DET_ERROR_INVALID_VALUE;

@@ -19,7 +19,7 @@ struct LaunchOverride {
 const LaunchOverride& launch_override();
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-inline size_t dtype_size(det_dtype d) { return d == DET_F64 ? 8 : 4; }
+inline size_t dtype_size(det_dtype d) { return d == DET_F64 ? 8 : 4; }   // f32, i32: 4
 
 // ---- sum
 size_t sum_workspace(int64_t n, det_dtype dt);

@@ -29,6 +29,8 @@
 // head flags of a tile come from a workgroup-parallel search of the offsets.  Reverse scans
 // read and write through mirrored indices (n - 1 - f); exclusive scans store each inclusive
 // value one position later (and +0.0 at position 0 and at segment heads).
+#include <type_traits>
+
 #include "det_device.h"
 #include "det_internal.h"
 
@@ -73,11 +75,23 @@ constexpr int slot_words() {
     return sizeof(T) == 4 ? 1 : 2;
 }
 
+// 32-bit payload bits of a 4-byte element (f32, or the int32 scan's uint32_t)
+template <typename T>
+__device__ __forceinline__ uint32_t to_bits32(T v) {
+    if constexpr (__is_same(T, float)) return __float_as_uint(v);
+    else return (uint32_t)v;
+}
+template <typename T>
+__device__ __forceinline__ T from_bits32(uint32_t u) {
+    if constexpr (__is_same(T, float)) return __uint_as_float(u);
+    else return (T)u;
+}
+
 template <typename T>
 __device__ __forceinline__ void publish(uint64_t* slot, const Seg<T>& s) {
     const uint64_t tag = (uint64_t)(kReady | (s.f ? kHeadTag : 0u)) << 32;
     if constexpr (sizeof(T) == 4) {
-        __hip_atomic_store(slot, tag | __float_as_uint(s.v), __ATOMIC_RELAXED,
+        __hip_atomic_store(slot, tag | to_bits32<T>(s.v), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     } else {
         const uint64_t b = (uint64_t)__double_as_longlong(s.v);
@@ -108,7 +122,7 @@ __device__ __forceinline__ uint64_t wait_word(uint64_t* w, uint32_t* err) {
 template <typename T>
 __device__ __forceinline__ Seg<T> unpack(uint64_t w0, uint64_t w1) {
     if constexpr (sizeof(T) == 4) {
-        return Seg<T>{__uint_as_float((uint32_t)w0), (uint32_t)(w0 >> 33) & 1u};
+        return Seg<T>{from_bits32<T>((uint32_t)w0), (uint32_t)(w0 >> 33) & 1u};
     } else {
         const uint64_t b = (w1 << 32) | (w0 & 0xffffffffull);
         return Seg<T>{__longlong_as_double((long long)b), (uint32_t)(w0 >> 33) & 1u};
@@ -119,7 +133,7 @@ template <typename T>
 __device__ __forceinline__ Seg<T> wait_slot(uint64_t* slot, uint32_t* err) {
     if constexpr (sizeof(T) == 4) {
         const uint64_t w = wait_word(slot, err);
-        return Seg<T>{__uint_as_float((uint32_t)w), (uint32_t)(w >> 33) & 1u};
+        return Seg<T>{from_bits32<T>((uint32_t)w), (uint32_t)(w >> 33) & 1u};
     } else {
         const uint64_t w0 = wait_word(slot, err);
         const uint64_t w1 = wait_word(slot + 1, err);
@@ -295,6 +309,10 @@ __device__ void build_heads(const int64_t* __restrict__ offs, int64_t nseg, int6
 // Vector types for 16-byte accesses with non-temporal hints (streaming data is touched once).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// the 16-byte vector of a 4-byte element type
+template <typename T>
+using v4_t = typename std::conditional<__is_same(T, float), f32x4, u32x4>::type;
 
 template <typename T>
 __device__ __forceinline__ bool aligned16(const T* p) {
@@ -317,7 +335,7 @@ __device__ __forceinline__ void load_run(const T* __restrict__ x, int64_t n, int
     if constexpr (sizeof(T) == 4) {
 #pragma unroll
         for (int i = 0; i < kV / 4; ++i) {
-            const f32x4 q = reinterpret_cast<const f32x4*>(p)[i];
+            const v4_t<T> q = reinterpret_cast<const v4_t<T>*>(p)[i];
             if (REV) {
                 r[kV - 1 - 4 * i] = q.x; r[kV - 2 - 4 * i] = q.y;
                 r[kV - 3 - 4 * i] = q.z; r[kV - 4 - 4 * i] = q.w;
@@ -360,8 +378,8 @@ constexpr int kGW = 16 / (int)sizeof(T);
 template <typename T>
 __device__ __forceinline__ void nt_store16(T* p, const T (&v)[kGW<T>]) {
     if constexpr (sizeof(T) == 4) {
-        f32x4 q = {v[0], v[1], v[2], v[3]};
-        __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(p));
+        v4_t<T> q = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(q, reinterpret_cast<v4_t<T>*>(p));
     } else {
         f64x2 q = {v[0], v[1]};
         __builtin_nontemporal_store(q, reinterpret_cast<f64x2*>(p));
@@ -847,7 +865,7 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     const LaunchOverride& ov = launch_override();
     const int A = ov.scan_A ? ov.scan_A : kScanA;
     const int A2 = ov.scan_A2 ? ov.scan_A2 : kScanA2;
-    const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32, A, A2);
+    const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32, A, A2);   // slot sizes
     const int64_t words = (int64_t)(L.used / 8);
     int zg = (int)((words + 255) / 256);
     if (zg > 1024) zg = 1024;
@@ -894,7 +912,8 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     if (ov.grid_wgs > 0 && grid > ov.grid_wgs) grid = ov.grid_wgs;
     a.nctr = (int)(grid < kCounters ? grid : kCounters);
     void* args[] = {&a};
-    KernelTimer kt(sizeof(T) == 4 ? "k_scan<f32>" : "k_scan<f64>", s);
+    KernelTimer kt(sizeof(T) == 8 ? "k_scan<f64>" : __is_same(T, float) ? "k_scan<f32>"
+                                                                        : "k_scan<i32>", s);
     if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, s) != hipSuccess)
         return DET_ERROR_LAUNCH;
     return launch_status();
@@ -922,6 +941,9 @@ det_status scan_launch(const void* x, void* y, int64_t n, det_dtype dt, unsigned
     if (dt == DET_F32)
         return scan_impl<float>(static_cast<const float*>(x), static_cast<float*>(y), n, flags,
                                 offs, nseg, static_cast<char*>(ws), s);
+    if (dt == DET_I32)   // two's-complement wrapping sums: computed on the unsigned bits
+        return scan_impl<uint32_t>(static_cast<const uint32_t*>(x), static_cast<uint32_t*>(y), n,
+                                   flags, offs, nseg, static_cast<char*>(ws), s);
     return scan_impl<double>(static_cast<const double*>(x), static_cast<double*>(y), n, flags,
                              offs, nseg, static_cast<char*>(ws), s);
 }

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libdet.so")
 
 DET_F32 = 0
 DET_F64 = 1
+DET_I32 = 2      # det_scan only
 DET_SCAN_EXCLUSIVE = 1
 DET_SCAN_REVERSE = 2
 
@@ -74,12 +75,15 @@ def lib() -> ctypes.CDLL:
     return L
 
 
-def _dtype_code(t: torch.Tensor) -> int:
+def _dtype_code(t: torch.Tensor, allow_int: bool = False) -> int:
     if t.dtype == torch.float32:
         return DET_F32
     if t.dtype == torch.float64:
         return DET_F64
-    raise TypeError(f"det supports float32 and float64, got {t.dtype}")
+    if allow_int and t.dtype == torch.int32:
+        return DET_I32
+    raise TypeError(f"det supports float32 and float64{' and int32' if allow_int else ''}, "
+                    f"got {t.dtype}")
 
 
 def _dev_ptr(t: Optional[torch.Tensor]):
@@ -143,9 +147,10 @@ def det_scan(x: torch.Tensor, y: Optional[torch.Tensor] = None, exclusive: bool 
              reverse: bool = False, offsets: Optional[torch.Tensor] = None,
              ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Reproducible prefix sum of ``x`` (1-D).  ``offsets``: int64 device tensor [S+1]
-    (0 = o_0 <= ... <= o_S = n) for a segmented scan."""
+    (0 = o_0 <= ... <= o_S = n) for a segmented scan.  int32 ``x`` gives wrapping integer
+    sums (the slot-allocation scan of count-scan-write)."""
     x = _flat(x)
-    dt = _dtype_code(x)
+    dt = _dtype_code(x, allow_int=True)
     n = x.numel()
     if y is None:
         y = torch.empty_like(x)

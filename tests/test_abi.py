@@ -82,6 +82,11 @@ def test_validation_errors_enqueue_nothing():
     assert lib.det_scan(FAKE, ctypes.c_void_p(0x900000), 1 << 20, 0, 0, NULL, 0, ws, 8,
                         NULL) == E_WORKSPACE
     assert lib.det_scan(FAKE, FAKE, 10, 3, 0, NULL, 0, ws, 1 << 20, NULL) == E_UNSUPPORTED
+    # int32 is a scan type only
+    assert lib.det_scan_workspace_size(1 << 20, 2, 1, 0) > 0
+    assert lib.det_sum(FAKE, 10, 2, FAKE, ws, 1 << 20, NULL) == E_UNSUPPORTED
+    assert lib.det_sum_workspace_size(10, 2) == 0
+    assert lib.det_scatter_add_workspace_size(10, 10, 1, 2) == 0
     assert lib.det_scan_error(NULL, FAKE, NULL) == E_INVALID
     assert lib.det_scan_error(FAKE, NULL, NULL) == E_INVALID
     # scatter

@@ -205,3 +205,40 @@ def test_scan_health_word_stays_clear(dev, dtype):
         for seg in (None, o):
             det.det_scan(t, exclusive=excl, reverse=rev, offsets=seg, ws=ws)
             assert int(det.det_scan_error(ws).item()) == 0, (excl, rev, seg is not None)
+
+
+# ---------------------------------------------------------------- int32 (slot allocation)
+
+@pytest.mark.parametrize("n", [1, 7, 8192, 8193, 164738, 1048577, 2 * 256 * 8192 + 5])
+def test_int32_scan_parity(dev, n):
+    rng = np.random.default_rng(n)
+    x = rng.integers(-2 ** 31, 2 ** 31, n).astype(np.int32)     # sums wrap
+    offs = random_offsets(n, max(1, n // 50), seed=n)
+    t = torch.from_numpy(x).to(dev)
+    o = torch.from_numpy(offs).to(dev)
+    for excl, rev in MODES:
+        got = det.det_scan(t, exclusive=excl, reverse=rev).cpu().numpy()
+        assert np.array_equal(got, oracle.scan_int32(x, excl, rev)), (excl, rev)
+        got = det.det_scan(t, exclusive=excl, reverse=rev, offsets=o).cpu().numpy()
+        assert np.array_equal(got, oracle.scan_int32(x, excl, rev, offs)), (excl, rev, "seg")
+
+
+def test_count_scan_write_compaction(dev):
+    # Warp "Deterministic Execution", Pattern 2: slot = atomic_add(count, 0, 1) for every
+    # positive value becomes count (1 or 0 per thread), exclusive scan (the slot), write.  The
+    # compacted array keeps thread order, the same on every run.
+    rng = np.random.default_rng(3)
+    n = 1_000_003
+    v = rng.standard_normal(n).astype(np.float32)
+    vt = torch.from_numpy(v).to(dev)
+    outs = set()
+    for _ in range(3):
+        want = (vt > 0).to(torch.int32)
+        slot = det.det_scan(want, exclusive=True)
+        total = int(slot[-1].item() + want[-1].item())
+        comp = torch.empty(total, dtype=torch.float32, device=dev)
+        keep = want.bool()
+        comp[slot[keep].long()] = vt[keep]
+        outs.add(comp.cpu().numpy().tobytes())
+    assert len(outs) == 1
+    assert np.array_equal(np.frombuffer(outs.pop(), np.float32), v[v > 0])

@@ -362,3 +362,55 @@ def test_error_bound_against_exact_prefix(dtype, u):
         acc += Fraction(float(x[i]))
         absacc += abs(float(x[i]))
         assert abs(Fraction(float(y[i])) - acc) <= Fraction(g * absacc * (1 + 1e-9)), i
+
+
+# ---------------------------------------------------------------- int32 scan (slot allocation)
+# Warp "Deterministic Execution", Pattern 2: count-scan-write's prefix scan over int32 counts.
+# Integer sums wrap modulo 2^32 and need no order; pinned by hand-worked values, a Python-int
+# loop, and the float oracle on integer data (whose sums are exact).
+
+def test_int32_scan_wraps_by_hand():
+    x = np.array([2 ** 31 - 1, 1, 5, -7], np.int32)
+    assert oracle.scan_int32(x).tolist() == [2147483647, -2147483648, -2147483643, -2147483650 + 2 ** 32]
+    assert oracle.scan_int32(x, exclusive=True).tolist() == [0, 2147483647, -2147483648, -2147483643]
+    assert oracle.scan_int32(x, reverse=True).tolist() == [2147483646, -1, -2, -7]
+    assert oracle.scan_int32(np.zeros(0, np.int32)).size == 0
+
+
+def _loop_scan(x, exclusive, reverse, offs):
+    # Python ints, one segment at a time, walked from its first element (its last for reverse)
+    xs = [int(v) for v in x]
+    y = [0] * len(xs)
+    for a, b in zip(offs[:-1], offs[1:]):
+        acc = 0
+        for i in (range(int(b) - 1, int(a) - 1, -1) if reverse else range(int(a), int(b))):
+            y[i] = acc if exclusive else acc + xs[i]
+            acc += xs[i]
+    return np.array([(v + 2 ** 31) % 2 ** 32 - 2 ** 31 for v in y], np.int64).astype(np.int32)
+
+
+def test_int32_scan_against_python_ints():
+    rng = np.random.default_rng(8)
+    for n in (1, 2, 7, 64, 300):
+        x = rng.integers(-2 ** 31, 2 ** 31, n).astype(np.int32)
+        cuts = np.sort(rng.choice(np.arange(1, n + 1), min(n, 5), replace=False)) if n > 1 else []
+        offs = np.unique(np.concatenate([[0], cuts, [n]])).astype(np.int64)
+        for excl in (False, True):
+            for rev in (False, True):
+                for o in (None, offs):
+                    oo = np.array([0, n], np.int64) if o is None else o
+                    want = _loop_scan(x, excl, rev, oo)
+                    got = oracle.scan_int32(x, exclusive=excl, reverse=rev, offsets=o)
+                    assert np.array_equal(got, want), (n, excl, rev, o is not None)
+
+
+def test_int32_scan_equals_float_oracle_on_integers():
+    rng = np.random.default_rng(9)
+    n = 3 * 8192 + 77
+    x = rng.integers(-1000, 1000, n).astype(np.int32)
+    offs = np.unique(np.concatenate([[0], rng.integers(1, n, 40), [n]])).astype(np.int64)
+    for excl in (False, True):
+        for rev in (False, True):
+            f = oracle.scan(x.astype(np.float64), exclusive=excl, reverse=rev, offsets=offs)
+            i = oracle.scan_int32(x, exclusive=excl, reverse=rev, offsets=offs)
+            assert np.array_equal(f.astype(np.int64), i.astype(np.int64)), (excl, rev)
