@@ -106,7 +106,7 @@ def measured_traffic(kernel):
     return None
 
 
-def time_configs(det, workloads, dev, log):
+def time_configs(det, workloads, dev, log, base_lib=None):
     """Times every configuration of the workload spec besides the headline step (one GPU,
     inputs resident): median over repetitions of one call, bracketed by events on the current
     stream.  Returns {case: {ms, GB_s, frac_hbm, Gelem_s}} with algorithmic bytes as in the
@@ -152,6 +152,15 @@ def time_configs(det, workloads, dev, log):
     w = ws_of(det.det_sum_workspace_size(1 << 20, 0))
     o = torch.empty((), dtype=torch.float32, device=dev)
     put("sum f32 n=2^20 U[0,1)", lambda: det.det_sum(x, out=o, ws=w), 4 << 20, 1 << 20, 50)
+    if base_lib is not None:
+        import ctypes as _ct0
+        sp0 = _ct0.c_void_p(stream.cuda_stream)
+        tmp = torch.empty((), dtype=torch.float32, device=dev)
+        bms = med(lambda: base_lib.detbase_atomic_sum(_ct0.c_void_p(x.data_ptr()),
+                                                      _ct0.c_int64(1 << 20), 0,
+                                                      _ct0.c_void_p(tmp.data_ptr()), sp0), 50)
+        res["sum f32 n=2^20 U[0,1)"]["nondet_baseline_ms"] = round(bms, 4)
+        res["sum f32 n=2^20 U[0,1)"]["det_overhead"] = round(res["sum f32 n=2^20 U[0,1)"]["ms"] / bms - 1.0, 4)
     ones = torch.ones(4096, dtype=torch.float32, device=dev)
     put("sum f32 n=4096 ones", lambda: det.det_sum(ones, out=o, ws=w), 4 * 4096, 4096, 50)
     # scatter, n = 2^24: uniform over 65,536 bins, and every value into bin 0
@@ -165,19 +174,58 @@ def time_configs(det, workloads, dev, log):
         put(f"scatter f32 n=2^24 into {label}",
             lambda: det.det_scatter_add(v, bi, out, ws=w), 8.0 * n + 8.0 * B, n, 20)
     del v
-    # scan: f32 and f64, inclusive/exclusive x forward/reverse
+    # scan: f32 and f64, inclusive/exclusive x forward/reverse; the inclusive forward scan
+    # beside the ROCm library's (hipCUB DeviceScan::InclusiveSum) on the same input, for the
+    # deterministic-mode overhead at the sizes the drjit page measures
+    import ctypes as _ct
     modes = ((False, False, "incl"), (True, False, "excl"), (False, True, "incl rev"),
              (True, True, "excl rev"))
+    sp = _ct.c_void_p(stream.cuda_stream)
     for dt, tdt, code in ((np.float32, torch.float32, 0), (np.float64, torch.float64, 1)):
         for n in (16384, 164738, 1048577, 1 << 28):
             xs = dev_t(workloads.scan_values(n, dt, seed=2))
             ys = torch.empty_like(xs)
             w = ws_of(det.det_scan_workspace_size(n, code, 3, 0))
+            reps = 20 if n < (1 << 28) else 10
+            name0 = None
             for ex, rv, tag in modes:
-                put(f"scan {np.dtype(dt).name} n={n if n < (1 << 28) else '2^28'} {tag}",
-                    lambda: det.det_scan(xs, y=ys, exclusive=ex, reverse=rv, ws=w),
-                    2.0 * n * xs.element_size(), n, 20 if n < (1 << 28) else 10)
+                name = f"scan {np.dtype(dt).name} n={n if n < (1 << 28) else '2^28'} {tag}"
+                name0 = name0 or name
+                put(name, lambda: det.det_scan(xs, y=ys, exclusive=ex, reverse=rv, ws=w),
+                    2.0 * n * xs.element_size(), n, reps)
+            if base_lib is not None:
+                f64 = code == 1
+                wsz = (base_lib.detbase_lib_scan64_workspace_size if f64
+                       else base_lib.detbase_lib_scan_workspace_size)(_ct.c_int64(n))
+                wb = ws_of(wsz)
+                fn = base_lib.detbase_lib_scan64 if f64 else base_lib.detbase_lib_scan
+                args = (_ct.c_void_p(xs.data_ptr()), _ct.c_void_p(ys.data_ptr()), _ct.c_int64(n),
+                        _ct.c_void_p(wb.data_ptr()), _ct.c_size_t(wsz), sp)
+                bms = med(lambda: fn(*args), reps)
+                res[name0]["nondet_baseline_ms"] = round(bms, 4)
+                res[name0]["det_overhead"] = round(res[name0]["ms"] / bms - 1.0, 4)
             del xs, ys
+    # the small latency-bound calls replayed from a captured HIP graph (launch gaps removed)
+    xg = dev_t(workloads.uniform01(1 << 20, seed=0))
+    wg = ws_of(det.det_sum_workspace_size(1 << 20, 0))
+    og = torch.empty((), dtype=torch.float32, device=dev)
+    xs = dev_t(workloads.scan_values(16384, np.float32, seed=2))
+    ys = torch.empty_like(xs)
+    wsg = ws_of(det.det_scan_workspace_size(16384, 0, 0, 0))
+    for name, fn, nb, ne in (("sum f32 n=2^20 U[0,1), graph replay",
+                              lambda: det.det_sum(xg, out=og, ws=wg), 4 << 20, 1 << 20),
+                             ("scan float32 n=16384 incl, graph replay",
+                              lambda: det.det_scan(xs, y=ys, ws=wsg), 8 * 16384, 16384)):
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.graph(graph, stream=side):
+            fn()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        put(name, graph.replay, nb, ne, 50)
     log("configs: sum, scatter, scan timed")
     # segmented scan f32 2^26 (geometric segments, mean 100) and the row accumulate
     n = 1 << 26
@@ -431,7 +479,12 @@ def main():
     # ---------------------------------------------------------------- the other configurations
     configs = None
     if not args.no_configs:
-        configs = time_configs(det, workloads, dev, log)
+        blib = None
+        if not args.no_baselines:
+            blib = ctypes.CDLL(os.path.join(ROOT, "scan_fixed_order_amd", "libdet_baselines.so"))
+            for nm in ("detbase_lib_scan_workspace_size", "detbase_lib_scan64_workspace_size"):
+                getattr(blib, nm).restype = ctypes.c_size_t
+        configs = time_configs(det, workloads, dev, log, blib)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None

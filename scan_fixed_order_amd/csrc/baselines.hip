@@ -135,4 +135,23 @@ int detbase_lib_scan(const float* x, float* y, int64_t n, void* ws, size_t ws_by
                : 5;
 }
 
+// Workspace and f64 inclusive forward scan by the library (n < 2^31)
+size_t detbase_lib_scan64_workspace_size(int64_t n) {
+    size_t bytes = 0;
+    if (hipcub::DeviceScan::InclusiveSum(nullptr, bytes, static_cast<const double*>(nullptr),
+                                         static_cast<double*>(nullptr), (int)n) != hipSuccess)
+        return 0;
+    return bytes;
+}
+
+int detbase_lib_scan64(const double* x, double* y, int64_t n, void* ws, size_t ws_bytes,
+                       void* stream) {
+    if (n <= 0) return 0;
+    size_t bytes = ws_bytes;
+    return hipcub::DeviceScan::InclusiveSum(ws, bytes, x, y, (int)n,
+                                            static_cast<hipStream_t>(stream)) == hipSuccess
+               ? 0
+               : 5;
+}
+
 }  // extern "C"
