@@ -816,6 +816,65 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     }
 }
 
+// Scans of at most kSmallTiles tiles, all in the first anchor interval: one workgroup walks the
+// tiles in order, keeping the tile totals in LDS, so there are no status words to clear, no
+// counters and no polls (one launch).  Tile j's trees are those of k_scan: W_j = PW(leaf t =
+// Agg_t for t < j, else the identity) and WG = PW(identity leaves); the carry is the identity;
+// E = (CC + WG) + W_j.  The next tile's loads are issued before the current tile's readout.
+constexpr int kSmallTiles = 3;   // beyond 3 tiles the persistent kernel is faster on MI355X
+
+template <typename T, bool SEG, bool REV, bool EXCL>
+__global__ __launch_bounds__(256) void k_scan_small(ScanArgs<T> a) {
+    __shared__ T s_park[kScanWaves][kPark];
+    __shared__ T s_x[kScanWaves][kScanW];
+    __shared__ uint32_t s_hbits[SEG ? kScanWaves : 1][kScanW];
+    __shared__ uint32_t s_heads[2][SEG ? kHeadWords : 1];
+    __shared__ Seg<T> s_tmp[2 * kScanWaves];
+    __shared__ Seg<T> s_wtot[kScanWaves];
+    __shared__ Seg<T> s_agg[kSmallTiles];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    T* pk = s_park[wave];
+    T* xs = s_x[wave];
+    const uint32_t* hbs = s_hbits[SEG ? wave : 0];
+    T r[kV], rn[kV];
+    load_tile<T, REV>(a, 0, wave, r, lane);
+    for (int j = 0; j < a.ntiles; ++j) {
+        uint32_t hb;
+        Seg<T> P, p;
+        const Seg<T> agg =
+            tile_local<T, SEG, REV>(a, j, r, hb, P, p, s_heads[j & 1], s_wtot, tid, lane, wave);
+        if (tid == 0) s_agg[j] = agg;
+        park_runs<T>(pk, r, lane);
+        if constexpr (SEG) s_hbits[wave][lane] = hb;
+        __syncthreads();
+        // the next tile's loads (past the end: element n - 1, never used)
+        load_tile<T, REV>(a, j + 1, wave, rn, lane);
+        // W_j; for tile 0 every leaf is the identity, whose tree is the identity; WG is a tree
+        // of identity leaves here, the identity
+        Seg<T> Wj = seg_ident<T>();
+        if (j > 0) Wj = block_pw<SEG, T>(tid < j ? s_agg[tid] : seg_ident<T>(), lane, wave, s_tmp);
+        const Seg<T> E = op<SEG>(op<SEG>(seg_ident<T>(), seg_ident<T>()), Wj);
+        xs[lane] = op<SEG>(op<SEG>(E, P), p).v;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int64_t F0 = (int64_t)j * kT;
+        const int64_t fw = F0 + (int64_t)wave * kWaveElems;
+        if (!EXCL)
+            readout_incl<T, SEG, REV>(a.y, a.n, fw, pk, xs, hbs, lane);
+        else
+            readout_excl<T, SEG, REV>(a.y, a.n, F0, fw, pk, xs, hbs, s_heads[j & 1], lane);
+        if (EXCL && j == 0 && tid == 0) a.y[REV ? a.n - 1 : 0] = T(0.0);
+        // every wave is done with this tile's LDS before the next tile overwrites it
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kV; ++k) r[k] = rn[k];
+    }
+}
+
 __global__ void k_copy_error(const uint32_t* err, int32_t* out) {
     out[0] = (int32_t)(err[0] != 0u);
 }
@@ -866,6 +925,39 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     const int A = ov.scan_A ? ov.scan_A : kScanA;
     const int A2 = ov.scan_A2 ? ov.scan_A2 : kScanA2;
     const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32, A, A2);   // slot sizes
+    const int mode0 = (offs ? 4 : 0) | ((flags & DET_SCAN_REVERSE) ? 2 : 0) |
+                      ((flags & DET_SCAN_EXCLUSIVE) ? 1 : 0);
+    if (L.ntiles <= kSmallTiles && L.ntiles <= A) {
+        ScanArgs<T> a{};
+        a.x = x;
+        a.y = y;
+        a.n = n;
+        a.offs = offs;
+        a.nseg = nseg;
+        a.dummy = reinterpret_cast<const T*>(ws + kDummyOff);
+        a.err = reinterpret_cast<uint32_t*>(ws + kErrOff);
+        a.ntiles = (int)L.ntiles;
+        a.rev = (mode0 & 2) ? 1 : 0;
+        a.excl = mode0 & 1;
+        a.A = A;
+        a.A2 = A2;
+        const void* fn = nullptr;
+        switch (mode0) {
+            case 0: fn = (const void*)k_scan_small<T, false, false, false>; break;
+            case 1: fn = (const void*)k_scan_small<T, false, false, true>; break;
+            case 2: fn = (const void*)k_scan_small<T, false, true, false>; break;
+            case 3: fn = (const void*)k_scan_small<T, false, true, true>; break;
+            case 4: fn = (const void*)k_scan_small<T, true, false, false>; break;
+            case 5: fn = (const void*)k_scan_small<T, true, false, true>; break;
+            case 6: fn = (const void*)k_scan_small<T, true, true, false>; break;
+            default: fn = (const void*)k_scan_small<T, true, true, true>; break;
+        }
+        void* args[] = {&a};
+        KernelTimer kt("k_scan_small", s);
+        if (hipLaunchKernel(fn, dim3(1), dim3(256), args, 0, s) != hipSuccess)
+            return DET_ERROR_LAUNCH;
+        return launch_status();
+    }
     const int64_t words = (int64_t)(L.used / 8);
     int zg = (int)((words + 255) / 256);
     if (zg > 1024) zg = 1024;
