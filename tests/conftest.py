@@ -53,3 +53,23 @@ def first_mismatch(got, want):
         return "no mismatch"
     i = int(idx[0])
     return f"{idx.size} mismatches, first at {i}: got {got[i]!r} want {want[i]!r}"
+
+
+def pw_ones(m, dtype):
+    """The adjacent-pair tree's sum of m ones in dtype, in O(log m): by the split lemma
+    PW(v) = PW(v[:2^k]) + PW(v[2^k:]) for 2^k < m <= 2^(k+1), and a full block of 2^k ones sums
+    to 2^k exactly, so PW(ones(m)) = 2^k + PW(ones(m - 2^k)), folded right to left."""
+    if m == 0:
+        return dtype(-0.0)
+    parts = []
+    while True:
+        k = 1 << (m.bit_length() - 1)
+        if k == m:
+            parts.append(dtype(m))
+            break
+        parts.append(dtype(k))
+        m -= k
+    acc = parts[-1]
+    for p in reversed(parts[:-1]):
+        acc = dtype(p + acc)
+    return acc

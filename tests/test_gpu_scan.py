@@ -242,3 +242,47 @@ def test_count_scan_write_compaction(dev):
         outs.add(comp.cpu().numpy().tobytes())
     assert len(outs) == 1
     assert np.array_equal(np.frombuffer(outs.pop(), np.float32), v[v > 0])
+
+
+# ---------------------------------------------------------------- special values
+
+def special_values(n, dtype, seed):
+    # mixed-magnitude values with infinities, NaNs, signed zeros, subnormals and values that
+    # overflow when summed, spread across tiles, waves and lanes
+    fi = np.finfo(dtype)
+    rng = np.random.default_rng(seed)
+    x = workloads.scan_values(n, dtype, seed=seed)
+    pool = np.array([np.inf, -np.inf, np.nan, 0.0, -0.0, fi.tiny / 4, -fi.tiny / 8,
+                     fi.max / 3, -fi.max / 3, fi.eps, 1.0], dtype)
+    pos = rng.choice(n, size=max(1, n // 50), replace=False)
+    x[pos] = pool[rng.integers(0, pool.size, pos.size)]
+    return x
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n", [33, 8193, 3 * 8192 + 17, 300007])
+def test_scan_special_values(dev, dtype, n):
+    x = special_values(n, dtype, seed=n)
+    offs = random_offsets(n, 700, seed=n + 1)
+    t = torch.from_numpy(x).to(dev)
+    o = torch.from_numpy(offs).to(dev)
+    for excl, rev in MODES:
+        got = det.det_scan(t, exclusive=excl, reverse=rev).cpu().numpy()
+        want = oracle.scan(x, exclusive=excl, reverse=rev)
+        assert bits_equal(got, want), (excl, rev, first_mismatch(got, want))
+        got = det.det_scan(t, exclusive=excl, reverse=rev, offsets=o).cpu().numpy()
+        want = oracle.scan(x, exclusive=excl, reverse=rev, offsets=offs)
+        assert bits_equal(got, want), (excl, rev, "seg", first_mismatch(got, want))
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_scan_all_negative_zero(dev, dtype):
+    # -0.0 + -0.0 = -0.0 all along; the exclusive scan starts at +0.0
+    n = 3 * 8192 + 5
+    x = np.full(n, -0.0, dtype)
+    t = torch.from_numpy(x).to(dev)
+    for excl, rev in MODES:
+        got = det.det_scan(t, exclusive=excl, reverse=rev).cpu().numpy()
+        assert bits_equal(got, oracle.scan(x, exclusive=excl, reverse=rev))
+        first = got[-1] if rev else got[0]
+        assert np.signbit(first) == (not excl)

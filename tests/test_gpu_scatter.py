@@ -219,3 +219,26 @@ def test_gather_gradient_is_the_fixed_scatter(dev, dtype):
     assert bits_equal(vals.grad.cpu().numpy(), want)
     with pytest.raises(IndexError):
         det.gather(vals, torch.tensor([src], dtype=torch.int32, device=dev))
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n,B", [(1000, 7), (300007, 1000), (70000, 1)])
+def test_scatter_special_values(dev, dtype, n, B):
+    # infinities, NaNs, signed zeros, subnormals and overflowing sums inside destinations, in
+    # the old values too; add and subtract
+    fi = np.finfo(dtype)
+    rng = np.random.default_rng(n + B)
+    v = rounding(n, dtype, n)
+    pool = np.array([np.inf, -np.inf, np.nan, 0.0, -0.0, fi.tiny / 4, fi.max / 3, -fi.max / 3],
+                    dtype)
+    pos = rng.choice(n, size=max(1, n // 40), replace=False)
+    v[pos] = pool[rng.integers(0, pool.size, pos.size)]
+    idx = rng.integers(0, B, n).astype(np.int32)
+    o = rounding(B, dtype, B)
+    o[: min(B, 3)] = np.array([-0.0, np.inf, fi.tiny / 2], dtype)[: min(B, 3)]
+    got, _, _ = gpu_scatter(v, idx, o, dev)
+    want, _, _ = oracle.scatter_add(v, idx, o)
+    assert bits_equal(got, want), first_mismatch(got, want)
+    got, _, _ = gpu_scatter_sub(v, idx, o, dev)
+    want, _, _ = oracle.scatter_sub(v, idx, o)
+    assert bits_equal(got, want), first_mismatch(got, want)

@@ -181,3 +181,27 @@ def test_identity_padding_and_split_lemmas(dtype):
         for b in reversed(blocks[:-1]):
             acc = b + acc
         assert acc.tobytes() == ref
+
+
+def test_ones_closed_form_matches_tree_and_oracle():
+    # the O(log m) closed form used by the largest-size GPU tests, against a literal level-by-
+    # level evaluation of the tree (small m) and against the oracle (m past 2^24, where the
+    # f32 sums of ones start to round)
+    from conftest import pw_ones
+
+    def levels(m):
+        p = 1
+        while p < m:
+            p *= 2
+        v = [np.float32(1.0)] * m + [np.float32(-0.0)] * (p - m)
+        while len(v) > 1:
+            v = [np.float32(v[i] + v[i + 1]) for i in range(0, len(v), 2)]
+        return v[0]
+
+    for m in (1, 2, 3, 5, 7, 100, 1000, 4097):
+        assert pw_ones(m, np.float32) == levels(m), m
+    for m in ((1 << 24) + 1, (1 << 25) + 12345, (1 << 26) - 1):
+        want = oracle.det_sum(np.ones(m, np.float32))
+        got = pw_ones(m, np.float32)
+        assert np.float32(want).view(np.uint32) == got.view(np.uint32), m
+    assert float(pw_ones((1 << 26) - 1, np.float32)) != (1 << 26) - 1   # the sum does round
