@@ -178,15 +178,56 @@ __global__ __launch_bounds__(256) void k_hist_apply(uint32_t* __restrict__ hist,
     }
 }
 
-// csum needs nb * nrb words, tot nb words (nb <= 257)
+// The same offsets for few rows, in one launch of one workgroup: thread d sums column d, an
+// exclusive scan over the digit totals gives each digit's base, thread d rewrites its column
+// as running offsets.  *valid (if given) receives the base of digit 256 (the keys in range).
+constexpr int64_t kSmallHistRows = 512;
+
+__global__ __launch_bounds__(256) void k_hist_offsets_small(uint32_t* __restrict__ hist,
+                                                            int64_t nrows, int nb,
+                                                            uint32_t* __restrict__ valid) {
+    __shared__ uint32_t s4[4];
+    const int t = threadIdx.x;
+    const bool extra = nb > 256 && t == 0;
+    uint32_t c0 = 0;
+#pragma unroll 8
+    for (int64_t r = 0; r < nrows; ++r) c0 += hist[r * nb + t];
+    uint32_t total;
+    uint32_t run0 = block_excl_scan_u32(c0, s4, &total);
+    uint32_t run1 = total;
+#pragma unroll 8
+    for (int64_t r = 0; r < nrows; ++r) {
+        const uint32_t v = hist[r * nb + t];
+        hist[r * nb + t] = run0;
+        run0 += v;
+        if (extra) {
+            const uint32_t w = hist[r * nb + 256];
+            hist[r * nb + 256] = run1;
+            run1 += w;
+        }
+    }
+    if (valid && t == 0) *valid = total;
+}
+
+__global__ void k_copy_word(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst) {
+    dst[0] = src[0];
+}
+
+// csum needs nb * nrb words, tot nb words (nb <= 257).  valid (first pass only): receives the
+// number of keys in range (the offset of the out-of-range bucket in chunk 0).
 det_status hist_offsets(uint32_t* hist, int64_t nrows, int nb, uint32_t* csum, uint32_t* tot,
-                        hipStream_t s) {
-    const int64_t nrb = cdiv(nrows, kRowBlk);
+                        uint32_t* valid, hipStream_t s) {
     KernelTimer kt("k_hist_offsets", s);
+    if (nrows <= kSmallHistRows) {
+        k_hist_offsets_small<<<1, 256, 0, s>>>(hist, nrows, nb, valid);
+        return launch_status();
+    }
+    const int64_t nrb = cdiv(nrows, kRowBlk);
     k_hist_colsums<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum);
     k_hist_colscan<<<dim3((unsigned)nb), dim3(256), 0, s>>>(csum, nrb, tot);
     k_hist_digitscan<<<1, 256, 0, s>>>(tot, nb);
     k_hist_apply<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum, tot);
+    if (valid) k_copy_word<<<1, 1, 0, s>>>(hist + 256, valid);
     return launch_status();
 }
 
@@ -423,10 +464,6 @@ __global__ __launch_bounds__(256) void k_radix_scatter(
         radix_rank_write<P, FIRST, ROWS, false, KO>(sm, key, pay, base, m, B, shift, off0, off1,
                                                 keys_out, pay_out, tid, lane, wave);
     }
-}
-
-__global__ void k_copy_word(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst) {
-    dst[0] = src[0];
 }
 
 // ---------------------------------------------------------------- destinations
@@ -962,10 +999,9 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
                 k_radix_hist<false><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb, L.nchunks,
                                                          (int)L.H, hist);
         }
-        det_status st = hist_offsets(hist, L.nchunks, nb, sums + 512, sums, s);
+        // bucket offsets; the first pass also counts the keys in range into ctrl[0]
+        det_status st = hist_offsets(hist, L.nchunks, nb, sums + 512, sums, first ? ctrl : nullptr, s);
         if (st != DET_SUCCESS) return st;
-        // valid keys = offset of the out-of-range bucket in chunk 0
-        if (first) k_copy_word<<<1, 1, 0, s>>>(hist + 256, ctrl);
         KernelTimer kt("k_radix_scatter", s);
         uint32_t* ko = keys[p & 1];
         uint16_t* ko16 = reinterpret_cast<uint16_t*>(ko);
