@@ -44,6 +44,21 @@ int64_t resident_wgs(const void* fn, int block) {
     return wgs;
 }
 
+int cu_count() {
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
 // ---------------------------------------------------------------- kernel timing hook
 
 namespace {

@@ -52,6 +52,9 @@ det_status scatter_launch(const void* values, const int32_t* index, int64_t n, i
 // (occupancy x compute units), cached per device and kernel; 0 if the runtime cannot tell.
 int64_t resident_wgs(const void* fn, int block);
 
+// Compute units of the current device (cached per device); 0 if the runtime cannot tell.
+int cu_count();
+
 // Kernel timing (a test hook): while it is switched on, a KernelTimer brackets one launch with
 // two HIP events on the launch's stream; det_debug_kernel_report reads them.  Off, it costs one
 // relaxed load.

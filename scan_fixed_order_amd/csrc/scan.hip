@@ -1000,6 +1000,10 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     // behind them, and a workgroup that starts late has lost its pipeline's overlap.
     int64_t grid = resident_wgs(fn, 256);
     if (grid <= 0) return DET_ERROR_LAUNCH;
+    // at most 3 workgroups per CU: for f32, 4 resident per CU measured 1-3% slower on MI355X
+    // (more tiles in flight than the memory system turns into bandwidth); f64 fits 2
+    const int64_t cap = 3 * (int64_t)cu_count();
+    if (cap > 0 && grid > cap) grid = cap;
     if (grid > L.ntiles) grid = L.ntiles;
     if (ov.grid_wgs > 0 && grid > ov.grid_wgs) grid = ov.grid_wgs;
     a.nctr = (int)(grid < kCounters ? grid : kCounters);
