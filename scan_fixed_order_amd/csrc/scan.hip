@@ -270,21 +270,30 @@ __device__ int64_t wg_lower_bound(const int64_t* __restrict__ offs, int64_t cnt,
     return lo + __syncthreads_count(pred);
 }
 
+// The smallest offset value that can mark a head in the tile starting at flipped position F0
+// (forward: F0; reverse: n - F0 - T, at least 1).  The tile's heads start at the first offset
+// index k in [0, nseg] with offs[k] >= that value.
+__device__ __forceinline__ int64_t heads_lo(int64_t n, bool rev, int64_t F0) {
+    if (!rev) return F0;
+    return (n - F0 - kT > 1) ? n - F0 - kT : 1;
+}
+
 // Bit b of s_heads marks flipped position F0 + b (b in [0, T]) as a segment head.
 // Forward: heads are the offsets o < n.  Reverse: flipped position n - o for offsets o > 0
-// (the last element of every non-empty segment).
+// (the last element of every non-empty segment).  k0_known: the first offset index for the
+// tile when computed before the scan, else -1 (searched here).
 __device__ void build_heads(const int64_t* __restrict__ offs, int64_t nseg, int64_t n, bool rev,
-                            int64_t F0, uint32_t* s_heads, int tid) {
+                            int64_t F0, uint32_t* s_heads, int tid, int64_t k0_known) {
     for (int i = tid; i < kHeadWords; i += 256) s_heads[i] = 0u;
-    int64_t lo_v, hi_v;
-    if (!rev) {
-        lo_v = F0;
-        hi_v = (F0 + kT < n - 1) ? F0 + kT : n - 1;
+    const int64_t lo_v = heads_lo(n, rev, F0);
+    const int64_t hi_v = !rev ? ((F0 + kT < n - 1) ? F0 + kT : n - 1) : n - F0;
+    int64_t k0;
+    if (k0_known >= 0) {
+        k0 = k0_known;
+        __syncthreads();   // the heads are cleared before any thread sets one
     } else {
-        lo_v = (n - F0 - kT > 1) ? n - F0 - kT : 1;
-        hi_v = n - F0;
+        k0 = wg_lower_bound(offs, nseg + 1, lo_v, tid);   // ends with a barrier
     }
-    const int64_t k0 = wg_lower_bound(offs, nseg + 1, lo_v, tid);   // ends with a barrier
     for (int64_t base = k0;; base += 256) {
         const int64_t k = base + tid;
         bool in = false;
@@ -505,6 +514,8 @@ struct ScanArgs {
     uint32_t* ticket;    // kCounters tile counters, kCounterStride words apart
     uint32_t* err;       // raised when a wait hit the spin bound
     const T* dummy;      // 256 bytes that the 16-byte loads of a non-vector run read instead
+    const int64_t* k0;   // segmented: per tile, the first offset index at or above the tile
+                         // (null: searched by the tile itself)
     int ntiles;
     int nctr;            // tile counters in use: min(kCounters, grid)
     int rev;
@@ -521,7 +532,7 @@ __device__ __forceinline__ Seg<T> tile_local(const ScanArgs<T>& a, int j, T (&r)
                                              Seg<T>* s_wtot, int tid, int lane, int wave) {
     const int64_t F0 = (int64_t)j * kT;
     if constexpr (SEG) {
-        build_heads(a.offs, a.nseg, a.n, REV, F0, s_heads, tid);
+        build_heads(a.offs, a.nseg, a.n, REV, F0, s_heads, tid, a.k0 ? a.k0[j] : -1);
         hb = s_heads[wave * 64 + lane];
     } else {
         hb = 0u;
@@ -875,6 +886,23 @@ __global__ __launch_bounds__(256) void k_scan_small(ScanArgs<T> a) {
     }
 }
 
+// Segmented scans: for every tile, the first offset index at or above the lowest position
+// the tile covers (the binary search each tile would otherwise run on its critical path).
+__global__ __launch_bounds__(256) void k_seg_first(const int64_t* __restrict__ offs, int64_t nseg,
+                                                   int64_t n, int rev, int64_t ntiles,
+                                                   int64_t* __restrict__ k0) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= ntiles) return;
+    const int64_t target = heads_lo(n, rev != 0, j * (int64_t)kT);
+    int64_t lo = 0, hi = nseg + 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (offs[mid] < target) lo = mid + 1;
+        else hi = mid;
+    }
+    k0[j] = lo;
+}
+
 __global__ void k_copy_error(const uint32_t* err, int32_t* out) {
     out[0] = (int32_t)(err[0] != 0u);
 }
@@ -893,7 +921,7 @@ constexpr size_t kHeader = kDummyOff + 256;
 
 struct Layout {
     int64_t ntiles, nq, nQ;
-    size_t agg_off, g_off, carry_off, used, total;
+    size_t agg_off, g_off, carry_off, used, k0_off, total;
 };
 
 // Slots for tile totals, interval totals and super-interval carries.  The reservation assumes
@@ -911,7 +939,8 @@ Layout layout(int64_t n, det_dtype dt, int A, int A2) {
     L.g_off = L.agg_off + tile_bytes;
     L.carry_off = L.g_off + tile_bytes;
     L.used = L.carry_off + round_up((size_t)(L.nQ + 1) * sw * 8, 256);
-    L.total = L.carry_off + worst;
+    L.k0_off = L.carry_off + worst;                       // segmented: a first index per tile
+    L.total = L.k0_off + round_up((size_t)L.ntiles * 8, 256);
     // the cleared range must cover the interval totals in use as well
     (void)L.nq;
     return L;
@@ -967,6 +996,15 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     }
     det_status st = launch_status();
     if (st != DET_SUCCESS) return st;
+    int64_t* k0 = reinterpret_cast<int64_t*>(ws + L.k0_off);
+    if (offs) {
+        KernelTimer kt("k_seg_first", s);
+        const int64_t g = (L.ntiles + 255) / 256;
+        k_seg_first<<<(unsigned)g, 256, 0, s>>>(offs, nseg, n, (flags & DET_SCAN_REVERSE) ? 1 : 0,
+                                                L.ntiles, k0);
+        st = launch_status();
+        if (st != DET_SUCCESS) return st;
+    }
     ScanArgs<T> a;
     a.x = x;
     a.y = y;
@@ -979,6 +1017,7 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     a.ticket = reinterpret_cast<uint32_t*>(ws);
     a.err = reinterpret_cast<uint32_t*>(ws + kErrOff);
     a.dummy = reinterpret_cast<const T*>(ws + kDummyOff);
+    a.k0 = offs ? k0 : nullptr;
     a.ntiles = (int)L.ntiles;
     a.rev = (flags & DET_SCAN_REVERSE) ? 1 : 0;
     a.excl = (flags & DET_SCAN_EXCLUSIVE) ? 1 : 0;

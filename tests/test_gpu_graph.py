@@ -137,3 +137,47 @@ def test_graph_replay_matches_direct_and_oracle(dev, dtype):
         got = snapshot()
         for k, (g, d) in enumerate(zip(got, direct)):
             assert bits_equal(g, d), ("replay", rep, k, first_mismatch(g, d))
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_streams_do_not_change_bits(dev, dtype):
+    # the same calls on the default stream and on two other streams running at the same time
+    # (each with its own workspace, as the interface requires of overlapping calls)
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    n = 3 * 256 * TILE + 777
+    x = torch.from_numpy(rounding(n, dtype, 5)).to(dev)
+    rng = np.random.default_rng(6)
+    idx = torch.from_numpy(rng.integers(0, 5000, n).astype(np.int32)).to(dev)
+
+    def run(ws_sum, ws_scan, ws_sc):
+        s = det.det_sum(x, ws=ws_sum)
+        y = det.det_scan(x, exclusive=True, reverse=True, ws=ws_scan)
+        o = torch.zeros(5000, dtype=tdt, device=dev)
+        det.det_scatter_add(x, idx, o, ws=ws_sc)
+        return s, y, o
+
+    code = 0 if dtype == np.float32 else 1
+
+    def workspaces():
+        return (ws_for(det.det_sum_workspace_size(n, code), dev),
+                ws_for(det.det_scan_workspace_size(n, code, 3, 0), dev),
+                ws_for(det.det_scatter_add_workspace_size(n, 5000, 1, code), dev))
+
+    ref = [t.cpu().numpy() for t in run(*workspaces())]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    w1, w2 = workspaces(), workspaces()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            r1 = run(*w1)
+        with torch.cuda.stream(s2):
+            r2 = run(*w2)
+        outs.append((r1, r2))
+    torch.cuda.synchronize()
+    for r1, r2 in outs:
+        for got in (r1, r2):
+            for g, w in zip(got, ref):
+                assert bits_equal(g.cpu().numpy().reshape(w.shape), w)
