@@ -17,6 +17,12 @@ Every function here follows the association order stated in ``detref.c``:
 * ``scatter_sub``   -- the values negated one by one, then ``scatter_add`` (Warp "Deterministic
                        Execution", Pattern 1: atomic_sub's values are negated and added in a
                        fixed order).
+* ``scatter_add_running`` -- ``scatter_add`` whose ``prev`` is the destination's value after
+                       the earlier contributions (in ascending source index): the initial
+                       value plus the segmented exclusive ``scan`` of the destinations'
+                       members laid end to end (reading R7 in ``detref.c``; the row-indexed
+                       accumulate of Warp's ``warp.tile_atomic_add_indexed`` returns such
+                       values, which that page calls not reproducible under repeats).
 * ``scan_int32``    -- int32 prefix sums modulo 2^32 (Warp "Deterministic Execution", Pattern 2:
                        the count-scan-write prefix scan); integers need no order, so this is
                        the plain definition, written in numpy.
@@ -92,6 +98,9 @@ def _load():
         f = getattr(lib, "oref_scan" + suf)
         f.argtypes = [p, p, i64, ctypes.c_uint, p, i64, i64, i64, i64, i64, i64]
         f.restype = ctypes.c_int
+        f = getattr(lib, "oref_scatter_add_running" + suf)
+        f.argtypes = [p, p, i64, i64, p, i64, p, i64, i64, i64, i64, i64]
+        f.restype = i64
     _lib = lib
     return lib
 
@@ -152,6 +161,35 @@ def scatter_add(values: np.ndarray, index: np.ndarray, out: np.ndarray,
                                                     _ptr(new), num_out, _ptr(prev))
     if k < 0:
         raise RuntimeError(f"oracle scatter_add failed ({k})")
+    return new, prev, int(k)
+
+
+def scatter_add_running(values: np.ndarray, index: np.ndarray, out: np.ndarray
+                        ) -> Tuple[np.ndarray, np.ndarray, int]:
+    """``scatter_add`` with the running ``prev`` of reading R7: for the member at position g
+    of the destination-grouped array (destination order, ascending source index inside),
+    ``prev = out_init`` at its destination's first position, else ``out_init + E[g]`` with
+    ``E`` the forward exclusive ``scan`` of that array (one segment per destination), per
+    column.  Returns ``(new_out, prev, n_skipped)``; skipped rows keep NaN in ``prev``."""
+    values = np.ascontiguousarray(values)
+    index = np.ascontiguousarray(index, dtype=np.int32).reshape(-1)
+    n = index.size
+    row_len = 1 if values.ndim == 1 else int(np.prod(values.shape[1:]))
+    if values.size != n * row_len:
+        raise ValueError("values and index disagree on n")
+    if out.dtype != values.dtype:
+        raise TypeError("values and out must share a dtype")
+    new = np.array(out, dtype=out.dtype, copy=True, order="C")
+    num_out = new.size // row_len if row_len else 0
+    if new.size != num_out * row_len:
+        raise ValueError("out is not a whole number of rows")
+    prev = np.full(values.shape, np.nan, dtype=values.dtype)
+    suf = _suffix(values.dtype)
+    k = getattr(_load(), "oref_scatter_add_running" + suf)(
+        _ptr(values), _ptr(index), n, row_len, _ptr(new), num_out, _ptr(prev),
+        SPEC_V, SPEC_W, SPEC_NW, SPEC_A, SPEC_A2)
+    if k < 0:
+        raise RuntimeError(f"oracle scatter_add_running failed ({k})")
     return new, prev, int(k)
 
 

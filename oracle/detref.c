@@ -45,6 +45,13 @@
  *  R6  exclusive = inclusive shifted by one with +0.0 entering at every segment
  *      head; reverse = flip, forward scan, flip; segments via head flags and the
  *      standard segmented operator (flag_a|flag_b, flag_b ? b : a+b).
+ *  R7  running prev (what a loop of atomic adds in ascending source index would hand
+ *      back, with the sums it holds formed in a fixed order): lay the members of every
+ *      destination (ascending source index, R4) end to end in destination order, one
+ *      segment per destination, and scan each column of that array exclusively (R5/R6,
+ *      forward).  The member at position g with source row i and destination r gets
+ *      prev[i][c] = out_init[r][c] when g is its destination's first position, else
+ *      out_init[r][c] + E[g].  out is updated as in R4.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -328,4 +335,56 @@ int FN(oref_scan)(const DET_T* x, DET_T* y, int64_t n, unsigned flags, const int
     }
     free(xs); free(ys); free(h);
     return rc;
+}
+
+/* ---------------------------------------------------------------- R7: running prev */
+
+/* Arguments as for oref_scatter_add; prev is required and receives the running value of R7
+ * (rows of skipped sources are not written); V, W, NW, A, A2 are the scan's constants.
+ * Returns the number of skipped source rows, or a negative error code. */
+int64_t FN(oref_scatter_add_running)(const DET_T* values, const int32_t* index, int64_t n,
+                                     int64_t row_len, DET_T* out, int64_t num_out, DET_T* prev,
+                                     int64_t V, int64_t W, int64_t NW, int64_t A, int64_t A2) {
+    if (n < 0 || row_len < 1 || num_out < 0 || !prev) return OREF_BAD_ARG;
+    int64_t* start = (int64_t*)calloc((size_t)num_out + 1, sizeof(int64_t));
+    if (!start) return OREF_NO_MEM;
+    int64_t valid = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t b = index[i];
+        if (b < 0 || b >= num_out) continue;
+        start[b + 1] += 1;
+        ++valid;
+    }
+    for (int64_t b = 0; b < num_out; ++b) start[b + 1] += start[b];
+    /* G: position g holds source row src[g] of destination dst[g] */
+    int64_t* src = (int64_t*)malloc((size_t)(valid > 0 ? valid : 1) * sizeof(int64_t));
+    int64_t* dst = (int64_t*)malloc((size_t)(valid > 0 ? valid : 1) * sizeof(int64_t));
+    int64_t* fill = (int64_t*)malloc((size_t)(num_out > 0 ? num_out : 1) * sizeof(int64_t));
+    DET_T* g_col = (DET_T*)malloc((size_t)(valid > 0 ? valid : 1) * sizeof(DET_T));
+    DET_T* e_col = (DET_T*)malloc((size_t)(valid > 0 ? valid : 1) * sizeof(DET_T));
+    int rc = OREF_OK;
+    if (!src || !dst || !fill || !g_col || !e_col) rc = OREF_NO_MEM;
+    if (rc == OREF_OK) {
+        for (int64_t b = 0; b < num_out; ++b) fill[b] = start[b];
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t b = index[i];
+            if (b < 0 || b >= num_out) continue;
+            src[fill[b]] = i;
+            dst[fill[b]] = b;
+            fill[b] += 1;
+        }
+        for (int64_t c = 0; c < row_len && rc == OREF_OK; ++c) {
+            for (int64_t g = 0; g < valid; ++g) g_col[g] = values[src[g] * row_len + c];
+            rc = FN(oref_scan)(g_col, e_col, valid, OREF_EXCLUSIVE, start, num_out, V, W, NW, A,
+                               A2);
+            if (rc != OREF_OK) break;
+            for (int64_t g = 0; g < valid; ++g) {
+                const DET_T init = out[dst[g] * row_len + c];
+                prev[src[g] * row_len + c] = (g == start[dst[g]]) ? init : init + e_col[g];
+            }
+        }
+    }
+    free(start); free(src); free(dst); free(fill); free(g_col); free(e_col);
+    if (rc != OREF_OK) return rc;
+    return FN(oref_scatter_add)(values, index, n, row_len, out, num_out, NULL);
 }
