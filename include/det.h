@@ -155,6 +155,35 @@ det_status det_scatter_sub(const void* values, const int32_t* index, int64_t n, 
                            det_dtype dtype, void* out, int64_t num_out, void* prev,
                            int64_t* n_skipped, void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of workspace det_scatter_add_running needs (0 when the arguments are invalid). */
+size_t det_scatter_add_running_workspace_size(int64_t n, int64_t num_out, int64_t row_len,
+                                              det_dtype dtype);
+
+/* det_scatter_add whose prev is the running value: what a loop of atomic adds in ascending
+ * source index would hand back to each source, with the sum of the earlier contributions
+ * formed in a fixed order.  The Warp reference "warp.tile_atomic_add_indexed" returns the
+ * destination rows as they were before the accumulate and leaves them unspecified under
+ * repeated indices; this entry point fixes them.
+ *
+ * Order: lay the members of every destination (ascending source index, as in
+ * det_scatter_add) end to end in destination order, one segment per destination, and take
+ * E = the forward exclusive segmented det_scan of each column of that array.  The member at
+ * position g of that array, source row i, destination r, gets
+ *   prev[i*row_len + c] = out[r*row_len + c]          at r's first position,
+ *   prev[i*row_len + c] = out[r*row_len + c] + E[g]   elsewhere
+ * (out as before the call).  out receives exactly what det_scatter_add gives it.
+ *
+ * values, index, out, n_skipped, row_len: as for det_scatter_add.
+ * prev:    device [n * row_len] of dtype, required when n > 0 (rows of skipped i are not
+ *          written); must not overlap values or out (DET_ERROR_INVALID_VALUE).
+ * row_len: 1 .. 65535 * 32 (DET_ERROR_TOO_LARGE beyond).
+ * Workspace: det_scatter_add_running_workspace_size bytes, about 2 * n * row_len elements
+ * more than det_scatter_add's.  Launches one scan per column. */
+det_status det_scatter_add_running(const void* values, const int32_t* index, int64_t n,
+                                   int64_t row_len, det_dtype dtype, void* out, int64_t num_out,
+                                   void* prev, int64_t* n_skipped, void* ws, size_t ws_bytes,
+                                   void* stream);
+
 /* ------------------------------------------------------------------ introspection */
 
 /* Version of the association order; results of one version never change. */

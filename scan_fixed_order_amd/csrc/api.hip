@@ -195,9 +195,26 @@ size_t det_scatter_add_workspace_size(int64_t n, int64_t num_out, int64_t row_le
     return scatter_workspace(n, num_out, row_len, dtype);
 }
 
+// columns of the running scatter: 32 per workgroup along the grid's y dimension (65535 at most)
+constexpr int64_t kRunningMaxRowLen = 65535LL * 32;
+
+size_t det_scatter_add_running_workspace_size(int64_t n, int64_t num_out, int64_t row_len,
+                                              det_dtype dtype) {
+    if (n < 0 || n > DET_MAX_N || num_out < 0 || num_out > DET_MAX_N || row_len < 1 ||
+        !valid_dtype(dtype))
+        return 0;
+    if (row_len > kRunningMaxRowLen) return 0;
+    return scatter_running_workspace(n, num_out, row_len, dtype);
+}
+
 }  // extern "C"
 
 namespace {
+bool overlaps(const void* a, size_t abytes, const void* b, size_t bbytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return abytes > 0 && bbytes > 0 && a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
 det_status scatter_checked(const void* values, const int32_t* index, int64_t n, int64_t row_len,
                            det_dtype dtype, void* out, int64_t num_out, void* prev,
                            int64_t* n_skipped, void* ws, size_t ws_bytes, bool negate,
@@ -241,6 +258,33 @@ det_status det_scatter_sub(const void* values, const int32_t* index, int64_t n, 
                            int64_t* n_skipped, void* ws, size_t ws_bytes, void* stream) {
     return scatter_checked(values, index, n, row_len, dtype, out, num_out, prev, n_skipped, ws,
                            ws_bytes, true, stream);
+}
+
+det_status det_scatter_add_running(const void* values, const int32_t* index, int64_t n,
+                                   int64_t row_len, det_dtype dtype, void* out, int64_t num_out,
+                                   void* prev, int64_t* n_skipped, void* ws, size_t ws_bytes,
+                                   void* stream) {
+    if (!valid_dtype(dtype)) return DET_ERROR_UNSUPPORTED;
+    if (n < 0 || num_out < 0 || row_len < 1) return DET_ERROR_INVALID_VALUE;
+    if (n > DET_MAX_N || num_out > DET_MAX_N) return DET_ERROR_TOO_LARGE;
+    if (row_len > kRunningMaxRowLen) return DET_ERROR_TOO_LARGE;
+    if ((double)n * (double)row_len > 9.0e18 || (double)num_out * (double)row_len > 9.0e18)
+        return DET_ERROR_TOO_LARGE;
+    if (n > 0 && (!values || !index || !prev)) return DET_ERROR_INVALID_VALUE;
+    if (num_out > 0 && !out) return DET_ERROR_INVALID_VALUE;
+    const size_t es = dtype_size(dtype);
+    if (!elem_aligned(values, es) || !elem_aligned(out, es) || !elem_aligned(prev, es) ||
+        !elem_aligned(index, sizeof(int32_t)) || !elem_aligned(n_skipped, sizeof(int64_t)))
+        return DET_ERROR_INVALID_VALUE;
+    const size_t vbytes = (size_t)n * row_len * es, obytes = (size_t)num_out * row_len * es;
+    if (overlaps(values, vbytes, out, obytes) || overlaps(prev, vbytes, out, obytes) ||
+        overlaps(prev, vbytes, values, vbytes))
+        return DET_ERROR_INVALID_VALUE;
+    if (!ws || !ws_aligned(ws) ||
+        ws_bytes < scatter_running_workspace(n, num_out, row_len, dtype))
+        return DET_ERROR_WORKSPACE;
+    return scatter_running_launch(values, index, n, row_len, dtype, out, num_out, prev, n_skipped,
+                                  ws, static_cast<hipStream_t>(stream));
 }
 
 int det_spec_version(void) { return 1; }

@@ -48,6 +48,12 @@ det_status scatter_launch(const void* values, const int32_t* index, int64_t n, i
                           det_dtype dt, void* out, int64_t num_out, void* prev, int64_t* n_skipped,
                           void* ws, size_t ws_bytes, bool negate, hipStream_t s);
 
+// scatter-add whose prev is the running value (prev required; arguments checked by the caller)
+size_t scatter_running_workspace(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt);
+det_status scatter_running_launch(const void* values, const int32_t* index, int64_t n,
+                                  int64_t row_len, det_dtype dt, void* out, int64_t num_out,
+                                  void* prev, int64_t* n_skipped, void* ws, hipStream_t s);
+
 // Workgroups of `block` threads of kernel `fn` that are resident on the current device at once
 // (occupancy x compute units), cached per device and kernel; 0 if the runtime cannot tell.
 int64_t resident_wgs(const void* fn, int block);

@@ -902,6 +902,89 @@ __global__ __launch_bounds__(256) void k_segred_rows_long(const uint32_t* __rest
     }
 }
 
+
+// ---------------------------------------------------------------- running prev
+
+// The destination-grouped members, one column after another: G[c * n + s] = values[src[s] *
+// d + c] for sorted positions s < nvalid and +0.0 past them.  A tile of 64 positions x 32
+// columns goes through LDS so that both the row reads and the column writes are contiguous.
+template <typename T>
+__global__ __launch_bounds__(256) void k_group_gather(const T* __restrict__ values,
+                                                      const uint32_t* __restrict__ src,
+                                                      const uint32_t* __restrict__ nvalid,
+                                                      int64_t n, int64_t d, T* __restrict__ G) {
+    __shared__ T t[64][33];
+    const int tid = threadIdx.x;
+    const int64_t s0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 32;
+    const int64_t m = *nvalid;
+    const int cl = tid & 31;
+    for (int r = tid >> 5; r < 64; r += 8) {
+        const int64_t sp = s0 + r, c = c0 + cl;
+        T v = T(0.0);
+        if (sp < m && c < d) v = values[(int64_t)src[sp] * d + c];
+        t[r][cl] = v;
+    }
+    __syncthreads();
+    const int sl = tid & 63;
+    for (int cc = tid >> 6; cc < 32; cc += 4) {
+        const int64_t sp = s0 + sl, c = c0 + cc;
+        if (sp < n && c < d) G[c * n + sp] = t[sl][cc];
+    }
+}
+
+// Offsets of the grouped array as the segmented scan takes them: o[b] = off[b] for b <= B
+// (destination b's members start at off[b]; off[B] = nvalid) and o[B + 1] = n (the skipped
+// sources, one more segment).
+__global__ void k_offsets64(const uint32_t* __restrict__ off, int64_t B, int64_t n,
+                            int64_t* __restrict__ o) {
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b <= B + 1;
+         b += (int64_t)gridDim.x * blockDim.x)
+        o[b] = b <= B ? (int64_t)off[b] : n;
+}
+
+// prev[src[s] * d + c] = out[r * d + c] at its destination r's first position s = off[r], else
+// out[r * d + c] + E[c * n + s] (E: the exclusive segmented scan of the grouped column c).
+// Runs before out is updated.  The same 64 x 32 tiling as k_group_gather, the other way round.
+template <typename T>
+__global__ __launch_bounds__(256) void k_running_prev(const uint32_t* __restrict__ K,
+                                                      const uint32_t* __restrict__ src,
+                                                      const uint32_t* __restrict__ off,
+                                                      const uint32_t* __restrict__ nvalid,
+                                                      int64_t n, int64_t d,
+                                                      const T* __restrict__ E,
+                                                      const T* __restrict__ out,
+                                                      T* __restrict__ prev) {
+    __shared__ T t[64][33];
+    __shared__ uint32_t s_src[64], s_dst[64], s_head[64];
+    const int tid = threadIdx.x;
+    const int64_t s0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 32;
+    const int64_t m = *nvalid;
+    if (s0 >= m) return;   // the same for the whole workgroup
+    if (tid < 64) {
+        const int64_t sp = s0 + tid;
+        if (sp < m) {
+            const uint32_t r = K[sp];
+            s_dst[tid] = r;
+            s_src[tid] = src[sp];
+            s_head[tid] = (uint32_t)(off[r] == (uint32_t)sp);
+        }
+    }
+    const int sl = tid & 63;
+    for (int cc = tid >> 6; cc < 32; cc += 4) {
+        const int64_t sp = s0 + sl, c = c0 + cc;
+        if (sp < m && c < d) t[sl][cc] = E[c * n + sp];
+    }
+    __syncthreads();
+    const int cl = tid & 31;
+    for (int r = tid >> 5; r < 64; r += 8) {
+        const int64_t sp = s0 + r, c = c0 + cl;
+        if (sp < m && c < d) {
+            const T init = out[(int64_t)s_dst[r] * d + c];
+            prev[(int64_t)s_src[r] * d + c] = s_head[r] ? init : init + t[r][cl];
+        }
+    }
+}
+
 // ---------------------------------------------------------------- host side
 
 int key_passes(int64_t B) {
@@ -916,10 +999,12 @@ struct SLayout {
     size_t keysA, keysB, payA, payB, hist, sums, ctrl, off, pF, pC, total;
 };
 
-SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
+// idx_payload: the sort carries source indices (4 bytes) even for scalar destinations
+SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt,
+                bool idx_payload = false) {
     SLayout L;
     const bool rows = row_len > 1;
-    const size_t pw = rows ? 4 : dtype_size(dt);    // payload bytes
+    const size_t pw = (rows || idx_payload) ? 4 : dtype_size(dt);    // payload bytes
     L.H = 256 * (pw == 4 ? kItems<uint32_t> : kItems<uint64_t>);
     L.nchunks = cdiv(n > 0 ? n : 1, L.H);
     L.nhist = (int64_t)kBuckets0 * L.nchunks;
@@ -948,47 +1033,28 @@ SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
     return L;
 }
 
-template <typename T, typename P, bool ROWS>
-det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_t row_len, T* out,
-                        int64_t num_out, T* prev, int64_t* n_skipped, char* ws, bool neg,
-                        hipStream_t s) {
-    const SLayout L = slayout(n, num_out, row_len, sizeof(T) == 8 ? DET_F64 : DET_F32);
-    if (n == 0) {
-        if (n_skipped) {
-            k_write_skipped_all<T><<<1, 1, 0, s>>>(n_skipped, 0);
-            return launch_status();
-        }
-        return DET_SUCCESS;
-    }
-    if (prev) {
-        const int64_t total = n * row_len;
-        int64_t g = cdiv(total, 256);
-        if (g > 65536) g = 65536;
-        k_prev_gather<T><<<dim3((unsigned)g), dim3(256), 0, s>>>(index, n, row_len, num_out, out, prev);
-    }
-    if (num_out == 0) {
-        if (n_skipped) k_write_skipped_all<T><<<1, 1, 0, s>>>(n_skipped, n);
-        return launch_status();
-    }
-    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);   // [0] = number of valid keys
+// Stable LSD radix sort of (destination, payload) by destination: the first pass takes the
+// keys from index and the payloads from pay_in (ROWS: the source index itself), and routes
+// out-of-range keys past the valid ones, whose count it leaves in ctrl[0]; later passes sort
+// only the valid prefix.  *K and *SP receive the sorted keys (16-bit when k16) and payloads.
+template <typename P, bool ROWS>
+det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64_t num_out,
+                        const SLayout& L, char* ws, bool k16, hipStream_t s, const uint32_t** K,
+                        const P** SP) {
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
     uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(ws + L.keysA),
                          reinterpret_cast<uint32_t*>(ws + L.keysB)};
     P* pay[2] = {reinterpret_cast<P*>(ws + L.payA), reinterpret_cast<P*>(ws + L.payB)};
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
     uint32_t* sums = reinterpret_cast<uint32_t*>(ws + L.sums);
-    uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
     const uint32_t B = (uint32_t)num_out;
     const int passes = key_passes(num_out);
-    // scalar destinations that all fit 16 bits: the last pass writes 16-bit keys, which the
-    // destination offsets and the reduction read (out-of-range keys land past the valid ones
-    // and are never read)
-    const bool k16 = !ROWS && num_out <= 65536;
     const unsigned grid = (unsigned)L.nchunks;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
         const bool first = p == 0;
         const uint32_t* kin = first ? reinterpret_cast<const uint32_t*>(index) : keys[(p - 1) & 1];
-        const P* pin = first ? reinterpret_cast<const P*>(values) : pay[(p - 1) & 1];
+        const P* pin = first ? pay_in0 : pay[(p - 1) & 1];
         const int nb = first ? kBuckets0 : 256;
         {
             KernelTimer kt("k_radix_hist", s);
@@ -1021,9 +1087,45 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
         st = launch_status();
         if (st != DET_SUCCESS) return st;
     }
-    const uint32_t* K = keys[(passes - 1) & 1];
+    *K = keys[(passes - 1) & 1];
+    *SP = pay[(passes - 1) & 1];
+    return DET_SUCCESS;
+}
+
+template <typename T, typename P, bool ROWS>
+det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_t row_len, T* out,
+                        int64_t num_out, T* prev, int64_t* n_skipped, char* ws, bool neg,
+                        hipStream_t s) {
+    const SLayout L = slayout(n, num_out, row_len, sizeof(T) == 8 ? DET_F64 : DET_F32);
+    if (n == 0) {
+        if (n_skipped) {
+            k_write_skipped_all<T><<<1, 1, 0, s>>>(n_skipped, 0);
+            return launch_status();
+        }
+        return DET_SUCCESS;
+    }
+    if (prev) {
+        const int64_t total = n * row_len;
+        int64_t g = cdiv(total, 256);
+        if (g > 65536) g = 65536;
+        k_prev_gather<T><<<dim3((unsigned)g), dim3(256), 0, s>>>(index, n, row_len, num_out, out, prev);
+    }
+    if (num_out == 0) {
+        if (n_skipped) k_write_skipped_all<T><<<1, 1, 0, s>>>(n_skipped, n);
+        return launch_status();
+    }
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);   // [0] = number of valid keys
+    uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
+    // scalar destinations that all fit 16 bits: the last pass writes 16-bit keys, which the
+    // destination offsets and the reduction read (out-of-range keys land past the valid ones
+    // and are never read)
+    const bool k16 = !ROWS && num_out <= 65536;
+    const uint32_t* K = nullptr;
+    const P* SP = nullptr;
+    det_status st = sort_by_dest<P, ROWS>(index, reinterpret_cast<const P*>(values), n, num_out,
+                                          L, ws, k16, s, &K, &SP);
+    if (st != DET_SUCCESS) return st;
     const uint16_t* K16 = reinterpret_cast<const uint16_t*>(K);
-    const P* SP = pay[(passes - 1) & 1];
     {
         int64_t g = cdiv(num_out + 1, 256);
         if (g > 8192) g = 8192;
@@ -1073,6 +1175,110 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
     return launch_status();
 }
 
+
+// Scatter-add with the running prev: the sort carries source indices; the grouped members are
+// gathered column by column, each column scanned (exclusive, forward, one segment per
+// destination and one for the skipped sources), prev written from the scan and the initial
+// values, and then out reduced exactly as det_scatter_add reduces it.
+struct RLayout {
+    SLayout S;
+    size_t o64, G, E, sws, total;
+};
+
+RLayout rlayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
+    RLayout R;
+    R.S = slayout(n, num_out, row_len, dt, true);
+    size_t o = R.S.total;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += round_up(bytes > 0 ? bytes : 1, 256);
+        return at;
+    };
+    const size_t cells = (size_t)n * (size_t)row_len * dtype_size(dt);
+    R.o64 = take((size_t)(num_out + 2) * 8);
+    R.G = take(cells);
+    R.E = take(cells);
+    R.sws = take(scan_workspace(n > 0 ? n : 1, dt, DET_SCAN_EXCLUSIVE, num_out + 1));
+    R.total = o;
+    return R;
+}
+
+template <typename T>
+det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n, int64_t row_len,
+                                T* out, int64_t num_out, T* prev, int64_t* n_skipped, char* ws,
+                                hipStream_t s) {
+    const det_dtype dt = sizeof(T) == 8 ? DET_F64 : DET_F32;
+    const RLayout R = rlayout(n, num_out, row_len, dt);
+    const SLayout& L = R.S;
+    if (n == 0 || num_out == 0) {
+        if (n_skipped) k_write_skipped_all<T><<<1, 1, 0, s>>>(n_skipped, num_out == 0 ? n : 0);
+        return launch_status();
+    }
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
+    uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
+    const uint32_t* K = nullptr;
+    const uint32_t* SRC = nullptr;
+    det_status st = sort_by_dest<uint32_t, true>(index, nullptr, n, num_out, L, ws, false, s, &K,
+                                                 &SRC);
+    if (st != DET_SUCCESS) return st;
+    {
+        int64_t g = cdiv(num_out + 1, 256);
+        if (g > 8192) g = 8192;
+        KernelTimer kt("k_bin_offsets", s);
+        k_bin_offsets<uint32_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(K, ctrl, num_out, n, off,
+                                                                         n_skipped);
+    }
+    int64_t* o64 = reinterpret_cast<int64_t*>(ws + R.o64);
+    T* G = reinterpret_cast<T*>(ws + R.G);
+    T* E = reinterpret_cast<T*>(ws + R.E);
+    {
+        int64_t g = cdiv(num_out + 2, 256);
+        if (g > 4096) g = 4096;
+        k_offsets64<<<dim3((unsigned)g), dim3(256), 0, s>>>(off, num_out, n, o64);
+    }
+    const dim3 tg((unsigned)cdiv(n, 64), (unsigned)cdiv(row_len, 32));
+    {
+        KernelTimer kt("k_group_gather", s);
+        k_group_gather<T><<<tg, dim3(256), 0, s>>>(values, SRC, ctrl, n, row_len, G);
+    }
+    st = launch_status();
+    if (st != DET_SUCCESS) return st;
+    const size_t sbytes = scan_workspace(n, dt, DET_SCAN_EXCLUSIVE, num_out + 1);
+    for (int64_t c = 0; c < row_len; ++c) {
+        st = scan_launch(G + c * n, E + c * n, n, dt, DET_SCAN_EXCLUSIVE, o64, num_out + 1,
+                         ws + R.sws, sbytes, s);
+        if (st != DET_SUCCESS) return st;
+    }
+    {
+        KernelTimer kt("k_running_prev", s);
+        k_running_prev<T><<<tg, dim3(256), 0, s>>>(K, SRC, off, ctrl, n, row_len, E, out, prev);
+    }
+    st = launch_status();
+    if (st != DET_SUCCESS) return st;
+    T* pF = reinterpret_cast<T*>(ws + L.pF);
+    T* pC = reinterpret_cast<T*>(ws + L.pC);
+    if (row_len == 1) {
+        {
+            KernelTimer kt("k_segred_scalar", s);
+            k_segred_scalar<T, uint32_t, false><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
+                K, G, off, ctrl, out, pF, pC);
+        }
+        int64_t lg = cdiv(num_out, 64 * 4);
+        if (lg > 4096) lg = 4096;
+        k_segred_scalar_long<T><<<dim3((unsigned)lg), dim3(256), 0, s>>>(off, num_out, pF, pC, out);
+    } else {
+        {
+            KernelTimer kt("k_segred_rows", s);
+            k_segred_rows<T, false><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
+                K, SRC, off, ctrl, values, row_len, out, pF, pC);
+        }
+        int64_t rg = cdiv(num_out, 256);
+        if (rg > 4096) rg = 4096;
+        k_segred_rows_long<T><<<dim3((unsigned)rg), dim3(256), 0, s>>>(off, num_out, row_len, pF,
+                                                                        pC, out);
+    }
+    return launch_status();
+}
 }  // namespace
 
 size_t scatter_workspace(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
@@ -1098,6 +1304,27 @@ det_status scatter_launch(const void* values, const int32_t* index, int64_t n, i
     if (row_len == 1)
         return scatter_impl<double, uint64_t, false>(v, index, n, 1, o, num_out, pr, n_skipped, w, negate, s);
     return scatter_impl<double, uint32_t, true>(v, index, n, row_len, o, num_out, pr, n_skipped, w, negate, s);
+}
+
+}  // namespace det
+
+namespace det {
+
+size_t scatter_running_workspace(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
+    return rlayout(n, num_out, row_len, dt).total;
+}
+
+det_status scatter_running_launch(const void* values, const int32_t* index, int64_t n,
+                                  int64_t row_len, det_dtype dt, void* out, int64_t num_out,
+                                  void* prev, int64_t* n_skipped, void* ws, hipStream_t s) {
+    char* w = static_cast<char*>(ws);
+    if (dt == DET_F32)
+        return scatter_running_impl<float>(static_cast<const float*>(values), index, n, row_len,
+                                           static_cast<float*>(out), num_out,
+                                           static_cast<float*>(prev), n_skipped, w, s);
+    return scatter_running_impl<double>(static_cast<const double*>(values), index, n, row_len,
+                                        static_cast<double*>(out), num_out,
+                                        static_cast<double*>(prev), n_skipped, w, s);
 }
 
 }  // namespace det

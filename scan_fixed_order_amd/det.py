@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
     L.det_scatter_add.restype = i
     L.det_scatter_sub.argtypes = [p, p, i64, i64, i, p, i64, p, p, p, sz, p]
     L.det_scatter_sub.restype = i
+    L.det_scatter_add_running_workspace_size.argtypes = [i64, i64, i64, i]
+    L.det_scatter_add_running_workspace_size.restype = sz
+    L.det_scatter_add_running.argtypes = [p, p, i64, i64, i, p, i64, p, p, p, sz, p]
+    L.det_scatter_add_running.restype = i
     L.det_spec_version.argtypes, L.det_spec_version.restype = [], i
     L.det_spec_constants.argtypes = [ctypes.POINTER(i64)] * 4
     L.det_spec_constants.restype = None
@@ -180,6 +184,11 @@ def det_scatter_add_workspace_size(n: int, num_out: int, row_len: int, dtype_cod
     return lib().det_scatter_add_workspace_size(n, num_out, row_len, dtype_code)
 
 
+def det_scatter_add_running_workspace_size(n: int, num_out: int, row_len: int,
+                                           dtype_code: int) -> int:
+    return lib().det_scatter_add_running_workspace_size(n, num_out, row_len, dtype_code)
+
+
 def _scatter(entry: str, values: torch.Tensor, index: torch.Tensor, out: torch.Tensor,
              prev: Optional[torch.Tensor], n_skipped: Optional[torch.Tensor],
              ws: Optional[torch.Tensor]) -> torch.Tensor:
@@ -206,7 +215,9 @@ def _scatter(entry: str, values: torch.Tensor, index: torch.Tensor, out: torch.T
             raise ValueError("prev must match values")
     if n_skipped is not None and (n_skipped.dtype != torch.int64 or n_skipped.numel() < 1):
         raise ValueError("n_skipped must be an int64 tensor with one element")
-    w = _workspace(det_scatter_add_workspace_size(n, num_out, row_len, dt), values.device, ws)
+    size_fn = (det_scatter_add_running_workspace_size if entry == "det_scatter_add_running"
+               else det_scatter_add_workspace_size)
+    w = _workspace(size_fn(n, num_out, row_len, dt), values.device, ws)
     _check(getattr(lib(), entry)(_dev_ptr(values), _dev_ptr(index), n, row_len, dt, _dev_ptr(out),
                                  num_out, _dev_ptr(prev), _dev_ptr(n_skipped), _dev_ptr(w),
                                  w.numel(), _stream(values.device)), entry)
@@ -230,6 +241,18 @@ def det_scatter_sub(values: torch.Tensor, index: torch.Tensor, out: torch.Tensor
     """``out[index[i]] -= values[i]``: the values negated, then added in the fixed order of
     det_scatter_add (arguments as there); returns ``out``."""
     return _scatter("det_scatter_sub", values, index, out, prev, n_skipped, ws)
+
+
+def det_scatter_add_running(values: torch.Tensor, index: torch.Tensor, out: torch.Tensor,
+                            prev: torch.Tensor, n_skipped: Optional[torch.Tensor] = None,
+                            ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """det_scatter_add whose ``prev`` (required, shape of values) receives the running value:
+    the destination's initial value plus the earlier contributions (ascending source index),
+    summed by the exclusive segmented det_scan of the destination-grouped members; the first
+    member of a destination gets the initial value itself.  Returns ``out``."""
+    if prev is None:
+        raise ValueError("det_scatter_add_running needs prev")
+    return _scatter("det_scatter_add_running", values, index, out, prev, n_skipped, ws)
 
 
 class _Gather(torch.autograd.Function):

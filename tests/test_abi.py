@@ -105,6 +105,28 @@ def test_validation_errors_enqueue_nothing():
               NULL) == E_UNSUPPORTED
 
 
+def test_running_scatter_validation():
+    lib = det.lib()
+    ra = lib.det_scatter_add_running
+    o = ctypes.c_void_p(0x900000)
+    big = 1 << 30
+    assert lib.det_scatter_add_running_workspace_size(1 << 20, 1000, 1, 0) > \
+        lib.det_scatter_add_workspace_size(1 << 20, 1000, 1, 0) + (1 << 20) * 8
+    assert lib.det_scatter_add_running_workspace_size(10, 10, 0, 0) == 0
+    assert lib.det_scatter_add_running_workspace_size(10, 10, 65535 * 32 + 1, 0) == 0
+    assert ra(FAKE, FAKE, 10, 1, 0, o, 4, NULL, NULL, FAKE, big, NULL) == E_INVALID  # no prev
+    assert ra(FAKE, FAKE, 10, 1, 0, o, 4, ctypes.c_void_p(0x900000 + 4), NULL, FAKE, big,
+              NULL) == E_INVALID                                                  # prev aliases out
+    assert ra(FAKE, FAKE, 10, 1, 0, o, 4, ctypes.c_void_p(0x10000 + 8), NULL, FAKE, big,
+              NULL) == E_INVALID                                                  # prev aliases values
+    assert ra(FAKE, FAKE, 10, 65535 * 32 + 1, 0, o, 4, ctypes.c_void_p(0xA00000), NULL, FAKE,
+              big, NULL) == E_TOO_LARGE
+    assert ra(FAKE, FAKE, 10, 1, 2, o, 4, ctypes.c_void_p(0xA00000), NULL, FAKE, big,
+              NULL) == E_UNSUPPORTED                                              # int32
+    assert ra(FAKE, FAKE, 1000, 1, 0, o, 4, ctypes.c_void_p(0xA00000), NULL, FAKE, 64,
+              NULL) == E_WORKSPACE
+
+
 def test_alignment_is_checked():
     lib = det.lib()
     ws_odd = ctypes.c_void_p(0x10000 + 128)        # 128-byte aligned only
