@@ -173,6 +173,14 @@ def time_configs(det, workloads, dev, log, base_lib=None):
         w = ws_of(det.det_scatter_add_workspace_size(n, B, 1, 0))
         put(f"scatter f32 n=2^24 into {label}",
             lambda: det.det_scatter_add(v, bi, out, ws=w), 8.0 * n + 8.0 * B, n, 20)
+        if B == 65536 and label.startswith("65536"):
+            # the same with prev as the running value (values, index read; prev written)
+            pv = torch.empty_like(v)
+            w2 = ws_of(det.det_scatter_add_running_workspace_size(n, B, 1, 0))
+            put(f"scatter f32 n=2^24 into {label}, running prev",
+                lambda: det.det_scatter_add_running(v, bi, out, prev=pv, ws=w2),
+                12.0 * n + 8.0 * B, n, 10)
+            del pv, w2
     del v
     # scan: f32 and f64, inclusive/exclusive x forward/reverse; the inclusive forward scan
     # beside the ROCm library's (hipCUB DeviceScan::InclusiveSum) on the same input, for the
@@ -245,6 +253,13 @@ def time_configs(det, workloads, dev, log, base_lib=None):
     w = ws_of(det.det_scatter_add_workspace_size(src.shape[0], out0.shape[0], src.shape[1], 0))
     put("rows f32 2^16x256 into 2^14 rows", lambda: det.det_scatter_add(st, rt, ot, ws=w),
         4.0 * src.size + 4.0 * rows.size + 8.0 * out0.size, src.size, 20)
+    pr = torch.empty_like(st)
+    w = ws_of(det.det_scatter_add_running_workspace_size(src.shape[0], out0.shape[0],
+                                                         src.shape[1], 0))
+    put("rows f32 2^16x256 into 2^14 rows, running prev",
+        lambda: det.det_scatter_add_running(st, rt, ot, prev=pr, ws=w),
+        8.0 * src.size + 4.0 * rows.size + 8.0 * out0.size, src.size, 20)
+    del pr
     log("configs: segmented scan and rows timed")
     # large mixed-magnitude f64, n = 2^29: sum, scan, scatter into 2^20 Zipf(1.1) bins
     n = 1 << 29

@@ -41,6 +41,12 @@ det_status scan_launch(const void* x, void* y, int64_t n, det_dtype dt, unsigned
                        const int64_t* offs, int64_t nseg, void* ws, size_t ws_bytes,
                        hipStream_t s);
 
+// ncols scans of n elements each (column c: x + c * n -> y + c * n) sharing flags and offsets,
+// with the bits of ncols separate scan_launch calls; the workspace of one n-element scan.
+det_status scan_columns_launch(const void* x, void* y, int64_t n, int64_t ncols, det_dtype dt,
+                               unsigned flags, const int64_t* offs, int64_t nseg, void* ws,
+                               hipStream_t s);
+
 // ---- scatter-add
 size_t scatter_workspace(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt);
 // negate: every value enters negated (scatter-subtract)

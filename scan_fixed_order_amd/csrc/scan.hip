@@ -516,6 +516,7 @@ struct ScanArgs {
     const T* dummy;      // 256 bytes that the 16-byte loads of a non-vector run read instead
     const int64_t* k0;   // segmented: per tile, the first offset index at or above the tile
                          // (null: searched by the tile itself)
+    int64_t col_stride;  // k_scan_small: elements between the columns workgroups take in turn
     int ntiles;
     int nctr;            // tile counters in use: min(kCounters, grid)
     int rev;
@@ -827,23 +828,27 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     }
 }
 
-// Scans of at most kSmallTiles tiles, all in the first anchor interval: one workgroup walks the
-// tiles in order, keeping the tile totals in LDS, so there are no status words to clear, no
-// counters and no polls (one launch).  Tile j's trees are those of k_scan: W_j = PW(leaf t =
+// Scans that fit in the first anchor interval: one workgroup walks the tiles in order, keeping
+// the tile totals in LDS, so there are no status words to clear, no counters and no polls (one
+// launch).  Workgroup b scans column b: x and y start b * col_stride elements on, all columns
+// share n and the segment offsets.  Tile j's trees are those of k_scan: W_j = PW(leaf t =
 // Agg_t for t < j, else the identity) and WG = PW(identity leaves); the carry is the identity;
 // E = (CC + WG) + W_j.  The next tile's loads are issued before the current tile's readout.
 constexpr int kSmallTiles = 3;   // beyond 3 tiles the persistent kernel is faster on MI355X
 
 template <typename T, bool SEG, bool REV, bool EXCL>
-__global__ __launch_bounds__(256) void k_scan_small(ScanArgs<T> a) {
+__global__ __launch_bounds__(256) void k_scan_small(ScanArgs<T> a0) {
     __shared__ T s_park[kScanWaves][kPark];
     __shared__ T s_x[kScanWaves][kScanW];
     __shared__ uint32_t s_hbits[SEG ? kScanWaves : 1][kScanW];
     __shared__ uint32_t s_heads[2][SEG ? kHeadWords : 1];
     __shared__ Seg<T> s_tmp[2 * kScanWaves];
     __shared__ Seg<T> s_wtot[kScanWaves];
-    __shared__ Seg<T> s_agg[kSmallTiles];
+    __shared__ Seg<T> s_agg[kScanA];
 
+    ScanArgs<T> a = a0;
+    a.x += (int64_t)blockIdx.x * a0.col_stride;
+    a.y += (int64_t)blockIdx.x * a0.col_stride;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -946,6 +951,53 @@ Layout layout(int64_t n, det_dtype dt, int A, int A2) {
     return L;
 }
 
+// One k_scan_small launch over ncols columns (workgroup b: x + b * stride, y + b * stride).
+template <typename T>
+det_status scan_small(const T* x, T* y, int64_t n, int64_t ncols, int64_t stride, int mode0,
+                      const int64_t* offs, int64_t nseg, char* ws, const Layout& L, int A, int A2,
+                      hipStream_t s) {
+    ScanArgs<T> a{};
+    a.x = x;
+    a.y = y;
+    a.n = n;
+    a.offs = offs;
+    a.nseg = nseg;
+    a.dummy = reinterpret_cast<const T*>(ws + kDummyOff);
+    a.err = reinterpret_cast<uint32_t*>(ws + kErrOff);
+    a.ntiles = (int)L.ntiles;
+    a.rev = (mode0 & 2) ? 1 : 0;
+    a.excl = mode0 & 1;
+    a.A = A;
+    a.A2 = A2;
+    a.col_stride = stride;
+    if (offs && ncols > 1) {
+        // every column has the same heads: find each tile's first offset index once
+        int64_t* k0 = reinterpret_cast<int64_t*>(ws + L.k0_off);
+        KernelTimer kt("k_seg_first", s);
+        k_seg_first<<<(unsigned)((L.ntiles + 255) / 256), 256, 0, s>>>(
+            offs, nseg, n, (mode0 & 2) ? 1 : 0, L.ntiles, k0);
+        const det_status st = launch_status();
+        if (st != DET_SUCCESS) return st;
+        a.k0 = k0;
+    }
+    const void* fn = nullptr;
+    switch (mode0) {
+        case 0: fn = (const void*)k_scan_small<T, false, false, false>; break;
+        case 1: fn = (const void*)k_scan_small<T, false, false, true>; break;
+        case 2: fn = (const void*)k_scan_small<T, false, true, false>; break;
+        case 3: fn = (const void*)k_scan_small<T, false, true, true>; break;
+        case 4: fn = (const void*)k_scan_small<T, true, false, false>; break;
+        case 5: fn = (const void*)k_scan_small<T, true, false, true>; break;
+        case 6: fn = (const void*)k_scan_small<T, true, true, false>; break;
+        default: fn = (const void*)k_scan_small<T, true, true, true>; break;
+    }
+    void* args[] = {&a};
+    KernelTimer kt("k_scan_small", s);
+    if (hipLaunchKernel(fn, dim3((unsigned)ncols), dim3(256), args, 0, s) != hipSuccess)
+        return DET_ERROR_LAUNCH;
+    return launch_status();
+}
+
 template <typename T>
 det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t* offs,
                      int64_t nseg, char* ws, hipStream_t s) {
@@ -956,37 +1008,8 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32, A, A2);   // slot sizes
     const int mode0 = (offs ? 4 : 0) | ((flags & DET_SCAN_REVERSE) ? 2 : 0) |
                       ((flags & DET_SCAN_EXCLUSIVE) ? 1 : 0);
-    if (L.ntiles <= kSmallTiles && L.ntiles <= A) {
-        ScanArgs<T> a{};
-        a.x = x;
-        a.y = y;
-        a.n = n;
-        a.offs = offs;
-        a.nseg = nseg;
-        a.dummy = reinterpret_cast<const T*>(ws + kDummyOff);
-        a.err = reinterpret_cast<uint32_t*>(ws + kErrOff);
-        a.ntiles = (int)L.ntiles;
-        a.rev = (mode0 & 2) ? 1 : 0;
-        a.excl = mode0 & 1;
-        a.A = A;
-        a.A2 = A2;
-        const void* fn = nullptr;
-        switch (mode0) {
-            case 0: fn = (const void*)k_scan_small<T, false, false, false>; break;
-            case 1: fn = (const void*)k_scan_small<T, false, false, true>; break;
-            case 2: fn = (const void*)k_scan_small<T, false, true, false>; break;
-            case 3: fn = (const void*)k_scan_small<T, false, true, true>; break;
-            case 4: fn = (const void*)k_scan_small<T, true, false, false>; break;
-            case 5: fn = (const void*)k_scan_small<T, true, false, true>; break;
-            case 6: fn = (const void*)k_scan_small<T, true, true, false>; break;
-            default: fn = (const void*)k_scan_small<T, true, true, true>; break;
-        }
-        void* args[] = {&a};
-        KernelTimer kt("k_scan_small", s);
-        if (hipLaunchKernel(fn, dim3(1), dim3(256), args, 0, s) != hipSuccess)
-            return DET_ERROR_LAUNCH;
-        return launch_status();
-    }
+    if (L.ntiles <= kSmallTiles && L.ntiles <= A)
+        return scan_small<T>(x, y, n, 1, 0, mode0, offs, nseg, ws, L, A, A2, s);
     const int64_t words = (int64_t)(L.used / 8);
     int zg = (int)((words + 255) / 256);
     if (zg > 1024) zg = 1024;
@@ -1018,6 +1041,7 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     a.err = reinterpret_cast<uint32_t*>(ws + kErrOff);
     a.dummy = reinterpret_cast<const T*>(ws + kDummyOff);
     a.k0 = offs ? k0 : nullptr;
+    a.col_stride = 0;
     a.ntiles = (int)L.ntiles;
     a.rev = (flags & DET_SCAN_REVERSE) ? 1 : 0;
     a.excl = (flags & DET_SCAN_EXCLUSIVE) ? 1 : 0;
@@ -1063,6 +1087,28 @@ det_status scan_error(const void* ws, int32_t* out, hipStream_t s) {
     return launch_status();
 }
 
+// ncols scans of n elements that share the flags and segment offsets: column c reads
+// x + c * n and writes y + c * n.  Columns that fit in one anchor interval go in one launch,
+// a workgroup per column; longer ones are scanned one launch after another.
+template <typename T>
+det_status scan_cols_impl(const T* x, T* y, int64_t n, int64_t ncols, unsigned flags,
+                          const int64_t* offs, int64_t nseg, char* ws, hipStream_t s) {
+    if (n == 0 || ncols == 0) return DET_SUCCESS;
+    const LaunchOverride& ov = launch_override();
+    const int A = ov.scan_A ? ov.scan_A : kScanA;
+    const int A2 = ov.scan_A2 ? ov.scan_A2 : kScanA2;
+    const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32, A, A2);
+    const int mode0 = (offs ? 4 : 0) | ((flags & DET_SCAN_REVERSE) ? 2 : 0) |
+                      ((flags & DET_SCAN_EXCLUSIVE) ? 1 : 0);
+    if (ncols > 1 && L.ntiles <= A)
+        return scan_small<T>(x, y, n, ncols, n, mode0, offs, nseg, ws, L, A, A2, s);
+    for (int64_t c = 0; c < ncols; ++c) {
+        const det_status st = scan_impl<T>(x + c * n, y + c * n, n, flags, offs, nseg, ws, s);
+        if (st != DET_SUCCESS) return st;
+    }
+    return DET_SUCCESS;
+}
+
 size_t scan_workspace(int64_t n, det_dtype dt, unsigned flags, int64_t num_segments) {
     (void)flags;
     (void)num_segments;
@@ -1081,6 +1127,23 @@ det_status scan_launch(const void* x, void* y, int64_t n, det_dtype dt, unsigned
                                    flags, offs, nseg, static_cast<char*>(ws), s);
     return scan_impl<double>(static_cast<const double*>(x), static_cast<double*>(y), n, flags,
                              offs, nseg, static_cast<char*>(ws), s);
+}
+
+}  // namespace det
+
+namespace det {
+
+det_status scan_columns_launch(const void* x, void* y, int64_t n, int64_t ncols, det_dtype dt,
+                               unsigned flags, const int64_t* offs, int64_t nseg, void* ws,
+                               hipStream_t s) {
+    char* w = static_cast<char*>(ws);
+    if (dt == DET_F32)
+        return scan_cols_impl<float>(static_cast<const float*>(x), static_cast<float*>(y), n,
+                                     ncols, flags, offs, nseg, w, s);
+    if (dt == DET_F64)
+        return scan_cols_impl<double>(static_cast<const double*>(x), static_cast<double*>(y), n,
+                                      ncols, flags, offs, nseg, w, s);
+    return DET_ERROR_UNSUPPORTED;
 }
 
 }  // namespace det

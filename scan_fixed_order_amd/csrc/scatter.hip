@@ -932,6 +932,36 @@ __global__ __launch_bounds__(256) void k_group_gather(const T* __restrict__ valu
     }
 }
 
+// Scalar destinations (one column): G[s] = values[src[s]] for s < nvalid, +0.0 past them.
+template <typename T>
+__global__ __launch_bounds__(256) void k_group_gather1(const T* __restrict__ values,
+                                                       const uint32_t* __restrict__ src,
+                                                       const uint32_t* __restrict__ nvalid,
+                                                       int64_t n, T* __restrict__ G) {
+    const int64_t m = *nvalid;
+    for (int64_t sp = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; sp < n;
+         sp += (int64_t)gridDim.x * blockDim.x)
+        G[sp] = sp < m ? values[src[sp]] : T(0.0);
+}
+
+// Scalar destinations: prev[src[s]] = out[r] at r's first position, else out[r] + E[s].
+template <typename T>
+__global__ __launch_bounds__(256) void k_running_prev1(const uint32_t* __restrict__ K,
+                                                       const uint32_t* __restrict__ src,
+                                                       const uint32_t* __restrict__ off,
+                                                       const uint32_t* __restrict__ nvalid,
+                                                       const T* __restrict__ E,
+                                                       const T* __restrict__ out,
+                                                       T* __restrict__ prev) {
+    const int64_t m = *nvalid;
+    for (int64_t sp = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; sp < m;
+         sp += (int64_t)gridDim.x * blockDim.x) {
+        const uint32_t r = K[sp];
+        const T init = out[r];
+        prev[src[sp]] = off[r] == (uint32_t)sp ? init : init + E[sp];
+    }
+}
+
 // Offsets of the grouped array as the segmented scan takes them: o[b] = off[b] for b <= B
 // (destination b's members start at off[b]; off[B] = nvalid) and o[B + 1] = n (the skipped
 // sources, one more segment).
@@ -1237,21 +1267,30 @@ det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n
         k_offsets64<<<dim3((unsigned)g), dim3(256), 0, s>>>(off, num_out, n, o64);
     }
     const dim3 tg((unsigned)cdiv(n, 64), (unsigned)cdiv(row_len, 32));
+    int64_t g1 = cdiv(n, 256);
+    if (g1 > 16384) g1 = 16384;
     {
         KernelTimer kt("k_group_gather", s);
-        k_group_gather<T><<<tg, dim3(256), 0, s>>>(values, SRC, ctrl, n, row_len, G);
+        if (row_len == 1)
+            k_group_gather1<T><<<dim3((unsigned)g1), dim3(256), 0, s>>>(values, SRC, ctrl, n, G);
+        else
+            k_group_gather<T><<<tg, dim3(256), 0, s>>>(values, SRC, ctrl, n, row_len, G);
     }
     st = launch_status();
     if (st != DET_SUCCESS) return st;
     const size_t sbytes = scan_workspace(n, dt, DET_SCAN_EXCLUSIVE, num_out + 1);
-    for (int64_t c = 0; c < row_len; ++c) {
-        st = scan_launch(G + c * n, E + c * n, n, dt, DET_SCAN_EXCLUSIVE, o64, num_out + 1,
-                         ws + R.sws, sbytes, s);
-        if (st != DET_SUCCESS) return st;
-    }
+    (void)sbytes;
+    st = scan_columns_launch(G, E, n, row_len, dt, DET_SCAN_EXCLUSIVE, o64, num_out + 1,
+                             ws + R.sws, s);
+    if (st != DET_SUCCESS) return st;
     {
         KernelTimer kt("k_running_prev", s);
-        k_running_prev<T><<<tg, dim3(256), 0, s>>>(K, SRC, off, ctrl, n, row_len, E, out, prev);
+        if (row_len == 1)
+            k_running_prev1<T><<<dim3((unsigned)g1), dim3(256), 0, s>>>(K, SRC, off, ctrl, E, out,
+                                                                        prev);
+        else
+            k_running_prev<T><<<tg, dim3(256), 0, s>>>(K, SRC, off, ctrl, n, row_len, E, out,
+                                                       prev);
     }
     st = launch_status();
     if (st != DET_SUCCESS) return st;

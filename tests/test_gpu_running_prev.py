@@ -64,7 +64,9 @@ def test_one_contended_destination(dev, dtype):
 
 
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
-@pytest.mark.parametrize("n,B,d", [(5000, 300, 96), (20011, 997, 33), (3, 2, 1000)])
+@pytest.mark.parametrize("n,B,d", [(5000, 300, 96), (20011, 997, 33), (3, 2, 1000),
+                                   (300007, 50000, 2), (256 * 8192, 9, 2),
+                                   (256 * 8192 + 5, 9, 2)])
 def test_rows_parity(dev, dtype, n, B, d):
     run_case(dev, dtype, n, B, d, seed=d)
 
