@@ -240,8 +240,9 @@ __device__ __forceinline__ int digit_of(uint32_t key, uint32_t B, int shift) {
     return (int)((key >> shift) & 255u);
 }
 
-template <bool FIRST>
-__global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n,
+// KI: the type keys are read in (16-bit after a pass that wrote them so)
+template <bool FIRST, typename KI>
+__global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys, int64_t n,
                                                     const uint32_t* __restrict__ nvalid, uint32_t B,
                                                     int shift, int nb, int64_t nchunks, int H,
                                                     uint32_t* __restrict__ hist) {
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(256) void k_radix_hist(const uint32_t* __restrict__
             const int64_t p = base + i0 + k * 256 + threadIdx.x;
             // non-temporal: each key is read once here (0.21 -> 0.18 ms per pass at 2^28)
             kb[k] = (i0 + k * 256 + (int)threadIdx.x < H && p < m)
-                        ? __builtin_nontemporal_load(keys + p)
+                        ? (uint32_t)__builtin_nontemporal_load(keys + p)
                         : 0u;
         }
 #pragma unroll
@@ -299,8 +300,8 @@ struct RadixSmem {
 // A chunk's keys and payloads, loaded by thread (wave w, lane l) at positions
 // base + w * 64 * IPT + k * 64 + l.  FULL: the whole chunk is in range (no checks, so every
 // path issues the same loads).
-template <typename P, bool FIRST, bool ROWS, bool FULL>
-__device__ __forceinline__ void radix_load(const uint32_t* __restrict__ keys_in,
+template <typename P, bool FIRST, bool ROWS, bool FULL, typename KI>
+__device__ __forceinline__ void radix_load(const KI* __restrict__ keys_in,
                                            const P* __restrict__ pay_in, int64_t base, int64_t m,
                                            uint32_t (&key)[kItems<P>], P (&pay)[kItems<P>],
                                            int wave, int lane) {
@@ -309,7 +310,7 @@ __device__ __forceinline__ void radix_load(const uint32_t* __restrict__ keys_in,
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
         const int64_t p = p0 + k * 64;
-        key[k] = (FULL || p < m) ? keys_in[p] : 0u;
+        key[k] = (FULL || p < m) ? (uint32_t)keys_in[p] : 0u;
     }
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
@@ -431,10 +432,11 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
 // One chunk per workgroup, chunk xcd_chunk(b) for workgroup b: the dispatcher starts
 // workgroups in order, so the chunks an XCD holds at any moment are neighbours and their
 // writes into each bucket's region merge in its L2.
-// KO: the type keys are written in (uint16_t for the last pass when every valid key fits).
-template <typename P, bool FIRST, bool ROWS, typename KO>
+// KO: the type keys are written in, KI the type they are read in (uint16_t for passes after
+// the first when every valid key fits 16 bits).
+template <typename P, bool FIRST, bool ROWS, typename KO, typename KI>
 __global__ __launch_bounds__(256) void k_radix_scatter(
-    const uint32_t* __restrict__ keys_in, const P* __restrict__ pay_in,
+    const KI* __restrict__ keys_in, const P* __restrict__ pay_in,
     KO* __restrict__ keys_out, P* __restrict__ pay_out, int64_t n,
     const uint32_t* __restrict__ nvalid, uint32_t B, int shift, int64_t nchunks,
     const uint32_t* __restrict__ hist_ex) {
@@ -454,12 +456,12 @@ __global__ __launch_bounds__(256) void k_radix_scatter(
     uint32_t key[IPT];
     P pay[IPT];
     if (base + H <= m) {
-        radix_load<P, FIRST, ROWS, true>(keys_in, pay_in, base, m, key, pay, wave, lane);
+        radix_load<P, FIRST, ROWS, true, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
         __syncthreads();
         radix_rank_write<P, FIRST, ROWS, true, KO>(sm, key, pay, base, m, B, shift, off0, off1,
                                                keys_out, pay_out, tid, lane, wave);
     } else {
-        radix_load<P, FIRST, ROWS, false>(keys_in, pay_in, base, m, key, pay, wave, lane);
+        radix_load<P, FIRST, ROWS, false, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
         __syncthreads();
         radix_rank_write<P, FIRST, ROWS, false, KO>(sm, key, pay, base, m, B, shift, off0, off1,
                                                 keys_out, pay_out, tid, lane, wave);
@@ -1083,17 +1085,23 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
         const bool first = p == 0;
+        // with k16 every pass writes 16-bit keys (valid keys fit; the out-of-range ones, placed
+        // past the valid ones by the first pass, are never read again)
         const uint32_t* kin = first ? reinterpret_cast<const uint32_t*>(index) : keys[(p - 1) & 1];
+        const uint16_t* kin16 = reinterpret_cast<const uint16_t*>(kin);
         const P* pin = first ? pay_in0 : pay[(p - 1) & 1];
         const int nb = first ? kBuckets0 : 256;
         {
             KernelTimer kt("k_radix_hist", s);
             if (first)
-                k_radix_hist<true><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb, L.nchunks,
-                                                        (int)L.H, hist);
+                k_radix_hist<true, uint32_t><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb,
+                                                                  L.nchunks, (int)L.H, hist);
+            else if (k16)
+                k_radix_hist<false, uint16_t><<<grid, 256, 0, s>>>(kin16, n, ctrl, B, shift, nb,
+                                                                   L.nchunks, (int)L.H, hist);
             else
-                k_radix_hist<false><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb, L.nchunks,
-                                                         (int)L.H, hist);
+                k_radix_hist<false, uint32_t><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb,
+                                                                   L.nchunks, (int)L.H, hist);
         }
         // bucket offsets; the first pass also counts the keys in range into ctrl[0]
         det_status st = hist_offsets(hist, L.nchunks, nb, sums + 512, sums, first ? ctrl : nullptr, s);
@@ -1101,18 +1109,17 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
         KernelTimer kt("k_radix_scatter", s);
         uint32_t* ko = keys[p & 1];
         uint16_t* ko16 = reinterpret_cast<uint16_t*>(ko);
-        const bool last16 = k16 && p == passes - 1;
-        if (first && last16)
-            k_radix_scatter<P, true, ROWS, uint16_t><<<grid, 256, 0, s>>>(
+        if (first && k16)
+            k_radix_scatter<P, true, ROWS, uint16_t, uint32_t><<<grid, 256, 0, s>>>(
                 kin, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         else if (first)
-            k_radix_scatter<P, true, ROWS, uint32_t><<<grid, 256, 0, s>>>(
+            k_radix_scatter<P, true, ROWS, uint32_t, uint32_t><<<grid, 256, 0, s>>>(
                 kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
-        else if (last16)
-            k_radix_scatter<P, false, ROWS, uint16_t><<<grid, 256, 0, s>>>(
-                kin, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
+        else if (k16)
+            k_radix_scatter<P, false, ROWS, uint16_t, uint16_t><<<grid, 256, 0, s>>>(
+                kin16, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         else
-            k_radix_scatter<P, false, ROWS, uint32_t><<<grid, 256, 0, s>>>(
+            k_radix_scatter<P, false, ROWS, uint32_t, uint32_t><<<grid, 256, 0, s>>>(
                 kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         st = launch_status();
         if (st != DET_SUCCESS) return st;
@@ -1146,9 +1153,9 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
     }
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);   // [0] = number of valid keys
     uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
-    // scalar destinations that all fit 16 bits: the last pass writes 16-bit keys, which the
-    // destination offsets and the reduction read (out-of-range keys land past the valid ones
-    // and are never read)
+    // scalar destinations that all fit 16 bits: every pass writes 16-bit keys, which the next
+    // pass, the destination offsets and the reduction read (out-of-range keys land past the
+    // valid ones and are never read)
     const bool k16 = !ROWS && num_out <= 65536;
     const uint32_t* K = nullptr;
     const P* SP = nullptr;
