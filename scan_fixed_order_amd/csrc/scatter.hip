@@ -513,22 +513,29 @@ __global__ void k_write_skipped_all(int64_t* n_skipped, int64_t n) {
 // PW over p[0 .. len) (each element negated when NEG; the identity padding is not), len <= 256
 // NBLK (element 0 replaced by v0 when use_v0): NBLK blocks
 // of 256; lane l of block i holds elements 256 i + 4 l .. + 4 combined as (a0 + a1) + (a2 + a3),
-// then the wave butterfly; the NBLK block values meet in a log2(NBLK)-level tree (identity for
-// blocks past len), which is PW over 256 NBLK padded positions, the same value as over len.
-// The loads of G blocks are in flight together.  Uniform result.
+// then the wave butterfly; the block values meet in the log2(NBLK)-level tree (identity for
+// blocks past len), built as a binary counter of complete subtrees and folded right-nested at
+// the end, which is PW over 256 NBLK padded positions, the same value as over len.  The loads
+// of G blocks are in flight together.  Uniform result.
 template <typename T, int NBLK = 32, bool NEG = false>
 __device__ __forceinline__ T wave_pw_range(const T* __restrict__ p, int64_t len, int lane,
                                            bool use_v0, T v0) {
-    constexpr int G0 = sizeof(T) == 4 ? 16 : 8;
+    // blocks whose loads are in flight together: few enough registers that more workgroups
+    // fit per CU (f32 2^28 into 65,536 bins on MI355X: 16 blocks 0.40 ms, 8 0.36, 4 0.34;
+    // f64 2^27 into 2^20 bins: 8 blocks 0.68 ms, 4 0.69, 2 0.71)
+    constexpr int G0 = sizeof(T) == 4 ? 4 : 8;
     constexpr int G = G0 < NBLK ? G0 : NBLK;
-    T b[NBLK];
+    constexpr int LV = NBLK <= 2 ? 2 : NBLK <= 8 ? 4 : 6;   // stack levels (log2 NBLK + 1)
+    // complete subtrees of the block values pushed so far, by level (a binary counter): leaf
+    // L merges with the stack's top levels for the trailing ones of L, exactly the pairs of the
+    // NBLK-leaf tree
+    T stk[LV];
+#pragma unroll
+    for (int l = 0; l < LV; ++l) stk[l] = ident<T>();
+    int nleaf = 0;
 #pragma unroll
     for (int g0 = 0; g0 < NBLK; g0 += G) {
-        if ((int64_t)g0 * 256 >= len) {
-#pragma unroll
-            for (int i = 0; i < G; ++i) b[g0 + i] = ident<T>();
-            continue;
-        }
+        if ((int64_t)g0 * 256 >= len) break;
         T a[G][4];
 #pragma unroll
         for (int i = 0; i < G; ++i) {
@@ -540,19 +547,34 @@ __device__ __forceinline__ T wave_pw_range(const T* __restrict__ p, int64_t len,
         }
 #pragma unroll
         for (int i = 0; i < G; ++i) {
-            if (use_v0 && g0 + i == 0 && lane == 0) a[i][0] = v0;
-            b[g0 + i] = (int64_t)(g0 + i) * 256 < len
-                            ? wave_pw<T>((a[i][0] + a[i][1]) + (a[i][2] + a[i][3]))
-                            : ident<T>();
+            const int L = g0 + i;
+            if ((int64_t)L * 256 < len) {
+                if (use_v0 && L == 0 && lane == 0) a[i][0] = v0;
+                T v = wave_pw<T>((a[i][0] + a[i][1]) + (a[i][2] + a[i][3]));
+                const int tz = __builtin_ctz(~(unsigned)L);   // trailing ones of L
+#pragma unroll
+                for (int l = 0; l < LV; ++l)
+                    if (l < tz) v = stk[l] + v;
+#pragma unroll
+                for (int l = 0; l < LV; ++l)
+                    if (l == tz) stk[l] = v;
+                nleaf = L + 1;
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+    // the padded tree's value: the complete subtrees of nleaf's binary expansion folded
+    // right-nested (identity leaves change nothing)
+    T acc = ident<T>();
+    bool have = false;
 #pragma unroll
-    for (int w = NBLK; w > 1; w /= 2) {
-#pragma unroll
-        for (int i = 0; i < w / 2; ++i) b[i] = b[2 * i] + b[2 * i + 1];
+    for (int l = 0; l < LV; ++l) {
+        if ((nleaf >> l) & 1) {
+            acc = have ? stk[l] + acc : stk[l];
+            have = true;
+        }
     }
-    return b[0];
+    return acc;
 }
 
 // PW over p[0 .. len) for any len (element 0 replaced by v0 when use_v0): blocks of 8192
@@ -636,7 +658,7 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const KT* __restrict__ K,
     // destination's first and end positions (read once, by the thread that found the block)
     __shared__ uint32_t s_big[kSegD / 32 + 2][4];
     __shared__ uint32_t s_nbig;
-    __shared__ uint32_t s_key[kSegD];
+    __shared__ KT s_key[kSegD];
     __shared__ uint32_t s_prev;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t m = *nvalid;
@@ -658,16 +680,7 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const KT* __restrict__ K,
             q[i] = reinterpret_cast<const u32x4*>(K + lo)[i * 256 + tid];
 #pragma unroll
         for (int i = 0; i < kSegD / KPV / 256; ++i) {
-            if constexpr (sizeof(KT) == 4) {
-                reinterpret_cast<u32x4*>(s_key)[i * 256 + tid] = q[i];
-            } else {
-                // 8 keys: low and high halves of each word, in address order
-                const int e0 = (i * 256 + tid) * 8;
-                const u32x4 lo4 = {q[i].x & 0xffffu, q[i].x >> 16, q[i].y & 0xffffu, q[i].y >> 16};
-                const u32x4 hi4 = {q[i].z & 0xffffu, q[i].z >> 16, q[i].w & 0xffffu, q[i].w >> 16};
-                reinterpret_cast<u32x4*>(s_key + e0)[0] = lo4;
-                reinterpret_cast<u32x4*>(s_key + e0)[1] = hi4;
-            }
+            reinterpret_cast<u32x4*>(s_key)[i * 256 + tid] = q[i];
         }
     } else {
         for (int i = tid; i < (int)(hi - lo); i += 256) s_key[i] = K[lo + i];
