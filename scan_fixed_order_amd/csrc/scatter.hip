@@ -254,6 +254,38 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
     __syncthreads();
     const int64_t m = FIRST ? n : (int64_t)*nvalid;
     const int64_t base = (int64_t)blockIdx.x * H;
+    auto count = [&](uint32_t key, bool valid) {
+        const int d = digit_of<FIRST>(key, B, shift);
+        const uint64_t vm = __ballot(valid);
+        if (vm == 0ull) return;
+        const int first = __ffsll((long long)vm) - 1;
+        const int d0 = __shfl(d, first, 64);
+        if (__ballot(valid && d == d0) == vm) {
+            if (lane == first) atomicAdd(&cnt[wave][d0], (uint32_t)__popcll(vm));
+        } else if (valid) {
+            atomicAdd(&cnt[wave][d], 1u);
+        }
+    };
+    if constexpr (sizeof(KI) == 2) {
+        // 16-bit keys two to a 32-bit word (H is even and the keys 256-byte aligned, so a
+        // chunk's words start on its first key)
+        const uint32_t* kw = reinterpret_cast<const uint32_t*>(keys) + base / 2;
+        for (int i0 = 0; i0 < H / 2; i0 += 256 * 16) {
+            uint32_t wb[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int w = i0 + k * 256 + (int)threadIdx.x;
+                wb[k] = (w < H / 2 && base + 2 * w < m) ? __builtin_nontemporal_load(kw + w) : 0u;
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int w = i0 + k * 256 + (int)threadIdx.x;
+                const int64_t p = base + 2 * (int64_t)w;
+                count(wb[k] & 0xffffu, w < H / 2 && p < m);
+                count(wb[k] >> 16, w < H / 2 && p + 1 < m);
+            }
+        }
+    } else {
     // keys in batches of 16 per thread, all loads of a batch issued before the first count
     for (int i0 = 0; i0 < H; i0 += 256 * 16) {
         uint32_t kb[16];
@@ -268,18 +300,9 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int64_t p = base + i0 + k * 256 + threadIdx.x;
-            const bool valid = i0 + k * 256 + (int)threadIdx.x < H && p < m;
-            const int d = digit_of<FIRST>(kb[k], B, shift);
-            const uint64_t vm = __ballot(valid);
-            if (vm == 0ull) continue;
-            const int first = __ffsll((long long)vm) - 1;
-            const int d0 = __shfl(d, first, 64);
-            if (__ballot(valid && d == d0) == vm) {
-                if (lane == first) atomicAdd(&cnt[wave][d0], (uint32_t)__popcll(vm));
-            } else if (valid) {
-                atomicAdd(&cnt[wave][d], 1u);
-            }
+            count(kb[k], i0 + k * 256 + (int)threadIdx.x < H && p < m);
         }
+    }
     }
     __syncthreads();
     for (int d = threadIdx.x; d < nb; d += 256)
