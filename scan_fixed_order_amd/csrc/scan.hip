@@ -280,20 +280,14 @@ __device__ __forceinline__ int64_t heads_lo(int64_t n, bool rev, int64_t F0) {
 
 // Bit b of s_heads marks flipped position F0 + b (b in [0, T]) as a segment head.
 // Forward: heads are the offsets o < n.  Reverse: flipped position n - o for offsets o > 0
-// (the last element of every non-empty segment).  k0_known: the first offset index for the
-// tile when computed before the scan, else -1 (searched here).
+// (the last element of every non-empty segment).  Used by single-workgroup scans; the others
+// take the same bits from a bitmap built before the scan (k_mark_heads).
 __device__ void build_heads(const int64_t* __restrict__ offs, int64_t nseg, int64_t n, bool rev,
-                            int64_t F0, uint32_t* s_heads, int tid, int64_t k0_known) {
+                            int64_t F0, uint32_t* s_heads, int tid) {
     for (int i = tid; i < kHeadWords; i += 256) s_heads[i] = 0u;
     const int64_t lo_v = heads_lo(n, rev, F0);
     const int64_t hi_v = !rev ? ((F0 + kT < n - 1) ? F0 + kT : n - 1) : n - F0;
-    int64_t k0;
-    if (k0_known >= 0) {
-        k0 = k0_known;
-        __syncthreads();   // the heads are cleared before any thread sets one
-    } else {
-        k0 = wg_lower_bound(offs, nseg + 1, lo_v, tid);   // ends with a barrier
-    }
+    const int64_t k0 = wg_lower_bound(offs, nseg + 1, lo_v, tid);   // ends with a barrier
     for (int64_t base = k0;; base += 256) {
         const int64_t k = base + tid;
         bool in = false;
@@ -514,8 +508,8 @@ struct ScanArgs {
     uint32_t* ticket;    // kCounters tile counters, kCounterStride words apart
     uint32_t* err;       // raised when a wait hit the spin bound
     const T* dummy;      // 256 bytes that the 16-byte loads of a non-vector run read instead
-    const int64_t* k0;   // segmented: per tile, the first offset index at or above the tile
-                         // (null: searched by the tile itself)
+    const uint32_t* hbits;  // segmented: bit f marks flipped position f as a segment head
+                            // (null: each tile searches the offsets itself)
     int64_t col_stride;  // k_scan_small: elements between the columns workgroups take in turn
     int ntiles;
     int nctr;            // tile counters in use: min(kCounters, grid)
@@ -525,16 +519,45 @@ struct ScanArgs {
     int A2;              // intervals per super-interval (likewise)
 };
 
+// A tile's head words from the bitmap: word i of tile j is bitmap word 256 j + i, i in [0, 256]
+// (word 256 is the next tile's first).  Every thread loads two words, the second the same for
+// all, and a tile past the end reads tile 0's (never used), so every path issues the same loads.
+struct HeadWords {
+    uint32_t w, w256;
+};
+
+template <typename T, bool SEG>
+__device__ __forceinline__ HeadWords load_head_words(const ScanArgs<T>& a, int j, int tid) {
+    HeadWords h{0u, 0u};
+    if constexpr (SEG) {
+        if (a.hbits) {
+            const size_t t = j < a.ntiles ? (size_t)j * (kHeadWords - 1) : 0;
+            h.w = a.hbits[t + tid];
+            h.w256 = a.hbits[t + (kHeadWords - 1)];
+        }
+    }
+    return h;
+}
+
 // Local part of one tile once its runs are in registers: segment heads, lane-serial prefixes
 // (left in r), in-wave and wave-level Kogge-Stone; returns the tile total.
 template <typename T, bool SEG, bool REV>
 __device__ __forceinline__ Seg<T> tile_local(const ScanArgs<T>& a, int j, T (&r)[kV], uint32_t& hb,
                                              Seg<T>& P, Seg<T>& p, uint32_t* s_heads,
-                                             Seg<T>* s_wtot, int tid, int lane, int wave) {
+                                             Seg<T>* s_wtot, int tid, int lane, int wave,
+                                             HeadWords hw) {
     const int64_t F0 = (int64_t)j * kT;
     if constexpr (SEG) {
-        build_heads(a.offs, a.nseg, a.n, REV, F0, s_heads, tid, a.k0 ? a.k0[j] : -1);
-        hb = s_heads[wave * 64 + lane];
+        if (a.hbits) {
+            // the words were loaded with the tile; the barrier below publishes them before any
+            // readout looks at another thread's word
+            s_heads[tid] = hw.w;
+            if (tid == 0) s_heads[kHeadWords - 1] = hw.w256;
+            hb = hw.w;
+        } else {
+            build_heads(a.offs, a.nseg, a.n, REV, F0, s_heads, tid);
+            hb = s_heads[wave * 64 + lane];
+        }
     } else {
         hb = 0u;
     }
@@ -754,12 +777,13 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     if (c >= a.ntiles) return;
     T r[kV];
     load_tile<T, REV>(a, c, wave, r, lane0);
+    HeadWords hwc = load_head_words<T, SEG>(a, c, tid);
     uint32_t claimed = 0u;
     if (tid == 0) claimed = claim_issue(a.ticket, ctr);
     uint32_t hbc;
     Seg<T> Pc, pc;
-    Seg<T> aggc =
-        tile_local<T, SEG, REV>(a, c, r, hbc, Pc, pc, s_heads[0], s_wtot, tid, lane0, wave);
+    Seg<T> aggc = tile_local<T, SEG, REV>(a, c, r, hbc, Pc, pc, s_heads[0], s_wtot, tid, lane0,
+                                          wave, hwc);
     if (tid == 0) {
         publish<T>(a.agg + (size_t)c * SW, aggc);
         s_tick[1] = ticket_tile(claimed, ctr, nc);
@@ -771,6 +795,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     int u = __builtin_amdgcn_readfirstlane(s_tick[1]);
     // u's loads (a tile past the end reads element n - 1 and is never used)
     load_tile<T, REV>(a, u, wave, r, lane0);
+    HeadWords hwu = load_head_words<T, SEG>(a, u, tid);
     if (tid == 0 && u < a.ntiles) claimed = claim_issue(a.ticket, ctr);
     LookBack lbc = look_back_of(c, a.A, a.A2);
     GCache<T> gc{seg_ident<T>(), 0, -1};
@@ -788,7 +813,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
         Seg<T> Pu = seg_ident<T>(), pu = seg_ident<T>(), aggu = seg_ident<T>();
         if (have_u) {
             aggu = tile_local<T, SEG, REV>(a, u, r, hbu, Pu, pu, s_heads[par ^ 1], s_wtot, tid,
-                                           lane, wave);
+                                           lane, wave, hwu);
             if (tid == 0) publish<T>(a.agg + (size_t)u * SW, aggu);
             publish_interval_total<SEG, T>(a, u, aggu, s_tmp, tid, lane, wave);
         }
@@ -804,6 +829,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
         // ---- v: loads issued now, consumed in the next iteration; the tile after v claimed
         T rv[kV];
         load_tile<T, REV>(a, v, wave, rv, lane);
+        const HeadWords hwv = load_head_words<T, SEG>(a, v, tid);
         if (tid == 0 && have_v) claimed = claim_issue(a.ticket, ctr);
 
         // ---- c: finish the look-back, store from LDS
@@ -816,6 +842,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
         if constexpr (SEG) s_hbits[wave][lane] = hbu;
 #pragma unroll
         for (int k = 0; k < kV; ++k) r[k] = rv[k];
+        hwu = hwv;
         Pc = Pu;
         pc = pu;
         aggc = aggu;
@@ -857,17 +884,19 @@ __global__ __launch_bounds__(256) void k_scan_small(ScanArgs<T> a0) {
     const uint32_t* hbs = s_hbits[SEG ? wave : 0];
     T r[kV], rn[kV];
     load_tile<T, REV>(a, 0, wave, r, lane);
+    HeadWords hw = load_head_words<T, SEG>(a, 0, tid);
     for (int j = 0; j < a.ntiles; ++j) {
         uint32_t hb;
         Seg<T> P, p;
-        const Seg<T> agg =
-            tile_local<T, SEG, REV>(a, j, r, hb, P, p, s_heads[j & 1], s_wtot, tid, lane, wave);
+        const Seg<T> agg = tile_local<T, SEG, REV>(a, j, r, hb, P, p, s_heads[j & 1], s_wtot, tid,
+                                                   lane, wave, hw);
         if (tid == 0) s_agg[j] = agg;
         park_runs<T>(pk, r, lane);
         if constexpr (SEG) s_hbits[wave][lane] = hb;
         __syncthreads();
         // the next tile's loads (past the end: element n - 1, never used)
         load_tile<T, REV>(a, j + 1, wave, rn, lane);
+        const HeadWords hwn = load_head_words<T, SEG>(a, j + 1, tid);
         // W_j; for tile 0 every leaf is the identity, whose tree is the identity; WG is a tree
         // of identity leaves here, the identity
         Seg<T> Wj = seg_ident<T>();
@@ -888,24 +917,43 @@ __global__ __launch_bounds__(256) void k_scan_small(ScanArgs<T> a0) {
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < kV; ++k) r[k] = rn[k];
+        hw = hwn;
     }
 }
 
-// Segmented scans: for every tile, the first offset index at or above the lowest position
-// the tile covers (the binary search each tile would otherwise run on its critical path).
-__global__ __launch_bounds__(256) void k_seg_first(const int64_t* __restrict__ offs, int64_t nseg,
-                                                   int64_t n, int rev, int64_t ntiles,
-                                                   int64_t* __restrict__ k0) {
-    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (j >= ntiles) return;
-    const int64_t target = heads_lo(n, rev != 0, j * (int64_t)kT);
-    int64_t lo = 0, hi = nseg + 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (offs[mid] < target) lo = mid + 1;
-        else hi = mid;
+// Segment heads as a bitmap over flipped positions, built before a segmented scan on a
+// cleared bitmap: forward, bit o for every offset o < n; reverse, bit n - o for every offset
+// o > 0 (offsets outside [0, n] are ignored, so broken preconditions never write out of
+// range).  A thread per offset; lanes on the same 32-bit word (neighbours, the offsets being
+// sorted) OR their bits together and the first of them sets them with one atomic OR (order-
+// free, so the bitmap does not depend on timing).
+__global__ __launch_bounds__(256) void k_mark_heads(const int64_t* __restrict__ offs,
+                                                    int64_t nseg, int64_t n, int rev,
+                                                    uint32_t* __restrict__ bits) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t k0 = (int64_t)blockIdx.x * blockDim.x; k0 <= nseg;
+         k0 += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t k = k0 + threadIdx.x;
+        int64_t f = -1;
+        if (k <= nseg) {
+            const int64_t o = offs[k];
+            if (!rev) {
+                if (o >= 0 && o < n) f = o;
+            } else {
+                if (o > 0 && o <= n) f = n - o;
+            }
+        }
+        const int64_t w = f >= 0 ? (f >> 5) : -1;
+        uint32_t m = f >= 0 ? (1u << (f & 31)) : 0u;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t mo = __shfl_down(m, d, 64);
+            const int64_t wo = __shfl_down(w, d, 64);
+            if (lane + d < 64 && wo == w) m |= mo;
+        }
+        const int64_t wp = __shfl_up(w, 1, 64);
+        if (w >= 0 && (lane == 0 || wp != w)) atomicOr(&bits[w], m);
     }
-    k0[j] = lo;
 }
 
 __global__ void k_copy_error(const uint32_t* err, int32_t* out) {
@@ -926,13 +974,15 @@ constexpr size_t kHeader = kDummyOff + 256;
 
 struct Layout {
     int64_t ntiles, nq, nQ;
-    size_t agg_off, g_off, carry_off, used, k0_off, total;
+    size_t agg_off, g_off, carry_off, used, hb_off, hb_words, clear, total;
 };
 
 // Slots for tile totals, interval totals and super-interval carries.  The reservation assumes
 // the smallest anchors (A = A2 = 1) so the test hook never needs a larger workspace; only the
 // part the current constants use is cleared.
-Layout layout(int64_t n, det_dtype dt, int A, int A2) {
+// seg: room for the head bitmap (256 words per tile and one more), right after the status
+// slots in use, so one clear covers both
+Layout layout(int64_t n, det_dtype dt, int A, int A2, bool seg) {
     Layout L;
     const size_t sw = dt == DET_F64 ? 2 : 1;
     L.ntiles = (n + kT - 1) / kT;
@@ -944,11 +994,34 @@ Layout layout(int64_t n, det_dtype dt, int A, int A2) {
     L.g_off = L.agg_off + tile_bytes;
     L.carry_off = L.g_off + tile_bytes;
     L.used = L.carry_off + round_up((size_t)(L.nQ + 1) * sw * 8, 256);
-    L.k0_off = L.carry_off + worst;                       // segmented: a first index per tile
-    L.total = L.k0_off + round_up((size_t)L.ntiles * 8, 256);
-    // the cleared range must cover the interval totals in use as well
-    (void)L.nq;
+    L.hb_off = L.used;
+    L.hb_words = seg ? (size_t)L.ntiles * (kHeadWords - 1) + 1 : 0;
+    L.clear = L.hb_off + round_up(L.hb_words * 4, 256);
+    L.total = L.clear > L.carry_off + worst ? L.clear : L.carry_off + worst;
     return L;
+}
+
+// Clears words [from, to) of the workspace (bytes, multiples of 8), then, for a segmented scan,
+// marks the heads into the bitmap of L.
+det_status clear_and_mark(char* ws, size_t from, size_t to, const Layout& L,
+                          const int64_t* offs, int64_t nseg, int64_t n, bool rev, hipStream_t s) {
+    const int64_t words = (int64_t)((to - from) / 8);
+    if (words > 0) {
+        int zg = (int)((words + 255) / 256);
+        if (zg > 1024) zg = 1024;
+        KernelTimer kt("k_zero_words", s);
+        k_zero_words<<<zg, 256, 0, s>>>(reinterpret_cast<uint64_t*>(ws + from), words);
+    }
+    det_status st = launch_status();
+    if (st != DET_SUCCESS || !offs) return st;
+    int64_t g = (nseg + 1 + 255) / 256;
+    if (g > 16384) g = 16384;
+    {
+        KernelTimer kt("k_mark_heads", s);
+        k_mark_heads<<<(unsigned)g, 256, 0, s>>>(offs, nseg, n, rev ? 1 : 0,
+                                                 reinterpret_cast<uint32_t*>(ws + L.hb_off));
+    }
+    return launch_status();
 }
 
 // One k_scan_small launch over ncols columns (workgroup b: x + b * stride, y + b * stride).
@@ -971,14 +1044,11 @@ det_status scan_small(const T* x, T* y, int64_t n, int64_t ncols, int64_t stride
     a.A2 = A2;
     a.col_stride = stride;
     if (offs && ncols > 1) {
-        // every column has the same heads: find each tile's first offset index once
-        int64_t* k0 = reinterpret_cast<int64_t*>(ws + L.k0_off);
-        KernelTimer kt("k_seg_first", s);
-        k_seg_first<<<(unsigned)((L.ntiles + 255) / 256), 256, 0, s>>>(
-            offs, nseg, n, (mode0 & 2) ? 1 : 0, L.ntiles, k0);
-        const det_status st = launch_status();
+        // every column has the same heads: one bitmap, loaded with each tile's data
+        const det_status st = clear_and_mark(ws, L.hb_off, L.clear, L, offs, nseg, n,
+                                             (mode0 & 2) != 0, s);
         if (st != DET_SUCCESS) return st;
-        a.k0 = k0;
+        a.hbits = reinterpret_cast<const uint32_t*>(ws + L.hb_off);
     }
     const void* fn = nullptr;
     switch (mode0) {
@@ -1005,29 +1075,15 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     const LaunchOverride& ov = launch_override();
     const int A = ov.scan_A ? ov.scan_A : kScanA;
     const int A2 = ov.scan_A2 ? ov.scan_A2 : kScanA2;
-    const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32, A, A2);   // slot sizes
+    const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32, A, A2, offs != nullptr);
     const int mode0 = (offs ? 4 : 0) | ((flags & DET_SCAN_REVERSE) ? 2 : 0) |
                       ((flags & DET_SCAN_EXCLUSIVE) ? 1 : 0);
     if (L.ntiles <= kSmallTiles && L.ntiles <= A)
         return scan_small<T>(x, y, n, 1, 0, mode0, offs, nseg, ws, L, A, A2, s);
-    const int64_t words = (int64_t)(L.used / 8);
-    int zg = (int)((words + 255) / 256);
-    if (zg > 1024) zg = 1024;
-    {
-        KernelTimer kt("k_zero_words", s);
-        k_zero_words<<<zg, 256, 0, s>>>(reinterpret_cast<uint64_t*>(ws), words);
-    }
-    det_status st = launch_status();
+    // status slots and counters (and the head bitmap) cleared, heads marked
+    det_status st = clear_and_mark(ws, 0, L.clear, L, offs, nseg, n,
+                                   (flags & DET_SCAN_REVERSE) != 0, s);
     if (st != DET_SUCCESS) return st;
-    int64_t* k0 = reinterpret_cast<int64_t*>(ws + L.k0_off);
-    if (offs) {
-        KernelTimer kt("k_seg_first", s);
-        const int64_t g = (L.ntiles + 255) / 256;
-        k_seg_first<<<(unsigned)g, 256, 0, s>>>(offs, nseg, n, (flags & DET_SCAN_REVERSE) ? 1 : 0,
-                                                L.ntiles, k0);
-        st = launch_status();
-        if (st != DET_SUCCESS) return st;
-    }
     ScanArgs<T> a;
     a.x = x;
     a.y = y;
@@ -1040,7 +1096,7 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     a.ticket = reinterpret_cast<uint32_t*>(ws);
     a.err = reinterpret_cast<uint32_t*>(ws + kErrOff);
     a.dummy = reinterpret_cast<const T*>(ws + kDummyOff);
-    a.k0 = offs ? k0 : nullptr;
+    a.hbits = offs ? reinterpret_cast<const uint32_t*>(ws + L.hb_off) : nullptr;
     a.col_stride = 0;
     a.ntiles = (int)L.ntiles;
     a.rev = (flags & DET_SCAN_REVERSE) ? 1 : 0;
@@ -1097,7 +1153,7 @@ det_status scan_cols_impl(const T* x, T* y, int64_t n, int64_t ncols, unsigned f
     const LaunchOverride& ov = launch_override();
     const int A = ov.scan_A ? ov.scan_A : kScanA;
     const int A2 = ov.scan_A2 ? ov.scan_A2 : kScanA2;
-    const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32, A, A2);
+    const Layout L = layout(n, sizeof(T) == 8 ? DET_F64 : DET_F32, A, A2, offs != nullptr);
     const int mode0 = (offs ? 4 : 0) | ((flags & DET_SCAN_REVERSE) ? 2 : 0) |
                       ((flags & DET_SCAN_EXCLUSIVE) ? 1 : 0);
     if (ncols > 1 && L.ntiles <= A)
@@ -1111,8 +1167,7 @@ det_status scan_cols_impl(const T* x, T* y, int64_t n, int64_t ncols, unsigned f
 
 size_t scan_workspace(int64_t n, det_dtype dt, unsigned flags, int64_t num_segments) {
     (void)flags;
-    (void)num_segments;
-    return layout(n, dt, 1, 1).total;
+    return layout(n, dt, 1, 1, num_segments > 0).total;
 }
 
 det_status scan_launch(const void* x, void* y, int64_t n, det_dtype dt, unsigned flags,
