@@ -36,6 +36,13 @@ constexpr int kBuckets0 = 257;  // first pass: 256 digits + the out-of-range buc
 // scattered writes leave mostly whole lines.
 template <typename P>
 constexpr int kItems = sizeof(P) == 4 ? 32 : 16;
+// Waves per radix-scatter workgroup: 8 waves of 16 items (f32 payloads) need about 112 VGPRs,
+// so a CU holds two such workgroups (16 waves) where 4 waves of 32 items needed about 190 and
+// held 8 waves (f32 2^28 into 65,536 bins on MI355X: 0.80 -> 0.74 ms per pass, same ranks).
+constexpr int kRadixNW = 8;
+constexpr int kRadixNT = 64 * kRadixNW;
+template <typename P>
+constexpr int kRadixIPT = 256 * kItems<P> / kRadixNT;   // items per thread
 
 // Workgroup b runs on XCD b mod 8 (round-robin dispatch); give each XCD a contiguous range of
 // chunks, so the writes of consecutive chunks into a bucket's region meet in one L2 and leave
@@ -65,7 +72,8 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* s4) {
     return t;
 }
 
-// exclusive prefix over the 256 threads (integers: exact in any order); *total = sum
+// exclusive prefix over the NW * 64 threads (integers: exact in any order); *total = sum
+template <int NW = 4>
 __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s4, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     uint32_t inc = v;
@@ -75,9 +83,13 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s4
     }
     if (lane == 63) s4[wave] = inc;
     __syncthreads();
-    uint32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += s4[w];
-    *total = s4[0] + s4[1] + s4[2] + s4[3];
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        if (w < wave) before += s4[w];
+        all += s4[w];
+    }
+    *total = all;
     __syncthreads();
     return before + inc - v;
 }
@@ -314,10 +326,10 @@ template <typename P>
 struct RadixSmem {
     uint32_t keys[256 * kItems<P>];
     P pay[256 * kItems<P>];
-    uint32_t cnt[4][kBuckets0];   // per-wave digit counters, then wave offsets
+    uint32_t cnt[kRadixNW][kBuckets0];   // per-wave digit counters, then wave offsets
     uint32_t dstart[kBuckets0];
     int64_t gbase[kBuckets0];
-    uint32_t s4[4];
+    uint32_t s4[kRadixNW];
 };
 
 // A chunk's keys and payloads, loaded by thread (wave w, lane l) at positions
@@ -326,9 +338,9 @@ struct RadixSmem {
 template <typename P, bool FIRST, bool ROWS, bool FULL, typename KI>
 __device__ __forceinline__ void radix_load(const KI* __restrict__ keys_in,
                                            const P* __restrict__ pay_in, int64_t base, int64_t m,
-                                           uint32_t (&key)[kItems<P>], P (&pay)[kItems<P>],
+                                           uint32_t (&key)[kRadixIPT<P>], P (&pay)[kRadixIPT<P>],
                                            int wave, int lane) {
-    constexpr int IPT = kItems<P>;
+    constexpr int IPT = kRadixIPT<P>;
     const int64_t p0 = base + (int64_t)wave * 64 * IPT + lane;
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
@@ -355,14 +367,15 @@ __device__ __forceinline__ void radix_load(const KI* __restrict__ keys_in,
 // Integers only, so exact.  Leaves every barrier it passes balanced; ends with the LDS counters
 // cleared for the next chunk.
 template <typename P, bool FIRST, bool ROWS, bool FULL, typename KO>
-__device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_t (&key)[kItems<P>],
-                                                 const P (&pay)[kItems<P>], int64_t base, int64_t m,
+__device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_t (&key)[kRadixIPT<P>],
+                                                 const P (&pay)[kRadixIPT<P>], int64_t base, int64_t m,
                                                  uint32_t B, int shift, uint32_t off0,
                                                  uint32_t off1, KO* __restrict__ keys_out,
                                                  P* __restrict__ pay_out, int tid, int lane,
                                                  int wave) {
-    constexpr int IPT = kItems<P>;
-    constexpr int H = 256 * IPT;
+    constexpr int IPT = kRadixIPT<P>;
+    constexpr int H = 256 * kItems<P>;
+    constexpr int NT = kRadixNT;
     constexpr int BITS = FIRST ? 9 : 8;
     constexpr int NB = FIRST ? kBuckets0 : 256;
     uint32_t rk[IPT];
@@ -391,10 +404,10 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
     __syncthreads();
     // per digit: wave offsets (exclusive over waves) and the chunk's count
     uint32_t tot = 0;
-    {
+    if (tid < 256) {
         uint32_t run = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < kRadixNW; ++w) {
             const uint32_t cw = sm.cnt[w][tid];
             sm.cnt[w][tid] = run;
             run += cw;
@@ -403,7 +416,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         if (NB > 256 && tid == 0) {
             uint32_t r2 = 0;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < kRadixNW; ++w) {
                 const uint32_t cw = sm.cnt[w][256];
                 sm.cnt[w][256] = r2;
                 r2 += cw;
@@ -411,9 +424,11 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         }
     }
     uint32_t total;
-    const uint32_t ds = block_excl_scan_u32(tot, sm.s4, &total);
-    sm.dstart[tid] = ds;
-    sm.gbase[tid] = (int64_t)off0 - (int64_t)ds;
+    const uint32_t ds = block_excl_scan_u32<kRadixNW>(tot, sm.s4, &total);
+    if (tid < 256) {
+        sm.dstart[tid] = ds;
+        sm.gbase[tid] = (int64_t)off0 - (int64_t)ds;
+    }
     if (NB > 256 && tid == 0) {
         sm.dstart[256] = total;
         sm.gbase[256] = (int64_t)off1 - (int64_t)total;
@@ -429,12 +444,12 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         }
     }
     __syncthreads();
-    for (int i = tid; i < 4 * kBuckets0; i += 256) (&sm.cnt[0][0])[i] = 0u;
+    for (int i = tid; i < kRadixNW * kBuckets0; i += NT) (&sm.cnt[0][0])[i] = 0u;
     if constexpr (FULL) {
         // a fixed number of stores, so a later wait on loads issued before them stays partial
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
-            const int i = k * 256 + tid;
+            const int i = k * NT + tid;
             const uint32_t kk = sm.keys[i];
             const int64_t g = sm.gbase[digit_of<FIRST>(kk, B, shift)] + i;
             keys_out[g] = (KO)kk;
@@ -442,7 +457,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         }
     } else {
         const int cntc = (int)((m - base) < H ? (m - base) : H);
-        for (int i = tid; i < cntc; i += 256) {
+        for (int i = tid; i < cntc; i += NT) {
             const uint32_t kk = sm.keys[i];
             const int64_t g = sm.gbase[digit_of<FIRST>(kk, B, shift)] + i;
             keys_out[g] = (KO)kk;
@@ -458,13 +473,13 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
 // KO: the type keys are written in, KI the type they are read in (uint16_t for passes after
 // the first when every valid key fits 16 bits).
 template <typename P, bool FIRST, bool ROWS, typename KO, typename KI>
-__global__ __launch_bounds__(256) void k_radix_scatter(
+__global__ __launch_bounds__(kRadixNT) void k_radix_scatter(
     const KI* __restrict__ keys_in, const P* __restrict__ pay_in,
     KO* __restrict__ keys_out, P* __restrict__ pay_out, int64_t n,
     const uint32_t* __restrict__ nvalid, uint32_t B, int shift, int64_t nchunks,
     const uint32_t* __restrict__ hist_ex) {
-    constexpr int IPT = kItems<P>;
-    constexpr int H = 256 * IPT;
+    constexpr int IPT = kRadixIPT<P>;
+    constexpr int H = 256 * kItems<P>;
     constexpr int NB = FIRST ? kBuckets0 : 256;
     __shared__ RadixSmem<P> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -473,9 +488,9 @@ __global__ __launch_bounds__(256) void k_radix_scatter(
     const int64_t base = c * H;
     if (base >= m) return;
     // this chunk's bucket offsets, fetched with the keys
-    const uint32_t off0 = hist_ex[c * NB + tid];
+    const uint32_t off0 = tid < 256 ? hist_ex[c * NB + tid] : 0u;
     const uint32_t off1 = (NB > 256 && tid == 0) ? hist_ex[c * NB + 256] : 0u;
-    for (int i = tid; i < 4 * kBuckets0; i += 256) (&sm.cnt[0][0])[i] = 0u;
+    for (int i = tid; i < kRadixNW * kBuckets0; i += kRadixNT) (&sm.cnt[0][0])[i] = 0u;
     uint32_t key[IPT];
     P pay[IPT];
     if (base + H <= m) {
@@ -1146,16 +1161,16 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
         uint32_t* ko = keys[p & 1];
         uint16_t* ko16 = reinterpret_cast<uint16_t*>(ko);
         if (first && k16)
-            k_radix_scatter<P, true, ROWS, uint16_t, uint32_t><<<grid, 256, 0, s>>>(
+            k_radix_scatter<P, true, ROWS, uint16_t, uint32_t><<<grid, kRadixNT, 0, s>>>(
                 kin, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         else if (first)
-            k_radix_scatter<P, true, ROWS, uint32_t, uint32_t><<<grid, 256, 0, s>>>(
+            k_radix_scatter<P, true, ROWS, uint32_t, uint32_t><<<grid, kRadixNT, 0, s>>>(
                 kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         else if (k16)
-            k_radix_scatter<P, false, ROWS, uint16_t, uint16_t><<<grid, 256, 0, s>>>(
+            k_radix_scatter<P, false, ROWS, uint16_t, uint16_t><<<grid, kRadixNT, 0, s>>>(
                 kin16, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         else
-            k_radix_scatter<P, false, ROWS, uint32_t, uint32_t><<<grid, 256, 0, s>>>(
+            k_radix_scatter<P, false, ROWS, uint32_t, uint32_t><<<grid, kRadixNT, 0, s>>>(
                 kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         st = launch_status();
         if (st != DET_SUCCESS) return st;
