@@ -36,13 +36,17 @@ constexpr int kBuckets0 = 257;  // first pass: 256 digits + the out-of-range buc
 // scattered writes leave mostly whole lines.
 template <typename P>
 constexpr int kItems = sizeof(P) == 4 ? 32 : 16;
-// Waves per radix-scatter workgroup: 8 waves of 16 items (f32 payloads) need about 112 VGPRs,
-// so a CU holds two such workgroups (16 waves) where 4 waves of 32 items needed about 190 and
-// held 8 waves (f32 2^28 into 65,536 bins on MI355X: 0.80 -> 0.74 ms per pass, same ranks).
-constexpr int kRadixNW = 8;
-constexpr int kRadixNT = 64 * kRadixNW;
+// Waves per radix-scatter workgroup: for 4-byte payloads 8 waves of 16 items need about 112
+// VGPRs, so a CU holds two such workgroups (16 waves) where 4 waves of 32 items needed about
+// 190 and held 8 waves (f32 2^28 into 65,536 bins on MI355X: 0.80 -> 0.74 ms per pass, same
+// ranks); 8-byte payloads keep 4 waves of 16 (8 waves: f64 2^29 into 2^20 Zipf bins 2.50 ->
+// 2.65 ms per pass).
 template <typename P>
-constexpr int kRadixIPT = 256 * kItems<P> / kRadixNT;   // items per thread
+constexpr int kRadixNW = sizeof(P) == 4 ? 8 : 4;
+template <typename P>
+constexpr int kRadixNT = 64 * kRadixNW<P>;
+template <typename P>
+constexpr int kRadixIPT = 256 * kItems<P> / kRadixNT<P>;   // items per thread
 
 // Workgroup b runs on XCD b mod 8 (round-robin dispatch); give each XCD a contiguous range of
 // chunks, so the writes of consecutive chunks into a bucket's region meet in one L2 and leave
@@ -307,8 +311,18 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
             if (__builtin_amdgcn_ballot_w64(!same) == 0ull) {
                 if (lane == 0) atomicAdd(&cnt[wave][dref], (uint32_t)(64 * NK));
             } else {
+                // row by row: a row on one digit (skewed keys) is added with one atomic rather
+                // than 64 on the same counter
 #pragma unroll
-                for (int k = 0; k < NK; ++k) atomicAdd(&cnt[wave][digit_of<FIRST>(kk[k], B, shift)], 1u);
+                for (int k = 0; k < NK; ++k) {
+                    const int d = digit_of<FIRST>(kk[k], B, shift);
+                    const int d0 = __builtin_amdgcn_readfirstlane(d);
+                    if (__builtin_amdgcn_ballot_w64(d != d0) == 0ull) {
+                        if (lane == 0) atomicAdd(&cnt[wave][d0], 64u);
+                    } else {
+                        atomicAdd(&cnt[wave][d], 1u);
+                    }
+                }
             }
         } else {
 #pragma unroll
@@ -328,10 +342,10 @@ template <typename P>
 struct RadixSmem {
     uint32_t keys[256 * kItems<P>];
     P pay[256 * kItems<P>];
-    uint32_t cnt[kRadixNW][kBuckets0];   // per-wave digit counters, then wave offsets
+    uint32_t cnt[kRadixNW<P>][kBuckets0];   // per-wave digit counters, then wave offsets
     uint32_t dstart[kBuckets0];
     int64_t gbase[kBuckets0];
-    uint32_t s4[kRadixNW];
+    uint32_t s4[kRadixNW<P>];
 };
 
 // A chunk's keys and payloads, loaded by thread (wave w, lane l) at positions
@@ -377,7 +391,8 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
                                                  int wave) {
     constexpr int IPT = kRadixIPT<P>;
     constexpr int H = 256 * kItems<P>;
-    constexpr int NT = kRadixNT;
+    constexpr int NT = kRadixNT<P>;
+    constexpr int NW = kRadixNW<P>;
     constexpr int BITS = FIRST ? 9 : 8;
     constexpr int NB = FIRST ? kBuckets0 : 256;
     uint32_t rk[IPT];
@@ -409,7 +424,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
     if (tid < 256) {
         uint32_t run = 0;
 #pragma unroll
-        for (int w = 0; w < kRadixNW; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const uint32_t cw = sm.cnt[w][tid];
             sm.cnt[w][tid] = run;
             run += cw;
@@ -418,7 +433,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         if (NB > 256 && tid == 0) {
             uint32_t r2 = 0;
 #pragma unroll
-            for (int w = 0; w < kRadixNW; ++w) {
+            for (int w = 0; w < NW; ++w) {
                 const uint32_t cw = sm.cnt[w][256];
                 sm.cnt[w][256] = r2;
                 r2 += cw;
@@ -426,7 +441,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         }
     }
     uint32_t total;
-    const uint32_t ds = block_excl_scan_u32<kRadixNW>(tot, sm.s4, &total);
+    const uint32_t ds = block_excl_scan_u32<NW>(tot, sm.s4, &total);
     if (tid < 256) {
         sm.dstart[tid] = ds;
         sm.gbase[tid] = (int64_t)off0 - (int64_t)ds;
@@ -446,7 +461,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         }
     }
     __syncthreads();
-    for (int i = tid; i < kRadixNW * kBuckets0; i += NT) (&sm.cnt[0][0])[i] = 0u;
+    for (int i = tid; i < NW * kBuckets0; i += NT) (&sm.cnt[0][0])[i] = 0u;
     if constexpr (FULL) {
         // a fixed number of stores, so a later wait on loads issued before them stays partial
 #pragma unroll
@@ -475,7 +490,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
 // KO: the type keys are written in, KI the type they are read in (uint16_t for passes after
 // the first when every valid key fits 16 bits).
 template <typename P, bool FIRST, bool ROWS, typename KO, typename KI>
-__global__ __launch_bounds__(kRadixNT) void k_radix_scatter(
+__global__ __launch_bounds__(kRadixNT<P>) void k_radix_scatter(
     const KI* __restrict__ keys_in, const P* __restrict__ pay_in,
     KO* __restrict__ keys_out, P* __restrict__ pay_out, int64_t n,
     const uint32_t* __restrict__ nvalid, uint32_t B, int shift, int64_t nchunks,
@@ -492,7 +507,7 @@ __global__ __launch_bounds__(kRadixNT) void k_radix_scatter(
     // this chunk's bucket offsets, fetched with the keys
     const uint32_t off0 = tid < 256 ? hist_ex[c * NB + tid] : 0u;
     const uint32_t off1 = (NB > 256 && tid == 0) ? hist_ex[c * NB + 256] : 0u;
-    for (int i = tid; i < kRadixNW * kBuckets0; i += kRadixNT) (&sm.cnt[0][0])[i] = 0u;
+    for (int i = tid; i < kRadixNW<P> * kBuckets0; i += kRadixNT<P>) (&sm.cnt[0][0])[i] = 0u;
     uint32_t key[IPT];
     P pay[IPT];
     if (base + H <= m) {
@@ -1163,16 +1178,16 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
         uint32_t* ko = keys[p & 1];
         uint16_t* ko16 = reinterpret_cast<uint16_t*>(ko);
         if (first && k16)
-            k_radix_scatter<P, true, ROWS, uint16_t, uint32_t><<<grid, kRadixNT, 0, s>>>(
+            k_radix_scatter<P, true, ROWS, uint16_t, uint32_t><<<grid, kRadixNT<P>, 0, s>>>(
                 kin, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         else if (first)
-            k_radix_scatter<P, true, ROWS, uint32_t, uint32_t><<<grid, kRadixNT, 0, s>>>(
+            k_radix_scatter<P, true, ROWS, uint32_t, uint32_t><<<grid, kRadixNT<P>, 0, s>>>(
                 kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         else if (k16)
-            k_radix_scatter<P, false, ROWS, uint16_t, uint16_t><<<grid, kRadixNT, 0, s>>>(
+            k_radix_scatter<P, false, ROWS, uint16_t, uint16_t><<<grid, kRadixNT<P>, 0, s>>>(
                 kin16, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         else
-            k_radix_scatter<P, false, ROWS, uint32_t, uint32_t><<<grid, kRadixNT, 0, s>>>(
+            k_radix_scatter<P, false, ROWS, uint32_t, uint32_t><<<grid, kRadixNT<P>, 0, s>>>(
                 kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
         st = launch_status();
         if (st != DET_SUCCESS) return st;

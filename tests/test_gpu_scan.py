@@ -73,6 +73,8 @@ def test_segment_edge_layouts(dev):
         np.array([0, 0, 0, n, n]),                               # empty segments at both ends
         np.array([0, T - 1, T, T + 1, 2 * T, n]),                # heads around tile borders
         np.concatenate([[0], np.arange(32, n, 32), [n]]),        # heads at lane starts
+        np.concatenate([np.repeat(np.arange(0, n, 3), 2), [n]]),  # every offset twice (empty
+                                                                  # segments between dense heads)
     ]
     for offs in layouts:
         for excl, rev in MODES:
