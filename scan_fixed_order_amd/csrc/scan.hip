@@ -513,17 +513,28 @@ __device__ __forceinline__ void readout_excl(T* __restrict__ y, int64_t n, int64
         y[k] = excl_value<T, SEG, REV>(n, F0, fw, k, pk, xs, hbs, s_heads);
     for (int64_t k = Z + lane; k < hi; k += 64)
         y[k] = excl_value<T, SEG, REV>(n, F0, fw, k, pk, xs, hbs, s_heads);
-    const int64_t ngroups = (Z - A) / GW;   // at most 2048 / GW
+    const int ngroups = (int)((Z - A) / GW);   // at most 2048 / GW
+    // wave element read for address A + m: forward e = e0 + m, reverse e = e0 - m (e0 small);
+    // its segment-head bit, when segmented: flipped position - F0 = hoff + e + 1
+    const int e0 = REV ? (int)(n - 2 - fw - A) : (int)(A - 1 - fw);
+    const int hoff = (int)(fw - F0);
+    T* const yA = y + A;
 #pragma unroll
     for (int r = 0; r < kWaveElems / (64 * (int)GW); ++r) {
-        const int64_t gi = (int64_t)r * 64 + lane;
+        const int gi = r * 64 + lane;
         if (gi < ngroups) {
-            const int64_t g = A + GW * gi;
             T v[GW];
 #pragma unroll
-            for (int k = 0; k < (int)GW; ++k)
-                v[k] = excl_value<T, SEG, REV>(n, F0, fw, g + k, pk, xs, hbs, s_heads);
-            nt_store16<T>(y + g, v);
+            for (int k = 0; k < (int)GW; ++k) {
+                const int e = REV ? e0 - ((int)GW * gi + k) : e0 + ((int)GW * gi + k);
+                T val = combine_at<T, SEG>(pk, xs, hbs, e);
+                if constexpr (SEG) {
+                    const int bit = hoff + e + 1;
+                    if ((s_heads[bit >> 5] >> (bit & 31)) & 1u) val = T(0.0);
+                }
+                v[k] = val;
+            }
+            nt_store16<T>(yA + (int64_t)GW * gi, v);
         }
     }
 }
