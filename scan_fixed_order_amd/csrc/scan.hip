@@ -26,9 +26,12 @@
 // counters are cleared by a small kernel before each scan.
 //
 // Segmented scans run the pair operator (f1 | f2, f2 ? b : a + b) through the same dataflow;
-// head flags of a tile come from a workgroup-parallel search of the offsets.  Reverse scans
-// read and write through mirrored indices (n - 1 - f); exclusive scans store each inclusive
-// value one position later (and +0.0 at position 0 and at segment heads).
+// the head flags come from a bitmap marked before the scan (k_mark_heads), each tile loading
+// its 257 words with its data (a scan of at most 3 tiles searches the offsets instead).
+// Reverse scans read and write through mirrored indices (n - 1 - f); exclusive scans store
+// each inclusive value one position later (and +0.0 at position 0 and at segment heads).
+// Tiles are loaded coalesced and turned into lane runs through LDS; every output is written
+// with 16-byte non-temporal stores.
 #include <type_traits>
 
 #include "det_device.h"

@@ -11,16 +11,20 @@
 //   prev   optional snapshot prev[i] = out[index[i]] before anything changes;
 //   sort   stable LSD radix sort of (key, payload) with 8-bit digits; the first pass also
 //          splits off out-of-range keys into a 257th bucket at the end, and later passes only
-//          see the valid prefix.  Payload = the value (row_len 1) or the source row (rows).
-//          Per pass: per-chunk digit histogram, integer exclusive scan, then each workgroup
-//          ranks its chunk stably (wave ballots + per-wave digit counters), stages it in LDS
-//          in digit order and writes contiguous runs;
+//          see the valid prefix.  Payload = the value (row_len 1) or the source row (rows and
+//          the running prev).  Keys travel as 16 bits when every destination fits.  Per pass:
+//          per-chunk digit histogram, integer exclusive scan, then each workgroup ranks its
+//          chunk stably (wave ballots + per-wave digit counters), stages it in LDS in digit
+//          order and writes contiguous runs;
 //   bins   off[b] = first sorted position with key >= b (binary search per bin);
 //   reduce a destination's members are cut at local ranks that are multiples of D (D = 8192
 //          values, or 64 rows).  Each block is a subtree of PW; one pass reduces every block
 //          (a lane per block of at most 32 values, a wave per larger block) and applies
 //          destinations with one block; a second pass combines the block values of longer
 //          destinations by the same tree and applies them.
+// The running prev (det_scatter_add_running) adds, between sort and reduce: the grouped values
+// gathered column by column, the exclusive segmented det_scan of each column (one segment per
+// destination), and prev written from it and the old values.
 #include "det_device.h"
 #include "det_internal.h"
 
