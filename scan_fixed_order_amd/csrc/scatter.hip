@@ -159,14 +159,20 @@ __global__ __launch_bounds__(256) void k_hist_colscan(uint32_t* __restrict__ csu
 }
 
 // tot[d] <- keys with a digit below d (d < nb <= 257; thread 0 also handles d = 256)
-__global__ __launch_bounds__(256) void k_hist_digitscan(uint32_t* __restrict__ tot, int nb) {
+// ident: set to 1 when one bucket holds every key (the pass is then the identity permutation)
+__global__ __launch_bounds__(256) void k_hist_digitscan(uint32_t* __restrict__ tot, int nb,
+                                                        uint32_t* __restrict__ ident) {
     __shared__ uint32_t s4[4];
     const int t = threadIdx.x;
     const uint32_t v = tot[t];
+    const uint32_t v256 = nb > 256 ? tot[256] : 0u;
     uint32_t total;
     const uint32_t ex = block_excl_scan_u32(v, s4, &total);
+    const uint32_t grand = total + v256;
+    const int one = __syncthreads_or(v == grand || v256 == grand);
     tot[t] = ex;
     if (nb > 256 && t == 0) tot[256] = total;
+    if (t == 0) *ident = one ? 1u : 0u;
 }
 
 __global__ __launch_bounds__(256) void k_hist_apply(uint32_t* __restrict__ hist, int64_t nrows,
@@ -205,15 +211,24 @@ constexpr int64_t kSmallHistRows = 512;
 
 __global__ __launch_bounds__(256) void k_hist_offsets_small(uint32_t* __restrict__ hist,
                                                             int64_t nrows, int nb,
-                                                            uint32_t* __restrict__ valid) {
+                                                            uint32_t* __restrict__ valid,
+                                                            uint32_t* __restrict__ ident) {
     __shared__ uint32_t s4[4];
+    __shared__ uint32_t s_c256;
     const int t = threadIdx.x;
     const bool extra = nb > 256 && t == 0;
-    uint32_t c0 = 0;
+    uint32_t c0 = 0, c256 = 0;
 #pragma unroll 8
-    for (int64_t r = 0; r < nrows; ++r) c0 += hist[r * nb + t];
+    for (int64_t r = 0; r < nrows; ++r) {
+        c0 += hist[r * nb + t];
+        if (extra) c256 += hist[r * nb + 256];
+    }
+    if (t == 0) s_c256 = c256;
     uint32_t total;
-    uint32_t run0 = block_excl_scan_u32(c0, s4, &total);
+    uint32_t run0 = block_excl_scan_u32(c0, s4, &total);   // its barriers publish s_c256
+    const uint32_t grand = total + s_c256;
+    const int one = __syncthreads_or(c0 == grand || s_c256 == grand);
+    if (t == 0) *ident = one ? 1u : 0u;
     uint32_t run1 = total;
 #pragma unroll 8
     for (int64_t r = 0; r < nrows; ++r) {
@@ -234,18 +249,19 @@ __global__ void k_copy_word(const uint32_t* __restrict__ src, uint32_t* __restri
 }
 
 // csum needs nb * nrb words, tot nb words (nb <= 257).  valid (first pass only): receives the
-// number of keys in range (the offset of the out-of-range bucket in chunk 0).
+// number of keys in range (the offset of the out-of-range bucket in chunk 0).  ident: 1 when
+// one bucket holds every key, else 0.
 det_status hist_offsets(uint32_t* hist, int64_t nrows, int nb, uint32_t* csum, uint32_t* tot,
-                        uint32_t* valid, hipStream_t s) {
+                        uint32_t* valid, uint32_t* ident, hipStream_t s) {
     KernelTimer kt("k_hist_offsets", s);
     if (nrows <= kSmallHistRows) {
-        k_hist_offsets_small<<<1, 256, 0, s>>>(hist, nrows, nb, valid);
+        k_hist_offsets_small<<<1, 256, 0, s>>>(hist, nrows, nb, valid, ident);
         return launch_status();
     }
     const int64_t nrb = cdiv(nrows, kRowBlk);
     k_hist_colsums<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum);
     k_hist_colscan<<<dim3((unsigned)nb), dim3(256), 0, s>>>(csum, nrb, tot);
-    k_hist_digitscan<<<1, 256, 0, s>>>(tot, nb);
+    k_hist_digitscan<<<1, 256, 0, s>>>(tot, nb, ident);
     k_hist_apply<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum, tot);
     if (valid) k_copy_word<<<1, 1, 0, s>>>(hist + 256, valid);
     return launch_status();
@@ -498,7 +514,7 @@ __global__ __launch_bounds__(kRadixNT<P>) void k_radix_scatter(
     const KI* __restrict__ keys_in, const P* __restrict__ pay_in,
     KO* __restrict__ keys_out, P* __restrict__ pay_out, int64_t n,
     const uint32_t* __restrict__ nvalid, uint32_t B, int shift, int64_t nchunks,
-    const uint32_t* __restrict__ hist_ex) {
+    const uint32_t* __restrict__ hist_ex, const uint32_t* __restrict__ ident) {
     constexpr int IPT = kRadixIPT<P>;
     constexpr int H = 256 * kItems<P>;
     constexpr int NB = FIRST ? kBuckets0 : 256;
@@ -508,6 +524,22 @@ __global__ __launch_bounds__(kRadixNT<P>) void k_radix_scatter(
     const int64_t c = xcd_chunk(blockIdx.x, nchunks);
     const int64_t base = c * H;
     if (base >= m) return;
+    if (*ident) {
+        // one bucket holds every key: the stable pass leaves every item where it is
+        uint32_t key[IPT];
+        P pay[IPT];
+        radix_load<P, FIRST, ROWS, false, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
+        const int64_t p0 = base + (int64_t)wave * 64 * IPT + lane;
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int64_t p = p0 + k * 64;
+            if (p < m) {
+                keys_out[p] = (KO)key[k];
+                pay_out[p] = pay[k];
+            }
+        }
+        return;
+    }
     // this chunk's bucket offsets, fetched with the keys
     const uint32_t off0 = tid < 256 ? hist_ex[c * NB + tid] : 0u;
     const uint32_t off1 = (NB > 256 && tid == 0) ? hist_ex[c * NB + 256] : 0u;
@@ -1176,23 +1208,25 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
                                                                    L.nchunks, (int)L.H, hist);
         }
         // bucket offsets; the first pass also counts the keys in range into ctrl[0]
-        det_status st = hist_offsets(hist, L.nchunks, nb, sums + 512, sums, first ? ctrl : nullptr, s);
+        uint32_t* ident = ctrl + 16 + p;   // one word per pass (at most 4 passes)
+        det_status st = hist_offsets(hist, L.nchunks, nb, sums + 512, sums, first ? ctrl : nullptr,
+                                     ident, s);
         if (st != DET_SUCCESS) return st;
         KernelTimer kt("k_radix_scatter", s);
         uint32_t* ko = keys[p & 1];
         uint16_t* ko16 = reinterpret_cast<uint16_t*>(ko);
         if (first && k16)
             k_radix_scatter<P, true, ROWS, uint16_t, uint32_t><<<grid, kRadixNT<P>, 0, s>>>(
-                kin, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
+                kin, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         else if (first)
             k_radix_scatter<P, true, ROWS, uint32_t, uint32_t><<<grid, kRadixNT<P>, 0, s>>>(
-                kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
+                kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         else if (k16)
             k_radix_scatter<P, false, ROWS, uint16_t, uint16_t><<<grid, kRadixNT<P>, 0, s>>>(
-                kin16, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
+                kin16, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         else
             k_radix_scatter<P, false, ROWS, uint32_t, uint32_t><<<grid, kRadixNT<P>, 0, s>>>(
-                kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist);
+                kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         st = launch_status();
         if (st != DET_SUCCESS) return st;
     }
