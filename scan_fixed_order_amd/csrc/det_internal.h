@@ -42,10 +42,12 @@ det_status scan_launch(const void* x, void* y, int64_t n, det_dtype dt, unsigned
                        hipStream_t s);
 
 // ncols scans of n elements each (column c: x + c * n -> y + c * n) sharing flags and offsets,
-// with the bits of ncols separate scan_launch calls; the workspace of one n-element scan.
+// with the bits of ncols separate scan_launch calls; ws: the workspace of one n-element scan;
+// cagg: scan_columns_agg_bytes(n, ncols) more bytes (tile totals of every column), 256-aligned.
 det_status scan_columns_launch(const void* x, void* y, int64_t n, int64_t ncols, det_dtype dt,
                                unsigned flags, const int64_t* offs, int64_t nseg, void* ws,
-                               hipStream_t s);
+                               void* cagg, hipStream_t s);
+size_t scan_columns_agg_bytes(int64_t n, int64_t ncols);
 
 // ---- scatter-add
 size_t scatter_workspace(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt);

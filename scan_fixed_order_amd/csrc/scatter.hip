@@ -1325,7 +1325,7 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
 // values, and then out reduced exactly as det_scatter_add reduces it.
 struct RLayout {
     SLayout S;
-    size_t o64, G, E, sws, total;
+    size_t o64, G, E, sws, cagg, total;
 };
 
 RLayout rlayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
@@ -1342,6 +1342,7 @@ RLayout rlayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
     R.G = take(cells);
     R.E = take(cells);
     R.sws = take(scan_workspace(n > 0 ? n : 1, dt, DET_SCAN_EXCLUSIVE, num_out + 1));
+    R.cagg = take(scan_columns_agg_bytes(n > 0 ? n : 1, row_len));
     R.total = o;
     return R;
 }
@@ -1394,7 +1395,7 @@ det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n
     const size_t sbytes = scan_workspace(n, dt, DET_SCAN_EXCLUSIVE, num_out + 1);
     (void)sbytes;
     st = scan_columns_launch(G, E, n, row_len, dt, DET_SCAN_EXCLUSIVE, o64, num_out + 1,
-                             ws + R.sws, s);
+                             ws + R.sws, ws + R.cagg, s);
     if (st != DET_SUCCESS) return st;
     {
         KernelTimer kt("k_running_prev", s);
