@@ -334,43 +334,8 @@ __device__ __forceinline__ bool aligned16(const T* p) {
 // draining the queue.  No streaming hint: consecutive loads of a lane share cache lines.
 template <typename T, bool REV>
 __device__ __forceinline__ void load_run(const T* __restrict__ x, int64_t n, int64_t fw, bool vec,
-                                         const T* __restrict__ dummy, T (&r)[kV], int lane,
-                                         bool coal = false) {
+                                         const T* __restrict__ dummy, T (&r)[kV], int lane) {
     const int64_t f0 = fw + (int64_t)lane * kV;
-    if (coal) {
-        // the wave's 2048 elements in memory order, 16 bytes per lane per load, coalesced:
-        // r[g * G + i] = x[reg0 + (g * 64 + lane) * G + i] (G elements per 16 bytes), turned
-        // into runs by runs_from_lds; a wave that is not whole or not aligned loads the dummy
-        // line and then its run by elements, already in run order.  (Each lane loading its own
-        // 128-byte run touches 64 lines per load instruction; coalesced, a load covers 1 KiB:
-        // on MI355X at 2^28 the exclusive f32 scan went 0.45 -> 0.42 ms, the segmented one
-        // 0.49 -> 0.46 ms, f64 0.39 -> 0.38 ms, the inclusive f32 scan unchanged.)
-        constexpr int G = 16 / (int)sizeof(T);
-        const int64_t reg0 = REV ? n - fw - kWaveElems : fw;
-        const v4_t<T>* q4 = reinterpret_cast<const v4_t<T>*>(vec ? x + reg0 : dummy);
-#pragma unroll
-        for (int g = 0; g < kV / G; ++g) {
-            const int idx = vec ? g * 64 + lane : (g & 15);
-            if constexpr (sizeof(T) == 4) {
-                const v4_t<T> q = q4[idx];
-                r[4 * g] = q.x; r[4 * g + 1] = q.y; r[4 * g + 2] = q.z; r[4 * g + 3] = q.w;
-            } else {
-                const f64x2 q = reinterpret_cast<const f64x2*>(q4)[idx];
-                r[2 * g] = q.x; r[2 * g + 1] = q.y;
-            }
-        }
-        if (!vec) {
-            const T id = ident<T>();
-#pragma unroll
-            for (int k = 0; k < kV; ++k) {
-                const int64_t f = f0 + k;
-                const int64_t fc = f < n ? f : n - 1;
-                const T v = x[REV ? n - 1 - fc : fc];
-                r[k] = (f < n) ? v : id;
-            }
-        }
-        return;
-    }
     // forward: run = x[f0 .. f0 + 32); reverse: original x[n - f0 - 32 .. n - f0) backwards
     const T* p = vec ? (REV ? x + (n - f0 - kV) : x + f0) : dummy;
     if constexpr (sizeof(T) == 4) {
@@ -451,8 +416,14 @@ __device__ __forceinline__ T combine_at(const T* pk, const T* xs, const uint32_t
     return xs[L] + sv;
 }
 
+template <typename T, bool SEG, bool REV, bool EXCL>
+__device__ __forceinline__ void readout_range(T* __restrict__ y, int64_t n, int64_t F0, int64_t fw,
+                                              const T* pk, const T* xs, const uint32_t* hbs,
+                                              const uint32_t* s_heads, int lane);
+
 // Whole-wave readout, inclusive: flipped positions fw .. fw + 2047 to y.  16-byte
-// non-temporal stores where the wave is in range and aligned, else element stores.
+// non-temporal stores where the wave is in range and aligned, else readout_range (its aligned
+// interior by 16-byte stores, the ends by elements).
 template <typename T, bool SEG, bool REV>
 __device__ __forceinline__ void readout_incl(T* __restrict__ y, int64_t n, int64_t fw, const T* pk,
                                              const T* xs, const uint32_t* hbs, int lane) {
@@ -470,42 +441,41 @@ __device__ __forceinline__ void readout_incl(T* __restrict__ y, int64_t n, int64
             nt_store16<T>(base + o, v);
         }
     } else {
-        const int64_t left = n - fw;
-        const int valid = left < 0 ? 0 : (left < kWaveElems ? (int)left : kWaveElems);
-#pragma unroll 8
-        for (int r = 0; r < kWaveElems / 64; ++r) {
-            const int e = r * 64 + lane;
-            if (e < valid) y[REV ? (n - 1 - fw) - e : fw + e] = combine_at<T, SEG>(pk, xs, hbs, e);
-        }
+        // a partial or unaligned wave: aligned interior with 16-byte stores, ends by elements
+        readout_range<T, SEG, REV, false>(y, n, fw, fw, pk, xs, hbs, nullptr, lane);
     }
 }
 
-// Whole-wave readout, exclusive: the inclusive value of flipped position f goes to f + 1
-// (+0.0 where f + 1 is a segment head).  The wave's output is one contiguous range of original
-// addresses; its 16-byte-aligned interior is written with 16-byte non-temporal stores, the at
-// most 3 + 3 elements at its ends with element stores.
-template <typename T, bool SEG, bool REV>
-__device__ __forceinline__ T excl_value(int64_t n, int64_t F0, int64_t fw, int64_t addr,
-                                       const T* pk, const T* xs, const uint32_t* hbs,
-                                       const uint32_t* s_heads) {
+// Readout of a wave's range at any alignment: the output value of flipped position f is the
+// inclusive value of f - SH (SH = 1 exclusive, 0 inclusive), +0.0 where an exclusive scan's f
+// is a segment head.  The flipped positions fw + SH .. fw + 2047 + SH, clipped to n - 1, are
+// one contiguous range of original addresses; its 16-byte-aligned interior is written with
+// 16-byte non-temporal stores, the at most 3 + 3 elements at its ends with element stores.
+template <typename T, bool SEG, bool REV, bool EXCL>
+__device__ __forceinline__ T range_value(int64_t n, int64_t F0, int64_t fw, int64_t addr,
+                                        const T* pk, const T* xs, const uint32_t* hbs,
+                                        const uint32_t* s_heads) {
+    constexpr int SH = EXCL ? 1 : 0;
     const int64_t fp = REV ? n - 1 - addr : addr;   // flipped position written
-    const int e = (int)(fp - 1 - fw);               // wave element whose inclusive value it takes
-    if constexpr (SEG) {
+    const int e = (int)(fp - SH - fw);              // wave element whose inclusive value it takes
+    if constexpr (SEG && EXCL) {
         const int bit = (int)(fp - F0);
         if ((s_heads[bit >> 5] >> (bit & 31)) & 1u) return T(0.0);
     }
     return combine_at<T, SEG>(pk, xs, hbs, e);
 }
 
-template <typename T, bool SEG, bool REV>
-__device__ __forceinline__ void readout_excl(T* __restrict__ y, int64_t n, int64_t F0, int64_t fw,
-                                             const T* pk, const T* xs, const uint32_t* hbs,
-                                             const uint32_t* s_heads, int lane) {
-    // flipped positions fw + 1 .. fw + 2048, clipped to n - 1; as original addresses [lo, hi)
-    const int64_t last = (fw + kWaveElems < n - 1) ? fw + kWaveElems : n - 1;
-    if (last < fw + 1) return;
-    const int64_t lo = REV ? n - 1 - last : fw + 1;
-    const int64_t hi = REV ? n - 1 - fw : last + 1;
+template <typename T, bool SEG, bool REV, bool EXCL>
+__device__ __forceinline__ void readout_range(T* __restrict__ y, int64_t n, int64_t F0, int64_t fw,
+                                              const T* pk, const T* xs, const uint32_t* hbs,
+                                              const uint32_t* s_heads, int lane) {
+    constexpr int SH = EXCL ? 1 : 0;
+    // flipped positions fw + SH .. fw + 2047 + SH, clipped to n - 1; as addresses [lo, hi)
+    const int64_t flo = fw + SH;
+    const int64_t last = (fw + kWaveElems - 1 + SH < n - 1) ? fw + kWaveElems - 1 + SH : n - 1;
+    if (last < flo) return;
+    const int64_t lo = REV ? n - 1 - last : flo;
+    const int64_t hi = REV ? n - flo : last + 1;
     // interior [A, Z): starts at the first 16-byte-aligned element, whole 16-byte groups
     constexpr int64_t GW = kGW<T>;   // elements per 16 bytes
     const int64_t ye = (int64_t)(reinterpret_cast<uintptr_t>(y) / sizeof(T));
@@ -513,13 +483,13 @@ __device__ __forceinline__ void readout_excl(T* __restrict__ y, int64_t n, int64
     if (A > hi) A = hi;
     const int64_t Z = A + ((hi - A) / GW) * GW;
     for (int64_t k = lo + lane; k < A; k += 64)
-        y[k] = excl_value<T, SEG, REV>(n, F0, fw, k, pk, xs, hbs, s_heads);
+        y[k] = range_value<T, SEG, REV, EXCL>(n, F0, fw, k, pk, xs, hbs, s_heads);
     for (int64_t k = Z + lane; k < hi; k += 64)
-        y[k] = excl_value<T, SEG, REV>(n, F0, fw, k, pk, xs, hbs, s_heads);
+        y[k] = range_value<T, SEG, REV, EXCL>(n, F0, fw, k, pk, xs, hbs, s_heads);
     const int ngroups = (int)((Z - A) / GW);   // at most 2048 / GW
     // wave element read for address A + m: forward e = e0 + m, reverse e = e0 - m (e0 small);
-    // its segment-head bit, when segmented: flipped position - F0 = hoff + e + 1
-    const int e0 = REV ? (int)(n - 2 - fw - A) : (int)(A - 1 - fw);
+    // its segment-head bit, when segmented: flipped position - F0 = hoff + e + SH
+    const int e0 = REV ? (int)(n - 1 - SH - fw - A) : (int)(A - SH - fw);
     const int hoff = (int)(fw - F0);
     T* const yA = y + A;
 #pragma unroll
@@ -531,8 +501,8 @@ __device__ __forceinline__ void readout_excl(T* __restrict__ y, int64_t n, int64
             for (int k = 0; k < (int)GW; ++k) {
                 const int e = REV ? e0 - ((int)GW * gi + k) : e0 + ((int)GW * gi + k);
                 T val = combine_at<T, SEG>(pk, xs, hbs, e);
-                if constexpr (SEG) {
-                    const int bit = hoff + e + 1;
+                if constexpr (SEG && EXCL) {
+                    const int bit = hoff + e + SH;
                     if ((s_heads[bit >> 5] >> (bit & 31)) & 1u) val = T(0.0);
                 }
                 v[k] = val;
@@ -540,6 +510,13 @@ __device__ __forceinline__ void readout_excl(T* __restrict__ y, int64_t n, int64
             nt_store16<T>(yA + (int64_t)GW * gi, v);
         }
     }
+}
+
+template <typename T, bool SEG, bool REV>
+__device__ __forceinline__ void readout_excl(T* __restrict__ y, int64_t n, int64_t F0, int64_t fw,
+                                             const T* pk, const T* xs, const uint32_t* hbs,
+                                             const uint32_t* s_heads, int lane) {
+    readout_range<T, SEG, REV, true>(y, n, F0, fw, pk, xs, hbs, s_heads, lane);
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -638,39 +615,145 @@ __device__ __forceinline__ Seg<T> tile_local(const ScanArgs<T>& a, int j, T (&r)
     return om3;
 }
 
+// Where a whole wave's memory range [p0, p0 + 2048) meets 16-byte alignment: h elements before
+// the first aligned one, then ng whole 16-byte groups, then 2048 - h - ng G trailing elements
+// (h and the trailing count are below G).  The same for every lane.
+template <typename T>
+struct WaveSplit {
+    int h, ng;
+};
+
+template <typename T>
+__device__ __forceinline__ WaveSplit<T> wave_split(const T* p0) {
+    constexpr int G = 16 / (int)sizeof(T);
+    const int h = (int)(((uintptr_t)0 - reinterpret_cast<uintptr_t>(p0)) % 16 / sizeof(T));
+    return WaveSplit<T>{h, (kWaveElems - h) / G};
+}
+
+// The edge element lane l loads for a split: index m in the wave's range, or -1.
+template <typename T>
+__device__ __forceinline__ int edge_index(WaveSplit<T> sp, int lane) {
+    constexpr int G = 16 / (int)sizeof(T);
+    const int tail0 = sp.h + sp.ng * G;
+    if (lane < sp.h) return lane;
+    if (lane - sp.h < kWaveElems - tail0) return tail0 + (lane - sp.h);
+    return -1;
+}
+
+// The wave's 2048 elements in memory order, coalesced, for a whole wave: its ng whole 16-byte
+// groups, r[g * G + i] = element h + (g * 64 + lane) * G + i of the wave's memory range (a lane
+// past the last group loads that group again, unused), and the at most 2 (G - 1) elements
+// before and after them, one per lane, into *edge; runs_from_lds turns them into runs.  Every
+// address is the wave's base plus a lane offset.  (Each lane loading its own 128-byte run
+// touches 64 lines per load instruction; coalesced, a load covers 1 KiB: on MI355X at 2^28 the
+// exclusive f32 scan went 0.45 -> 0.42 ms, the segmented one 0.49 -> 0.46 ms, f64 0.39 -> 0.38
+// ms, the inclusive f32 scan unchanged.)  A wave that is not whole loads the dummy line and
+// then its run by elements, already in run order.  With ALN, a wave that starts 16-byte aligned
+// skips the edge load (a wave-uniform branch); runs_from_lds takes the same flag.  On MI355X
+// the branches paid in the segmented scan (f32 at 2^28: 448 -> 434 us) and cost in the others
+// (inclusive 392 -> 398 us), so the segmented kernels take them.
+template <typename T, bool REV, bool ALN>
+__device__ __forceinline__ void load_wave_coal(const T* __restrict__ x, int64_t n, int64_t fw,
+                                               const T* __restrict__ dummy, T (&r)[kV], T& edge,
+                                               int lane) {
+    constexpr int G = 16 / (int)sizeof(T);
+    const bool whole = fw + kWaveElems <= n;
+    const T* p0 = whole ? x + (REV ? n - fw - kWaveElems : fw) : dummy;
+    const WaveSplit<T> sp = whole ? wave_split<T>(p0) : WaveSplit<T>{0, 16};
+    const v4_t<T>* base = reinterpret_cast<const v4_t<T>*>(p0 + sp.h);
+#pragma unroll
+    for (int g = 0; g < kV / G; ++g) {
+        const int idx = g * 64 + lane;
+        const int off = whole ? (idx < sp.ng ? idx : sp.ng - 1) : (g & 15);
+        if constexpr (sizeof(T) == 4) {
+            const v4_t<T> q = base[off];
+            r[4 * g] = q.x; r[4 * g + 1] = q.y; r[4 * g + 2] = q.z; r[4 * g + 3] = q.w;
+        } else {
+            const f64x2 q = reinterpret_cast<const f64x2*>(base)[off];
+            r[2 * g] = q.x; r[2 * g + 1] = q.y;
+        }
+    }
+    edge = T(0);
+    if (whole && (!ALN || sp.h != 0)) {
+        const int m = edge_index<T>(sp, lane);
+        edge = p0[m >= 0 ? m : 0];
+    }
+    if (!whole) {
+        const int64_t f0 = fw + (int64_t)lane * kV;
+        const T id = ident<T>();
+#pragma unroll
+        for (int k = 0; k < kV; ++k) {
+            const int64_t f = f0 + k;
+            const int64_t fc = f < n ? f : n - 1;
+            const T v = x[REV ? n - 1 - fc : fc];
+            r[k] = (f < n) ? v : id;
+        }
+    }
+}
+
 // Runs of the wave's part of tile j into registers (vector loads when the wave is whole and
 // aligned, else element loads with identity past n).
 template <typename T, bool REV>
 __device__ __forceinline__ void load_tile(const ScanArgs<T>& a, int j, int wave, T (&r)[kV],
-                                          int lane, bool coal = false) {
+                                          int lane) {
     const int64_t fw = (int64_t)j * kT + (int64_t)wave * kWaveElems;
     const int64_t reg0 = REV ? a.n - fw - kWaveElems : fw;   // lowest original index
     const bool vec = (fw + kWaveElems <= a.n) && aligned16(a.x + reg0);
-    load_run<T, REV>(a.x, a.n, fw, vec, a.dummy, r, lane, coal);
+    load_run<T, REV>(a.x, a.n, fw, vec, a.dummy, r, lane);
 }
 
-// Whether load_tile took the coalesced path for tile j's wave (then r is in memory order and
-// goes through runs_from_lds before use).
+// The same wave, coalesced (load_wave_coal); whole waves then go through runs_from_lds.
+template <typename T, bool REV, bool ALN>
+__device__ __forceinline__ void load_tile_coal(const ScanArgs<T>& a, int j, int wave, T (&r)[kV],
+                                               T& edge, int lane) {
+    const int64_t fw = (int64_t)j * kT + (int64_t)wave * kWaveElems;
+    load_wave_coal<T, REV, ALN>(a.x, a.n, fw, a.dummy, r, edge, lane);
+}
+
+// Whether tile j's wave is whole (then load_tile_coal left it in memory order, for
+// runs_from_lds).
 template <typename T, bool REV>
 __device__ __forceinline__ bool tile_vec(const ScanArgs<T>& a, int j, int wave) {
     const int64_t fw = (int64_t)j * kT + (int64_t)wave * kWaveElems;
-    const int64_t reg0 = REV ? a.n - fw - kWaveElems : fw;
-    return (fw + kWaveElems <= a.n) && aligned16(a.x + reg0);
+    return fw + kWaveElems <= a.n;
 }
 
 // Coalesced wave data (memory order) to lane runs through the wave's park area: element m of
 // the wave's memory range is flipped element e = m (forward) or 2047 - m (reverse), written at
 // pad(e); lane t then reads its run at t * 33.  The park area must be free.
-template <typename T, bool REV>
-__device__ __forceinline__ void runs_from_lds(T* pk, T (&r)[kV], int lane) {
+template <typename T, bool REV, bool ALN>
+__device__ __forceinline__ void runs_from_lds(const ScanArgs<T>& a, int j, int wave, T* pk,
+                                              T (&r)[kV], T edge, int lane) {
     constexpr int G = 16 / (int)sizeof(T);
+    const int64_t fw = (int64_t)j * kT + (int64_t)wave * kWaveElems;
+    const WaveSplit<T> sp = wave_split<T>(a.x + (REV ? a.n - fw - kWaveElems : fw));
+    if (ALN && sp.h == 0) {
+        // aligned: every lane holds whole groups, no edge
 #pragma unroll
-    for (int g = 0; g < kV / G; ++g) {
+        for (int g = 0; g < kV / G; ++g) {
 #pragma unroll
-        for (int i = 0; i < G; ++i) {
-            const int m = (g * 64 + lane) * G + i;
-            const int e = REV ? (kWaveElems - 1) - m : m;
-            pk[pad(e)] = r[g * G + i];
+            for (int i = 0; i < G; ++i) {
+                const int m = (g * 64 + lane) * G + i;
+                const int e = REV ? (kWaveElems - 1) - m : m;
+                pk[pad(e)] = r[g * G + i];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < kV / G; ++g) {
+            if (g * 64 + lane < sp.ng) {
+#pragma unroll
+                for (int i = 0; i < G; ++i) {
+                    const int m = sp.h + (g * 64 + lane) * G + i;
+                    const int e = REV ? (kWaveElems - 1) - m : m;
+                    pk[pad(e)] = r[g * G + i];
+                }
+            }
+        }
+        const int me = edge_index<T>(sp, lane);
+        if (me >= 0) {
+            const int e = REV ? (kWaveElems - 1) - me : me;
+            pk[pad(e)] = edge;
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -834,7 +917,8 @@ __device__ __forceinline__ int ticket_tile(uint32_t k, int c, int nc) { return (
 // claimed in counter order by running workgroups that publish and finish them without
 // waiting on it, so every wait ends.
 template <typename T, bool SEG, bool REV, bool EXCL>
-__global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 3 : 2)))
+void k_scan(ScanArgs<T> a) {
     __shared__ T s_park[kScanWaves][kPark];
     __shared__ T s_x[kScanWaves][kScanW];
     __shared__ uint32_t s_hbits[SEG ? kScanWaves : 1][kScanW];
@@ -860,11 +944,12 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     int c = __builtin_amdgcn_readfirstlane(s_tick[0]);
     if (c >= a.ntiles) return;
     T r[kV];
-    load_tile<T, REV>(a, c, wave, r, lane0, true);
+    T edc;
+    load_tile_coal<T, REV, SEG>(a, c, wave, r, edc, lane0);
     HeadWords hwc = load_head_words<T, SEG>(a, c, tid);
     uint32_t claimed = 0u;
     if (tid == 0) claimed = claim_issue(a.ticket, ctr);
-    if (tile_vec<T, REV>(a, c, wave)) runs_from_lds<T, REV>(pk, r, lane0);
+    if (tile_vec<T, REV>(a, c, wave)) runs_from_lds<T, REV, SEG>(a, c, wave, pk, r, edc, lane0);
     uint32_t hbc;
     Seg<T> Pc, pc;
     Seg<T> aggc = tile_local<T, SEG, REV>(a, c, r, hbc, Pc, pc, s_heads[0], s_wtot, tid, lane0,
@@ -880,9 +965,10 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
     // u's loads (a tile past the end reads element n - 1 and is never used), brought into
     // runs through the park area before c is parked there
     T ru[kV];
-    load_tile<T, REV>(a, u, wave, ru, lane0, true);
+    T edu;
+    load_tile_coal<T, REV, SEG>(a, u, wave, ru, edu, lane0);
     HeadWords hwu = load_head_words<T, SEG>(a, u, tid);
-    if (tile_vec<T, REV>(a, u, wave)) runs_from_lds<T, REV>(pk, ru, lane0);
+    if (tile_vec<T, REV>(a, u, wave)) runs_from_lds<T, REV, SEG>(a, u, wave, pk, ru, edu, lane0);
     park_runs<T>(pk, r, lane0);
 #pragma unroll
     for (int k = 0; k < kV; ++k) r[k] = ru[k];
@@ -918,7 +1004,8 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
 
         // ---- v: loads issued now, consumed in the next iteration; the tile after v claimed
         T rv[kV];
-        load_tile<T, REV>(a, v, wave, rv, lane, true);
+        T edv;
+        load_tile_coal<T, REV, SEG>(a, v, wave, rv, edv, lane);
         const HeadWords hwv = load_head_words<T, SEG>(a, v, tid);
         if (tid == 0 && have_v) claimed = claim_issue(a.ticket, ctr);
 
@@ -929,7 +1016,7 @@ __global__ __launch_bounds__(256) void k_scan(ScanArgs<T> a) {
 
         // ---- v's data into runs through the park area (this wave's readout of c is complete),
         // then u takes c's place there
-        if (tile_vec<T, REV>(a, v, wave)) runs_from_lds<T, REV>(pk, rv, lane);
+        if (tile_vec<T, REV>(a, v, wave)) runs_from_lds<T, REV, SEG>(a, v, wave, pk, rv, edv, lane);
         park_runs<T>(pk, r, lane);
         if constexpr (SEG) s_hbits[wave][lane] = hbu;
 #pragma unroll
@@ -1041,12 +1128,13 @@ __global__ __launch_bounds__(256) void k_scan_two(ScanArgs<T> a0) {
     const uint32_t* hbs = s_hbits[SEG ? wave : 0];
     Seg<T>* agg_slots = reinterpret_cast<Seg<T>*>(a0.agg) + (int64_t)blockIdx.y * a0.ntiles;
     T r[kV];
-    load_tile<T, REV>(a, j, wave, r, lane, true);
+    T ed;
+    load_tile_coal<T, REV, SEG>(a, j, wave, r, ed, lane);
     const HeadWords hw = load_head_words<T, SEG>(a, j, tid);
     // the second launch's totals of the earlier tiles, loaded with the tile
     Seg<T> before = seg_ident<T>();
     if (SECOND && tid < j) before = agg_slots[tid];
-    if (tile_vec<T, REV>(a, j, wave)) runs_from_lds<T, REV>(pk, r, lane);
+    if (tile_vec<T, REV>(a, j, wave)) runs_from_lds<T, REV, SEG>(a, j, wave, pk, r, ed, lane);
     uint32_t hb;
     Seg<T> P, p;
     const Seg<T> agg = tile_local<T, SEG, REV>(a, j, r, hb, P, p, s_heads, s_wtot, tid, lane,
