@@ -651,8 +651,9 @@ __device__ __forceinline__ int edge_index(WaveSplit<T> sp, int lane) {
 // then its run by elements, already in run order.  With ALN, a wave that starts 16-byte aligned
 // skips the edge load (a wave-uniform branch); runs_from_lds takes the same flag.  On MI355X
 // the branches paid in the segmented scan (f32 at 2^28: 448 -> 434 us) and cost in the others
-// (inclusive 392 -> 398 us), so the segmented kernels take them.
-template <typename T, bool REV, bool ALN>
+// (inclusive 392 -> 398 us), so the segmented kernels take them.  NT marks the group loads
+// non-temporal (taken for inputs of 512 MiB and more, twice the GPU's last-level cache).
+template <typename T, bool REV, bool ALN, bool NT>
 __device__ __forceinline__ void load_wave_coal(const T* __restrict__ x, int64_t n, int64_t fw,
                                                const T* __restrict__ dummy, T (&r)[kV], T& edge,
                                                int lane) {
@@ -666,10 +667,11 @@ __device__ __forceinline__ void load_wave_coal(const T* __restrict__ x, int64_t 
         const int idx = g * 64 + lane;
         const int off = whole ? (idx < sp.ng ? idx : sp.ng - 1) : (g & 15);
         if constexpr (sizeof(T) == 4) {
-            const v4_t<T> q = base[off];
+            const v4_t<T> q = NT ? __builtin_nontemporal_load(base + off) : base[off];
             r[4 * g] = q.x; r[4 * g + 1] = q.y; r[4 * g + 2] = q.z; r[4 * g + 3] = q.w;
         } else {
-            const f64x2 q = reinterpret_cast<const f64x2*>(base)[off];
+            const f64x2* b2 = reinterpret_cast<const f64x2*>(base);
+            const f64x2 q = NT ? __builtin_nontemporal_load(b2 + off) : b2[off];
             r[2 * g] = q.x; r[2 * g + 1] = q.y;
         }
     }
@@ -703,11 +705,11 @@ __device__ __forceinline__ void load_tile(const ScanArgs<T>& a, int j, int wave,
 }
 
 // The same wave, coalesced (load_wave_coal); whole waves then go through runs_from_lds.
-template <typename T, bool REV, bool ALN>
+template <typename T, bool REV, bool ALN, bool NT>
 __device__ __forceinline__ void load_tile_coal(const ScanArgs<T>& a, int j, int wave, T (&r)[kV],
                                                T& edge, int lane) {
     const int64_t fw = (int64_t)j * kT + (int64_t)wave * kWaveElems;
-    load_wave_coal<T, REV, ALN>(a.x, a.n, fw, a.dummy, r, edge, lane);
+    load_wave_coal<T, REV, ALN, NT>(a.x, a.n, fw, a.dummy, r, edge, lane);
 }
 
 // Whether tile j's wave is whole (then load_tile_coal left it in memory order, for
@@ -916,7 +918,7 @@ __device__ __forceinline__ int ticket_tile(uint32_t k, int c, int nc) { return (
 // counts only the loads issued after them.  A workgroup only waits on smaller tiles, which are
 // claimed in counter order by running workgroups that publish and finish them without
 // waiting on it, so every wait ends.
-template <typename T, bool SEG, bool REV, bool EXCL>
+template <typename T, bool SEG, bool REV, bool EXCL, bool NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 3 : 2)))
 void k_scan(ScanArgs<T> a) {
     __shared__ T s_park[kScanWaves][kPark];
@@ -945,7 +947,7 @@ void k_scan(ScanArgs<T> a) {
     if (c >= a.ntiles) return;
     T r[kV];
     T edc;
-    load_tile_coal<T, REV, SEG>(a, c, wave, r, edc, lane0);
+    load_tile_coal<T, REV, SEG, NT>(a, c, wave, r, edc, lane0);
     HeadWords hwc = load_head_words<T, SEG>(a, c, tid);
     uint32_t claimed = 0u;
     if (tid == 0) claimed = claim_issue(a.ticket, ctr);
@@ -966,7 +968,7 @@ void k_scan(ScanArgs<T> a) {
     // runs through the park area before c is parked there
     T ru[kV];
     T edu;
-    load_tile_coal<T, REV, SEG>(a, u, wave, ru, edu, lane0);
+    load_tile_coal<T, REV, SEG, NT>(a, u, wave, ru, edu, lane0);
     HeadWords hwu = load_head_words<T, SEG>(a, u, tid);
     if (tile_vec<T, REV>(a, u, wave)) runs_from_lds<T, REV, SEG>(a, u, wave, pk, ru, edu, lane0);
     park_runs<T>(pk, r, lane0);
@@ -1005,7 +1007,7 @@ void k_scan(ScanArgs<T> a) {
         // ---- v: loads issued now, consumed in the next iteration; the tile after v claimed
         T rv[kV];
         T edv;
-        load_tile_coal<T, REV, SEG>(a, v, wave, rv, edv, lane);
+        load_tile_coal<T, REV, SEG, NT>(a, v, wave, rv, edv, lane);
         const HeadWords hwv = load_head_words<T, SEG>(a, v, tid);
         if (tid == 0 && have_v) claimed = claim_issue(a.ticket, ctr);
 
@@ -1129,7 +1131,7 @@ __global__ __launch_bounds__(256) void k_scan_two(ScanArgs<T> a0) {
     Seg<T>* agg_slots = reinterpret_cast<Seg<T>*>(a0.agg) + (int64_t)blockIdx.y * a0.ntiles;
     T r[kV];
     T ed;
-    load_tile_coal<T, REV, SEG>(a, j, wave, r, ed, lane);
+    load_tile_coal<T, REV, SEG, false>(a, j, wave, r, ed, lane);
     const HeadWords hw = load_head_words<T, SEG>(a, j, tid);
     // the second launch's totals of the earlier tiles, loaded with the tile
     Seg<T> before = seg_ident<T>();
@@ -1362,6 +1364,20 @@ det_status scan_two(const T* x, T* y, int64_t n, int64_t ncols, int64_t stride, 
     return launch_status();
 }
 
+template <typename T, bool NT>
+const void* k_scan_fn(int mode) {
+    switch (mode) {
+        case 0: return (const void*)k_scan<T, false, false, false, NT>;
+        case 1: return (const void*)k_scan<T, false, false, true, NT>;
+        case 2: return (const void*)k_scan<T, false, true, false, NT>;
+        case 3: return (const void*)k_scan<T, false, true, true, NT>;
+        case 4: return (const void*)k_scan<T, true, false, false, NT>;
+        case 5: return (const void*)k_scan<T, true, false, true, NT>;
+        case 6: return (const void*)k_scan<T, true, true, false, NT>;
+        default: return (const void*)k_scan<T, true, true, true, NT>;
+    }
+}
+
 template <typename T>
 det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t* offs,
                      int64_t nseg, char* ws, hipStream_t s) {
@@ -1403,17 +1419,13 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     a.A = A;
     a.A2 = A2;
     const int mode = (offs ? 4 : 0) | (a.rev ? 2 : 0) | (a.excl ? 1 : 0);
-    const void* fn = nullptr;
-    switch (mode) {
-        case 0: fn = (const void*)k_scan<T, false, false, false >; break;
-        case 1: fn = (const void*)k_scan<T, false, false, true >; break;
-        case 2: fn = (const void*)k_scan<T, false, true, false >; break;
-        case 3: fn = (const void*)k_scan<T, false, true, true >; break;
-        case 4: fn = (const void*)k_scan<T, true, false, false >; break;
-        case 5: fn = (const void*)k_scan<T, true, false, true >; break;
-        case 6: fn = (const void*)k_scan<T, true, true, false >; break;
-        default: fn = (const void*)k_scan<T, true, true, true >; break;
-    }
+    // Inputs of 512 MiB and more are read with non-temporal loads: on MI355X at 2^28 (1 GiB)
+    // f32 inclusive 390 -> 384 us, exclusive 409 -> 402 us, f64 inclusive 727 -> 711 us, and
+    // f64 at 2^26 (512 MiB) 197 -> 193 us; at 2^26 and 2^26 + 1 f32 (256 MiB, the size of the
+    // last-level cache) repeated calls that found part of their input in that cache lost it
+    // (92 -> 104 us), so smaller inputs keep ordinary loads.
+    const bool nt = (uint64_t)n * sizeof(T) >= (512ull << 20);
+    const void* fn = nt ? k_scan_fn<T, true>(mode) : k_scan_fn<T, false>(mode);
     // Persistent grid: as many workgroups as are resident at once.  More would only queue
     // behind them, and a workgroup that starts late has lost its pipeline's overlap.
     int64_t grid = resident_wgs(fn, 256);
