@@ -92,6 +92,22 @@ def test_empty_inputs(dev):
     assert got.size == 0 and k == 9
 
 
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("B", [160, 256, 400, 505])
+def test_blocks_between_2048_and_8192(dev, dtype, B):
+    # destinations of about 2,000 to 6,600 members: blocks longer than 2048 values, up to four
+    # of them starting in one 8192-position range, at every offset
+    n = 1 << 20
+    rng = np.random.default_rng(B)
+    v = rounding(n, dtype, B + 1)
+    idx = rng.integers(-1, B + 1, n).astype(np.int32)
+    o = rounding(B, dtype, B + 2)
+    got, _, k = gpu_scatter(v, idx, o, dev)
+    want, _, wk = oracle.scatter_add(v, idx, o)
+    assert bits_equal(got, want), (B, first_mismatch(got, want))
+    assert k == wk
+
+
 def test_c2_shape_2_24(dev):
     n = 1 << 24
     v = workloads.normal(n, seed=1)
