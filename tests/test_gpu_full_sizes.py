@@ -57,6 +57,21 @@ def test_scan_f32_2_28(dev, scan_2_28, excl, rev):
     assert bits_equal(got, want), first_mismatch(got, want)
 
 
+@pytest.mark.parametrize("excl,rev", [(False, True), (True, False)])
+def test_scan_unaligned_views_above_512_mib(dev, scan_2_28, excl, rev):
+    # inputs of 512 MiB and more take non-temporal loads: views of 2^27 + 5 f32 elements at
+    # element offsets 1 (input) and 2 (output)
+    n = (1 << 27) + 5
+    xs = scan_2_28[1:1 + n]
+    t = torch.from_numpy(scan_2_28[: n + 4]).to(dev)
+    yb = torch.empty(n + 4, dtype=torch.float32, device=dev)
+    y = yb[2:2 + n]
+    det.det_scan(t[1:1 + n], y=y, exclusive=excl, reverse=rev)
+    want = oracle.scan(xs, exclusive=excl, reverse=rev)
+    got = y.cpu().numpy()
+    assert bits_equal(got, want), first_mismatch(got, want)
+
+
 def test_scatter_f32_2_28_65536_bins(dev):
     n, B = 1 << 28, 65536
     v = workloads.normal(n, seed=1)

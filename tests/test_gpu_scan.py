@@ -193,6 +193,32 @@ def test_exclusive_into_unaligned_output(dev, dtype):
 
 
 @pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("n", [5 * T + 77, 2 * A * T + 333])
+def test_unaligned_input_and_output(dev, dtype, n):
+    # x and y views at independent element offsets within 16 bytes: each wave's coalesced
+    # loads take the aligned interior and load the elements around it one per lane, and the
+    # readout aligns its stores to y; both launch paths (a few tiles, and more than one anchor
+    # interval), every mode, with and without segments
+    x = workloads.scan_values(n + 4, dtype, seed=n % 97)
+    offs = random_offsets(n, 900, seed=n % 89)
+    xb = torch.from_numpy(x).to(dev)
+    o = torch.from_numpy(offs).to(dev)
+    yb = torch.empty(n + 4, dtype=xb.dtype, device=dev)
+    for kx, ky in ((1, 0), (2, 0), (3, 0), (0, 2), (1, 3), (2, 1), (3, 3)):
+        xs = x[kx:kx + n]
+        for excl, rev in MODES:
+            for seg in (None, offs):
+                y = yb[ky:ky + n]
+                y.fill_(float("nan"))
+                det.det_scan(xb[kx:kx + n], y=y, exclusive=excl, reverse=rev,
+                             offsets=o if seg is not None else None)
+                want = oracle.scan(xs, exclusive=excl, reverse=rev, offsets=seg)
+                got = y.cpu().numpy()
+                assert bits_equal(got, want), (kx, ky, excl, rev, seg is not None,
+                                               first_mismatch(got, want))
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
 def test_scan_health_word_stays_clear(dev, dtype):
     # every look-back wait of these scans ends normally: the workspace's health word reads 0
     n = 5 * A * T + 77
