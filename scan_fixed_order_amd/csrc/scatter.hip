@@ -561,16 +561,31 @@ __global__ __launch_bounds__(kRadixNT<P>) void k_radix_scatter(
 
 // ---------------------------------------------------------------- destinations
 
-// off[b] = first sorted position with key >= b, for b in [0, B]; n_skipped = n - valid
+// off[b] = first sorted position with key >= b, for b in [0, B]; n_skipped = n - valid.
+// row0: the last radix pass's bucket starts (row 0 of its offsets), or null.  With one pass
+// (destinations below 256: every key is one bucket) they are the answer; with two passes over
+// 16-bit keys the keys of high byte h lie in that pass's bucket h, so the search for b stays
+// inside bucket b >> 8 (f32 2^28 into 65,536 bins on MI355X: 31 -> 18 us).
 template <typename KT>
 __global__ __launch_bounds__(256) void k_bin_offsets(const KT* __restrict__ K,
                                                      const uint32_t* __restrict__ nvalid,
                                                      int64_t B, int64_t n, uint32_t* __restrict__ off,
-                                                     int64_t* __restrict__ n_skipped) {
+                                                     int64_t* __restrict__ n_skipped,
+                                                     const uint32_t* __restrict__ row0,
+                                                     int passes) {
     const int64_t m = *nvalid;
     for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b <= B;
          b += (int64_t)gridDim.x * blockDim.x) {
+        if (row0 && passes == 1) {   // b <= B <= 256; row0[256] is the out-of-range bucket's start, m
+            off[b] = row0[b];
+            continue;
+        }
         int64_t lo = 0, hi = m;
+        if (row0 && passes == 2) {
+            const int64_t h = b >> 8;
+            lo = h < 256 ? (int64_t)row0[h] : m;
+            hi = h < 255 ? (int64_t)row0[h + 1] : m;
+        }
         while (lo < hi) {
             const int64_t mid = (lo + hi) >> 1;
             if ((int64_t)K[mid] < b) lo = mid + 1;
@@ -1273,12 +1288,16 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
         int64_t g = cdiv(num_out + 1, 256);
         if (g > 8192) g = 8192;
         KernelTimer kt("k_bin_offsets", s);
+        // the last pass's bucket starts: row 0 of its offsets, still in the histogram buffer
+        const uint32_t* row0 = reinterpret_cast<const uint32_t*>(ws + L.hist);
+        const int passes = key_passes(num_out);
         if (k16)
-            k_bin_offsets<uint16_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(K16, ctrl, num_out, n,
-                                                                             off, n_skipped);
+            k_bin_offsets<uint16_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(
+                K16, ctrl, num_out, n, off, n_skipped, row0, passes);
         else
             k_bin_offsets<uint32_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(K, ctrl, num_out, n,
-                                                                             off, n_skipped);
+                                                                             off, n_skipped,
+                                                                             nullptr, 0);
     }
     T* pF = reinterpret_cast<T*>(ws + L.pF);
     T* pC = reinterpret_cast<T*>(ws + L.pC);
@@ -1370,7 +1389,7 @@ det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n
         if (g > 8192) g = 8192;
         KernelTimer kt("k_bin_offsets", s);
         k_bin_offsets<uint32_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(K, ctrl, num_out, n, off,
-                                                                         n_skipped);
+                                                                         n_skipped, nullptr, 0);
     }
     int64_t* o64 = reinterpret_cast<int64_t*>(ws + R.o64);
     T* G = reinterpret_cast<T*>(ws + R.G);

@@ -40,14 +40,26 @@ def test_max_n_sum_of_ones(dev):
 def test_max_n_scan_of_ones(dev, dtype):
     x = torch.ones(NMAX, dtype=dtype, device=dev)
     y = torch.empty_like(x)
+    code = 1 if dtype == torch.float64 else 2
     for excl, rev in ((False, False), (True, False), (False, True), (True, True)):
-        det.det_scan(x, y=y, exclusive=excl, reverse=rev)
+        flags = (1 if excl else 0) | (2 if rev else 0)
+        ws = torch.empty(det.det_scan_workspace_size(NMAX, code, flags, 0), dtype=torch.uint8,
+                         device=dev)
+        det.det_scan(x, y=y, exclusive=excl, reverse=rev, ws=ws)
+        # every bounded wait of the scan ended normally
+        assert int(det.det_scan_error(ws).item()) == 0, (dtype, excl, rev, "health word")
         for a in range(0, NMAX, SLICE):
             b = min(NMAX, a + SLICE)
             i = torch.arange(a, b, dtype=torch.int64, device=dev)
             want = (NMAX - i if rev else i + 1) - (1 if excl else 0)
-            ok = torch.equal(y[a:b].to(torch.int64), want)
-            assert ok, (dtype, excl, rev, a)
+            got = y[a:b].to(torch.int64)
+            if not torch.equal(got, want):
+                bad = torch.nonzero(got != want).flatten()
+                k = int(bad[0])
+                raise AssertionError((dtype, excl, rev, "slice", a, "mismatches", bad.numel(),
+                                      "first index", a + k, "got", int(got[k]), "want",
+                                      int(want[k]), "last index", a + int(bad[-1])))
+        del ws
     del x, y
     torch.cuda.empty_cache()
 
