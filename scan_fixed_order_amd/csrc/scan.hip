@@ -832,25 +832,16 @@ __device__ __forceinline__ void finish_tile(const ScanArgs<T>& a, int j, const L
     gc.Q = lb.Q;
     Seg<T> Wj, WG;
     block_pw2<SEG, T>(mine, gmine, lane, wave, s_tmp, Wj, WG);
-    // the interval total G_q was published by this tile's local step (publish_interval_total);
-    // the super-interval's last tile needs it again for the next carry
-    const bool ianchor = (lb.cnt == a.A - 1) && (j + 1 < a.ntiles);
-    const bool sanchor = ianchor && (lb.qcnt == a.A2 - 1);
-    Seg<T> H = seg_ident<T>();
-    if (sanchor) {
-        const Seg<T> Gq = block_pw<SEG, T>(tid == a.A - 1 ? agg : mine, lane, wave, s_tmp);
-        H = block_pw<SEG, T>(tid == a.A2 - 1 ? Gq : gmine, lane, wave, s_tmp);
-    }
+    (void)agg;
 
-    // carry into the super-interval (the identity for the first); its last tile forwards the
-    // next one
+    // carry into the super-interval (the identity for the first), published by the previous
+    // super-interval's last tile in its local step (publish_interval_total)
     Seg<T> CC = seg_ident<T>();
     if (lb.Q > 0) {
         if (tid == 0) s_carry = wait_slot<T>(a.carry + (size_t)lb.Q * SW, err);
         __syncthreads();
         CC = s_carry;
     }
-    if (sanchor && tid == 0) publish<T>(a.carry + (size_t)(lb.Q + 1) * SW, op<SEG>(CC, H));
     const Seg<T> E = op<SEG>(op<SEG>(CC, WG), Wj);
     xs[lane] = op<SEG>(op<SEG>(E, P), p).v;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -894,6 +885,22 @@ __device__ __forceinline__ void publish_interval_total(const ScanArgs<T>& a, int
     const Seg<T> m = poll_finish_set<T>(pa.w, slot, tid < lb.cnt, a.err);
     const Seg<T> G = block_pw<SEG, T>(tid == a.A - 1 ? aggu : m, lane, wave, s_tmp);
     if (tid == 0) publish<T>(a.gtot + (size_t)lb.q * SW, G);
+    // The super-interval's last tile forwards the carry CC_{Q+1} = CC_Q + PW(all A2 interval
+    // totals of Q) here, in its local step, where it waits only on smaller tiles and the
+    // previous carry.  (Forwarded from the tile's finish instead, the carry waited behind the
+    // workgroup's next tile: when that tile closed a later interval, its local step waited on
+    // tiles whose workgroups were waiting for this carry.)
+    if (lb.qcnt != a.A2 - 1) return;
+    const uint64_t* gslot = a.gtot + (size_t)(lb.Q * a.A2 + tid) * SW;
+    Poll<T> pg;
+    poll_issue<T>(pg, gslot, tid < lb.qcnt, gslot, false);
+    const Seg<T> gm = poll_finish_set<T>(pg.w, gslot, tid < lb.qcnt, a.err);
+    const Seg<T> H = block_pw<SEG, T>(tid == a.A2 - 1 ? G : gm, lane, wave, s_tmp);
+    if (tid == 0) {
+        const Seg<T> CC = lb.Q > 0 ? wait_slot<T>(a.carry + (size_t)lb.Q * SW, a.err)
+                                   : seg_ident<T>();
+        publish<T>(a.carry + (size_t)(lb.Q + 1) * SW, op<SEG>(CC, H));
+    }
 }
 
 // Issues the claim of counter c's next ticket k; the tile is k * nc + c.  The counter offset
@@ -915,9 +922,13 @@ __device__ __forceinline__ int ticket_tile(uint32_t k, int c, int nc) { return (
 // is stored from LDS while v's loads are in flight; u is parked in c's place.  A tile's total
 // is thus published one iteration before its workgroup waits on anything.  Tile indices are
 // kept wave-uniform (scalar) and every path issues the same loads, so the wait for c's polls
-// counts only the loads issued after them.  A workgroup only waits on smaller tiles, which are
-// claimed in counter order by running workgroups that publish and finish them without
-// waiting on it, so every wait ends.
+// counts only the loads issued after them.  Every value a tile waits for (tile totals,
+// interval totals, super-interval carries) is published in the local step of a smaller tile,
+// and a local step waits only on values published by smaller tiles' local steps (its
+// workgroup's previous finish waits likewise).  Tiles are claimed in counter order by running
+// workgroups, so the smallest tile whose local step has not run can always run it, and every
+// wait ends.  (A value published in a finish instead would wait behind that workgroup's next
+// local step, whose tile may be far later.)
 template <typename T, bool SEG, bool REV, bool EXCL, bool NT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 4 ? 3 : 2)))
 void k_scan(ScanArgs<T> a) {

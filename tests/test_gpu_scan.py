@@ -172,6 +172,31 @@ def test_small_anchor_variants(dev, dtype, A, A2):
 
 
 @pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("A,A2", [(2, 2), (4, 3)])
+def test_many_super_intervals_on_a_full_grid(dev, dtype, A, A2):
+    # Hundreds of super-interval carries with the full persistent grid: a workgroup's next tile
+    # is often the last of a later interval, so the carry must not wait behind that tile's
+    # local step (it once did, and about 1% of the scans of 2^31 - 1 f64 elements stalled
+    # until the bounded wait gave up).  Bits against the oracle, and a clear health word.
+    n = 1500 * T + 77
+    x = workloads.scan_values(n, dtype, seed=A * 7 + A2)
+    t = torch.from_numpy(x).to(dev)
+    code = 0 if dtype == F32 else 1
+    try:
+        det.det_debug_set_scan_anchors(A, A2)
+        for excl, rev in ((False, False), (True, True)):
+            flags = (1 if excl else 0) | (2 if rev else 0)
+            ws = torch.empty(det.det_scan_workspace_size(n, code, flags, 0), dtype=torch.uint8,
+                             device=dev)
+            got = det.det_scan(t, exclusive=excl, reverse=rev, ws=ws).cpu().numpy()
+            assert int(det.det_scan_error(ws).item()) == 0, (A, A2, excl, rev, "health word")
+            want = oracle.scan(x, exclusive=excl, reverse=rev, A=A, A2=A2)
+            assert bits_equal(got, want), (A, A2, excl, rev, first_mismatch(got, want))
+    finally:
+        det.det_debug_set_scan_anchors(0, 0)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
 def test_exclusive_into_unaligned_output(dev, dtype):
     # the exclusive readout aligns its 16-byte stores to y's address: y views at every
     # element offset within 16 bytes, both directions, ragged n
