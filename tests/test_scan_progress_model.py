@@ -1,0 +1,131 @@
+"""Forward progress of the persistent scan, checked on a model of its workgroups (CPU only).
+
+The model follows the kernel's schedule per workgroup: tiles are claimed from counter
+b mod nc (the k-th claim of counter c is tile k * nc + c); a tile's local step publishes its
+total and, for the last tile of an anchor interval, waits for the interval's tile totals and
+publishes the interval total; the last tile of a super-interval also waits for the
+super-interval's interval totals and the previous carry and publishes the next carry; a tile's
+finish waits for the earlier tile totals of its interval, the earlier interval totals of its
+super-interval and its carry.  Per workgroup: claim c, local(c), then repeatedly local(u),
+take the ticket claimed earlier as v and claim the next, finish(c), shift.  Random
+interleavings of workgroup steps must always finish.  With the carry forwarded from the
+finish of the super-interval's last tile instead (the schedule the kernel once had), the
+model finds the cycle: that finish waits behind the workgroup's next local step, which can
+close a later interval whose tiles' workgroups wait for the carry.
+"""
+import random
+
+import pytest
+
+
+class Model:
+    def __init__(self, ntiles, A, A2, nwg, carry_in_local, seed):
+        self.N, self.A, self.A2 = ntiles, A, A2
+        self.nc = min(8, nwg)
+        self.ctr = [0] * self.nc
+        self.agg, self.G, self.carry = set(), set(), {0}   # carry[0]: the identity, always known
+        self.local_carry = carry_in_local
+        self.rng = random.Random(seed)
+        self.wgs = [self.program(b) for b in range(nwg)]
+        self.pending = [next(w) for w in self.wgs]          # each yields (wait-set, action)
+
+    def claim(self, b):
+        c = b % self.nc
+        t = self.ctr[c] * self.nc + c
+        self.ctr[c] += 1
+        return t
+
+    def lb(self, t):
+        q = t // self.A
+        return q, t - q * self.A, q // self.A2, q - (q // self.A2) * self.A2
+
+    def local(self, t):
+        # publish the tile total, then (anchors) the interval total and (super-interval
+        # anchors, with the carry forwarded here) the next carry
+        yield (set(), lambda: self.agg.add(t))
+        q, cnt, Q, qcnt = self.lb(t)
+        if cnt == self.A - 1 and t + 1 < self.N:
+            need = {("a", q * self.A + i) for i in range(cnt)}
+            yield (need, lambda: self.G.add(q))
+            if self.local_carry and qcnt == self.A2 - 1:
+                need = {("g", Q * self.A2 + i) for i in range(qcnt)} | {("c", Q)}
+                yield (need, lambda: self.carry.add(Q + 1))
+
+    def finish(self, t):
+        q, cnt, Q, qcnt = self.lb(t)
+        need = ({("a", q * self.A + i) for i in range(cnt)}
+                | {("g", Q * self.A2 + i) for i in range(qcnt)} | {("c", Q)})
+        sanchor = cnt == self.A - 1 and t + 1 < self.N and qcnt == self.A2 - 1
+        if sanchor and not self.local_carry:
+            yield (need, lambda: self.carry.add(Q + 1))
+        else:
+            yield (need, lambda: None)
+
+    def program(self, b):
+        box = {}
+        yield (set(), lambda: box.__setitem__("c", self.claim(b)))
+        c = box["c"]
+        if c >= self.N:
+            return
+        yield (set(), lambda: box.__setitem__("k", self.claim(b)))
+        yield from self.local(c)
+        u = box["k"]
+        if u < self.N:
+            yield (set(), lambda: box.__setitem__("k", self.claim(b)))
+        while True:
+            if u < self.N:
+                yield from self.local(u)
+            v = box["k"] if u < self.N else self.N
+            if v < self.N:
+                yield (set(), lambda: box.__setitem__("k", self.claim(b)))
+            yield from self.finish(c)
+            if u >= self.N:
+                return
+            c, u = u, v
+
+    def ready(self, need):
+        for kind, i in need:
+            if kind == "a" and i not in self.agg:
+                return False
+            if kind == "g" and i not in self.G:
+                return False
+            if kind == "c" and i not in self.carry:
+                return False
+        return True
+
+    def run(self):
+        """True if every workgroup finishes; False at the first state where none can move."""
+        live = [b for b in range(len(self.wgs)) if self.pending[b] is not None]
+        while live:
+            movable = [b for b in live if self.ready(self.pending[b][0])]
+            if not movable:
+                return False
+            b = self.rng.choice(movable)
+            self.pending[b][1]()
+            try:
+                self.pending[b] = next(self.wgs[b])
+            except StopIteration:
+                self.pending[b] = None
+                live.remove(b)
+        return len(self.agg) == self.N
+
+
+@pytest.mark.parametrize("A,A2", [(2, 2), (4, 3), (3, 5), (1, 2), (8, 1)])
+def test_every_schedule_finishes(A, A2):
+    for seed in range(40):
+        rng = random.Random(seed)
+        ntiles = rng.randint(1, 900)
+        nwg = rng.choice([1, 2, 3, 8, 13, 40, 96])
+        assert Model(ntiles, A, A2, nwg, True, seed).run(), (A, A2, ntiles, nwg, seed)
+
+
+def test_the_carry_forwarded_from_the_finish_can_deadlock():
+    # the earlier schedule: some interleaving leaves every workgroup waiting
+    found = False
+    for seed in range(200):
+        rng = random.Random(1000 + seed)
+        ntiles = rng.randint(200, 900)
+        if not Model(ntiles, 2, 2, 64, False, seed).run():
+            found = True
+            break
+    assert found
