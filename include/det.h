@@ -111,11 +111,16 @@ det_status det_scan(const void* x, void* y, int64_t n, det_dtype dtype, unsigned
                     void* stream);
 
 /* Health word of the last det_scan run in workspace ws, for callers that want to verify it.
- * A scan's waits on its predecessors are bounded; a wait that runs past its bound (only a
- * hardware fault or broken offsets precondition can cause one) sets this word and leaves y
- * unspecified.  Enqueues on `stream` a copy of the word into *out (device int32: 0 = every
- * wait ended normally, 1 = some wait gave up); returns without waiting.  ws: the workspace
- * the scan used (device); out: device int32 (written).  DET_ERROR_INVALID_VALUE for NULL. */
+ * A scan of more than one anchor interval (more than 256 * 8192 elements) waits on status words
+ * that earlier tiles publish.  Each such wait is bounded: after 2 seconds of the GPU's constant
+ * 100 MHz clock it gives up, sets this word and leaves y unspecified while det_scan has already
+ * returned DET_SUCCESS.  Any failure of the kernel's forward progress (a broken offsets
+ * precondition, a hardware fault, a scheduler that never runs a workgroup holding a claimed
+ * tile) ends that way, never in a hang; a silent wrong result is possible only if a status
+ * word arrives corrupted yet tagged ready.  Shorter scans never wait and leave the word at 0.
+ * Enqueues on `stream` a copy of the word into *out (device int32: 0 = every wait ended
+ * normally, 1 = some wait gave up); returns without waiting.  ws: the workspace the scan used
+ * (device); out: device int32 (written).  DET_ERROR_INVALID_VALUE for NULL. */
 det_status det_scan_error(const void* ws, int32_t* out, void* stream);
 
 /* ------------------------------------------------------------------ scatter-add */
@@ -199,10 +204,35 @@ const char* det_status_string(det_status s);
 /* ------------------------------------------------------------------ test hooks */
 
 /* Not part of the stable interface.  Overrides how the work is spread over the GPU, for the
- * tests that show the bits do not depend on it: grid_wgs > 0 caps the number of workgroups
- * of the sum and scan kernels (0 = default); sum_chunk_log2 in [14, 24] sets the elements per
- * sum partial (0 = default).  Process-wide; returns DET_ERROR_INVALID_VALUE when out of range. */
-det_status det_debug_set_launch(int grid_wgs, int sum_chunk_log2);
+ * tests that show the bits depend on neither the block count nor the occupancy:
+ *   grid_wgs > 0 sets the number of workgroups of the sum kernel and of the look-back scan
+ *     kernel, also beyond the number that fit on the GPU at once (workgroups that start late
+ *     claim their tiles when they start); 0 = the default;
+ *   extra_lds_bytes in [0, 65536] adds that much dynamic LDS to every workgroup of the sum,
+ *     look-back scan and radix-sort kernels, which lowers how many fit per compute unit.
+ * Process-wide; DET_ERROR_INVALID_VALUE when out of range. */
+det_status det_debug_set_launch(int grid_wgs, int extra_lds_bytes);
+
+/* Not part of the stable interface.  chunk_log2 in [14, 24] sets the elements per partial of
+ * the sum's first level (0 = default, 14).  Process-wide; DET_ERROR_INVALID_VALUE when out of
+ * range. */
+det_status det_debug_set_sum_chunk(int chunk_log2);
+
+/* Not part of the stable interface.  The launch shape the library last used: the grid of the
+ * sum kernel's first level, the grid of the look-back scan kernel and the scan workgroups the
+ * runtime reported resident per compute unit for that launch (with its extra LDS).  Any
+ * pointer may be NULL; values are 0 before the first such launch. */
+void det_debug_last_launch(int64_t* sum_grid, int64_t* scan_grid, int64_t* scan_per_cu);
+
+/* Not part of the stable interface.  Seeded pauses in the look-back scan: with max_us > 0,
+ * the publishing thread of one status publication in four (tile totals, interval totals,
+ * super-interval carries) first pauses for a time in [0, max_us] microseconds chosen by a
+ * hash of seed, tile and publication kind, so successors find predecessors' status words
+ * ready or not at different moments (drjit-core pull request "Make CUDA floating-point prefix
+ * sums deterministic", section "Root cause": results must not depend on the states a tile
+ * observes).  max_us in [0, 1000], 0 = off.  Process-wide; DET_ERROR_INVALID_VALUE when out
+ * of range. */
+det_status det_debug_set_scan_delay(unsigned seed, int max_us);
 
 /* Not part of the stable interface.  Replaces the scan's anchor constants (tiles per anchor
  * interval A, intervals per super-interval A2; each in [1, 256], 0 = the spec's 256) so tests

@@ -15,32 +15,47 @@
 
 namespace det {
 
-static LaunchOverride g_override = {0, 0, 0, 0};
+static LaunchOverride g_override = {0, 0, 0, 0, 0, 0u, 0u};
 
 const LaunchOverride& launch_override() { return g_override; }
 
-int64_t resident_wgs(const void* fn, int block) {
+static std::atomic<int64_t> g_last_sum_grid{0}, g_last_scan_grid{0}, g_last_scan_per_cu{0};
+
+void note_sum_grid(int64_t grid) { g_last_sum_grid.store(grid, std::memory_order_relaxed); }
+
+void note_scan_grid(int64_t grid, int64_t per_cu) {
+    g_last_scan_grid.store(grid, std::memory_order_relaxed);
+    g_last_scan_per_cu.store(per_cu, std::memory_order_relaxed);
+}
+
+int64_t resident_wgs(const void* fn, int block, int dyn_lds, int* per_cu_out) {
     struct Entry {
         int dev;
         const void* fn;
-        int block;
+        int block, lds, per_cu;
         int64_t wgs;
     };
     static std::mutex mu;
-    static Entry cache[64];
+    static Entry cache[128];
     static int used = 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     std::lock_guard<std::mutex> lock(mu);
     for (int i = 0; i < used; ++i)
-        if (cache[i].dev == dev && cache[i].fn == fn && cache[i].block == block)
+        if (cache[i].dev == dev && cache[i].fn == fn && cache[i].block == block &&
+            cache[i].lds == dyn_lds) {
+            if (per_cu_out) *per_cu_out = cache[i].per_cu;
             return cache[i].wgs;
+        }
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, (size_t)dyn_lds) !=
+            hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
-    const int64_t wgs = (int64_t)(per_cu < 1 ? 1 : per_cu) * cus;
-    if (used < 64) cache[used++] = Entry{dev, fn, block, wgs};
+    if (per_cu < 1) per_cu = 1;
+    const int64_t wgs = (int64_t)per_cu * cus;
+    if (used < 128) cache[used++] = Entry{dev, fn, block, dyn_lds, per_cu, wgs};
+    if (per_cu_out) *per_cu_out = per_cu;
     return wgs;
 }
 
@@ -308,12 +323,30 @@ const char* det_status_string(det_status s) {
     return "DET_UNKNOWN_STATUS";
 }
 
-det_status det_debug_set_launch(int grid_wgs, int sum_chunk_log2) {
-    if (grid_wgs < 0) return DET_ERROR_INVALID_VALUE;
-    if (sum_chunk_log2 != 0 && (sum_chunk_log2 < 14 || sum_chunk_log2 > 24))
+det_status det_debug_set_launch(int grid_wgs, int extra_lds_bytes) {
+    if (grid_wgs < 0 || extra_lds_bytes < 0 || extra_lds_bytes > kMaxExtraLds)
         return DET_ERROR_INVALID_VALUE;
     g_override.grid_wgs = grid_wgs;
-    g_override.sum_chunk_log2 = sum_chunk_log2;
+    g_override.extra_lds = extra_lds_bytes;
+    return DET_SUCCESS;
+}
+
+det_status det_debug_set_sum_chunk(int chunk_log2) {
+    if (chunk_log2 != 0 && (chunk_log2 < 14 || chunk_log2 > 24)) return DET_ERROR_INVALID_VALUE;
+    g_override.sum_chunk_log2 = chunk_log2;
+    return DET_SUCCESS;
+}
+
+void det_debug_last_launch(int64_t* sum_grid, int64_t* scan_grid, int64_t* scan_per_cu) {
+    if (sum_grid) *sum_grid = g_last_sum_grid.load(std::memory_order_relaxed);
+    if (scan_grid) *scan_grid = g_last_scan_grid.load(std::memory_order_relaxed);
+    if (scan_per_cu) *scan_per_cu = g_last_scan_per_cu.load(std::memory_order_relaxed);
+}
+
+det_status det_debug_set_scan_delay(unsigned seed, int max_us) {
+    if (max_us < 0 || max_us > 1000) return DET_ERROR_INVALID_VALUE;
+    g_override.delay_seed = seed;
+    g_override.delay_us = (uint32_t)max_us;
     return DET_SUCCESS;
 }
 

@@ -11,12 +11,20 @@ namespace det {
 
 // Launch overrides for the shape-invariance tests (0 = default).
 struct LaunchOverride {
-    int grid_wgs;
+    int grid_wgs;        // workgroups of the sum and look-back scan kernels
+    int extra_lds;       // dynamic LDS bytes added to k_scan, k_sum_chunks and the radix kernels
     int sum_chunk_log2;
-    int scan_A;    // test-only scan anchor constants (0 = the spec's)
+    int scan_A;          // test-only scan anchor constants (0 = the spec's)
     int scan_A2;
+    uint32_t delay_seed; // test-only: seeded delays before the scan's status publications
+    uint32_t delay_us;   //   (at most this many microseconds each; 0 = none)
 };
 const LaunchOverride& launch_override();
+constexpr int kMaxExtraLds = 65536;   // largest extra_lds the test hook accepts
+
+// What the most recent launches used (for the tests that show the launch shape changed).
+void note_sum_grid(int64_t grid);
+void note_scan_grid(int64_t grid, int64_t per_cu);
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline size_t dtype_size(det_dtype d) { return d == DET_F64 ? 8 : 4; }   // f32, i32: 4
@@ -62,9 +70,11 @@ det_status scatter_running_launch(const void* values, const int32_t* index, int6
                                   int64_t row_len, det_dtype dt, void* out, int64_t num_out,
                                   void* prev, int64_t* n_skipped, void* ws, hipStream_t s);
 
-// Workgroups of `block` threads of kernel `fn` that are resident on the current device at once
-// (occupancy x compute units), cached per device and kernel; 0 if the runtime cannot tell.
-int64_t resident_wgs(const void* fn, int block);
+// Workgroups of `block` threads of kernel `fn` with `dyn_lds` bytes of dynamic LDS that are
+// resident on the current device at once (occupancy x compute units), cached per device,
+// kernel and LDS size; 0 if the runtime cannot tell.  *per_cu (optional) receives the
+// occupancy per compute unit.
+int64_t resident_wgs(const void* fn, int block, int dyn_lds = 0, int* per_cu = nullptr);
 
 // Compute units of the current device (cached per device); 0 if the runtime cannot tell.
 int cu_count();

@@ -104,15 +104,29 @@ __device__ __forceinline__ void publish(uint64_t* slot, const Seg<T>& s) {
     }
 }
 
-// Spin bound: a predecessor's slot is normally ready within microseconds.  Past the bound the
-// wait gives up and raises the error word, so no wave can wait forever.
-constexpr uint32_t kSpinLimit = 1u << 24;
+// Wait bound: a predecessor's slot is normally ready within microseconds.  A wait that has
+// polled for more than kWaitTicks of the GPU's constant 100 MHz clock (2 seconds) gives up and
+// raises the error word, so no wave can wait forever; the scan's result is then unspecified.
+constexpr uint64_t kWaitTicks = 200000000ull;
+
+// Called once per unsuccessful poll; true once the wait has lasted past the bound.  The clock
+// is read on the first poll and then every 256th.
+__device__ __forceinline__ bool wait_expired(uint32_t& polls, uint64_t& t0) {
+    if ((polls++ & 255u) != 0u) return false;
+    const uint64_t now = __builtin_amdgcn_s_memrealtime();
+    if (polls == 1u) {
+        t0 = now;
+        return false;
+    }
+    return now - t0 > kWaitTicks;
+}
 
 __device__ __forceinline__ uint64_t wait_word(uint64_t* w, uint32_t* err) {
     uint64_t v = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t spins = 0;
+    uint32_t polls = 0;
+    uint64_t t0 = 0;
     while (!((v >> 32) & kReady)) {
-        if (++spins > kSpinLimit) {
+        if (wait_expired(polls, t0)) {
             __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
@@ -177,12 +191,13 @@ template <typename T>
 __device__ __forceinline__ Seg<T> poll_finish_set(uint64_t* w, const uint64_t* slot, bool use,
                                                   uint32_t* err) {
     constexpr int SW = slot_words<T>();
-    uint32_t spins = 0;
+    uint32_t polls = 0;
+    uint64_t t0 = 0;
     for (;;) {
         bool all = (w[0] >> 32) & kReady;
         if constexpr (SW == 2) all = all && ((w[1] >> 32) & kReady);
         if (all) break;
-        if (++spins > kSpinLimit) {
+        if (wait_expired(polls, t0)) {
             __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
@@ -543,7 +558,28 @@ struct ScanArgs {
     int excl;
     int A;               // tiles per anchor interval (the spec's 256; smaller only in tests)
     int A2;              // intervals per super-interval (likewise)
+    uint32_t delay_seed; // test only: seeded pauses before status publications (delay_us > 0)
+    uint32_t delay_us;
 };
+
+// Test only (delay_us > 0): a pause of up to delay_us microseconds, chosen by a hash of the
+// seed, the tile and the kind of publication, taken by the publishing thread of one
+// publication in four before it writes its status words.  Successors then find those words
+// ready or not ready at different times from seed to seed, which must not change a bit.
+template <typename T>
+__device__ __forceinline__ void test_delay(const ScanArgs<T>& a, int j, uint32_t kind) {
+    if (a.delay_us == 0u) return;
+    uint32_t h = a.delay_seed ^ ((uint32_t)j * 0x9E3779B1u) ^ (kind * 0x85EBCA77u);
+    h ^= h >> 15;
+    h *= 0x2C1B3C6Du;
+    h ^= h >> 12;
+    h *= 0x297A2D39u;
+    h ^= h >> 15;
+    if (h & 3u) return;
+    const uint64_t ticks = (uint64_t)((h >> 2) % (a.delay_us + 1u)) * 100u;   // 100 MHz clock
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(8);
+}
 
 // A tile's head words from the bitmap: word i of tile j is bitmap word 256 j + i, i in [0, 256]
 // (word 256 is the next tile's first).  Every thread loads two words, the second the same for
@@ -865,7 +901,12 @@ __device__ __forceinline__ void finish_tile(const ScanArgs<T>& a, int j, const L
 // this chip, well below the tile rate at full bandwidth).  Each counter's tiles are claimed in
 // order, and workgroups 0 .. nc-1, the first on their counters, are dispatched no later than
 // any other workgroup of their counter, so every counter keeps a running workgroup until its
-// tiles run out and every tile a workgroup waits on is, or will be, claimed by one.
+// tiles run out and every tile a workgroup waits on is, or will be, claimed by one.  A grid
+// larger than the resident count (a test hook) changes nothing here as long as there are no
+// more counters than resident workgroups (the host sees to it): a workgroup claims tiles only
+// once it runs, and the first of each counter runs until that counter's tiles are gone.  (On
+// MI355X workgroup b goes to XCD b mod 8 and each XCD dispatches its share in order, so with 8
+// counters the first workgroup of each counter is the first on its XCD.)
 constexpr int kCounters = 8;
 constexpr int kCounterStride = 64;   // words between counters
 
@@ -884,7 +925,10 @@ __device__ __forceinline__ void publish_interval_total(const ScanArgs<T>& a, int
     poll_issue<T>(pa, slot, tid < lb.cnt, slot, false);
     const Seg<T> m = poll_finish_set<T>(pa.w, slot, tid < lb.cnt, a.err);
     const Seg<T> G = block_pw<SEG, T>(tid == a.A - 1 ? aggu : m, lane, wave, s_tmp);
-    if (tid == 0) publish<T>(a.gtot + (size_t)lb.q * SW, G);
+    if (tid == 0) {
+        test_delay<T>(a, u, 1u);
+        publish<T>(a.gtot + (size_t)lb.q * SW, G);
+    }
     // The super-interval's last tile forwards the carry CC_{Q+1} = CC_Q + PW(all A2 interval
     // totals of Q) here, in its local step, where it waits only on smaller tiles and the
     // previous carry.  (Forwarded from the tile's finish instead, the carry waited behind the
@@ -899,6 +943,7 @@ __device__ __forceinline__ void publish_interval_total(const ScanArgs<T>& a, int
     if (tid == 0) {
         const Seg<T> CC = lb.Q > 0 ? wait_slot<T>(a.carry + (size_t)lb.Q * SW, a.err)
                                    : seg_ident<T>();
+        test_delay<T>(a, u, 2u);
         publish<T>(a.carry + (size_t)(lb.Q + 1) * SW, op<SEG>(CC, H));
     }
 }
@@ -968,6 +1013,7 @@ void k_scan(ScanArgs<T> a) {
     Seg<T> aggc = tile_local<T, SEG, REV>(a, c, r, hbc, Pc, pc, s_heads[0], s_wtot, tid, lane0,
                                           wave, hwc);
     if (tid == 0) {
+        test_delay<T>(a, c, 0u);
         publish<T>(a.agg + (size_t)c * SW, aggc);
         s_tick[1] = ticket_tile(claimed, ctr, nc);
     }
@@ -1003,7 +1049,10 @@ void k_scan(ScanArgs<T> a) {
         if (have_u) {
             aggu = tile_local<T, SEG, REV>(a, u, r, hbu, Pu, pu, s_heads[par ^ 1], s_wtot, tid,
                                            lane, wave, hwu);
-            if (tid == 0) publish<T>(a.agg + (size_t)u * SW, aggu);
+            if (tid == 0) {
+                test_delay<T>(a, u, 0u);
+                publish<T>(a.agg + (size_t)u * SW, aggu);
+            }
             publish_interval_total<SEG, T>(a, u, aggu, s_tmp, tid, lane, wave);
         }
         // the ticket claimed last iteration (v, if u exists); then c's look-back polls go out
@@ -1071,6 +1120,7 @@ __global__ __launch_bounds__(256) void k_scan_small(ScanArgs<T> a0) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (blockIdx.x == 0 && tid == 0) *a0.err = 0u;   // nothing here waits: the health word is 0
     T* pk = s_park[wave];
     T* xs = s_x[wave];
     const uint32_t* hbs = s_hbits[SEG ? wave : 0];
@@ -1133,6 +1183,8 @@ __global__ __launch_bounds__(256) void k_scan_two(ScanArgs<T> a0) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = (int)blockIdx.x;
+    // nothing here waits: the first launch leaves the health word at 0
+    if (!SECOND && j == 0 && blockIdx.y == 0 && tid == 0) *a0.err = 0u;
     ScanArgs<T> a = a0;
     a.x += (int64_t)blockIdx.y * a0.col_stride;
     a.y += (int64_t)blockIdx.y * a0.col_stride;
@@ -1439,19 +1491,32 @@ det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t*
     const void* fn = nt ? k_scan_fn<T, true>(mode) : k_scan_fn<T, false>(mode);
     // Persistent grid: as many workgroups as are resident at once.  More would only queue
     // behind them, and a workgroup that starts late has lost its pipeline's overlap.
-    int64_t grid = resident_wgs(fn, 256);
-    if (grid <= 0) return DET_ERROR_LAUNCH;
+    const int extra = ov.extra_lds;
+    int per_cu = 0;
+    const int64_t resident = resident_wgs(fn, 256, extra, &per_cu);
+    if (resident <= 0) return DET_ERROR_LAUNCH;
+    int64_t grid = resident;
     // at most 3 workgroups per CU: for f32, 4 resident per CU measured 1-3% slower on MI355X
     // (more tiles in flight than the memory system turns into bandwidth); f64 fits 2
     const int64_t cap = 3 * (int64_t)cu_count();
     if (cap > 0 && grid > cap) grid = cap;
     if (grid > L.ntiles) grid = L.ntiles;
-    if (ov.grid_wgs > 0 && grid > ov.grid_wgs) grid = ov.grid_wgs;
-    a.nctr = (int)(grid < kCounters ? grid : kCounters);
+    // the test hook sets the grid, also beyond the resident count: workgroups that start late
+    // claim their tiles when they start, and those past the last tile return at once
+    if (ov.grid_wgs > 0) grid = ov.grid_wgs;
+    note_scan_grid(grid, per_cu);
+    // one counter per workgroup that surely runs: never more counters than resident
+    // workgroups, or a counter could be left with none running while others wait on its tiles
+    int64_t nctr = grid < kCounters ? grid : kCounters;
+    if (nctr > resident) nctr = resident;
+    a.nctr = (int)nctr;
+    a.delay_seed = ov.delay_seed;
+    a.delay_us = ov.delay_us;
     void* args[] = {&a};
     KernelTimer kt(sizeof(T) == 8 ? "k_scan<f64>" : __is_same(T, float) ? "k_scan<f32>"
                                                                         : "k_scan<i32>", s);
-    if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, 0, s) != hipSuccess)
+    if (hipLaunchKernel(fn, dim3((unsigned)grid), dim3(256), args, (size_t)extra, s) !=
+        hipSuccess)
         return DET_ERROR_LAUNCH;
     return launch_status();
 }

@@ -1201,6 +1201,8 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
     const uint32_t B = (uint32_t)num_out;
     const int passes = key_passes(num_out);
     const unsigned grid = (unsigned)L.nchunks;
+    // test hook: extra dynamic LDS per workgroup lowers the radix kernels' occupancy
+    const size_t lds = (size_t)launch_override().extra_lds;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
         const bool first = p == 0;
@@ -1213,13 +1215,13 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
         {
             KernelTimer kt("k_radix_hist", s);
             if (first)
-                k_radix_hist<true, uint32_t><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb,
+                k_radix_hist<true, uint32_t><<<grid, 256, lds, s>>>(kin, n, ctrl, B, shift, nb,
                                                                   L.nchunks, (int)L.H, hist);
             else if (k16)
-                k_radix_hist<false, uint16_t><<<grid, 256, 0, s>>>(kin16, n, ctrl, B, shift, nb,
+                k_radix_hist<false, uint16_t><<<grid, 256, lds, s>>>(kin16, n, ctrl, B, shift, nb,
                                                                    L.nchunks, (int)L.H, hist);
             else
-                k_radix_hist<false, uint32_t><<<grid, 256, 0, s>>>(kin, n, ctrl, B, shift, nb,
+                k_radix_hist<false, uint32_t><<<grid, 256, lds, s>>>(kin, n, ctrl, B, shift, nb,
                                                                    L.nchunks, (int)L.H, hist);
         }
         // bucket offsets; the first pass also counts the keys in range into ctrl[0]
@@ -1231,16 +1233,16 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
         uint32_t* ko = keys[p & 1];
         uint16_t* ko16 = reinterpret_cast<uint16_t*>(ko);
         if (first && k16)
-            k_radix_scatter<P, true, ROWS, uint16_t, uint32_t><<<grid, kRadixNT<P>, 0, s>>>(
+            k_radix_scatter<P, true, ROWS, uint16_t, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
                 kin, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         else if (first)
-            k_radix_scatter<P, true, ROWS, uint32_t, uint32_t><<<grid, kRadixNT<P>, 0, s>>>(
+            k_radix_scatter<P, true, ROWS, uint32_t, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
                 kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         else if (k16)
-            k_radix_scatter<P, false, ROWS, uint16_t, uint16_t><<<grid, kRadixNT<P>, 0, s>>>(
+            k_radix_scatter<P, false, ROWS, uint16_t, uint16_t><<<grid, kRadixNT<P>, lds, s>>>(
                 kin16, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         else
-            k_radix_scatter<P, false, ROWS, uint32_t, uint32_t><<<grid, kRadixNT<P>, 0, s>>>(
+            k_radix_scatter<P, false, ROWS, uint32_t, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
                 kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         st = launch_status();
         if (st != DET_SUCCESS) return st;

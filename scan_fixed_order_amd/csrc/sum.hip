@@ -144,10 +144,13 @@ det_status sum_impl(const T* x, int64_t n, T* out, char* ws, hipStream_t s) {
     for (;;) {
         const int64_t nchunks = ceil_div(m, int64_t(1) << clog2);
         T* dst = (nchunks == 1) ? out : reinterpret_cast<T*>(ws);
+        // one workgroup per chunk; the test hook sets any grid (workgroups stride over chunks)
         int64_t grid = nchunks;
-        if (ov.grid_wgs > 0 && grid > ov.grid_wgs) grid = ov.grid_wgs;
+        if (ov.grid_wgs > 0) grid = ov.grid_wgs;
+        if (src == x) note_sum_grid(grid);
         KernelTimer kt(sizeof(T) == 4 ? "k_sum_chunks<f32>" : "k_sum_chunks<f64>", s);
-        k_sum_chunks<T><<<dim3((unsigned)grid), dim3(256), 0, s>>>(src, m, clog2, nchunks, dst);
+        k_sum_chunks<T><<<dim3((unsigned)grid), dim3(256), (size_t)ov.extra_lds, s>>>(
+            src, m, clog2, nchunks, dst);
         det_status st = launch_status();
         if (st != DET_SUCCESS || nchunks == 1) return st;
         src = dst;

@@ -38,6 +38,10 @@ class DetError(RuntimeError):
         self.status = status
 
 
+class ScanWaitError(RuntimeError):
+    """A look-back wait of det_scan gave up (its health word is set): the output is unspecified."""
+
+
 _lib = None
 
 
@@ -71,6 +75,10 @@ def lib() -> ctypes.CDLL:
     L.det_status_string.argtypes, L.det_status_string.restype = [i], ctypes.c_char_p
     L.det_scan_error.argtypes, L.det_scan_error.restype = [p, p, p], i
     L.det_debug_set_launch.argtypes, L.det_debug_set_launch.restype = [i, i], i
+    L.det_debug_set_sum_chunk.argtypes, L.det_debug_set_sum_chunk.restype = [i], i
+    L.det_debug_last_launch.argtypes = [ctypes.POINTER(i64)] * 3
+    L.det_debug_last_launch.restype = None
+    L.det_debug_set_scan_delay.argtypes, L.det_debug_set_scan_delay.restype = [u, i], i
     L.det_debug_set_scan_anchors.argtypes, L.det_debug_set_scan_anchors.restype = [i, i], i
     L.det_debug_kernel_timing.argtypes, L.det_debug_kernel_timing.restype = [i], i
     L.det_debug_kernel_report.argtypes = [ctypes.c_char_p, sz]
@@ -149,10 +157,16 @@ def det_scan_workspace_size(n: int, dtype_code: int, flags: int = 0, num_segment
 
 def det_scan(x: torch.Tensor, y: Optional[torch.Tensor] = None, exclusive: bool = False,
              reverse: bool = False, offsets: Optional[torch.Tensor] = None,
-             ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+             ws: Optional[torch.Tensor] = None, check: bool = False,
+             health: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Reproducible prefix sum of ``x`` (1-D).  ``offsets``: int64 device tensor [S+1]
     (0 = o_0 <= ... <= o_S = n) for a segmented scan.  int32 ``x`` gives wrapping integer
-    sums (the slot-allocation scan of count-scan-write)."""
+    sums (the slot-allocation scan of count-scan-write).
+
+    The library's look-back waits are bounded; one that gives up leaves ``y`` unspecified and
+    sets the workspace's health word.  ``health`` (device int32, one element) receives that
+    word without synchronising; ``check=True`` waits for the scan and raises ScanWaitError
+    when the word is set."""
     x = _flat(x)
     dt = _dtype_code(x, allow_int=True)
     n = x.numel()
@@ -168,6 +182,14 @@ def det_scan(x: torch.Tensor, y: Optional[torch.Tensor] = None, exclusive: bool 
     w = _workspace(det_scan_workspace_size(n, dt, flags, max(nseg, 0)), x.device, ws)
     _check(lib().det_scan(_dev_ptr(x), _dev_ptr(y), n, dt, flags, _dev_ptr(offsets), nseg,
                           _dev_ptr(w), w.numel(), _stream(x.device)), "det_scan")
+    if check or health is not None:
+        h = health if health is not None else torch.empty((), dtype=torch.int32, device=x.device)
+        if h.dtype != torch.int32 or h.numel() != 1:
+            raise ValueError("health must be an int32 tensor with one element")
+        _check(lib().det_scan_error(_dev_ptr(w), _dev_ptr(h), _stream(x.device)),
+               "det_scan_error")
+        if check and int(h.item()) != 0:
+            raise ScanWaitError("det_scan: a look-back wait gave up; the output is unspecified")
     return y
 
 
@@ -300,8 +322,28 @@ def det_status_string(status: int) -> str:
     return lib().det_status_string(status).decode()
 
 
-def det_debug_set_launch(grid_wgs: int = 0, sum_chunk_log2: int = 0) -> None:
-    _check(lib().det_debug_set_launch(grid_wgs, sum_chunk_log2), "det_debug_set_launch")
+def det_debug_set_launch(grid_wgs: int = 0, extra_lds_bytes: int = 0) -> None:
+    """Test hook: workgroups of the sum and look-back scan kernels (0 = default; may exceed the
+    resident count) and extra dynamic LDS per workgroup (lowers occupancy)."""
+    _check(lib().det_debug_set_launch(grid_wgs, extra_lds_bytes), "det_debug_set_launch")
+
+
+def det_debug_set_sum_chunk(chunk_log2: int = 0) -> None:
+    """Test hook: elements per partial of the sum's first level, as a power of two (0 = 14)."""
+    _check(lib().det_debug_set_sum_chunk(chunk_log2), "det_debug_set_sum_chunk")
+
+
+def det_debug_last_launch() -> dict:
+    """Test hook: {sum_grid, scan_grid, scan_per_cu} of the library's most recent launches."""
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    lib().det_debug_last_launch(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c))
+    return {"sum_grid": a.value, "scan_grid": b.value, "scan_per_cu": c.value}
+
+
+def det_debug_set_scan_delay(seed: int = 0, max_us: int = 0) -> None:
+    """Test hook: seeded pauses of up to ``max_us`` microseconds before the look-back scan's
+    status publications (0 = off)."""
+    _check(lib().det_debug_set_scan_delay(seed & 0xFFFFFFFF, max_us), "det_debug_set_scan_delay")
 
 
 def det_debug_set_scan_anchors(A: int = 0, A2: int = 0) -> None:

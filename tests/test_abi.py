@@ -151,9 +151,20 @@ def test_alignment_is_checked():
 def test_debug_hook_range():
     lib = det.lib()
     assert lib.det_debug_set_launch(-1, 0) == E_INVALID
-    assert lib.det_debug_set_launch(0, 13) == E_INVALID
-    assert lib.det_debug_set_launch(0, 25) == E_INVALID
+    assert lib.det_debug_set_launch(0, -1) == E_INVALID
+    assert lib.det_debug_set_launch(0, 65537) == E_INVALID
+    assert lib.det_debug_set_launch(5000, 65536) == 0
     assert lib.det_debug_set_launch(0, 0) == 0
+    assert lib.det_debug_set_sum_chunk(13) == E_INVALID
+    assert lib.det_debug_set_sum_chunk(25) == E_INVALID
+    assert lib.det_debug_set_sum_chunk(24) == 0
+    assert lib.det_debug_set_sum_chunk(0) == 0
+    assert lib.det_debug_set_scan_delay(1, -1) == E_INVALID
+    assert lib.det_debug_set_scan_delay(1, 1001) == E_INVALID
+    assert lib.det_debug_set_scan_delay(0xFFFFFFFF, 1000) == 0
+    assert lib.det_debug_set_scan_delay(0, 0) == 0
+    last = det.det_debug_last_launch()
+    assert set(last) == {"sum_grid", "scan_grid", "scan_per_cu"}
     assert lib.det_debug_set_scan_anchors(257, 0) == E_INVALID
     assert lib.det_debug_set_scan_anchors(0, -1) == E_INVALID
     assert lib.det_debug_set_scan_anchors(0, 0) == 0

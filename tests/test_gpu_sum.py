@@ -96,10 +96,15 @@ def test_launch_shape_invariance(dev, dtype):
     want = np.asarray(oracle.det_sum(x), dtype)
     t = torch.from_numpy(x).to(dev)
     try:
-        for grid, clog2 in [(0, 0), (1, 0), (7, 0), (256, 0), (512, 0), (1024, 0), (0, 16),
-                            (3, 18), (0, 20), (1, 24)]:
-            det.det_debug_set_launch(grid, clog2)
+        for grid, clog2, lds in [(0, 0, 0), (1, 0, 0), (7, 0, 0), (256, 0, 0), (512, 0, 0),
+                                 (1024, 0, 0), (0, 16, 0), (3, 18, 0), (0, 20, 0), (1, 24, 0),
+                                 (100000, 0, 0), (0, 0, 40000), (2048, 0, 65536)]:
+            det.det_debug_set_launch(grid, lds)
+            det.det_debug_set_sum_chunk(clog2)
             got = det.det_sum(t).cpu().numpy()
-            assert bits_equal(got, want), (grid, clog2)
+            assert bits_equal(got, want), (grid, clog2, lds)
+            if grid:
+                assert det.det_debug_last_launch()["sum_grid"] == grid
     finally:
         det.det_debug_set_launch(0, 0)
+        det.det_debug_set_sum_chunk(0)

@@ -12,6 +12,12 @@ interleavings of workgroup steps must always finish.  With the carry forwarded f
 finish of the super-interval's last tile instead (the schedule the kernel once had), the
 model finds the cycle: that finish waits behind the workgroup's next local step, which can
 close a later interval whose tiles' workgroups wait for the carry.
+
+Grids larger than the number of workgroups that fit at once (a test hook of the library) are
+modelled by a dispatch queue: workgroups start in index order, at most `resident` at a time,
+and a waiting one starts only when a running one has returned.  The host uses no more claim
+counters than resident workgroups; with more, a counter can be left with no running workgroup
+while the running ones wait on its tiles, and the model finds that stall.
 """
 import random
 
@@ -19,9 +25,10 @@ import pytest
 
 
 class Model:
-    def __init__(self, ntiles, A, A2, nwg, carry_in_local, seed):
+    def __init__(self, ntiles, A, A2, nwg, carry_in_local, seed, resident=None):
         self.N, self.A, self.A2 = ntiles, A, A2
-        self.nc = min(8, nwg)
+        self.resident = nwg if resident is None else min(resident, nwg)
+        self.nc = min(8, nwg, self.resident)      # the host never uses more counters
         self.ctr = [0] * self.nc
         self.agg, self.G, self.carry = set(), set(), {0}   # carry[0]: the identity, always known
         self.local_carry = carry_in_local
@@ -95,7 +102,9 @@ class Model:
 
     def run(self):
         """True if every workgroup finishes; False at the first state where none can move."""
-        live = [b for b in range(len(self.wgs)) if self.pending[b] is not None]
+        nwg = len(self.wgs)
+        live = list(range(self.resident))        # dispatched in index order
+        queued = self.resident                    # next workgroup waiting for a slot
         while live:
             movable = [b for b in live if self.ready(self.pending[b][0])]
             if not movable:
@@ -107,7 +116,10 @@ class Model:
             except StopIteration:
                 self.pending[b] = None
                 live.remove(b)
-        return len(self.agg) == self.N
+                if queued < nwg:                  # its slot goes to the next workgroup
+                    live.append(queued)
+                    queued += 1
+        return len(self.agg) == self.N and queued == nwg
 
 
 @pytest.mark.parametrize("A,A2", [(2, 2), (4, 3), (3, 5), (1, 2), (8, 1)])
@@ -129,3 +141,25 @@ def test_the_carry_forwarded_from_the_finish_can_deadlock():
             found = True
             break
     assert found
+
+
+@pytest.mark.parametrize("A,A2", [(2, 2), (4, 3), (256, 256), (1, 1)])
+def test_grids_beyond_the_resident_count_finish(A, A2):
+    # more workgroups than fit at once: 1x to 16x the resident count, which itself ranges from
+    # a single workgroup to many; the waiting ones claim tiles only when they start
+    for seed in range(40):
+        rng = random.Random(5000 + seed)
+        ntiles = rng.randint(1, 700)
+        resident = rng.choice([1, 2, 3, 8, 9, 24, 64])
+        nwg = resident * rng.choice([1, 2, 4, 16])
+        assert Model(ntiles, A, A2, nwg, True, seed, resident).run(), (A, A2, ntiles, nwg,
+                                                                       resident, seed)
+
+
+def test_more_counters_than_resident_workgroups_can_stall():
+    # why the host caps the counters at the resident count: 8 counters, 3 resident workgroups
+    m = Model(239, 2, 2, 48, True, 0, resident=3)
+    m.nc = 8
+    m.wgs = [m.program(b) for b in range(48)]
+    m.pending = [next(w) for w in m.wgs]
+    assert not m.run()
