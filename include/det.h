@@ -74,6 +74,20 @@ size_t det_sum_workspace_size(int64_t n, det_dtype dtype);
 det_status det_sum(const void* x, int64_t n, det_dtype dtype, void* out, void* ws,
                    size_t ws_bytes, void* stream);
 
+/* det_sum for callers that cannot allocate device memory (code under HIP graph capture that
+ * must not call hipMalloc, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument and no allocation; the result bits are det_sum's.
+ * x, out, n, dtype, stream and the errors are det_sum's (n up to DET_MAX_N, beyond it
+ * DET_ERROR_TOO_LARGE); DET_ERROR_LAUNCH if the runtime cannot give the array's address.
+ * The partial sums live in a static device array of DET_SUM_NOALLOC_SCRATCH_BYTES bytes, one
+ * per GPU the library runs on, loaded with the library's code and held until the process
+ * ends; that size covers every n up to DET_MAX_N in f32 and f64.  Every call on one GPU uses
+ * that GPU's single array, which keeps the last call's partials: calls that overlap in time
+ * on one GPU (different streams or host threads without ordering) race and give unspecified
+ * results.  Calls ordered on one stream are safe. */
+#define DET_SUM_NOALLOC_SCRATCH_BYTES (1048576 + 256)
+det_status det_sum_noalloc(const void* x, int64_t n, det_dtype dtype, void* out, void* stream);
+
 /* ------------------------------------------------------------------ scan */
 
 /* Bytes of workspace det_scan needs. */

@@ -15,6 +15,9 @@
 
 namespace det {
 
+static_assert(DET_SUM_NOALLOC_SCRATCH_BYTES == kSumNoAllocBytes,
+              "the header and the library disagree on the no-allocation array's size");
+
 static LaunchOverride g_override = {0, 0, 0, 0, 0, 0u, 0u};
 
 const LaunchOverride& launch_override() { return g_override; }
@@ -167,6 +170,16 @@ det_status det_sum(const void* x, int64_t n, det_dtype dtype, void* out, void* w
         return DET_ERROR_INVALID_VALUE;
     if (!ws || !ws_aligned(ws) || ws_bytes < sum_workspace(n, dtype)) return DET_ERROR_WORKSPACE;
     return sum_launch(x, n, dtype, out, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+det_status det_sum_noalloc(const void* x, int64_t n, det_dtype dtype, void* out, void* stream) {
+    if (!valid_dtype(dtype)) return DET_ERROR_UNSUPPORTED;
+    if (n < 0) return DET_ERROR_INVALID_VALUE;
+    if (n > DET_MAX_N) return DET_ERROR_TOO_LARGE;
+    if (!out || (n > 0 && !x)) return DET_ERROR_INVALID_VALUE;
+    if (!elem_aligned(out, dtype_size(dtype)) || !elem_aligned(x, dtype_size(dtype)))
+        return DET_ERROR_INVALID_VALUE;
+    return sum_noalloc_launch(x, n, dtype, out, static_cast<hipStream_t>(stream));
 }
 
 size_t det_scan_workspace_size(int64_t n, det_dtype dtype, unsigned flags, int64_t num_segments) {

@@ -33,6 +33,10 @@ inline size_t dtype_size(det_dtype d) { return d == DET_F64 ? 8 : 4; }   // f32,
 size_t sum_workspace(int64_t n, det_dtype dt);
 det_status sum_launch(const void* x, int64_t n, det_dtype dt, void* out, void* ws, size_t ws_bytes,
                       hipStream_t s);
+// det_sum with the partials in the library's own per-GPU array (no workspace argument)
+constexpr size_t kSumNoAllocBytes = ((size_t)1 << 20) + 256;
+constexpr int kMaxDevices = 64;
+det_status sum_noalloc_launch(const void* x, int64_t n, det_dtype dt, void* out, hipStream_t s);
 
 // ---- scan
 constexpr int kScanV = 32;       // elements per lane

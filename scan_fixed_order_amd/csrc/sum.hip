@@ -16,6 +16,8 @@
 //            by a binary counter (right-nested fold of the leftover dyadic blocks at the end);
 //   levels = one launch writes one value per chunk; the next launch reduces those values the
 //            same way until one value remains, written to *out.
+#include <mutex>
+
 #include "det_device.h"
 #include "det_internal.h"
 
@@ -180,6 +182,40 @@ det_status sum_launch(const void* x, int64_t n, det_dtype dt, void* out, void* w
                                static_cast<char*>(ws), s);
     return sum_impl<double>(static_cast<const double*>(x), n, static_cast<double*>(out),
                             static_cast<char*>(ws), s);
+}
+
+// ---------------------------------------------------------------- det_sum_noalloc
+
+// The partials of det_sum_noalloc: one array per GPU, in the library's code object, so no
+// call allocates.  Its size covers every n up to 2^31 - 1 in f64 (131072 first-level partials
+// of 8 bytes, then 8 more).  Nothing in it needs to start at zero: each level writes every
+// partial before the next level reads it.  Host code never uses the array's name as an
+// address: that is a host-side stand-in; the device address comes from hipGetSymbolAddress,
+// once per device.
+static __device__ __align__(256) unsigned char scratch[kSumNoAllocBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+det_status sum_noalloc_launch(const void* x, int64_t n, det_dtype dt, void* out, hipStream_t s) {
+    if (sum_workspace(n, dt) > kSumNoAllocBytes) return DET_ERROR_TOO_LARGE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return DET_ERROR_LAUNCH;
+    void* ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            void* p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+                return DET_ERROR_LAUNCH;
+            g_scratch_ptr[dev] = p;
+        }
+        ptr = g_scratch_ptr[dev];
+    }
+    return sum_launch(x, n, dt, out, ptr, kSumNoAllocBytes, s);
 }
 
 }  // namespace det

@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
     p, i64, sz, u, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint, ctypes.c_int
     L.det_sum_workspace_size.argtypes, L.det_sum_workspace_size.restype = [i64, i], sz
     L.det_sum.argtypes, L.det_sum.restype = [p, i64, i, p, p, sz, p], i
+    L.det_sum_noalloc.argtypes, L.det_sum_noalloc.restype = [p, i64, i, p, p], i
     L.det_scan_workspace_size.argtypes, L.det_scan_workspace_size.restype = [i64, i, u, i64], sz
     L.det_scan.argtypes, L.det_scan.restype = [p, p, i64, i, u, p, i64, p, sz, p], i
     L.det_scatter_add_workspace_size.argtypes = [i64, i64, i64, i]
@@ -146,6 +147,19 @@ def det_sum(x: torch.Tensor, out: Optional[torch.Tensor] = None,
     w = _workspace(det_sum_workspace_size(n, dt), x.device, ws)
     _check(lib().det_sum(_dev_ptr(x), n, dt, _dev_ptr(out), _dev_ptr(w), w.numel(),
                          _stream(x.device)), "det_sum")
+    return out
+
+
+def det_sum_noalloc(x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """det_sum through the entry point that allocates nothing (its partials live in the
+    library's per-GPU array); ``out`` (one element, dtype of x) is filled and returned.  Calls
+    that overlap in time on one GPU race."""
+    x = _flat(x)
+    dt = _dtype_code(x)
+    if out.dtype != x.dtype or out.numel() != 1:
+        raise ValueError("out must be one element of x's dtype")
+    _check(lib().det_sum_noalloc(_dev_ptr(x), x.numel(), dt, _dev_ptr(out), _stream(x.device)),
+           "det_sum_noalloc")
     return out
 
 
