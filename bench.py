@@ -12,14 +12,19 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                 algorithmic bytes per launch over its average launch time, against 8 TB/s; and
                 `traffic`, the HBM bytes per launch that rocprofv3 counters measured for the same
                 kernel source (read from profiles/, null when that source has changed since);
+  attainable    what a plain streaming read and a plain copy reach on the same GPU in the same run;
   kernels       every library kernel of the step: launches per step, average ms;
-  ops           per operation: time, GB/s, Gelem/s, fraction of 8 TB/s, the non-deterministic
-                baseline's time on the same input (atomic-tail sum, per-element atomic
-                scatter, the ROCm library scan), the deterministic-mode overhead, and the number
-                of distinct results over repeated runs of each;
+  ops           per operation: time (mean, median, p10, p90), GB/s, Gelem/s, fraction of 8 TB/s,
+                the non-deterministic baselines on the same input and the deterministic-mode
+                overhead, distinct results over repeated runs (every output element of every
+                run compared with the first run on the device, and 64-bit fingerprints of the
+                baselines' outputs), the error against a double-precision reference next to the
+                baselines' errors, and the SHA-256 digest of the output bytes;
+  configs       every other configuration of the workload spec (see time_configs);
   cpu_baseline  the CPU oracle (single thread) on the same workload, timed on the host.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -48,6 +53,8 @@ def parse():
                     help="runs whose distinct results are counted (library and baselines)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip timing the other configurations (parity cases) of the spec")
+    ap.add_argument("--no-accuracy", action="store_true",
+                    help="skip the host-side error and digest computations")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain device copy of 2^log2n f32 (1 GiB each way at 2^28): "
                          "the known-size kernel that scales rocprofv3 byte counters")
@@ -107,22 +114,126 @@ def measured_traffic(kernel):
     return None
 
 
+def host_info():
+    model, mem = "unknown", None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                mem = round(int(line.split()[1]) / (1 << 20), 1)
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "mem_total_GiB": mem, "visible_cores": os.cpu_count(),
+            "usable_cores": usable}
+
+
+# ---------------------------------------------------------------- device helpers
+
+def ibits(t):
+    import torch
+    return t.view(torch.int64 if t.dtype == torch.float64 else torch.int32)
+
+
+def fingerprint(t):
+    """64-bit weighted sum (mod 2^64) of the output's bit patterns, computed on the device with
+    integer arithmetic (any order gives the same value); distinct outputs collide with
+    probability about 2^-64."""
+    import torch
+    b = ibits(t).reshape(-1).to(torch.int64)
+    w = torch.arange(1, b.numel() + 1, device=t.device, dtype=torch.int64)
+    w = w * 0x5851F42D4C957F2D + 0x14057B7EF767814F
+    return int((b * (w | 1)).sum().item())
+
+
+def distinct_runs(fn, runs):
+    """(distinct results, first output): every run's output compared, element by element on the
+    device, with the first run's, and fingerprinted."""
+    import torch
+    first = fn().clone()
+    fps = {fingerprint(first)}
+    same = 0
+    for _ in range(runs - 1):
+        o = fn()
+        fps.add(fingerprint(o))
+        same += int(torch.equal(ibits(o), ibits(first)))
+    # every run equal to the first means one result; else count fingerprints
+    return (1 if same == runs - 1 else max(2, len(fps))), first
+
+
+def stats(ts):
+    import numpy as np
+    a = np.asarray(ts, dtype=np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)),
+            "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90))}
+
+
+# ---------------------------------------------------------------- accuracy (host)
+
+def sum_error(got, x):
+    import numpy as np
+    ref = float(np.sum(x, dtype=np.float64))
+    return abs(float(got) - ref) / abs(ref) if ref else abs(float(got))
+
+
+def scan_error(got, x):
+    """max_i |y_i - r_i| / sum_{k<=i} |x_k|: the normwise error against a double-precision
+    prefix sum (its own error is at most n * 2^-53 relative to the same norm)."""
+    import numpy as np
+    r = np.cumsum(x, dtype=np.float64)
+    d = np.abs(got.astype(np.float64) - r)
+    del r
+    a = np.cumsum(np.abs(x), dtype=np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        q = np.where(a > 0, d / np.where(a > 0, a, 1.0), d)
+    return float(q.max())
+
+
+def scatter_error(got, v, b, B, init):
+    """max over destinations of |out - ref| / (|init| + sum |v|), ref in double precision."""
+    import numpy as np
+    ok = (b >= 0) & (b < B)
+    ref = np.bincount(b[ok], weights=v[ok].astype(np.float64), minlength=B) + init
+    den = np.bincount(b[ok], weights=np.abs(v[ok]).astype(np.float64), minlength=B) + np.abs(init)
+    d = np.abs(got.astype(np.float64) - ref)
+    q = np.where(den > 0, d / np.where(den > 0, den, 1.0), d)
+    return float(q.max())
+
+
+def sha256_of(t):
+    return hashlib.sha256(t.detach().cpu().numpy().tobytes()).hexdigest()
+
+
+# ---------------------------------------------------------------- the other configurations
+
 def time_configs(det, workloads, dev, log, base_lib=None):
     """Times every configuration of the workload spec besides the headline step (one GPU,
-    inputs resident): median over repetitions of one call, bracketed by events on the current
-    stream.  Returns {case: {ms, GB_s, frac_hbm, Gelem_s}} with algorithmic bytes as in the
-    headline step; the large f64 case also reports the distinct results over launch grids of
-    1x, 2x and 4x the compute-unit count."""
-    import hashlib as _h
+    inputs resident): median (and p10/p90) over repetitions of one call, bracketed by events on
+    the current stream.  Returns {case: {...}} with algorithmic bytes as in the headline step.
 
+    Besides the spec's cases: the scan beside the same kernel with the adaptive look-back and
+    beside the ROCm library scan, with distinct results over 100 runs of each; the segmented
+    scan of 200,000 elements in blocks of 65,537 (drjit-core pull request, "Microbenchmark");
+    Warp's accumulation grid (writes 65,536 / 262,144 / 1,048,576 into 1 or 65,536 outputs,
+    a graph replay of zero + launch, "Performance"); the small calls 20 to a graph; and the
+    f64 2^29 sum and scan over launch grids of 1x, 2x and 4x the CU count at two occupancies."""
     import numpy as np
     import torch
 
     stream = torch.cuda.current_stream(dev)
     res = {}
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
 
-    def med(fn, reps):
-        for _ in range(2):
+    def times(fn, reps, warm=2):
+        for _ in range(warm):
             fn()
         torch.cuda.synchronize()
         ts = []
@@ -134,13 +245,17 @@ def time_configs(det, workloads, dev, log, base_lib=None):
             b.record(stream)
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b))
-        return float(np.median(ts))
+        return stats(ts)
 
-    def put(name, fn, nbytes, nelem, reps):
-        ms = med(fn, reps)
+    def put(name, fn, nbytes, nelem, reps, per_call=1):
+        st = times(fn, reps)
+        ms = st["median"] / per_call
         gbs = nbytes / (ms * 1e-3) / 1e9
-        res[name] = {"ms": round(ms, 4), "GB_s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_GBS, 4),
+        res[name] = {"ms": round(ms, 4), "p10_ms": round(st["p10"] / per_call, 4),
+                     "p90_ms": round(st["p90"] / per_call, 4), "GB_s": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_GBS, 4),
                      "Gelem_s": round(nelem / (ms * 1e-3) / 1e9, 3)}
+        return res[name]
 
     def dev_t(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
@@ -148,22 +263,42 @@ def time_configs(det, workloads, dev, log, base_lib=None):
     def ws_of(nbytes):
         return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
 
+    def graph_of(fn, k):
+        """A HIP graph holding k calls of fn, captured on a side stream."""
+        fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.graph(gr, stream=side):
+            for _ in range(k):
+                fn()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        return gr
+
     # sum, n = 2^20 uniform and n = 4096 ones
     x = dev_t(workloads.uniform01(1 << 20, seed=0))
     w = ws_of(det.det_sum_workspace_size(1 << 20, 0))
     o = torch.empty((), dtype=torch.float32, device=dev)
     put("sum f32 n=2^20 U[0,1)", lambda: det.det_sum(x, out=o, ws=w), 4 << 20, 1 << 20, 50)
     if base_lib is not None:
-        import ctypes as _ct0
-        sp0 = _ct0.c_void_p(stream.cuda_stream)
         tmp = torch.empty((), dtype=torch.float32, device=dev)
-        bms = med(lambda: base_lib.detbase_atomic_sum(_ct0.c_void_p(x.data_ptr()),
-                                                      _ct0.c_int64(1 << 20), 0,
-                                                      _ct0.c_void_p(tmp.data_ptr()), sp0), 50)
-        res["sum f32 n=2^20 U[0,1)"]["nondet_baseline_ms"] = round(bms, 4)
-        res["sum f32 n=2^20 U[0,1)"]["det_overhead"] = round(res["sum f32 n=2^20 U[0,1)"]["ms"] / bms - 1.0, 4)
+        bms = times(lambda: base_lib.detbase_atomic_sum(vp(x), ctypes.c_int64(1 << 20), 0,
+                                                        vp(tmp), sp), 50)["median"]
+        r = res["sum f32 n=2^20 U[0,1)"]
+        r["nondet_baseline_ms"] = round(bms, 4)
+        r["det_overhead"] = round(r["ms"] / bms - 1.0, 4)
     ones = torch.ones(4096, dtype=torch.float32, device=dev)
     put("sum f32 n=4096 ones", lambda: det.det_sum(ones, out=o, ws=w), 4 * 4096, 4096, 50)
+    # the small latency-bound calls, 20 to a captured graph: the per-call cost without launch
+    # gaps (one call per replay mostly measures the graph launch itself)
+    gr = graph_of(lambda: det.det_sum(x, out=o, ws=w), 20)
+    put("sum f32 n=2^20 U[0,1), per call in a graph of 20", gr.replay, 4 << 20, 1 << 20, 30,
+        per_call=20)
+    gr1 = graph_of(lambda: det.det_sum(x, out=o, ws=w), 1)
+    put("sum f32 n=2^20 U[0,1), graph of 1 call", gr1.replay, 4 << 20, 1 << 20, 30)
+    del gr, gr1
     # scatter, n = 2^24: uniform over 65,536 bins, and every value into bin 0
     n = 1 << 24
     v = dev_t(workloads.normal(n, seed=1))
@@ -183,59 +318,112 @@ def time_configs(det, workloads, dev, log, base_lib=None):
                 12.0 * n + 8.0 * B, n, 10)
             del pv, w2
     del v
-    # scan: f32 and f64, inclusive/exclusive x forward/reverse; the inclusive forward scan
-    # beside the ROCm library's (hipCUB DeviceScan::InclusiveSum) on the same input, for the
-    # deterministic-mode overhead at the sizes the drjit page measures
-    import ctypes as _ct
+    # Warp's accumulation grid: graph replay of (zero the outputs + the scatter), f32 values,
+    # all writes into one output or uniform over 65,536; det_scatter_add beside per-element
+    # float atomics
+    for writes in (65536, 262144, 1048576):
+        vv = dev_t(workloads.normal(writes, seed=31))
+        for B in (1, 65536):
+            bi = dev_t(np.zeros(writes, np.int32) if B == 1
+                       else workloads.bins_uniform(writes, B, seed=31))
+            out = torch.zeros(B, dtype=torch.float32, device=dev)
+            w = ws_of(det.det_scatter_add_workspace_size(writes, B, 1, 0))
+
+            def det_call():
+                out.zero_()
+                det.det_scatter_add(vv, bi, out, ws=w)
+
+            name = f"pattern A: {writes} writes into {B} output(s), graph replay of zero + launch"
+            r = put(name, graph_of(det_call, 1).replay, 8.0 * writes + 8.0 * B, writes, 50)
+            r20 = times(graph_of(det_call, 20).replay, 20)["median"] / 20
+            r["ms_per_call_in_graph_of_20"] = round(r20, 4)
+            if base_lib is not None:
+                def nd_call():
+                    out.zero_()
+                    base_lib.detbase_atomic_scatter(vp(vv), vp(bi), ctypes.c_int64(writes), 0,
+                                                    vp(out), ctypes.c_int64(B), sp)
+
+                nd = times(graph_of(nd_call, 1).replay, 50)["median"]
+                nd20 = times(graph_of(nd_call, 20).replay, 20)["median"] / 20
+                r["nondet_baseline_ms"] = round(nd, 4)
+                r["nondet_baseline_ms_per_call_in_graph_of_20"] = round(nd20, 4)
+                r["det_overhead"] = round(r["ms"] / nd - 1.0, 4)
+    log("configs: sum, scatter, pattern A timed")
+    # scan: f32 and f64, inclusive/exclusive x forward/reverse; beside the same kernel with the
+    # adaptive look-back (every mode) and the ROCm library's inclusive scan
     modes = ((False, False, "incl"), (True, False, "excl"), (False, True, "incl rev"),
              (True, True, "excl rev"))
-    sp = _ct.c_void_p(stream.cuda_stream)
-    for dt, tdt, code in ((np.float32, torch.float32, 0), (np.float64, torch.float64, 1)):
+    for dt, code in ((np.float32, 0), (np.float64, 1)):
         for n in (16384, 164738, 1048577, 1 << 28):
             xs = dev_t(workloads.scan_values(n, dt, seed=2))
             ys = torch.empty_like(xs)
             w = ws_of(det.det_scan_workspace_size(n, code, 3, 0))
             reps = 20 if n < (1 << 28) else 10
-            name0 = None
+            wa = None
+            if base_lib is not None:
+                wa = ws_of(base_lib.detbase_adaptive_scan_workspace_size(ctypes.c_int64(n), code,
+                                                                         ctypes.c_int64(0)))
             for ex, rv, tag in modes:
                 name = f"scan {np.dtype(dt).name} n={n if n < (1 << 28) else '2^28'} {tag}"
-                name0 = name0 or name
-                put(name, lambda: det.det_scan(xs, y=ys, exclusive=ex, reverse=rv, ws=w),
-                    2.0 * n * xs.element_size(), n, reps)
+                r = put(name, lambda: det.det_scan(xs, y=ys, exclusive=ex, reverse=rv, ws=w),
+                        2.0 * n * xs.element_size(), n, reps)
+                if wa is not None:
+                    flags = (1 if ex else 0) | (2 if rv else 0)
+
+                    def ad(flags=flags):
+                        base_lib.detbase_adaptive_scan(vp(xs), vp(ys), ctypes.c_int64(n), code,
+                                                       flags, None, ctypes.c_int64(0), vp(wa),
+                                                       ctypes.c_size_t(wa.numel()), sp)
+                        return ys
+
+                    ams = times(ad, reps)["median"]
+                    r["adaptive_lookback_ms"] = round(ams, 4)
+                    r["det_overhead_vs_adaptive"] = round(r["ms"] / ams - 1.0, 4)
+                    if tag == "incl":
+                        runs = 100
+                        r["distinct_results_100_runs"] = {
+                            "det": distinct_runs(lambda: det.det_scan(xs, y=ys, ws=w), runs)[0],
+                            "adaptive_lookback": distinct_runs(ad, runs)[0]}
             if base_lib is not None:
                 f64 = code == 1
                 wsz = (base_lib.detbase_lib_scan64_workspace_size if f64
-                       else base_lib.detbase_lib_scan_workspace_size)(_ct.c_int64(n))
+                       else base_lib.detbase_lib_scan_workspace_size)(ctypes.c_int64(n))
                 wb = ws_of(wsz)
                 fn = base_lib.detbase_lib_scan64 if f64 else base_lib.detbase_lib_scan
-                args = (_ct.c_void_p(xs.data_ptr()), _ct.c_void_p(ys.data_ptr()), _ct.c_int64(n),
-                        _ct.c_void_p(wb.data_ptr()), _ct.c_size_t(wsz), sp)
-                bms = med(lambda: fn(*args), reps)
-                res[name0]["nondet_baseline_ms"] = round(bms, 4)
-                res[name0]["det_overhead"] = round(res[name0]["ms"] / bms - 1.0, 4)
-            del xs, ys
-    # the small latency-bound calls replayed from a captured HIP graph (launch gaps removed)
-    xg = dev_t(workloads.uniform01(1 << 20, seed=0))
-    wg = ws_of(det.det_sum_workspace_size(1 << 20, 0))
-    og = torch.empty((), dtype=torch.float32, device=dev)
+                args = (vp(xs), vp(ys), ctypes.c_int64(n), vp(wb), ctypes.c_size_t(wsz), sp)
+                name0 = f"scan {np.dtype(dt).name} n={n if n < (1 << 28) else '2^28'} incl"
+                bms = times(lambda: fn(*args), reps)["median"]
+                res[name0]["rocm_library_scan_ms"] = round(bms, 4)
+                res[name0]["det_overhead_vs_library"] = round(res[name0]["ms"] / bms - 1.0, 4)
+            del xs, ys, w, wa
     xs = dev_t(workloads.scan_values(16384, np.float32, seed=2))
     ys = torch.empty_like(xs)
     wsg = ws_of(det.det_scan_workspace_size(16384, 0, 0, 0))
-    for name, fn, nb, ne in (("sum f32 n=2^20 U[0,1), graph replay",
-                              lambda: det.det_sum(xg, out=og, ws=wg), 4 << 20, 1 << 20),
-                             ("scan float32 n=16384 incl, graph replay",
-                              lambda: det.det_scan(xs, y=ys, ws=wsg), 8 * 16384, 16384)):
-        fn()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.graph(graph, stream=side):
-            fn()
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        put(name, graph.replay, nb, ne, 50)
-    log("configs: sum, scatter, scan timed")
+    gr = graph_of(lambda: det.det_scan(xs, y=ys, ws=wsg), 20)
+    put("scan float32 n=16384 incl, per call in a graph of 20", gr.replay, 8 * 16384, 16384, 30,
+        per_call=20)
+    del gr
+    log("configs: scans timed")
+    # the drjit microbenchmark's segmented case: 200,000 elements in blocks of 65,537
+    n = 200000
+    offs = dev_t(np.array([0, 65537, 131074, 196611, 200000], np.int64))
+    for dt, code in ((np.float32, 0), (np.float64, 1)):
+        xs = dev_t(workloads.scan_values(n, dt, seed=2))
+        ys = torch.empty_like(xs)
+        w = ws_of(det.det_scan_workspace_size(n, code, 3, 4))
+        wa = None if base_lib is None else ws_of(base_lib.detbase_adaptive_scan_workspace_size(
+            ctypes.c_int64(n), code, ctypes.c_int64(4)))
+        for ex, rv, tag in modes:
+            name = f"segmented scan {np.dtype(dt).name} n=200000 blocks of 65537 {tag}"
+            r = put(name, lambda: det.det_scan(xs, y=ys, exclusive=ex, reverse=rv, offsets=offs,
+                                               ws=w), 2.0 * n * xs.element_size(), n, 20)
+            if wa is not None:
+                flags = (1 if ex else 0) | (2 if rv else 0)
+                ams = times(lambda: base_lib.detbase_adaptive_scan(
+                    vp(xs), vp(ys), ctypes.c_int64(n), code, flags, vp(offs), ctypes.c_int64(4),
+                    vp(wa), ctypes.c_size_t(wa.numel()), sp), 20)["median"]
+                r["adaptive_lookback_ms"] = round(ams, 4)
+                r["det_overhead_vs_adaptive"] = round(r["ms"] / ams - 1.0, 4)
     # segmented scan f32 2^26 (geometric segments, mean 100) and the row accumulate
     n = 1 << 26
     xs = dev_t(workloads.scan_values(n, np.float32, seed=3))
@@ -261,7 +449,7 @@ def time_configs(det, workloads, dev, log, base_lib=None):
         lambda: det.det_scatter_add_running(st, rt, ot, prev=pr, ws=w),
         8.0 * src.size + 4.0 * rows.size + 8.0 * out0.size, src.size, 20)
     del pr
-    log("configs: segmented scan and rows timed")
+    log("configs: segmented scans and rows timed")
     # large mixed-magnitude f64, n = 2^29: sum, scan, scatter into 2^20 Zipf(1.1) bins
     n = 1 << 29
     xm = dev_t(workloads.mixed_f64(n, seed=4))
@@ -270,19 +458,30 @@ def time_configs(det, workloads, dev, log, base_lib=None):
     put("sum f64 n=2^29 mixed", lambda: det.det_sum(xm, out=o64, ws=w), 8.0 * n, n, 10)
     ym = torch.empty_like(xm)
     put("scan f64 n=2^29 mixed incl", lambda: det.det_scan(xm, y=ym, ws=w), 16.0 * n, n, 5)
+    # launch grids of 1x, 2x, 4x the CU count, each at the default occupancy and with 24 KiB
+    # more LDS per workgroup (one f64 scan workgroup per CU instead of two); the shapes that
+    # actually ran are read back from the library
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    hs = {"sum": set(), "scan": set()}
-    for g in (cus, 2 * cus, 4 * cus):
-        det.det_debug_set_launch(g, 0)
+    ref_scan = ref_sum = None
+    shapes, same_sum, same_scan = [], True, True
+    for grid, lds in ((cus, 0), (2 * cus, 0), (4 * cus, 0), (cus, 24576), (2 * cus, 24576),
+                      (4 * cus, 24576)):
+        det.det_debug_set_launch(grid, lds)
         det.det_sum(xm, out=o64, ws=w)
         det.det_scan(xm, y=ym, ws=w)
         torch.cuda.synchronize()
-        hs["sum"].add(_h.sha256(o64.cpu().numpy().tobytes()).hexdigest())
-        hs["scan"].add(_h.sha256(ym.cpu().numpy().tobytes()).hexdigest())
+        last = det.det_debug_last_launch()
+        shapes.append({"requested_grid": grid, "extra_lds": lds, **last})
+        if ref_scan is None:
+            ref_scan, ref_sum = ym.clone(), o64.clone()
+        else:
+            same_scan &= torch.equal(ibits(ym), ibits(ref_scan))
+            same_sum &= torch.equal(ibits(o64), ibits(ref_sum))
     det.det_debug_set_launch(0, 0)
-    res["sum f64 n=2^29 mixed"]["distinct_over_grids_1x_2x_4x_CUs"] = len(hs["sum"])
-    res["scan f64 n=2^29 mixed incl"]["distinct_over_grids_1x_2x_4x_CUs"] = len(hs["scan"])
-    del ym
+    res["sum f64 n=2^29 mixed"]["distinct_over_launch_shapes"] = 1 if same_sum else 2
+    res["scan f64 n=2^29 mixed incl"]["distinct_over_launch_shapes"] = 1 if same_scan else 2
+    res["scan f64 n=2^29 mixed incl"]["launch_shapes"] = shapes
+    del ym, ref_scan
     bi = dev_t(workloads.zipf_bins(n, 1 << 20, 1.1, seed=4))
     out = torch.zeros(1 << 20, dtype=torch.float64, device=dev)
     w = ws_of(det.det_scatter_add_workspace_size(n, 1 << 20, 1, 1))
@@ -299,11 +498,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
-                          "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only (nothing here uses a "
+                                   "second one); run it with --gpus 1", "n_gpus": args.gpus}))
         sys.exit(2)
-
-    import ctypes
 
     import numpy as np
     import torch
@@ -333,6 +530,7 @@ def main():
     ws = torch.empty(max(det.det_sum_workspace_size(n, 0), det.det_scan_workspace_size(n, 0, 0, 0),
                          det.det_scatter_add_workspace_size(n, B, 1, 0)),
                      dtype=torch.uint8, device=dev)
+    health = torch.zeros((), dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
     ops = []
@@ -367,6 +565,11 @@ def main():
     torch.cuda.synchronize()
     step_ms = start.elapsed_time(stop) / args.steps
     log(f"timed {args.steps} steps: {step_ms:.3f} ms/step")
+    if "scan" in only:
+        # the scans' bounded waits all ended normally (the workspace's health word)
+        det.det_scan(g["x_scan"], y=y_scan, ws=ws, health=health)
+        if int(health.item()) != 0:
+            raise SystemExit("det_scan health word set: a look-back wait gave up")
 
     ev = {name: [] for name, _, _ in ops}
     for _ in range(args.steps):
@@ -378,7 +581,7 @@ def main():
             b.record(stream)
             ev[name].append((a, b))
     torch.cuda.synchronize()
-    op_ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name in ev}
+    op_st = {name: stats([a.elapsed_time(b) for a, b in ev[name]]) for name in ev}
 
     det.det_debug_kernel_timing(True)
     torch.cuda.synchronize()
@@ -388,7 +591,7 @@ def main():
     torch.cuda.synchronize()
     kernels = det.det_debug_kernel_report()
     det.det_debug_kernel_timing(False)
-    log(f"per-operation and per-kernel passes done")
+    log("per-operation and per-kernel passes done")
 
     step_bytes = sum(bts for _, _, bts in ops)
     value = step_bytes / (step_ms * 1e-3) / 1e9
@@ -402,27 +605,42 @@ def main():
         log(f"calibration copy: {n} f32 elements, 3 times")
 
     # ---------------------------------------------------------------- non-deterministic baselines
-    base_ms = {}
-    distinct = {}
+    base_ms, distinct, outs_base = {}, {}, {}
+    attainable = None
+    bl = None
     if not args.no_baselines:
         bl = ctypes.CDLL(os.path.join(ROOT, "scan_fixed_order_amd", "libdet_baselines.so"))
+        for nm in ("detbase_lib_scan_workspace_size", "detbase_lib_scan64_workspace_size",
+                   "detbase_adaptive_scan_workspace_size"):
+            getattr(bl, nm).restype = ctypes.c_size_t
         sp = ctypes.c_void_p(stream.cuda_stream)
         vp = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
         tmp = torch.empty((), dtype=torch.float32, device=dev)
         out_b = torch.zeros(B, dtype=torch.float32, device=dev)
-        bl.detbase_lib_scan_workspace_size.restype = ctypes.c_size_t
+        y_b = torch.empty(n, dtype=torch.float32, device=dev) if "scan" in only else None
         wsb_bytes = bl.detbase_lib_scan_workspace_size(ctypes.c_int64(n))
         wsb = torch.empty(max(wsb_bytes, 256), dtype=torch.uint8, device=dev)
+        wsa_bytes = bl.detbase_adaptive_scan_workspace_size(ctypes.c_int64(n), 0,
+                                                            ctypes.c_int64(0))
+        wsa = torch.empty(max(wsa_bytes, 256), dtype=torch.uint8, device=dev)
         calls = {
-            "sum": lambda: bl.detbase_atomic_sum(vp(g["x_sum"]), ctypes.c_int64(n), 0, vp(tmp), sp),
-            "scan": lambda: bl.detbase_lib_scan(vp(g["x_scan"]), vp(y_scan), ctypes.c_int64(n),
-                                                vp(wsb), ctypes.c_size_t(wsb_bytes), sp),
-            "scatter": lambda: bl.detbase_atomic_scatter(vp(g["v_sc"]), vp(g["b_sc"]),
-                                                         ctypes.c_int64(n), 0, vp(out_b),
-                                                         ctypes.c_int64(B), sp),
+            "sum": lambda: (bl.detbase_atomic_sum(vp(g["x_sum"]), ctypes.c_int64(n), 0, vp(tmp),
+                                                  sp), tmp)[1],
+            "scan": lambda: (bl.detbase_adaptive_scan(vp(g["x_scan"]), vp(y_b), ctypes.c_int64(n),
+                                                      0, 0, None, ctypes.c_int64(0), vp(wsa),
+                                                      ctypes.c_size_t(wsa_bytes), sp), y_b)[1],
+            "scatter": lambda: (out_b.zero_(),
+                                bl.detbase_atomic_scatter(vp(g["v_sc"]), vp(g["b_sc"]),
+                                                          ctypes.c_int64(n), 0, vp(out_b),
+                                                          ctypes.c_int64(B), sp), out_b)[2],
         }
-        for name, _, _ in ops:
-            fn = calls[name]
+
+        def lib_scan():
+            bl.detbase_lib_scan(vp(g["x_scan"]), vp(y_b), ctypes.c_int64(n), vp(wsb),
+                                ctypes.c_size_t(wsb_bytes), sp)
+            return y_b
+
+        def timed_loop(fn):
             for _ in range(2):
                 fn()
             torch.cuda.synchronize()
@@ -433,45 +651,103 @@ def main():
                 fn()
             b.record(stream)
             torch.cuda.synchronize()
-            base_ms[name] = a.elapsed_time(b) / args.steps
+            return a.elapsed_time(b) / args.steps
+
+        for name, _, _ in ops:
+            base_ms[name] = timed_loop(calls[name])
+        if "scan" in only:
+            base_ms["scan_library"] = timed_loop(lib_scan)
         log("baselines timed")
 
-        # distinct results over repeated runs: the library and the baselines on the same input
-        # (the scan's output compared on its last 2^20 elements, which depend on every input)
-        import hashlib as _h
+        # what this GPU's HBM gives a plain kernel, in the same run: a streaming read of 2^log2n
+        # f32 (16-byte non-temporal loads), and a copy of as many
+        xr = g.get("x_sum", g.get("x_scan", g.get("v_sc")))
+        sink = torch.zeros(4096, dtype=torch.float32, device=dev)
+        yr = torch.empty_like(xr)
+        nb = xr.numel() * 4
+        rd = timed_loop(lambda: bl.detbase_stream_read(vp(xr), ctypes.c_int64(nb), vp(sink), sp))
+        cp = timed_loop(lambda: bl.detbase_copy(vp(xr), vp(yr), ctypes.c_int64(nb), sp))
+        attainable = {"stream_read_GB_s": round(nb / (rd * 1e-3) / 1e9, 1),
+                      "copy_GB_s": round(2 * nb / (cp * 1e-3) / 1e9, 1),
+                      "bytes_read": nb, "note": "16-byte non-temporal accesses, 4096 workgroups"}
+        del yr
+        log(f"attainable: read {attainable['stream_read_GB_s']} GB/s, "
+            f"copy {attainable['copy_GB_s']} GB/s")
 
-        def digest(t):
-            return _h.sha256(t.cpu().numpy().tobytes()).hexdigest()
-
-        tail = min(n, 1 << 20)
+        # distinct results over repeated runs: the library and the baselines on the same input,
+        # every output element of every run compared with the first run's on the device
         probes = {
-            "sum": (lambda: (det.det_sum(g["x_sum"], out=s_out, ws=ws), s_out)[1],
-                    lambda: (calls["sum"](), tmp)[1]),
-            "scan": (lambda: det.det_scan(g["x_scan"], y=y_scan, ws=ws)[-tail:],
-                     lambda: (calls["scan"](), y_scan)[1][-tail:]),
-            "scatter": (lambda: (out_sc.zero_(), det.det_scatter_add(g["v_sc"], g["b_sc"], out_sc,
-                                                                      ws=ws))[1],
-                        lambda: (out_b.zero_(), calls["scatter"](), out_b)[2]),
+            "sum": lambda: det.det_sum(g["x_sum"], out=s_out, ws=ws),
+            "scan": lambda: det.det_scan(g["x_scan"], y=y_scan, ws=ws),
+            "scatter": lambda: (out_sc.zero_(), det.det_scatter_add(g["v_sc"], g["b_sc"], out_sc,
+                                                                     ws=ws))[1],
         }
         for name, _, _ in ops:
-            dfn, bfn = probes[name]
-            hashes_det = {digest(dfn()) for _ in range(args.repeat_runs)}
-            hashes_base = {digest(bfn()) for _ in range(args.repeat_runs)}
-            distinct[name] = {"det": len(hashes_det), "nondet_baseline": len(hashes_base)}
+            dn, _ = distinct_runs(probes[name], args.repeat_runs)
+            bn, first_b = distinct_runs(calls[name], args.repeat_runs)
+            outs_base[name] = first_b
+            distinct[name] = {"det": dn, "nondet_baseline": bn, "runs": args.repeat_runs,
+                              "compared": "every output element of every run, on the device"}
+            if name == "scan":
+                distinct[name]["rocm_library_scan"] = distinct_runs(lib_scan,
+                                                                    args.repeat_runs)[0]
         log(f"repeatability over {args.repeat_runs} runs: {distinct}")
+
+    # ---------------------------------------------------------------- accuracy and digests
+    accuracy = {}
+    if not args.no_accuracy:
+        for name, fn, _ in ops:
+            if name == "scatter":
+                out_sc.zero_()
+            o = fn()
+            torch.cuda.synchronize()
+            r = {"sha256": sha256_of(o)}
+            if name == "sum":
+                r["det_rel_err"] = sum_error(o.item(), host["x_sum"])
+                if "sum" in outs_base:
+                    r["nondet_baseline_rel_err"] = sum_error(outs_base["sum"].item(),
+                                                             host["x_sum"])
+                r["measure"] = "|s - ref| / |ref|, ref the float64 sum"
+            elif name == "scan":
+                r["det_rel_err"] = scan_error(o.cpu().numpy(), host["x_scan"])
+                if "scan" in outs_base:
+                    r["nondet_baseline_rel_err"] = scan_error(outs_base["scan"].cpu().numpy(),
+                                                              host["x_scan"])
+                r["measure"] = "max_i |y_i - r_i| / sum_{k<=i} |x_k|, r the float64 prefix sum"
+            else:
+                r["det_rel_err"] = scatter_error(o.cpu().numpy(), host["v_sc"], host["b_sc"], B,
+                                                 np.zeros(B))
+                if "scatter" in outs_base:
+                    r["nondet_baseline_rel_err"] = scatter_error(
+                        outs_base["scatter"].cpu().numpy(), host["v_sc"], host["b_sc"], B,
+                        np.zeros(B))
+                r["measure"] = "max_b |out_b - r_b| / sum_{i in b} |v_i|, r in float64"
+            accuracy[name] = r
+        log("accuracy and digests done")
 
     # ---------------------------------------------------------------- per-op report
     op_rep = {}
     for name, _, bts in ops:
-        ms = op_ms[name]
+        st = op_st[name]
+        ms = st["mean"]
         gbs = bts / (ms * 1e-3) / 1e9
-        r = {"ms": round(ms, 4), "GB_s": round(gbs, 1), "Gelem_s": round(n / (ms * 1e-3) / 1e9, 2),
+        r = {"ms": round(ms, 4), "median_ms": round(st["median"], 4),
+             "p10_ms": round(st["p10"], 4), "p90_ms": round(st["p90"], 4),
+             "GB_s": round(gbs, 1), "Gelem_s": round(n / (ms * 1e-3) / 1e9, 2),
              "frac_hbm": round(gbs / PEAK_GBS, 4), "algorithmic_bytes": int(bts)}
         if name in base_ms:
             r["nondet_baseline_ms"] = round(base_ms[name], 4)
             r["det_overhead"] = round(ms / base_ms[name] - 1.0, 4)
+            r["nondet_baseline"] = {"sum": "atomic tail (one float atomic per workgroup)",
+                                    "scan": "the same scan kernel with the adaptive look-back",
+                                    "scatter": "one float atomic per element"}[name]
+        if name == "scan" and "scan_library" in base_ms:
+            r["rocm_library_scan_ms"] = round(base_ms["scan_library"], 4)
+            r["det_overhead_vs_library"] = round(ms / base_ms["scan_library"] - 1.0, 4)
         if name in distinct:
-            r["distinct_results"] = dict(distinct[name], runs=args.repeat_runs)
+            r["distinct_results"] = distinct[name]
+        if name in accuracy:
+            r["accuracy"] = accuracy[name]
         op_rep[name] = r
 
     # ---------------------------------------------------------------- dominant kernel
@@ -495,12 +771,7 @@ def main():
     # ---------------------------------------------------------------- the other configurations
     configs = None
     if not args.no_configs:
-        blib = None
-        if not args.no_baselines:
-            blib = ctypes.CDLL(os.path.join(ROOT, "scan_fixed_order_amd", "libdet_baselines.so"))
-            for nm in ("detbase_lib_scan_workspace_size", "detbase_lib_scan64_workspace_size"):
-                getattr(blib, nm).restype = ctypes.c_size_t
-        configs = time_configs(det, workloads, dev, log, blib)
+        configs = time_configs(det, workloads, dev, log, bl)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -522,11 +793,13 @@ def main():
             dt += time.perf_counter() - t
             cpu_bytes += step_bytes
             reps += 1
+        hi = host_info()
         cpu = {"value": round(cpu_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
                "sample": f"the whole step's workload ({', '.join(sorted(only))} at n=2^{args.log2n}, "
                          f"{B} bins) run {reps} time(s) through the single-threaded C oracle: "
-                         f"{dt:.1f} s on {os.cpu_count()} visible host cores"}
+                         f"{dt:.1f} s on one of {hi['usable_cores']} usable host cores",
+               "host": hi}
         log(f"cpu oracle: {reps} pass(es), {dt:.1f}s")
 
     line = {
@@ -548,6 +821,7 @@ def main():
                    "n": n, "bins": B, "ops": sorted(only)},
         "frac_hbm": round(value / PEAK_GBS, 4),
         "roofline": roofline,
+        "attainable": attainable,
         "kernels": kern_rep,
         "ops": op_rep,
         "cpu_baseline": cpu,
