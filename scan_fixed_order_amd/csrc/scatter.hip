@@ -358,13 +358,18 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
 }
 
 // P: payload word (uint32_t: f32 value bits or source row; uint64_t: f64 value bits)
+// The staged chunk: for 4-byte payloads key and payload share one 64-bit word (kp), so each
+// item's scattered LDS write is one instruction; 8-byte payloads keep two arrays.
 template <typename P>
 struct RadixSmem {
-    uint32_t keys[256 * kItems<P>];
-    P pay[256 * kItems<P>];
-    uint32_t cnt[kRadixNW<P>][kBuckets0];   // per-wave digit counters, then wave offsets
-    uint32_t dstart[kBuckets0];
-    int64_t gbase[kBuckets0];
+    static constexpr bool kPacked = sizeof(P) == 4;
+    uint64_t kp[kPacked ? 256 * kItems<P> : 1];
+    uint32_t keys[kPacked ? 1 : 256 * kItems<P>];
+    P pay[kPacked ? 1 : 256 * kItems<P>];
+    // per-wave digit counters; then each wave's first position per digit in the staged chunk
+    uint32_t cnt[kRadixNW<P>][kBuckets0];
+    // global index of staged position 0 for each digit, modulo 2^32 (every index is below 2^31)
+    uint32_t gbase[kBuckets0];
     uint32_t s4[kRadixNW<P>];
 };
 
@@ -417,6 +422,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
     constexpr int NB = FIRST ? kBuckets0 : 256;
     uint32_t rk[IPT];
     const int64_t p0 = base + (int64_t)wave * 64 * IPT + lane;
+    uint32_t* const wcnt = sm.cnt[wave];
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
         const bool valid = FULL || p0 + k * 64 < m;
@@ -425,18 +431,25 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         uint32_t phi = FULL ? ~0u : (uint32_t)(__ballot(valid) >> 32);
 #pragma unroll
         for (int b = 0; b < BITS; ++b) {
-            const int rep = __builtin_amdgcn_sbfe(d, b, 1);   // 0 or all ones: the lane's bit
-            const uint64_t mb = __builtin_amdgcn_ballot_w64(rep != 0);
-            plo &= ~((uint32_t)mb ^ (uint32_t)rep);      // keep lanes whose bit b agrees
-            phi &= ~((uint32_t)(mb >> 32) ^ (uint32_t)rep);
+            // the lane's bit b as 0 or all ones, kept opaque so the ballot compares it directly
+            uint32_t rep = (uint32_t)__builtin_amdgcn_sbfe(d, b, 1);
+            asm volatile("" : "+v"(rep));
+            const uint64_t mb = __builtin_amdgcn_ballot_w64(rep != 0u);
+            // keep the lanes whose bit b agrees with this lane's: mask & ~(rep ^ ballot), one
+            // three-input bit operation per 32-lane half (truth table 0x90)
+            plo = __builtin_amdgcn_bitop3_b32(plo, rep, (uint32_t)mb, 0x90);
+            phi = __builtin_amdgcn_bitop3_b32(phi, rep, (uint32_t)(mb >> 32), 0x90);
         }
         const uint32_t below = __builtin_amdgcn_mbcnt_hi(phi, __builtin_amdgcn_mbcnt_lo(plo, 0u));
-        const uint32_t cnt = (uint32_t)__popc(plo) + (uint32_t)__popc(phi);
-        uint32_t old = 0u;
-        if (valid && below == 0u) old = atomicAdd(&sm.cnt[wave][d], cnt);
-        const int leader = plo ? __builtin_ctz(plo) : 32 + __builtin_ctz(phi | 0x80000000u);
-        const uint32_t seen = (uint32_t)__builtin_amdgcn_ds_bpermute(leader << 2, (int)old);
-        rk[k] = seen + below;
+        // every lane reads its digit's counter; then the lowest lane of each group of peers
+        // adds the group's size.  A wave's LDS instructions run in order and each write waits
+        // for its row's read, so the next row reads the advanced counters.
+        const uint32_t old = valid ? wcnt[d] : 0u;
+        if (valid && below == 0u) wcnt[d] = old + (uint32_t)__popc(plo) + (uint32_t)__popc(phi);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        rk[k] = old + below;
     }
     __syncthreads();
     // per digit: wave offsets (exclusive over waves) and the chunk's count
@@ -462,44 +475,58 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
     }
     uint32_t total;
     const uint32_t ds = block_excl_scan_u32<NW>(tot, sm.s4, &total);
+    // the digit's start in the staged chunk folded into every wave's offset, so staging reads
+    // one counter per item
     if (tid < 256) {
-        sm.dstart[tid] = ds;
-        sm.gbase[tid] = (int64_t)off0 - (int64_t)ds;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sm.cnt[w][tid] += ds;
+        sm.gbase[tid] = off0 - ds;
     }
     if (NB > 256 && tid == 0) {
-        sm.dstart[256] = total;
-        sm.gbase[256] = (int64_t)off1 - (int64_t)total;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sm.cnt[w][256] += total;
+        sm.gbase[256] = off1 - total;
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
         if (FULL || p0 + k * 64 < m) {
             const int d = digit_of<FIRST>(key[k], B, shift);
-            const uint32_t lp = sm.dstart[d] + sm.cnt[wave][d] + rk[k];
-            sm.keys[lp] = key[k];
-            sm.pay[lp] = pay[k];
+            const uint32_t lp = sm.cnt[wave][d] + rk[k];
+            if constexpr (RadixSmem<P>::kPacked) {
+                sm.kp[lp] = (uint64_t)key[k] | ((uint64_t)pay[k] << 32);
+            } else {
+                sm.keys[lp] = key[k];
+                sm.pay[lp] = pay[k];
+            }
         }
     }
     __syncthreads();
     for (int i = tid; i < NW * kBuckets0; i += NT) (&sm.cnt[0][0])[i] = 0u;
+    // staged position i to its global index: gbase[digit] + i (below 2^31, so the 32-bit sum
+    // is exact)
+    auto emit = [&](int i) {
+        uint32_t kk;
+        P pp;
+        if constexpr (RadixSmem<P>::kPacked) {
+            const uint64_t v = sm.kp[i];
+            kk = (uint32_t)v;
+            pp = (P)(v >> 32);
+        } else {
+            kk = sm.keys[i];
+            pp = sm.pay[i];
+        }
+        const int64_t g = (int64_t)(sm.gbase[digit_of<FIRST>(kk, B, shift)] + (uint32_t)i);
+        keys_out[g] = (KO)kk;
+        pay_out[g] = pp;
+    };
     if constexpr (FULL) {
         // a fixed number of stores, so a later wait on loads issued before them stays partial
 #pragma unroll
-        for (int k = 0; k < IPT; ++k) {
-            const int i = k * NT + tid;
-            const uint32_t kk = sm.keys[i];
-            const int64_t g = sm.gbase[digit_of<FIRST>(kk, B, shift)] + i;
-            keys_out[g] = (KO)kk;
-            pay_out[g] = sm.pay[i];
-        }
+        for (int k = 0; k < IPT; ++k) emit(k * NT + tid);
     } else {
         const int cntc = (int)((m - base) < H ? (m - base) : H);
-        for (int i = tid; i < cntc; i += NT) {
-            const uint32_t kk = sm.keys[i];
-            const int64_t g = sm.gbase[digit_of<FIRST>(kk, B, shift)] + i;
-            keys_out[g] = (KO)kk;
-            pay_out[g] = sm.pay[i];
-        }
+        for (int i = tid; i < cntc; i += NT) emit(i);
     }
     __syncthreads();
 }
