@@ -69,19 +69,20 @@ def log(msg):
 def kernel_bytes_per_step(n, B):
     """Algorithmic HBM bytes each library kernel must move in one step (f32, row_len 1).
 
-    The scatter's two radix passes move key and value in and out.  When every destination fits
-    16 bits, every pass writes 16-bit keys and the later passes read them: the first pass reads
-    4 + 4 and writes 2 + 4 bytes per element, the second reads and writes 2 + 4 (else 4-byte
-    keys throughout).  The segment reduction reads the sorted keys and values, and reads and
-    writes each destination once."""
+    With 256 < B <= 65536 the scatter sorts in two radix passes on byte keys: the first reads
+    the 4-byte destination and the value and writes the destination's high byte and the value
+    (8 + 5 bytes per element); the second reads those and writes the value (5 + 4); the two
+    histogram passes read the destinations (4) and the bytes (1); the destination offsets come
+    from the histograms, so the reduction reads only the sorted values (4) and reads and writes
+    each destination once."""
     parts = -(-n // (1 << 14))
-    kb = 2.0 if B <= 65536 else 4.0
+    assert 256 < B <= 65536, "the byte model covers destinations in (256, 65536]"
     return {
         "k_sum_chunks<f32>": 4.0 * n + 4.0 * parts,       # values, then the partials' level
         "k_scan<f32>": 8.0 * n,                           # read x, write y
-        "k_radix_hist": 4.0 * n + kb * n,                 # keys, one pass per 8-bit digit
-        "k_radix_scatter": (12.0 + kb) * n + (8.0 + 2 * kb) * n,   # first pass, second pass
-        "k_segred_scalar": (kb + 4.0) * n + 8.0 * B,      # sorted keys + values, out r/w
+        "k_radix_hist": 4.0 * n + 1.0 * n,                # destinations, then key bytes
+        "k_radix_scatter": 13.0 * n + 9.0 * n,            # first pass, second pass
+        "k_segred_scalar": 4.0 * n + 8.0 * B,             # sorted values, out r/w
     }
 
 

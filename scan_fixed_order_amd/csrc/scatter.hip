@@ -35,6 +35,21 @@ constexpr int kSegD = 8192;     // scalar: ranks per block
 constexpr int kRowD = 64;       // rows: member rows per block
 constexpr int kBuckets0 = 257;  // first pass: 256 digits + the out-of-range bucket
 
+// Key output of a radix pass: uint32_t / uint16_t keys as they are; uint8_t, only the key's
+// second byte (the next pass's digit: the two-pass byte path); NoKey, none (the last pass of
+// that path, whose destination offsets come from the histograms).
+struct NoKey {};
+template <typename KO>
+__device__ __forceinline__ void put_key(KO* keys_out, int64_t g, uint32_t kk) {
+    if constexpr (__is_same(KO, NoKey)) {
+        (void)keys_out, (void)g, (void)kk;
+    } else if constexpr (sizeof(KO) == 1) {
+        keys_out[g] = (KO)(kk >> 8);
+    } else {
+        keys_out[g] = (KO)kk;
+    }
+}
+
 // keys per thread of a radix chunk: 8192 keys for 4-byte payloads, 4096 for 8-byte ones.
 // Long chunks give long runs per bucket (32 keys on average for 256 buckets), so the
 // scattered writes leave mostly whole lines.
@@ -293,21 +308,24 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
     // whose keys all share the digit of the wave's first key is added with one atomic
     // (skewed and contended inputs), any other batch key by key (testing each key of a row
     // for one shared digit cost more than it saved: 0.164 -> 0.151 ms per pass at 2^28)
-    constexpr int NK = sizeof(KI) == 2 ? 32 : 16;
+    constexpr int NK = sizeof(KI) < 4 ? 32 : 16;
+    constexpr int KPW = 4 / (int)sizeof(KI);      // keys per 32-bit word
     constexpr int PER = 256 * NK;                 // keys per batch of the workgroup
     for (int i0 = 0; i0 < H; i0 += PER) {
         uint32_t kk[NK];
-        // thread t takes keys i0 + k * 256 + t (4-byte keys) or the pair at i0 + 2 (k * 256 + t)
-        // (16-bit keys, two to a 32-bit word: H is even and the keys 256-byte aligned)
-        if constexpr (sizeof(KI) == 2) {
-            const uint32_t* kw = reinterpret_cast<const uint32_t*>(keys) + base / 2;
+        // thread t takes keys i0 + k * 256 + t (4-byte keys) or the KPW keys of word
+        // i0 / KPW + k * 256 + t (16-bit and byte keys, packed in 32-bit words: H is a multiple
+        // of 4 and the keys 256-byte aligned)
+        if constexpr (sizeof(KI) < 4) {
+            const uint32_t* kw = reinterpret_cast<const uint32_t*>(keys) + base / KPW;
 #pragma unroll
-            for (int k = 0; k < NK / 2; ++k) {
-                const int w = i0 / 2 + k * 256 + (int)threadIdx.x;
-                const uint32_t x = (2 * w < H && base + 2 * w < m)
+            for (int k = 0; k < NK / KPW; ++k) {
+                const int w = i0 / KPW + k * 256 + (int)threadIdx.x;
+                const uint32_t x = (KPW * w < H && base + KPW * w < m)
                                        ? __builtin_nontemporal_load(kw + w) : 0u;
-                kk[2 * k] = x & 0xffffu;
-                kk[2 * k + 1] = x >> 16;
+#pragma unroll
+                for (int j = 0; j < KPW; ++j)
+                    kk[KPW * k + j] = (x >> (32 / KPW * j)) & (0xffffffffu >> (32 - 32 / KPW));
             }
         } else {
 #pragma unroll
@@ -319,8 +337,8 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
             }
         }
         auto pos = [&](int k) -> int {   // position of kk[k] in the chunk
-            return sizeof(KI) == 2 ? i0 + 2 * ((k >> 1) * 256 + (int)threadIdx.x) + (k & 1)
-                                   : i0 + k * 256 + (int)threadIdx.x;
+            return sizeof(KI) < 4 ? i0 + KPW * ((k / KPW) * 256 + (int)threadIdx.x) + k % KPW
+                                  : i0 + k * 256 + (int)threadIdx.x;
         };
         const bool full = i0 + PER <= H && base + i0 + PER <= m;   // the same for all threads
         if (full) {
@@ -517,7 +535,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
             pp = sm.pay[i];
         }
         const int64_t g = (int64_t)(sm.gbase[digit_of<FIRST>(kk, B, shift)] + (uint32_t)i);
-        keys_out[g] = (KO)kk;
+        put_key<KO>(keys_out, g, kk);
         pay_out[g] = pp;
     };
     if constexpr (FULL) {
@@ -561,7 +579,7 @@ __global__ __launch_bounds__(kRadixNT<P>) void k_radix_scatter(
         for (int k = 0; k < IPT; ++k) {
             const int64_t p = p0 + k * 64;
             if (p < m) {
-                keys_out[p] = (KO)key[k];
+                put_key<KO>(keys_out, p, key[k]);
                 pay_out[p] = pay[k];
             }
         }
@@ -621,6 +639,65 @@ __global__ __launch_bounds__(256) void k_bin_offsets(const KT* __restrict__ K,
         off[b] = (uint32_t)lo;
     }
     if (blockIdx.x == 0 && threadIdx.x == 0 && n_skipped) *n_skipped = n - m;
+}
+
+// The two-pass byte path (destinations below 2^16, scalar values): off[b] for b = 256 h + l
+// (high byte h, low byte l) is the number of valid keys below b, i.e. those with a high byte
+// below h, plus those with high byte h and a low byte below l.  The first pass sorted by the
+// low byte, so the keys with a low byte below l are its output's positions [0, row1[l]) (row1:
+// that pass's bucket starts); the second pass's offsets ex2[c][h] count the keys with a high
+// byte below h plus those with high byte h in the chunks (of H positions of the first pass's
+// output) before c.  With c the chunk holding position row1[l], off[b] = ex2[c][h] + the keys
+// of high byte h in [c H, row1[l]), counted here from the first pass's key bytes; when
+// row1[l] = m no key has a low byte of l or more, and off[b] = the start of bucket h + 1.
+// Integers only.  A workgroup per low byte, a thread per high byte.
+__global__ __launch_bounds__(256) void k_bin_offsets_bytes(
+    const uint32_t* __restrict__ row1, const uint32_t* __restrict__ ex2,
+    const uint8_t* __restrict__ hb, const uint32_t* __restrict__ nvalid, int64_t B, int64_t n,
+    int64_t H, uint32_t* __restrict__ off, int64_t* __restrict__ n_skipped) {
+    __shared__ uint32_t cnt[256];
+    const int l = blockIdx.x, h = threadIdx.x;
+    const int64_t m = *nvalid;
+    const int64_t pos = row1[l];
+    cnt[h] = 0u;
+    __syncthreads();
+    const int64_t c = pos / H;
+    if (pos < m)
+        for (int64_t q = c * H + h; q < pos; q += 256) atomicAdd(&cnt[hb[q]], 1u);
+    __syncthreads();
+    const int64_t b = (int64_t)h * 256 + l;
+    if (b < B) {
+        uint32_t o;
+        if (pos < m) o = ex2[c * 256 + h] + cnt[h];
+        else o = h < 255 ? ex2[h + 1] : (uint32_t)m;   // row 0 of ex2: the bucket starts
+        off[b] = o;
+    }
+    if (l == 0 && h == 0) {
+        off[B] = (uint32_t)m;
+        if (n_skipped) *n_skipped = n - m;
+    }
+}
+
+// rbin[r] = the destination holding sorted position p = r * kSegD, for r < nr = ceil(m / kSegD):
+// the last b in [0, B) with off[b] <= p (off[0] = 0 <= p and off[B] = m > p, so it exists, and
+// off[b + 1] > p).  A wave per range narrows [lo, hi) 64 ways per step (a ballot over 64 probes
+// of the non-decreasing offsets).
+__global__ __launch_bounds__(256) void k_range_bins(const uint32_t* __restrict__ off, int64_t B,
+                                                    int64_t nr, uint32_t* __restrict__ rbin) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= nr) return;
+    const int64_t p = r * kSegD;
+    int64_t lo = 0, hi = B;
+    while (hi - lo > 1) {
+        const int64_t step = cdiv(hi - lo, 64);
+        const int64_t k = lo + (int64_t)lane * step;
+        const uint64_t le = __ballot(k < hi && (int64_t)off[k] <= p);   // lane 0 always
+        const int last = 63 - __builtin_clzll(le);
+        lo += (int64_t)last * step;
+        if (lo + step < hi) hi = lo + step;
+    }
+    if (lane == 0) rbin[r] = (uint32_t)lo;
 }
 
 template <typename T>
@@ -862,6 +939,79 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const KT* __restrict__ K,
         // the destination's old value is read alongside the block's values
         const T o = single ? out[b] : T(0);
         // the shortest padded width that holds the block (all give the same value)
+        T S;
+        if (len <= 512) S = wave_pw_range<T, 2, NEG>(V + ps, len, lane, false, ident<T>());
+        else if (len <= 2048) S = wave_pw_range<T, 8, NEG>(V + ps, len, lane, false, ident<T>());
+        else S = wave_pw_range<T, 32, NEG>(V + ps, len, lane, false, ident<T>());
+        if (lane == 0) {
+            if (single) out[b] = o + S;
+            else if (ps == seg_s) pF[ps / kSegD] = S;
+            else pC[ps / kSegD] = S;
+        }
+    }
+}
+
+// k_segred_scalar without keys (the byte path): the destinations meeting this range are
+// rbin[range] (the one holding its first position) and those after it that start before the
+// range's end, found from the offsets; every block and every value as in k_segred_scalar.
+template <typename T, bool NEG>
+__global__ __launch_bounds__(256) void k_segred_off(const T* __restrict__ V,
+                                                    const uint32_t* __restrict__ off, int64_t B,
+                                                    const uint32_t* __restrict__ rbin,
+                                                    const uint32_t* __restrict__ nvalid,
+                                                    T* __restrict__ out, T* __restrict__ pF,
+                                                    T* __restrict__ pC) {
+    __shared__ uint32_t s_big[kSegD / 32 + 2][4];
+    __shared__ uint32_t s_nbig;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t m = *nvalid;
+    const int64_t lo = (int64_t)blockIdx.x * kSegD;
+    if (lo >= m) return;
+    const int64_t hi = (lo + kSegD < m) ? lo + kSegD : m;
+    if (tid == 0) s_nbig = 0u;
+    const int64_t b0 = rbin[blockIdx.x];
+    __syncthreads();
+    auto item = [&](int64_t ps, uint32_t b, int64_t seg_s, int64_t seg_e) {
+        const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
+        if (len <= 32) {
+            const T S = lane_pw_32<T, NEG>(V + ps, (int)len);
+            emit_scalar<T>(S, ps, b, seg_s, seg_e, out, pF, pC);
+        } else {
+            uint32_t* e = s_big[atomicAdd(&s_nbig, 1u)];
+            e[0] = (uint32_t)(ps - lo);
+            e[1] = b;
+            e[2] = (uint32_t)seg_s;
+            e[3] = (uint32_t)seg_e;
+        }
+    };
+    // destinations b0, b0 + 1, ... while they start before hi (at most kSegD + 1 of them)
+    for (int64_t bb = b0;; bb += 256) {
+        const int64_t b = bb + tid;
+        bool more = false;
+        if (b < B) {
+            const int64_t s0 = off[b], e0 = off[b + 1];
+            more = s0 < hi;
+            if (more && s0 < e0) {
+                if (s0 >= lo) {
+                    item(s0, (uint32_t)b, s0, e0);
+                } else {
+                    // the destination running into the range: its next multiple of D
+                    const int64_t pc = s0 + cdiv(lo - s0, kSegD) * kSegD;
+                    if (pc < hi && pc < e0) item(pc, (uint32_t)b, s0, e0);
+                }
+            }
+        }
+        if (!__syncthreads_or(more)) break;
+    }
+    __syncthreads();
+    const int nbig = (int)s_nbig;
+    for (int it = wave; it < nbig; it += 4) {
+        const int64_t ps = lo + s_big[it][0];
+        const uint32_t b = s_big[it][1];
+        const int64_t seg_s = s_big[it][2], seg_e = s_big[it][3];
+        const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
+        const bool single = seg_e - seg_s <= kSegD;
+        const T o = single ? out[b] : T(0);
         T S;
         if (len <= 512) S = wave_pw_range<T, 2, NEG>(V + ps, len, lane, false, ident<T>());
         else if (len <= 2048) S = wave_pw_range<T, 8, NEG>(V + ps, len, lane, false, ident<T>());
@@ -1174,7 +1324,8 @@ int key_passes(int64_t B) {
 
 struct SLayout {
     int64_t H, nchunks, nhist, nsums, nrange;
-    size_t keysA, keysB, payA, payB, hist, sums, ctrl, off, pF, pC, total;
+    bool bytes;   // the two-pass byte path (scalar destinations in (256, 65536])
+    size_t keysA, keysB, payA, payB, hist, hist2, sums, ctrl, off, rbin, pF, pC, total;
 };
 
 // idx_payload: the sort carries source indices (4 bytes) even for scalar destinations
@@ -1205,6 +1356,9 @@ SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt,
     L.hist = take((size_t)L.nhist * 4);
     L.sums = take((size_t)L.nsums * 4);
     L.off = take((size_t)(num_out + 1) * 4);
+    L.bytes = !rows && !idx_payload && key_passes(num_out) == 2;
+    L.hist2 = take(L.bytes ? (size_t)256 * L.nchunks * 4 : 4);
+    L.rbin = take(L.bytes ? (size_t)L.nrange * 4 : 4);
     L.pF = take((size_t)L.nrange * pe);
     L.pC = take((size_t)L.nrange * pe);
     L.total = o;
@@ -1279,6 +1433,56 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
     return DET_SUCCESS;
 }
 
+// The two-pass byte path (scalar destinations in (256, 65536]): the first pass sorts by the
+// low byte and writes only each key's high byte, the second sorts by that byte and writes no
+// keys; k_bin_offsets_bytes derives the destination offsets from the two passes' offsets.
+// *HB receives the first pass's key bytes, *SP the sorted payloads.
+template <typename P>
+det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
+                              int64_t num_out, const SLayout& L, char* ws, hipStream_t s,
+                              const uint8_t** HB, const P** SP) {
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
+    uint8_t* kb = reinterpret_cast<uint8_t*>(ws + L.keysA);
+    P* pay[2] = {reinterpret_cast<P*>(ws + L.payA), reinterpret_cast<P*>(ws + L.payB)};
+    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    uint32_t* hist2 = reinterpret_cast<uint32_t*>(ws + L.hist2);
+    uint32_t* sums = reinterpret_cast<uint32_t*>(ws + L.sums);
+    const uint32_t* kin = reinterpret_cast<const uint32_t*>(index);
+    const uint32_t B = (uint32_t)num_out;
+    const unsigned grid = (unsigned)L.nchunks;
+    const size_t lds = (size_t)launch_override().extra_lds;
+    {
+        KernelTimer kt("k_radix_hist", s);
+        k_radix_hist<true, uint32_t><<<grid, 256, lds, s>>>(kin, n, ctrl, B, 0, kBuckets0,
+                                                            L.nchunks, (int)L.H, hist);
+    }
+    det_status st = hist_offsets(hist, L.nchunks, kBuckets0, sums + 512, sums, ctrl, ctrl + 16, s);
+    if (st != DET_SUCCESS) return st;
+    {
+        KernelTimer kt("k_radix_scatter", s);
+        k_radix_scatter<P, true, false, uint8_t, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
+            kin, pay_in0, kb, pay[0], n, ctrl, B, 0, L.nchunks, hist, ctrl + 16);
+    }
+    if ((st = launch_status()) != DET_SUCCESS) return st;
+    {
+        KernelTimer kt("k_radix_hist", s);
+        k_radix_hist<false, uint8_t><<<grid, 256, lds, s>>>(kb, n, ctrl, B, 0, 256, L.nchunks,
+                                                           (int)L.H, hist2);
+    }
+    st = hist_offsets(hist2, L.nchunks, 256, sums + 512, sums, nullptr, ctrl + 17, s);
+    if (st != DET_SUCCESS) return st;
+    {
+        KernelTimer kt("k_radix_scatter", s);
+        k_radix_scatter<P, false, false, NoKey, uint8_t><<<grid, kRadixNT<P>, lds, s>>>(
+            kb, pay[0], static_cast<NoKey*>(nullptr), pay[1], n, ctrl, B, 0, L.nchunks, hist2,
+            ctrl + 17);
+    }
+    if ((st = launch_status()) != DET_SUCCESS) return st;
+    *HB = kb;
+    *SP = pay[1];
+    return DET_SUCCESS;
+}
+
 template <typename T, typename P, bool ROWS>
 det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_t row_len, T* out,
                         int64_t num_out, T* prev, int64_t* n_skipped, char* ws, bool neg,
@@ -1303,6 +1507,44 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
     }
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);   // [0] = number of valid keys
     uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
+    if constexpr (!ROWS) {
+        if (L.bytes) {
+            // two passes with byte keys, offsets from the histograms, no key reads after
+            const uint8_t* HB = nullptr;
+            const P* SP = nullptr;
+            det_status st = sort_by_dest_bytes<P>(index, reinterpret_cast<const P*>(values), n,
+                                                  num_out, L, ws, s, &HB, &SP);
+            if (st != DET_SUCCESS) return st;
+            uint32_t* rbin = reinterpret_cast<uint32_t*>(ws + L.rbin);
+            {
+                KernelTimer kt("k_bin_offsets", s);
+                k_bin_offsets_bytes<<<256, 256, 0, s>>>(
+                    reinterpret_cast<const uint32_t*>(ws + L.hist),
+                    reinterpret_cast<const uint32_t*>(ws + L.hist2), HB, ctrl, num_out, n, L.H,
+                    off, n_skipped);
+                k_range_bins<<<dim3((unsigned)cdiv(L.nrange, 4)), dim3(256), 0, s>>>(
+                    off, num_out, L.nrange, rbin);
+            }
+            T* pF = reinterpret_cast<T*>(ws + L.pF);
+            T* pC = reinterpret_cast<T*>(ws + L.pC);
+            const T* SV = reinterpret_cast<const T*>(SP);
+            {
+                KernelTimer kt("k_segred_scalar", s);
+                const dim3 g((unsigned)L.nrange), b(256);
+                if (!neg)
+                    k_segred_off<T, false><<<g, b, 0, s>>>(SV, off, num_out, rbin, ctrl, out, pF,
+                                                           pC);
+                else
+                    k_segred_off<T, true><<<g, b, 0, s>>>(SV, off, num_out, rbin, ctrl, out, pF,
+                                                          pC);
+            }
+            int64_t lg = cdiv(num_out, 64 * 4);
+            if (lg > 4096) lg = 4096;
+            k_segred_scalar_long<T><<<dim3((unsigned)lg), dim3(256), 0, s>>>(off, num_out, pF, pC,
+                                                                              out);
+            return launch_status();
+        }
+    }
     // scalar destinations that all fit 16 bits: every pass writes 16-bit keys, which the next
     // pass, the destination offsets and the reduction read (out-of-range keys land past the
     // valid ones and are never read)
