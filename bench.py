@@ -76,14 +76,13 @@ def kernel_bytes_per_step(n, B):
     from the histograms, so the reduction reads only the sorted values (4) and reads and writes
     each destination once."""
     parts = -(-n // (1 << 14))
-    assert 256 < B <= 65536, "the byte model covers destinations in (256, 65536]"
-    return {
-        "k_sum_chunks<f32>": 4.0 * n + 4.0 * parts,       # values, then the partials' level
-        "k_scan<f32>": 8.0 * n,                           # read x, write y
-        "k_radix_hist": 4.0 * n + 1.0 * n,                # destinations, then key bytes
-        "k_radix_scatter": 13.0 * n + 9.0 * n,            # first pass, second pass
-        "k_segred_scalar": 4.0 * n + 8.0 * B,             # sorted values, out r/w
-    }
+    rows = {"k_sum_chunks<f32>": 4.0 * n + 4.0 * parts,  # values, then the partials' level
+            "k_scan<f32>": 8.0 * n}                      # read x, write y
+    if 256 < B <= 65536:
+        rows.update({"k_radix_hist": 4.0 * n + 1.0 * n,          # destinations, then key bytes
+                     "k_radix_scatter": 13.0 * n + 9.0 * n,      # first pass, second pass
+                     "k_segred_scalar": 4.0 * n + 8.0 * B})      # sorted values, out r/w
+    return rows
 
 
 def source_hash(path):
