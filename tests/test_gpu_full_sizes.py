@@ -53,7 +53,7 @@ def test_sum_f32_2_28(dev):
 def test_scan_f32_2_28(dev, scan_2_28, excl, rev):
     x = scan_2_28
     t = torch.from_numpy(x).to(dev)
-    got = det.det_scan(t, exclusive=excl, reverse=rev).cpu().numpy()
+    got = det.det_scan(t, exclusive=excl, reverse=rev, check=True).cpu().numpy()
     want = oracle.scan(x, exclusive=excl, reverse=rev)
     assert bits_equal(got, want), first_mismatch(got, want)
 
@@ -67,7 +67,7 @@ def test_scan_unaligned_views_above_512_mib(dev, scan_2_28, excl, rev):
     t = torch.from_numpy(scan_2_28[: n + 4]).to(dev)
     yb = torch.empty(n + 4, dtype=torch.float32, device=dev)
     y = yb[2:2 + n]
-    det.det_scan(t[1:1 + n], y=y, exclusive=excl, reverse=rev)
+    det.det_scan(t[1:1 + n], y=y, exclusive=excl, reverse=rev, check=True)
     want = oracle.scan(xs, exclusive=excl, reverse=rev)
     got = y.cpu().numpy()
     assert bits_equal(got, want), first_mismatch(got, want)
@@ -90,7 +90,7 @@ def test_segmented_scan_f32_2_26(dev, excl, rev):
     x = workloads.scan_values(n, F32, seed=3)
     offs = workloads.segment_offsets(n, 100.0, seed=3)
     got = det.det_scan(torch.from_numpy(x).to(dev), exclusive=excl, reverse=rev,
-                       offsets=torch.from_numpy(offs).to(dev)).cpu().numpy()
+                       offsets=torch.from_numpy(offs).to(dev), check=True).cpu().numpy()
     want = oracle.scan(x, exclusive=excl, reverse=rev, offsets=offs)
     assert bits_equal(got, want), first_mismatch(got, want)
 
@@ -122,7 +122,7 @@ def test_hundred_runs_one_hash(dev):
         for excl in (False, True):
             for rev in (False, True):
                 assert len(sha_runs(lambda: det.det_scan(s, y=y, exclusive=excl,
-                                                         reverse=rev))) == 1, (n, excl, rev)
+                                                         reverse=rev, check=True))) == 1, (n, excl, rev)
     v = torch.from_numpy(workloads.normal(1 << 24, seed=1)).to(dev)
     for b in (workloads.bins_uniform(1 << 24, 65536, seed=1), np.zeros(1 << 24, np.int32)):
         bt = torch.from_numpy(b).to(dev)

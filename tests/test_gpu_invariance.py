@@ -272,5 +272,5 @@ def test_health_word_cleared_on_every_path(dev, n):
     x = torch.from_numpy(workloads.scan_values(n, F32, seed=4)).to(dev)
     ws = torch.full((det.det_scan_workspace_size(n, 0, 3, 0),), 255, dtype=torch.uint8,
                     device=dev)
-    det.det_scan(x, ws=ws)
+    det.det_scan(x, ws=ws, check=True)
     assert int(det.det_scan_error(ws).item()) == 0, n

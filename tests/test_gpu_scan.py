@@ -25,7 +25,7 @@ MODES = [(False, False), (True, False), (False, True), (True, True)]
 def gpu_scan(x, dev, exclusive=False, reverse=False, offsets=None):
     t = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
     o = None if offsets is None else torch.from_numpy(np.asarray(offsets, np.int64)).to(dev)
-    return det.det_scan(t, exclusive=exclusive, reverse=reverse, offsets=o).cpu().numpy()
+    return det.det_scan(t, exclusive=exclusive, reverse=reverse, offsets=o, check=True).cpu().numpy()
 
 
 def random_offsets(n, mean, seed, empty_every=0):
@@ -100,7 +100,7 @@ def test_repeat_164738_twenty_times(dev, dtype):
     t = torch.from_numpy(x).to(dev)
     for excl, rev in MODES:
         want = oracle.scan(x, exclusive=excl, reverse=rev)
-        outs = [det.det_scan(t, exclusive=excl, reverse=rev) for _ in range(20)]
+        outs = [det.det_scan(t, exclusive=excl, reverse=rev, check=True) for _ in range(20)]
         for o in outs:
             assert bits_equal(o.cpu().numpy(), want), (excl, rev)
 
@@ -111,12 +111,12 @@ def test_in_place_and_unaligned(dev, dtype):
     x = workloads.scan_values(n, dtype, seed=5)
     want = oracle.scan(x)
     t = torch.from_numpy(x).to(dev)
-    det.det_scan(t, y=t)                                     # inclusive in place
+    det.det_scan(t, y=t, check=True)                                     # inclusive in place
     assert bits_equal(t.cpu().numpy(), want)
     t = torch.from_numpy(x).to(dev)
     for k in (1, 3):
         for excl, rev in MODES:
-            got = det.det_scan(t[k:], exclusive=excl, reverse=rev).cpu().numpy()
+            got = det.det_scan(t[k:], exclusive=excl, reverse=rev, check=True).cpu().numpy()
             assert bits_equal(got, oracle.scan(x[k:], exclusive=excl, reverse=rev)), (k, excl, rev)
 
 
@@ -132,17 +132,17 @@ def test_grid_invariance(dev, dtype):
     try:
         for grid in (1, 2, 7, 64, 256, 1000):
             det.det_debug_set_launch(grid, 0)
-            assert bits_equal(det.det_scan(t).cpu().numpy(), want), grid
-            assert bits_equal(det.det_scan(t, offsets=o, reverse=True).cpu().numpy(), wseg), grid
+            assert bits_equal(det.det_scan(t, check=True).cpu().numpy(), want), grid
+            assert bits_equal(det.det_scan(t, offsets=o, reverse=True, check=True).cpu().numpy(), wseg), grid
     finally:
         det.det_debug_set_launch(0, 0)
 
 
 def test_empty_scan(dev):
     t = torch.empty(0, device=dev)
-    assert det.det_scan(t).numel() == 0
+    assert det.det_scan(t, check=True).numel() == 0
     assert det.det_scan(t, exclusive=True, offsets=torch.zeros(1, dtype=torch.int64,
-                                                               device=dev)).numel() == 0
+                                                               device=dev), check=True).numel() == 0
 
 
 @pytest.mark.parametrize("dtype", [F32, F64])
@@ -160,10 +160,10 @@ def test_small_anchor_variants(dev, dtype, A, A2):
         for grid in (0, 1, 3):
             det.det_debug_set_launch(grid, 0)
             for excl, rev in MODES:
-                got = det.det_scan(t, exclusive=excl, reverse=rev).cpu().numpy()
+                got = det.det_scan(t, exclusive=excl, reverse=rev, check=True).cpu().numpy()
                 want = oracle.scan(x, exclusive=excl, reverse=rev, A=A, A2=A2)
                 assert bits_equal(got, want), (grid, excl, rev, first_mismatch(got, want))
-                got = det.det_scan(t, exclusive=excl, reverse=rev, offsets=o).cpu().numpy()
+                got = det.det_scan(t, exclusive=excl, reverse=rev, offsets=o, check=True).cpu().numpy()
                 want = oracle.scan(x, exclusive=excl, reverse=rev, offsets=offs, A=A, A2=A2)
                 assert bits_equal(got, want), (grid, excl, rev, "seg", first_mismatch(got, want))
     finally:
@@ -188,7 +188,7 @@ def test_many_super_intervals_on_a_full_grid(dev, dtype, A, A2):
             flags = (1 if excl else 0) | (2 if rev else 0)
             ws = torch.empty(det.det_scan_workspace_size(n, code, flags, 0), dtype=torch.uint8,
                              device=dev)
-            got = det.det_scan(t, exclusive=excl, reverse=rev, ws=ws).cpu().numpy()
+            got = det.det_scan(t, exclusive=excl, reverse=rev, ws=ws, check=True).cpu().numpy()
             assert int(det.det_scan_error(ws).item()) == 0, (A, A2, excl, rev, "health word")
             want = oracle.scan(x, exclusive=excl, reverse=rev, A=A, A2=A2)
             assert bits_equal(got, want), (A, A2, excl, rev, first_mismatch(got, want))
@@ -209,10 +209,10 @@ def test_exclusive_into_unaligned_output(dev, dtype):
     for k in range(4):
         for rev in (False, True):
             y = buf[k:k + n]
-            det.det_scan(t, y=y, exclusive=True, reverse=rev)
+            det.det_scan(t, y=y, exclusive=True, reverse=rev, check=True)
             want = oracle.scan(x, exclusive=True, reverse=rev)
             assert bits_equal(y.cpu().numpy(), want), (k, rev, first_mismatch(y.cpu().numpy(), want))
-            det.det_scan(t, y=y, exclusive=True, reverse=rev, offsets=o)
+            det.det_scan(t, y=y, exclusive=True, reverse=rev, offsets=o, check=True)
             want = oracle.scan(x, exclusive=True, reverse=rev, offsets=offs)
             assert bits_equal(y.cpu().numpy(), want), (k, rev, "seg")
 
@@ -236,7 +236,7 @@ def test_unaligned_input_and_output(dev, dtype, n):
                 y = yb[ky:ky + n]
                 y.fill_(float("nan"))
                 det.det_scan(xb[kx:kx + n], y=y, exclusive=excl, reverse=rev,
-                             offsets=o if seg is not None else None)
+                             offsets=o if seg is not None else None, check=True)
                 want = oracle.scan(xs, exclusive=excl, reverse=rev, offsets=seg)
                 got = y.cpu().numpy()
                 assert bits_equal(got, want), (kx, ky, excl, rev, seg is not None,
@@ -256,7 +256,7 @@ def test_scan_health_word_stays_clear(dev, dtype):
                      device=dev)
     for excl, rev in MODES:
         for seg in (None, o):
-            det.det_scan(t, exclusive=excl, reverse=rev, offsets=seg, ws=ws)
+            det.det_scan(t, exclusive=excl, reverse=rev, offsets=seg, ws=ws, check=True)
             assert int(det.det_scan_error(ws).item()) == 0, (excl, rev, seg is not None)
 
 
@@ -270,9 +270,9 @@ def test_int32_scan_parity(dev, n):
     t = torch.from_numpy(x).to(dev)
     o = torch.from_numpy(offs).to(dev)
     for excl, rev in MODES:
-        got = det.det_scan(t, exclusive=excl, reverse=rev).cpu().numpy()
+        got = det.det_scan(t, exclusive=excl, reverse=rev, check=True).cpu().numpy()
         assert np.array_equal(got, oracle.scan_int32(x, excl, rev)), (excl, rev)
-        got = det.det_scan(t, exclusive=excl, reverse=rev, offsets=o).cpu().numpy()
+        got = det.det_scan(t, exclusive=excl, reverse=rev, offsets=o, check=True).cpu().numpy()
         assert np.array_equal(got, oracle.scan_int32(x, excl, rev, offs)), (excl, rev, "seg")
 
 
@@ -287,7 +287,7 @@ def test_count_scan_write_compaction(dev):
     outs = set()
     for _ in range(3):
         want = (vt > 0).to(torch.int32)
-        slot = det.det_scan(want, exclusive=True)
+        slot = det.det_scan(want, exclusive=True, check=True)
         total = int(slot[-1].item() + want[-1].item())
         comp = torch.empty(total, dtype=torch.float32, device=dev)
         keep = want.bool()
@@ -320,10 +320,10 @@ def test_scan_special_values(dev, dtype, n):
     t = torch.from_numpy(x).to(dev)
     o = torch.from_numpy(offs).to(dev)
     for excl, rev in MODES:
-        got = det.det_scan(t, exclusive=excl, reverse=rev).cpu().numpy()
+        got = det.det_scan(t, exclusive=excl, reverse=rev, check=True).cpu().numpy()
         want = oracle.scan(x, exclusive=excl, reverse=rev)
         assert bits_equal(got, want), (excl, rev, first_mismatch(got, want))
-        got = det.det_scan(t, exclusive=excl, reverse=rev, offsets=o).cpu().numpy()
+        got = det.det_scan(t, exclusive=excl, reverse=rev, offsets=o, check=True).cpu().numpy()
         want = oracle.scan(x, exclusive=excl, reverse=rev, offsets=offs)
         assert bits_equal(got, want), (excl, rev, "seg", first_mismatch(got, want))
 
@@ -335,7 +335,7 @@ def test_scan_all_negative_zero(dev, dtype):
     x = np.full(n, -0.0, dtype)
     t = torch.from_numpy(x).to(dev)
     for excl, rev in MODES:
-        got = det.det_scan(t, exclusive=excl, reverse=rev).cpu().numpy()
+        got = det.det_scan(t, exclusive=excl, reverse=rev, check=True).cpu().numpy()
         assert bits_equal(got, oracle.scan(x, exclusive=excl, reverse=rev))
         first = got[-1] if rev else got[0]
         assert np.signbit(first) == (not excl)
