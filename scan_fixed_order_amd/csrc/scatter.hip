@@ -35,16 +35,21 @@ constexpr int kSegD = 8192;     // scalar: ranks per block
 constexpr int kRowD = 64;       // rows: member rows per block
 constexpr int kBuckets0 = 257;  // first pass: 256 digits + the out-of-range bucket
 
-// Key output of a radix pass: uint32_t / uint16_t keys as they are; uint8_t, only the key's
-// second byte (the next pass's digit: the two-pass byte path); NoKey, none (the last pass of
-// that path, whose destination offsets come from the histograms).
+// Key output of a radix pass: uint32_t / uint16_t keys as they are; KeyHi8 / KeyHi16, the
+// key shifted down by the byte this pass sorted on, as one or two bytes (the later passes'
+// digits: the byte paths, whose keys shrink pass by pass); NoKey, none (the last pass of a
+// byte path, whose destination offsets come from the histograms).
 struct NoKey {};
+struct KeyHi8 {};
+struct KeyHi16 {};
 template <typename KO>
 __device__ __forceinline__ void put_key(KO* keys_out, int64_t g, uint32_t kk) {
     if constexpr (__is_same(KO, NoKey)) {
         (void)keys_out, (void)g, (void)kk;
-    } else if constexpr (sizeof(KO) == 1) {
-        keys_out[g] = (KO)(kk >> 8);
+    } else if constexpr (__is_same(KO, KeyHi8)) {
+        reinterpret_cast<uint8_t*>(keys_out)[g] = (uint8_t)(kk >> 8);
+    } else if constexpr (__is_same(KO, KeyHi16)) {
+        reinterpret_cast<uint16_t*>(keys_out)[g] = (uint16_t)(kk >> 8);
     } else {
         keys_out[g] = (KO)kk;
     }
@@ -115,6 +120,27 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s4
     *total = all;
     __syncthreads();
     return before + inc - v;
+}
+
+// One count per active lane into the LDS counters cnt[d] (integers, so any order is exact).
+// When at least 8 lanes share the first active lane's digit (a wave-uniform test), those lanes
+// add theirs as one addition by the lowest of them: skewed digits (a contended destination, a
+// heavy Zipf head, the few values of a key's top bits) otherwise put most lanes of one atomic
+// on one counter.  Other rows, the usual case for uniform keys, take one atomic per lane.
+__device__ __forceinline__ void count_digit(uint32_t* cnt, int d) {
+    const int d0 = __builtin_amdgcn_readfirstlane(d);
+    const uint64_t m0 = __ballot(d == d0);
+    if (__popcll(m0) >= 8) {
+        if (d == d0) {
+            if (__builtin_amdgcn_mbcnt_hi((uint32_t)(m0 >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m0, 0u)) == 0u)
+                atomicAdd(&cnt[d0], (uint32_t)__popcll(m0));
+        } else {
+            atomicAdd(&cnt[d], 1u);
+        }
+    } else {
+        atomicAdd(&cnt[d], 1u);
+    }
 }
 
 // ---------------------------------------------------------------- histogram offsets
@@ -349,24 +375,15 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
             if (__builtin_amdgcn_ballot_w64(!same) == 0ull) {
                 if (lane == 0) atomicAdd(&cnt[wave][dref], (uint32_t)(64 * NK));
             } else {
-                // row by row: a row on one digit (skewed keys) is added with one atomic rather
-                // than 64 on the same counter
+                // row by row, the lanes on the first lane's digit as one addition
 #pragma unroll
-                for (int k = 0; k < NK; ++k) {
-                    const int d = digit_of<FIRST>(kk[k], B, shift);
-                    const int d0 = __builtin_amdgcn_readfirstlane(d);
-                    if (__builtin_amdgcn_ballot_w64(d != d0) == 0ull) {
-                        if (lane == 0) atomicAdd(&cnt[wave][d0], 64u);
-                    } else {
-                        atomicAdd(&cnt[wave][d], 1u);
-                    }
-                }
+                for (int k = 0; k < NK; ++k) count_digit(cnt[wave], digit_of<FIRST>(kk[k], B, shift));
             }
         } else {
 #pragma unroll
             for (int k = 0; k < NK; ++k) {
                 const int q = pos(k);
-                if (q < H && base + q < m) atomicAdd(&cnt[wave][digit_of<FIRST>(kk[k], B, shift)], 1u);
+                if (q < H && base + q < m) count_digit(cnt[wave], digit_of<FIRST>(kk[k], B, shift));
             }
         }
     }
@@ -651,9 +668,13 @@ __global__ __launch_bounds__(256) void k_bin_offsets(const KT* __restrict__ K,
 // of high byte h in [c H, row1[l]), counted here from the first pass's key bytes; when
 // row1[l] = m no key has a low byte of l or more, and off[b] = the start of bucket h + 1.
 // Integers only.  A workgroup per low byte, a thread per high byte.
+// (Three-pass path: the same with KH = uint16_t, the first pass's output keys holding bits
+// 8..23, whose low byte is the second digit; it yields the offsets of the 16-bit low part of
+// every key, B = 65536, and k_bin_offsets_third takes it from there.)
+template <typename KH>
 __global__ __launch_bounds__(256) void k_bin_offsets_bytes(
     const uint32_t* __restrict__ row1, const uint32_t* __restrict__ ex2,
-    const uint8_t* __restrict__ hb, const uint32_t* __restrict__ nvalid, int64_t B, int64_t n,
+    const KH* __restrict__ hb, const uint32_t* __restrict__ nvalid, int64_t B, int64_t n,
     int64_t H, uint32_t* __restrict__ off, int64_t* __restrict__ n_skipped) {
     __shared__ uint32_t cnt[256];
     const int l = blockIdx.x, h = threadIdx.x;
@@ -663,7 +684,7 @@ __global__ __launch_bounds__(256) void k_bin_offsets_bytes(
     __syncthreads();
     const int64_t c = pos / H;
     if (pos < m)
-        for (int64_t q = c * H + h; q < pos; q += 256) atomicAdd(&cnt[hb[q]], 1u);
+        for (int64_t q = c * H + h; q < pos; q += 256) count_digit(cnt, (int)(hb[q] & 255u));
     __syncthreads();
     const int64_t b = (int64_t)h * 256 + l;
     if (b < B) {
@@ -673,6 +694,42 @@ __global__ __launch_bounds__(256) void k_bin_offsets_bytes(
         off[b] = o;
     }
     if (l == 0 && h == 0) {
+        off[B] = (uint32_t)m;
+        if (n_skipped) *n_skipped = n - m;
+    }
+}
+
+// The three-pass path (scalar destinations in (65536, 2^24]): off[b] for b = 65536 t + p (t the
+// key's third byte, p its low 16 bits) = the keys with a third byte below t, plus those with
+// third byte t and low part below p.  off2[p] (k_bin_offsets_bytes on the first two passes) is
+// where the low parts of p and above start in the second pass's output, which the third pass
+// sorted by the third byte; with c the chunk holding position off2[p], off[b] = ex3[c][t] + the
+// keys of third byte t in [c H, off2[p]), counted from the second pass's key bytes; when
+// off2[p] = m, off[b] = the start of the third pass's bucket t + 1.  A workgroup per p, a thread
+// per t.
+__global__ __launch_bounds__(256) void k_bin_offsets_third(
+    const uint32_t* __restrict__ off2, const uint32_t* __restrict__ ex3,
+    const uint8_t* __restrict__ tb, const uint32_t* __restrict__ nvalid, int64_t B, int64_t n,
+    int64_t H, uint32_t* __restrict__ off, int64_t* __restrict__ n_skipped) {
+    __shared__ uint32_t cnt[256];
+    const int64_t p = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t m = *nvalid;
+    const int64_t pos = off2[p];
+    cnt[t] = 0u;
+    __syncthreads();
+    const int64_t c = pos / H;
+    if (pos < m)
+        for (int64_t q = c * H + t; q < pos; q += 256) count_digit(cnt, (int)tb[q]);
+    __syncthreads();
+    const int64_t b = (int64_t)t * 65536 + p;
+    if (b < B) {
+        uint32_t o;
+        if (pos < m) o = ex3[c * 256 + t] + cnt[t];
+        else o = t < 255 ? ex3[t + 1] : (uint32_t)m;   // row 0 of ex3: the bucket starts
+        off[b] = o;
+    }
+    if (p == 0 && t == 0) {
         off[B] = (uint32_t)m;
         if (n_skipped) *n_skipped = n - m;
     }
@@ -1324,8 +1381,10 @@ int key_passes(int64_t B) {
 
 struct SLayout {
     int64_t H, nchunks, nhist, nsums, nrange;
-    bool bytes;   // the two-pass byte path (scalar destinations in (256, 65536])
-    size_t keysA, keysB, payA, payB, hist, hist2, sums, ctrl, off, rbin, pF, pC, total;
+    int bytes;    // byte paths for scalar destinations: 2 passes for (256, 65536], 3 passes
+                  // for (65536, 2^24]; 0 otherwise
+    size_t keysA, keysB, payA, payB, hist, hist2, hist3, off2, sums, ctrl, off, rbin, pF, pC,
+        total;
 };
 
 // idx_payload: the sort carries source indices (4 bytes) even for scalar destinations
@@ -1356,8 +1415,11 @@ SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt,
     L.hist = take((size_t)L.nhist * 4);
     L.sums = take((size_t)L.nsums * 4);
     L.off = take((size_t)(num_out + 1) * 4);
-    L.bytes = !rows && !idx_payload && key_passes(num_out) == 2;
+    const int kp = key_passes(num_out);
+    L.bytes = (!rows && !idx_payload && (kp == 2 || kp == 3)) ? kp : 0;
     L.hist2 = take(L.bytes ? (size_t)256 * L.nchunks * 4 : 4);
+    L.hist3 = take(L.bytes == 3 ? (size_t)256 * L.nchunks * 4 : 4);
+    L.off2 = take(L.bytes == 3 ? (size_t)(65536 + 1) * 4 : 4);
     L.rbin = take(L.bytes ? (size_t)L.nrange * 4 : 4);
     L.pF = take((size_t)L.nrange * pe);
     L.pC = take((size_t)L.nrange * pe);
@@ -1433,53 +1495,102 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
     return DET_SUCCESS;
 }
 
-// The two-pass byte path (scalar destinations in (256, 65536]): the first pass sorts by the
-// low byte and writes only each key's high byte, the second sorts by that byte and writes no
-// keys; k_bin_offsets_bytes derives the destination offsets from the two passes' offsets.
-// *HB receives the first pass's key bytes, *SP the sorted payloads.
+// The byte paths (scalar destinations): the keys shrink pass by pass.  Two passes for
+// (256, 65536]: the first sorts by the low byte and writes only each key's second byte, the
+// second sorts by that byte and writes no keys.  Three passes for (65536, 2^24]: the first
+// writes bits 8..23 as 16 bits, the second sorts by their low byte and writes the third byte,
+// the third sorts by it and writes no keys.  The destination offsets then follow from the
+// passes' offsets (k_bin_offsets_bytes, k_bin_offsets_third).  *SP receives the sorted
+// payloads.
 template <typename P>
 det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
                               int64_t num_out, const SLayout& L, char* ws, hipStream_t s,
-                              const uint8_t** HB, const P** SP) {
+                              const P** SP) {
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
-    uint8_t* kb = reinterpret_cast<uint8_t*>(ws + L.keysA);
     P* pay[2] = {reinterpret_cast<P*>(ws + L.payA), reinterpret_cast<P*>(ws + L.payB)};
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
     uint32_t* hist2 = reinterpret_cast<uint32_t*>(ws + L.hist2);
+    uint32_t* hist3 = reinterpret_cast<uint32_t*>(ws + L.hist3);
     uint32_t* sums = reinterpret_cast<uint32_t*>(ws + L.sums);
     const uint32_t* kin = reinterpret_cast<const uint32_t*>(index);
     const uint32_t B = (uint32_t)num_out;
     const unsigned grid = (unsigned)L.nchunks;
     const size_t lds = (size_t)launch_override().extra_lds;
+    const int nc = (int)L.H;
+    auto hist_of = [&](uint32_t* h, int nb, uint32_t* ident, bool first) {
+        return hist_offsets(h, L.nchunks, nb, sums + 512, sums, first ? ctrl : nullptr, ident, s);
+    };
+    // pass 1: the low byte (and the out-of-range bucket)
     {
         KernelTimer kt("k_radix_hist", s);
         k_radix_hist<true, uint32_t><<<grid, 256, lds, s>>>(kin, n, ctrl, B, 0, kBuckets0,
-                                                            L.nchunks, (int)L.H, hist);
+                                                            L.nchunks, nc, hist);
     }
-    det_status st = hist_offsets(hist, L.nchunks, kBuckets0, sums + 512, sums, ctrl, ctrl + 16, s);
+    det_status st = hist_of(hist, kBuckets0, ctrl + 16, true);
     if (st != DET_SUCCESS) return st;
+    if (L.bytes == 2) {
+        uint8_t* kb = reinterpret_cast<uint8_t*>(ws + L.keysA);
+        {
+            KernelTimer kt("k_radix_scatter", s);
+            k_radix_scatter<P, true, false, KeyHi8, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
+                kin, pay_in0, reinterpret_cast<KeyHi8*>(kb), pay[0], n, ctrl, B, 0, L.nchunks,
+                hist, ctrl + 16);
+        }
+        if ((st = launch_status()) != DET_SUCCESS) return st;
+        {
+            KernelTimer kt("k_radix_hist", s);
+            k_radix_hist<false, uint8_t><<<grid, 256, lds, s>>>(kb, n, ctrl, B, 0, 256,
+                                                               L.nchunks, nc, hist2);
+        }
+        if ((st = hist_of(hist2, 256, ctrl + 17, false)) != DET_SUCCESS) return st;
+        {
+            KernelTimer kt("k_radix_scatter", s);
+            k_radix_scatter<P, false, false, NoKey, uint8_t><<<grid, kRadixNT<P>, lds, s>>>(
+                kb, pay[0], static_cast<NoKey*>(nullptr), pay[1], n, ctrl, B, 0, L.nchunks,
+                hist2, ctrl + 17);
+        }
+        if ((st = launch_status()) != DET_SUCCESS) return st;
+        *SP = pay[1];
+        return DET_SUCCESS;
+    }
+    uint16_t* k16 = reinterpret_cast<uint16_t*>(ws + L.keysA);
+    uint8_t* kb = reinterpret_cast<uint8_t*>(ws + L.keysB);
     {
         KernelTimer kt("k_radix_scatter", s);
-        k_radix_scatter<P, true, false, uint8_t, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
-            kin, pay_in0, kb, pay[0], n, ctrl, B, 0, L.nchunks, hist, ctrl + 16);
+        k_radix_scatter<P, true, false, KeyHi16, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
+            kin, pay_in0, reinterpret_cast<KeyHi16*>(k16), pay[0], n, ctrl, B, 0, L.nchunks,
+            hist, ctrl + 16);
     }
     if ((st = launch_status()) != DET_SUCCESS) return st;
+    // pass 2: the second byte, the low byte of the 16-bit keys
     {
         KernelTimer kt("k_radix_hist", s);
-        k_radix_hist<false, uint8_t><<<grid, 256, lds, s>>>(kb, n, ctrl, B, 0, 256, L.nchunks,
-                                                           (int)L.H, hist2);
+        k_radix_hist<false, uint16_t><<<grid, 256, lds, s>>>(k16, n, ctrl, B, 0, 256,
+                                                            L.nchunks, nc, hist2);
     }
-    st = hist_offsets(hist2, L.nchunks, 256, sums + 512, sums, nullptr, ctrl + 17, s);
-    if (st != DET_SUCCESS) return st;
+    if ((st = hist_of(hist2, 256, ctrl + 17, false)) != DET_SUCCESS) return st;
     {
         KernelTimer kt("k_radix_scatter", s);
-        k_radix_scatter<P, false, false, NoKey, uint8_t><<<grid, kRadixNT<P>, lds, s>>>(
-            kb, pay[0], static_cast<NoKey*>(nullptr), pay[1], n, ctrl, B, 0, L.nchunks, hist2,
+        k_radix_scatter<P, false, false, KeyHi8, uint16_t><<<grid, kRadixNT<P>, lds, s>>>(
+            k16, pay[0], reinterpret_cast<KeyHi8*>(kb), pay[1], n, ctrl, B, 0, L.nchunks, hist2,
             ctrl + 17);
     }
     if ((st = launch_status()) != DET_SUCCESS) return st;
-    *HB = kb;
-    *SP = pay[1];
+    // pass 3: the third byte
+    {
+        KernelTimer kt("k_radix_hist", s);
+        k_radix_hist<false, uint8_t><<<grid, 256, lds, s>>>(kb, n, ctrl, B, 0, 256, L.nchunks,
+                                                           nc, hist3);
+    }
+    if ((st = hist_of(hist3, 256, ctrl + 18, false)) != DET_SUCCESS) return st;
+    {
+        KernelTimer kt("k_radix_scatter", s);
+        k_radix_scatter<P, false, false, NoKey, uint8_t><<<grid, kRadixNT<P>, lds, s>>>(
+            kb, pay[1], static_cast<NoKey*>(nullptr), pay[0], n, ctrl, B, 0, L.nchunks, hist3,
+            ctrl + 18);
+    }
+    if ((st = launch_status()) != DET_SUCCESS) return st;
+    *SP = pay[0];
     return DET_SUCCESS;
 }
 
@@ -1509,19 +1620,30 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
     uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
     if constexpr (!ROWS) {
         if (L.bytes) {
-            // two passes with byte keys, offsets from the histograms, no key reads after
-            const uint8_t* HB = nullptr;
+            // byte keys, offsets from the histograms, no key reads after the sort
             const P* SP = nullptr;
             det_status st = sort_by_dest_bytes<P>(index, reinterpret_cast<const P*>(values), n,
-                                                  num_out, L, ws, s, &HB, &SP);
+                                                  num_out, L, ws, s, &SP);
             if (st != DET_SUCCESS) return st;
             uint32_t* rbin = reinterpret_cast<uint32_t*>(ws + L.rbin);
+            const uint32_t* h1 = reinterpret_cast<const uint32_t*>(ws + L.hist);
+            const uint32_t* h2 = reinterpret_cast<const uint32_t*>(ws + L.hist2);
             {
                 KernelTimer kt("k_bin_offsets", s);
-                k_bin_offsets_bytes<<<256, 256, 0, s>>>(
-                    reinterpret_cast<const uint32_t*>(ws + L.hist),
-                    reinterpret_cast<const uint32_t*>(ws + L.hist2), HB, ctrl, num_out, n, L.H,
-                    off, n_skipped);
+                if (L.bytes == 2) {
+                    k_bin_offsets_bytes<uint8_t><<<256, 256, 0, s>>>(
+                        h1, h2, reinterpret_cast<const uint8_t*>(ws + L.keysA), ctrl, num_out, n,
+                        L.H, off, n_skipped);
+                } else {
+                    uint32_t* off2 = reinterpret_cast<uint32_t*>(ws + L.off2);
+                    k_bin_offsets_bytes<uint16_t><<<256, 256, 0, s>>>(
+                        h1, h2, reinterpret_cast<const uint16_t*>(ws + L.keysA), ctrl, 65536, n,
+                        L.H, off2, nullptr);
+                    k_bin_offsets_third<<<65536, 256, 0, s>>>(
+                        off2, reinterpret_cast<const uint32_t*>(ws + L.hist3),
+                        reinterpret_cast<const uint8_t*>(ws + L.keysB), ctrl, num_out, n, L.H,
+                        off, n_skipped);
+                }
                 k_range_bins<<<dim3((unsigned)cdiv(L.nrange, 4)), dim3(256), 0, s>>>(
                     off, num_out, L.nrange, rbin);
             }

@@ -41,7 +41,9 @@ def rounding(shape, dtype, seed):
 @pytest.mark.parametrize("dtype", [F32, F64])
 @pytest.mark.parametrize("n,B", [(1, 1), (7, 1), (1000, 7), (65537, 256), (65537, 257),
                                  (100003, 1000), (300007, 65536), (300007, 65537),
-                                 (1 << 20, 1 << 20), (200000, 3)])
+                                 (1 << 20, 1 << 20), (200000, 3), (2000003, 131073),
+                                 (500009, (1 << 24) - 1), (500009, 1 << 24),
+                                 (300007, (1 << 24) + 1)])
 def test_scalar_parity(dev, dtype, n, B):
     rng = np.random.default_rng(n + B)
     v = rounding(n, dtype, n)
@@ -55,14 +57,15 @@ def test_scalar_parity(dev, dtype, n, B):
 
 
 @pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("B", [65536, 1 << 20])
 @pytest.mark.parametrize("n", [1, 4096, 8192, 8193, 100003, 3 * 8192 * 8192 // 1024 + 1])
-def test_contended_one_bin(dev, dtype, n):
+def test_contended_one_bin(dev, dtype, n, B):
     v = rounding(n, dtype, 1)
     idx = np.zeros(n, np.int32)
-    o = np.zeros(65536, dtype)
+    o = np.zeros(B, dtype)
     got, _, k = gpu_scatter(v, idx, o, dev)
     want, _, _ = oracle.scatter_add(v, idx, o)
-    assert bits_equal(got, want), first_mismatch(got, want)
+    assert bits_equal(got, want), (B, first_mismatch(got, want))
     assert k == 0
     # cross-op identity: +0.0 plus the reproducible sum
     s = det.det_sum(torch.from_numpy(v).to(dev)).cpu().numpy()
