@@ -85,7 +85,7 @@ det_status det_sum(const void* x, int64_t n, det_dtype dtype, void* out, void* w
  * that GPU's single array, which keeps the last call's partials: calls that overlap in time
  * on one GPU (different streams or host threads without ordering) race and give unspecified
  * results.  Calls ordered on one stream are safe. */
-#define DET_SUM_NOALLOC_SCRATCH_BYTES (1048576 + 256)
+#define DET_SUM_NOALLOC_SCRATCH_BYTES (1048576 + 16384 + 256)
 det_status det_sum_noalloc(const void* x, int64_t n, det_dtype dtype, void* out, void* stream);
 
 /* ------------------------------------------------------------------ scan */
@@ -131,7 +131,8 @@ det_status det_scan(const void* x, void* y, int64_t n, det_dtype dtype, unsigned
  * returned DET_SUCCESS.  Any failure of the kernel's forward progress (a broken offsets
  * precondition, a hardware fault, a scheduler that never runs a workgroup holding a claimed
  * tile) ends that way, never in a hang; a silent wrong result is possible only if a status
- * word arrives corrupted yet tagged ready.  Shorter scans never wait and leave the word at 0.
+ * word arrives corrupted yet tagged ready.  Shorter and empty scans never wait and leave the
+ * word at 0.
  * Enqueues on `stream` a copy of the word into *out (device int32: 0 = every wait ended
  * normally, 1 = some wait gave up); returns without waiting.  ws: the workspace the scan used
  * (device); out: device int32 (written).  DET_ERROR_INVALID_VALUE for NULL. */

@@ -34,7 +34,7 @@ size_t sum_workspace(int64_t n, det_dtype dt);
 det_status sum_launch(const void* x, int64_t n, det_dtype dt, void* out, void* ws, size_t ws_bytes,
                       hipStream_t s);
 // det_sum with the partials in the library's own per-GPU array (no workspace argument)
-constexpr size_t kSumNoAllocBytes = ((size_t)1 << 20) + 256;
+constexpr size_t kSumNoAllocBytes = ((size_t)1 << 20) + ((size_t)1 << 14) + 256;
 constexpr int kMaxDevices = 64;
 det_status sum_noalloc_launch(const void* x, int64_t n, det_dtype dt, void* out, hipStream_t s);
 

@@ -208,7 +208,10 @@ const void* k_scan_fn(int mode) {
 template <typename T>
 det_status scan_impl(const T* x, T* y, int64_t n, unsigned flags, const int64_t* offs,
                      int64_t nseg, char* ws, hipStream_t s) {
-    if (n == 0) return DET_SUCCESS;
+    if (n == 0) {   // nothing to scan; the health word still reports this call: no wait
+        k_zero_words<<<1, 64, 0, s>>>(reinterpret_cast<uint64_t*>(ws + kErrOff), 1);
+        return launch_status();
+    }
     const LaunchOverride& ov = launch_override();
     const int A = ov.scan_A ? ov.scan_A : kScanA;
     const int A2 = ov.scan_A2 ? ov.scan_A2 : kScanA2;

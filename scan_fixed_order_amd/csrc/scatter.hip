@@ -12,16 +12,23 @@
 //   sort   stable LSD radix sort of (key, payload) with 8-bit digits; the first pass also
 //          splits off out-of-range keys into a 257th bucket at the end, and later passes only
 //          see the valid prefix.  Payload = the value (row_len 1) or the source row (rows and
-//          the running prev).  Keys travel as 16 bits when every destination fits.  Per pass:
-//          per-chunk digit histogram, integer exclusive scan, then each workgroup ranks its
-//          chunk stably (wave ballots + per-wave digit counters), stages it in LDS in digit
-//          order and writes contiguous runs;
-//   bins   off[b] = first sorted position with key >= b (binary search per bin);
+//          the running prev).  Per pass: per-chunk digit histogram, integer exclusive scan,
+//          then each workgroup ranks its chunk stably (wave ballots + per-wave digit
+//          counters), stages it in LDS in digit order and writes contiguous runs.  Scalar
+//          values into 257..2^24 destinations take the byte paths: each pass writes only the
+//          key bytes the later passes sort on (2 or 3 passes: 4 -> 1 -> 0 or 4 -> 2 -> 1 -> 0
+//          bytes), and no sorted key is ever read again.  Otherwise keys travel as 16 bits
+//          when every destination fits;
+//   bins   off[b] = first sorted position with key >= b: on the byte paths from the passes'
+//          bucket offsets and a count of key bytes inside one chunk, otherwise by binary
+//          search per bin;
 //   reduce a destination's members are cut at local ranks that are multiples of D (D = 8192
 //          values, or 64 rows).  Each block is a subtree of PW; one pass reduces every block
 //          (a lane per block of at most 32 values, a wave per larger block) and applies
 //          destinations with one block; a second pass combines the block values of longer
-//          destinations by the same tree and applies them.
+//          destinations by the same tree and applies them.  Without sorted keys (byte paths)
+//          each range of D positions starts from the destination holding its first position
+//          (a 64-way search per range) and walks the offsets.
 // The running prev (det_scatter_add_running) adds, between sort and reduce: the grouped values
 // gathered column by column, the exclusive segmented det_scan of each column (one segment per
 // destination), and prev written from it and the old values.
@@ -148,10 +155,10 @@ __device__ __forceinline__ void count_digit(uint32_t* cnt, int d) {
 // The digit histogram of a pass is row-major, hist[c * nb + d] = keys of chunk c with digit d,
 // so each workgroup writes its counts contiguously.  The scatter needs, for chunk c and digit
 // d, off[c][d] = (keys with a digit below d) + (keys with digit d in chunks before c): an
-// exclusive scan in digit-major order, done in four launches over blocks of kRowBlk rows:
+// exclusive scan in digit-major order, done in three launches over blocks of kRowBlk rows:
 // column sums per row block (stored column-major), an exclusive scan of each column's block
-// sums, an exclusive scan of the digit totals, then each row block writes its offsets in
-// place.  Integers, so exact in any order.
+// sums, then each row block scans the digit totals and writes its offsets in place.
+// Integers, so exact in any order.
 constexpr int kRowBlk = 128;
 constexpr int kRowBatch = 16;   // rows whose loads are in flight together
 
@@ -199,33 +206,33 @@ __global__ __launch_bounds__(256) void k_hist_colscan(uint32_t* __restrict__ csu
     if (threadIdx.x == 0) tot[blockIdx.x] = carry;
 }
 
-// tot[d] <- keys with a digit below d (d < nb <= 257; thread 0 also handles d = 256)
-// ident: set to 1 when one bucket holds every key (the pass is then the identity permutation)
-__global__ __launch_bounds__(256) void k_hist_digitscan(uint32_t* __restrict__ tot, int nb,
-                                                        uint32_t* __restrict__ ident) {
-    __shared__ uint32_t s4[4];
-    const int t = threadIdx.x;
-    const uint32_t v = tot[t];
-    const uint32_t v256 = nb > 256 ? tot[256] : 0u;
-    uint32_t total;
-    const uint32_t ex = block_excl_scan_u32(v, s4, &total);
-    const uint32_t grand = total + v256;
-    const int one = __syncthreads_or(v == grand || v256 == grand);
-    tot[t] = ex;
-    if (nb > 256 && t == 0) tot[256] = total;
-    if (t == 0) *ident = one ? 1u : 0u;
-}
-
+// tot[d] = the keys of digit d (column totals).  Each workgroup turns them into the digit
+// bases (keys with a digit below d; d = 256, the out-of-range bucket, after every digit) and
+// writes its row block's offsets in place.  Workgroup 0 also sets *ident = 1 when one bucket
+// holds every key (the pass is then the identity permutation), else 0, and *valid (if given)
+// = the keys in range (the base of bucket 256).
 __global__ __launch_bounds__(256) void k_hist_apply(uint32_t* __restrict__ hist, int64_t nrows,
                                                     int nb, int64_t nrb,
                                                     const uint32_t* __restrict__ csum,
-                                                    const uint32_t* __restrict__ tot) {
+                                                    const uint32_t* __restrict__ tot,
+                                                    uint32_t* __restrict__ ident,
+                                                    uint32_t* __restrict__ valid) {
+    __shared__ uint32_t s4[4];
     const int t = threadIdx.x;
     const bool extra = nb > 256 && t == 0;
+    const uint32_t v = tot[t];
+    const uint32_t v256 = nb > 256 ? tot[256] : 0u;
+    uint32_t total;
+    const uint32_t base = block_excl_scan_u32(v, s4, &total);
+    const int one = __syncthreads_or(v == total + v256 || v256 == total + v256);
+    if (blockIdx.x == 0 && t == 0) {
+        *ident = one ? 1u : 0u;
+        if (valid) *valid = total;
+    }
     const int64_t r0 = (int64_t)blockIdx.x * kRowBlk;
     const int64_t r1 = (r0 + kRowBlk < nrows) ? r0 + kRowBlk : nrows;
-    uint32_t run0 = tot[t] + csum[(int64_t)t * nrb + blockIdx.x];
-    uint32_t run1 = extra ? tot[256] + csum[(int64_t)256 * nrb + blockIdx.x] : 0u;
+    uint32_t run0 = base + csum[(int64_t)t * nrb + blockIdx.x];
+    uint32_t run1 = extra ? total + csum[(int64_t)256 * nrb + blockIdx.x] : 0u;
     for (int64_t r = r0; r < r1; r += kRowBatch) {
         uint32_t v[kRowBatch], w[kRowBatch];
 #pragma unroll
@@ -285,10 +292,6 @@ __global__ __launch_bounds__(256) void k_hist_offsets_small(uint32_t* __restrict
     if (valid && t == 0) *valid = total;
 }
 
-__global__ void k_copy_word(const uint32_t* __restrict__ src, uint32_t* __restrict__ dst) {
-    dst[0] = src[0];
-}
-
 // csum needs nb * nrb words, tot nb words (nb <= 257).  valid (first pass only): receives the
 // number of keys in range (the offset of the out-of-range bucket in chunk 0).  ident: 1 when
 // one bucket holds every key, else 0.
@@ -302,9 +305,8 @@ det_status hist_offsets(uint32_t* hist, int64_t nrows, int nb, uint32_t* csum, u
     const int64_t nrb = cdiv(nrows, kRowBlk);
     k_hist_colsums<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum);
     k_hist_colscan<<<dim3((unsigned)nb), dim3(256), 0, s>>>(csum, nrb, tot);
-    k_hist_digitscan<<<1, 256, 0, s>>>(tot, nb, ident);
-    k_hist_apply<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum, tot);
-    if (valid) k_copy_word<<<1, 1, 0, s>>>(hist + 256, valid);
+    k_hist_apply<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum, tot, ident,
+                                                          valid);
     return launch_status();
 }
 
@@ -438,8 +440,8 @@ __device__ __forceinline__ void radix_load(const KI* __restrict__ keys_in,
 // digit's run to its place in the output.  Rank of an item = (items of the chunk with a smaller
 // digit) + (items of its digit in earlier waves) + (items of its digit earlier in its wave):
 // the last part from the wave's ballots on each digit bit (the lanes that agree on every bit
-// are the item's peers), taken in item order k = 0 .. IPT-1 against per-wave counters in LDS,
-// which the lowest peer advances with one LDS atomic whose old value it hands to its peers.
+// are the item's peers), taken in item order k = 0 .. IPT-1 against per-wave counters in LDS:
+// every lane reads its digit's counter, then the lowest peer writes it advanced by the peers.
 // Integers only, so exact.  Leaves every barrier it passes balanced; ends with the LDS counters
 // cleared for the next chunk.
 template <typename P, bool FIRST, bool ROWS, bool FULL, typename KO>

@@ -108,3 +108,55 @@ def test_launch_shape_invariance(dev, dtype):
     finally:
         det.det_debug_set_launch(0, 0)
         det.det_debug_set_sum_chunk(0)
+
+
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_finishing_launch_reuses_workspace(dev, dtype):
+    """Sums of 2 to 1,024 chunks finish in the launch that writes the chunk values: each value
+    goes to a workspace slot tagged for the call, and the grid's last workgroup waits for every
+    tag, reduces the values and clears the tags.  Whatever the slots hold beforehand (a fresh
+    workspace's bytes, another size's values, a captured graph's earlier replay with the same
+    tag), every call must give the oracle's bits."""
+    # 2, 65, 184 and 1024 chunk values finish in one launch; 1025 take a second one
+    sizes = [16385, (1 << 20) + 7, 3_000_017, (1 << 24) - 5, (1 << 24) + 3]
+    xs = [rounding(n, dtype, n) for n in sizes]
+    wants = [np.asarray(oracle.det_sum(x), dtype) for x in xs]
+    ts = [torch.from_numpy(x).to(dev) for x in xs]
+    ws = torch.empty(det.det_sum_workspace_size(max(sizes), 0 if dtype == F32 else 1),
+                     dtype=torch.uint8, device=dev)
+    tdt = torch.float32 if dtype == F32 else torch.float64
+    outs = [torch.empty((), dtype=tdt, device=dev) for _ in sizes]
+
+    def check(k, tag):
+        assert bits_equal(outs[k].cpu().numpy(), wants[k]), (sizes[k], tag)
+
+    for fill in (0x00, 0xFF, 0x5A):
+        ws.fill_(fill)
+        for k in range(len(sizes)):
+            det.det_sum(ts[k], out=outs[k], ws=ws)
+            check(k, f"fill {fill:#x}")
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=gen))
+    graphs = []
+    side = torch.cuda.Stream()
+    for k in (0, 3):
+        det.det_sum(ts[k], out=outs[k], ws=ws)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=side):
+            det.det_sum(ts[k], out=outs[k], ws=ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs.append((k, g))
+    for rep in range(3):
+        for k, g in graphs:
+            outs[k].fill_(0.0)
+            g.replay()
+            torch.cuda.synchronize()
+            check(k, f"replay {rep}")
+            for j in (1, 2, 4):
+                outs[j].fill_(0.0)
+                det.det_sum(ts[j], out=outs[j], ws=ws)
+                torch.cuda.synchronize()
+                check(j, f"eager between replays {rep}")
