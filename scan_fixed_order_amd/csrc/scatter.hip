@@ -319,36 +319,49 @@ __device__ __forceinline__ int digit_of(uint32_t key, uint32_t B, int shift) {
     return (int)((key >> shift) & 255u);
 }
 
-// KI: the type keys are read in (16-bit after a pass that wrote them so)
-template <bool FIRST, typename KI>
+// Per-chunk digit counts: hist[c * nb + d] = keys of chunk c (positions [c H, c H + H)) with
+// digit d.  WPC waves per chunk, each counting into its own LDS histogram.  WPC = 1 (many
+// chunks): four chunks per workgroup, each wave writes its own row and no workgroup barrier is
+// needed, so a chunk of byte keys (4 or 8 KB) does not cost a whole workgroup's setup (f64 2^29
+// into 2^20 Zipf bins on MI355X: 1.21 -> 0.99 ms for the three passes' counts).  WPC = 4 (few
+// chunks, so the chunk's waves run side by side): the four histograms are summed.
+// KI: the type keys are read in (16-bit or byte keys after a pass that wrote them so).
+template <bool FIRST, typename KI, int WPC>
 __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys, int64_t n,
                                                     const uint32_t* __restrict__ nvalid, uint32_t B,
                                                     int shift, int nb, int64_t nchunks, int H,
                                                     uint32_t* __restrict__ hist) {
-    // one histogram per wave (fewer LDS atomics on the same counter)
+    static_assert(WPC == 1 || WPC == 4, "one wave or the whole workgroup per chunk");
     __shared__ uint32_t cnt[4][kBuckets0];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int i = threadIdx.x; i < 4 * kBuckets0; i += 256) (&cnt[0][0])[i] = 0u;
-    __syncthreads();
+    const int64_t c = WPC == 1 ? (int64_t)blockIdx.x * 4 + wave : (int64_t)blockIdx.x;
+    if (WPC == 1 && c >= nchunks) return;   // a whole wave; it then waits for no other wave
+    const int tt = WPC == 1 ? lane : (int)threadIdx.x;   // index in the chunk's team of waves
+    constexpr int TS = 64 * WPC;                          // the team's threads
+    uint32_t* const wc = cnt[wave];
+    for (int d = lane; d < kBuckets0; d += 64) wc[d] = 0u;
+    // a wave's LDS instructions run in order: its counts below follow its zeroing
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int64_t m = FIRST ? n : (int64_t)*nvalid;
-    const int64_t base = (int64_t)blockIdx.x * H;
+    const int64_t base = c * H;
     // a batch of NK keys per thread, all loads issued before the first count; a whole batch
-    // whose keys all share the digit of the wave's first key is added with one atomic
-    // (skewed and contended inputs), any other batch key by key (testing each key of a row
-    // for one shared digit cost more than it saved: 0.164 -> 0.151 ms per pass at 2^28)
+    // of a wave whose keys all share the digit of its first lane's first key is added with one
+    // atomic (skewed and contended inputs), any other batch row by row (count_digit)
     constexpr int NK = sizeof(KI) < 4 ? 32 : 16;
     constexpr int KPW = 4 / (int)sizeof(KI);      // keys per 32-bit word
-    constexpr int PER = 256 * NK;                 // keys per batch of the workgroup
+    constexpr int PER = TS * NK;                  // keys per batch of the team
     for (int i0 = 0; i0 < H; i0 += PER) {
         uint32_t kk[NK];
-        // thread t takes keys i0 + k * 256 + t (4-byte keys) or the KPW keys of word
-        // i0 / KPW + k * 256 + t (16-bit and byte keys, packed in 32-bit words: H is a multiple
+        // thread tt takes keys i0 + k * TS + tt (4-byte keys) or the KPW keys of word
+        // i0 / KPW + k * TS + tt (16-bit and byte keys, packed in 32-bit words: H is a multiple
         // of 4 and the keys 256-byte aligned)
         if constexpr (sizeof(KI) < 4) {
             const uint32_t* kw = reinterpret_cast<const uint32_t*>(keys) + base / KPW;
 #pragma unroll
             for (int k = 0; k < NK / KPW; ++k) {
-                const int w = i0 / KPW + k * 256 + (int)threadIdx.x;
+                const int w = i0 / KPW + k * TS + tt;
                 const uint32_t x = (KPW * w < H && base + KPW * w < m)
                                        ? __builtin_nontemporal_load(kw + w) : 0u;
 #pragma unroll
@@ -358,40 +371,60 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
         } else {
 #pragma unroll
             for (int k = 0; k < NK; ++k) {
-                const int64_t p = base + i0 + k * 256 + threadIdx.x;
+                const int64_t p = base + i0 + k * TS + tt;
                 // non-temporal: each key is read once here (0.21 -> 0.18 ms per pass at 2^28)
-                kk[k] = (i0 + k * 256 + (int)threadIdx.x < H && p < m)
+                kk[k] = (i0 + k * TS + tt < H && p < m)
                             ? (uint32_t)__builtin_nontemporal_load(keys + p) : 0u;
             }
         }
         auto pos = [&](int k) -> int {   // position of kk[k] in the chunk
-            return sizeof(KI) < 4 ? i0 + KPW * ((k / KPW) * 256 + (int)threadIdx.x) + k % KPW
-                                  : i0 + k * 256 + (int)threadIdx.x;
+            return sizeof(KI) < 4 ? i0 + KPW * ((k / KPW) * TS + tt) + k % KPW
+                                  : i0 + k * TS + tt;
         };
-        const bool full = i0 + PER <= H && base + i0 + PER <= m;   // the same for all threads
+        const bool full = i0 + PER <= H && base + i0 + PER <= m;   // uniform over the team
         if (full) {
             const int dref = __builtin_amdgcn_readfirstlane(digit_of<FIRST>(kk[0], B, shift));
             bool same = true;
 #pragma unroll
             for (int k = 0; k < NK; ++k) same = same && digit_of<FIRST>(kk[k], B, shift) == dref;
             if (__builtin_amdgcn_ballot_w64(!same) == 0ull) {
-                if (lane == 0) atomicAdd(&cnt[wave][dref], (uint32_t)(64 * NK));
+                if (lane == 0) atomicAdd(&wc[dref], (uint32_t)(64 * NK));
             } else {
-                // row by row, the lanes on the first lane's digit as one addition
 #pragma unroll
-                for (int k = 0; k < NK; ++k) count_digit(cnt[wave], digit_of<FIRST>(kk[k], B, shift));
+                for (int k = 0; k < NK; ++k) count_digit(wc, digit_of<FIRST>(kk[k], B, shift));
             }
         } else {
 #pragma unroll
             for (int k = 0; k < NK; ++k) {
                 const int q = pos(k);
-                if (q < H && base + q < m) count_digit(cnt[wave], digit_of<FIRST>(kk[k], B, shift));
+                if (q < H && base + q < m) count_digit(wc, digit_of<FIRST>(kk[k], B, shift));
             }
         }
     }
-    __syncthreads();
-    for (int d = threadIdx.x; d < nb; d += 256)
-        hist[(int64_t)blockIdx.x * nb + d] = (cnt[0][d] + cnt[1][d]) + (cnt[2][d] + cnt[3][d]);
+    if constexpr (WPC == 1) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int d = lane; d < nb; d += 64) hist[c * nb + d] = wc[d];
+    } else {
+        __syncthreads();
+        for (int d = threadIdx.x; d < nb; d += 256)
+            hist[c * nb + d] = (cnt[0][d] + cnt[1][d]) + (cnt[2][d] + cnt[3][d]);
+    }
+}
+
+// Launches k_radix_hist with one wave per chunk when there are enough chunks to fill the GPU
+// that way (four per compute unit), else with a workgroup per chunk.
+template <bool FIRST, typename KI>
+void radix_hist(const KI* keys, int64_t n, const uint32_t* nvalid, uint32_t B, int shift, int nb,
+                int64_t nchunks, int H, uint32_t* hist, size_t lds, hipStream_t s) {
+    KernelTimer kt("k_radix_hist", s);
+    if (nchunks >= 4 * (int64_t)cu_count())
+        k_radix_hist<FIRST, KI, 1><<<dim3((unsigned)cdiv(nchunks, 4)), dim3(256), lds, s>>>(
+            keys, n, nvalid, B, shift, nb, nchunks, H, hist);
+    else
+        k_radix_hist<FIRST, KI, 4><<<dim3((unsigned)nchunks), dim3(256), lds, s>>>(
+            keys, n, nvalid, B, shift, nb, nchunks, H, hist);
 }
 
 // P: payload word (uint32_t: f32 value bits or source row; uint64_t: f64 value bits)
@@ -1457,18 +1490,12 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
         const uint16_t* kin16 = reinterpret_cast<const uint16_t*>(kin);
         const P* pin = first ? pay_in0 : pay[(p - 1) & 1];
         const int nb = first ? kBuckets0 : 256;
-        {
-            KernelTimer kt("k_radix_hist", s);
-            if (first)
-                k_radix_hist<true, uint32_t><<<grid, 256, lds, s>>>(kin, n, ctrl, B, shift, nb,
-                                                                  L.nchunks, (int)L.H, hist);
-            else if (k16)
-                k_radix_hist<false, uint16_t><<<grid, 256, lds, s>>>(kin16, n, ctrl, B, shift, nb,
-                                                                   L.nchunks, (int)L.H, hist);
-            else
-                k_radix_hist<false, uint32_t><<<grid, 256, lds, s>>>(kin, n, ctrl, B, shift, nb,
-                                                                   L.nchunks, (int)L.H, hist);
-        }
+        if (first)
+            radix_hist<true>(kin, n, ctrl, B, shift, nb, L.nchunks, (int)L.H, hist, lds, s);
+        else if (k16)
+            radix_hist<false>(kin16, n, ctrl, B, shift, nb, L.nchunks, (int)L.H, hist, lds, s);
+        else
+            radix_hist<false>(kin, n, ctrl, B, shift, nb, L.nchunks, (int)L.H, hist, lds, s);
         // bucket offsets; the first pass also counts the keys in range into ctrl[0]
         uint32_t* ident = ctrl + 16 + p;   // one word per pass (at most 4 passes)
         det_status st = hist_offsets(hist, L.nchunks, nb, sums + 512, sums, first ? ctrl : nullptr,
@@ -1523,11 +1550,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
         return hist_offsets(h, L.nchunks, nb, sums + 512, sums, first ? ctrl : nullptr, ident, s);
     };
     // pass 1: the low byte (and the out-of-range bucket)
-    {
-        KernelTimer kt("k_radix_hist", s);
-        k_radix_hist<true, uint32_t><<<grid, 256, lds, s>>>(kin, n, ctrl, B, 0, kBuckets0,
-                                                            L.nchunks, nc, hist);
-    }
+    radix_hist<true>(kin, n, ctrl, B, 0, kBuckets0, L.nchunks, nc, hist, lds, s);
     det_status st = hist_of(hist, kBuckets0, ctrl + 16, true);
     if (st != DET_SUCCESS) return st;
     if (L.bytes == 2) {
@@ -1539,11 +1562,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
                 hist, ctrl + 16);
         }
         if ((st = launch_status()) != DET_SUCCESS) return st;
-        {
-            KernelTimer kt("k_radix_hist", s);
-            k_radix_hist<false, uint8_t><<<grid, 256, lds, s>>>(kb, n, ctrl, B, 0, 256,
-                                                               L.nchunks, nc, hist2);
-        }
+        radix_hist<false>(kb, n, ctrl, B, 0, 256, L.nchunks, nc, hist2, lds, s);
         if ((st = hist_of(hist2, 256, ctrl + 17, false)) != DET_SUCCESS) return st;
         {
             KernelTimer kt("k_radix_scatter", s);
@@ -1565,11 +1584,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
     }
     if ((st = launch_status()) != DET_SUCCESS) return st;
     // pass 2: the second byte, the low byte of the 16-bit keys
-    {
-        KernelTimer kt("k_radix_hist", s);
-        k_radix_hist<false, uint16_t><<<grid, 256, lds, s>>>(k16, n, ctrl, B, 0, 256,
-                                                            L.nchunks, nc, hist2);
-    }
+    radix_hist<false>(k16, n, ctrl, B, 0, 256, L.nchunks, nc, hist2, lds, s);
     if ((st = hist_of(hist2, 256, ctrl + 17, false)) != DET_SUCCESS) return st;
     {
         KernelTimer kt("k_radix_scatter", s);
@@ -1579,11 +1594,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
     }
     if ((st = launch_status()) != DET_SUCCESS) return st;
     // pass 3: the third byte
-    {
-        KernelTimer kt("k_radix_hist", s);
-        k_radix_hist<false, uint8_t><<<grid, 256, lds, s>>>(kb, n, ctrl, B, 0, 256, L.nchunks,
-                                                           nc, hist3);
-    }
+    radix_hist<false>(kb, n, ctrl, B, 0, 256, L.nchunks, nc, hist3, lds, s);
     if ((st = hist_of(hist3, 256, ctrl + 18, false)) != DET_SUCCESS) return st;
     {
         KernelTimer kt("k_radix_scatter", s);
