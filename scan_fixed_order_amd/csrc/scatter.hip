@@ -152,19 +152,21 @@ __device__ __forceinline__ void count_digit(uint32_t* cnt, int d) {
 
 // ---------------------------------------------------------------- histogram offsets
 
-// The digit histogram of a pass is row-major, hist[c * nb + d] = keys of chunk c with digit d,
-// so each workgroup writes its counts contiguously.  The scatter needs, for chunk c and digit
-// d, off[c][d] = (keys with a digit below d) + (keys with digit d in chunks before c): an
-// exclusive scan in digit-major order, done in three launches over blocks of kRowBlk rows:
-// column sums per row block (stored column-major), an exclusive scan of each column's block
-// sums, then each row block scans the digit totals and writes its offsets in place.
-// Integers, so exact in any order.
+// The digit counts of a pass are row-major, cnt[c * nb + d] = keys of chunk c with digit d (16
+// bits: a chunk holds at most 8192 keys), so each chunk's counts are written contiguously.  The
+// scatter needs, for chunk c and digit d, off[c][d] = (keys with a digit below d) + (keys with
+// digit d in chunks before c): an exclusive scan in digit-major order, done in three launches
+// over blocks of kRowBlk rows: column sums per row block (stored column-major), an exclusive
+// scan of each column's block sums, then each row block scans the digit totals and writes its
+// 32-bit offsets, off[c * nb + d].  Integers, so exact in any order.  (32-bit counts rewritten
+// in place moved more bytes: f64 2^29 into 2^20 Zipf bins on MI355X, 0.25 -> 0.18 ms for the
+// three passes' offsets.)
 constexpr int kRowBlk = 128;
 constexpr int kRowBatch = 16;   // rows whose loads are in flight together
 
 // csum[d * nrb + rb] = sum over the rows of block rb of column d (thread t: column t, and
 // thread 0 also column 256 when nb = 257)
-__global__ __launch_bounds__(256) void k_hist_colsums(const uint32_t* __restrict__ hist,
+__global__ __launch_bounds__(256) void k_hist_colsums(const uint16_t* __restrict__ hist,
                                                       int64_t nrows, int nb, int64_t nrb,
                                                       uint32_t* __restrict__ csum) {
     const int t = threadIdx.x;
@@ -208,10 +210,11 @@ __global__ __launch_bounds__(256) void k_hist_colscan(uint32_t* __restrict__ csu
 
 // tot[d] = the keys of digit d (column totals).  Each workgroup turns them into the digit
 // bases (keys with a digit below d; d = 256, the out-of-range bucket, after every digit) and
-// writes its row block's offsets in place.  Workgroup 0 also sets *ident = 1 when one bucket
-// holds every key (the pass is then the identity permutation), else 0, and *valid (if given)
-// = the keys in range (the base of bucket 256).
-__global__ __launch_bounds__(256) void k_hist_apply(uint32_t* __restrict__ hist, int64_t nrows,
+// writes its row block's offsets.  Workgroup 0 also sets *ident = 1 when one bucket holds
+// every key (the pass is then the identity permutation), else 0, and *valid (if given) = the
+// keys in range (the base of bucket 256).
+__global__ __launch_bounds__(256) void k_hist_apply(const uint16_t* __restrict__ hist,
+                                                    uint32_t* __restrict__ off, int64_t nrows,
                                                     int nb, int64_t nrb,
                                                     const uint32_t* __restrict__ csum,
                                                     const uint32_t* __restrict__ tot,
@@ -243,8 +246,8 @@ __global__ __launch_bounds__(256) void k_hist_apply(uint32_t* __restrict__ hist,
 #pragma unroll
         for (int k = 0; k < kRowBatch; ++k) {
             if (r + k < r1) {
-                hist[(r + k) * nb + t] = run0;
-                if (extra) hist[(r + k) * nb + 256] = run1;
+                off[(r + k) * nb + t] = run0;
+                if (extra) off[(r + k) * nb + 256] = run1;
             }
             run0 += v[k];
             run1 += w[k];
@@ -253,11 +256,12 @@ __global__ __launch_bounds__(256) void k_hist_apply(uint32_t* __restrict__ hist,
 }
 
 // The same offsets for few rows, in one launch of one workgroup: thread d sums column d, an
-// exclusive scan over the digit totals gives each digit's base, thread d rewrites its column
-// as running offsets.  *valid (if given) receives the base of digit 256 (the keys in range).
+// exclusive scan over the digit totals gives each digit's base, thread d writes its column's
+// running offsets.  *valid (if given) receives the base of digit 256 (the keys in range).
 constexpr int64_t kSmallHistRows = 512;
 
-__global__ __launch_bounds__(256) void k_hist_offsets_small(uint32_t* __restrict__ hist,
+__global__ __launch_bounds__(256) void k_hist_offsets_small(const uint16_t* __restrict__ hist,
+                                                            uint32_t* __restrict__ off,
                                                             int64_t nrows, int nb,
                                                             uint32_t* __restrict__ valid,
                                                             uint32_t* __restrict__ ident) {
@@ -281,11 +285,11 @@ __global__ __launch_bounds__(256) void k_hist_offsets_small(uint32_t* __restrict
 #pragma unroll 8
     for (int64_t r = 0; r < nrows; ++r) {
         const uint32_t v = hist[r * nb + t];
-        hist[r * nb + t] = run0;
+        off[r * nb + t] = run0;
         run0 += v;
         if (extra) {
             const uint32_t w = hist[r * nb + 256];
-            hist[r * nb + 256] = run1;
+            off[r * nb + 256] = run1;
             run1 += w;
         }
     }
@@ -295,18 +299,19 @@ __global__ __launch_bounds__(256) void k_hist_offsets_small(uint32_t* __restrict
 // csum needs nb * nrb words, tot nb words (nb <= 257).  valid (first pass only): receives the
 // number of keys in range (the offset of the out-of-range bucket in chunk 0).  ident: 1 when
 // one bucket holds every key, else 0.
-det_status hist_offsets(uint32_t* hist, int64_t nrows, int nb, uint32_t* csum, uint32_t* tot,
-                        uint32_t* valid, uint32_t* ident, hipStream_t s) {
+det_status hist_offsets(const uint16_t* hist, uint32_t* off, int64_t nrows, int nb,
+                        uint32_t* csum, uint32_t* tot, uint32_t* valid, uint32_t* ident,
+                        hipStream_t s) {
     KernelTimer kt("k_hist_offsets", s);
     if (nrows <= kSmallHistRows) {
-        k_hist_offsets_small<<<1, 256, 0, s>>>(hist, nrows, nb, valid, ident);
+        k_hist_offsets_small<<<1, 256, 0, s>>>(hist, off, nrows, nb, valid, ident);
         return launch_status();
     }
     const int64_t nrb = cdiv(nrows, kRowBlk);
     k_hist_colsums<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum);
     k_hist_colscan<<<dim3((unsigned)nb), dim3(256), 0, s>>>(csum, nrb, tot);
-    k_hist_apply<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum, tot, ident,
-                                                          valid);
+    k_hist_apply<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, off, nrows, nb, nrb, csum, tot,
+                                                          ident, valid);
     return launch_status();
 }
 
@@ -330,7 +335,7 @@ template <bool FIRST, typename KI, int WPC>
 __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys, int64_t n,
                                                     const uint32_t* __restrict__ nvalid, uint32_t B,
                                                     int shift, int nb, int64_t nchunks, int H,
-                                                    uint32_t* __restrict__ hist) {
+                                                    uint16_t* __restrict__ hist) {
     static_assert(WPC == 1 || WPC == 4, "one wave or the whole workgroup per chunk");
     __shared__ uint32_t cnt[4][kBuckets0];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -405,11 +410,11 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int d = lane; d < nb; d += 64) hist[c * nb + d] = wc[d];
+        for (int d = lane; d < nb; d += 64) hist[c * nb + d] = (uint16_t)wc[d];
     } else {
         __syncthreads();
         for (int d = threadIdx.x; d < nb; d += 256)
-            hist[c * nb + d] = (cnt[0][d] + cnt[1][d]) + (cnt[2][d] + cnt[3][d]);
+            hist[c * nb + d] = (uint16_t)((cnt[0][d] + cnt[1][d]) + (cnt[2][d] + cnt[3][d]));
     }
 }
 
@@ -417,7 +422,7 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
 // that way (four per compute unit), else with a workgroup per chunk.
 template <bool FIRST, typename KI>
 void radix_hist(const KI* keys, int64_t n, const uint32_t* nvalid, uint32_t B, int shift, int nb,
-                int64_t nchunks, int H, uint32_t* hist, size_t lds, hipStream_t s) {
+                int64_t nchunks, int H, uint16_t* hist, size_t lds, hipStream_t s) {
     KernelTimer kt("k_radix_hist", s);
     if (nchunks >= 4 * (int64_t)cu_count())
         k_radix_hist<FIRST, KI, 1><<<dim3((unsigned)cdiv(nchunks, 4)), dim3(256), lds, s>>>(
@@ -740,31 +745,66 @@ __global__ __launch_bounds__(256) void k_bin_offsets_bytes(
 // where the low parts of p and above start in the second pass's output, which the third pass
 // sorted by the third byte; with c the chunk holding position off2[p], off[b] = ex3[c][t] + the
 // keys of third byte t in [c H, off2[p]), counted from the second pass's key bytes; when
-// off2[p] = m, off[b] = the start of the third pass's bucket t + 1.  A workgroup per p, a thread
-// per t.
+// off2[p] = m, off[b] = the start of the third pass's bucket t + 1.  A wave per p (f64 2^29
+// into 2^20 Zipf bins on MI355X, the whole offsets step: 0.24 ms with a workgroup per p counting
+// from the chunk start, 0.11 ms now), a lane per four t.
 __global__ __launch_bounds__(256) void k_bin_offsets_third(
     const uint32_t* __restrict__ off2, const uint32_t* __restrict__ ex3,
     const uint8_t* __restrict__ tb, const uint32_t* __restrict__ nvalid, int64_t B, int64_t n,
     int64_t H, uint32_t* __restrict__ off, int64_t* __restrict__ n_skipped) {
-    __shared__ uint32_t cnt[256];
-    const int64_t p = blockIdx.x;
-    const int t = threadIdx.x;
+    // a wave per low part p (four per workgroup), its own counters; lane l reads the key bytes
+    // four to a word (H is a multiple of 4, the bytes 256-byte aligned)
+    __shared__ uint32_t cnt[4][256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t p = (int64_t)blockIdx.x * 4 + wave;
+    if (p >= 65536) return;   // a whole wave; nothing below waits for other waves
+    uint32_t* const wc = cnt[wave];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) wc[lane + 64 * k] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int64_t m = *nvalid;
     const int64_t pos = off2[p];
-    cnt[t] = 0u;
-    __syncthreads();
     const int64_t c = pos / H;
-    if (pos < m)
-        for (int64_t q = c * H + t; q < pos; q += 256) count_digit(cnt, (int)tb[q]);
-    __syncthreads();
-    const int64_t b = (int64_t)t * 65536 + p;
-    if (b < B) {
-        uint32_t o;
-        if (pos < m) o = ex3[c * 256 + t] + cnt[t];
-        else o = t < 255 ? ex3[t + 1] : (uint32_t)m;   // row 0 of ex3: the bucket starts
-        off[b] = o;
+    const int64_t cend = (c + 1) * H < m ? (c + 1) * H : m;   // end of chunk c's keys
+    // count the bytes of chunk c before pos, or, when fewer, those from pos to its end and
+    // take them from where the chunk's digit t ends (the next chunk's offset, or for the last
+    // chunk the end of bucket t)
+    const bool after = cend - pos < pos - c * H;
+    if (pos < m) {
+        const int64_t q0 = after ? pos : c * H, q1 = after ? cend : pos;
+        // words from the one holding q0 (H is a multiple of 4, the bytes 256-byte aligned)
+        const uint32_t* tw = reinterpret_cast<const uint32_t*>(tb) + q0 / 4;
+        const int64_t w0 = q0 & ~int64_t(3);
+        for (int64_t w = lane; w0 + 4 * w < q1; w += 64) {
+            const uint32_t x = tw[w];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t q = w0 + 4 * w + j;
+                if (q >= q0 && q < q1) count_digit(wc, (int)((x >> (8 * j)) & 255u));
+            }
+        }
     }
-    if (p == 0 && t == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t nch = (n + H - 1) / H;   // rows of ex3
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int t = lane + 64 * k;
+        const int64_t b = (int64_t)t * 65536 + p;
+        if (b < B) {
+            // row 0 of ex3 holds the bucket starts; bucket t ends where t + 1 starts
+            const uint32_t bend = t < 255 ? ex3[t + 1] : (uint32_t)m;
+            uint32_t o;
+            if (pos >= m) o = bend;
+            else if (!after) o = ex3[c * 256 + t] + wc[t];
+            else o = (c + 1 < nch ? ex3[(c + 1) * 256 + t] : bend) - wc[t];
+            off[b] = o;
+        }
+    }
+    if (p == 0 && lane == 0) {
         off[B] = (uint32_t)m;
         if (n_skipped) *n_skipped = n - m;
     }
@@ -1418,8 +1458,8 @@ struct SLayout {
     int64_t H, nchunks, nhist, nsums, nrange;
     int bytes;    // byte paths for scalar destinations: 2 passes for (256, 65536], 3 passes
                   // for (65536, 2^24]; 0 otherwise
-    size_t keysA, keysB, payA, payB, hist, hist2, hist3, off2, sums, ctrl, off, rbin, pF, pC,
-        total;
+    size_t keysA, keysB, payA, payB, cnt, hist, hist2, hist3, off2, sums, ctrl, off, rbin, pF,
+        pC, total;
 };
 
 // idx_payload: the sort carries source indices (4 bytes) even for scalar destinations
@@ -1447,7 +1487,8 @@ SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt,
     L.keysB = take((size_t)n * 4);
     L.payA = take((size_t)n * pw);
     L.payB = take((size_t)n * pw);
-    L.hist = take((size_t)L.nhist * 4);
+    L.cnt = take((size_t)L.nhist * 2);    // a pass's per-chunk digit counts (16-bit)
+    L.hist = take((size_t)L.nhist * 4);   // its bucket offsets
     L.sums = take((size_t)L.nsums * 4);
     L.off = take((size_t)(num_out + 1) * 4);
     const int kp = key_passes(num_out);
@@ -1474,6 +1515,7 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
     uint32_t* keys[2] = {reinterpret_cast<uint32_t*>(ws + L.keysA),
                          reinterpret_cast<uint32_t*>(ws + L.keysB)};
     P* pay[2] = {reinterpret_cast<P*>(ws + L.payA), reinterpret_cast<P*>(ws + L.payB)};
+    uint16_t* cnt = reinterpret_cast<uint16_t*>(ws + L.cnt);
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
     uint32_t* sums = reinterpret_cast<uint32_t*>(ws + L.sums);
     const uint32_t B = (uint32_t)num_out;
@@ -1491,15 +1533,15 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
         const P* pin = first ? pay_in0 : pay[(p - 1) & 1];
         const int nb = first ? kBuckets0 : 256;
         if (first)
-            radix_hist<true>(kin, n, ctrl, B, shift, nb, L.nchunks, (int)L.H, hist, lds, s);
+            radix_hist<true>(kin, n, ctrl, B, shift, nb, L.nchunks, (int)L.H, cnt, lds, s);
         else if (k16)
-            radix_hist<false>(kin16, n, ctrl, B, shift, nb, L.nchunks, (int)L.H, hist, lds, s);
+            radix_hist<false>(kin16, n, ctrl, B, shift, nb, L.nchunks, (int)L.H, cnt, lds, s);
         else
-            radix_hist<false>(kin, n, ctrl, B, shift, nb, L.nchunks, (int)L.H, hist, lds, s);
+            radix_hist<false>(kin, n, ctrl, B, shift, nb, L.nchunks, (int)L.H, cnt, lds, s);
         // bucket offsets; the first pass also counts the keys in range into ctrl[0]
         uint32_t* ident = ctrl + 16 + p;   // one word per pass (at most 4 passes)
-        det_status st = hist_offsets(hist, L.nchunks, nb, sums + 512, sums, first ? ctrl : nullptr,
-                                     ident, s);
+        det_status st = hist_offsets(cnt, hist, L.nchunks, nb, sums + 512, sums,
+                                     first ? ctrl : nullptr, ident, s);
         if (st != DET_SUCCESS) return st;
         KernelTimer kt("k_radix_scatter", s);
         uint32_t* ko = keys[p & 1];
@@ -1537,6 +1579,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
                               const P** SP) {
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
     P* pay[2] = {reinterpret_cast<P*>(ws + L.payA), reinterpret_cast<P*>(ws + L.payB)};
+    uint16_t* cnt = reinterpret_cast<uint16_t*>(ws + L.cnt);
     uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
     uint32_t* hist2 = reinterpret_cast<uint32_t*>(ws + L.hist2);
     uint32_t* hist3 = reinterpret_cast<uint32_t*>(ws + L.hist3);
@@ -1546,11 +1589,13 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
     const unsigned grid = (unsigned)L.nchunks;
     const size_t lds = (size_t)launch_override().extra_lds;
     const int nc = (int)L.H;
+    // each pass counts into cnt, and its offsets go to h
     auto hist_of = [&](uint32_t* h, int nb, uint32_t* ident, bool first) {
-        return hist_offsets(h, L.nchunks, nb, sums + 512, sums, first ? ctrl : nullptr, ident, s);
+        return hist_offsets(cnt, h, L.nchunks, nb, sums + 512, sums, first ? ctrl : nullptr, ident,
+                            s);
     };
     // pass 1: the low byte (and the out-of-range bucket)
-    radix_hist<true>(kin, n, ctrl, B, 0, kBuckets0, L.nchunks, nc, hist, lds, s);
+    radix_hist<true>(kin, n, ctrl, B, 0, kBuckets0, L.nchunks, nc, cnt, lds, s);
     det_status st = hist_of(hist, kBuckets0, ctrl + 16, true);
     if (st != DET_SUCCESS) return st;
     if (L.bytes == 2) {
@@ -1562,7 +1607,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
                 hist, ctrl + 16);
         }
         if ((st = launch_status()) != DET_SUCCESS) return st;
-        radix_hist<false>(kb, n, ctrl, B, 0, 256, L.nchunks, nc, hist2, lds, s);
+        radix_hist<false>(kb, n, ctrl, B, 0, 256, L.nchunks, nc, cnt, lds, s);
         if ((st = hist_of(hist2, 256, ctrl + 17, false)) != DET_SUCCESS) return st;
         {
             KernelTimer kt("k_radix_scatter", s);
@@ -1584,7 +1629,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
     }
     if ((st = launch_status()) != DET_SUCCESS) return st;
     // pass 2: the second byte, the low byte of the 16-bit keys
-    radix_hist<false>(k16, n, ctrl, B, 0, 256, L.nchunks, nc, hist2, lds, s);
+    radix_hist<false>(k16, n, ctrl, B, 0, 256, L.nchunks, nc, cnt, lds, s);
     if ((st = hist_of(hist2, 256, ctrl + 17, false)) != DET_SUCCESS) return st;
     {
         KernelTimer kt("k_radix_scatter", s);
@@ -1594,7 +1639,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
     }
     if ((st = launch_status()) != DET_SUCCESS) return st;
     // pass 3: the third byte
-    radix_hist<false>(kb, n, ctrl, B, 0, 256, L.nchunks, nc, hist3, lds, s);
+    radix_hist<false>(kb, n, ctrl, B, 0, 256, L.nchunks, nc, cnt, lds, s);
     if ((st = hist_of(hist3, 256, ctrl + 18, false)) != DET_SUCCESS) return st;
     {
         KernelTimer kt("k_radix_scatter", s);
@@ -1652,7 +1697,7 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
                     k_bin_offsets_bytes<uint16_t><<<256, 256, 0, s>>>(
                         h1, h2, reinterpret_cast<const uint16_t*>(ws + L.keysA), ctrl, 65536, n,
                         L.H, off2, nullptr);
-                    k_bin_offsets_third<<<65536, 256, 0, s>>>(
+                    k_bin_offsets_third<<<65536 / 4, 256, 0, s>>>(
                         off2, reinterpret_cast<const uint32_t*>(ws + L.hist3),
                         reinterpret_cast<const uint8_t*>(ws + L.keysB), ctrl, num_out, n, L.H,
                         off, n_skipped);

@@ -43,7 +43,11 @@ def rounding(shape, dtype, seed):
                                  (100003, 1000), (300007, 65536), (300007, 65537),
                                  (1 << 20, 1 << 20), (200000, 3), (2000003, 131073),
                                  (500009, (1 << 24) - 1), (500009, 1 << 24),
-                                 (300007, (1 << 24) + 1)])
+                                 (300007, (1 << 24) + 1),
+                                 # three passes with a short last chunk (f64: 4096 keys per
+                                 # chunk, f32: 8192): destination offsets counted from either
+                                 # end of a chunk, and from the end of a bucket
+                                 (3 * 4096 + 100, 70001), (2 * 8192 + 50, 200003)])
 def test_scalar_parity(dev, dtype, n, B):
     rng = np.random.default_rng(n + B)
     v = rounding(n, dtype, n)
