@@ -62,11 +62,15 @@ __device__ __forceinline__ void put_key(KO* keys_out, int64_t g, uint32_t kk) {
     }
 }
 
-// keys per thread of a radix chunk: 8192 keys for 4-byte payloads, 4096 for 8-byte ones.
-// Long chunks give long runs per bucket (32 keys on average for 256 buckets), so the
-// scattered writes leave mostly whole lines.
+// Keys of a radix chunk (one workgroup's share of a pass): 8192 for 4-byte payloads, 4096 for
+// 8-byte ones.  Long chunks give long runs per bucket (32 keys on average for 256 buckets), so
+// the scattered writes leave mostly whole lines.  Inputs of at most kSmallN keys take chunks of
+// 1024, so a pass has more workgroups than a handful (f32 into 65,536 bins on MI355X: 2^16
+// values 128 -> 115 us, 2^18 99 -> 81 us, 2^20 96 -> 82 us per call).
 template <typename P>
-constexpr int kItems = sizeof(P) == 4 ? 32 : 16;
+constexpr int kChunkBig = sizeof(P) == 4 ? 8192 : 4096;
+constexpr int kChunkSmall = 1024;
+constexpr int64_t kSmallN = int64_t(1) << 20;
 // Waves per radix-scatter workgroup: for 4-byte payloads 8 waves of 16 items need about 112
 // VGPRs, so a CU holds two such workgroups (16 waves) where 4 waves of 32 items needed about
 // 190 and held 8 waves (f32 2^28 into 65,536 bins on MI355X: 0.80 -> 0.74 ms per pass, same
@@ -76,8 +80,8 @@ template <typename P>
 constexpr int kRadixNW = sizeof(P) == 4 ? 8 : 4;
 template <typename P>
 constexpr int kRadixNT = 64 * kRadixNW<P>;
-template <typename P>
-constexpr int kRadixIPT = 256 * kItems<P> / kRadixNT<P>;   // items per thread
+template <typename P, int CH>
+constexpr int kRadixIPT = CH / kRadixNT<P>;   // items per thread for chunks of CH keys
 
 // Workgroup b runs on XCD b mod 8 (round-robin dispatch); give each XCD a contiguous range of
 // chunks, so the writes of consecutive chunks into a bucket's region meet in one L2 and leave
@@ -156,23 +160,27 @@ __device__ __forceinline__ void count_digit(uint32_t* cnt, int d) {
 // bits: a chunk holds at most 8192 keys), so each chunk's counts are written contiguously.  The
 // scatter needs, for chunk c and digit d, off[c][d] = (keys with a digit below d) + (keys with
 // digit d in chunks before c): an exclusive scan in digit-major order, done in three launches
-// over blocks of kRowBlk rows: column sums per row block (stored column-major), an exclusive
+// over blocks of rb rows: column sums per row block (stored column-major), an exclusive
 // scan of each column's block sums, then each row block scans the digit totals and writes its
 // 32-bit offsets, off[c * nb + d].  Integers, so exact in any order.  (32-bit counts rewritten
 // in place moved more bytes: f64 2^29 into 2^20 Zipf bins on MI355X, 0.25 -> 0.18 ms for the
 // three passes' offsets.)
+// Row blocks: 128 rows, or 16 when there are at most 4096 rows, so that few rows still make
+// many short workgroups (2^22 f32 values into 65,536 bins, 512 rows, on MI355X: the call 275 ->
+// 138 us; the single-workgroup kernel below walked 512 rows in 103 us per pass).
 constexpr int kRowBlk = 128;
+constexpr int kRowBlkFew = 16;
 constexpr int kRowBatch = 16;   // rows whose loads are in flight together
 
 // csum[d * nrb + rb] = sum over the rows of block rb of column d (thread t: column t, and
 // thread 0 also column 256 when nb = 257)
 __global__ __launch_bounds__(256) void k_hist_colsums(const uint16_t* __restrict__ hist,
-                                                      int64_t nrows, int nb, int64_t nrb,
+                                                      int64_t nrows, int nb, int64_t nrb, int rb,
                                                       uint32_t* __restrict__ csum) {
     const int t = threadIdx.x;
     const bool extra = nb > 256 && t == 0;
-    const int64_t r0 = (int64_t)blockIdx.x * kRowBlk;
-    const int64_t r1 = (r0 + kRowBlk < nrows) ? r0 + kRowBlk : nrows;
+    const int64_t r0 = (int64_t)blockIdx.x * rb;
+    const int64_t r1 = (r0 + rb < nrows) ? r0 + rb : nrows;
     uint32_t s0 = 0, s1 = 0;
     for (int64_t r = r0; r < r1; r += kRowBatch) {
         uint32_t v[kRowBatch], w[kRowBatch];
@@ -215,7 +223,7 @@ __global__ __launch_bounds__(256) void k_hist_colscan(uint32_t* __restrict__ csu
 // keys in range (the base of bucket 256).
 __global__ __launch_bounds__(256) void k_hist_apply(const uint16_t* __restrict__ hist,
                                                     uint32_t* __restrict__ off, int64_t nrows,
-                                                    int nb, int64_t nrb,
+                                                    int nb, int64_t nrb, int rb,
                                                     const uint32_t* __restrict__ csum,
                                                     const uint32_t* __restrict__ tot,
                                                     uint32_t* __restrict__ ident,
@@ -232,8 +240,8 @@ __global__ __launch_bounds__(256) void k_hist_apply(const uint16_t* __restrict__
         *ident = one ? 1u : 0u;
         if (valid) *valid = total;
     }
-    const int64_t r0 = (int64_t)blockIdx.x * kRowBlk;
-    const int64_t r1 = (r0 + kRowBlk < nrows) ? r0 + kRowBlk : nrows;
+    const int64_t r0 = (int64_t)blockIdx.x * rb;
+    const int64_t r1 = (r0 + rb < nrows) ? r0 + rb : nrows;
     uint32_t run0 = base + csum[(int64_t)t * nrb + blockIdx.x];
     uint32_t run1 = extra ? total + csum[(int64_t)256 * nrb + blockIdx.x] : 0u;
     for (int64_t r = r0; r < r1; r += kRowBatch) {
@@ -255,10 +263,11 @@ __global__ __launch_bounds__(256) void k_hist_apply(const uint16_t* __restrict__
     }
 }
 
-// The same offsets for few rows, in one launch of one workgroup: thread d sums column d, an
-// exclusive scan over the digit totals gives each digit's base, thread d writes its column's
-// running offsets.  *valid (if given) receives the base of digit 256 (the keys in range).
-constexpr int64_t kSmallHistRows = 512;
+// The same offsets for at most 16 rows, in one launch of one workgroup: thread d sums column
+// d, an exclusive scan over the digit totals gives each digit's base, thread d writes its
+// column's running offsets.  *valid (if given) receives the base of digit 256 (the keys in
+// range).
+constexpr int64_t kSmallHistRows = 16;
 
 __global__ __launch_bounds__(256) void k_hist_offsets_small(const uint16_t* __restrict__ hist,
                                                             uint32_t* __restrict__ off,
@@ -307,11 +316,12 @@ det_status hist_offsets(const uint16_t* hist, uint32_t* off, int64_t nrows, int 
         k_hist_offsets_small<<<1, 256, 0, s>>>(hist, off, nrows, nb, valid, ident);
         return launch_status();
     }
-    const int64_t nrb = cdiv(nrows, kRowBlk);
-    k_hist_colsums<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, csum);
+    const int rb = nrows <= 4096 ? kRowBlkFew : kRowBlk;
+    const int64_t nrb = cdiv(nrows, rb);
+    k_hist_colsums<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, rb, csum);
     k_hist_colscan<<<dim3((unsigned)nb), dim3(256), 0, s>>>(csum, nrb, tot);
-    k_hist_apply<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, off, nrows, nb, nrb, csum, tot,
-                                                          ident, valid);
+    k_hist_apply<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, off, nrows, nb, nrb, rb, csum,
+                                                          tot, ident, valid);
     return launch_status();
 }
 
@@ -435,12 +445,12 @@ void radix_hist(const KI* keys, int64_t n, const uint32_t* nvalid, uint32_t B, i
 // P: payload word (uint32_t: f32 value bits or source row; uint64_t: f64 value bits)
 // The staged chunk: for 4-byte payloads key and payload share one 64-bit word (kp), so each
 // item's scattered LDS write is one instruction; 8-byte payloads keep two arrays.
-template <typename P>
+template <typename P, int CH>
 struct RadixSmem {
     static constexpr bool kPacked = sizeof(P) == 4;
-    uint64_t kp[kPacked ? 256 * kItems<P> : 1];
-    uint32_t keys[kPacked ? 1 : 256 * kItems<P>];
-    P pay[kPacked ? 1 : 256 * kItems<P>];
+    uint64_t kp[kPacked ? CH : 1];
+    uint32_t keys[kPacked ? 1 : CH];
+    P pay[kPacked ? 1 : CH];
     // per-wave digit counters; then each wave's first position per digit in the staged chunk
     uint32_t cnt[kRadixNW<P>][kBuckets0];
     // global index of staged position 0 for each digit, modulo 2^32 (every index is below 2^31)
@@ -451,12 +461,12 @@ struct RadixSmem {
 // A chunk's keys and payloads, loaded by thread (wave w, lane l) at positions
 // base + w * 64 * IPT + k * 64 + l.  FULL: the whole chunk is in range (no checks, so every
 // path issues the same loads).
-template <typename P, bool FIRST, bool ROWS, bool FULL, typename KI>
+template <typename P, int CH, bool FIRST, bool ROWS, bool FULL, typename KI>
 __device__ __forceinline__ void radix_load(const KI* __restrict__ keys_in,
                                            const P* __restrict__ pay_in, int64_t base, int64_t m,
-                                           uint32_t (&key)[kRadixIPT<P>], P (&pay)[kRadixIPT<P>],
-                                           int wave, int lane) {
-    constexpr int IPT = kRadixIPT<P>;
+                                           uint32_t (&key)[kRadixIPT<P, CH>],
+                                           P (&pay)[kRadixIPT<P, CH>], int wave, int lane) {
+    constexpr int IPT = kRadixIPT<P, CH>;
     const int64_t p0 = base + (int64_t)wave * 64 * IPT + lane;
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
@@ -482,15 +492,17 @@ __device__ __forceinline__ void radix_load(const KI* __restrict__ keys_in,
 // every lane reads its digit's counter, then the lowest peer writes it advanced by the peers.
 // Integers only, so exact.  Leaves every barrier it passes balanced; ends with the LDS counters
 // cleared for the next chunk.
-template <typename P, bool FIRST, bool ROWS, bool FULL, typename KO>
-__device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_t (&key)[kRadixIPT<P>],
-                                                 const P (&pay)[kRadixIPT<P>], int64_t base, int64_t m,
+template <typename P, int CH, bool FIRST, bool ROWS, bool FULL, typename KO>
+__device__ __forceinline__ void radix_rank_write(RadixSmem<P, CH>& sm,
+                                                 const uint32_t (&key)[kRadixIPT<P, CH>],
+                                                 const P (&pay)[kRadixIPT<P, CH>], int64_t base,
+                                                 int64_t m,
                                                  uint32_t B, int shift, uint32_t off0,
                                                  uint32_t off1, KO* __restrict__ keys_out,
                                                  P* __restrict__ pay_out, int tid, int lane,
                                                  int wave) {
-    constexpr int IPT = kRadixIPT<P>;
-    constexpr int H = 256 * kItems<P>;
+    constexpr int IPT = kRadixIPT<P, CH>;
+    constexpr int H = CH;
     constexpr int NT = kRadixNT<P>;
     constexpr int NW = kRadixNW<P>;
     constexpr int BITS = FIRST ? 9 : 8;
@@ -568,7 +580,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
         if (FULL || p0 + k * 64 < m) {
             const int d = digit_of<FIRST>(key[k], B, shift);
             const uint32_t lp = sm.cnt[wave][d] + rk[k];
-            if constexpr (RadixSmem<P>::kPacked) {
+            if constexpr (RadixSmem<P, CH>::kPacked) {
                 sm.kp[lp] = (uint64_t)key[k] | ((uint64_t)pay[k] << 32);
             } else {
                 sm.keys[lp] = key[k];
@@ -583,7 +595,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
     auto emit = [&](int i) {
         uint32_t kk;
         P pp;
-        if constexpr (RadixSmem<P>::kPacked) {
+        if constexpr (RadixSmem<P, CH>::kPacked) {
             const uint64_t v = sm.kp[i];
             kk = (uint32_t)v;
             pp = (P)(v >> 32);
@@ -611,16 +623,16 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P>& sm, const uint32_
 // writes into each bucket's region merge in its L2.
 // KO: the type keys are written in, KI the type they are read in (uint16_t for passes after
 // the first when every valid key fits 16 bits).
-template <typename P, bool FIRST, bool ROWS, typename KO, typename KI>
+template <typename P, int CH, bool FIRST, bool ROWS, typename KO, typename KI>
 __global__ __launch_bounds__(kRadixNT<P>) void k_radix_scatter(
     const KI* __restrict__ keys_in, const P* __restrict__ pay_in,
     KO* __restrict__ keys_out, P* __restrict__ pay_out, int64_t n,
     const uint32_t* __restrict__ nvalid, uint32_t B, int shift, int64_t nchunks,
     const uint32_t* __restrict__ hist_ex, const uint32_t* __restrict__ ident) {
-    constexpr int IPT = kRadixIPT<P>;
-    constexpr int H = 256 * kItems<P>;
+    constexpr int IPT = kRadixIPT<P, CH>;
+    constexpr int H = CH;
     constexpr int NB = FIRST ? kBuckets0 : 256;
-    __shared__ RadixSmem<P> sm;
+    __shared__ RadixSmem<P, CH> sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t m = FIRST ? n : (int64_t)*nvalid;
     const int64_t c = xcd_chunk(blockIdx.x, nchunks);
@@ -630,7 +642,7 @@ __global__ __launch_bounds__(kRadixNT<P>) void k_radix_scatter(
         // one bucket holds every key: the stable pass leaves every item where it is
         uint32_t key[IPT];
         P pay[IPT];
-        radix_load<P, FIRST, ROWS, false, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
+        radix_load<P, CH, FIRST, ROWS, false, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
         const int64_t p0 = base + (int64_t)wave * 64 * IPT + lane;
 #pragma unroll
         for (int k = 0; k < IPT; ++k) {
@@ -649,16 +661,30 @@ __global__ __launch_bounds__(kRadixNT<P>) void k_radix_scatter(
     uint32_t key[IPT];
     P pay[IPT];
     if (base + H <= m) {
-        radix_load<P, FIRST, ROWS, true, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
+        radix_load<P, CH, FIRST, ROWS, true, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
         __syncthreads();
-        radix_rank_write<P, FIRST, ROWS, true, KO>(sm, key, pay, base, m, B, shift, off0, off1,
+        radix_rank_write<P, CH, FIRST, ROWS, true, KO>(sm, key, pay, base, m, B, shift, off0, off1,
                                                keys_out, pay_out, tid, lane, wave);
     } else {
-        radix_load<P, FIRST, ROWS, false, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
+        radix_load<P, CH, FIRST, ROWS, false, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
         __syncthreads();
-        radix_rank_write<P, FIRST, ROWS, false, KO>(sm, key, pay, base, m, B, shift, off0, off1,
+        radix_rank_write<P, CH, FIRST, ROWS, false, KO>(sm, key, pay, base, m, B, shift, off0, off1,
                                                 keys_out, pay_out, tid, lane, wave);
     }
+}
+
+// One radix pass over chunks of H keys (kChunkSmall or kChunkBig<P>, as the layout chose).
+template <typename P, bool FIRST, bool ROWS, typename KO, typename KI>
+void radix_scatter(int64_t H, unsigned grid, size_t lds, hipStream_t s, const KI* keys_in,
+                   const P* pay_in, KO* keys_out, P* pay_out, int64_t n, const uint32_t* nvalid,
+                   uint32_t B, int shift, int64_t nchunks, const uint32_t* hist_ex,
+                   const uint32_t* ident) {
+    if (H == kChunkSmall)
+        k_radix_scatter<P, kChunkSmall, FIRST, ROWS, KO, KI><<<grid, kRadixNT<P>, lds, s>>>(
+            keys_in, pay_in, keys_out, pay_out, n, nvalid, B, shift, nchunks, hist_ex, ident);
+    else
+        k_radix_scatter<P, kChunkBig<P>, FIRST, ROWS, KO, KI><<<grid, kRadixNT<P>, lds, s>>>(
+            keys_in, pay_in, keys_out, pay_out, n, nvalid, B, shift, nchunks, hist_ex, ident);
 }
 
 // ---------------------------------------------------------------- destinations
@@ -1468,10 +1494,12 @@ SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt,
     SLayout L;
     const bool rows = row_len > 1;
     const size_t pw = (rows || idx_payload) ? 4 : dtype_size(dt);    // payload bytes
-    L.H = 256 * (pw == 4 ? kItems<uint32_t> : kItems<uint64_t>);
+    L.H = n <= kSmallN ? kChunkSmall : (pw == 4 ? kChunkBig<uint32_t> : kChunkBig<uint64_t>);
     L.nchunks = cdiv(n > 0 ? n : 1, L.H);
     L.nhist = (int64_t)kBuckets0 * L.nchunks;
-    L.nsums = (int64_t)kBuckets0 * cdiv(L.nchunks, kRowBlk) + 512;   // column sums + totals
+    // column sums (row blocks of 16 up to 4096 rows, else 128) + totals
+    L.nsums = (int64_t)kBuckets0 * cdiv(L.nchunks, L.nchunks <= 4096 ? kRowBlkFew : kRowBlk) +
+              512;
     const int64_t D = rows ? kRowD : kSegD;
     L.nrange = cdiv(n > 0 ? n : 1, D);
     const size_t es = dtype_size(dt);
@@ -1547,16 +1575,16 @@ det_status sort_by_dest(const int32_t* index, const P* pay_in0, int64_t n, int64
         uint32_t* ko = keys[p & 1];
         uint16_t* ko16 = reinterpret_cast<uint16_t*>(ko);
         if (first && k16)
-            k_radix_scatter<P, true, ROWS, uint16_t, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
+            radix_scatter<P, true, ROWS, uint16_t, uint32_t>(L.H, grid, lds, s,
                 kin, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         else if (first)
-            k_radix_scatter<P, true, ROWS, uint32_t, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
+            radix_scatter<P, true, ROWS, uint32_t, uint32_t>(L.H, grid, lds, s,
                 kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         else if (k16)
-            k_radix_scatter<P, false, ROWS, uint16_t, uint16_t><<<grid, kRadixNT<P>, lds, s>>>(
+            radix_scatter<P, false, ROWS, uint16_t, uint16_t>(L.H, grid, lds, s,
                 kin16, pin, ko16, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         else
-            k_radix_scatter<P, false, ROWS, uint32_t, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
+            radix_scatter<P, false, ROWS, uint32_t, uint32_t>(L.H, grid, lds, s,
                 kin, pin, ko, pay[p & 1], n, ctrl, B, shift, L.nchunks, hist, ident);
         st = launch_status();
         if (st != DET_SUCCESS) return st;
@@ -1602,7 +1630,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
         uint8_t* kb = reinterpret_cast<uint8_t*>(ws + L.keysA);
         {
             KernelTimer kt("k_radix_scatter", s);
-            k_radix_scatter<P, true, false, KeyHi8, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
+            radix_scatter<P, true, false, KeyHi8, uint32_t>(L.H, grid, lds, s,
                 kin, pay_in0, reinterpret_cast<KeyHi8*>(kb), pay[0], n, ctrl, B, 0, L.nchunks,
                 hist, ctrl + 16);
         }
@@ -1611,7 +1639,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
         if ((st = hist_of(hist2, 256, ctrl + 17, false)) != DET_SUCCESS) return st;
         {
             KernelTimer kt("k_radix_scatter", s);
-            k_radix_scatter<P, false, false, NoKey, uint8_t><<<grid, kRadixNT<P>, lds, s>>>(
+            radix_scatter<P, false, false, NoKey, uint8_t>(L.H, grid, lds, s,
                 kb, pay[0], static_cast<NoKey*>(nullptr), pay[1], n, ctrl, B, 0, L.nchunks,
                 hist2, ctrl + 17);
         }
@@ -1623,7 +1651,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
     uint8_t* kb = reinterpret_cast<uint8_t*>(ws + L.keysB);
     {
         KernelTimer kt("k_radix_scatter", s);
-        k_radix_scatter<P, true, false, KeyHi16, uint32_t><<<grid, kRadixNT<P>, lds, s>>>(
+        radix_scatter<P, true, false, KeyHi16, uint32_t>(L.H, grid, lds, s,
             kin, pay_in0, reinterpret_cast<KeyHi16*>(k16), pay[0], n, ctrl, B, 0, L.nchunks,
             hist, ctrl + 16);
     }
@@ -1633,7 +1661,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
     if ((st = hist_of(hist2, 256, ctrl + 17, false)) != DET_SUCCESS) return st;
     {
         KernelTimer kt("k_radix_scatter", s);
-        k_radix_scatter<P, false, false, KeyHi8, uint16_t><<<grid, kRadixNT<P>, lds, s>>>(
+        radix_scatter<P, false, false, KeyHi8, uint16_t>(L.H, grid, lds, s,
             k16, pay[0], reinterpret_cast<KeyHi8*>(kb), pay[1], n, ctrl, B, 0, L.nchunks, hist2,
             ctrl + 17);
     }
@@ -1643,7 +1671,7 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
     if ((st = hist_of(hist3, 256, ctrl + 18, false)) != DET_SUCCESS) return st;
     {
         KernelTimer kt("k_radix_scatter", s);
-        k_radix_scatter<P, false, false, NoKey, uint8_t><<<grid, kRadixNT<P>, lds, s>>>(
+        radix_scatter<P, false, false, NoKey, uint8_t>(L.H, grid, lds, s,
             kb, pay[1], static_cast<NoKey*>(nullptr), pay[0], n, ctrl, B, 0, L.nchunks, hist3,
             ctrl + 18);
     }
