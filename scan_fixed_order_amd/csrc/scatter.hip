@@ -1196,17 +1196,26 @@ __global__ __launch_bounds__(256) void k_segred_scalar_long(const uint32_t* __re
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
     const int64_t nw = (int64_t)gridDim.x * 4;
-    // a destination per wave at a time, so neighbouring long destinations (a skewed head) go
-    // to different waves (64 neighbours per wave: f64 2^29 into 2^20 Zipf bins on MI355X,
-    // 0.24 ms for this kernel)
-    for (int64_t b = gw; b < B; b += nw) {
-        const int64_t seg_s = off[b], seg_e = off[b + 1];
-        if (seg_e - seg_s <= kSegD) continue;
-        const int64_t nblk = cdiv(seg_e - seg_s, kSegD);
-        const int64_t r0 = seg_s / kSegD;
-        // block values: pF[r0] for the first block, pC[r0 + k] for block k >= 1
-        const T S = wave_pw_long<T>(pC + r0, nblk, lane, true, pF[r0], s_stk[wave]);
-        if (lane == 0) out[b] = out[b] + S;
+    // lane l of wave w checks destination w + l * nw (+ 64 nw per round), so neighbouring long
+    // destinations (a skewed head) go to different waves; a wave then combines its long ones
+    // one after another (64 neighbours per wave: f64 2^29 into 2^20 Zipf bins on MI355X, 0.24
+    // ms for this kernel; one destination per wave and round: 26 us with no long destination
+    // at 65,536 bins)
+    for (int64_t g = gw; g < B; g += 64 * nw) {
+        const int64_t b = g + (int64_t)lane * nw;
+        const bool lng = b < B && (int64_t)off[b + 1] - (int64_t)off[b] > kSegD;
+        uint64_t mask = __ballot(lng);
+        while (mask) {
+            const int l = __ffsll((long long)mask) - 1;
+            mask &= mask - 1;
+            const int64_t bb = g + (int64_t)l * nw;
+            const int64_t seg_s = off[bb], seg_e = off[bb + 1];
+            const int64_t nblk = cdiv(seg_e - seg_s, kSegD);
+            const int64_t r0 = seg_s / kSegD;
+            // block values: pF[r0] for the first block, pC[r0 + k] for block k >= 1
+            const T S = wave_pw_long<T>(pC + r0, nblk, lane, true, pF[r0], s_stk[wave]);
+            if (lane == 0) out[bb] = out[bb] + S;
+        }
     }
 }
 
