@@ -138,7 +138,8 @@ __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* s4
 // add theirs as one addition by the lowest of them: skewed digits (a contended destination, a
 // heavy Zipf head, the few values of a key's top bits) otherwise put most lanes of one atomic
 // on one counter.  Other rows, the usual case for uniform keys, take one atomic per lane.
-__device__ __forceinline__ void count_digit(uint32_t* cnt, int d) {
+// Returns (uniformly) whether the row was aggregated.
+__device__ __forceinline__ bool count_digit(uint32_t* cnt, int d) {
     const int d0 = __builtin_amdgcn_readfirstlane(d);
     const uint64_t m0 = __ballot(d == d0);
     if (__popcll(m0) >= 8) {
@@ -149,9 +150,10 @@ __device__ __forceinline__ void count_digit(uint32_t* cnt, int d) {
         } else {
             atomicAdd(&cnt[d], 1u);
         }
-    } else {
-        atomicAdd(&cnt[d], 1u);
+        return true;
     }
+    atomicAdd(&cnt[d], 1u);
+    return false;
 }
 
 // ---------------------------------------------------------------- histogram offsets
@@ -367,6 +369,7 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
     constexpr int NK = sizeof(KI) < 4 ? 32 : 16;
     constexpr int KPW = 4 / (int)sizeof(KI);      // keys per 32-bit word
     constexpr int PER = TS * NK;                  // keys per batch of the team
+    bool skew = true;                             // uniform over the wave
     for (int i0 = 0; i0 < H; i0 += PER) {
         uint32_t kk[NK];
         // thread tt takes keys i0 + k * TS + tt (4-byte keys) or the KPW keys of word
@@ -404,9 +407,25 @@ __global__ __launch_bounds__(256) void k_radix_hist(const KI* __restrict__ keys,
             for (int k = 0; k < NK; ++k) same = same && digit_of<FIRST>(kk[k], B, shift) == dref;
             if (__builtin_amdgcn_ballot_w64(!same) == 0ull) {
                 if (lane == 0) atomicAdd(&wc[dref], (uint32_t)(64 * NK));
-            } else {
+            } else if (sizeof(KI) == 4 || skew ||
+                       __popcll(__builtin_amdgcn_ballot_w64(digit_of<FIRST>(kk[0], B, shift) ==
+                                                            dref)) >= 8) {
+                // skewed (and always for 4-byte keys, whose pass is bound by its reads, where
+                // a moderately skewed low byte made plain atomics slower: f64 2^29 into 2^20
+                // Zipf(1.1) bins): row by row, the lanes on the first active lane's digit as
+                // one addition; the wave stays in this mode while some row of a batch
+                // aggregates
+                bool agg = false;
 #pragma unroll
-                for (int k = 0; k < NK; ++k) count_digit(wc, digit_of<FIRST>(kk[k], B, shift));
+                for (int k = 0; k < NK; ++k)
+                    agg = count_digit(wc, digit_of<FIRST>(kk[k], B, shift)) || agg;
+                skew = agg;
+            } else {
+                // spread digits in 1- or 2-byte keys (no row of the last batch aggregated, nor
+                // this batch's first row): one LDS atomic per key without the per-row test
+                // (f32 2^28 into 65,536 bins on MI355X: the two passes' counts 0.31 -> 0.28 ms)
+#pragma unroll
+                for (int k = 0; k < NK; ++k) atomicAdd(&wc[digit_of<FIRST>(kk[k], B, shift)], 1u);
             }
         } else {
 #pragma unroll
