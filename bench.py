@@ -21,7 +21,9 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                 baselines' outputs), the error against a double-precision reference next to the
                 baselines' errors, and the SHA-256 digest of the output bytes;
   configs       every other configuration of the workload spec (see time_configs);
-  cpu_baseline  the CPU oracle (single thread) on the same workload, timed on the host.
+  cpu_baseline  the CPU oracle (single thread) on the same workload, timed on the host; its
+                `parallel` entry: the OpenMP driver of the same oracle functions on the usable
+                cores, with a check that it gives the single-threaded bits.
 """
 import argparse
 import ctypes
@@ -782,14 +784,15 @@ def main():
         xc = host.get("x_scan")
         vs, bs = host.get("v_sc"), host.get("b_sc")
         reps, dt, cpu_bytes = 0, 0.0, 0.0
+        ref = {}
         while reps < 3 and dt < 10.0:
             t = time.perf_counter()
             if xs is not None:
-                oracle.det_sum(xs)
+                ref["sum"] = oracle.det_sum(xs)
             if xc is not None:
-                oracle.scan(xc)
+                ref["scan"] = oracle.scan(xc)
             if vs is not None:
-                oracle.scatter_add(vs, bs, np.zeros(B, np.float32))
+                ref["scatter"] = oracle.scatter_add(vs, bs, np.zeros(B, np.float32))[0]
             dt += time.perf_counter() - t
             cpu_bytes += step_bytes
             reps += 1
@@ -801,6 +804,30 @@ def main():
                          f"{dt:.1f} s on one of {hi['usable_cores']} usable host cores",
                "host": hi}
         log(f"cpu oracle: {reps} pass(es), {dt:.1f}s")
+        # the same oracle functions over independent units on OpenMP threads (same bits)
+        preps, pdt, pbytes, same = 0, 0.0, 0.0, True
+        while preps < 5 and pdt < 5.0:
+            t = time.perf_counter()
+            got = {}
+            if xs is not None:
+                got["sum"] = oracle.par_det_sum(xs)
+            if xc is not None:
+                got["scan"] = oracle.par_scan(xc)
+            if vs is not None:
+                got["scatter"] = oracle.par_scatter_add(vs, bs, np.zeros(B, np.float32))[0]
+            pdt += time.perf_counter() - t
+            pbytes += step_bytes
+            preps += 1
+            for k, v in got.items():
+                same = same and np.asarray(v).tobytes() == np.asarray(ref[k]).tobytes()
+        cpu["parallel"] = {"value": round(pbytes / pdt / 1e9, 3), "unit": "GB/s",
+                           "cores": oracle.par_threads(), "kind": "oracle, OpenMP driver",
+                           "same_bits_as_single_thread": bool(same),
+                           "sample": f"the same workload run {preps} time(s) with aligned sum "
+                                     f"chunks, destinations and scan tiles on "
+                                     f"{oracle.par_threads()} threads: {pdt:.1f} s"}
+        log(f"cpu oracle, {oracle.par_threads()} threads: {preps} pass(es), {pdt:.1f}s, "
+            f"same bits: {same}")
 
     line = {
         "metric": "GB/s & % HBM peak for bit-reproducible f32 sum/scatter-add/scan at 2^28, 1 GPU",

@@ -29,6 +29,11 @@ Every function here follows the association order stated in ``detref.c``:
 * ``scan``          -- tiles of V*W*NW elements, anchors every A tiles and every A*A2 tiles
                        (drjit-core pull request "Make CUDA floating-point prefix sums
                        deterministic").
+
+``par_det_sum``, ``par_scatter_add`` and ``par_scan`` run the same C functions over
+independent units (aligned sum chunks, destinations, scan tiles) on OpenMP threads
+(``detref_par.c``), for the benchmark's multi-core CPU figure; the tests check that they give
+the single-threaded oracle's bits.
 """
 from __future__ import annotations
 
@@ -42,6 +47,8 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "detref.c")
 _LIB_PATH = os.path.join(_HERE, "libdetref.so")
+_PAR_SRC = os.path.join(_HERE, "detref_par.c")
+_PAR_LIB_PATH = os.path.join(_HERE, "libdetref_par.so")
 
 # Spec constants of the scan: V elements per lane, W lanes per wave, NW waves per tile
 # (tile = V * W * NW = 8192 elements), A tiles per anchor interval, A2 intervals per
@@ -58,21 +65,28 @@ REVERSE = 2
 _CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-std=c99", "-Wall"]
 
 
-def build(force: bool = True) -> str:
-    """Compile detref.c twice (f32, f64) with gcc and link libdetref.so."""
-    if not force and os.path.exists(_LIB_PATH):
-        return _LIB_PATH
+def _build_one(src: str, lib: str, extra) -> None:
     objs = []
+    stem = os.path.splitext(os.path.basename(src))[0]
     for t, suf in (("float", "_f32"), ("double", "_f64")):
-        obj = os.path.join(_HERE, f"detref{suf}.o")
-        subprocess.check_call(["gcc", *_CFLAGS, f"-DDET_T={t}", f"-DDET_SUF={suf}", "-c", _SRC,
-                               "-o", obj])
+        obj = os.path.join(_HERE, f"{stem}{suf}.o")
+        subprocess.check_call(["gcc", *_CFLAGS, *extra, f"-DDET_T={t}", f"-DDET_SUF={suf}", "-c",
+                               src, "-o", obj])
         objs.append(obj)
-    tmp = _LIB_PATH + ".tmp"
-    subprocess.check_call(["gcc", "-shared", "-o", tmp, *objs])
-    os.replace(tmp, _LIB_PATH)
+    tmp = lib + ".tmp"
+    subprocess.check_call(["gcc", "-shared", *extra, "-o", tmp, *objs])
+    os.replace(tmp, lib)
     for o in objs:
         os.remove(o)
+
+
+def build(force: bool = True) -> str:
+    """Compile detref.c twice (f32, f64) with gcc and link libdetref.so; the same for the
+    OpenMP driver detref_par.c (libdetref_par.so)."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.exists(_PAR_LIB_PATH):
+        return _LIB_PATH
+    _build_one(_SRC, _LIB_PATH, [])
+    _build_one(_PAR_SRC, _PAR_LIB_PATH, ["-fopenmp"])
     return _LIB_PATH
 
 
@@ -102,6 +116,31 @@ def _load():
         f.argtypes = [p, p, i64, i64, p, i64, p, i64, i64, i64, i64, i64]
         f.restype = i64
     _lib = lib
+    return lib
+
+
+_par = None
+
+
+def _load_par():
+    global _par
+    if _par is not None:
+        return _par
+    if not os.path.exists(_PAR_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_PAR_LIB_PATH)
+    for suf, ct in (("_f32", ctypes.c_float), ("_f64", ctypes.c_double)):
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        f = getattr(lib, "opar_sum" + suf)
+        f.argtypes, f.restype = [p, i64], ct
+        f = getattr(lib, "opar_scatter_add" + suf)
+        f.argtypes, f.restype = [p, p, i64, i64, p, i64], i64
+        f = getattr(lib, "opar_scan" + suf)
+        f.argtypes = [p, p, i64, ctypes.c_uint, p, i64, i64, i64, i64, i64, i64]
+        f.restype = ctypes.c_int
+        getattr(lib, "opar_threads" + suf).restype = ctypes.c_int
+    _par = lib
     return lib
 
 
@@ -245,4 +284,63 @@ def scan(x: np.ndarray, exclusive: bool = False, reverse: bool = False,
                                              V, W, NW, A, A2)
     if rc != 0:
         raise ValueError(f"oracle scan rejected its arguments ({rc})")
+    return y
+
+
+# ---------------------------------------------------------------- the OpenMP driver
+
+
+def par_threads() -> int:
+    """Threads the OpenMP driver uses (OMP_NUM_THREADS, else the usable cores)."""
+    return int(_load_par().opar_threads_f32())
+
+
+def par_det_sum(x: np.ndarray):
+    """``det_sum`` with aligned chunks of 2^20 elements on several threads (same bits)."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    suf = _suffix(x.dtype)
+    return x.dtype.type(getattr(_load_par(), "opar_sum" + suf)(_ptr(x), x.size))
+
+
+def par_scatter_add(values: np.ndarray, index: np.ndarray, out: np.ndarray
+                    ) -> Tuple[np.ndarray, int]:
+    """``scatter_add`` (without prev) with the destinations on several threads (same bits).
+    Returns ``(new_out, n_skipped)``."""
+    values = np.ascontiguousarray(values)
+    index = np.ascontiguousarray(index, dtype=np.int32).reshape(-1)
+    n = index.size
+    row_len = 1 if values.ndim == 1 else int(np.prod(values.shape[1:]))
+    if values.size != n * row_len:
+        raise ValueError("values and index disagree on n")
+    if out.dtype != values.dtype:
+        raise TypeError("values and out must share a dtype")
+    new = np.array(out, dtype=out.dtype, copy=True, order="C")
+    num_out = new.size // row_len
+    suf = _suffix(values.dtype)
+    k = getattr(_load_par(), "opar_scatter_add" + suf)(_ptr(values), _ptr(index), n, row_len,
+                                                        _ptr(new), num_out)
+    if k < 0:
+        raise RuntimeError(f"oracle par_scatter_add failed ({k})")
+    return new, int(k)
+
+
+def par_scan(x: np.ndarray, exclusive: bool = False, reverse: bool = False,
+             offsets: Optional[np.ndarray] = None, V: int = SPEC_V, W: int = SPEC_W,
+             NW: int = SPEC_NW, A: int = SPEC_A, A2: int = SPEC_A2) -> np.ndarray:
+    """``scan`` with the tiles' local parts and combines on several threads (same bits)."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    y = np.empty_like(x)
+    flags = (EXCLUSIVE if exclusive else 0) | (REVERSE if reverse else 0)
+    offs = None
+    nseg = 0
+    if offsets is not None:
+        offs = np.ascontiguousarray(offsets, dtype=np.int64).reshape(-1)
+        nseg = offs.size - 1
+        if nseg < 0:
+            raise ValueError("offsets needs at least one entry")
+    suf = _suffix(x.dtype)
+    rc = getattr(_load_par(), "opar_scan" + suf)(_ptr(x), _ptr(y), x.size, flags, _ptr(offs),
+                                                 nseg, V, W, NW, A, A2)
+    if rc != 0:
+        raise ValueError(f"oracle par_scan rejected its arguments ({rc})")
     return y
