@@ -240,7 +240,10 @@ __global__ __launch_bounds__(256) void k_hist_apply(const uint16_t* __restrict__
     const int one = __syncthreads_or(v == total + v256 || v256 == total + v256);
     if (blockIdx.x == 0 && t == 0) {
         *ident = one ? 1u : 0u;
-        if (valid) *valid = total;
+        if (valid) {
+            valid[0] = total;
+            valid[1] = v256 == 0u ? 1u : 0u;   // no key out of range
+        }
     }
     const int64_t r0 = (int64_t)blockIdx.x * rb;
     const int64_t r1 = (r0 + rb < nrows) ? r0 + rb : nrows;
@@ -304,7 +307,10 @@ __global__ __launch_bounds__(256) void k_hist_offsets_small(const uint16_t* __re
             run1 += w;
         }
     }
-    if (valid && t == 0) *valid = total;
+    if (valid && t == 0) {
+        valid[0] = total;
+        valid[1] = s_c256 == 0u ? 1u : 0u;   // no key out of range
+    }
 }
 
 // csum needs nb * nrb words, tot nb words (nb <= 257).  valid (first pass only): receives the
@@ -511,7 +517,7 @@ __device__ __forceinline__ void radix_load(const KI* __restrict__ keys_in,
 // every lane reads its digit's counter, then the lowest peer writes it advanced by the peers.
 // Integers only, so exact.  Leaves every barrier it passes balanced; ends with the LDS counters
 // cleared for the next chunk.
-template <typename P, int CH, bool FIRST, bool ROWS, bool FULL, typename KO>
+template <typename P, int CH, bool FIRST, bool ROWS, bool FULL, typename KO, bool OOR = FIRST>
 __device__ __forceinline__ void radix_rank_write(RadixSmem<P, CH>& sm,
                                                  const uint32_t (&key)[kRadixIPT<P, CH>],
                                                  const P (&pay)[kRadixIPT<P, CH>], int64_t base,
@@ -524,7 +530,9 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P, CH>& sm,
     constexpr int H = CH;
     constexpr int NT = kRadixNT<P>;
     constexpr int NW = kRadixNW<P>;
-    constexpr int BITS = FIRST ? 9 : 8;
+    // digits up to 256 (the out-of-range bucket) need 9 bits; a first pass whose histogram
+    // found no key out of range (OOR false) ranks the low byte alone
+    constexpr int BITS = OOR ? 9 : 8;
     constexpr int NB = FIRST ? kBuckets0 : 256;
     uint32_t rk[IPT];
     const int64_t p0 = base + (int64_t)wave * 64 * IPT + lane;
@@ -532,7 +540,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P, CH>& sm,
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
         const bool valid = FULL || p0 + k * 64 < m;
-        const int d = valid ? digit_of<FIRST>(key[k], B, shift) : 0;
+        const int d = valid ? digit_of<OOR>(key[k], B, shift) : 0;
         uint32_t plo = FULL ? ~0u : (uint32_t)__ballot(valid);
         uint32_t phi = FULL ? ~0u : (uint32_t)(__ballot(valid) >> 32);
 #pragma unroll
@@ -597,7 +605,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P, CH>& sm,
 #pragma unroll
     for (int k = 0; k < IPT; ++k) {
         if (FULL || p0 + k * 64 < m) {
-            const int d = digit_of<FIRST>(key[k], B, shift);
+            const int d = digit_of<OOR>(key[k], B, shift);
             const uint32_t lp = sm.cnt[wave][d] + rk[k];
             if constexpr (RadixSmem<P, CH>::kPacked) {
                 sm.kp[lp] = (uint64_t)key[k] | ((uint64_t)pay[k] << 32);
@@ -622,7 +630,7 @@ __device__ __forceinline__ void radix_rank_write(RadixSmem<P, CH>& sm,
             kk = sm.keys[i];
             pp = sm.pay[i];
         }
-        const int64_t g = (int64_t)(sm.gbase[digit_of<FIRST>(kk, B, shift)] + (uint32_t)i);
+        const int64_t g = (int64_t)(sm.gbase[digit_of<OOR>(kk, B, shift)] + (uint32_t)i);
         put_key<KO>(keys_out, g, kk);
         pay_out[g] = pp;
     };
@@ -682,8 +690,13 @@ __global__ __launch_bounds__(kRadixNT<P>) void k_radix_scatter(
     if (base + H <= m) {
         radix_load<P, CH, FIRST, ROWS, true, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
         __syncthreads();
-        radix_rank_write<P, CH, FIRST, ROWS, true, KO>(sm, key, pay, base, m, B, shift, off0, off1,
-                                               keys_out, pay_out, tid, lane, wave);
+        if (FIRST && nvalid[1])   // no key out of range: 8-bit ranking
+            radix_rank_write<P, CH, FIRST, ROWS, true, KO, false>(
+                sm, key, pay, base, m, B, shift, off0, off1, keys_out, pay_out, tid, lane, wave);
+        else
+            radix_rank_write<P, CH, FIRST, ROWS, true, KO>(sm, key, pay, base, m, B, shift, off0,
+                                                           off1, keys_out, pay_out, tid, lane,
+                                                           wave);
     } else {
         radix_load<P, CH, FIRST, ROWS, false, KI>(keys_in, pay_in, base, m, key, pay, wave, lane);
         __syncthreads();
