@@ -70,7 +70,13 @@ size_t det_sum_workspace_size(int64_t n, det_dtype dtype);
  * The fixed tree replaces the atomic tail of a block-partials reduction (course page
  * "Floating point and reproducibility", sections "Twenty answers, none of them wrong" and
  * "Fix the order of every addition").  Any aligned power-of-two chunk of x is a subtree of
- * PW, so the kernels may split x into chunks of any power-of-two size without moving a bit. */
+ * PW, so the kernels may split x into chunks of any power-of-two size without moving a bit.
+ * ws: device, at least det_sum_workspace_size(n, dtype) bytes, 256-byte aligned, any initial
+ * contents; the call leaves it holding partial values.  Sums of 2 to 1024 chunks of 2^14
+ * elements (up to 2^24 elements) finish in one launch: the grid's last workgroup waits for
+ * the chunk values tagged for the call, a wait bounded at 2 seconds of the GPU's 100 MHz
+ * clock after which *out receives a NaN instead of the sum (a failure of the GPU's forward
+ * progress, not of the data).  Calls that share a workspace must be ordered on one stream. */
 det_status det_sum(const void* x, int64_t n, det_dtype dtype, void* out, void* ws,
                    size_t ws_bytes, void* stream);
 
