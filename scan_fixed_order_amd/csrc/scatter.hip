@@ -268,26 +268,34 @@ __global__ __launch_bounds__(256) void k_hist_apply(const uint16_t* __restrict__
     }
 }
 
-// The same offsets for at most 16 rows, in one launch of one workgroup: thread d sums column
-// d, an exclusive scan over the digit totals gives each digit's base, thread d writes its
-// column's running offsets.  *valid (if given) receives the base of digit 256 (the keys in
-// range).
-constexpr int64_t kSmallHistRows = 16;
+// The same offsets for at most 64 rows, in one launch of one workgroup: thread d loads column
+// d of every row at once (one round trip), an exclusive scan over the digit totals gives each
+// digit's base, and thread d writes its column's running offsets from the values it holds.
+// *valid (if given) receives the base of digit 256 (the keys in range) and valid[1] whether no
+// key is out of range.  (Walking the rows 8 at a time took 20 us for 64 rows on MI355X.)
+constexpr int64_t kSmallHistRows = 64;
 
 __global__ __launch_bounds__(256) void k_hist_offsets_small(const uint16_t* __restrict__ hist,
                                                             uint32_t* __restrict__ off,
                                                             int64_t nrows, int nb,
                                                             uint32_t* __restrict__ valid,
                                                             uint32_t* __restrict__ ident) {
+    constexpr int R = (int)kSmallHistRows;
     __shared__ uint32_t s4[4];
     __shared__ uint32_t s_c256;
     const int t = threadIdx.x;
     const bool extra = nb > 256 && t == 0;
+    uint32_t v[R], w[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        v[r] = r < nrows ? (uint32_t)hist[(int64_t)r * nb + t] : 0u;
+        w[r] = (extra && r < nrows) ? (uint32_t)hist[(int64_t)r * nb + 256] : 0u;
+    }
     uint32_t c0 = 0, c256 = 0;
-#pragma unroll 8
-    for (int64_t r = 0; r < nrows; ++r) {
-        c0 += hist[r * nb + t];
-        if (extra) c256 += hist[r * nb + 256];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        c0 += v[r];
+        c256 += w[r];
     }
     if (t == 0) s_c256 = c256;
     uint32_t total;
@@ -296,16 +304,14 @@ __global__ __launch_bounds__(256) void k_hist_offsets_small(const uint16_t* __re
     const int one = __syncthreads_or(c0 == grand || s_c256 == grand);
     if (t == 0) *ident = one ? 1u : 0u;
     uint32_t run1 = total;
-#pragma unroll 8
-    for (int64_t r = 0; r < nrows; ++r) {
-        const uint32_t v = hist[r * nb + t];
-        off[r * nb + t] = run0;
-        run0 += v;
-        if (extra) {
-            const uint32_t w = hist[r * nb + 256];
-            off[r * nb + 256] = run1;
-            run1 += w;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        if (r < nrows) {
+            off[(int64_t)r * nb + t] = run0;
+            if (extra) off[(int64_t)r * nb + 256] = run1;
         }
+        run0 += v[r];
+        run1 += w[r];
     }
     if (valid && t == 0) {
         valid[0] = total;
