@@ -1154,6 +1154,8 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const KT* __restrict__ K,
 // k_segred_scalar without keys (the byte path): the destinations meeting this range are
 // rbin[range] (the one holding its first position) and those after it that start before the
 // range's end, found from the offsets; every block and every value as in k_segred_scalar.
+// Workgroup (range, y) of gridDim.y takes every gridDim.y-th group of 256 of them, so a range
+// holding many short destinations is shared out (each destination to one workgroup).
 template <typename T, bool NEG>
 __global__ __launch_bounds__(256) void k_segred_off(const T* __restrict__ V,
                                                     const uint32_t* __restrict__ off, int64_t B,
@@ -1185,7 +1187,7 @@ __global__ __launch_bounds__(256) void k_segred_off(const T* __restrict__ V,
         }
     };
     // destinations b0, b0 + 1, ... while they start before hi (at most kSegD + 1 of them)
-    for (int64_t bb = b0;; bb += 256) {
+    for (int64_t bb = b0 + (int64_t)blockIdx.y * 256;; bb += 256 * (int64_t)gridDim.y) {
         const int64_t b = bb + tid;
         bool more = false;
         if (b < B) {
@@ -1785,7 +1787,11 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
             const T* SV = reinterpret_cast<const T*>(SP);
             {
                 KernelTimer kt("k_segred_scalar", s);
-                const dim3 g((unsigned)L.nrange), b(256);
+                // destinations per range (on average) in groups of 256, one workgroup each, at
+                // most 32 per range
+                int64_t split = cdiv(cdiv(num_out * kSegD, n), 256);
+                if (split > 32) split = 32;
+                const dim3 g((unsigned)L.nrange, (unsigned)split), b(256);
                 if (!neg)
                     k_segred_off<T, false><<<g, b, 0, s>>>(SV, off, num_out, rbin, ctrl, out, pF,
                                                            pC);
