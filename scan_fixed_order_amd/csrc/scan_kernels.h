@@ -928,20 +928,29 @@ __device__ __forceinline__ void finish_tile(const ScanArgs<T>& a, int j, const L
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Tiles are claimed from nc <= kCounters counters (nc <= the grid), one per 256-byte line:
-// workgroup b draws from counter c = b mod nc, whose k-th claim is tile k * nc + c.  One
-// counter would serialise every claim on a single address (about 87 claims per microsecond on
-// this chip, well below the tile rate at full bandwidth).  Each counter's tiles are claimed in
-// order, and workgroups 0 .. nc-1, the first on their counters, are dispatched no later than
-// any other workgroup of their counter, so every counter keeps a running workgroup until its
-// tiles run out and every tile a workgroup waits on is, or will be, claimed by one.  A grid
-// larger than the resident count (a test hook) changes nothing here as long as there are no
-// more counters than resident workgroups (the host sees to it): a workgroup claims tiles only
-// once it runs, and the first of each counter runs until that counter's tiles are gone.  (On
-// MI355X workgroup b goes to XCD b mod 8 and each XCD dispatches its share in order, so with 8
-// counters the first workgroup of each counter is the first on its XCD.)
+// Tiles are claimed from nc <= kCounters counters (nc <= the grid), one per 256-byte line, and
+// counter c's k-th claim is tile k * nc + c.  One counter would serialise every claim on a
+// single address (about 87 claims per microsecond on this chip, below the tile rate of an f32
+// scan at full bandwidth: 2^28 elements 380 -> 440 us, 2^24 28 -> 50 us).  Workgroup b belongs
+// to group g = b mod 8 (on MI355X the XCD it runs on) and takes a rank r in its group as it
+// starts (one rank word per group); it draws from counter (g + r) mod nc while r < nc, else
+// from counter g mod nc.  Each counter's tiles are claimed in order, and a workgroup claims
+// until its counter's tiles run out, so once some group has started nc workgroups every counter
+// has a running workgroup until its tiles are gone, and every tile a workgroup waits on is, or
+// will be, claimed by a running one.  That holds whatever else shares the GPU: with the counter
+// tied to the workgroup index alone (b mod nc) two f64 scans on two streams, each filling the
+// chip, could each hold every slot of an XCD the other needed for the first workgroup of a
+// counter, and both waited until the wait bound gave up.  By rank, while no group of a scan has
+// started nc workgroups the scan holds fewer than nc slots per XCD, and an XCD has 64 or more
+// per scan kernel, so more workgroups start.  (A CPU model of two full-chip scans checks both
+// choices.)  Workgroups after the first nc of a group keep the counter of their XCD, whose
+// claims then stay mostly on one XCD; one rank word for the whole grid cost 7 us at the start
+// of every call (about 768 workgroups on one address).  A grid larger than the resident count
+// (a test hook) changes nothing as long as there are no more counters than resident workgroups
+// (the host sees to it).
 constexpr int kCounters = 8;
 constexpr int kCounterStride = 64;   // words between counters
+constexpr int kRankWord = 32;        // group g's rank word: word 32 of counter g's line
 
 // The last tile of an anchor interval publishes the interval total G_q = PW(all A tile totals)
 // right after its own local step, while its later tiles are still loading: G_q needs nothing but
@@ -1018,6 +1027,7 @@ void k_scan(ScanArgs<T> a) {
     __shared__ Seg<T> s_wtot[kScanWaves];
     __shared__ Seg<T> s_carry;
     __shared__ int s_tick[2];
+    __shared__ int s_ctr;
     __shared__ int s_best[ADAPTIVE ? 4 : 1];
 
     const int tid = threadIdx.x;
@@ -1028,11 +1038,20 @@ void k_scan(ScanArgs<T> a) {
     T* xs = s_x[wave];
     const uint32_t* hbs = s_hbits[SEG ? wave : 0];
     const int nc = a.nctr;
-    const int ctr = (int)(blockIdx.x % (unsigned)nc);
 
-    // ---- prologue: c loaded, local, published, parked; u's loads issued
-    if (tid == 0) s_tick[0] = ticket_tile(claim_issue(a.ticket, ctr), ctr, nc);
+    // ---- prologue: the counter from this workgroup's start rank, then c loaded, local,
+    // published, parked; u's loads issued
+    if (tid == 0) {
+        const int g = (int)(blockIdx.x & 7u);
+        const uint32_t rank = __hip_atomic_fetch_add(a.ticket + g * kCounterStride + kRankWord,
+                                                     1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        const int cr = rank < (uint32_t)nc ? (int)((g + (int)rank) % nc) : g % nc;
+        s_ctr = cr;
+        s_tick[0] = ticket_tile(claim_issue(a.ticket, cr), cr, nc);
+    }
     __syncthreads();
+    const int ctr = __builtin_amdgcn_readfirstlane(s_ctr);
     int c = __builtin_amdgcn_readfirstlane(s_tick[0]);
     if (c >= a.ntiles) return;
     T r[kV];

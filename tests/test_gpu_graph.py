@@ -177,7 +177,9 @@ def test_streams_do_not_change_bits(dev, dtype):
             r2 = run(*w2)
         outs.append((r1, r2))
     torch.cuda.synchronize()
-    for r1, r2 in outs:
-        for got in (r1, r2):
-            for g, w in zip(got, ref):
-                assert bits_equal(g.cpu().numpy().reshape(w.shape), w)
+    for it, (r1, r2) in enumerate(outs):
+        for si, got in enumerate((r1, r2)):
+            for name, g, w in zip(("sum", "scan", "scatter"), got, ref):
+                g = g.cpu().numpy().reshape(w.shape)
+                assert bits_equal(g, w), (name, "round", it, "stream", si + 1,
+                                          first_mismatch(g.reshape(-1), w.reshape(-1)))
