@@ -66,11 +66,13 @@ __device__ __forceinline__ void put_key(KO* keys_out, int64_t g, uint32_t kk) {
 // 8-byte ones.  Long chunks give long runs per bucket (32 keys on average for 256 buckets), so
 // the scattered writes leave mostly whole lines.  Inputs of at most kSmallN keys take chunks of
 // 1024, so a pass has more workgroups than a handful (f32 into 65,536 bins on MI355X: 2^16
-// values 128 -> 115 us, 2^18 99 -> 81 us, 2^20 96 -> 82 us per call).
+// values 128 -> 115 us, 2^18 99 -> 81 us, 2^20 96 -> 82 us, 2^21 111 -> 96 us per call; f32 2^22
+// into 2^20 bins 258 -> 173 us; above 2^22 the long chunks are faster: 2^24 into 65,536 bins
+// 203 against 289 us).
 template <typename P>
 constexpr int kChunkBig = sizeof(P) == 4 ? 8192 : 4096;
 constexpr int kChunkSmall = 1024;
-constexpr int64_t kSmallN = int64_t(1) << 20;
+constexpr int64_t kSmallN = int64_t(1) << 22;
 // Waves per radix-scatter workgroup: for 4-byte payloads 8 waves of 16 items need about 112
 // VGPRs, so a CU holds two such workgroups (16 waves) where 4 waves of 32 items needed about
 // 190 and held 8 waves (f32 2^28 into 65,536 bins on MI355X: 0.80 -> 0.74 ms per pass, same
