@@ -151,10 +151,14 @@ def test_streams_do_not_change_bits(dev, dtype):
 
     def run(ws_sum, ws_scan, ws_sc):
         s = det.det_sum(x, ws=ws_sum)
-        y = det.det_scan(x, exclusive=True, reverse=True, ws=ws_scan)
+        h = torch.full((), -1, dtype=torch.int32, device=dev)   # the scan's health word
+        y = det.det_scan(x, exclusive=True, reverse=True, ws=ws_scan, health=h)
         o = torch.zeros(5000, dtype=tdt, device=dev)
         det.det_scatter_add(x, idx, o, ws=ws_sc)
+        healths.append(h)
         return s, y, o
+
+    healths = []
 
     code = 0 if dtype == np.float32 else 1
 
@@ -177,6 +181,8 @@ def test_streams_do_not_change_bits(dev, dtype):
             r2 = run(*w2)
         outs.append((r1, r2))
     torch.cuda.synchronize()
+    # 0: no look-back wait of any scan hit its time bound
+    assert [int(h.item()) for h in healths] == [0] * len(healths)
     for it, (r1, r2) in enumerate(outs):
         for si, got in enumerate((r1, r2)):
             for name, g, w in zip(("sum", "scan", "scatter"), got, ref):
