@@ -34,6 +34,7 @@
 // destination), and prev written from it and the old values.
 #include "det_device.h"
 #include "det_internal.h"
+#include <type_traits>
 
 namespace det {
 namespace {
@@ -338,6 +339,214 @@ det_status hist_offsets(const uint16_t* hist, uint32_t* off, int64_t nrows, int 
     k_hist_colscan<<<dim3((unsigned)nb), dim3(256), 0, s>>>(csum, nrb, tot);
     k_hist_apply<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, off, nrows, nb, nrb, rb, csum,
                                                           tot, ident, valid);
+    return launch_status();
+}
+
+// ---------------------------------------------------------------- 10-bit digits
+
+// f64 values into more than 65,536 and at most 2^20 destinations (chunks of 4096 keys) sort in
+// two passes of 10-bit digits instead of three of 8: the first on the low 10 bits (bucket 1024
+// for keys out of range), writing the high 10 bits as 16-bit keys, the second on those, writing
+// no key.  The kernels below are the 8-bit ones widened to kWideB buckets (plus one); every
+// count and offset is an integer, so the order of additions changes nothing.
+constexpr int kWideBits = 10;
+constexpr int kWideB = 1 << kWideBits;   // 1024 digits
+constexpr int kWideCols = kWideB + 1;    // and the out-of-range bucket of the first pass
+constexpr int kWideRowBatch = 8;         // rows whose loads are in flight together
+constexpr int kWidePer = (kWideCols + 255) / 256;   // columns per thread (5)
+
+template <bool OOR>
+__device__ __forceinline__ int wide_digit(uint32_t key, uint32_t B, int shift) {
+    if (OOR && key >= B) return kWideB;
+    return (int)((key >> shift) & (uint32_t)(kWideB - 1));
+}
+
+// Per-chunk digit counts (16-bit), a wave per chunk (four per workgroup), as k_radix_hist:
+// a batch whose keys share one digit adds with one atomic, others row by row (count_digit).
+template <bool FIRST, typename KI>
+__global__ __launch_bounds__(256) void k_radix_hist_w(const KI* __restrict__ keys, int64_t n,
+                                                      const uint32_t* __restrict__ nvalid,
+                                                      uint32_t B, int nb, int64_t nchunks, int H,
+                                                      uint16_t* __restrict__ hist) {
+    __shared__ uint32_t cnt[4][kWideCols];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t c = (int64_t)blockIdx.x * 4 + wave;
+    if (c >= nchunks) return;   // a whole wave; it waits for no other wave
+    uint32_t* const wc = cnt[wave];
+    for (int d = lane; d < kWideCols; d += 64) wc[d] = 0u;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int64_t m = FIRST ? n : (int64_t)*nvalid;
+    const int64_t base = c * H;
+    constexpr int NK = 16;
+    constexpr int PER = 64 * NK;
+    constexpr int KPW = 4 / (int)sizeof(KI);   // keys per 32-bit word
+    // position in the chunk of kk[k]: 4-byte keys i0 + k * 64 + lane; 16-bit keys two to a
+    // word, word i0 / 2 + (k / 2) * 64 + lane
+    auto pos = [&](int i0, int k) -> int {
+        return KPW == 1 ? i0 + k * 64 + lane : i0 + KPW * ((k / KPW) * 64 + lane) + k % KPW;
+    };
+    for (int i0 = 0; i0 < H; i0 += PER) {
+        uint32_t kk[NK];
+        if constexpr (KPW == 1) {
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+                const int64_t p = base + i0 + k * 64 + lane;
+                kk[k] = (i0 + k * 64 + lane < H && p < m)
+                            ? (uint32_t)__builtin_nontemporal_load(keys + p) : 0u;
+            }
+        } else {
+            // chunk starts are multiples of 4096 and the keys 256-byte aligned
+            const uint32_t* kw = reinterpret_cast<const uint32_t*>(keys) + base / KPW;
+#pragma unroll
+            for (int k = 0; k < NK / KPW; ++k) {
+                const int w = i0 / KPW + k * 64 + lane;
+                const uint32_t x = (KPW * w < H && base + KPW * w < m)
+                                       ? __builtin_nontemporal_load(kw + w) : 0u;
+#pragma unroll
+                for (int j = 0; j < KPW; ++j)
+                    kk[KPW * k + j] = (x >> (32 / KPW * j)) & (0xffffffffu >> (32 - 32 / KPW));
+            }
+        }
+        const bool full = i0 + PER <= H && base + i0 + PER <= m;   // uniform over the wave
+        if (full) {
+            const int dref = __builtin_amdgcn_readfirstlane(wide_digit<FIRST>(kk[0], B, 0));
+            bool same = true;
+#pragma unroll
+            for (int k = 0; k < NK; ++k) same = same && wide_digit<FIRST>(kk[k], B, 0) == dref;
+            if (__builtin_amdgcn_ballot_w64(!same) == 0ull) {
+                if (lane == 0) atomicAdd(&wc[dref], (uint32_t)PER);
+            } else {
+#pragma unroll
+                for (int k = 0; k < NK; ++k) count_digit(wc, wide_digit<FIRST>(kk[k], B, 0));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NK; ++k) {
+                const int q = pos(i0, k);
+                if (q < H && base + q < m) count_digit(wc, wide_digit<FIRST>(kk[k], B, 0));
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int d = lane; d < nb; d += 64) hist[c * nb + d] = (uint16_t)wc[d];
+}
+
+// csum[d * nrb + rb] = sum over the rows of block rb of column d (thread t: columns t + 256 j)
+__global__ __launch_bounds__(256) void k_hist_colsums_w(const uint16_t* __restrict__ hist,
+                                                        int64_t nrows, int nb, int64_t nrb,
+                                                        int rb, uint32_t* __restrict__ csum) {
+    const int t = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * rb;
+    const int64_t r1 = (r0 + rb < nrows) ? r0 + rb : nrows;
+    uint32_t sum[kWidePer];
+#pragma unroll
+    for (int j = 0; j < kWidePer; ++j) sum[j] = 0u;
+    for (int64_t r = r0; r < r1; r += kWideRowBatch) {
+        uint32_t v[kWideRowBatch][kWidePer];
+#pragma unroll
+        for (int k = 0; k < kWideRowBatch; ++k)
+#pragma unroll
+            for (int j = 0; j < kWidePer; ++j) {
+                const int col = t + 256 * j;
+                v[k][j] = (r + k < r1 && col < nb) ? hist[(r + k) * nb + col] : 0u;
+            }
+#pragma unroll
+        for (int k = 0; k < kWideRowBatch; ++k)
+#pragma unroll
+            for (int j = 0; j < kWidePer; ++j) sum[j] += v[k][j];
+    }
+#pragma unroll
+    for (int j = 0; j < kWidePer; ++j) {
+        const int col = t + 256 * j;
+        if (col < nb) csum[(int64_t)col * nrb + blockIdx.x] = sum[j];
+    }
+}
+
+// tot[d] = the keys of digit d (column totals, from k_hist_colscan).  Each workgroup turns them
+// into the digit bases (keys with a smaller digit; column 1024, the out-of-range bucket, after
+// every digit) and writes its row block's offsets.  Workgroup 0 also sets *ident (one bucket
+// holds every key) and *valid (if given: the keys in range, and whether none is out of range).
+__global__ __launch_bounds__(256) void k_hist_apply_w(const uint16_t* __restrict__ hist,
+                                                      uint32_t* __restrict__ off, int64_t nrows,
+                                                      int nb, int64_t nrb, int rb,
+                                                      const uint32_t* __restrict__ csum,
+                                                      const uint32_t* __restrict__ tot,
+                                                      uint32_t* __restrict__ ident,
+                                                      uint32_t* __restrict__ valid) {
+    __shared__ uint32_t s4[4];
+    __shared__ uint32_t s_base[kWideCols];
+    const int t = threadIdx.x;
+    // thread t scans digits 4t .. 4t + 3 (the 1024 regular ones)
+    uint32_t v[4], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[j] = tot[4 * t + j];
+        loc += v[j];
+    }
+    const uint32_t voor = nb > kWideB ? tot[kWideB] : 0u;
+    uint32_t total;
+    uint32_t ex = block_excl_scan_u32(loc, s4, &total);
+    const uint32_t grand = total + voor;
+    bool one = voor == grand;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        s_base[4 * t + j] = ex;
+        one = one || v[j] == grand;
+        ex += v[j];
+    }
+    if (t == 0) s_base[kWideB] = total;
+    const int anyone = __syncthreads_or(one);   // also publishes s_base
+    if (blockIdx.x == 0 && t == 0) {
+        *ident = anyone ? 1u : 0u;
+        if (valid) {
+            valid[0] = total;
+            valid[1] = voor == 0u ? 1u : 0u;
+        }
+    }
+    const int64_t r0 = (int64_t)blockIdx.x * rb;
+    const int64_t r1 = (r0 + rb < nrows) ? r0 + rb : nrows;
+    uint32_t run[kWidePer];
+#pragma unroll
+    for (int j = 0; j < kWidePer; ++j) {
+        const int col = t + 256 * j;
+        run[j] = col < nb ? s_base[col] + csum[(int64_t)col * nrb + blockIdx.x] : 0u;
+    }
+    for (int64_t r = r0; r < r1; r += kWideRowBatch) {
+        uint32_t w[kWideRowBatch][kWidePer];
+#pragma unroll
+        for (int k = 0; k < kWideRowBatch; ++k)
+#pragma unroll
+            for (int j = 0; j < kWidePer; ++j) {
+                const int col = t + 256 * j;
+                w[k][j] = (r + k < r1 && col < nb) ? hist[(r + k) * nb + col] : 0u;
+            }
+#pragma unroll
+        for (int k = 0; k < kWideRowBatch; ++k)
+#pragma unroll
+            for (int j = 0; j < kWidePer; ++j) {
+                const int col = t + 256 * j;
+                if (r + k < r1 && col < nb) off[(r + k) * nb + col] = run[j];
+                run[j] += w[k][j];
+            }
+    }
+}
+
+// Offsets of nb = 1025 or 1024 columns for nrows chunks (three launches, as hist_offsets).
+// csum needs nb * nrb words, tot nb words.
+det_status hist_offsets_w(const uint16_t* hist, uint32_t* off, int64_t nrows, int nb,
+                          uint32_t* csum, uint32_t* tot, uint32_t* valid, uint32_t* ident,
+                          hipStream_t s) {
+    KernelTimer kt("k_hist_offsets", s);
+    const int rb = nrows <= 4096 ? kRowBlkFew : kRowBlk;
+    const int64_t nrb = cdiv(nrows, rb);
+    k_hist_colsums_w<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, nrows, nb, nrb, rb, csum);
+    k_hist_colscan<<<dim3((unsigned)nb), dim3(256), 0, s>>>(csum, nrb, tot);
+    k_hist_apply_w<<<dim3((unsigned)nrb), dim3(256), 0, s>>>(hist, off, nrows, nb, nrb, rb, csum,
+                                                            tot, ident, valid);
     return launch_status();
 }
 
@@ -727,6 +936,189 @@ void radix_scatter(int64_t H, unsigned grid, size_t lds, hipStream_t s, const KI
             keys_in, pay_in, keys_out, pay_out, n, nvalid, B, shift, nchunks, hist_ex, ident);
 }
 
+// ---------------------------------------------------------------- 10-bit radix pass (f64)
+
+// Chunks of 4096 (key, f64 payload), 4 waves of 16 items per thread, as k_radix_scatter with
+// 1024 digits (1025 in a first pass that may meet keys out of range).  LDS: keys 16 KB,
+// payloads 32 KB, per-wave counters 16 KB, digit bases 4 KB: two workgroups per CU.
+constexpr int kWideCH = 4096;
+struct RadixSmemW {
+    uint32_t keys[kWideCH];
+    uint64_t pay[kWideCH];
+    uint32_t cnt[4][kWideCols];
+    uint32_t gbase[kWideCols];
+    uint32_t s4[4];
+};
+struct KeyW16 {};   // the key's high 10 bits as a 16-bit key
+
+template <typename KO>
+__device__ __forceinline__ void put_key_w(KO* keys_out, int64_t g, uint32_t kk) {
+    if constexpr (__is_same(KO, KeyW16))
+        reinterpret_cast<uint16_t*>(keys_out)[g] = (uint16_t)(kk >> kWideBits);
+    else
+        (void)keys_out, (void)g, (void)kk;
+}
+
+// Rank, stage and write one loaded chunk (as radix_rank_write).  Thread t owns digits 4t ..
+// 4t + 3 for the per-digit steps, and thread 0 also digit 1024 in a first pass.
+template <bool FIRST, bool FULL, typename KO, bool OOR>
+__device__ __forceinline__ void radix_rank_write_w(RadixSmemW& sm, const uint32_t (&key)[16],
+                                                   const uint64_t (&pay)[16], int64_t base,
+                                                   int64_t m, uint32_t B,
+                                                   const uint32_t (&off0)[4], uint32_t off1,
+                                                   KO* __restrict__ keys_out,
+                                                   uint64_t* __restrict__ pay_out, int tid,
+                                                   int lane, int wave) {
+    constexpr int IPT = 16, NT = 256, NW = 4;
+    constexpr int BITS = OOR ? kWideBits + 1 : kWideBits;
+    uint32_t rk[IPT];
+    const int64_t p0 = base + (int64_t)wave * 64 * IPT + lane;
+    uint32_t* const wcnt = sm.cnt[wave];
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+        const bool valid = FULL || p0 + k * 64 < m;
+        const int d = valid ? wide_digit<OOR>(key[k], B, 0) : 0;
+        uint32_t plo = FULL ? ~0u : (uint32_t)__ballot(valid);
+        uint32_t phi = FULL ? ~0u : (uint32_t)(__ballot(valid) >> 32);
+#pragma unroll
+        for (int b = 0; b < BITS; ++b) {
+            uint32_t rep = (uint32_t)__builtin_amdgcn_sbfe(d, b, 1);
+            asm volatile("" : "+v"(rep));
+            const uint64_t mb = __builtin_amdgcn_ballot_w64(rep != 0u);
+            plo = __builtin_amdgcn_bitop3_b32(plo, rep, (uint32_t)mb, 0x90);
+            phi = __builtin_amdgcn_bitop3_b32(phi, rep, (uint32_t)(mb >> 32), 0x90);
+        }
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi(phi, __builtin_amdgcn_mbcnt_lo(plo, 0u));
+        const uint32_t old = valid ? wcnt[d] : 0u;
+        if (valid && below == 0u) wcnt[d] = old + (uint32_t)__popc(plo) + (uint32_t)__popc(phi);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        rk[k] = old + below;
+    }
+    __syncthreads();
+    // per digit: the waves' exclusive offsets and the chunk's count
+    uint32_t dtot[4], loc = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int d = 4 * tid + j;
+        uint32_t run = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const uint32_t cw = sm.cnt[w][d];
+            sm.cnt[w][d] = run;
+            run += cw;
+        }
+        dtot[j] = run;
+        loc += run;
+    }
+    if (FIRST && tid == 0) {
+        uint32_t r2 = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const uint32_t cw = sm.cnt[w][kWideB];
+            sm.cnt[w][kWideB] = r2;
+            r2 += cw;
+        }
+    }
+    uint32_t total;
+    uint32_t ds = block_excl_scan_u32<NW>(loc, sm.s4, &total);
+    // each digit's start in the staged chunk folded into every wave's offset
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int d = 4 * tid + j;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sm.cnt[w][d] += ds;
+        sm.gbase[d] = off0[j] - ds;
+        ds += dtot[j];
+    }
+    if (FIRST && tid == 0) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sm.cnt[w][kWideB] += total;
+        sm.gbase[kWideB] = off1 - total;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+        if (FULL || p0 + k * 64 < m) {
+            const int d = wide_digit<OOR>(key[k], B, 0);
+            const uint32_t lp = sm.cnt[wave][d] + rk[k];
+            sm.keys[lp] = key[k];
+            sm.pay[lp] = pay[k];
+        }
+    }
+    __syncthreads();
+    auto emit = [&](int i) {
+        const uint32_t kk = sm.keys[i];
+        const int64_t g = (int64_t)(sm.gbase[wide_digit<OOR>(kk, B, 0)] + (uint32_t)i);
+        put_key_w<KO>(keys_out, g, kk);
+        pay_out[g] = sm.pay[i];
+    };
+    if constexpr (FULL) {
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) emit(k * NT + tid);
+    } else {
+        const int cntc = (int)((m - base) < kWideCH ? (m - base) : kWideCH);
+        for (int i = tid; i < cntc; i += NT) emit(i);
+    }
+}
+
+// One chunk per workgroup (xcd_chunk placement), as k_radix_scatter.
+template <bool FIRST, typename KO, typename KI>
+__global__ __launch_bounds__(256) void k_radix_scatter_w(
+    const KI* __restrict__ keys_in, const uint64_t* __restrict__ pay_in,
+    KO* __restrict__ keys_out, uint64_t* __restrict__ pay_out, int64_t n,
+    const uint32_t* __restrict__ nvalid, uint32_t B, int64_t nchunks,
+    const uint32_t* __restrict__ hist_ex, const uint32_t* __restrict__ ident) {
+    constexpr int IPT = 16;
+    constexpr int NB = FIRST ? kWideCols : kWideB;
+    __shared__ RadixSmemW sm;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t m = FIRST ? n : (int64_t)*nvalid;
+    const int64_t c = xcd_chunk(blockIdx.x, nchunks);
+    const int64_t base = c * kWideCH;
+    if (base >= m) return;
+    uint32_t key[IPT];
+    uint64_t pay[IPT];
+    if (*ident) {
+        // one bucket holds every key: the pass leaves every item where it is
+        radix_load<uint64_t, kWideCH, FIRST, false, false, KI>(keys_in, pay_in, base, m, key, pay,
+                                                                wave, lane);
+        const int64_t p0 = base + (int64_t)wave * 64 * IPT + lane;
+#pragma unroll
+        for (int k = 0; k < IPT; ++k) {
+            const int64_t p = p0 + k * 64;
+            if (p < m) {
+                put_key_w<KO>(keys_out, p, key[k]);
+                pay_out[p] = pay[k];
+            }
+        }
+        return;
+    }
+    uint32_t off0[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) off0[j] = hist_ex[c * NB + 4 * tid + j];
+    const uint32_t off1 = (FIRST && tid == 0) ? hist_ex[c * NB + kWideB] : 0u;
+    for (int i = tid; i < 4 * kWideCols; i += 256) (&sm.cnt[0][0])[i] = 0u;
+    if (base + kWideCH <= m) {
+        radix_load<uint64_t, kWideCH, FIRST, false, true, KI>(keys_in, pay_in, base, m, key, pay,
+                                                               wave, lane);
+        __syncthreads();
+        if (FIRST && nvalid[1])   // no key out of range: 10-bit ranking
+            radix_rank_write_w<FIRST, true, KO, false>(sm, key, pay, base, m, B, off0, off1,
+                                                       keys_out, pay_out, tid, lane, wave);
+        else
+            radix_rank_write_w<FIRST, true, KO, FIRST>(sm, key, pay, base, m, B, off0, off1,
+                                                       keys_out, pay_out, tid, lane, wave);
+    } else {
+        radix_load<uint64_t, kWideCH, FIRST, false, false, KI>(keys_in, pay_in, base, m, key, pay,
+                                                                wave, lane);
+        __syncthreads();
+        radix_rank_write_w<FIRST, false, KO, FIRST>(sm, key, pay, base, m, B, off0, off1,
+                                                    keys_out, pay_out, tid, lane, wave);
+    }
+}
+
 // ---------------------------------------------------------------- destinations
 
 // off[b] = first sorted position with key >= b, for b in [0, B]; n_skipped = n - valid.
@@ -800,6 +1192,49 @@ __global__ __launch_bounds__(256) void k_bin_offsets_bytes(
         off[b] = o;
     }
     if (l == 0 && h == 0) {
+        off[B] = (uint32_t)m;
+        if (n_skipped) *n_skipped = n - m;
+    }
+}
+
+// The 10-bit path: off[b] for b = 1024 h + l (l the low 10 bits, h the high ones) = the keys
+// with a high part below h, plus those with high part h and low part below l.  The first pass
+// put low part l at positions from pos = row1[l] on; with c the chunk holding pos, the second
+// pass's offset of digit h in chunk c counts the first kind and the keys of high part h in
+// chunk c before pos, and the keys of [c H, pos) with high part h (counted here from the first
+// pass's 16-bit keys) complete it; when pos = m, off[b] = the start of the second pass's bucket
+// h + 1.  Workgroup l, thread t takes h = t + 256 j.
+__global__ __launch_bounds__(256) void k_bin_offsets_w(const uint32_t* __restrict__ row1,
+                                                       const uint32_t* __restrict__ ex2,
+                                                       const uint16_t* __restrict__ hb,
+                                                       const uint32_t* __restrict__ nvalid,
+                                                       int64_t B, int64_t n, int64_t H,
+                                                       uint32_t* __restrict__ off,
+                                                       int64_t* __restrict__ n_skipped) {
+    __shared__ uint32_t cnt[kWideB];
+    const int l = blockIdx.x, t = threadIdx.x;
+    const int64_t m = *nvalid;
+    const int64_t pos = row1[l];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cnt[t + 256 * j] = 0u;
+    __syncthreads();
+    const int64_t c = pos / H;
+    if (pos < m)
+        for (int64_t q = c * H + t; q < pos; q += 256)
+            count_digit(cnt, (int)(hb[q] & (uint32_t)(kWideB - 1)));
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int h = t + 256 * j;
+        const int64_t b = (int64_t)h * kWideB + l;
+        if (b < B) {
+            uint32_t o;
+            if (pos < m) o = ex2[c * kWideB + h] + cnt[h];
+            else o = h < kWideB - 1 ? ex2[h + 1] : (uint32_t)m;   // row 0: the bucket starts
+            off[b] = o;
+        }
+    }
+    if (l == 0 && t == 0) {
         off[B] = (uint32_t)m;
         if (n_skipped) *n_skipped = n - m;
     }
@@ -1535,6 +1970,7 @@ struct SLayout {
     int64_t H, nchunks, nhist, nsums, nrange;
     int bytes;    // byte paths for scalar destinations: 2 passes for (256, 65536], 3 passes
                   // for (65536, 2^24]; 0 otherwise
+    bool wide;    // f64 into (65536, 2^20] destinations, more than kSmallN keys: two 10-bit passes
     size_t keysA, keysB, payA, payB, cnt, hist, hist2, hist3, off2, sums, ctrl, off, rbin, pF,
         pC, total;
 };
@@ -1547,10 +1983,13 @@ SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt,
     const size_t pw = (rows || idx_payload) ? 4 : dtype_size(dt);    // payload bytes
     L.H = n <= kSmallN ? kChunkSmall : (pw == 4 ? kChunkBig<uint32_t> : kChunkBig<uint64_t>);
     L.nchunks = cdiv(n > 0 ? n : 1, L.H);
-    L.nhist = (int64_t)kBuckets0 * L.nchunks;
+    L.wide = !rows && !idx_payload && dt == DET_F64 && num_out > 65536 &&
+             num_out <= ((int64_t)1 << 20) && n > kSmallN;   // chunks of kWideCH = 4096
+    const int64_t cols = L.wide ? kWideCols : kBuckets0;
+    L.nhist = cols * L.nchunks;
     // column sums (row blocks of 16 up to 4096 rows, else 128) + totals
-    L.nsums = (int64_t)kBuckets0 * cdiv(L.nchunks, L.nchunks <= 4096 ? kRowBlkFew : kRowBlk) +
-              512;
+    L.nsums = cols * cdiv(L.nchunks, L.nchunks <= 4096 ? kRowBlkFew : kRowBlk) +
+              (L.wide ? 2048 : 512);
     const int64_t D = rows ? kRowD : kSegD;
     L.nrange = cdiv(n > 0 ? n : 1, D);
     const size_t es = dtype_size(dt);
@@ -1572,10 +2011,11 @@ SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt,
     L.off = take((size_t)(num_out + 1) * 4);
     const int kp = key_passes(num_out);
     L.bytes = (!rows && !idx_payload && (kp == 2 || kp == 3)) ? kp : 0;
-    L.hist2 = take(L.bytes ? (size_t)256 * L.nchunks * 4 : 4);
-    L.hist3 = take(L.bytes == 3 ? (size_t)256 * L.nchunks * 4 : 4);
-    L.off2 = take(L.bytes == 3 ? (size_t)(65536 + 1) * 4 : 4);
-    L.rbin = take(L.bytes ? (size_t)L.nrange * 4 : 4);
+    L.hist2 = take(L.wide ? (size_t)kWideB * L.nchunks * 4
+                          : L.bytes ? (size_t)256 * L.nchunks * 4 : 4);
+    L.hist3 = take(L.bytes == 3 && !L.wide ? (size_t)256 * L.nchunks * 4 : 4);
+    L.off2 = take(L.bytes == 3 && !L.wide ? (size_t)(65536 + 1) * 4 : 4);
+    L.rbin = take(L.bytes || L.wide ? (size_t)L.nrange * 4 : 4);
     L.pF = take((size_t)L.nrange * pe);
     L.pC = take((size_t)L.nrange * pe);
     L.total = o;
@@ -1731,6 +2171,62 @@ det_status sort_by_dest_bytes(const int32_t* index, const P* pay_in0, int64_t n,
     return DET_SUCCESS;
 }
 
+// The 10-bit path (L.wide): two passes over chunks of 4096, the first on the low 10 bits
+// writing the high 10 as 16-bit keys (keysA), the second on those writing no key.  *SP
+// receives the sorted payloads.
+static_assert(kChunkBig<uint64_t> == kWideCH, "the 10-bit passes take the f64 chunk size");
+det_status sort_by_dest_w(const int32_t* index, const uint64_t* pay_in0, int64_t n,
+                          int64_t num_out, const SLayout& L, char* ws, hipStream_t s,
+                          const uint64_t** SP) {
+    uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);
+    uint64_t* pay[2] = {reinterpret_cast<uint64_t*>(ws + L.payA),
+                        reinterpret_cast<uint64_t*>(ws + L.payB)};
+    uint16_t* cnt = reinterpret_cast<uint16_t*>(ws + L.cnt);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+    uint32_t* hist2 = reinterpret_cast<uint32_t*>(ws + L.hist2);
+    uint32_t* sums = reinterpret_cast<uint32_t*>(ws + L.sums);
+    uint16_t* k16 = reinterpret_cast<uint16_t*>(ws + L.keysA);
+    const uint32_t* kin = reinterpret_cast<const uint32_t*>(index);
+    const uint32_t B = (uint32_t)num_out;
+    const unsigned grid = (unsigned)L.nchunks;
+    const unsigned hgrid = (unsigned)cdiv(L.nchunks, 4);
+    const size_t lds = (size_t)launch_override().extra_lds;
+    const int H = (int)L.H;
+    det_status st;
+    {
+        KernelTimer kt("k_radix_hist", s);
+        k_radix_hist_w<true, uint32_t><<<hgrid, 256, lds, s>>>(kin, n, ctrl, B, kWideCols,
+                                                                L.nchunks, H, cnt);
+    }
+    if ((st = hist_offsets_w(cnt, hist, L.nchunks, kWideCols, sums + 2048, sums, ctrl, ctrl + 16,
+                             s)) != DET_SUCCESS)
+        return st;
+    {
+        KernelTimer kt("k_radix_scatter", s);
+        k_radix_scatter_w<true, KeyW16, uint32_t><<<grid, 256, lds, s>>>(
+            kin, pay_in0, reinterpret_cast<KeyW16*>(k16), pay[0], n, ctrl, B, L.nchunks, hist,
+            ctrl + 16);
+    }
+    if ((st = launch_status()) != DET_SUCCESS) return st;
+    {
+        KernelTimer kt("k_radix_hist", s);
+        k_radix_hist_w<false, uint16_t><<<hgrid, 256, lds, s>>>(k16, n, ctrl, B, kWideB,
+                                                                 L.nchunks, H, cnt);
+    }
+    if ((st = hist_offsets_w(cnt, hist2, L.nchunks, kWideB, sums + 2048, sums, nullptr,
+                             ctrl + 17, s)) != DET_SUCCESS)
+        return st;
+    {
+        KernelTimer kt("k_radix_scatter", s);
+        k_radix_scatter_w<false, NoKey, uint16_t><<<grid, 256, lds, s>>>(
+            k16, pay[0], static_cast<NoKey*>(nullptr), pay[1], n, ctrl, B, L.nchunks, hist2,
+            ctrl + 17);
+    }
+    if ((st = launch_status()) != DET_SUCCESS) return st;
+    *SP = pay[1];
+    return DET_SUCCESS;
+}
+
 template <typename T, typename P, bool ROWS>
 det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_t row_len, T* out,
                         int64_t num_out, T* prev, int64_t* n_skipped, char* ws, bool neg,
@@ -1756,18 +2252,33 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
     uint32_t* ctrl = reinterpret_cast<uint32_t*>(ws + L.ctrl);   // [0] = number of valid keys
     uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
     if constexpr (!ROWS) {
-        if (L.bytes) {
-            // byte keys, offsets from the histograms, no key reads after the sort
+        if (L.bytes || L.wide) {
+            // byte keys (or 10-bit digits), offsets from the histograms, no key reads after the
+            // sort
             const P* SP = nullptr;
-            det_status st = sort_by_dest_bytes<P>(index, reinterpret_cast<const P*>(values), n,
-                                                  num_out, L, ws, s, &SP);
+            det_status st;
+            if constexpr (std::is_same_v<P, uint64_t>) {
+                if (L.wide)
+                    st = sort_by_dest_w(index, reinterpret_cast<const uint64_t*>(values), n,
+                                        num_out, L, ws, s, &SP);
+                else
+                    st = sort_by_dest_bytes<P>(index, reinterpret_cast<const P*>(values), n,
+                                               num_out, L, ws, s, &SP);
+            } else {
+                st = sort_by_dest_bytes<P>(index, reinterpret_cast<const P*>(values), n, num_out,
+                                           L, ws, s, &SP);
+            }
             if (st != DET_SUCCESS) return st;
             uint32_t* rbin = reinterpret_cast<uint32_t*>(ws + L.rbin);
             const uint32_t* h1 = reinterpret_cast<const uint32_t*>(ws + L.hist);
             const uint32_t* h2 = reinterpret_cast<const uint32_t*>(ws + L.hist2);
             {
                 KernelTimer kt("k_bin_offsets", s);
-                if (L.bytes == 2) {
+                if (L.wide) {
+                    k_bin_offsets_w<<<kWideB, 256, 0, s>>>(
+                        h1, h2, reinterpret_cast<const uint16_t*>(ws + L.keysA), ctrl, num_out, n,
+                        L.H, off, n_skipped);
+                } else if (L.bytes == 2) {
                     k_bin_offsets_bytes<uint8_t><<<256, 256, 0, s>>>(
                         h1, h2, reinterpret_cast<const uint8_t*>(ws + L.keysA), ctrl, num_out, n,
                         L.H, off, n_skipped);

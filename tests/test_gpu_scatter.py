@@ -135,6 +135,51 @@ def test_zipf_f64(dev):
     assert bits_equal(got, want), first_mismatch(got, want)
 
 
+# f64 into (65536, 2^20] destinations with more than 2^22 values: two 10-bit digit passes
+@pytest.mark.parametrize("n,B", [((1 << 22) + 4097, 65537), ((1 << 22) + 1, 1 << 20),
+                                 (5_000_011, 300_007)])
+def test_ten_bit_passes_parity(dev, n, B):
+    rng = np.random.default_rng(n ^ B)
+    v = rounding(n, F64, n % 1000)
+    idx = rng.integers(-2, B + 2, n).astype(np.int32)   # a few out of range
+    o = rounding(B, F64, B % 1000)
+    got, prev, k = gpu_scatter(v, idx, o, dev, want_prev=True)
+    want, wprev, wk = oracle.scatter_add(v, idx, o, want_prev=True)
+    assert bits_equal(got, want), (n, B, first_mismatch(got, want))
+    assert k == wk
+    assert bits_equal(prev, wprev)
+
+
+@pytest.mark.parametrize("kind", ["zipf", "one_low_digit", "one_high_digit", "one_bin", "sub"])
+def test_ten_bit_passes_skew(dev, kind):
+    n, B = (1 << 22) + 777, 1 << 20
+    rng = np.random.default_rng(7)
+    v = rounding(n, F64, 3)
+    if kind == "zipf":
+        idx = workloads.zipf_bins(n, B, seed=5)
+    elif kind == "one_low_digit":    # every key in one bucket of the first pass
+        idx = (rng.integers(0, B >> 10, n) * 1024 + 5).astype(np.int32)
+    elif kind == "one_high_digit":   # every key in one bucket of the second pass
+        idx = rng.integers(0, 1024, n).astype(np.int32)
+    elif kind == "one_bin":
+        idx = np.full(n, B - 1, np.int32)
+    else:
+        idx = rng.integers(0, B, n).astype(np.int32)
+    o = rounding(B, F64, 11)
+    if kind == "sub":
+        vt = torch.from_numpy(v).to(dev)
+        it = torch.from_numpy(idx).to(dev)
+        ot = torch.from_numpy(o.copy()).to(dev)
+        det.det_scatter_sub(vt, it, ot)
+        got = ot.cpu().numpy()
+        want = oracle.scatter_sub(v, idx, o)
+        want = want[0] if isinstance(want, tuple) else want
+    else:
+        got, _, _ = gpu_scatter(v, idx, o, dev)
+        want, _, _ = oracle.scatter_add(v, idx, o)
+    assert bits_equal(got, want), (kind, first_mismatch(got, want))
+
+
 # ---------------------------------------------------------------- rows
 
 def test_rows_worked_example(dev):
