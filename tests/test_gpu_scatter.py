@@ -180,6 +180,25 @@ def test_ten_bit_passes_skew(dev, kind):
     assert bits_equal(got, want), (kind, first_mismatch(got, want))
 
 
+def test_ten_bit_path_is_taken(dev):
+    # f64 into (65536, 2^20] destinations: two radix passes above 2^22 values, three 8-bit
+    # passes up to 2^22 (same bits either way, checked above)
+    B = 1 << 20
+    for n, passes in [((1 << 22) + 1, 2), (1 << 22, 3)]:
+        v = torch.zeros(n, dtype=torch.float64, device=dev)
+        idx = torch.zeros(n, dtype=torch.int32, device=dev)
+        out = torch.zeros(B, dtype=torch.float64, device=dev)
+        torch.cuda.synchronize()
+        det.det_debug_kernel_timing(True)
+        try:
+            det.det_scatter_add(v, idx, out)
+            torch.cuda.synchronize()
+            rep = det.det_debug_kernel_report()
+        finally:
+            det.det_debug_kernel_timing(False)
+        assert rep["k_radix_scatter"][0] == passes, (n, rep["k_radix_scatter"])
+
+
 # ---------------------------------------------------------------- rows
 
 def test_rows_worked_example(dev):
