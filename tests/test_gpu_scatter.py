@@ -150,7 +150,8 @@ def test_ten_bit_passes_parity(dev, n, B):
     assert bits_equal(prev, wprev)
 
 
-@pytest.mark.parametrize("kind", ["zipf", "one_low_digit", "one_high_digit", "one_bin", "sub"])
+@pytest.mark.parametrize("kind", ["zipf", "one_low_digit", "one_high_digit", "one_bin", "sub",
+                                  "all_out"])
 def test_ten_bit_passes_skew(dev, kind):
     n, B = (1 << 22) + 777, 1 << 20
     rng = np.random.default_rng(7)
@@ -163,6 +164,8 @@ def test_ten_bit_passes_skew(dev, kind):
         idx = rng.integers(0, 1024, n).astype(np.int32)
     elif kind == "one_bin":
         idx = np.full(n, B - 1, np.int32)
+    elif kind == "all_out":          # every key out of range: nothing is added
+        idx = np.where(rng.random(n) < 0.5, -1, B + 7).astype(np.int32)
     else:
         idx = rng.integers(0, B, n).astype(np.int32)
     o = rounding(B, F64, 11)
@@ -175,8 +178,9 @@ def test_ten_bit_passes_skew(dev, kind):
         want = oracle.scatter_sub(v, idx, o)
         want = want[0] if isinstance(want, tuple) else want
     else:
-        got, _, _ = gpu_scatter(v, idx, o, dev)
-        want, _, _ = oracle.scatter_add(v, idx, o)
+        got, _, k = gpu_scatter(v, idx, o, dev)
+        want, _, wk = oracle.scatter_add(v, idx, o)
+        assert k == wk
     assert bits_equal(got, want), (kind, first_mismatch(got, want))
 
 
