@@ -1707,27 +1707,47 @@ __global__ __launch_bounds__(256) void k_segred_rows(const uint32_t* __restrict_
                                                      T* __restrict__ out, T* __restrict__ pF,
                                                      T* __restrict__ pC) {
     constexpr int CPL = 4;   // columns per lane per pass
+    // the keys and source rows of positions [lo, lo + 2 kRowD) (a block starting in this range
+    // reaches at most kRowD positions past it), and per block its first position and its
+    // destination's bounds, all fetched up front so a block's only dependent loads are its rows
+    __shared__ uint32_t s_K[2 * kRowD];
+    __shared__ uint32_t s_R[2 * kRowD];
     __shared__ uint32_t s_item[kRowD + 2];
+    __shared__ uint32_t s_seg[kRowD + 2][2];
     __shared__ uint32_t s_nitem;
-    __shared__ uint32_t s_rows[4][kRowD];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t m = *nvalid;
     const int64_t lo = (int64_t)blockIdx.x * kRowD;
     if (lo >= m) return;
     const int64_t hi = (lo + kRowD < m) ? lo + kRowD : m;
     if (tid == 0) s_nitem = 0u;
+    if (tid < 2 * kRowD && lo + tid < m) {
+        s_K[tid] = K[lo + tid];
+        s_R[tid] = R[lo + tid];
+    }
     __syncthreads();
     if (tid < kRowD) {
         const int64_t p = lo + tid;
         if (p < hi) {
-            const uint32_t b = K[p];
-            if (p == 0 || K[p - 1] != b) s_item[atomicAdd(&s_nitem, 1u)] = (uint32_t)p;
-            if (p == lo) {
-                const int64_t s0 = off[b];
-                if (s0 < lo) {
+            const uint32_t b = s_K[tid];
+            const bool head = p == 0 || (tid > 0 ? s_K[tid - 1] : K[p - 1]) != b;
+            if (head || p == lo) {
+                const uint32_t s0 = off[b], e0 = off[b + 1];
+                if (head) {
+                    const uint32_t k = atomicAdd(&s_nitem, 1u);
+                    s_item[k] = (uint32_t)p;
+                    s_seg[k][0] = s0;
+                    s_seg[k][1] = e0;
+                } else if ((int64_t)s0 < lo) {
+                    // the destination running into the range: its block at the next multiple of
+                    // kRowD of its ranks
                     const int64_t pc = s0 + cdiv(lo - s0, kRowD) * kRowD;
-                    if (pc < hi && pc < (int64_t)off[b + 1])
-                        s_item[atomicAdd(&s_nitem, 1u)] = (uint32_t)pc;
+                    if (pc < hi && pc < (int64_t)e0) {
+                        const uint32_t k = atomicAdd(&s_nitem, 1u);
+                        s_item[k] = (uint32_t)pc;
+                        s_seg[k][0] = s0;
+                        s_seg[k][1] = e0;
+                    }
                 }
             }
         }
@@ -1736,13 +1756,10 @@ __global__ __launch_bounds__(256) void k_segred_rows(const uint32_t* __restrict_
     const int nitem = (int)s_nitem;
     for (int it = wave; it < nitem; it += 4) {
         const int64_t ps = s_item[it];
-        const uint32_t b = K[ps];
-        const int64_t seg_s = off[b], seg_e = off[b + 1];
+        const uint32_t b = s_K[ps - lo];
+        const int64_t seg_s = s_seg[it][0], seg_e = s_seg[it][1];
         const int len = (int)((seg_e - ps) < kRowD ? (seg_e - ps) : kRowD);
-        if (lane < len) s_rows[wave][lane] = R[ps + lane];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const uint32_t* rows = s_R + (ps - lo);   // ps - lo + len <= 2 kRowD
         T* dst;
         if (seg_e - seg_s <= kRowD) dst = out + (int64_t)b * d;
         else if (ps == seg_s) dst = pF + (ps / kRowD) * d;
@@ -1764,7 +1781,7 @@ __global__ __launch_bounds__(256) void k_segred_rows(const uint32_t* __restrict_
                 for (int r = 0; r < 8; ++r) {
                     const int q = gi * 8 + r;
                     if (q < len) {
-                        const T* row = src + (int64_t)s_rows[wave][q] * d;
+                        const T* row = src + (int64_t)rows[q] * d;
 #pragma unroll
                         for (int cc = 0; cc < CPL; ++cc) {
                             const int64_t col = c0 + cc * 64 + lane;
@@ -1788,60 +1805,84 @@ __global__ __launch_bounds__(256) void k_segred_rows(const uint32_t* __restrict_
                 if (col < d) dst[col] = single ? dst[col] + r : r;
             }
         }
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
-// rows of destinations with more than 64 members: PW over their block rows per column
+// rows of destinations with more than 64 members: PW over their block rows per column.  A wave
+// takes one long destination and 64 columns (one per lane); blockIdx.y walks the column chunks.
+// Blocks are read 8 at a time: 8 consecutive blocks starting at a multiple of 8 are an aligned
+// subtree, reduced in registers and pushed as one node of a binary counter (levels of 8 blocks
+// and up, in LDS); a last, partial group is the same 8-leaf tree with the identity past the end,
+// which equals the PW of its blocks, and stands for the counter's three lowest levels.
 template <typename T>
 __global__ __launch_bounds__(256) void k_segred_rows_long(const uint32_t* __restrict__ off,
                                                           int64_t B, int64_t d,
                                                           const T* __restrict__ pF,
                                                           const T* __restrict__ pC,
                                                           T* __restrict__ out) {
-    __shared__ T s_stk[32][256];
-    __shared__ uint32_t s_list[256];
-    __shared__ uint32_t s_n;
-    const int tid = threadIdx.x;
-    for (int64_t g = blockIdx.x; g * 256 < B; g += gridDim.x) {
-        if (tid == 0) s_n = 0u;
-        __syncthreads();
-        const int64_t b = g * 256 + tid;
-        if (b < B && (int64_t)off[b + 1] - (int64_t)off[b] > kRowD)
-            s_list[atomicAdd(&s_n, 1u)] = (uint32_t)tid;
-        __syncthreads();
-        const int cnt = (int)s_n;
-        for (int i = 0; i < cnt; ++i) {
-            const int64_t bb = g * 256 + s_list[i];
+    constexpr int LV = 24;   // counter levels of 8 .. 2^26 blocks (2^32 members)
+    __shared__ T s_stk[4][LV][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    // lane l checks destination g + l nw, as in the scalar case
+    for (int64_t g = gw; g < B; g += 64 * nw) {
+        const int64_t b = g + (int64_t)lane * nw;
+        const bool lng = b < B && (int64_t)off[b + 1] - (int64_t)off[b] > kRowD;
+        uint64_t mask = __ballot(lng);
+        while (mask) {
+            const int l = __ffsll((long long)mask) - 1;
+            mask &= mask - 1;
+            const int64_t bb = g + (int64_t)l * nw;
             const int64_t seg_s = off[bb], seg_e = off[bb + 1];
             const int64_t nblk = cdiv(seg_e - seg_s, kRowD);
             const int64_t r0 = seg_s / kRowD;
-            for (int64_t col = tid; col < d; col += 256) {
-                // binary counter over the block rows, stack in LDS (one column per thread)
-                for (int64_t s = 0; s < nblk; ++s) {
-                    T v = (s == 0) ? pF[r0 * d + col] : pC[(r0 + s) * d + col];
-                    int64_t k = s;
+            for (int64_t col = (int64_t)blockIdx.y * 64 + lane; col < d;
+                 col += 64 * (int64_t)gridDim.y) {
+                // block k of the destination: pF[r0] for k = 0, pC[r0 + k] after it
+                int64_t s = 0;
+                for (; s + 8 <= nblk; s += 8) {
+                    T v[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        v[j] = (s + j == 0 ? pF : pC)[(r0 + s + j) * d + col];
+                    T t = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+                    int64_t k = s >> 3;
                     int lvl = 0;
                     while (k & 1) {
-                        v = s_stk[lvl][tid] + v;
+                        t = s_stk[wave][lvl][lane] + t;
                         k >>= 1;
                         ++lvl;
                     }
-                    s_stk[lvl][tid] = v;
+                    s_stk[wave][lvl][lane] = t;
                 }
                 T acc = ident<T>();
-                bool have = false;
-                for (int lvl = 0; lvl < 32; ++lvl) {
-                    if ((nblk >> lvl) & 1) {
-                        acc = have ? s_stk[lvl][tid] + acc : s_stk[lvl][tid];
-                        have = true;
-                    }
+                if (s < nblk) {
+                    T v[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        v[j] = s + j < nblk ? (s + j == 0 ? pF : pC)[(r0 + s + j) * d + col]
+                                            : ident<T>();
+                    acc = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
                 }
+                const int64_t q = nblk >> 3;
+                for (int lvl = 0; lvl < LV; ++lvl)
+                    if ((q >> lvl) & 1) acc = s_stk[wave][lvl][lane] + acc;
                 out[bb * d + col] = out[bb * d + col] + acc;
             }
         }
-        __syncthreads();
     }
+}
+
+// Launch shape of k_segred_rows_long: one chunk of 64 columns per blockIdx.y, and enough
+// waves that a few long destinations each get their own.
+inline dim3 rows_long_grid(int64_t B, int64_t d) {
+    int64_t gy = cdiv(d, 64);
+    if (gy > 64) gy = 64;
+    int64_t gx = cdiv(B, 4);
+    const int64_t cap = 2048 / gy;
+    if (gx > cap) gx = cap;
+    return dim3((unsigned)gx, (unsigned)gy);
 }
 
 
@@ -2374,10 +2415,9 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
                 k_segred_rows<T, true><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
                     K, SR, off, ctrl, values, row_len, out, pF, pC);
         }
-        int64_t rg = cdiv(num_out, 256);
-        if (rg > 4096) rg = 4096;
-        k_segred_rows_long<T><<<dim3((unsigned)rg), dim3(256), 0, s>>>(off, num_out, row_len, pF,
-                                                                        pC, out);
+        KernelTimer kt("k_segred_rows_long", s);
+        k_segred_rows_long<T><<<rows_long_grid(num_out, row_len), dim3(256), 0, s>>>(
+            off, num_out, row_len, pF, pC, out);
     }
     return launch_status();
 }
@@ -2489,10 +2529,9 @@ det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n
             k_segred_rows<T, false><<<dim3((unsigned)L.nrange), dim3(256), 0, s>>>(
                 K, SRC, off, ctrl, values, row_len, out, pF, pC);
         }
-        int64_t rg = cdiv(num_out, 256);
-        if (rg > 4096) rg = 4096;
-        k_segred_rows_long<T><<<dim3((unsigned)rg), dim3(256), 0, s>>>(off, num_out, row_len, pF,
-                                                                        pC, out);
+        KernelTimer kt("k_segred_rows_long", s);
+        k_segred_rows_long<T><<<rows_long_grid(num_out, row_len), dim3(256), 0, s>>>(
+            off, num_out, row_len, pF, pC, out);
     }
     return launch_status();
 }

@@ -227,6 +227,27 @@ def test_rows_parity(dev, dtype, n, d, B):
     assert k == wk and bits_equal(prev, wprev)
 
 
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("sizes,d", [
+    # member counts chosen for the long-destination counter: 2..7 blocks of 64, whole groups of
+    # 8 blocks (one and several counter levels), groups plus a partial last group
+    ((65, 64 * 7 + 1, 64 * 8, 64 * 8 + 1, 64 * 8 * 3 + 64 * 5 + 10, 64 * 64 * 2 + 3), 5),
+    ((1024,) * 16, 256),
+    # more than 64 chunks of 64 columns: a wave walks the column chunks
+    ((150, 151), 4160)])
+def test_rows_long_destinations(dev, dtype, sizes, d):
+    rng = np.random.default_rng(sum(sizes) + d)
+    idx = np.concatenate([np.full(c, b, np.int32) for b, c in enumerate(sizes)])
+    idx = np.concatenate([idx, np.array([-1, len(sizes)], np.int32)])
+    idx = idx[rng.permutation(idx.size)]
+    v = rounding((idx.size, d), dtype, d)
+    o = rounding((len(sizes), d), dtype, 1)
+    got, prev, k = gpu_scatter(v, idx, o, dev, want_prev=True)
+    want, wprev, wk = oracle.scatter_add(v, idx, o, want_prev=True)
+    assert bits_equal(got, want), (sizes, d, first_mismatch(got, want))
+    assert k == wk == 2 and bits_equal(prev, wprev)
+
+
 def test_rows_c4_shape(dev):
     src, rows, out0 = workloads.rows_case()
     got, _, _ = gpu_scatter(src, rows, out0, dev)
