@@ -284,41 +284,52 @@ __global__ __launch_bounds__(256) void k_hist_offsets_small(const uint16_t* __re
                                                             uint32_t* __restrict__ valid,
                                                             uint32_t* __restrict__ ident) {
     constexpr int R = (int)kSmallHistRows;
+    static_assert(R == 64, "the out-of-range column takes one row per lane of a wave");
     __shared__ uint32_t s4[4];
     __shared__ uint32_t s_c256;
-    const int t = threadIdx.x;
-    const bool extra = nb > 256 && t == 0;
-    uint32_t v[R], w[R];
+    const int t = threadIdx.x, lane = t & 63;
+    const int nr = (int)nrows;   // 1 .. R
+    // column t; rows past nr load row nr - 1 (in bounds, no branch) and count as zero
+    uint32_t v[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        v[r] = r < nrows ? (uint32_t)hist[(int64_t)r * nb + t] : 0u;
-        w[r] = (extra && r < nrows) ? (uint32_t)hist[(int64_t)r * nb + 256] : 0u;
+        const uint32_t x = hist[(int64_t)(r < nr ? r : nr - 1) * nb + t];
+        v[r] = r < nr ? x : 0u;
     }
-    uint32_t c0 = 0, c256 = 0;
+    // the out-of-range column (nb = 257): row lane of wave 0, an inclusive scan over the rows
+    const bool extra = nb > 256 && t < 64;
+    uint32_t w = 0u, winc = 0u;
+    if (extra) {
+        w = lane < nr ? (uint32_t)hist[(int64_t)lane * nb + 256] : 0u;
+        winc = w;
+        for (int dd = 1; dd < 64; dd <<= 1) {
+            const uint32_t o = shfl_up(winc, dd, lane);
+            if (lane >= dd) winc += o;
+        }
+        if (lane == 63) s_c256 = winc;
+    } else if (t == 0) {
+        s_c256 = 0u;
+    }
+    uint32_t c0 = 0;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        c0 += v[r];
-        c256 += w[r];
-    }
-    if (t == 0) s_c256 = c256;
+    for (int r = 0; r < R; ++r) c0 += v[r];
     uint32_t total;
     uint32_t run0 = block_excl_scan_u32(c0, s4, &total);   // its barriers publish s_c256
-    const uint32_t grand = total + s_c256;
-    const int one = __syncthreads_or(c0 == grand || s_c256 == grand);
+    const uint32_t c256 = s_c256;
+    const uint32_t grand = total + c256;
+    const int one = __syncthreads_or(c0 == grand || c256 == grand);
     if (t == 0) *ident = one ? 1u : 0u;
-    uint32_t run1 = total;
+    uint32_t* po = off + t;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        if (r < nrows) {
-            off[(int64_t)r * nb + t] = run0;
-            if (extra) off[(int64_t)r * nb + 256] = run1;
-        }
+        if (r < nr) po[0] = run0;
+        po += nb;
         run0 += v[r];
-        run1 += w[r];
     }
+    if (extra && lane < nr) off[(int64_t)lane * nb + 256] = total + winc - w;
     if (valid && t == 0) {
         valid[0] = total;
-        valid[1] = s_c256 == 0u ? 1u : 0u;   // no key out of range
+        valid[1] = c256 == 0u ? 1u : 0u;   // no key out of range
     }
 }
 
