@@ -333,6 +333,103 @@ __global__ __launch_bounds__(256) void k_hist_offsets_small(const uint16_t* __re
     }
 }
 
+// The same for 65 to 256 rows in one launch of one workgroup of 1024 threads: thread (q, d)
+// holds rows 64 q .. 64 q + 63 of column d in registers; the column totals are the four
+// quarters' sums, and quarter q starts its running offsets after the quarters before it.  The
+// out-of-range column goes a row per lane to the first wave of each quarter.
+constexpr int64_t kMidHistRows = 256;
+
+__global__ __launch_bounds__(1024) void k_hist_offsets_mid(const uint16_t* __restrict__ hist,
+                                                           uint32_t* __restrict__ off,
+                                                           int64_t nrows, int nb,
+                                                           uint32_t* __restrict__ valid,
+                                                           uint32_t* __restrict__ ident) {
+    __shared__ uint32_t s_part[4][256];
+    __shared__ uint32_t s_base[256];
+    __shared__ uint32_t s4[4];
+    __shared__ uint32_t s_oor[4];
+    __shared__ uint32_t s_total;
+    const int t = threadIdx.x, d = t & 255, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6), q = wave >> 2;   // uniform per wave
+    const int nr = (int)nrows;   // 65 .. 256
+    const int r0 = 64 * q;
+    // rows past nr load row nr - 1 (in bounds, no branch); they are a suffix, left out of the
+    // sum and written nowhere
+    uint32_t v[64];
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+        const int rr = r0 + r;
+        v[r] = hist[(int64_t)(rr < nr ? rr : nr - 1) * nb + d];
+    }
+    uint32_t cq = 0;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) cq += r0 + r < nr ? v[r] : 0u;
+    s_part[q][d] = cq;
+    const bool extra = nb > 256 && d < 64;   // the first wave of each quarter
+    uint32_t w = 0u, winc = 0u;
+    if (extra) {
+        const int rr = r0 + lane;
+        w = rr < nr ? (uint32_t)hist[(int64_t)rr * nb + 256] : 0u;
+        winc = w;
+        for (int dd = 1; dd < 64; dd <<= 1) {
+            const uint32_t o = shfl_up(winc, dd, lane);
+            if (lane >= dd) winc += o;
+        }
+        if (lane == 63) s_oor[q] = winc;
+    } else if (nb <= 256 && t < 4) {
+        s_oor[t] = 0u;
+    }
+    __syncthreads();
+    // column totals, and their exclusive scan over the 256 digits (the first four waves)
+    uint32_t tot = 0u, inc = 0u;
+    if (t < 256) {
+        tot = s_part[0][d] + s_part[1][d] + s_part[2][d] + s_part[3][d];
+        inc = tot;
+        for (int dd = 1; dd < 64; dd <<= 1) {
+            const uint32_t o = shfl_up(inc, dd, lane);
+            if (lane >= dd) inc += o;
+        }
+        if (lane == 63) s4[wave] = inc;
+    }
+    __syncthreads();
+    if (t < 256) {
+        uint32_t before = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (k < wave) before += s4[k];
+        s_base[d] = before + inc - tot;
+        if (t == 0) s_total = s4[0] + s4[1] + s4[2] + s4[3];
+    }
+    __syncthreads();
+    const uint32_t total = s_total;
+    const uint32_t c256 = s_oor[0] + s_oor[1] + s_oor[2] + s_oor[3];
+    const uint32_t grand = total + c256;
+    const int one = __syncthreads_or((t < 256 && tot == grand) || c256 == grand);
+    if (t == 0) *ident = one ? 1u : 0u;
+    uint32_t run0 = s_base[d];
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+        if (k < q) run0 += s_part[k][d];
+    uint32_t* po = off + (int64_t)r0 * nb + d;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+        if (r0 + r < nr) po[0] = run0;
+        po += nb;
+        run0 += v[r];
+    }
+    if (extra && r0 + lane < nr) {
+        uint32_t ob = total;
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            if (k < q) ob += s_oor[k];
+        off[(int64_t)(r0 + lane) * nb + 256] = ob + winc - w;
+    }
+    if (valid && t == 0) {
+        valid[0] = total;
+        valid[1] = c256 == 0u ? 1u : 0u;   // no key out of range
+    }
+}
+
 // csum needs nb * nrb words, tot nb words (nb <= 257).  valid (first pass only): receives the
 // number of keys in range (the offset of the out-of-range bucket in chunk 0).  ident: 1 when
 // one bucket holds every key, else 0.
@@ -342,6 +439,10 @@ det_status hist_offsets(const uint16_t* hist, uint32_t* off, int64_t nrows, int 
     KernelTimer kt("k_hist_offsets", s);
     if (nrows <= kSmallHistRows) {
         k_hist_offsets_small<<<1, 256, 0, s>>>(hist, off, nrows, nb, valid, ident);
+        return launch_status();
+    }
+    if (nrows <= kMidHistRows) {
+        k_hist_offsets_mid<<<1, 1024, 0, s>>>(hist, off, nrows, nb, valid, ident);
         return launch_status();
     }
     const int rb = nrows <= 4096 ? kRowBlkFew : kRowBlk;

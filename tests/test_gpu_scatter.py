@@ -44,6 +44,9 @@ def rounding(shape, dtype, seed):
                                  (1 << 20, 1 << 20), (200000, 3), (2000003, 131073),
                                  (500009, (1 << 24) - 1), (500009, 1 << 24),
                                  (300007, (1 << 24) + 1),
+                                 # 256 and 257 chunks of 1024 keys: the last size whose
+                                 # bucket offsets take one launch, and the first that takes three
+                                 (1 << 18, 300), ((1 << 18) + 1, 300), (3 * 1024 + 5, 70001),
                                  # three passes with a short last chunk (f64: 4096 keys per
                                  # chunk, f32: 8192): destination offsets counted from either
                                  # end of a chunk, and from the end of a bucket
