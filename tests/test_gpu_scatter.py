@@ -251,6 +251,24 @@ def test_rows_long_destinations(dev, dtype, sizes, d):
     assert k == wk == 2 and bits_equal(prev, wprev)
 
 
+@pytest.mark.parametrize("dtype", [F32, F64])
+def test_rows_long_destinations_far_apart(dev, dtype):
+    # 2^20 destinations of 2 columns: the long-destination search walks them in rounds of
+    # 64 per wave, so long destinations sit in the first round, past 2^19 and at the end
+    B, d = 1 << 20, 2
+    rng = np.random.default_rng(17)
+    long_ones = {3: 100, 600_000: 130, 1_000_003: 64 * 9 + 1, B - 1: 700}
+    idx = np.concatenate([np.full(c, b, np.int32) for b, c in long_ones.items()]
+                         + [rng.integers(0, B, 3000).astype(np.int32)])
+    idx = idx[rng.permutation(idx.size)]
+    v = rounding((idx.size, d), dtype, 5)
+    o = rounding((B, d), dtype, 6)
+    got, _, k = gpu_scatter(v, idx, o, dev)
+    want, _, _ = oracle.scatter_add(v, idx, o)
+    assert bits_equal(got, want), first_mismatch(got, want)
+    assert k == 0
+
+
 def test_rows_c4_shape(dev):
     src, rows, out0 = workloads.rows_case()
     got, _, _ = gpu_scatter(src, rows, out0, dev)
