@@ -1604,6 +1604,66 @@ __device__ __forceinline__ void emit_scalar(T S, int64_t ps, uint32_t b, int64_t
     }
 }
 
+// Blocks longer than 32 values (s_big: position in the range, destination, the destination's
+// first and end positions), reduced by all four waves of the workgroup: each block is cut at
+// multiples of 1024 of its positions (aligned subtrees of its tree) and a wave takes one piece at
+// a time; then a thread per block combines the block's up to 8 piece values by the 8-leaf tree
+// (missing pieces are the identity), which is the block's PW, and stores it.  A range holding
+// one or two long blocks so keeps every wave loading, where a wave per block left two of four
+// idle for four rounds of loads each.
+constexpr int kPiece = 1024;
+constexpr int kMaxBig = kSegD / 32 + 2;
+constexpr int kMaxPieces = kMaxBig + 2 * (kSegD / kPiece);   // lengths sum to at most 2 kSegD
+
+template <typename T, bool NEG>
+__device__ __forceinline__ void reduce_big_blocks(const uint32_t (*s_big)[4], int nbig,
+                                                  int64_t lo, const T* __restrict__ V,
+                                                  T* __restrict__ out, T* __restrict__ pF,
+                                                  T* __restrict__ pC, uint16_t* s_piece,
+                                                  T* s_pval, uint32_t* s4, int tid, int lane,
+                                                  int wave) {
+    static_assert(kSegD / 33 + 1 <= 256, "a thread per block");
+    static_assert(kSegD / kPiece <= 8 && kMaxBig * 8 < 65536, "piece index in 16 bits");
+    int64_t ps = 0, seg_s = 0, seg_e = 0;
+    uint32_t b = 0, cnt = 0;
+    T o = T(0);
+    if (tid < nbig) {
+        ps = lo + s_big[tid][0];
+        b = s_big[tid][1];
+        seg_s = s_big[tid][2];
+        seg_e = s_big[tid][3];
+        const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
+        cnt = (uint32_t)cdiv(len, kPiece);
+        if (seg_e - seg_s <= kSegD) o = out[b];   // the old value, read before the pieces
+    }
+    uint32_t total;
+    const uint32_t first = block_excl_scan_u32(cnt, s4, &total);
+    for (uint32_t k = 0; k < cnt; ++k) s_piece[first + k] = (uint16_t)((tid << 3) | k);
+    __syncthreads();
+    for (int u = wave; u < (int)total; u += 4) {
+        const int h = s_piece[u] >> 3, k = s_piece[u] & 7;
+        const int64_t hp = lo + s_big[h][0];
+        const int64_t hlen = ((int64_t)s_big[h][3] - hp) < kSegD ? ((int64_t)s_big[h][3] - hp)
+                                                                  : kSegD;
+        const int64_t l = (hlen - (int64_t)k * kPiece) < kPiece ? (hlen - (int64_t)k * kPiece)
+                                                                : kPiece;
+        const T* v = V + hp + (int64_t)k * kPiece;
+        const T S = l <= 512 ? wave_pw_range<T, 2, NEG>(v, l, lane, false, ident<T>())
+                             : wave_pw_range<T, 4, NEG>(v, l, lane, false, ident<T>());
+        if (lane == 0) s_pval[u] = S;
+    }
+    __syncthreads();
+    if (tid < nbig) {
+        T a[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = k < (int)cnt ? s_pval[first + k] : ident<T>();
+        const T S = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+        if (seg_e - seg_s <= kSegD) out[b] = o + S;
+        else if (ps == seg_s) pF[ps / kSegD] = S;
+        else pC[ps / kSegD] = S;
+    }
+}
+
 // NEG: every value enters negated (scatter-subtract: the values are negated, then added in the
 // same order).
 template <typename T, typename KT, bool NEG>
@@ -1615,8 +1675,11 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const KT* __restrict__ K,
                                                        T* __restrict__ pC) {
     // blocks longer than 32 values, for the waves: position in the range, destination, and the
     // destination's first and end positions (read once, by the thread that found the block)
-    __shared__ uint32_t s_big[kSegD / 32 + 2][4];
+    __shared__ uint32_t s_big[kMaxBig][4];
     __shared__ uint32_t s_nbig;
+    __shared__ uint16_t s_piece[kMaxPieces];
+    __shared__ T s_pval[kMaxPieces];
+    __shared__ uint32_t s4[4];
     __shared__ KT s_key[kSegD];
     __shared__ uint32_t s_prev;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1678,26 +1741,8 @@ __global__ __launch_bounds__(256) void k_segred_scalar(const KT* __restrict__ K,
         }
     }
     __syncthreads();
-    const int nbig = (int)s_nbig;
-    for (int it = wave; it < nbig; it += 4) {
-        const int64_t ps = lo + s_big[it][0];
-        const uint32_t b = s_big[it][1];
-        const int64_t seg_s = s_big[it][2], seg_e = s_big[it][3];
-        const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
-        const bool single = seg_e - seg_s <= kSegD;
-        // the destination's old value is read alongside the block's values
-        const T o = single ? out[b] : T(0);
-        // the shortest padded width that holds the block (all give the same value)
-        T S;
-        if (len <= 512) S = wave_pw_range<T, 2, NEG>(V + ps, len, lane, false, ident<T>());
-        else if (len <= 2048) S = wave_pw_range<T, 8, NEG>(V + ps, len, lane, false, ident<T>());
-        else S = wave_pw_range<T, 32, NEG>(V + ps, len, lane, false, ident<T>());
-        if (lane == 0) {
-            if (single) out[b] = o + S;
-            else if (ps == seg_s) pF[ps / kSegD] = S;
-            else pC[ps / kSegD] = S;
-        }
-    }
+    reduce_big_blocks<T, NEG>(s_big, (int)s_nbig, lo, V, out, pF, pC, s_piece, s_pval, s4, tid,
+                              lane, wave);
 }
 
 // k_segred_scalar without keys (the byte path): the destinations meeting this range are
@@ -1712,8 +1757,11 @@ __global__ __launch_bounds__(256) void k_segred_off(const T* __restrict__ V,
                                                     const uint32_t* __restrict__ nvalid,
                                                     T* __restrict__ out, T* __restrict__ pF,
                                                     T* __restrict__ pC) {
-    __shared__ uint32_t s_big[kSegD / 32 + 2][4];
+    __shared__ uint32_t s_big[kMaxBig][4];
     __shared__ uint32_t s_nbig;
+    __shared__ uint16_t s_piece[kMaxPieces];
+    __shared__ T s_pval[kMaxPieces];
+    __shared__ uint32_t s4[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t m = *nvalid;
     const int64_t lo = (int64_t)blockIdx.x * kSegD;
@@ -1755,24 +1803,8 @@ __global__ __launch_bounds__(256) void k_segred_off(const T* __restrict__ V,
         if (!__syncthreads_or(more)) break;
     }
     __syncthreads();
-    const int nbig = (int)s_nbig;
-    for (int it = wave; it < nbig; it += 4) {
-        const int64_t ps = lo + s_big[it][0];
-        const uint32_t b = s_big[it][1];
-        const int64_t seg_s = s_big[it][2], seg_e = s_big[it][3];
-        const int64_t len = (seg_e - ps) < kSegD ? (seg_e - ps) : kSegD;
-        const bool single = seg_e - seg_s <= kSegD;
-        const T o = single ? out[b] : T(0);
-        T S;
-        if (len <= 512) S = wave_pw_range<T, 2, NEG>(V + ps, len, lane, false, ident<T>());
-        else if (len <= 2048) S = wave_pw_range<T, 8, NEG>(V + ps, len, lane, false, ident<T>());
-        else S = wave_pw_range<T, 32, NEG>(V + ps, len, lane, false, ident<T>());
-        if (lane == 0) {
-            if (single) out[b] = o + S;
-            else if (ps == seg_s) pF[ps / kSegD] = S;
-            else pC[ps / kSegD] = S;
-        }
-    }
+    reduce_big_blocks<T, NEG>(s_big, (int)s_nbig, lo, V, out, pF, pC, s_piece, s_pval, s4, tid,
+                              lane, wave);
 }
 
 // destinations with more than D members: PW over their block values, then apply
