@@ -1497,8 +1497,21 @@ __device__ __forceinline__ T wave_pw_range(const T* __restrict__ p, int64_t len,
             const int blk = (g0 + i) * 256;
             const T* q = p + blk + 4 * lane;
             const int rem = (int)((len - blk) < 256 ? (len - blk) : 256) - 4 * lane;
+            if (sizeof(T) == 4 && rem >= 4) {
+                // f32: the lane's 4 values by one 16-byte load (element-aligned only: the
+                // hardware takes unaligned vector accesses; f32 2^24 into 65,536 bins on MI355X
+                // 26.3 -> 18.5 us for the reduction, while f64's two 16-byte loads were no faster)
+                typedef T T4 __attribute__((ext_vector_type(4)));
+                T4 x;
+                __builtin_memcpy(&x, q, sizeof(T4));
+                a[i][0] = NEG ? -x.x : x.x;
+                a[i][1] = NEG ? -x.y : x.y;
+                a[i][2] = NEG ? -x.z : x.z;
+                a[i][3] = NEG ? -x.w : x.w;
+            } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a[i][r] = rem > r ? (NEG ? -q[r] : q[r]) : ident<T>();
+                for (int r = 0; r < 4; ++r) a[i][r] = rem > r ? (NEG ? -q[r] : q[r]) : ident<T>();
+            }
         }
 #pragma unroll
         for (int i = 0; i < G; ++i) {
@@ -1575,12 +1588,23 @@ __device__ __forceinline__ T wave_pw_long(const T* __restrict__ p, int64_t len, 
 // the identity, 5-level tree
 template <typename T, bool NEG = false>
 __device__ __forceinline__ T lane_pw_32(const T* __restrict__ v, int len) {
+    // whole groups of W values by one 16-byte load each (element-aligned only: the hardware
+    // takes unaligned vector accesses), the rest one by one
+    constexpr int W = 16 / (int)sizeof(T);
+    typedef T TW __attribute__((ext_vector_type(W)));
     T a[32];
 #pragma unroll
-    for (int q = 0; q < 32; ++q) a[q] = ident<T>();
+    for (int q = 0; q < 32; q += W) {
+        if (q + W <= len) {
+            TW x;
+            __builtin_memcpy(&x, v + q, 16);
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-        if (q < len) a[q] = NEG ? -v[q] : v[q];
+            for (int r = 0; r < W; ++r) a[q + r] = NEG ? -x[r] : x[r];
+        } else {
+#pragma unroll
+            for (int r = 0; r < W; ++r)
+                a[q + r] = q + r < len ? (NEG ? -v[q + r] : v[q + r]) : ident<T>();
+        }
     }
 #pragma unroll
     for (int w = 32; w > 1; w /= 2) {
