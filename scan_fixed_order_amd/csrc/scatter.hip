@@ -173,35 +173,41 @@ __device__ __forceinline__ bool count_digit(uint32_t* cnt, int d) {
 // Row blocks: 128 rows, or 16 when there are at most 4096 rows, so that few rows still make
 // many short workgroups (2^22 f32 values into 65,536 bins, 512 rows, on MI355X: the call 275 ->
 // 138 us; the single-workgroup kernel below walked 512 rows in 103 us per pass).
-constexpr int kRowBlk = 128;
+constexpr int kRowBlk = 64;
 constexpr int kRowBlkFew = 16;
 constexpr int kRowBatch = 16;   // rows whose loads are in flight together
 
-// csum[d * nrb + rb] = sum over the rows of block rb of column d (thread t: column t, and
-// thread 0 also column 256 when nb = 257)
+// csum[d * nrb + rb] = sum over the rows of block rb of column d (thread t: column t; column
+// 256, when nb = 257, a row per thread and a block sum).  Whole batches of rows load without a
+// per-row test.
 __global__ __launch_bounds__(256) void k_hist_colsums(const uint16_t* __restrict__ hist,
                                                       int64_t nrows, int nb, int64_t nrb, int rb,
                                                       uint32_t* __restrict__ csum) {
+    static_assert(kRowBlk <= 256 && kRowBlkFew <= 256, "column 256: a row per thread");
+    __shared__ uint32_t s4[4];
     const int t = threadIdx.x;
-    const bool extra = nb > 256 && t == 0;
     const int64_t r0 = (int64_t)blockIdx.x * rb;
     const int64_t r1 = (r0 + rb < nrows) ? r0 + rb : nrows;
-    uint32_t s0 = 0, s1 = 0;
-    for (int64_t r = r0; r < r1; r += kRowBatch) {
-        uint32_t v[kRowBatch], w[kRowBatch];
+    uint32_t s0 = 0;
+    const uint16_t* hp = hist + r0 * nb + t;
+    for (int64_t r = r0; r < r1; r += kRowBatch, hp += (int64_t)kRowBatch * nb) {
+        uint32_t v[kRowBatch];
+        if (r + kRowBatch <= r1) {
 #pragma unroll
-        for (int k = 0; k < kRowBatch; ++k) {
-            v[k] = (r + k < r1) ? hist[(r + k) * nb + t] : 0u;
-            w[k] = (extra && r + k < r1) ? hist[(r + k) * nb + 256] : 0u;
+            for (int k = 0; k < kRowBatch; ++k) v[k] = hp[(int64_t)k * nb];
+        } else {
+#pragma unroll
+            for (int k = 0; k < kRowBatch; ++k) v[k] = r + k < r1 ? hp[(int64_t)k * nb] : 0u;
         }
 #pragma unroll
-        for (int k = 0; k < kRowBatch; ++k) {
-            s0 += v[k];
-            s1 += w[k];
-        }
+        for (int k = 0; k < kRowBatch; ++k) s0 += v[k];
     }
     csum[(int64_t)t * nrb + blockIdx.x] = s0;
-    if (extra) csum[(int64_t)256 * nrb + blockIdx.x] = s1;
+    if (nb > 256) {
+        const uint32_t w = t < r1 - r0 ? (uint32_t)hist[(r0 + t) * nb + 256] : 0u;
+        const uint32_t s1 = block_sum_u32(w, s4);
+        if (t == 0) csum[(int64_t)256 * nrb + blockIdx.x] = s1;
+    }
 }
 
 // column d = blockIdx.x: exclusive scan of its block sums in place; tot[d] = the column total
@@ -223,9 +229,9 @@ __global__ __launch_bounds__(256) void k_hist_colscan(uint32_t* __restrict__ csu
 
 // tot[d] = the keys of digit d (column totals).  Each workgroup turns them into the digit
 // bases (keys with a digit below d; d = 256, the out-of-range bucket, after every digit) and
-// writes its row block's offsets.  Workgroup 0 also sets *ident = 1 when one bucket holds
-// every key (the pass is then the identity permutation), else 0, and *valid (if given) = the
-// keys in range (the base of bucket 256).
+// writes its row block's offsets (column 256: a row per thread, a block scan).  Workgroup 0
+// also sets *ident = 1 when one bucket holds every key (the pass is then the identity
+// permutation), else 0, and *valid (if given) = the keys in range (the base of bucket 256).
 __global__ __launch_bounds__(256) void k_hist_apply(const uint16_t* __restrict__ hist,
                                                     uint32_t* __restrict__ off, int64_t nrows,
                                                     int nb, int64_t nrb, int rb,
@@ -235,7 +241,6 @@ __global__ __launch_bounds__(256) void k_hist_apply(const uint16_t* __restrict__
                                                     uint32_t* __restrict__ valid) {
     __shared__ uint32_t s4[4];
     const int t = threadIdx.x;
-    const bool extra = nb > 256 && t == 0;
     const uint32_t v = tot[t];
     const uint32_t v256 = nb > 256 ? tot[256] : 0u;
     uint32_t total;
@@ -250,23 +255,35 @@ __global__ __launch_bounds__(256) void k_hist_apply(const uint16_t* __restrict__
     }
     const int64_t r0 = (int64_t)blockIdx.x * rb;
     const int64_t r1 = (r0 + rb < nrows) ? r0 + rb : nrows;
+    if (nb > 256) {
+        const bool in = t < r1 - r0;
+        const uint32_t w = in ? (uint32_t)hist[(r0 + t) * nb + 256] : 0u;
+        uint32_t wt;
+        const uint32_t ex = block_excl_scan_u32(w, s4, &wt);
+        if (in) off[(r0 + t) * nb + 256] = total + csum[(int64_t)256 * nrb + blockIdx.x] + ex;
+    }
     uint32_t run0 = base + csum[(int64_t)t * nrb + blockIdx.x];
-    uint32_t run1 = extra ? total + csum[(int64_t)256 * nrb + blockIdx.x] : 0u;
-    for (int64_t r = r0; r < r1; r += kRowBatch) {
-        uint32_t v[kRowBatch], w[kRowBatch];
+    const uint16_t* hp = hist + r0 * nb + t;
+    uint32_t* op = off + r0 * nb + t;
+    for (int64_t r = r0; r < r1;
+         r += kRowBatch, hp += (int64_t)kRowBatch * nb, op += (int64_t)kRowBatch * nb) {
+        uint32_t v[kRowBatch];
+        if (r + kRowBatch <= r1) {
 #pragma unroll
-        for (int k = 0; k < kRowBatch; ++k) {
-            v[k] = (r + k < r1) ? hist[(r + k) * nb + t] : 0u;
-            w[k] = (extra && r + k < r1) ? hist[(r + k) * nb + 256] : 0u;
-        }
+            for (int k = 0; k < kRowBatch; ++k) v[k] = hp[(int64_t)k * nb];
 #pragma unroll
-        for (int k = 0; k < kRowBatch; ++k) {
-            if (r + k < r1) {
-                off[(r + k) * nb + t] = run0;
-                if (extra) off[(r + k) * nb + 256] = run1;
+            for (int k = 0; k < kRowBatch; ++k) {
+                op[(int64_t)k * nb] = run0;
+                run0 += v[k];
             }
-            run0 += v[k];
-            run1 += w[k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < kRowBatch; ++k) v[k] = r + k < r1 ? hp[(int64_t)k * nb] : 0u;
+#pragma unroll
+            for (int k = 0; k < kRowBatch; ++k) {
+                if (r + k < r1) op[(int64_t)k * nb] = run0;
+                run0 += v[k];
+            }
         }
     }
 }
