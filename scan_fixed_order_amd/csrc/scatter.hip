@@ -2112,6 +2112,35 @@ __global__ __launch_bounds__(256) void k_group_gather1(const T* __restrict__ val
         G[sp] = sp < m ? values[src[sp]] : T(0.0);
 }
 
+// The scalar f32 running prev sorts 8-byte payloads, an f32 value's bits above its source
+// index, so the grouped values come out of the sort in order instead of through a gather of
+// random reads by the sorted indices.
+__global__ __launch_bounds__(256) void k_pack_value_index(const uint32_t* __restrict__ vbits,
+                                                          int64_t n, uint64_t* __restrict__ pk) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        pk[i] = ((uint64_t)vbits[i] << 32) | (uint64_t)i;
+}
+
+// G[s] = the value and src[s] = the source index of sorted position s < nvalid; G = +0.0 past
+// them (as k_group_gather1).
+__global__ __launch_bounds__(256) void k_unpack_value_index(const uint64_t* __restrict__ SP,
+                                                            const uint32_t* __restrict__ nvalid,
+                                                            int64_t n, float* __restrict__ G,
+                                                            uint32_t* __restrict__ src) {
+    const int64_t m = *nvalid;
+    for (int64_t sp = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; sp < n;
+         sp += (int64_t)gridDim.x * blockDim.x) {
+        if (sp < m) {
+            const uint64_t v = SP[sp];
+            G[sp] = __uint_as_float((uint32_t)(v >> 32));
+            src[sp] = (uint32_t)v;
+        } else {
+            G[sp] = 0.0f;
+        }
+    }
+}
+
 // Scalar destinations: prev[src[s]] = out[r] at r's first position, else out[r] + E[s].
 template <typename T>
 __global__ __launch_bounds__(256) void k_running_prev1(const uint32_t* __restrict__ K,
@@ -2202,11 +2231,13 @@ struct SLayout {
 };
 
 // idx_payload: the sort carries source indices (4 bytes) even for scalar destinations
+// idx_payload: the sort carries source indices (rows, the running prev); packed: 8-byte
+// payloads of an f32 value and its source index (the scalar f32 running prev).
 SLayout slayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt,
-                bool idx_payload = false) {
+                bool idx_payload = false, bool packed = false) {
     SLayout L;
     const bool rows = row_len > 1;
-    const size_t pw = (rows || idx_payload) ? 4 : dtype_size(dt);    // payload bytes
+    const size_t pw = packed ? 8 : (rows || idx_payload) ? 4 : dtype_size(dt);   // payload bytes
     L.H = n <= kSmallN ? kChunkSmall : (pw == 4 ? kChunkBig<uint32_t> : kChunkBig<uint64_t>);
     L.nchunks = cdiv(n > 0 ? n : 1, L.H);
     L.wide = !rows && !idx_payload && dt == DET_F64 && num_out > 65536 &&
@@ -2617,9 +2648,17 @@ struct RLayout {
     size_t o64, G, E, sws, cagg, total;
 };
 
+// The scalar f32 running prev above 2^21 members sorts 8-byte payloads (value and source index)
+// instead of gathering the values through the sorted indices (MI355X, f32 into 65,536 bins:
+// 2^24 members 1.04 -> 0.90 ms; 2^22 into 2^20 bins 0.41 -> 0.38 ms; 2^20 members 111 ->
+// 117 us, the packing launch not paid back).
+inline bool running_packed(int64_t n, int64_t row_len, det_dtype dt) {
+    return row_len == 1 && dt == DET_F32 && n > ((int64_t)1 << 21);
+}
+
 RLayout rlayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
     RLayout R;
-    R.S = slayout(n, num_out, row_len, dt, true);
+    R.S = slayout(n, num_out, row_len, dt, true, running_packed(n, row_len, dt));
     size_t o = R.S.total;
     auto take = [&](size_t bytes) {
         const size_t at = o;
@@ -2651,8 +2690,32 @@ det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n
     uint32_t* off = reinterpret_cast<uint32_t*>(ws + L.off);
     const uint32_t* K = nullptr;
     const uint32_t* SRC = nullptr;
-    det_status st = sort_by_dest<uint32_t, true>(index, nullptr, n, num_out, L, ws, false, s, &K,
-                                                 &SRC);
+    T* G = reinterpret_cast<T*>(ws + R.G);
+    T* E = reinterpret_cast<T*>(ws + R.E);
+    int64_t g1 = cdiv(n, 256);
+    if (g1 > 16384) g1 = 16384;
+    // value and source index travel through the sort together (scalar f32, large n)
+    const bool packed = running_packed(n, row_len, dt);
+    det_status st;
+    if (packed) {
+        // the packed input lives in G's and E's space (8 bytes per member, free until the
+        // sort's first pass has read it)
+        uint64_t* pk = reinterpret_cast<uint64_t*>(ws + R.G);
+        k_pack_value_index<<<dim3((unsigned)g1), dim3(256), 0, s>>>(
+            reinterpret_cast<const uint32_t*>(values), n, pk);
+        const uint64_t* SP = nullptr;
+        st = sort_by_dest<uint64_t, false>(index, pk, n, num_out, L, ws, false, s, &K, &SP);
+        if (st != DET_SUCCESS) return st;
+        // the source indices into the payload buffer the sort did not end in
+        uint32_t* src = reinterpret_cast<uint32_t*>(
+            reinterpret_cast<const char*>(SP) == ws + L.payA ? ws + L.payB : ws + L.payA);
+        KernelTimer kt("k_group_gather", s);
+        k_unpack_value_index<<<dim3((unsigned)g1), dim3(256), 0, s>>>(
+            SP, ctrl, n, reinterpret_cast<float*>(G), src);
+        SRC = src;
+    } else {
+        st = sort_by_dest<uint32_t, true>(index, nullptr, n, num_out, L, ws, false, s, &K, &SRC);
+    }
     if (st != DET_SUCCESS) return st;
     {
         int64_t g = cdiv(num_out + 1, 256);
@@ -2662,17 +2725,13 @@ det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n
                                                                          n_skipped, nullptr, 0);
     }
     int64_t* o64 = reinterpret_cast<int64_t*>(ws + R.o64);
-    T* G = reinterpret_cast<T*>(ws + R.G);
-    T* E = reinterpret_cast<T*>(ws + R.E);
     {
         int64_t g = cdiv(num_out + 2, 256);
         if (g > 4096) g = 4096;
         k_offsets64<<<dim3((unsigned)g), dim3(256), 0, s>>>(off, num_out, n, o64);
     }
     const dim3 tg((unsigned)cdiv(n, 64), (unsigned)cdiv(row_len, 32));
-    int64_t g1 = cdiv(n, 256);
-    if (g1 > 16384) g1 = 16384;
-    {
+    if (!packed) {
         KernelTimer kt("k_group_gather", s);
         if (row_len == 1)
             k_group_gather1<T><<<dim3((unsigned)g1), dim3(256), 0, s>>>(values, SRC, ctrl, n, G);

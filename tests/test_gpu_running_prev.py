@@ -52,7 +52,10 @@ def run_case(dev, dtype, n, B, d, seed, lo=-3, contended=False):
 
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 @pytest.mark.parametrize("n,B", [(1, 1), (1000, 7), (300007, 4099), (70001, 70000),
-                                 (2 * 256 * 8192 + 777, 65536)])
+                                 (2 * 256 * 8192 + 777, 65536),
+                                 # either side of the size from which f32 values travel
+                                 # through the sort beside their source indices
+                                 (1 << 21, 3), ((1 << 21) + 1, 3), ((1 << 21) + 7, 1 << 20)])
 def test_scalar_parity(dev, dtype, n, B):
     run_case(dev, dtype, n, B, 1, seed=n % 1000 + B)
 
