@@ -2159,6 +2159,81 @@ __global__ __launch_bounds__(256) void k_running_prev1(const uint32_t* __restric
     }
 }
 
+// The packed path's prev values, in sorted order, as (value bits above the source index)
+// pairs keyed by the source's window (index >> wbits), so that a radix pass on the key groups
+// the writes by window; positions past nvalid get a key past every window.  Windows of 2^wbits
+// sources, about 256 of them (one radix pass, and a workgroup per window), at most 2^16.
+constexpr int kPrevPart = 32768;   // sources per LDS pass of the window write (128 KB of f32)
+inline int prev_window_bits(int64_t n) {
+    int bits = 0;
+    while (bits < 32 && ((n - 1) >> bits)) ++bits;
+    const int w = bits - 8;
+    return w < 10 ? 10 : w > 16 ? 16 : w;
+}
+__global__ __launch_bounds__(256) void k_running_prev1_pairs(const uint32_t* __restrict__ K,
+                                                             const uint32_t* __restrict__ src,
+                                                             const uint32_t* __restrict__ off,
+                                                             const uint32_t* __restrict__ nvalid,
+                                                             const float* __restrict__ E,
+                                                             const float* __restrict__ out,
+                                                             int64_t n, int wbits,
+                                                             uint32_t* __restrict__ key2,
+                                                             uint64_t* __restrict__ pair2) {
+    const int64_t m = *nvalid;
+    for (int64_t sp = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; sp < n;
+         sp += (int64_t)gridDim.x * blockDim.x) {
+        if (sp < m) {
+            const uint32_t r = K[sp];
+            const float init = out[r];
+            const float v = off[r] == (uint32_t)sp ? init : init + E[sp];
+            const uint32_t i = src[sp];
+            pair2[sp] = ((uint64_t)__float_as_uint(v) << 32) | (uint64_t)i;
+            key2[sp] = i >> wbits;
+        } else {
+            key2[sp] = 0xffffffffu;
+        }
+    }
+}
+
+// prev[i] = v for the (v, i) pairs of window w = blockIdx.x (positions wstart[w] ..
+// wstart[w + 1] of the pairs sorted by window), kPrevPart sources at a time: the part's values
+// go to a copy in LDS, with a bit per source written, and the part goes out with contiguous
+// stores of the written sources (a window of 2^16 sources takes two parts, the second reading
+// the window's pairs again, from cache).  Each source has at most one pair, so the order of
+// the writes does not matter.
+__global__ __launch_bounds__(1024) void k_write_prev_window(const uint64_t* __restrict__ SP,
+                                                            const uint32_t* __restrict__ wstart,
+                                                            int64_t n, int wbits,
+                                                            float* __restrict__ prev) {
+    __shared__ float s_v[kPrevPart];
+    __shared__ uint32_t s_bits[kPrevPart / 32];
+    const int t = threadIdx.x;
+    const int64_t w = blockIdx.x;
+    const int64_t a = wstart[w], b = wstart[w + 1];
+    const uint32_t wmask = (1u << wbits) - 1u;
+    const int parts = wbits > 15 ? 1 << (wbits - 15) : 1;
+    const int psize = wbits > 15 ? kPrevPart : 1 << wbits;
+    for (int part = 0; part < parts; ++part) {
+        for (int i = t; i < psize / 32; i += 1024) s_bits[i] = 0u;
+        __syncthreads();
+        for (int64_t sp = a + t; sp < b; sp += 1024) {
+            const uint64_t v = SP[sp];
+            const uint32_t i = (uint32_t)v & wmask;
+            if ((int)(i / (uint32_t)psize) == part) {
+                const uint32_t j = i % (uint32_t)psize;
+                s_v[j] = __uint_as_float((uint32_t)(v >> 32));
+                atomicOr(&s_bits[j >> 5], 1u << (j & 31u));
+            }
+        }
+        __syncthreads();
+        const int64_t base = (w << wbits) + (int64_t)part * psize;
+        for (int i = t; i < psize; i += 1024) {
+            if (base + i < n && ((s_bits[i >> 5] >> (i & 31)) & 1u)) prev[base + i] = s_v[i];
+        }
+        __syncthreads();   // the next part reuses the LDS copy
+    }
+}
+
 // Offsets of the grouped array as the segmented scan takes them: o[b] = off[b] for b <= B
 // (destination b's members start at off[b]; off[B] = nvalid) and o[B + 1] = n (the skipped
 // sources, one more segment).
@@ -2645,7 +2720,7 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
 // values, and then out reduced exactly as det_scatter_add reduces it.
 struct RLayout {
     SLayout S;
-    size_t o64, G, E, sws, cagg, total;
+    size_t o64, G, E, sws, cagg, key2, pair2, wstart, total;
 };
 
 // The scalar f32 running prev above 2^21 members sorts 8-byte payloads (value and source index)
@@ -2671,6 +2746,11 @@ RLayout rlayout(int64_t n, int64_t num_out, int64_t row_len, det_dtype dt) {
     R.E = take(cells);
     R.sws = take(scan_workspace(n > 0 ? n : 1, dt, DET_SCAN_EXCLUSIVE, num_out + 1));
     R.cagg = take(scan_columns_agg_bytes(n > 0 ? n : 1, row_len));
+    // the packed path's (value, source) pairs and their window keys, for the bucketed write
+    const bool pk = running_packed(n, row_len, dt);
+    R.key2 = take(pk ? (size_t)n * 4 : 4);
+    R.pair2 = take(pk ? (size_t)n * 8 : 8);
+    R.wstart = take(pk ? (size_t)(cdiv(n, (int64_t)1 << prev_window_bits(n)) + 1) * 4 : 4);
     R.total = o;
     return R;
 }
@@ -2747,7 +2827,12 @@ det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n
     if (st != DET_SUCCESS) return st;
     {
         KernelTimer kt("k_running_prev", s);
-        if (row_len == 1)
+        if (packed)
+            k_running_prev1_pairs<<<dim3((unsigned)g1), dim3(256), 0, s>>>(
+                K, SRC, off, ctrl, reinterpret_cast<const float*>(E),
+                reinterpret_cast<const float*>(out), n, prev_window_bits(n),
+                reinterpret_cast<uint32_t*>(ws + R.key2), reinterpret_cast<uint64_t*>(ws + R.pair2));
+        else if (row_len == 1)
             k_running_prev1<T><<<dim3((unsigned)g1), dim3(256), 0, s>>>(K, SRC, off, ctrl, E, out,
                                                                         prev);
         else
@@ -2767,6 +2852,28 @@ det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n
         int64_t lg = cdiv(num_out, 64 * 4);
         if (lg > 4096) lg = 4096;
         k_segred_scalar_long<T><<<dim3((unsigned)lg), dim3(256), 0, s>>>(off, num_out, pF, pC, out);
+        if (packed) {
+            // the prev writes grouped by window: one radix pass on the window keys (the sort's
+            // buffers are free once the reduction has read them), then the writes
+            const uint32_t* K2 = nullptr;
+            const uint64_t* SP2 = nullptr;
+            const int wbits = prev_window_bits(n);
+            const int64_t nwin = cdiv(n, (int64_t)1 << wbits);
+            st = sort_by_dest<uint64_t, false>(
+                reinterpret_cast<const int32_t*>(ws + R.key2),
+                reinterpret_cast<const uint64_t*>(ws + R.pair2), n, nwin, L, ws, false, s, &K2,
+                &SP2);
+            if (st != DET_SUCCESS) return st;
+            // each window's first position among the sorted pairs (the pass's bucket starts,
+            // row 0 of its offsets, narrow the search), then a workgroup per window
+            uint32_t* wstart = reinterpret_cast<uint32_t*>(ws + R.wstart);
+            k_bin_offsets<uint32_t><<<dim3((unsigned)cdiv(nwin + 1, 256)), dim3(256), 0, s>>>(
+                K2, ctrl, nwin, n, wstart, nullptr,
+                reinterpret_cast<const uint32_t*>(ws + L.hist), key_passes(nwin));
+            KernelTimer kt("k_write_prev_window", s);
+            k_write_prev_window<<<dim3((unsigned)nwin), dim3(1024), 0, s>>>(
+                SP2, wstart, n, wbits, reinterpret_cast<float*>(prev));
+        }
     } else {
         {
             KernelTimer kt("k_segred_rows", s);

@@ -55,7 +55,10 @@ def run_case(dev, dtype, n, B, d, seed, lo=-3, contended=False):
                                  (2 * 256 * 8192 + 777, 65536),
                                  # either side of the size from which f32 values travel
                                  # through the sort beside their source indices
-                                 (1 << 21, 3), ((1 << 21) + 1, 3), ((1 << 21) + 7, 1 << 20)])
+                                 (1 << 21, 3), ((1 << 21) + 1, 3), ((1 << 21) + 7, 1 << 20),
+                                 # the prev writes through windows of 2^16 sources written in
+                                 # two parts, 256 windows and 257 (two radix passes over them)
+                                 (1 << 24, 65536), ((1 << 24) + 3, 70001)])
 def test_scalar_parity(dev, dtype, n, B):
     run_case(dev, dtype, n, B, 1, seed=n % 1000 + B)
 
