@@ -2789,7 +2789,7 @@ det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n
         // the source indices into the payload buffer the sort did not end in
         uint32_t* src = reinterpret_cast<uint32_t*>(
             reinterpret_cast<const char*>(SP) == ws + L.payA ? ws + L.payB : ws + L.payA);
-        KernelTimer kt("k_group_gather", s);
+        KernelTimer kt("k_unpack_value_index", s);
         k_unpack_value_index<<<dim3((unsigned)g1), dim3(256), 0, s>>>(
             SP, ctrl, n, reinterpret_cast<float*>(G), src);
         SRC = src;
