@@ -1310,8 +1310,25 @@ __global__ __launch_bounds__(256) void k_bin_offsets_bytes(
     cnt[h] = 0u;
     __syncthreads();
     const int64_t c = pos / H;
-    if (pos < m)
-        for (int64_t q = c * H + h; q < pos; q += 256) count_digit(cnt, (int)(hb[q] & 255u));
+    if (pos < m) {
+        // the keys of [c H, pos), four 8-bit or two 16-bit keys to a 32-bit word (chunk starts
+        // are multiples of H, so the words are aligned), every word of a thread loaded before
+        // any is counted; the last word may reach past pos, inside the key array
+        constexpr int KPW = 4 / (int)sizeof(KH);
+        constexpr int MAXW = kChunkBig<uint32_t> / KPW / 256;   // H is at most 8192
+        const int nk = (int)(pos - c * H);
+        const int nw = (nk + KPW - 1) / KPW;
+        const uint32_t* hw = reinterpret_cast<const uint32_t*>(hb + c * H);
+        uint32_t x[MAXW];
+#pragma unroll
+        for (int k = 0; k < MAXW; ++k) x[k] = k * 256 + h < nw ? hw[k * 256 + h] : 0u;
+#pragma unroll
+        for (int k = 0; k < MAXW; ++k)
+#pragma unroll
+            for (int j = 0; j < KPW; ++j)
+                if (KPW * (k * 256 + h) + j < nk)
+                    count_digit(cnt, (int)((x[k] >> (32 / KPW * j)) & 255u));
+    }
     __syncthreads();
     const int64_t b = (int64_t)h * 256 + l;
     if (b < B) {
@@ -1348,9 +1365,23 @@ __global__ __launch_bounds__(256) void k_bin_offsets_w(const uint32_t* __restric
     for (int j = 0; j < 4; ++j) cnt[t + 256 * j] = 0u;
     __syncthreads();
     const int64_t c = pos / H;
-    if (pos < m)
-        for (int64_t q = c * H + t; q < pos; q += 256)
-            count_digit(cnt, (int)(hb[q] & (uint32_t)(kWideB - 1)));
+    if (pos < m) {
+        // the 16-bit keys of [c H, pos), two to a 32-bit word, every word of a thread loaded
+        // before any is counted (as k_bin_offsets_bytes)
+        constexpr int MAXW = kWideCH / 2 / 256;
+        const int nk = (int)(pos - c * H);
+        const int nw = (nk + 1) / 2;
+        const uint32_t* hw = reinterpret_cast<const uint32_t*>(hb + c * H);
+        uint32_t x[MAXW];
+#pragma unroll
+        for (int k = 0; k < MAXW; ++k) x[k] = k * 256 + t < nw ? hw[k * 256 + t] : 0u;
+#pragma unroll
+        for (int k = 0; k < MAXW; ++k)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (2 * (k * 256 + t) + j < nk)
+                    count_digit(cnt, (int)((x[k] >> (16 * j)) & (uint32_t)(kWideB - 1)));
+    }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
