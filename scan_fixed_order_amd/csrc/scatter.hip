@@ -1970,17 +1970,25 @@ __global__ __launch_bounds__(256) void k_segred_rows(const uint32_t* __restrict_
     }
     __syncthreads();
     const int nitem = (int)s_nitem;
-    for (int it = wave; it < nitem; it += 4) {
+    // block it: its first position, length, source rows, and where its value goes (added to
+    // the destination row when the destination has at most kRowD members, else a partial)
+    auto block = [&](int it, int& len, const uint32_t*& rows, T*& dst, bool& single) {
         const int64_t ps = s_item[it];
         const uint32_t b = s_K[ps - lo];
         const int64_t seg_s = s_seg[it][0], seg_e = s_seg[it][1];
-        const int len = (int)((seg_e - ps) < kRowD ? (seg_e - ps) : kRowD);
-        const uint32_t* rows = s_R + (ps - lo);   // ps - lo + len <= 2 kRowD
-        T* dst;
-        if (seg_e - seg_s <= kRowD) dst = out + (int64_t)b * d;
+        len = (int)((seg_e - ps) < kRowD ? (seg_e - ps) : kRowD);
+        rows = s_R + (ps - lo);   // ps - lo + len <= 2 kRowD
+        single = seg_e - seg_s <= kRowD;
+        if (single) dst = out + (int64_t)b * d;
         else if (ps == seg_s) dst = pF + (ps / kRowD) * d;
         else dst = pC + (ps / kRowD) * d;
-        const bool single = seg_e - seg_s <= kRowD;
+    };
+    auto reduce_block = [&](int it) {
+        int len;
+        const uint32_t* rows;
+        T* dst;
+        bool single;
+        block(it, len, rows, dst, single);
         for (int64_t c0 = 0; c0 < d; c0 += 64 * CPL) {
             // PW over the 64 rank positions of the block (identity past len): 8 groups of 8
             // rows, each a 3-level tree, then a 3-level tree over the group values
@@ -2021,7 +2029,55 @@ __global__ __launch_bounds__(256) void k_segred_rows(const uint32_t* __restrict_
                 if (col < d) dst[col] = single ? dst[col] + r : r;
             }
         }
+    };
+    int it = wave;
+    // two blocks of at most 8 rows each (a few members per destination, the usual case) with
+    // the loads of both, and the destination rows they add to, in flight together; a block of
+    // at most 8 rows has the value of its first group (the other groups are the identity)
+    for (; it + 4 < nitem; it += 8) {
+        int la, lb;
+        const uint32_t *ra, *rb;
+        T *da, *db;
+        bool sa, sb;
+        block(it, la, ra, da, sa);
+        block(it + 4, lb, rb, db, sb);
+        if (la > 8 || lb > 8 || d > 64 * CPL) {
+            reduce_block(it);
+            reduce_block(it + 4);
+            continue;
+        }
+        T va[8][CPL], vb[8][CPL], oa[CPL], ob[CPL];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const T* rowa = src + (int64_t)ra[r < la ? r : 0] * d;
+            const T* rowb = src + (int64_t)rb[r < lb ? r : 0] * d;
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const int col = cc * 64 + lane;
+                va[r][cc] = (r < la && col < d) ? (NEG ? -rowa[col] : rowa[col]) : ident<T>();
+                vb[r][cc] = (r < lb && col < d) ? (NEG ? -rowb[col] : rowb[col]) : ident<T>();
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const int col = cc * 64 + lane;
+            oa[cc] = (sa && col < d) ? da[col] : T(0);
+            ob[cc] = (sb && col < d) ? db[col] : T(0);
+        }
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const int col = cc * 64 + lane;
+            const T xa = ((va[0][cc] + va[1][cc]) + (va[2][cc] + va[3][cc])) +
+                         ((va[4][cc] + va[5][cc]) + (va[6][cc] + va[7][cc]));
+            const T xb = ((vb[0][cc] + vb[1][cc]) + (vb[2][cc] + vb[3][cc])) +
+                         ((vb[4][cc] + vb[5][cc]) + (vb[6][cc] + vb[7][cc]));
+            if (col < d) {
+                da[col] = sa ? oa[cc] + xa : xa;
+                db[col] = sb ? ob[cc] + xb : xb;
+            }
+        }
     }
+    if (it < nitem) reduce_block(it);
 }
 
 // rows of destinations with more than 64 members: PW over their block rows per column.  A wave
