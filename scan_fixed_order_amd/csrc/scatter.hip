@@ -1253,8 +1253,9 @@ __global__ __launch_bounds__(256) void k_radix_scatter_w(
 // off[b] = first sorted position with key >= b, for b in [0, B]; n_skipped = n - valid.
 // row0: the last radix pass's bucket starts (row 0 of its offsets), or null.  With one pass
 // (destinations below 256: every key is one bucket) they are the answer; with two passes over
-// 16-bit keys the keys of high byte h lie in that pass's bucket h, so the search for b stays
-// inside bucket b >> 8 (f32 2^28 into 65,536 bins on MI355X: 31 -> 18 us).
+// keys below 2^16 (16- or 32-bit) the keys of high byte h lie in that pass's bucket h, so the
+// search for b stays inside bucket b >> 8 (f32 2^28 into 65,536 bins on MI355X: 31 -> 18 us);
+// with more passes the whole array is searched.
 template <typename KT>
 __global__ __launch_bounds__(256) void k_bin_offsets(const KT* __restrict__ K,
                                                      const uint32_t* __restrict__ nvalid,
@@ -2759,9 +2760,8 @@ det_status scatter_impl(const T* values, const int32_t* index, int64_t n, int64_
             k_bin_offsets<uint16_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(
                 K16, ctrl, num_out, n, off, n_skipped, row0, passes);
         else
-            k_bin_offsets<uint32_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(K, ctrl, num_out, n,
-                                                                             off, n_skipped,
-                                                                             nullptr, 0);
+            k_bin_offsets<uint32_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(
+                K, ctrl, num_out, n, off, n_skipped, row0, passes);
     }
     T* pF = reinterpret_cast<T*>(ws + L.pF);
     T* pC = reinterpret_cast<T*>(ws + L.pC);
@@ -2888,8 +2888,10 @@ det_status scatter_running_impl(const T* values, const int32_t* index, int64_t n
         int64_t g = cdiv(num_out + 1, 256);
         if (g > 8192) g = 8192;
         KernelTimer kt("k_bin_offsets", s);
-        k_bin_offsets<uint32_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(K, ctrl, num_out, n, off,
-                                                                         n_skipped, nullptr, 0);
+        // the last pass's bucket starts (row 0 of its offsets) narrow each search
+        k_bin_offsets<uint32_t><<<dim3((unsigned)g), dim3(256), 0, s>>>(
+            K, ctrl, num_out, n, off, n_skipped, reinterpret_cast<const uint32_t*>(ws + L.hist),
+            key_passes(num_out));
     }
     int64_t* o64 = reinterpret_cast<int64_t*>(ws + R.o64);
     {
