@@ -83,6 +83,35 @@ def test_rows_accumulate_shape(dev):
 
 
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_special_values_above_the_packing_size(dev, dtype):
+    # f32 values travel through the sort as bits beside their source indices above 2^21
+    # members: NaN, infinities, signed zeros and subnormals must come out bit for bit, and
+    # skipped sources keep their prev untouched
+    rng = np.random.default_rng(23)
+    n, B = (1 << 21) + 9, 5000
+    v = spread(rng, n, dtype)
+    tiny = np.finfo(dtype).smallest_subnormal
+    special = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0, tiny, -tiny], dtype)
+    pos = rng.choice(n, 7000, replace=False)
+    v[pos] = special[rng.integers(0, special.size, pos.size)]
+    idx = rng.integers(-2, B + 2, n).astype(np.int32)
+    o = spread(rng, B, dtype)
+    print(f"[case] running prev special values dtype={np.dtype(dtype).name} n={n}", flush=True)
+    want_out, want_prev, want_k = oracle.scatter_add_running(v, idx, o)
+    tv, ti, to = (torch.from_numpy(a).to(dev) for a in (v, idx, o))
+    tp = torch.full((n,), 7.0, dtype=tv.dtype, device=dev)
+    nk = torch.full((1,), -1, dtype=torch.int64, device=dev)
+    det.det_scatter_add_running(tv, ti, to, prev=tp, n_skipped=nk)
+    got_prev = tp.cpu().numpy()
+    skipped = (idx < 0) | (idx >= B)
+    assert (got_prev[skipped] == 7.0).all()
+    assert bits_equal(got_prev[~skipped], want_prev[~skipped]), \
+        first_mismatch(got_prev[~skipped], want_prev[~skipped])
+    assert bits_equal(to.cpu().numpy(), want_out)
+    assert int(nk.item()) == want_k == int(skipped.sum())
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_all_skipped_and_empty(dev, dtype):
     tdt = torch.float32 if dtype == np.float32 else torch.float64
     v = torch.ones(50, dtype=tdt, device=dev)

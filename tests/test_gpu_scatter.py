@@ -269,6 +269,29 @@ def test_rows_long_destinations_far_apart(dev, dtype):
     assert k == 0
 
 
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("d", [70, 256, 300])
+def test_rows_special_values_short_blocks(dev, dtype, d):
+    # a few members per destination (blocks of at most 8 rows, taken two per wave when the row
+    # fits one pass of columns), ragged column counts, NaN, infinities, signed zeros and
+    # subnormals, out-of-range rows
+    rng = np.random.default_rng(d)
+    n, B = 20000, 5000
+    v = rounding((n, d), dtype, d + 1)
+    tiny = np.finfo(dtype).smallest_subnormal
+    special = np.array([np.nan, np.inf, -np.inf, -0.0, 0.0, tiny, -tiny], dtype)
+    flat = v.reshape(-1)
+    pos = rng.choice(flat.size, 5000, replace=False)
+    flat[pos] = special[rng.integers(0, special.size, pos.size)]
+    idx = rng.integers(-1, B + 1, n).astype(np.int32)
+    o = rounding((B, d), dtype, d + 2)
+    o.reshape(-1)[::7] = -0.0
+    got, prev, k = gpu_scatter(v, idx, o, dev, want_prev=True)
+    want, wprev, wk = oracle.scatter_add(v, idx, o, want_prev=True)
+    assert bits_equal(got, want), (d, first_mismatch(got, want))
+    assert k == wk and bits_equal(prev, wprev)
+
+
 def test_rows_c4_shape(dev):
     src, rows, out0 = workloads.rows_case()
     got, _, _ = gpu_scatter(src, rows, out0, dev)
