@@ -206,6 +206,29 @@ def test_ten_bit_path_is_taken(dev):
         assert rep["k_radix_scatter"][0] == passes, (n, rep["k_radix_scatter"])
 
 
+@pytest.mark.parametrize("dtype", [F32, F64])
+@pytest.mark.parametrize("B", [100, 300])
+def test_scalar_piece_boundaries(dev, dtype, B):
+    # member counts around the reduction's cuts: one lane (<= 32), a piece of 512 or 1024
+    # positions, several 1024-position pieces of one block (up to 8), whole 8192-position
+    # blocks and the long-destination combine; B = 100 takes the 32-bit-key reduction, 300 the
+    # byte path's
+    sizes = [1, 32, 33, 512, 513, 1023, 1024, 1025, 2047, 2049, 4096, 5000, 8191, 8192, 8193,
+             3 * 8192 + 1000]
+    rng = np.random.default_rng(B + len(sizes))
+    listed = [(7 * k) % B for k in range(len(sizes))]
+    others = np.array([b for b in range(-1, B + 1) if b not in listed], np.int32)
+    idx = np.concatenate([np.full(c, b, np.int32) for b, c in zip(listed, sizes)]
+                         + [others[rng.integers(0, others.size, 3001)]])
+    idx = idx[rng.permutation(idx.size)]
+    v = rounding(idx.size, dtype, B)
+    o = rounding(B, dtype, B + 1)
+    got, prev, k = gpu_scatter(v, idx, o, dev, want_prev=True)
+    want, wprev, wk = oracle.scatter_add(v, idx, o, want_prev=True)
+    assert bits_equal(got, want), (B, first_mismatch(got, want))
+    assert k == wk and bits_equal(prev, wprev)
+
+
 # ---------------------------------------------------------------- rows
 
 def test_rows_worked_example(dev):
