@@ -129,6 +129,15 @@ def test_all_skipped_and_empty(dev, dtype):
     det.det_scatter_add_running(v, idx, torch.zeros(0, dtype=tdt, device=dev), prev=prev,
                                 n_skipped=nk)
     assert int(nk.item()) == 50
+    # every source skipped above the size from which f32 values ride through the sort and
+    # prev goes out through source windows: no pair in any window
+    n = (1 << 21) + 1
+    v = torch.ones(n, dtype=tdt, device=dev)
+    idx = torch.full((n,), -1, dtype=torch.int32, device=dev)
+    idx[::2] = 4
+    prev = torch.full((n,), float("nan"), dtype=tdt, device=dev)
+    det.det_scatter_add_running(v, idx, out, prev=prev, n_skipped=nk)
+    assert int(nk.item()) == n and torch.isnan(prev).all() and (out == 0).all()
 
 
 def test_integer_data_is_a_loop_of_atomics(dev):
