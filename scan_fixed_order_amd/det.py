@@ -8,6 +8,7 @@ PyTorch fallback, and a missing library is an error.
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional
 
@@ -100,15 +101,24 @@ def _dtype_code(t: torch.Tensor, allow_int: bool = False) -> int:
 
 
 def _dev_ptr(t: Optional[torch.Tensor]):
+    # plain integers: ctypes passes them as void* (the argument types are declared)
     if t is None:
         return None
     if not t.is_cuda:
         raise ValueError("det operates on device tensors")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
-def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+# the current stream's raw handle without building a torch Stream object per call (what
+# torch.cuda.current_stream(device).cuda_stream returns), when this torch has the accessor
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(device) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None
+                           else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> torch.Tensor:
@@ -132,6 +142,7 @@ def _flat(t: torch.Tensor) -> torch.Tensor:
 
 # ------------------------------------------------------------------ sum
 
+@functools.lru_cache(maxsize=256)
 def det_sum_workspace_size(n: int, dtype_code: int) -> int:
     return lib().det_sum_workspace_size(n, dtype_code)
 
@@ -165,6 +176,7 @@ def det_sum_noalloc(x: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
 
 # ------------------------------------------------------------------ scan
 
+@functools.lru_cache(maxsize=256)
 def det_scan_workspace_size(n: int, dtype_code: int, flags: int = 0, num_segments: int = 0) -> int:
     return lib().det_scan_workspace_size(n, dtype_code, flags, num_segments)
 
@@ -216,10 +228,12 @@ def det_scan_error(ws: torch.Tensor) -> torch.Tensor:
 
 # ------------------------------------------------------------------ scatter-add
 
+@functools.lru_cache(maxsize=256)
 def det_scatter_add_workspace_size(n: int, num_out: int, row_len: int, dtype_code: int) -> int:
     return lib().det_scatter_add_workspace_size(n, num_out, row_len, dtype_code)
 
 
+@functools.lru_cache(maxsize=256)
 def det_scatter_add_running_workspace_size(n: int, num_out: int, row_len: int,
                                            dtype_code: int) -> int:
     return lib().det_scatter_add_running_workspace_size(n, num_out, row_len, dtype_code)
