@@ -155,9 +155,10 @@ def det_sum(x: torch.Tensor, out: Optional[torch.Tensor] = None,
     n = x.numel()
     if out is None:
         out = torch.empty((), dtype=x.dtype, device=x.device)
-    w = _workspace(det_sum_workspace_size(n, dt), x.device, ws)
+    dev = x.device
+    w = _workspace(det_sum_workspace_size(n, dt), dev, ws)
     _check(lib().det_sum(_dev_ptr(x), n, dt, _dev_ptr(out), _dev_ptr(w), w.numel(),
-                         _stream(x.device)), "det_sum")
+                         _stream(dev)), "det_sum")
     return out
 
 
@@ -205,9 +206,10 @@ def det_scan(x: torch.Tensor, y: Optional[torch.Tensor] = None, exclusive: bool 
             raise TypeError("offsets must be int64")
         offsets = _flat(offsets)
         nseg = offsets.numel() - 1
-    w = _workspace(det_scan_workspace_size(n, dt, flags, max(nseg, 0)), x.device, ws)
+    dev = x.device
+    w = _workspace(det_scan_workspace_size(n, dt, flags, max(nseg, 0)), dev, ws)
     _check(lib().det_scan(_dev_ptr(x), _dev_ptr(y), n, dt, flags, _dev_ptr(offsets), nseg,
-                          _dev_ptr(w), w.numel(), _stream(x.device)), "det_scan")
+                          _dev_ptr(w), w.numel(), _stream(dev)), "det_scan")
     if check or health is not None:
         h = health if health is not None else torch.empty((), dtype=torch.int32, device=x.device)
         if h.dtype != torch.int32 or h.numel() != 1:
@@ -267,10 +269,11 @@ def _scatter(entry: str, values: torch.Tensor, index: torch.Tensor, out: torch.T
         raise ValueError("n_skipped must be an int64 tensor with one element")
     size_fn = (det_scatter_add_running_workspace_size if entry == "det_scatter_add_running"
                else det_scatter_add_workspace_size)
-    w = _workspace(size_fn(n, num_out, row_len, dt), values.device, ws)
+    dev = values.device
+    w = _workspace(size_fn(n, num_out, row_len, dt), dev, ws)
     _check(getattr(lib(), entry)(_dev_ptr(values), _dev_ptr(index), n, row_len, dt, _dev_ptr(out),
                                  num_out, _dev_ptr(prev), _dev_ptr(n_skipped), _dev_ptr(w),
-                                 w.numel(), _stream(values.device)), entry)
+                                 w.numel(), _stream(dev)), entry)
     return out
 
 
